@@ -1,0 +1,439 @@
+"""Pins for the CPU oracle: each check ties a part of the oracle to something
+other than itself -- a figure the pages print, a closed form, an invariant, a
+library routine the oracle does not use, or exact rational arithmetic on tiny
+inputs -- chosen so that a dropped term, a wrong sign or index, or a
+transposed operand fails at least one of them.  CPU only."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import mpmath
+import numpy as np
+import pytest
+import torch
+
+from oracle import hc_oracle as O
+from tests import numerics as N
+from transformer_hyper_connection_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(12345)
+
+
+def page(key):
+    with open(os.path.join(GOLDEN, "page_figures.json")) as f:
+        return json.load(f)[key]
+
+
+def rand_bf16(shape, scale=1.0):
+    return synth.f64_to_bf16_bits(rng.standard_normal(shape) * scale)
+
+
+def rand_coefs(n, hc=4):
+    post = rng.uniform(0, 2, (n, hc)).astype(np.float32)
+    comb = rng.uniform(0, 1, (n, hc, hc)).astype(np.float32)
+    return post, comb
+
+
+# ------------------------------------------------------------ page figures
+def test_parameter_count_matches_page():
+    hc, d = page("hc_mult")["value"], page("dim")["value"]
+    fn, base, scale = synth.hc_params("step", 2, hc, d)
+    assert fn.size + base.size + scale.size == page("stream_weights_per_sublayer")["value"]
+    # the oracle consumes exactly those shapes: 24 mixes out of one projection
+    x = rand_bf16((2, hc, d))
+    m = O.hc_mixes(x, fn, 1e-6)
+    assert m.shape == (2, (2 + hc) * hc)
+    # the reading weights use hc offsets and one scale
+    lp = page("learned_pre_params")
+    assert lp["offsets"] == hc and lp["offsets"] + lp["scales"] == lp["value"]
+    pre, post, comb = O.hc_split_sinkhorn(m, scale, base, hc)
+    assert pre.shape == (2, hc) and post.shape == (2, hc) and comb.shape == (2, hc, hc)
+
+
+def test_final_norm_width_matches_page():
+    d = page("final_norm_params")["value"]
+    y = rand_bf16((3, d))
+    assert O.rms_norm(y, np.ones(d, np.float32), page("final_norm_eps")["value"]).shape == (3, d)
+
+
+# ------------------------------------------------------------ dtype helpers
+def test_bf16_rounding_exact_rational_and_torch():
+    # includes exact ties, subnormals, large values
+    vals = np.concatenate([
+        rng.standard_normal(4000).astype(np.float32),
+        (rng.standard_normal(500) * 1e-38).astype(np.float32),
+        (rng.standard_normal(500) * 1e30).astype(np.float32),
+        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** -130, 0.0, -0.0], np.float32),
+    ])
+    got = O.f32_to_bf16(vals)
+    for v, b in zip(vals[:1500], got[:1500]):
+        ref = N.rne_bf16(Fraction(float(v)))
+        assert N.bits_to_f64([b])[0] == float(ref)
+    tb = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, tb)
+    # round trip is exact
+    assert np.array_equal(O.f32_to_bf16(O.bf16_to_f32(got)), got)
+
+
+def test_f32_arithmetic_is_ieee():
+    a = rng.standard_normal(300).astype(np.float32)
+    b = rng.standard_normal(300).astype(np.float32)
+    for x, y, s, p in zip(a, b, a + b, a * b):
+        assert Fraction(float(s)) == N.rne_f32(Fraction(float(x)) + Fraction(float(y)))
+        assert Fraction(float(p)) == N.rne_f32(Fraction(float(x)) * Fraction(float(y)))
+
+
+# ------------------------------------------------------------ hc_post
+def test_hc_post_identity_comb_zero_post_returns_streams():
+    x = rand_bf16((5, 4, 64)); delta = rand_bf16((5, 64))
+    post = np.zeros((5, 4), np.float32)
+    comb = np.broadcast_to(np.eye(4, dtype=np.float32), (5, 4, 4)).copy()
+    assert np.array_equal(O.hc_post(delta, x, post, comb), x)
+
+
+def test_hc_post_permutation_comb_permutes_streams():
+    x = rand_bf16((5, 4, 64)); delta = rand_bf16((5, 64))
+    perm = [2, 0, 3, 1]                      # destination k takes source perm[k]
+    comb = np.zeros((5, 4, 4), np.float32)
+    for k, j in enumerate(perm):
+        comb[:, j, k] = 1.0
+    out = O.hc_post(delta, x, np.zeros((5, 4), np.float32), comb)
+    for k, j in enumerate(perm):
+        assert np.array_equal(out[:, k], x[:, j])
+
+
+def test_hc_post_orientation_source_row_destination_column():
+    x = rand_bf16((3, 4, 32)); delta = rand_bf16((3, 32))
+    comb = np.zeros((3, 4, 4), np.float32)
+    comb[:, 0, 1] = 1.0                      # C[j=0][k=1]: stream 0 -> stream 1
+    out = O.hc_post(delta, x, np.zeros((3, 4), np.float32), comb)
+    assert np.array_equal(out[:, 1], x[:, 0])
+    for o in (0, 2, 3):
+        assert not (out[:, o] & 0x7FFF).any()       # zeros (signed)
+
+
+def test_hc_post_delta_enters_only_weighted_stream():
+    x = rand_bf16((4, 4, 48)); delta = rand_bf16((4, 48))
+    for k in range(4):
+        post = np.zeros((4, 4), np.float32); post[:, k] = 1.0
+        out = O.hc_post(delta, x, post, np.zeros((4, 4, 4), np.float32))
+        assert np.array_equal(out[:, k], delta)
+        for o in range(4):
+            if o != k:
+                assert not (out[:, o] & 0x7FFF).any()
+
+
+def test_hc_post_unit_post_identity_comb_is_bf16_add():
+    x = rand_bf16((6, 4, 80)); delta = rand_bf16((6, 80))
+    out = O.hc_post(delta, x, np.ones((6, 4), np.float32),
+                    np.broadcast_to(np.eye(4, dtype=np.float32), (6, 4, 4)).copy())
+    tx = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+    td = torch.from_numpy(delta.view(np.int16)).view(torch.bfloat16)
+    ref = (tx + td[:, None, :]).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(out, ref)
+
+
+def test_hc_post_power_of_two_homogeneous():
+    x = rand_bf16((4, 4, 40)); delta = rand_bf16((4, 40))
+    post, comb = rand_coefs(4)
+    a = O.hc_post(delta, x, post, comb)
+    x2 = O.f32_to_bf16(O.bf16_to_f32(x) * 4); d2 = O.f32_to_bf16(O.bf16_to_f32(delta) * 4)
+    b = O.hc_post(d2, x2, post, comb)
+    assert np.array_equal(O.bf16_to_f32(b), O.bf16_to_f32(a) * 4)
+
+
+def test_hc_post_exact_rational_tiny():
+    n, hc, d = 2, 4, 6
+    x = rand_bf16((n, hc, d)); delta = rand_bf16((n, d))
+    post, comb = rand_coefs(n)
+    out = O.hc_post(delta, x, post, comb)
+    X = N.bits_to_f64(x); D = N.bits_to_f64(delta)
+    for t in range(n):
+        for k in range(hc):
+            for i in range(d):
+                a = N.rne_f32(Fraction(float(post[t, k])) * Fraction(D[t, i]))
+                s = N.rne_f32(Fraction(float(comb[t, 0, k])) * Fraction(X[t, 0, i]))
+                for j in range(1, hc):
+                    s = N.rne_f32(s + N.rne_f32(Fraction(float(comb[t, j, k])) * Fraction(X[t, j, i])))
+                ref = N.rne_bf16(N.rne_f32(a + s))
+                assert N.bits_to_f64([out[t, k, i]])[0] == float(ref)
+
+
+# ------------------------------------------------------------ hc_pre
+def test_hc_pre_one_hot_returns_stream():
+    x = rand_bf16((5, 4, 64))
+    for j in range(4):
+        p = np.zeros((5, 4), np.float32); p[:, j] = 1.0
+        assert np.array_equal(O.hc_pre(x, p), x[:, j])
+
+
+def test_hc_pre_quarter_on_identical_streams():
+    h = rand_bf16((7, 96))
+    x = np.repeat(h[:, None], 4, axis=1)
+    assert np.array_equal(O.hc_pre(x, np.full((7, 4), 0.25, np.float32)), h)
+
+
+def test_hc_pre_weights_and_exact_rational():
+    x = rand_bf16((2, 4, 8))
+    p = rng.uniform(0, 1, (2, 4)).astype(np.float32)
+    y = O.hc_pre(x, p)
+    X = N.bits_to_f64(x)
+    for t in range(2):
+        for i in range(8):
+            s = N.rne_f32(Fraction(float(p[t, 0])) * Fraction(X[t, 0, i]))
+            for j in range(1, 4):
+                s = N.rne_f32(s + N.rne_f32(Fraction(float(p[t, j])) * Fraction(X[t, j, i])))
+            assert N.bits_to_f64([y[t, i]])[0] == float(N.rne_bf16(s))
+
+
+# ------------------------------------------------------------ hc_mixes
+def test_rms_statistic_stream_constants_closed_form():
+    c = np.array([0.5, -1.25, 2.0, 3.0])
+    d = 64
+    x = np.repeat(O.f32_to_bf16(np.float32(c))[None, :, None], d, axis=2)  # [1,4,d]
+    r = O.rms_statistic(x, 1e-6)
+    eps = float(np.float32(1e-6))
+    assert r[0] == pytest.approx(1 / math.sqrt((c ** 2).sum() / 4 + eps), rel=1e-15)
+
+
+def test_mixes_one_hot_weight_picks_flattened_entry():
+    hc, d = 4, 16
+    x = rand_bf16((3, hc, d))
+    fn = np.zeros((24, hc * d), np.float32)
+    picks = [(0, 0), (1, 5), (2, 15), (3, 7), (3, 0)]
+    for q, (j, i) in enumerate(picks):
+        fn[q, j * d + i] = 1.0
+    m = O.hc_mixes(x, fn, 0.0)
+    X = N.bits_to_f64(x)
+    r = 1 / np.sqrt((X.reshape(3, -1) ** 2).mean(axis=1))
+    for q, (j, i) in enumerate(picks):
+        np.testing.assert_allclose(m[:, q], X[:, j, i] * r, rtol=1e-7)
+    assert not m[:, len(picks):].any()
+
+
+def test_mixes_power_of_two_scale_invariance():
+    x = rand_bf16((4, 4, 32))
+    fn = (rng.standard_normal((24, 128)) * 0.02).astype(np.float32)
+    a = O.hc_mixes(x, fn, 0.0)
+    b = O.hc_mixes(O.f32_to_bf16(O.bf16_to_f32(x) * 8), fn, 0.0)
+    assert np.array_equal(a, b)
+
+
+def test_mixes_high_precision_brute_force():
+    mpmath.mp.dps = 40
+    hc, d = 4, 8
+    x = rand_bf16((2, hc, d))
+    fn = (rng.standard_normal((24, hc * d)) * 0.3).astype(np.float32)
+    m = O.hc_mixes(x, fn, 1e-6)
+    X = N.bits_to_f64(x).reshape(2, -1)
+    eps = mpmath.mpf(float(np.float32(1e-6)))
+    for t in range(2):
+        ms = sum(mpmath.mpf(v) ** 2 for v in X[t]) / (hc * d)
+        r = 1 / mpmath.sqrt(ms + eps)
+        for q in range(24):
+            ref = r * sum(mpmath.mpf(float(w)) * mpmath.mpf(v) for w, v in zip(fn[q], X[t]))
+            assert float(m[t, q]) == float(np.float32(float(ref)))
+
+
+# ------------------------------------------------------------ split
+def test_split_zero_mix_zero_base():
+    m = np.zeros((3, 24), np.float32)
+    pre, post, comb = O.hc_split_sinkhorn(m, np.ones(3, np.float32), np.zeros(24, np.float32))
+    assert np.all(pre == np.float32(0.5 + 1e-6))
+    assert np.all(post == 1.0)
+
+
+def test_split_uses_documented_slices_and_scales():
+    # distinct values route to distinct outputs: pre <- m[0:4]*s0+b[0:4],
+    # post <- m[4:8]*s1+b[4:8], comb logits <- m[8+4j+k]*s2+b[8+4j+k]
+    ln3 = math.log(3.0)
+    m = np.zeros((1, 24), np.float32)
+    b = np.zeros(24, np.float32)
+    s = np.array([1.0, 2.0, 0.5], np.float32)
+    m[0, 1] = ln3                      # pre_1 = sigma(ln 3) + eps = 3/4 + eps
+    b[2] = -ln3                        # pre_2 = sigma(-ln 3) + eps = 1/4 + eps
+    m[0, 5] = ln3 / 2                  # post_1 = 2 sigma(2 * ln3/2) = 3/2
+    b[6] = math.log(7.0)               # post_2 = 2 sigma(ln 7) = 7/4
+    pre, post, _ = O.hc_split_sinkhorn(m, s, b)
+    np.testing.assert_allclose(pre[0], [0.5 + 1e-6, 0.75 + 1e-6, 0.25 + 1e-6, 0.5 + 1e-6], atol=2e-7)
+    np.testing.assert_allclose(post[0], [1.0, 1.5, 1.75, 1.0], atol=2e-7)
+
+
+def test_split_sigmoid_high_precision_and_ranges():
+    mpmath.mp.dps = 30
+    m = (rng.standard_normal((200, 24)) * 6).astype(np.float32)
+    s = np.array([0.7, 1.9, 1.3], np.float32)
+    b = (rng.standard_normal(24) * 0.1).astype(np.float32)
+    pre, post, comb = O.hc_split_sinkhorn(m, s, b)
+    eps = float(np.float32(1e-6))
+    for t in range(0, 200, 17):
+        for j in range(4):
+            u = mpmath.mpf(float(m[t, j])) * mpmath.mpf(float(s[0])) + mpmath.mpf(float(b[j]))
+            assert float(pre[t, j]) == float(np.float32(float(1 / (1 + mpmath.exp(-u)) + eps)))
+            u = mpmath.mpf(float(m[t, 4 + j])) * mpmath.mpf(float(s[1])) + mpmath.mpf(float(b[4 + j]))
+            assert float(post[t, j]) == float(np.float32(float(2 / (1 + mpmath.exp(-u)))))
+    assert pre.min() >= np.float32(eps) and pre.max() <= np.float32(1 + eps)
+    assert post.min() >= 0 and post.max() <= 2
+    assert comb.min() >= 0
+
+
+# ------------------------------------------------------------ Sinkhorn
+def _uniform_closed_form(iters, eps):
+    """Equal logits: every entry follows a -> a/(4a+eps) from a0 = 1/4 + eps,
+    2*iters-1 times; with b = 1/a that is b -> 4 + eps*b, a linear recurrence
+    solved exactly in rationals."""
+    e = Fraction(eps)
+    b = 1 / (Fraction(1, 4) + e)
+    for _ in range(2 * iters - 1):
+        b = 4 + e * b
+    return 1 / b
+
+
+@pytest.mark.parametrize("iters", [1, 2, 5, 20])
+def test_sinkhorn_uniform_logits_closed_form(iters):
+    eps = float(np.float32(1e-6))
+    A = O.sinkhorn(np.full((2, 4, 4), 0.37), iters, 1e-6)
+    ref = float(_uniform_closed_form(iters, eps))
+    np.testing.assert_allclose(A, ref, rtol=1e-14)
+    if iters == 20:
+        assert abs(ref - 0.24999975) < 1e-12          # (1 - eps)/4 to within eps^2
+        assert np.float32(ref) == np.float32(0.24999975)
+
+
+def test_sinkhorn_additive_logits_give_quarter_without_eps():
+    u = rng.standard_normal((6, 4, 1)); v = rng.standard_normal((6, 1, 4))
+    for iters in (1, 3, 20):
+        A = O.sinkhorn(u + v, iters, 0.0)
+        np.testing.assert_allclose(A, 0.25, atol=1e-15)
+
+
+def test_sinkhorn_last_step_is_column_normalisation():
+    L = rng.standard_normal((50, 4, 4)) * 3
+    eps = float(np.float32(1e-6))
+    for iters in (1, 2, 7):
+        prev = O.sinkhorn(L, iters, 1e-6)
+        # recompute the final column step on the state before it
+        A = np.exp(L - L.max(-1, keepdims=True)); A = A / A.sum(-1, keepdims=True) + eps
+        if iters > 1:
+            A = O.sinkhorn(L, iters - 1, 1e-6)
+            A = A / (A.sum(-1, keepdims=True) + eps)
+        S = A.sum(-2)
+        np.testing.assert_allclose(prev.sum(-2), S / (S + eps), rtol=1e-13)
+    # orientation: with iters=1 the columns are (nearly) normalised, rows are not
+    A1 = O.sinkhorn(L, 1, 1e-6)
+    assert np.abs(A1.sum(-2) - 1).max() < 1e-3
+    assert np.abs(A1.sum(-1) - 1).max() > 1e-2
+
+
+def test_sinkhorn_row_deviation_non_increasing():
+    L = rng.standard_normal((2000, 4, 4)) * 2.86 * 1.25
+    prev = None
+    for iters in (1, 2, 3, 5, 10, 20, 50, 100, 1000):
+        A = O.sinkhorn(L, iters, 1e-6)
+        dev = np.abs(A.sum(-1) - 1).sum(-1)
+        if prev is not None:
+            assert np.all(dev <= prev + 1e-12)
+        prev = dev
+    assert prev.max() < 1e-2     # converging toward doubly stochastic
+
+
+def test_sinkhorn_permutation_equivariance():
+    L = rng.standard_normal((20, 4, 4)) * 2
+    pr, pc = [3, 1, 0, 2], [1, 2, 3, 0]
+    A = O.sinkhorn(L, 20, 1e-6)
+    B = O.sinkhorn(L[:, pr][:, :, pc], 20, 1e-6)
+    np.testing.assert_allclose(B, A[:, pr][:, :, pc], rtol=1e-12)
+
+
+def test_sinkhorn_high_precision_brute_force():
+    mpmath.mp.dps = 40
+    L = rng.standard_normal((3, 4, 4)) * 4
+    A = O.sinkhorn(L, 20, 1e-6)
+    e = mpmath.mpf(float(np.float32(1e-6)))
+    for t in range(3):
+        M = [[mpmath.mpf(float(L[t, j, k])) for k in range(4)] for j in range(4)]
+        for j in range(4):
+            mx = max(M[j]); ex = [mpmath.exp(v - mx) for v in M[j]]; s = sum(ex)
+            M[j] = [v / s + e for v in ex]
+
+        def col():
+            for k in range(4):
+                c = sum(M[j][k] for j in range(4)) + e
+                for j in range(4):
+                    M[j][k] /= c
+        col()
+        for _ in range(19):
+            for j in range(4):
+                r = sum(M[j]) + e
+                M[j] = [v / r for v in M[j]]
+            col()
+        np.testing.assert_allclose(A[t], np.array([[float(v) for v in row] for row in M]), rtol=1e-13)
+
+
+def test_sinkhorn_rejects_zero_iterations():
+    with pytest.raises(ValueError):
+        O.sinkhorn(np.zeros((1, 4, 4)), 0)
+
+
+# ------------------------------------------------------------ RMSNorm
+def test_rms_norm_textbook_example():
+    mpmath.mp.dps = 30
+    y = O.f32_to_bf16(np.array([[3.0, 4.0]], np.float32))
+    z = O.rms_norm(y, np.array([1.0, 2.0], np.float32), 0.0)
+    r = 1 / mpmath.sqrt(mpmath.mpf(25) / 2)
+    for i, (g, v) in enumerate([(1, 3), (2, 4)]):
+        exact = float(g * v * r)
+        assert N.bits_to_f64([z[0, i]])[0] == float(N.rne_bf16(N.rne_f32(Fraction(exact))))
+
+
+def test_rms_norm_unit_gain_unit_mean_square():
+    y = rand_bf16((10, 5120), 3.0)
+    z = N.bits_to_f64(O.rms_norm(y, np.ones(5120, np.float32), 1e-6))
+    np.testing.assert_allclose((z ** 2).mean(-1), 1.0, rtol=3e-3)
+
+
+def test_rms_norm_eps_dominates_zero_row():
+    y = np.zeros((1, 16), np.uint16)
+    assert not O.rms_norm(y, np.ones(16, np.float32), 1e-6).any()
+
+
+# ------------------------------------------------------------ compositions
+def test_boundary_with_identity_write_equals_entry():
+    hc, d, n = 4, 64, 6
+    x = rand_bf16((n, hc, d)); delta = rand_bf16((n, d))
+    fn = (rng.standard_normal((24, hc * d)) * 0.05).astype(np.float32)
+    base = (rng.standard_normal(24) * 0.1).astype(np.float32)
+    scale = np.array([1.0, 1.5, 0.8], np.float32)
+    pre_in = rng.uniform(0, 1, (n, hc)).astype(np.float32)
+    g = (1 + rng.standard_normal(d) * 0.1).astype(np.float32)
+    eye = np.broadcast_to(np.eye(4, dtype=np.float32), (n, 4, 4)).copy()
+    a = O.boundary(x=x, delta=delta, post_in=np.zeros((n, 4), np.float32), comb_in=eye,
+                   pre_in=pre_in, hc_fn=fn, hc_base=base, hc_scale=scale, gamma=g)
+    b = O.boundary(x=x, pre_in=pre_in, hc_fn=fn, hc_base=base, hc_scale=scale, gamma=g)
+    assert np.array_equal(a["x_out"], x)
+    for k in ("mixes", "pre", "post", "comb", "y"):
+        assert np.array_equal(a[k], b[k])
+
+
+def test_boundary_fresh_mode_reads_with_new_pre():
+    hc, d, n = 4, 64, 4
+    x = rand_bf16((n, hc, d))
+    fn = (rng.standard_normal((24, hc * d)) * 0.05).astype(np.float32)
+    base = np.zeros(24, np.float32); scale = np.ones(3, np.float32)
+    o = O.boundary(x=x, hc_fn=fn, hc_base=base, hc_scale=scale)
+    assert np.array_equal(o["y"], O.hc_pre(x, o["pre"]))
+
+
+def test_stack_identical_streams_first_read_is_embedding():
+    # with 0.25 per stream, the first read of four identical copies is the
+    # embedding itself, so the first stand-in output is RMSNorm(embedding)
+    n, d = 3, 64
+    h = rand_bf16((n, d))
+    fn = (rng.standard_normal((24, 4 * d)) * 0.05).astype(np.float32)
+    params = [(fn, np.zeros(24, np.float32), np.ones(3, np.float32))] * 2
+    gammas = [np.ones(d, np.float32)] * 2
+    rec = []
+    O.stack(h=h, params=params, gammas=gammas, gamma_final=np.ones(d, np.float32), record=rec)
+    assert np.array_equal(rec[0][1], O.rms_norm(h, np.ones(d, np.float32), 1e-6))
