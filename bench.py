@@ -1,0 +1,200 @@
+"""Benchmark: fused HC sublayer boundary, prefill T=4096, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode fresh|lag] [--no-cpu]
+
+One step = one fused sublayer-boundary call over the whole 4096-token batch:
+hc_post(delta, X, post, comb) -> hc_mixes on X' -> split/Sinkhorn -> hc_pre ->
+RMSNorm, all inside libhc.  --mode fresh (default) reads X' with the pre this
+call derives; --mode lag reads it with the pre of the previous boundary (the
+data flow of the pages' Block.forward).  Inputs are seeded synthetic tensors
+(transformer_hyper_connection_amd.synth, workload "prefill"), resident in HBM
+before timing; several input/output buffer sets rotate so that repeated steps
+do not hit in the 256 MB last-level cache.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import transformer_hyper_connection_amd as T  # noqa: E402
+from transformer_hyper_connection_amd import synth  # noqa: E402
+
+N_TOK = synth.WORKLOAD_TOKENS["prefill"]
+HC, D, MIX = 4, 5120, 24
+PEAK_HBM_GBS = 8000.0
+# algorithmic bytes: per token  X 4*d*2 + delta d*2 + X' 4*d*2 + z d*2 (bf16)
+#                               + post_in/comb_in 16+64 (+ pre_in 16 in lag mode) + pre/post/comb out 96
+#                    per call   hc_fn (fp32) 24*4d*4 + base 96 + scale 12 + gamma d*4
+BYTES_TOKEN_COMMON = 4 * D * 2 + D * 2 + 4 * D * 2 + D * 2 + 16 + 64 + 96
+BYTES_CALL = MIX * 4 * D * 4 + MIX * 4 + 3 * 4 + D * 4
+
+
+def algorithmic_bytes(n: int, mode: str) -> int:
+    per_tok = BYTES_TOKEN_COMMON + (16 if mode == "lag" else 0)
+    return n * per_tok + BYTES_CALL
+
+
+def bf(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def f32(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+
+def make_sets(s, dev, n_sets):
+    base = {"x": bf(s["x"], dev), "delta": bf(s["delta"], dev), "post_in": f32(s["post_in"], dev),
+            "comb_in": f32(s["comb_in"], dev), "pre_in": f32(s["pre_in"], dev)}
+    sets = []
+    for i in range(n_sets):
+        ins = base if i == 0 else {k: v.clone() for k, v in base.items()}
+        outs = {"x_out": torch.empty(N_TOK, HC, D, dtype=torch.bfloat16, device=dev),
+                "y": torch.empty(N_TOK, D, dtype=torch.bfloat16, device=dev),
+                "pre": torch.empty(N_TOK, HC, device=dev), "post": torch.empty(N_TOK, HC, device=dev),
+                "comb": torch.empty(N_TOK, HC, HC, device=dev)}
+        sets.append((ins, outs))
+    return sets
+
+
+def time_mode(mode, sets, params, steps, warmup):
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        ins, outs = sets[i % len(sets)]
+        T.hc_boundary(ins["x"], delta=ins["delta"], post_in=ins["post_in"], comb_in=ins["comb_in"],
+                      pre_in=ins["pre_in"] if mode == "lag" else None, out=outs, **params)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call_ms = [a.elapsed_time(b) for a, b in ev]
+    return wall, per_call_ms
+
+
+def copy_bandwidth(dev, nbytes=1 << 30, reps=10):
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def cpu_baseline(s, repeats=2):
+    """The CPU oracle on the same workload, timed on this host."""
+    from oracle import hc_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        O.boundary(x=s["x"], delta=s["delta"], post_in=s["post_in"], comb_in=s["comb_in"], pre_in=None,
+                   hc_fn=s["hc_fn"], hc_base=s["hc_base"], hc_scale=s["hc_scale"], gamma=s["gamma"])
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    return {"value": round(N_TOK / med, 1), "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"the whole {N_TOK}-token prefill batch, fresh-read boundary, median of {repeats} runs "
+                      f"({med:.2f} s each); float64 BLAS projection on {blas_threads} threads, fp32/fp64 "
+                      f"elementwise NumPy on 1 thread; host has {len(os.sched_getaffinity(0))} usable cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--mode", choices=["fresh", "lag"], default="fresh")
+    ap.add_argument("--sets", type=int, default=4, help="rotating input/output buffer sets")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; the glue is per-token and would shard over "
+              "tokens with no exchange (see DESIGN.md).  Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating the {N_TOK}-token prefill workload", file=sys.stderr, flush=True)
+    s = synth.boundary_inputs("prefill")
+    sets = make_sets(s, dev, args.sets)
+    params = dict(fn_packed=T.hc_fn_pack(f32(s["hc_fn"], dev)), hc_base=f32(s["hc_base"], dev),
+                  hc_scale=f32(s["hc_scale"], dev), gamma=f32(s["gamma"], dev), iters=20, hc_eps=1e-6,
+                  norm_eps=1e-6, rms_eps=1e-6)
+    torch.cuda.synchronize()
+
+    results = {}
+    for mode in ("fresh", "lag"):
+        print(f"[bench] timing mode={mode}", file=sys.stderr, flush=True)
+        wall, per_call = time_mode(mode, sets, params, args.steps, args.warmup)
+        nbytes = algorithmic_bytes(N_TOK, mode)
+        med = statistics.median(per_call)
+        results[mode] = {
+            "wall_s": wall, "ms_per_step": wall / args.steps * 1e3, "call_ms_median": med,
+            "call_ms_p10": float(np.percentile(per_call, 10)), "call_ms_p90": float(np.percentile(per_call, 90)),
+            "call_ms_mean": float(np.mean(per_call)), "algorithmic_bytes": nbytes,
+            "tokens_per_s": N_TOK * args.steps / wall, "gbs_at_median": nbytes / (med * 1e-3) / 1e9,
+        }
+    copy_gbs = copy_bandwidth(dev)
+    head = results[args.mode]
+    mean_ms = head["call_ms_mean"]
+    achieved = head["algorithmic_bytes"] / (mean_ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(s)
+    line = {
+        "metric": "tokens/s of fused HC sublayer boundary (T=4096); HBM GB/s as % of peak",
+        "value": round(head["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 streams, fp32 arithmetic",
+        "data": "synthetic (seeded; shapes and distributions of the prefill boundary workload)",
+        "config": {"workload": "fused sublayer boundary, prefill B=1 T=4096, hc=4, d=5120, sinkhorn_iters=20, "
+                               f"RMSNorm; read with the {'freshly derived' if args.mode == 'fresh' else 'previous'} pre",
+                   "tokens": N_TOK, "read_mode": args.mode, "buffer_sets": args.sets},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "hc_boundary (fused boundary call)",
+                     "algorithmic_bytes_per_launch": head["algorithmic_bytes"],
+                     "avg_launch_ms": round(mean_ms, 5)},
+        "cpu_baseline": cpu,
+        "modes": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                  for k, v in results.items()},
+        "copy_kernel_gbs": round(copy_gbs, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

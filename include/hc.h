@@ -1,0 +1,192 @@
+/*
+ * hc.h -- C ABI of libhc, the Hyper-Connections (HC) residual glue for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * In a Hyper-Connections block the residual is hc parallel copies ("streams")
+ * of width d.  Around every sublayer the glue
+ *   - derives 24 mix numbers per token from the streams (hc_mixes),
+ *   - turns them into reading weights pre, writing weights post and a
+ *     Sinkhorn-normalised hc x hc combination comb (hc_split_sinkhorn),
+ *   - reads the streams into one sublayer input (hc_pre),
+ *   - writes the sublayer output back into the streams (hc_post).
+ * Sources: the model-atlas pages "Source layer, pairs pooled" (Block code
+ * panel: hc_mixes, hc_pre, hc_post, forward), "Reading weights" (reading-weight
+ * equation; split/Sinkhorn kernel panel), "Write the streams" (stream-update
+ * equation) and "Final RMSNorm" (RMSNorm equation and class).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller, row-major and
+ *     contiguous.  The library keeps no pointer after a call returns and
+ *     allocates no memory in any compute entry point.
+ *   - bf16 tensors are passed as raw bit patterns (hc_bf16) and must be 16-byte
+ *     aligned; float tensors must be 16-byte aligned.
+ *   - n = number of tokens (batch x positions, flattened).  hc must be 4.
+ *     d must be a positive multiple of 64 and at most 5120.
+ *   - stream is a hipStream_t (NULL = the null stream).  Calls enqueue work on
+ *     it and return without synchronising; the current HIP device of the
+ *     calling thread is used.  Calls on distinct streams may run concurrently
+ *     from different threads.
+ *   - Arguments are validated before any HIP call: a bad argument returns
+ *     HC_EINVAL or HC_ENOTSUP and enqueues nothing.  n == 0 returns HC_OK and
+ *     enqueues nothing.  A failed launch returns HC_EHIP; hc_last_error() then
+ *     names the HIP error.  Faults inside a kernel surface, as with any
+ *     asynchronous HIP work, at the caller's next synchronisation.
+ *   - Inputs and outputs must not overlap unless an entry point says so.
+ *   - No NaN/Inf checks are made; non-finite inputs propagate.
+ */
+#ifndef HC_H
+#define HC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t hc_bf16; /* raw bf16 bit pattern */
+
+enum hc_status {
+  HC_OK = 0,
+  HC_EINVAL = -1,  /* NULL or misaligned pointer, negative size, iters < 1, ... */
+  HC_ENOTSUP = -2, /* hc != 4, d not a multiple of 64 or above 5120            */
+  HC_EHIP = -3,    /* a HIP call or kernel launch failed                        */
+  HC_ENODEV = -4   /* no HIP device is visible                                  */
+};
+
+/* Library version as 10000*major + 100*minor + patch. */
+int hc_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* hc_strerror(int status);
+
+/* Detail of the last failure on the calling thread ("" if none).  The string
+ * stays valid until the next call on this thread. */
+const char* hc_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Projection weight packing.
+ * The projection weight hc_fn is [(2+hc)*hc, hc*d] float32 in the out x in
+ * layout of a linear layer ("Source layer, pairs pooled": Block constructor).
+ * The compute entry points take it pre-packed: each fp32 weight is split into
+ * three bf16 terms hi + mid + lo (each the nearest bf16 to what the previous
+ * terms leave), which together hold the fp32 value to about 2^-26 relative,
+ * laid out in the tile order of the matrix-core kernels.  Pack once per
+ * parameter set.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of the packed weight for (hc, d); 0 if (hc, d) is not supported. */
+size_t hc_fn_packed_bytes(int hc, int d);
+
+/* hc_fn [(2+hc)*hc, hc*d] float32 -> fn_packed (hc_fn_packed_bytes(hc, d)
+ * bytes, 16-byte aligned). */
+int hc_fn_pack(const float* hc_fn, int hc, int d, void* fn_packed, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * hc_mixes -- "Source layer, pairs pooled", Block.hc_mixes.
+ *   r[t]        = 1 / sqrt(mean_c x[t,c]^2 + norm_eps), c over the flattened
+ *                 hc*d row (index j*d + i)
+ *   mixes[t,q]  = r[t] * sum_c hc_fn[q,c] * x[t,c]
+ * x      [n, hc, d] bf16;  fn_packed from hc_fn_pack.
+ * mixes  [n, (2+hc)*hc] float32 output, or NULL.
+ * If pre, post and comb are all non-NULL the split/Sinkhorn step of
+ * hc_split_sinkhorn also runs (with hc_scale, hc_base, iters, hc_eps) and
+ * writes them, as Block.hc_mixes returns them; otherwise hc_scale/hc_base/
+ * iters/hc_eps are ignored.  At least one of mixes or (pre, post, comb) must
+ * be given.
+ * ------------------------------------------------------------------------- */
+int hc_mixes(const hc_bf16* x, const void* fn_packed, int64_t n, int hc, int d, float norm_eps,
+             float* mixes, const float* hc_scale, const float* hc_base, int iters, float hc_eps,
+             float* pre, float* post, float* comb, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * hc_split_sinkhorn -- "Reading weights": reading-weight equation and the
+ * split/Sinkhorn kernel panel.  With m = mixes[t], s = hc_scale, b = hc_base:
+ *   pre[t,j]  = sigmoid(s[0]*m[j] + b[j]) + hc_eps                 j < hc
+ *   post[t,j] = 2 * sigmoid(s[1]*m[hc+j] + b[hc+j])                j < hc
+ *   L[j][k]   = s[2]*m[2hc + j*hc + k] + b[2hc + j*hc + k]
+ *   comb      = row softmax of L, + hc_eps; each column divided by (its sum +
+ *               hc_eps); then iters-1 rounds of: each row divided by (its sum
+ *               + hc_eps), each column divided by (its sum + hc_eps).
+ * mixes [n, (2+hc)*hc], hc_scale [3], hc_base [(2+hc)*hc] float32 inputs;
+ * pre, post [n, hc] and comb [n, hc, hc] float32 outputs, comb[t][j][k] with
+ * j the source stream (row) and k the destination stream (column).
+ * iters >= 1.  Arithmetic is fp32.
+ * ------------------------------------------------------------------------- */
+int hc_split_sinkhorn(const float* mixes, const float* hc_scale, const float* hc_base, int64_t n,
+                      int hc, int iters, float hc_eps, float* pre, float* post, float* comb,
+                      void* stream);
+
+/* ---------------------------------------------------------------------------
+ * hc_pre -- "Source layer, pairs pooled", Block.hc_pre.
+ *   y[t,i] = bf16( sum_j pre_mix[t,j] * x[t,j,i] )
+ * computed in fp32 with one rounding per product and per partial sum, j
+ * ascending (bit-identical to that sequence of fp32 operations).
+ * x [n, hc, d] bf16, pre_mix [n, hc] float32 -> y [n, d] bf16.
+ * ------------------------------------------------------------------------- */
+int hc_pre(const hc_bf16* x, const float* pre_mix, int64_t n, int hc, int d, hc_bf16* y,
+           void* stream);
+
+/* ---------------------------------------------------------------------------
+ * hc_post -- "Write the streams" stream-update equation; "Source layer, pairs
+ * pooled", Block.hc_post (argument order as there: sublayer output first).
+ *   x_out[t,k,i] = bf16( post[t,k]*delta[t,i] + sum_j comb[t,j,k]*x[t,j,i] )
+ * in fp32 with one rounding per product and per sum: the comb terms summed
+ * j ascending, then added to the post term (bit-identical to that sequence).
+ * delta [n, d] bf16, x [n, hc, d] bf16, post [n, hc], comb [n, hc, hc]
+ * float32 -> x_out [n, hc, d] bf16 (must not overlap x or delta).
+ * ------------------------------------------------------------------------- */
+int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const float* comb,
+            int64_t n, int hc, int d, hc_bf16* x_out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * hc_boundary -- one sublayer boundary in one pass over the streams, read off
+ * "Source layer, pairs pooled", Block.forward:
+ *   X'              = hc_post(delta, x, post_in, comb_in)       (skipped if delta == NULL: X' = x)
+ *   pre/post/comb   = hc_split_sinkhorn(hc_mixes(X'))           (skipped if fn_packed == NULL)
+ *   y               = hc_pre(X', pre_in)                        (pre_in == NULL: the pre just derived)
+ *   y_out           = gamma ? RMSNorm_gamma(y, rms_eps) : y
+ * RMSNorm ("Final RMSNorm"): y_out[t,i] = bf16(gamma[i] * (y[t,i] * r)),
+ * r = 1/sqrt(mean_i y[t,i]^2 + rms_eps), on the bf16 y.
+ * With pre_in given the call follows the pages' data flow: the streams are
+ * read with the reading mix of the previous boundary and the call returns the
+ * (pre, post, comb) of this boundary for the next one.  Use delta == NULL at a
+ * block entry and fn_packed == NULL at the stack exit.
+ * x_out must not overlap x; y_out must not overlap x, x_out or delta.
+ * workspace/workspace_bytes: scratch for the small-n path, at least
+ * hc_boundary_workspace_bytes(n, hc, d) bytes (may be NULL when that is 0).
+ * ------------------------------------------------------------------------- */
+typedef struct hc_boundary_args {
+  uint32_t struct_size; /* = sizeof(hc_boundary_args) */
+  int32_t hc, d, iters;
+  int64_t n;
+  float hc_eps, norm_eps, rms_eps;
+  const hc_bf16* delta;    /* [n, d] or NULL (block entry)                      */
+  const hc_bf16* x;        /* [n, hc, d]                                         */
+  const float* post_in;    /* [n, hc]      required iff delta != NULL            */
+  const float* comb_in;    /* [n, hc, hc]  required iff delta != NULL            */
+  const float* pre_in;     /* [n, hc] or NULL (read with the pre just derived)   */
+  const void* fn_packed;   /* packed weight, or NULL (stack exit: no mixes)      */
+  const float* hc_base;    /* [(2+hc)*hc]  required iff fn_packed != NULL        */
+  const float* hc_scale;   /* [3]          required iff fn_packed != NULL        */
+  const float* gamma;      /* [d] RMSNorm gain, or NULL (no RMSNorm)             */
+  hc_bf16* x_out;          /* [n, hc, d]   required iff delta != NULL            */
+  hc_bf16* y_out;          /* [n, d]       required                              */
+  float* mixes_out;        /* [n, (2+hc)*hc] or NULL                             */
+  float* pre_out;          /* [n, hc]      required iff fn_packed != NULL        */
+  float* post_out;         /* [n, hc]      required iff fn_packed != NULL        */
+  float* comb_out;         /* [n, hc, hc]  required iff fn_packed != NULL        */
+  void* workspace;
+  size_t workspace_bytes;
+} hc_boundary_args;
+
+int hc_boundary(const hc_boundary_args* args, void* stream);
+
+/* Scratch bytes hc_boundary needs for n tokens (0 = none). */
+size_t hc_boundary_workspace_bytes(int64_t n, int hc, int d);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HC_H */

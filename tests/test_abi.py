@@ -1,0 +1,149 @@
+"""C-ABI contract of libhc on the CPU: the library loads, exports every symbol
+include/hc.h declares, the ctypes mirror of hc_boundary_args matches the C
+layout, and argument validation returns its status codes before any HIP call
+(fake, never-dereferenced pointers are used; nothing is launched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from transformer_hyper_connection_amd import hc as H
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hc.h")
+
+P = 0x10000          # a 16-byte aligned fake device address (never dereferenced)
+MIS = 0x10004        # misaligned fake address
+S = None             # null stream
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"\b(hc_[a-z_0-9]+)\s*\(", src)) - {"hc_boundary_args"}
+
+
+@pytest.fixture(scope="module")
+def L():
+    return H.lib()
+
+
+def test_library_exports_every_header_symbol(L):
+    funcs = header_functions()
+    assert funcs == set(H.SIGNATURES), "binding and header disagree"
+    out = subprocess.run(["nm", "-D", "--defined-only", H.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (hc_\w+)", out))
+    assert funcs <= exported, funcs - exported
+    for f in funcs:
+        assert hasattr(L, f)
+
+
+def test_boundary_struct_layout_matches_c(tmp_path):
+    fields = [f for f, _ in H.BoundaryArgs._fields_]
+    prog = tmp_path / "layout.c"
+    prog.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "hc.h"\nint main(void){\n'
+        'printf("%zu\\n", sizeof(hc_boundary_args));\n'
+        + "".join(f'printf("%zu\\n", offsetof(hc_boundary_args, {f}));\n' for f in fields)
+        + "return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), str(prog), "-o", str(exe)],
+                   check=True)
+    vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(H.BoundaryArgs)
+    for f, off in zip(fields, vals[1:]):
+        assert getattr(H.BoundaryArgs, f).offset == off, f
+
+
+def test_header_compiles_as_cxx(tmp_path):
+    src = tmp_path / "t.cpp"
+    src.write_text('#include "hc.h"\nint main(){ return hc_version() > 0 ? 0 : 1; }\n')
+    subprocess.run(["g++", "-std=c++11", "-Wall", "-Werror", "-fsyntax-only", "-I", os.path.dirname(HEADER), str(src)],
+                   check=True)
+
+
+def test_strerror_and_version(L):
+    assert L.hc_version() >= 100
+    for code in (0, -1, -2, -3, -4, 7):
+        assert L.hc_strerror(code)
+
+
+def test_packed_bytes(L):
+    assert L.hc_fn_packed_bytes(4, 5120) == 72 * 4 * 5120 * 2 * 80 // 72  # 80 rows incl. 8 zero rows
+    assert L.hc_fn_packed_bytes(3, 5120) == 0
+    assert L.hc_fn_packed_bytes(4, 100) == 0
+    assert L.hc_fn_packed_bytes(4, 5184) == 0
+
+
+@pytest.mark.parametrize("hc,d,code", [(3, 5120, H.HC_ENOTSUP), (8, 5120, H.HC_ENOTSUP), (4, 100, H.HC_ENOTSUP),
+                                       (4, 0, H.HC_ENOTSUP), (4, 5184, H.HC_ENOTSUP)])
+def test_unsupported_shapes(L, hc, d, code):
+    assert L.hc_pre(P, P, 16, hc, d, P, S) == code
+    assert L.hc_post(P, P, P, P, 16, hc, d, P, S) == code
+    assert L.hc_mixes(P, P, 16, hc, d, 1e-6, P, None, None, 20, 1e-6, None, None, None, S) == code
+    assert L.hc_fn_pack(P, hc, d, P, S) == code
+    assert L.hc_last_error()
+
+
+def test_null_misaligned_negative(L):
+    assert L.hc_pre(None, P, 16, 4, 64, P, S) == H.HC_EINVAL
+    assert b"x" in L.hc_last_error()
+    assert L.hc_pre(MIS, P, 16, 4, 64, P, S) == H.HC_EINVAL
+    assert b"aligned" in L.hc_last_error()
+    assert L.hc_pre(P, P, -1, 4, 64, P, S) == H.HC_EINVAL
+    assert L.hc_post(P, P, P, P, 16, 4, 64, P, S) == H.HC_EINVAL           # x_out aliases x
+    assert L.hc_mixes(P, P, 16, 4, 64, 1e-6, None, None, None, 20, 1e-6, None, None, None, S) == H.HC_EINVAL
+    assert L.hc_mixes(P, P, 16, 4, 64, 1e-6, None, P, P, 0, 1e-6, P, P, P, S) == H.HC_EINVAL  # iters 0
+    assert L.hc_mixes(P, P, 16, 4, 64, 1e-6, None, P, P, 20, 1e-6, P, None, P, S) == H.HC_EINVAL  # partial split
+    assert L.hc_split_sinkhorn(P, P, P, 16, 4, 0, 1e-6, P, P, P, S) == H.HC_EINVAL
+    assert L.hc_split_sinkhorn(P, P, P, 16, 3, 20, 1e-6, P, P, P, S) == H.HC_ENOTSUP
+    assert L.hc_split_sinkhorn(P, P, None, 16, 4, 20, 1e-6, P, P, P, S) == H.HC_EINVAL
+
+
+def test_zero_tokens_is_a_no_op(L):
+    assert L.hc_pre(P, P, 0, 4, 64, P, S) == H.HC_OK
+    assert L.hc_post(P, P + 16, P, P, 0, 4, 64, P + 32, S) == H.HC_OK
+    assert L.hc_mixes(P, P, 0, 4, 64, 1e-6, P, None, None, 20, 1e-6, None, None, None, S) == H.HC_OK
+    assert L.hc_split_sinkhorn(P, P, P, 0, 4, 20, 1e-6, P, P, P, S) == H.HC_OK
+
+
+def _args(**kw):
+    a = H.BoundaryArgs()
+    a.struct_size = ctypes.sizeof(H.BoundaryArgs)
+    a.hc, a.d, a.iters, a.n = 4, 64, 20, 16
+    a.hc_eps = a.norm_eps = a.rms_eps = 1e-6
+    a.x, a.y_out = P, P + 0x100
+    a.delta, a.post_in, a.comb_in, a.x_out = P + 0x200, P + 0x300, P + 0x400, P + 0x500
+    a.pre_in = P + 0x600
+    a.fn_packed, a.hc_base, a.hc_scale = P + 0x700, P + 0x800, P + 0x900
+    a.pre_out, a.post_out, a.comb_out = P + 0xA00, P + 0xB00, P + 0xC00
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_boundary_validation(L):
+    call = lambda a: L.hc_boundary(ctypes.byref(a), S)  # noqa: E731
+    assert L.hc_boundary(None, S) == H.HC_EINVAL
+    assert call(_args(struct_size=8)) == H.HC_EINVAL
+    assert call(_args(hc=2)) == H.HC_ENOTSUP
+    assert call(_args(x=None)) == H.HC_EINVAL
+    assert call(_args(y_out=None)) == H.HC_EINVAL
+    assert call(_args(post_in=None)) == H.HC_EINVAL           # delta given, post_in missing
+    assert call(_args(x_out=P)) == H.HC_EINVAL                # x_out aliases x
+    assert call(_args(pre_out=None)) == H.HC_EINVAL           # mixes derived, outputs missing
+    assert call(_args(fn_packed=None, pre_in=None)) == H.HC_EINVAL   # nothing to read with
+    assert call(_args(iters=0)) == H.HC_EINVAL
+    assert call(_args(gamma=MIS)) == H.HC_EINVAL
+    assert call(_args(n=0)) == H.HC_OK
+    assert call(_args(n=0, delta=None, post_in=None, comb_in=None, x_out=None)) == H.HC_OK
+    assert L.hc_boundary_workspace_bytes(4096, 4, 5120) == 0
+
+
+def test_no_device_reported_without_gpu(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert L.hc_pre(P, P, 16, 4, 64, P + 0x100, S) == H.HC_ENODEV

@@ -1,0 +1,275 @@
+"""GPU parity: every libhc entry point against the CPU oracle on the same
+seeded inputs, through the C ABI (via the ctypes binding).
+
+Bars: bf16 stream outputs bit-exact where both sides run the same fp32
+operation sequence on the same inputs (hc_post, hc_pre), else within 1 bf16
+ulp; mixes floored relative error <= 1e-4; pre/post/comb absolute error <=
+1e-5."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import hc_oracle as O
+from tests import numerics as N
+from tests.gpu_util import (DEV, assert_bf16_close, assert_bits_equal, assert_coef_close, assert_mixes_close,
+                            bf16_dev, f32_dev, host_bits, host_f32, say, write_floor)
+from transformer_hyper_connection_amd import hc as H
+from transformer_hyper_connection_amd import synth
+
+pytestmark = pytest.mark.gpu
+rng = np.random.default_rng(777)
+
+
+def rand_bits(shape, scale=1.0):
+    return synth.f64_to_bf16_bits(rng.standard_normal(shape) * scale)
+
+
+def params(d, seed=3):
+    g = np.random.default_rng(seed)
+    fn = (g.standard_normal((24, 4 * d)) * 0.02).astype(np.float32)
+    base = (g.standard_normal(24) * 0.1).astype(np.float32)
+    scale = g.uniform(0.5, 2.0, 3).astype(np.float32)
+    return fn, base, scale
+
+
+def packed(fn):
+    return H.hc_fn_pack(f32_dev(fn))
+
+
+# ------------------------------------------------------------------ packing
+@pytest.mark.parametrize("d", [64, 5120])
+def test_pack_terms_reconstruct_weight(d):
+    say(f"[pack] d={d}")
+    fn, _, _ = params(d)
+    p = packed(fn).cpu().numpy().view(np.uint16)
+    rec = p.reshape(d // 64, 4, 5, 64, 16)            # [step][k][tile][lane][16]
+    W = np.zeros((80, 4 * d), np.float64)
+    for st in range(d // 64):
+        for k in range(4):
+            for nt in range(5):
+                for g in range(4):
+                    rows = nt * 16 + np.arange(16)
+                    cols = k * d + st * 64 + g * 16 + np.arange(16)
+                    W[np.ix_(rows, cols)] = N.bits_to_f64(rec[st, k, nt, g * 16:(g + 1) * 16])
+    assert not W[72:].any()
+    hi, mid, lo = W[:24], W[24:48], W[48:72]
+    thi = torch.from_numpy(fn).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(hi, thi)                      # hi = nearest bf16 of w
+    err = np.abs(hi + mid + lo - fn.astype(np.float64))
+    assert (err <= 2.0 ** -25 * np.abs(fn) + 1e-45).all()
+
+
+# ------------------------------------------------------------------ split / Sinkhorn
+@pytest.mark.parametrize("iters", [1, 20])
+def test_split_sinkhorn_stage(iters):
+    say(f"[split] iters={iters}")
+    n = 1000
+    mixes = (rng.standard_normal((n, 24)) * 2.86).astype(np.float32)
+    _, base, scale = params(64, 11)
+    pre, post, comb = H.hc_split_sinkhorn(f32_dev(mixes), f32_dev(scale), f32_dev(base), 4, iters, 1e-6)
+    rp, rq, rc = O.hc_split_sinkhorn(mixes, scale, base, 4, iters, 1e-6)
+    assert_coef_close(host_f32(pre), rp, "pre")
+    assert_coef_close(host_f32(post), rq, "post")
+    assert_coef_close(host_f32(comb), rc, "comb")
+
+
+# ------------------------------------------------------------------ hc_post / hc_pre
+@pytest.mark.parametrize("n,d", [(37, 5120), (16, 64), (1, 128), (300, 320)])
+def test_hc_post_bit_exact(n, d):
+    say(f"[hc_post] n={n} d={d}")
+    x = rand_bits((n, 4, d)); delta = rand_bits((n, d))
+    post = rng.uniform(0, 2, (n, 4)).astype(np.float32)
+    comb = rng.dirichlet(np.ones(4), (n, 4)).transpose(0, 2, 1).astype(np.float32)
+    got = H.hc_post(bf16_dev(delta), bf16_dev(x), f32_dev(post), f32_dev(comb))
+    assert_bits_equal(host_bits(got), O.hc_post(delta, x, post, comb), "x_out")
+
+
+@pytest.mark.parametrize("n,d", [(37, 5120), (16, 64), (300, 320)])
+def test_hc_pre_bit_exact(n, d):
+    say(f"[hc_pre] n={n} d={d}")
+    x = rand_bits((n, 4, d))
+    pre = rng.uniform(0, 1, (n, 4)).astype(np.float32)
+    got = H.hc_pre(bf16_dev(x), f32_dev(pre))
+    assert_bits_equal(host_bits(got), O.hc_pre(x, pre), "y")
+
+
+def test_identities_on_gpu():
+    say("[identities]")
+    n, d = 20, 512
+    x = rand_bits((n, 4, d)); delta = rand_bits((n, d))
+    eye = np.broadcast_to(np.eye(4, dtype=np.float32), (n, 4, 4)).copy()
+    got = H.hc_post(bf16_dev(delta), bf16_dev(x), f32_dev(np.zeros((n, 4), np.float32)), f32_dev(eye))
+    assert_bits_equal(host_bits(got), x, "post=0, comb=I")
+    for j in range(4):
+        p = np.zeros((n, 4), np.float32); p[:, j] = 1
+        assert_bits_equal(host_bits(H.hc_pre(bf16_dev(x), f32_dev(p))), x[:, j], f"one-hot pre {j}")
+
+
+# ------------------------------------------------------------------ hc_mixes
+@pytest.mark.parametrize("n,d", [(32, 5120), (45, 5120), (16, 64), (3, 1024)])
+def test_hc_mixes_end_to_end(n, d):
+    say(f"[hc_mixes] n={n} d={d}")
+    x = rand_bits((n, 4, d))
+    fn, base, scale = params(d)
+    pre, post, comb, mixes = H.hc_mixes(bf16_dev(x), packed(fn), f32_dev(scale), f32_dev(base),
+                                        return_mixes=True)
+    rm = O.hc_mixes(x, fn, 1e-6)
+    assert_mixes_close(host_f32(mixes), rm)
+    rp, rq, rc = O.hc_split_sinkhorn(rm, scale, base)
+    assert_coef_close(host_f32(pre), rp, "pre")
+    assert_coef_close(host_f32(post), rq, "post")
+    assert_coef_close(host_f32(comb), rc, "comb")
+    only = H.hc_mixes(bf16_dev(x), packed(fn))
+    assert torch.equal(only, mixes)
+
+
+# ------------------------------------------------------------------ one sublayer step (n=32)
+def test_step_workload():
+    say("[step workload] n=32")
+    s = synth.step_inputs()
+    x, delta, fn, base, scale, pre_in = (s[k] for k in ("x", "delta", "hc_fn", "hc_base", "hc_scale", "pre_in"))
+    X = bf16_dev(x)
+    pre, post, comb = H.hc_mixes(X, packed(fn), f32_dev(scale), f32_dev(base))
+    y = H.hc_pre(X, f32_dev(pre_in))
+    xo = H.hc_post(bf16_dev(delta), X, post, comb)
+    rm = O.hc_mixes(x, fn, 1e-6)
+    rp, rq, rc = O.hc_split_sinkhorn(rm, scale, base)
+    assert_coef_close(host_f32(pre), rp, "pre")
+    assert_coef_close(host_f32(post), rq, "post")
+    assert_coef_close(host_f32(comb), rc, "comb")
+    assert_bits_equal(host_bits(y), O.hc_pre(x, pre_in), "y")
+    assert_bf16_close(host_bits(xo), O.hc_post(delta, x, rq, rc), "x_out", floor=write_floor(delta, x))
+
+
+# ------------------------------------------------------------------ fused boundary
+def _boundary_case(workload, t0, t1, fresh, norm, entry=False, exit_=False, d=None):
+    s = synth.boundary_inputs(workload, t0, t1) if d is None else synth.boundary_inputs(workload, t0, t1, d)
+    kw = dict(x=s["x"], pre_in=None if fresh else s["pre_in"], gamma=s["gamma"] if norm else None)
+    if not entry:
+        kw.update(delta=s["delta"], post_in=s["post_in"], comb_in=s["comb_in"])
+    if not exit_:
+        kw.update(hc_fn=s["hc_fn"], hc_base=s["hc_base"], hc_scale=s["hc_scale"])
+    ref = O.boundary(**kw)
+    dev = {k: (bf16_dev(v) if v.dtype == np.uint16 else f32_dev(v)) for k, v in kw.items()
+           if v is not None and k != "hc_fn"}
+    if "hc_fn" in kw:
+        dev["fn_packed"] = packed(kw["hc_fn"])
+    x = dev.pop("x")
+    got = H.hc_boundary(x, **dev, want_mixes=not exit_)
+    return ref, got, s
+
+
+def _check_boundary(ref, got, s, fresh, norm):
+    if ref["x_out"] is not None:
+        assert_bits_equal(host_bits(got["x_out"]), ref["x_out"], "x_out")
+    if ref["mixes"] is not None:
+        assert_mixes_close(host_f32(got["mixes"]), ref["mixes"])
+        assert_coef_close(host_f32(got["pre"]), ref["pre"], "pre")
+        assert_coef_close(host_f32(got["post"]), ref["post"], "post")
+        assert_coef_close(host_f32(got["comb"]), ref["comb"], "comb")
+    y = host_bits(got["y"])
+    if fresh:
+        # the read weights of the two sides differ by <= 1e-5: allow 1 ulp or
+        # that drift carried through the read (and 2 ulp after the RMSNorm)
+        xp = ref["x_out"] if ref["x_out"] is not None else s["x"]
+        floor = N.COEF_ABS_TOL * np.abs(N.bits_to_f64(xp)).sum(axis=-2)
+        if norm:
+            assert_bf16_close(y, ref["y"], "z (fresh)", ulps=2)
+        else:
+            assert_bf16_close(y, ref["y"], "y (fresh)", floor=floor)
+    elif norm:
+        assert_bf16_close(y, ref["y"], "z")
+    else:
+        assert_bits_equal(y, ref["y"], "y")
+
+
+@pytest.mark.parametrize("fresh", [False, True])
+@pytest.mark.parametrize("norm", [False, True])
+def test_boundary_small(fresh, norm):
+    say(f"[boundary] prefill tokens 0..40 fresh={fresh} norm={norm}")
+    ref, got, s = _boundary_case("prefill", 0, 40, fresh, norm)
+    _check_boundary(ref, got, s, fresh, norm)
+
+
+@pytest.mark.parametrize("fresh", [False, True])
+def test_boundary_entry(fresh):
+    say(f"[boundary entry] fresh={fresh}")
+    ref, got, s = _boundary_case("prefill", 100, 133, fresh, True, entry=True)
+    assert got["x_out"] is None
+    _check_boundary(ref, got, s, fresh, True)
+
+
+def test_boundary_exit():
+    say("[boundary exit]")
+    ref, got, s = _boundary_case("prefill", 7, 30, False, True, exit_=True)
+    _check_boundary(ref, got, s, False, True)
+
+
+def test_boundary_stress_outliers_small():
+    say("[boundary] stress tokens 0..24")
+    ref, got, s = _boundary_case("stress", 0, 24, False, True)
+    _check_boundary(ref, got, s, False, True)
+
+
+def test_boundary_deterministic_and_guarded():
+    say("[boundary] determinism + guard bands")
+    s = synth.boundary_inputs("prefill", 0, 33)
+    n, d = 33, 5120
+    guard = 4096
+    dev = dict(delta=bf16_dev(s["delta"]), post_in=f32_dev(s["post_in"]), comb_in=f32_dev(s["comb_in"]),
+               pre_in=f32_dev(s["pre_in"]), fn_packed=packed(s["hc_fn"]), hc_base=f32_dev(s["hc_base"]),
+               hc_scale=f32_dev(s["hc_scale"]), gamma=f32_dev(s["gamma"]))
+    X = bf16_dev(s["x"])
+    outs = []
+    for rep in range(2):
+        bufs = {
+            "x_out": torch.full((n * 4 * d + 2 * guard,), 0x7A7A, dtype=torch.int16, device=DEV),
+            "y": torch.full((n * d + 2 * guard,), 0x7A7A, dtype=torch.int16, device=DEV),
+            "pre": torch.full((n * 4 + 2 * guard,), 7.5, device=DEV),
+            "post": torch.full((n * 4 + 2 * guard,), 7.5, device=DEV),
+            "comb": torch.full((n * 16 + 2 * guard,), 7.5, device=DEV),
+            "mixes": torch.full((n * 24 + 2 * guard,), 7.5, device=DEV),
+        }
+        shapes = {"x_out": (n, 4, d), "y": (n, d), "pre": (n, 4), "post": (n, 4), "comb": (n, 4, 4),
+                  "mixes": (n, 24)}
+        views = {}
+        for k, b in bufs.items():
+            v = b[guard:-guard]
+            if b.dtype == torch.int16:
+                v = v.view(torch.bfloat16)
+            views[k] = v.view(shapes[k])
+        H.hc_boundary(X, **dev, out=views)
+        torch.cuda.synchronize()
+        for k, b in bufs.items():
+            fill = 0x7A7A if b.dtype == torch.int16 else 7.5
+            assert bool((b[:guard] == fill).all()) and bool((b[-guard:] == fill).all()), f"guard of {k} touched"
+        outs.append({k: v.clone() for k, v in views.items()})
+    for k in outs[0]:
+        assert torch.equal(outs[0][k].view(torch.int16) if outs[0][k].dtype == torch.bfloat16 else outs[0][k],
+                           outs[1][k].view(torch.int16) if outs[1][k].dtype == torch.bfloat16 else outs[1][k]), k
+
+
+# ------------------------------------------------------------------ full size, sampled
+SAMPLE_RANGES = [(0, 3), (15, 18), (2047, 2049), (4093, 4096)]
+
+
+@pytest.mark.parametrize("fresh", [False, True])
+def test_prefill_full_size_sampled(fresh):
+    say(f"[prefill n=4096] fresh={fresh}: generating inputs")
+    n = 4096
+    s = synth.boundary_inputs("prefill")
+    X = bf16_dev(s["x"])
+    dev = dict(delta=bf16_dev(s["delta"]), post_in=f32_dev(s["post_in"]), comb_in=f32_dev(s["comb_in"]),
+               pre_in=None if fresh else f32_dev(s["pre_in"]), fn_packed=packed(s["hc_fn"]),
+               hc_base=f32_dev(s["hc_base"]), hc_scale=f32_dev(s["hc_scale"]), gamma=f32_dev(s["gamma"]))
+    say("  launching")
+    got = H.hc_boundary(X, **dev, want_mixes=True)
+    torch.cuda.synchronize()
+    for a, b in SAMPLE_RANGES:
+        say(f"  oracle tokens {a}..{b}")
+        ref = O.boundary(x=s["x"][a:b], delta=s["delta"][a:b], post_in=s["post_in"][a:b],
+                         comb_in=s["comb_in"][a:b], pre_in=None if fresh else s["pre_in"][a:b],
+                         hc_fn=s["hc_fn"], hc_base=s["hc_base"], hc_scale=s["hc_scale"], gamma=s["gamma"])
+        sub = {k: (v[a:b] if v is not None else None) for k, v in got.items() if k != "workspace"}
+        _check_boundary(ref, sub, {"x": s["x"][a:b]}, fresh, True)
+    assert got["y"].shape == (n, 5120)
