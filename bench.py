@@ -133,6 +133,8 @@ def main():
     ap.add_argument("--mode", choices=["fresh", "lag"], default="fresh")
     ap.add_argument("--sets", type=int, default=4, help="rotating input/output buffer sets")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--modes", default="fresh,lag", help="read modes to time (the headline mode is always timed)")
+    ap.add_argument("--no-copy", action="store_true", help="skip the 1 GB device-copy reference")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; the glue is per-token and would shard over "
@@ -148,7 +150,8 @@ def main():
     torch.cuda.synchronize()
 
     results = {}
-    for mode in ("fresh", "lag"):
+    modes = [args.mode] + [m for m in args.modes.split(",") if m and m != args.mode]
+    for mode in modes:
         print(f"[bench] timing mode={mode}", file=sys.stderr, flush=True)
         wall, per_call = time_mode(mode, sets, params, args.steps, args.warmup)
         nbytes = algorithmic_bytes(N_TOK, mode)
@@ -159,7 +162,7 @@ def main():
             "call_ms_mean": float(np.mean(per_call)), "algorithmic_bytes": nbytes,
             "tokens_per_s": N_TOK * args.steps / wall, "gbs_at_median": nbytes / (med * 1e-3) / 1e9,
         }
-    copy_gbs = copy_bandwidth(dev)
+    copy_gbs = None if args.no_copy else copy_bandwidth(dev)
     head = results[args.mode]
     mean_ms = head["call_ms_mean"]
     achieved = head["algorithmic_bytes"] / (mean_ms * 1e-3) / 1e9
@@ -191,7 +194,7 @@ def main():
         "cpu_baseline": cpu,
         "modes": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                   for k, v in results.items()},
-        "copy_kernel_gbs": round(copy_gbs, 1),
+        "copy_kernel_gbs": None if copy_gbs is None else round(copy_gbs, 1),
     }
     print(json.dumps(line), flush=True)
 

@@ -21,7 +21,8 @@
  *   - bf16 tensors are passed as raw bit patterns (hc_bf16) and must be 16-byte
  *     aligned; float tensors must be 16-byte aligned.
  *   - n = number of tokens (batch x positions, flattened).  hc must be 4.
- *     d must be a positive multiple of 64 and at most 5120.
+ *     d must be a positive multiple of 64 and at most 32768 (at most 10240
+ *     where the read row is RMS-normalised).
  *   - stream is a hipStream_t (NULL = the null stream).  Calls enqueue work on
  *     it and return without synchronising; the current HIP device of the
  *     calling thread is used.  Calls on distinct streams may run concurrently
@@ -49,7 +50,7 @@ typedef uint16_t hc_bf16; /* raw bf16 bit pattern */
 enum hc_status {
   HC_OK = 0,
   HC_EINVAL = -1,  /* NULL or misaligned pointer, negative size, iters < 1, ... */
-  HC_ENOTSUP = -2, /* hc != 4, d not a multiple of 64 or above 5120            */
+  HC_ENOTSUP = -2, /* hc != 4, d not a multiple of 64, or d too large          */
   HC_EHIP = -3,    /* a HIP call or kernel launch failed                        */
   HC_ENODEV = -4   /* no HIP device is visible                                  */
 };
@@ -83,6 +84,20 @@ size_t hc_fn_packed_bytes(int hc, int d);
 int hc_fn_pack(const float* hc_fn, int hc, int d, void* fn_packed, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Workspace.  The entry points that derive mixes (hc_mixes, hc_boundary with
+ * fn_packed) split the feature range of each token over several workgroups
+ * and meet their partial sums in a caller-owned device workspace of
+ * hc_workspace_bytes(n, hc, d) bytes (0 for n == 0).  It must be zero-filled
+ * before its first use; every call that completes leaves it zero-filled
+ * again, so one workspace can serve any number of calls on one stream.
+ * Calls that run concurrently (different streams) need different workspaces.
+ * Word 0 is a sticky error flag: a workgroup that waited about a second for
+ * the others of its tile sets it to nonzero (this happens only if the device
+ * cannot run all workgroups of the launch at once); results are then invalid.
+ * ------------------------------------------------------------------------- */
+size_t hc_workspace_bytes(int64_t n, int hc, int d);
+
+/* ---------------------------------------------------------------------------
  * hc_mixes -- "Source layer, pairs pooled", Block.hc_mixes.
  *   r[t]        = 1 / sqrt(mean_c x[t,c]^2 + norm_eps), c over the flattened
  *                 hc*d row (index j*d + i)
@@ -93,11 +108,12 @@ int hc_fn_pack(const float* hc_fn, int hc, int d, void* fn_packed, void* stream)
  * hc_split_sinkhorn also runs (with hc_scale, hc_base, iters, hc_eps) and
  * writes them, as Block.hc_mixes returns them; otherwise hc_scale/hc_base/
  * iters/hc_eps are ignored.  At least one of mixes or (pre, post, comb) must
- * be given.
+ * be given.  workspace: see hc_workspace_bytes.
  * ------------------------------------------------------------------------- */
 int hc_mixes(const hc_bf16* x, const void* fn_packed, int64_t n, int hc, int d, float norm_eps,
              float* mixes, const float* hc_scale, const float* hc_base, int iters, float hc_eps,
-             float* pre, float* post, float* comb, void* stream);
+             float* pre, float* post, float* comb, void* workspace, size_t workspace_bytes,
+             void* stream);
 
 /* ---------------------------------------------------------------------------
  * hc_split_sinkhorn -- "Reading weights": reading-weight equation and the
@@ -153,8 +169,8 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
  * (pre, post, comb) of this boundary for the next one.  Use delta == NULL at a
  * block entry and fn_packed == NULL at the stack exit.
  * x_out must not overlap x; y_out must not overlap x, x_out or delta.
- * workspace/workspace_bytes: scratch for the small-n path, at least
- * hc_boundary_workspace_bytes(n, hc, d) bytes (may be NULL when that is 0).
+ * workspace/workspace_bytes: required when fn_packed != NULL, see
+ * hc_workspace_bytes (hc_boundary_workspace_bytes returns the same size).
  * ------------------------------------------------------------------------- */
 typedef struct hc_boundary_args {
   uint32_t struct_size; /* = sizeof(hc_boundary_args) */
@@ -182,7 +198,7 @@ typedef struct hc_boundary_args {
 
 int hc_boundary(const hc_boundary_args* args, void* stream);
 
-/* Scratch bytes hc_boundary needs for n tokens (0 = none). */
+/* Workspace bytes hc_boundary needs for n tokens (= hc_workspace_bytes). */
 size_t hc_boundary_workspace_bytes(int64_t n, int hc, int d);
 
 #ifdef __cplusplus

@@ -70,19 +70,28 @@ def test_strerror_and_version(L):
         assert L.hc_strerror(code)
 
 
-def test_packed_bytes(L):
-    assert L.hc_fn_packed_bytes(4, 5120) == 72 * 4 * 5120 * 2 * 80 // 72  # 80 rows incl. 8 zero rows
+def test_packed_and_workspace_bytes(L):
+    assert L.hc_fn_packed_bytes(4, 5120) == 80 * 4 * 5120 * 2  # 72 split rows + 8 zero rows, bf16
     assert L.hc_fn_packed_bytes(3, 5120) == 0
     assert L.hc_fn_packed_bytes(4, 100) == 0
-    assert L.hc_fn_packed_bytes(4, 5184) == 0
+    assert L.hc_fn_packed_bytes(4, 5184) == 80 * 4 * 5184 * 2
+    assert L.hc_fn_packed_bytes(4, 32832) == 0
+    assert L.hc_workspace_bytes(0, 4, 5120) == 0
+    assert L.hc_workspace_bytes(4096, 3, 5120) == 0
+    w = L.hc_workspace_bytes(4096, 4, 5120)
+    # 64 tiles of 64 tokens x 16 slices x 28-float partial records, plus counters
+    assert 64 * 16 * 64 * 28 * 4 <= w <= 64 * 16 * 64 * 28 * 4 + 4096
+    assert L.hc_boundary_workspace_bytes(4096, 4, 5120) == w
+    assert L.hc_workspace_bytes(4097, 4, 5120) > w
 
 
 @pytest.mark.parametrize("hc,d,code", [(3, 5120, H.HC_ENOTSUP), (8, 5120, H.HC_ENOTSUP), (4, 100, H.HC_ENOTSUP),
-                                       (4, 0, H.HC_ENOTSUP), (4, 5184, H.HC_ENOTSUP)])
+                                       (4, 0, H.HC_ENOTSUP), (4, 5152, H.HC_ENOTSUP),
+                                       (4, 32832, H.HC_ENOTSUP)])
 def test_unsupported_shapes(L, hc, d, code):
     assert L.hc_pre(P, P, 16, hc, d, P, S) == code
     assert L.hc_post(P, P, P, P, 16, hc, d, P, S) == code
-    assert L.hc_mixes(P, P, 16, hc, d, 1e-6, P, None, None, 20, 1e-6, None, None, None, S) == code
+    assert L.hc_mixes(P, P, 16, hc, d, 1e-6, P, None, None, 20, 1e-6, None, None, None, P, 1 << 30, S) == code
     assert L.hc_fn_pack(P, hc, d, P, S) == code
     assert L.hc_last_error()
 
@@ -94,9 +103,10 @@ def test_null_misaligned_negative(L):
     assert b"aligned" in L.hc_last_error()
     assert L.hc_pre(P, P, -1, 4, 64, P, S) == H.HC_EINVAL
     assert L.hc_post(P, P, P, P, 16, 4, 64, P, S) == H.HC_EINVAL           # x_out aliases x
-    assert L.hc_mixes(P, P, 16, 4, 64, 1e-6, None, None, None, 20, 1e-6, None, None, None, S) == H.HC_EINVAL
-    assert L.hc_mixes(P, P, 16, 4, 64, 1e-6, None, P, P, 0, 1e-6, P, P, P, S) == H.HC_EINVAL  # iters 0
-    assert L.hc_mixes(P, P, 16, 4, 64, 1e-6, None, P, P, 20, 1e-6, P, None, P, S) == H.HC_EINVAL  # partial split
+    W = (P, 1 << 30)
+    assert L.hc_mixes(P, P, 16, 4, 64, 1e-6, None, None, None, 20, 1e-6, None, None, None, *W, S) == H.HC_EINVAL
+    assert L.hc_mixes(P, P, 16, 4, 64, 1e-6, None, P, P, 0, 1e-6, P, P, P, *W, S) == H.HC_EINVAL  # iters 0
+    assert L.hc_mixes(P, P, 16, 4, 64, 1e-6, None, P, P, 20, 1e-6, P, None, P, *W, S) == H.HC_EINVAL  # partial split
     assert L.hc_split_sinkhorn(P, P, P, 16, 4, 0, 1e-6, P, P, P, S) == H.HC_EINVAL
     assert L.hc_split_sinkhorn(P, P, P, 16, 3, 20, 1e-6, P, P, P, S) == H.HC_ENOTSUP
     assert L.hc_split_sinkhorn(P, P, None, 16, 4, 20, 1e-6, P, P, P, S) == H.HC_EINVAL
@@ -105,7 +115,7 @@ def test_null_misaligned_negative(L):
 def test_zero_tokens_is_a_no_op(L):
     assert L.hc_pre(P, P, 0, 4, 64, P, S) == H.HC_OK
     assert L.hc_post(P, P + 16, P, P, 0, 4, 64, P + 32, S) == H.HC_OK
-    assert L.hc_mixes(P, P, 0, 4, 64, 1e-6, P, None, None, 20, 1e-6, None, None, None, S) == H.HC_OK
+    assert L.hc_mixes(P, P, 0, 4, 64, 1e-6, P, None, None, 20, 1e-6, None, None, None, None, 0, S) == H.HC_OK
     assert L.hc_split_sinkhorn(P, P, P, 0, 4, 20, 1e-6, P, P, P, S) == H.HC_OK
 
 
@@ -139,7 +149,7 @@ def test_boundary_validation(L):
     assert call(_args(gamma=MIS)) == H.HC_EINVAL
     assert call(_args(n=0)) == H.HC_OK
     assert call(_args(n=0, delta=None, post_in=None, comb_in=None, x_out=None)) == H.HC_OK
-    assert L.hc_boundary_workspace_bytes(4096, 4, 5120) == 0
+    assert call(_args(d=10304, gamma=P + 0xD00)) == H.HC_ENOTSUP   # RMSNorm row too long
 
 
 def test_no_device_reported_without_gpu(L):

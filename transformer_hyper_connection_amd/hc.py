@@ -49,7 +49,9 @@ SIGNATURES = {
     "hc_fn_packed_bytes": (c_size_t, [c_int, c_int]),
     "hc_fn_pack": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p]),
     "hc_mixes": (c_int, [c_void_p, c_void_p, c_int64, c_int, c_int, c_float, c_void_p, c_void_p,
-                         c_void_p, c_int, c_float, c_void_p, c_void_p, c_void_p, c_void_p]),
+                         c_void_p, c_int, c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                         c_void_p]),
+    "hc_workspace_bytes": (c_size_t, [c_int64, c_int, c_int]),
     "hc_split_sinkhorn": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int, c_int, c_float,
                                   c_void_p, c_void_p, c_void_p, c_void_p]),
     "hc_pre": (c_int, [c_void_p, c_void_p, c_int64, c_int, c_int, c_void_p, c_void_p]),
@@ -89,6 +91,25 @@ def _ptr(t):
 
 def _stream(dev) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
+
+
+_workspaces: dict = {}
+
+
+def workspace(n: int, hc: int, d: int, device) -> torch.Tensor | None:
+    """A zero-filled device workspace of hc_workspace_bytes(n, hc, d) bytes,
+    cached per (device, stream): libhc leaves it zero-filled after every call
+    that completes, so calls on one stream can share it."""
+    nbytes = lib().hc_workspace_bytes(n, hc, d)
+    if nbytes == 0:
+        return None
+    dev = torch.device(device)
+    key = (dev, torch.cuda.current_stream(dev).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
 
 
 def _need(t, name, dtype, device=None, shape=None):
@@ -168,9 +189,10 @@ def hc_mixes(x, fn_packed, hc_scale=None, hc_base=None, *, norm_eps: float = 1e-
         pre = torch.empty(*lead, hc, dtype=torch.float32, device=dev)
         post = torch.empty_like(pre)
         comb = torch.empty(*lead, hc, hc, dtype=torch.float32, device=dev)
+    ws = workspace(n, hc, d, dev)
     _check(lib().hc_mixes(x.data_ptr(), fn_packed.data_ptr(), n, hc, d, norm_eps, _ptr(mixes),
                           _ptr(hc_scale), _ptr(hc_base), sinkhorn_iters, hc_eps, _ptr(pre), _ptr(post),
-                          _ptr(comb), _stream(dev)), "hc_mixes")
+                          _ptr(comb), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)), "hc_mixes")
     if not split:
         return mixes
     return (pre, post, comb, mixes) if return_mixes else (pre, post, comb)
@@ -209,7 +231,7 @@ def hc_boundary(x, *, delta=None, post_in=None, comb_in=None, pre_in=None, fn_pa
     """One fused sublayer boundary (see include/hc.h).  Returns a dict with
     x_out (None at a block entry), y, and pre/post/comb (+ mixes) unless
     fn_packed is None.  ``out`` may hold preallocated outputs under the same
-    keys; they are used as given."""
+    keys (and a zero-filled "workspace"); they are used as given."""
     dev = x.device
     _need(x, "x", torch.bfloat16)
     lead, n, hc, d = _streams_shape(x)
@@ -251,11 +273,11 @@ def hc_boundary(x, *, delta=None, post_in=None, comb_in=None, pre_in=None, fn_pa
     a.gamma, a.x_out, a.y_out = _ptr(gamma), _ptr(o.get("x_out")), o["y"].data_ptr()
     a.mixes_out, a.pre_out = _ptr(o.get("mixes")), _ptr(o.get("pre"))
     a.post_out, a.comb_out = _ptr(o.get("post")), _ptr(o.get("comb"))
-    ws_bytes = lib().hc_boundary_workspace_bytes(n, hc, d)
-    if ws_bytes:
+    if fn_packed is not None:
         ws = o.get("workspace")
-        if ws is None or ws.numel() < ws_bytes:
-            ws = o["workspace"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-        a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+        if ws is None:
+            ws = workspace(n, hc, d, dev)
+        if ws is not None:
+            a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
     _check(lib().hc_boundary(ctypes.byref(a), _stream(dev)), "hc_boundary")
     return o
