@@ -67,26 +67,34 @@ def make_sets(s, dev, n_sets):
 
 
 def time_mode(mode, sets, params, steps, warmup):
+    """Times `steps` boundary calls over the rotating buffer sets.  Returns the
+    wall time, the per-call device times (events on the launch stream around
+    each call) and the host time spent enqueueing the calls."""
     stream = torch.cuda.current_stream()
-
-    def step(i):
-        ins, outs = sets[i % len(sets)]
-        T.hc_boundary(ins["x"], delta=ins["delta"], post_in=ins["post_in"], comb_in=ins["comb_in"],
-                      pre_in=ins["pre_in"] if mode == "lag" else None, out=outs, **params)
-
+    calls = [T.BoundaryCall(ins["x"], delta=ins["delta"], post_in=ins["post_in"], comb_in=ins["comb_in"],
+                            pre_in=ins["pre_in"] if mode == "lag" else None, out=outs, **params)
+             for ins, outs in sets]
+    sid = stream.cuda_stream
     for i in range(warmup):
-        step(i)
+        calls[i % len(calls)].run(sid)
+    torch.cuda.synchronize()
+    # untimed-by-events pass: how long the host takes to enqueue a call
+    t0 = time.perf_counter()
+    for i in range(steps):
+        calls[i % len(calls)].run(sid)
+    host = time.perf_counter() - t0
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record(stream)
-        step(warmup + i)
+        calls[(warmup + i) % len(calls)].run(sid)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_call_ms = [a.elapsed_time(b) for a, b in ev]
-    return wall, per_call_ms
+    return wall, per_call_ms, host / steps * 1e6
 
 
 def copy_bandwidth(dev, nbytes=1 << 30, reps=10):
@@ -153,7 +161,7 @@ def main():
     modes = [args.mode] + [m for m in args.modes.split(",") if m and m != args.mode]
     for mode in modes:
         print(f"[bench] timing mode={mode}", file=sys.stderr, flush=True)
-        wall, per_call = time_mode(mode, sets, params, args.steps, args.warmup)
+        wall, per_call, host_us = time_mode(mode, sets, params, args.steps, args.warmup)
         nbytes = algorithmic_bytes(N_TOK, mode)
         med = statistics.median(per_call)
         results[mode] = {
@@ -161,6 +169,7 @@ def main():
             "call_ms_p10": float(np.percentile(per_call, 10)), "call_ms_p90": float(np.percentile(per_call, 90)),
             "call_ms_mean": float(np.mean(per_call)), "algorithmic_bytes": nbytes,
             "tokens_per_s": N_TOK * args.steps / wall, "gbs_at_median": nbytes / (med * 1e-3) / 1e9,
+            "host_enqueue_us_per_call": host_us,
         }
     copy_gbs = None if args.no_copy else copy_bandwidth(dev)
     head = results[args.mode]

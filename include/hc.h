@@ -85,15 +85,12 @@ int hc_fn_pack(const float* hc_fn, int hc, int d, void* fn_packed, void* stream)
 
 /* ---------------------------------------------------------------------------
  * Workspace.  The entry points that derive mixes (hc_mixes, hc_boundary with
- * fn_packed) split the feature range of each token over several workgroups
- * and meet their partial sums in a caller-owned device workspace of
- * hc_workspace_bytes(n, hc, d) bytes (0 for n == 0).  It must be zero-filled
- * before its first use; every call that completes leaves it zero-filled
- * again, so one workspace can serve any number of calls on one stream.
- * Calls that run concurrently (different streams) need different workspaces.
- * Word 0 is a sticky error flag: a workgroup that waited about a second for
- * the others of its tile sets it to nonzero (this happens only if the device
- * cannot run all workgroups of the launch at once); results are then invalid.
+ * fn_packed) split the feature range of each token over several workgroups,
+ * which leave per-token partial sums in a caller-owned device workspace of
+ * hc_workspace_bytes(n, hc, d) bytes (0 for n == 0), 16-byte aligned; a
+ * second kernel of the same call reads them.  Its contents before a call do
+ * not matter.  Calls that may run concurrently (different streams) need
+ * different workspaces; calls on one stream can share one.
  * ------------------------------------------------------------------------- */
 size_t hc_workspace_bytes(int64_t n, int hc, int d);
 
@@ -163,7 +160,11 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
  *   y               = hc_pre(X', pre_in)                        (pre_in == NULL: the pre just derived)
  *   y_out           = gamma ? RMSNorm_gamma(y, rms_eps) : y
  * RMSNorm ("Final RMSNorm"): y_out[t,i] = bf16(gamma[i] * (y[t,i] * r)),
- * r = 1/sqrt(mean_i y[t,i]^2 + rms_eps), on the bf16 y.
+ * r = 1/sqrt(mean_i y[t,i]^2 + rms_eps), on the bf16 y.  With pre_in == NULL
+ * the mean square is instead formed as p^T G p from the 4x4 Gram matrix G of
+ * the X' streams, i.e. of the y before its bf16 rounding, so that the row
+ * need not wait for its own mean square; the two differ by a relative 2^-8 at
+ * most (from the rounding of y), which moves z by at most half a bf16 ulp.
  * With pre_in given the call follows the pages' data flow: the streams are
  * read with the reading mix of the previous boundary and the call returns the
  * (pre, post, comb) of this boundary for the next one.  Use delta == NULL at a

@@ -79,8 +79,8 @@ def test_packed_and_workspace_bytes(L):
     assert L.hc_workspace_bytes(0, 4, 5120) == 0
     assert L.hc_workspace_bytes(4096, 3, 5120) == 0
     w = L.hc_workspace_bytes(4096, 4, 5120)
-    # 64 tiles of 64 tokens x 16 slices x 28-float partial records, plus counters
-    assert 64 * 16 * 64 * 28 * 4 <= w <= 64 * 16 * 64 * 28 * 4 + 4096
+    # 64 tiles of 64 tokens x 4 slices x 36-float records, plus counters
+    assert 64 * 4 * 64 * 36 * 4 <= w <= 64 * 4 * 64 * 36 * 4 + 4096
     assert L.hc_boundary_workspace_bytes(4096, 4, 5120) == w
     assert L.hc_workspace_bytes(4097, 4, 5120) > w
 

@@ -253,6 +253,29 @@ def test_boundary_deterministic_and_guarded():
                            outs[1][k].view(torch.int16) if outs[1][k].dtype == torch.bfloat16 else outs[1][k]), k
 
 
+def test_prepared_call_matches_and_repeats():
+    """BoundaryCall (checked once, re-enqueued) gives the bits of hc_boundary,
+    call after call on the same buffers and workspace."""
+    say("[boundary] prepared call, fresh read, n=300")
+    s = synth.boundary_inputs("prefill", 0, 300)
+    dev = dict(delta=bf16_dev(s["delta"]), post_in=f32_dev(s["post_in"]), comb_in=f32_dev(s["comb_in"]),
+               fn_packed=packed(s["hc_fn"]), hc_base=f32_dev(s["hc_base"]), hc_scale=f32_dev(s["hc_scale"]),
+               gamma=f32_dev(s["gamma"]))
+    X = bf16_dev(s["x"])
+    ref = H.hc_boundary(X, **dev, want_mixes=True)
+    call = H.BoundaryCall(X, **dev, want_mixes=True)
+    for rep in range(3):
+        for k in ("x_out", "y", "pre", "post", "comb", "mixes"):
+            call.outputs[k].fill_(7)
+        call.run()
+        torch.cuda.synchronize()
+        for k in ("x_out", "y", "pre", "post", "comb", "mixes"):
+            a, b = call.outputs[k], ref[k]
+            if a.dtype == torch.bfloat16:
+                a, b = a.view(torch.int16), b.view(torch.int16)
+            assert torch.equal(a, b), f"{k} differs on call {rep}"
+
+
 # ------------------------------------------------------------------ full size, sampled
 SAMPLE_RANGES = [(0, 3), (15, 18), (2047, 2049), (4093, 4096)]
 
@@ -277,3 +300,28 @@ def test_prefill_full_size_sampled(fresh):
         sub = {k: (v[a:b] if v is not None else None) for k, v in got.items() if k != "workspace"}
         _check_boundary(ref, sub, {"x": s["x"][a:b], "gamma": s["gamma"]}, fresh, True)
     assert got["y"].shape == (n, 5120)
+
+
+STRESS_RANGES = [(0, 2), (8191, 8193), (20001, 20003), (32766, 32768)]
+
+
+def test_stress_full_size_sampled():
+    """The bandwidth-stress boundary: B=4 T=8192 (32768 tokens, X = 1.34 GB),
+    heavy-tailed streams (1% of features x30), fresh read with the RMSNorm.
+    More tiles than workgroups per launch; sampled tokens across the batch."""
+    say("[stress n=32768] generating inputs")
+    s = synth.boundary_inputs("stress")
+    X = bf16_dev(s["x"])
+    dev = dict(delta=bf16_dev(s["delta"]), post_in=f32_dev(s["post_in"]), comb_in=f32_dev(s["comb_in"]),
+               fn_packed=packed(s["hc_fn"]), hc_base=f32_dev(s["hc_base"]), hc_scale=f32_dev(s["hc_scale"]),
+               gamma=f32_dev(s["gamma"]))
+    say("  launching")
+    got = H.hc_boundary(X, **dev, want_mixes=True)
+    torch.cuda.synchronize()
+    for a, b in STRESS_RANGES:
+        say(f"  oracle tokens {a}..{b}")
+        ref = O.boundary(x=s["x"][a:b], delta=s["delta"][a:b], post_in=s["post_in"][a:b],
+                         comb_in=s["comb_in"][a:b], pre_in=None, hc_fn=s["hc_fn"], hc_base=s["hc_base"],
+                         hc_scale=s["hc_scale"], gamma=s["gamma"])
+        sub = {k: (v[a:b] if v is not None else None) for k, v in got.items() if k != "workspace"}
+        _check_boundary(ref, sub, {"x": s["x"][a:b], "gamma": s["gamma"]}, True, True)

@@ -4,8 +4,8 @@ The compute lives in libhc.so (hand-written HIP kernels behind the C ABI of
 include/hc.h); ``hc`` is its Python binding and ``synth`` the seeded
 synthetic-input generator of the benchmark workloads.
 """
-from .hc import (HCError, hc_boundary, hc_fn_pack, hc_mixes, hc_post, hc_pre,  # noqa: F401
+from .hc import (BoundaryCall, HCError, hc_boundary, hc_fn_pack, hc_mixes, hc_post, hc_pre,  # noqa: F401
                  hc_split_sinkhorn, lib)
 
-__all__ = ["HCError", "hc_boundary", "hc_fn_pack", "hc_mixes", "hc_post", "hc_pre",
+__all__ = ["BoundaryCall", "HCError", "hc_boundary", "hc_fn_pack", "hc_mixes", "hc_post", "hc_pre",
            "hc_split_sinkhorn", "lib"]

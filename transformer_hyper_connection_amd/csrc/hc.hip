@@ -11,13 +11,13 @@
 // sequence of separately rounded fp32 products and sums, bit for bit).
 //
 // Kernels
-//   split_kernel_tiles<POST, PRE, NORM>  everything that derives mixes (hc_mixes,
-//       block entry, sublayer boundary): 64-token tiles x feature slices, the
-//       24-wide projection on the matrix cores with the weight tiles shared
-//       through LDS, per-slice partials met in a workspace (see below).
-//   row_kernel<POST, PRE, NORM, TPW>     streams only (hc_post, hc_pre, stack
-//       exit, the read of a boundary that uses the pre it derives): whole token
-//       rows per wave, 1 KB per load or store.
+//   tile_kernel<POST, RM, NORM>  everything that derives mixes (hc_mixes, block
+//       entry, sublayer boundary): 64-token tiles x feature slices, about one
+//       workgroup per compute unit; the 24-wide projection on the matrix cores
+//       with the weight tiles shared through LDS; the slices of a tile meet once
+//       in a workspace, then each writes its part of the read row.
+//   row_kernel<POST, PRE, NORM, TPW>  streams only (hc_post, hc_pre, the stack
+//       exit): whole token rows per wave, 1 KB per load or store.
 //   split_kernel    hc_split_sinkhorn, one token per lane.
 //   pack_kernel     fp32 projection weight -> bf16 hi/mid/lo terms in tile order.
 #include <hip/hip_runtime.h>
@@ -35,7 +35,6 @@ constexpr int kHC = 4;
 constexpr int kMix = (2 + kHC) * kHC;  // 24 mix numbers
 constexpr int kSplitRows = 3 * kMix;   // 72 = hi | mid | lo rows of the packed weight
 constexpr int kNT = 5;                 // 16-column matrix tiles covering 72 (+8 zero) rows
-constexpr int kTM = 16;                // tokens per workgroup tile
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kFPL = 8;                // features per lane per matrix-core step
@@ -200,8 +199,7 @@ __global__ void __launch_bounds__(256) pack_kernel(const float* __restrict__ fn,
 }
 
 // ================================================================ row kernel
-// Streams without the projection: hc_post, hc_pre, the stack exit and the
-// read of a boundary that uses the pre it derives.  One workgroup = 8 waves x
+// Streams without the projection: hc_post, hc_pre and the stack exit.  One workgroup = 8 waves x
 // TPW tokens; a wave owns whole token rows, a lane 8 consecutive features of
 // a 512-feature chunk, so every load and store moves 1 KB of one row.  The
 // per-token coefficients are wave-uniform (scalar registers).  With NORM the
@@ -385,56 +383,61 @@ __global__ void __launch_bounds__(kThreads) row_kernel(const RowArgs a) {
   }
 }
 
-// ============================================================== split kernel
-// Everything that derives mixes.  The tokens form tiles of 64 (4 row blocks of
-// 16); the features of each stream are cut into S slices of F = d/S (a
-// multiple of 64); one workgroup handles one (tile, slice) pair and loops over
-// the tiles of its slice (grid <= number of CUs, all resident).  Waves 2r and
-// 2r+1 share row block r: in the stream phase each owns 8 of its tokens (one
-// per lane group of 8 lanes, 8 features per lane, 128 B per token and
-// instruction); in the matrix phase each takes one of the chunk's two 32-
-// feature steps.  Per 64-feature chunk:
-//   stream phase: X' (and y) for the wave's 8 tokens; X' is stored and also
-//     written into the row block's LDS tile in the matrix-core A layout;
-//   barrier;  the weight tiles of the next chunk (staged through registers)
-//     go into the other half of a double-buffered LDS area;
-//   matrix phase: 4 streams x 5 tiles of 16x16x32 bf16 MFMA, A and B from LDS.
-// After the slice: per-token partials (24 dots, sum x'^2, sum y^2) go to the
-// workspace; the S workgroups of a tile meet at a counter; the owner of each
-// token reduces its partials in slice order, derives the mixes and runs the
-// split/Sinkhorn; every workgroup reads the row sums of squares it needs and
-// rescales its slice of the read row, parked in LDS (NORM).
+// ====================================================== boundary: two kernels
+// Everything that derives mixes (hc_mixes, block entry, sublayer boundary)
+// runs as two ordinary launches; the boundary between them is the only
+// device-wide synchronisation.
+//
+// stream_kernel: tokens form tiles of 64 (4 row blocks of 16); the features
+// of each stream are cut into S slices of F = d/S (a multiple of 64), S chosen
+// so that tiles*S is about one workgroup per compute unit.  One workgroup
+// handles one (tile, slice) pair.  Per 64-feature chunk, with waves 2r and
+// 2r+1 sharing row block r:
+//   stream phase: each wave owns 8 tokens, one per group of 8 lanes, with 8
+//     features per lane (128 B per token and instruction).  X' = hc_post(...)
+//     is stored and written into the row block's LDS tile in the matrix-core A
+//     layout.  With a given pre the read row y is formed and stored as well.
+//     The per-token sums the finish needs accumulate in registers: sum x'^2,
+//     and for the RMSNorm either sum y^2 (given pre) or the 4x4 Gram matrix of
+//     the X' streams (fresh pre: sum y^2 = p^T G p once p is known).
+//   barrier; the next chunk's weight tiles (staged through registers) go into
+//     the other half of a double-buffered LDS area.
+//   matrix phase: each wave of the pair takes one of the chunk's two 32-
+//     feature steps: 4 streams x 5 tiles of 16x16x32 bf16 MFMA, A and B from LDS.
+// At the end each workgroup writes one record per token of its slice to the
+// workspace: 24 projection dots, sum x'^2, the norm sums.
+//
+// finish_kernel: one workgroup per (tile, read slice).  It sums the tile's
+// records over the S slices in slice order (so every workgroup derives
+// bit-identical coefficients), derives the mixes, pre/post and the Sinkhorn
+// comb with 4 lanes per token (one comb row each; the owner of a token writes
+// them), and then writes its part of the read row: from the X' of the stream
+// kernel read back with the derived pre (fresh pre), or by rescaling the y it
+// stored (given pre with the RMSNorm).
 constexpr int kTT = 64;                  // tokens per tile
 constexpr int kCF = 64;                  // features per chunk
-constexpr int kMaxSliceY = 320;          // features per slice when the read row is parked in LDS
-constexpr int kPartials = kMix + 2;      // per token per slice: 24 dots, sum x'^2, sum y^2
-constexpr int kRec = 28;                 // partial record, padded to 7 x 16 B
-constexpr size_t kWeightStageBytes = 2 * 2 * 4 * 5 * 64 * 16;   // LDS weight staging, reused by the finish
-constexpr unsigned kSpinLimit = 1u << 23;
+constexpr int kGram = kHC * (kHC + 1) / 2;   // 10 distinct Gram entries
+constexpr int kRec = 36;                 // record: 24 dots, sum x'^2, then sum y^2 or the Gram entries; 9 x 16 B
+constexpr int kMaxSlices = 32;           // S is the smallest divisor of d/64 reaching min(256/tiles, this)
+constexpr int kFinThreads = 512;
 
-struct SplitArgs {
+enum ReadMode { kNoRead = 0, kGivenPre = 1, kFreshPre = 2 };
+
+template <int RM, bool NORM>
+constexpr int rec_used() { return kMix + 1 + (NORM ? (RM == kFreshPre ? kGram : 1) : 0); }
+
+struct StreamArgs {
   const hc_bf16* x;
   const hc_bf16* delta;
   const float* post_in;
   const float* comb_in;
   const float* pre_in;
   const u32x4* fn;
-  const float* hc_base;
-  const float* hc_scale;
-  const float* gamma;
   hc_bf16* x_out;
   hc_bf16* y_out;
-  float* mixes_out;
-  float* pre_out;
-  float* post_out;
-  float* comb_out;
-  unsigned* ws_err;   // sticky error word
-  unsigned* ws_cnt;   // [tiles] arrivals
-  unsigned* ws_done;  // [tiles] departures
-  float* ws_part;     // [tiles][S][kTT][kRec]
+  float* rec;         // [tiles][S][kTT][kRec]
   int64_t n;
-  int d, S, F, tiles, iters;
-  float hc_eps, norm_eps, rms_eps;
+  int d, S, F, tiles;
 };
 
 __device__ __forceinline__ void lds_barrier() {
@@ -443,44 +446,26 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Workgroups of a tile meet through the workspace using device-coherent
-// accesses only (buffer loads/stores with the system-coherence cache policy,
-// relaxed device-scope atomics for the counters), so no cache-wide write-back
-// or invalidation -- which a device-scope fence issues on this multi-L2
-// part -- is needed.  A writer waits for its stores to complete before its
-// workgroup raises the arrival counter; a reader issues its loads only after
-// the counter has been seen complete.  The buffer descriptor also bounds
-// every access to the workspace.
-constexpr int kCoherent = 16;            // cache-policy bit: coherent at device scope
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(float* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ void wait_vm_stores() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): every vector memory operation of this wave completed
-}
+// a store that the finish kernel reads back soon (kept cacheable)
+__device__ __forceinline__ void st_keep(u32x4* p, u32x4 v) { *p = v; }
 
-template <bool POST, bool PRE, bool NORM>
-__global__ void __launch_bounds__(kThreads, 1) split_kernel_tiles(const SplitArgs a) {
-  static_assert(!NORM || PRE, "RMSNorm needs the read row");
+template <bool POST, int RM, bool NORM>
+__global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a) {
+  static_assert(!NORM || RM != kNoRead, "RMSNorm needs the read row");
   __shared__ u32x4 w_lds[2][2][kHC][kNT][64];          // weight tiles, double buffered (80 KB)
-  static_assert(sizeof(w_lds) == kWeightStageBytes, "LDS staging size");
   __shared__ u32x4 a_lds[4][2][kHC][64];               // X' in A layout per row block (32 KB)
-  __shared__ u32x4 y_lds[NORM ? kTT : 1][kMaxSliceY / 8];  // read row of the slice (40 KB)
-  __shared__ float s_ry[kTT];
-  __shared__ float g_lds[NORM ? kMaxSliceY : 1];        // gamma of the slice
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rb = wave >> 1, hw = wave & 1;   // row block, half (stream phase) / step (matrix phase)
   const int d = a.d, S = a.S, F = a.F;
   const int nch = F / kCF;
-  const int groups = gridDim.x / S;
-  // XCD-aware: consecutive blocks land on different XCDs; the S blocks of a
-  // tile group are taken 8 apart so that they share one XCD (and its L2)
-  const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
-  const int lin = (gridDim.x & 7) ? blockIdx.x : xcd * (gridDim.x >> 3) + jx;
-  const int slice = lin % S;
-  const int group = lin / S;
+  // XCD-aware: consecutive blocks land on different XCDs.  Renumbered so that
+  // each XCD holds a contiguous run, then taken slice-major: the workgroups of
+  // an XCD share few slices, and so few weight columns in their L2.
+  const int lin = (gridDim.x & 7) ? blockIdx.x : (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int slice = lin / a.tiles;
+  const int tile = lin % a.tiles;
   const int fs = slice * F;                     // first feature of the slice (per stream)
 
   const int hl = lane >> 3;                     // token within the wave's 8
@@ -488,261 +473,379 @@ __global__ void __launch_bounds__(kThreads, 1) split_kernel_tiles(const SplitArg
   const int m = rb * 16 + hw * 8 + hl;          // token within the tile
   const int a_st = fl >> 5, a_g = (fl >> 3) & 3;
   const int a_lane = a_g * 16 + hw * 8 + hl;    // A-layout lane of this lane's 8 features
-  if constexpr (NORM) {
-    for (int i = threadIdx.x; i < F; i += kThreads) g_lds[i] = a.gamma[fs + i];
+  constexpr int kUsed = rec_used<RM, NORM>();
+  constexpr int kQuads = (kUsed + 3) / 4;
+
+  const int64_t t0 = (int64_t)tile * kTT;
+  const bool tv = t0 + m < a.n;
+  const unsigned lt = tv ? (unsigned)m : 0u;   // tokens past n read the tile's first and never store
+  const hc_bf16* xb = a.x + t0 * kHC * d;
+  const hc_bf16* db = POST ? a.delta + t0 * d : a.x;
+  hc_bf16* xob = POST ? a.x_out + t0 * kHC * d : nullptr;
+  hc_bf16* yb = RM == kGivenPre ? a.y_out + t0 * d : nullptr;
+
+  float cpost[kHC], ccomb[kHC * kHC], cpre[kHC];
+#pragma unroll
+  for (int j = 0; j < kHC; ++j) {
+    cpost[j] = POST ? a.post_in[(t0 + lt) * kHC + j] : 0.f;
+    cpre[j] = RM == kGivenPre ? a.pre_in[(t0 + lt) * kHC + j] : 0.f;
   }
-  const unsigned tile_bytes = (unsigned)S * kTT * kRec * 4;   // one tile's partials
+#pragma unroll
+  for (int j = 0; j < kHC * kHC; ++j) ccomb[j] = POST ? a.comb_in[(t0 + lt) * kHC * kHC + j] : 0.f;
 
-  for (int tile = group; tile < a.tiles; tile += groups) {
-    const int64_t t0 = (int64_t)tile * kTT;
-    const bool tv = t0 + m < a.n;
-    const unsigned lt = tv ? (unsigned)m : 0u;   // tokens past n read the tile's first and never store
-    const hc_bf16* xb = a.x + t0 * kHC * d;
-    const hc_bf16* db = POST ? a.delta + t0 * d : a.x;
-    hc_bf16* xob = POST ? a.x_out + t0 * kHC * d : nullptr;
-    hc_bf16* yb = PRE ? a.y_out + t0 * d : nullptr;
+  u32x4 cur[kHC + 1];
+  u32x4 wst[kNT];  // this wave's share (5 of 40 blocks) of the next chunk's weight tiles
+  f32x4 acc[kNT];
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ssx = 0.f, ssy = 0.f;
+  float gram[kGram];
+#pragma unroll
+  for (int g = 0; g < kGram; ++g) gram[g] = 0.f;
 
-    float cpost[kHC], ccomb[kHC * kHC], cpre[kHC];
+  auto load_wst = [&](int c) {
+    const int gstep = (fs + c * kCF) / 32;
 #pragma unroll
-    for (int j = 0; j < kHC; ++j) {
-      cpost[j] = POST ? a.post_in[(t0 + lt) * kHC + j] : 0.f;
-      cpre[j] = PRE ? a.pre_in[(t0 + lt) * kHC + j] : 0.f;
+    for (int i = 0; i < kNT; ++i) {
+      const int blk = wave + i * kWaves;          // (st, k, nt) = blk / 20, (blk / 5) % 4, blk % 5
+      const int st = blk / (kHC * kNT), k = (blk / kNT) % kHC, nt = blk % kNT;
+      wst[i] = a.fn[((size_t)((gstep + st) * kHC + k) * kNT + nt) * 64 + lane];
     }
+  };
+  auto store_wst = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < kHC * kHC; ++j) ccomb[j] = POST ? a.comb_in[(t0 + lt) * kHC * kHC + j] : 0.f;
-
-    u32x4 cur[kHC + 1];
-    u32x4 wst[kNT];  // this wave's share (5 of 40 blocks) of the next chunk's weight tiles
-    f32x4 acc[kNT];
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float ssx = 0.f, ssy = 0.f;
-
-    auto load_wst = [&](int c) {
-      const int gstep = (fs + c * kCF) / 32;
-#pragma unroll
-      for (int i = 0; i < kNT; ++i) {
-        const int blk = wave + i * kWaves;          // (st, k, nt) = blk / 20, (blk / 5) % 4, blk % 5
-        const int st = blk / (kHC * kNT), k = (blk / kNT) % kHC, nt = blk % kNT;
-        wst[i] = a.fn[((size_t)((gstep + st) * kHC + k) * kNT + nt) * 64 + lane];
-      }
-    };
-    auto store_wst = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < kNT; ++i) {
-        const int blk = wave + i * kWaves;
-        const int st = blk / (kHC * kNT), k = (blk / kNT) % kHC, nt = blk % kNT;
-        w_lds[buf][st][k][nt][lane] = wst[i];
-      }
-    };
-    auto load_stream = [&](int c) {
-      const unsigned f = fs + c * kCF + fl;
-#pragma unroll
-      for (int j = 0; j < kHC; ++j) cur[j] = ld_stream(reinterpret_cast<const u32x4*>(xb + (lt * kHC * d + j * d + f)));
-      cur[kHC] = POST ? ld_stream(reinterpret_cast<const u32x4*>(db + (lt * d + f))) : u32x4{0u, 0u, 0u, 0u};
-    };
-    auto stream_phase = [&](int c) {
-      const unsigned f = fs + c * kCF + fl;
-      u32 xp[kHC][4];
-      if constexpr (POST) {
-        post_8(cur, cpost, ccomb, xp);
-        if (tv) {
-#pragma unroll
-          for (int k = 0; k < kHC; ++k)
-            st_stream(reinterpret_cast<u32x4*>(xob + (lt * kHC * d + k * d + f)),
-                      u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]});
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < kHC; ++k)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) xp[k][e] = cur[k][e];
-      }
-#pragma unroll
-      for (int k = 0; k < kHC; ++k) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ssx = dot2_bf16(xp[k][e], xp[k][e], ssx);
-        a_lds[rb][a_st][k][a_lane] = u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]};
-      }
-      if constexpr (PRE) {
-        u32 yp[4];
-        pre_8(xp, cpre, yp);
-        if constexpr (NORM) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ssy = dot2_bf16(yp[e], yp[e], ssy);
-          y_lds[m][(c * kCF + fl) / 8] = u32x4{yp[0], yp[1], yp[2], yp[3]};
-        } else if (tv) {
-          st_stream(reinterpret_cast<u32x4*>(yb + (lt * d + f)), u32x4{yp[0], yp[1], yp[2], yp[3]});
-        }
-      }
-    };
-    auto matrix_phase = [&](int buf) {
-#pragma unroll
-      for (int k = 0; k < kHC; ++k) {
-        const bf16x8 A = __builtin_bit_cast(bf16x8, a_lds[rb][hw][k][lane]);
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt)
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              A, __builtin_bit_cast(bf16x8, w_lds[buf][hw][k][nt][lane]), acc[nt], 0, 0, 0);
-      }
-    };
-    // one chunk: its streams are in registers; the next chunk's weights (then
-    // streams) are requested before any compute of this one
-    auto chunk = [&](int c, bool more) {
-      if (more) load_wst(c + 1);
-      stream_phase(c);
-      if (more) load_stream(c + 1);
-      lds_barrier();                 // A tiles and chunk c's weights in place; previous matrix phase done
-      if (more) store_wst((c + 1) & 1);
-      matrix_phase(c & 1);
-      lds_barrier();                 // matrix phase done before the A tiles are rewritten
-    };
-
-    load_wst(0);
-    load_stream(0);
-    store_wst(0);
-    lds_barrier();
-    for (int c = 0; c + 1 < nch; ++c) chunk(c, true);
-    chunk(nch - 1, false);
-
-    // ---- per-token partials of this slice
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-      ssx += __shfl_xor(ssx, o);
-      ssy += __shfl_xor(ssy, o);
+    for (int i = 0; i < kNT; ++i) {
+      const int blk = wave + i * kWaves;
+      const int st = blk / (kHC * kNT), k = (blk / kNT) % kHC, nt = blk % kNT;
+      w_lds[buf][st][k][nt][lane] = wst[i];
     }
-    float* red = reinterpret_cast<float*>(&w_lds[0][0][0][0][0]);   // [4 rb][2 steps][16][80] | sums
+  };
+  auto load_stream = [&](int c) {
+    const unsigned f = fs + c * kCF + fl;
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        red[((rb * 2 + hw) * 16 + 4 * (lane >> 4) + rr) * 80 + nt * 16 + (lane & 15)] = acc[nt][rr];
-    float* sums = red + 4 * 2 * 16 * 80;                             // [2][kTT]
-    if ((lane & 7) == 0) {
-      sums[m] = ssx;
-      sums[kTT + m] = ssy;
-    }
-    lds_barrier();
-    float* tpw = a.ws_part + (size_t)tile * S * kTT * kRec;
-    const __amdgpu_buffer_rsrc_t rs = ws_rsrc(tpw, tile_bytes);
-    for (int idx = threadIdx.x; idx < kTT * (kRec / 4); idx += kThreads) {
-      const int tm = idx / (kRec / 4), q0 = (idx % (kRec / 4)) * 4;
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int q = q0 + i;
-        if (q < kMix) {
-          const float* r0 = red + ((tm >> 4) * 2 * 16 + (tm & 15)) * 80;   // step 0
-          const float* r1 = r0 + 16 * 80;                                 // step 1
-          v[i] = ((r0[q] + r0[kMix + q]) + r0[2 * kMix + q]) + ((r1[q] + r1[kMix + q]) + r1[2 * kMix + q]);
-        } else {
-          v[i] = q < kPartials ? sums[(q - kMix) * kTT + tm] : 0.f;
-        }
-      }
-      __builtin_amdgcn_raw_buffer_store_b128(f32x4{v[0], v[1], v[2], v[3]}, rs,
-                                             ((slice * kTT + tm) * kRec + q0) * 4, 0, kCoherent);
-    }
-    wait_vm_stores();
-    lds_barrier();
-    // ---- meet the other slices of this tile
-    if (threadIdx.x == 0) {
-      __hip_atomic_fetch_add(a.ws_cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      unsigned it = 0;
-      while (__hip_atomic_load(a.ws_cnt + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)S) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++it == kSpinLimit) {
-          __hip_atomic_fetch_or(a.ws_err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-      }
-    }
-    lds_barrier();
-    // gather what this workgroup needs, all loads in flight at once:
-    // the owned tokens' records from every slice, and every token's sum of y^2
-    const int own = (kTT + S - 1) / S;            // tokens owned by this slice
-    float* g_own = red;                           // [own][S][kRec]
-    float* g_yy = red + own * S * kRec;           // [kTT][S]
-    for (int i = threadIdx.x; i < own * S; i += kThreads) {
-      const int o = i / S, sl = i % S;
-      const int tm = min(slice * own + o, kTT - 1);
-#pragma unroll
-      for (int g4 = 0; g4 < kRec / 4; ++g4) {
-        const f32x4 v = (f32x4)__builtin_amdgcn_raw_buffer_load_b128(rs, ((sl * kTT + tm) * kRec + g4 * 4) * 4, 0, kCoherent);
-        *reinterpret_cast<f32x4*>(g_own + i * kRec + g4 * 4) = v;
-      }
-    }
-    if constexpr (NORM) {
-      for (int i = threadIdx.x; i < kTT * S; i += kThreads) {
-        const int tm = i / S, sl = i % S;
-        g_yy[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, ((sl * kTT + tm) * kRec + kMix + 1) * 4, 0, kCoherent));
-      }
-    }
-    lds_barrier();
-    if constexpr (NORM) {
-      if (threadIdx.x < kTT) {
-        float sy = 0.f;
-        for (int sl = 0; sl < S; ++sl) sy += g_yy[threadIdx.x * S + sl];
-        s_ry[threadIdx.x] = 1.0f / sqrtf(sy / (float)d + a.rms_eps);
-      }
-    }
-    // owned tokens: mixes and the split/Sinkhorn, one token per lane of wave 0
-    if (wave == 0 && lane < own) {
-      const int tm = slice * own + lane;
-      const int64_t t = t0 + tm;
-      if (tm < kTT && t < a.n) {
-        float dot[kMix];
-#pragma unroll
-        for (int q = 0; q < kMix; ++q) dot[q] = 0.f;
-        float sx = 0.f;
-        for (int sl = 0; sl < S; ++sl) {
-          const float* pp = g_own + (lane * S + sl) * kRec;
-#pragma unroll
-          for (int q = 0; q < kMix; ++q) dot[q] += pp[q];
-          sx += pp[kMix];
-        }
-        const float rx = 1.0f / sqrtf(sx / (float)(kHC * d) + a.norm_eps);
-        float mx[kMix];
-#pragma unroll
-        for (int q = 0; q < kMix; ++q) mx[q] = dot[q] * rx;
-        if (a.mixes_out) {
-#pragma unroll
-          for (int q = 0; q < kMix; q += 4)
-            *reinterpret_cast<f32x4*>(a.mixes_out + t * kMix + q) = f32x4{mx[q], mx[q + 1], mx[q + 2], mx[q + 3]};
-        }
-        if (a.pre_out) {
-          float bs[kMix];
-#pragma unroll
-          for (int q = 0; q < kMix; ++q) bs[q] = a.hc_base[q];
-          split_sinkhorn_one(mx, a.hc_scale[0], a.hc_scale[1], a.hc_scale[2], bs, a.iters, a.hc_eps,
-                             a.pre_out + t * kHC, a.post_out + t * kHC, a.comb_out + t * kHC * kHC);
-        }
-      }
-    }
-    if constexpr (NORM) lds_barrier();   // s_ry visible
-    // ---- rescale the parked read row: z = gamma * (y * r)  (NORM)
-    if constexpr (NORM) {
+    for (int j = 0; j < kHC; ++j) cur[j] = ld_stream(reinterpret_cast<const u32x4*>(xb + (lt * kHC * d + j * d + f)));
+    cur[kHC] = POST ? ld_stream(reinterpret_cast<const u32x4*>(db + (lt * d + f))) : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto stream_phase = [&](int c) {
+    const unsigned f = fs + c * kCF + fl;
+    u32 xp[kHC][4];
+    if constexpr (POST) {
+      post_8(cur, cpost, ccomb, xp);
       if (tv) {
-        const float ry = s_ry[m];
-        for (int c = 0; c < nch; ++c) {
-          const unsigned f = fs + c * kCF + fl;
-          const u32x4 yv = y_lds[m][(c * kCF + fl) / 8];
-          const f32x4 g0 = *reinterpret_cast<const f32x4*>(g_lds + c * kCF + fl);
-          const f32x4 g1 = *reinterpret_cast<const f32x4*>(g_lds + c * kCF + fl + 4);
-          const float gm[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
-          u32 zp[4];
 #pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2)
-            zp[e2] = pack_bf16(gm[2 * e2] * (bf_lo(yv[e2]) * ry), gm[2 * e2 + 1] * (bf_hi(yv[e2]) * ry));
-          st_stream(reinterpret_cast<u32x4*>(yb + (lt * d + f)), u32x4{zp[0], zp[1], zp[2], zp[3]});
+        for (int k = 0; k < kHC; ++k) {
+          u32x4* p = reinterpret_cast<u32x4*>(xob + (lt * kHC * d + k * d + f));
+          const u32x4 v = u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]};
+          if constexpr (RM == kFreshPre) st_keep(p, v); else st_stream(p, v);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kHC; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xp[k][e] = cur[k][e];
+    }
+#pragma unroll
+    for (int k = 0; k < kHC; ++k) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ssx = dot2_bf16(xp[k][e], xp[k][e], ssx);
+      a_lds[rb][a_st][k][a_lane] = u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]};
+    }
+    if constexpr (RM == kGivenPre) {
+      u32 yp[4];
+      pre_8(xp, cpre, yp);
+      if constexpr (NORM) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ssy = dot2_bf16(yp[e], yp[e], ssy);
+      }
+      if (tv) {
+        u32x4* p = reinterpret_cast<u32x4*>(yb + (lt * d + f));
+        const u32x4 v = u32x4{yp[0], yp[1], yp[2], yp[3]};
+        if constexpr (NORM) st_keep(p, v); else st_stream(p, v);
+      }
+    }
+    if constexpr (RM == kFreshPre && NORM) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        int g = 0;
+#pragma unroll
+        for (int j = 0; j < kHC; ++j)
+#pragma unroll
+          for (int l = j; l < kHC; ++l, ++g) gram[g] = dot2_bf16(xp[j][e], xp[l][e], gram[g]);
+      }
+    }
+  };
+  auto matrix_phase = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < kHC; ++k) {
+      const bf16x8 A = __builtin_bit_cast(bf16x8, a_lds[rb][hw][k][lane]);
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt)
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            A, __builtin_bit_cast(bf16x8, w_lds[buf][hw][k][nt][lane]), acc[nt], 0, 0, 0);
+    }
+  };
+  // one chunk: its streams are in registers; the next chunk's weights (then
+  // streams) are requested before any compute of this one
+  auto chunk = [&](int c, bool more) {
+    if (more) load_wst(c + 1);
+    stream_phase(c);
+    if (more) load_stream(c + 1);
+    lds_barrier();                 // A tiles and chunk c's weights in place; previous matrix phase done
+    if (more) store_wst((c + 1) & 1);
+    matrix_phase(c & 1);
+    lds_barrier();                 // matrix phase done before the A tiles are rewritten
+  };
+
+  load_wst(0);
+  load_stream(0);
+  store_wst(0);
+  lds_barrier();
+  for (int c = 0; c + 1 < nch; ++c) chunk(c, true);
+  chunk(nch - 1, false);
+
+  // ---- per-token records of this slice
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+    ssx += __shfl_xor(ssx, o);
+    if constexpr (RM == kGivenPre && NORM) ssy += __shfl_xor(ssy, o);
+    if constexpr (RM == kFreshPre && NORM) {
+#pragma unroll
+      for (int g = 0; g < kGram; ++g) gram[g] += __shfl_xor(gram[g], o);
+    }
+  }
+  float* red = reinterpret_cast<float*>(&w_lds[0][0][0][0][0]);   // [4 rb][2 steps][16][80] | extra
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      red[((rb * 2 + hw) * 16 + 4 * (lane >> 4) + rr) * 80 + nt * 16 + (lane & 15)] = acc[nt][rr];
+  float* extra = red + 4 * 2 * 16 * 80;                            // [kRec - kMix][kTT]
+  if ((lane & 7) == 0) {
+    extra[m] = ssx;
+    if constexpr (RM == kGivenPre && NORM) extra[kTT + m] = ssy;
+    if constexpr (RM == kFreshPre && NORM) {
+#pragma unroll
+      for (int g = 0; g < kGram; ++g) extra[(1 + g) * kTT + m] = gram[g];
+    }
+  }
+  lds_barrier();
+  float* rec = a.rec + ((size_t)tile * S + slice) * kTT * kRec;
+  for (int idx = threadIdx.x; idx < kTT * kQuads; idx += kThreads) {
+    const int tm = idx / kQuads, q0 = (idx % kQuads) * 4;
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = q0 + i;
+      if (q < kMix) {
+        const float* r0 = red + ((tm >> 4) * 2 * 16 + (tm & 15)) * 80;   // step 0
+        const float* r1 = r0 + 16 * 80;                                 // step 1
+        v[i] = ((r0[q] + r0[kMix + q]) + r0[2 * kMix + q]) + ((r1[q] + r1[kMix + q]) + r1[2 * kMix + q]);
+      } else {
+        v[i] = q < kUsed ? extra[(q - kMix) * kTT + tm] : 0.f;
+      }
+    }
+    *reinterpret_cast<f32x4*>(rec + tm * kRec + q0) = f32x4{v[0], v[1], v[2], v[3]};
+  }
+}
+
+struct FinishArgs {
+  const float* rec;         // [tiles][S][kTT][kRec] from stream_kernel
+  const hc_bf16* src;       // fresh pre: X' (or x at a block entry) [n, hc, d]; given pre: y [n, d]
+  hc_bf16* y_out;
+  const float* gamma;
+  const float* hc_base;
+  const float* hc_scale;
+  float* mixes_out;
+  float* pre_out;
+  float* post_out;
+  float* comb_out;
+  int64_t n;
+  int d, S, S2, F2, tiles, iters;
+  float hc_eps, norm_eps, rms_eps;
+};
+
+// Sum over the 4 lanes of a token's quad, by lane permutation within the
+// quad (no LDS round trip).  Butterfly order: every lane of the quad obtains
+// the same bits, (v0 + v1) + (v2 + v3) up to commutation.
+template <int CTRL>
+__device__ __forceinline__ float quad_perm(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  const float u = v + quad_perm<0xB1>(v);      // lanes [1,0,3,2]
+  return u + quad_perm<0x4E>(u);               // lanes [2,3,0,1]
+}
+
+template <int RM, bool NORM>
+__global__ void __launch_bounds__(kFinThreads) finish_kernel(const FinishArgs a) {
+  __shared__ float tot[kTT][kRec];          // the tile's records summed over the slices
+  __shared__ float s_pre[kTT][kHC];         // derived pre (fresh read)
+  __shared__ float s_r[kTT];                // RMSNorm factor of the read row
+  constexpr int kUsed = rec_used<RM, NORM>();
+  constexpr int kQuads = (kUsed + 3) / 4;
+  const int tile = blockIdx.x / a.S2, sl2 = blockIdx.x % a.S2;
+  const int64_t t0 = (int64_t)tile * kTT;
+  const int valid = (int)min<int64_t>(kTT, a.n - t0);
+  const int d = a.d, S = a.S;
+
+  // ---- sum the tile's records over the slices, in slice order
+  const float* rt = a.rec + (size_t)tile * S * kTT * kRec;
+  for (int cell = threadIdx.x; cell < valid * kQuads; cell += kFinThreads) {
+    const int tm = cell / kQuads, q0 = (cell % kQuads) * 4;
+    const float* p = rt + tm * kRec + q0;
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+    int sl = 0;
+    for (; sl + 8 <= S; sl += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(p + (size_t)(sl + u) * kTT * kRec);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; sl < S; ++sl) s += *reinterpret_cast<const f32x4*>(p + (size_t)sl * kTT * kRec);
+    *reinterpret_cast<f32x4*>(&tot[tm][q0]) = s;
+  }
+  __syncthreads();
+
+  // ---- derive: 4 lanes per token, lane j holds comb row j
+  if (threadIdx.x < kTT * kHC) {
+    const int tm = threadIdx.x >> 2, j = threadIdx.x & 3;
+    const int64_t t = t0 + tm;
+    const bool own = tm < valid && tm % a.S2 == sl2;
+    const float* rec = tot[tm];
+    const float rx = 1.0f / sqrtf(rec[kMix] / (float)(kHC * d) + a.norm_eps);
+    if (own && a.mixes_out) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(rec + 4 * j);
+      *reinterpret_cast<f32x4*>(a.mixes_out + t * kMix + 4 * j) = f32x4{v[0] * rx, v[1] * rx, v[2] * rx, v[3] * rx};
+      if (j < 2) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(rec + 16 + 4 * j);
+        *reinterpret_cast<f32x4*>(a.mixes_out + t * kMix + 16 + 4 * j) =
+            f32x4{w[0] * rx, w[1] * rx, w[2] * rx, w[3] * rx};
+      }
+    }
+    if (a.pre_out) {
+      const float s0 = a.hc_scale[0], s1 = a.hc_scale[1], s2 = a.hc_scale[2];
+      const float pre = sigmoidf_((rec[j] * rx) * s0 + a.hc_base[j]) + a.hc_eps;
+      const float post = 2.0f * sigmoidf_((rec[kHC + j] * rx) * s1 + a.hc_base[kHC + j]);
+      float A[kHC];
+      float mxr = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < kHC; ++k) {
+        const int q = 2 * kHC + j * kHC + k;
+        A[k] = (rec[q] * rx) * s2 + a.hc_base[q];
+        mxr = fmaxf(mxr, A[k]);
+      }
+      float rsum = 0.f;
+#pragma unroll
+      for (int k = 0; k < kHC; ++k) {
+        A[k] = expf(A[k] - mxr);
+        rsum = rsum + A[k];
+      }
+      const float rinv = __builtin_amdgcn_rcpf(rsum);
+#pragma unroll
+      for (int k = 0; k < kHC; ++k) A[k] = A[k] * rinv + a.hc_eps;
+      auto col_norm = [&]() {
+#pragma unroll
+        for (int k = 0; k < kHC; ++k) A[k] = A[k] * __builtin_amdgcn_rcpf(quad_sum(A[k]) + a.hc_eps);
+      };
+      col_norm();
+      for (int it = 1; it < a.iters; ++it) {
+        const float inv = __builtin_amdgcn_rcpf(((A[0] + A[1]) + A[2]) + A[3] + a.hc_eps);
+#pragma unroll
+        for (int k = 0; k < kHC; ++k) A[k] = A[k] * inv;
+        col_norm();
+      }
+      if (own) {
+        a.pre_out[t * kHC + j] = pre;
+        a.post_out[t * kHC + j] = post;
+        *reinterpret_cast<f32x4*>(a.comb_out + t * kHC * kHC + j * kHC) = f32x4{A[0], A[1], A[2], A[3]};
+      }
+      if constexpr (RM == kFreshPre) {
+        s_pre[tm][j] = pre;
+        if constexpr (NORM) {
+          // sum_i y_i^2 = p^T G p over the whole row, G summed over the slices
+          double p[kHC];
+#pragma unroll
+          for (int l = 0; l < kHC; ++l) p[l] = (double)__shfl(pre, (threadIdx.x & ~3) + l);
+          double yy = 0.0;
+          int g = 0;
+#pragma unroll
+          for (int l = 0; l < kHC; ++l)
+#pragma unroll
+            for (int l2 = l; l2 < kHC; ++l2, ++g)
+              yy += (l == l2 ? 1.0 : 2.0) * p[l] * p[l2] * (double)rec[kMix + 1 + g];
+          if (j == 0) s_r[tm] = 1.0f / sqrtf((float)(yy / (double)d) + a.rms_eps);
         }
       }
     }
-    lds_barrier();                   // all reads of the tile's partials, s_ry and y_lds done
-    if (threadIdx.x == 0) {
-      const unsigned prev = __hip_atomic_fetch_add(a.ws_done + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (prev == (unsigned)S - 1) {   // last one out leaves the counters zeroed for the next call
-        __hip_atomic_store(a.ws_cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(a.ws_done + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (RM == kGivenPre && NORM) {
+      if (j == 0) s_r[tm] = 1.0f / sqrtf(rec[kMix + 1] / (float)d + a.rms_eps);
+    }
+  }
+
+  // ---- this workgroup's slice of the read row
+  if constexpr (RM == kFreshPre || (RM == kGivenPre && NORM)) {
+    __syncthreads();                 // s_pre, s_r in place
+    const int m = threadIdx.x >> 3;              // token of the tile
+    const int fl = (threadIdx.x & 7) * 8;        // first feature within the chunk
+    const bool tv = m < valid;
+    const unsigned lt = tv ? (unsigned)m : 0u;
+    const int fs = sl2 * a.F2;
+    const int nch = a.F2 / kCF;
+    float p[kHC];
+#pragma unroll
+    for (int j = 0; j < kHC; ++j) p[j] = RM == kFreshPre ? s_pre[lt][j] : 0.f;
+    const float r = NORM ? s_r[lt] : 1.f;
+    constexpr int NL = RM == kFreshPre ? kHC : 1;
+    const int rstride = RM == kFreshPre ? kHC * d : d;
+    const hc_bf16* src = a.src + (t0 + lt) * rstride;
+    hc_bf16* yrow = a.y_out + (t0 + lt) * d;
+    // chunks in batches of U, all loads of a batch in flight at once, last
+    // written first (the most recent stores are the likeliest still cached)
+    constexpr int U = RM == kFreshPre ? 5 : 8;
+    for (int cb = nch; cb > 0; cb -= U) {
+      u32x4 ld[U][NL];
+      f32x4 gv[U][2];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = cb - 1 - u;
+        if (c >= 0) {
+          const unsigned f = fs + c * kCF + fl;
+#pragma unroll
+          for (int k = 0; k < NL; ++k) ld[u][k] = ld_stream(reinterpret_cast<const u32x4*>(src + (k * d + f)));
+          if constexpr (NORM) {
+            gv[u][0] = *reinterpret_cast<const f32x4*>(a.gamma + f);
+            gv[u][1] = *reinterpret_cast<const f32x4*>(a.gamma + f + 4);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = cb - 1 - u;
+        if (c >= 0) {
+          const unsigned f = fs + c * kCF + fl;
+          u32 yp[4];
+          if constexpr (RM == kFreshPre) {
+            u32 xp[kHC][4];
+#pragma unroll
+            for (int k = 0; k < kHC; ++k)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) xp[k][e] = ld[u][k][e];
+            pre_8(xp, p, yp);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) yp[e] = ld[u][0][e];
+          }
+          if constexpr (NORM) {
+            const float gm[8] = {gv[u][0][0], gv[u][0][1], gv[u][0][2], gv[u][0][3],
+                                 gv[u][1][0], gv[u][1][1], gv[u][1][2], gv[u][1][3]};
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2)
+              yp[e2] = pack_bf16(gm[2 * e2] * (bf_lo(yp[e2]) * r), gm[2 * e2 + 1] * (bf_hi(yp[e2]) * r));
+          }
+          if (tv) st_stream(reinterpret_cast<u32x4*>(yrow + f), u32x4{yp[0], yp[1], yp[2], yp[3]});
+        }
       }
     }
   }
@@ -784,16 +887,11 @@ int check_n(int64_t n) {
   return HC_OK;
 }
 
-int check_device(int* ncu) {
-  int count = 0, dev = 0;
-  hipError_t e = hipGetDeviceCount(&count);
+int check_device() {
+  int count = 0;
+  const hipError_t e = hipGetDeviceCount(&count);
   if (e != hipSuccess || count <= 0)
     return fail(HC_ENODEV, "no HIP device: %s", e == hipSuccess ? "count is 0" : hipGetErrorName(e));
-  if (ncu) {
-    if ((e = hipGetDevice(&dev)) != hipSuccess ||
-        (e = hipDeviceGetAttribute(ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
-      return fail(HC_EHIP, "device query failed: %s", hipGetErrorName(e));
-  }
   return HC_OK;
 }
 
@@ -802,81 +900,84 @@ int launched(hipError_t e, const char* what) {
   return HC_OK;
 }
 
-// ---- split kernel geometry and workspace
-// Slices per stream: the smallest divisor S of d/64 with F = d/S <= 320 (the
-// read row of a slice fits the registers) and tiles*S >= 256 (enough
-// workgroups for the 256 compute units of an MI355X).  Fixed by (n, d) alone
-// so that the workspace size is too.
-int split_slices(int64_t n, int d) {
-  const int64_t tiles = (n + kTT - 1) / kTT;
-  const int units = d / kCF;
-  const int64_t need = std::max<int64_t>((d + kMaxSliceY - 1) / kMaxSliceY, (256 + tiles - 1) / tiles);
+// ---- boundary geometry and workspace
+// Stream slices: the smallest divisor S of d/64 with tiles*S >= 256 (one
+// workgroup for each of the 256 compute units of an MI355X), capped at
+// kMaxSlices for short inputs.  Fixed by (n, d) alone so that the workspace
+// size is too.  Read slices of the finish: likewise with tiles*S2 >= 512.
+int divisor_at_least(int units, int64_t need) {
   for (int s = 1; s <= units; ++s)
     if (units % s == 0 && s >= need) return s;
   return units;
 }
-
-struct WsLayout {
-  size_t err, cnt, done, part, total;
-};
-
-WsLayout ws_layout(int64_t n, int d) {
+int stream_slices(int64_t n, int d) {
   const int64_t tiles = (n + kTT - 1) / kTT;
-  const int S = split_slices(n, d);
-  WsLayout w;
-  w.err = 0;
-  w.cnt = 256;
-  w.done = w.cnt + ((size_t)tiles * 4 + 255) / 256 * 256;
-  w.part = w.done + ((size_t)tiles * 4 + 255) / 256 * 256;
-  w.total = w.part + (size_t)tiles * S * kTT * kRec * 4;
-  return w;
+  return divisor_at_least(d / kCF, std::min<int64_t>((256 + tiles - 1) / tiles, kMaxSlices));
+}
+int read_slices(int64_t n, int d) {
+  const int64_t tiles = (n + kTT - 1) / kTT;
+  return divisor_at_least(d / kCF, std::min<int64_t>((512 + tiles - 1) / tiles, kMaxSlices));
+}
+size_t workspace_bytes(int64_t n, int d) {
+  const int64_t tiles = (n + kTT - 1) / kTT;
+  return (size_t)tiles * stream_slices(n, d) * kTT * kRec * 4;
 }
 
-template <bool POST, bool PRE, bool NORM>
-hipError_t launch_split_t(const SplitArgs& a, int grid, hipStream_t st) {
-  SplitArgs copy = a;
+template <bool POST, int RM, bool NORM>
+hipError_t launch_stream_t(const StreamArgs& a, unsigned grid, hipStream_t st) {
+  StreamArgs copy = a;
   void* args[] = {&copy};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&split_kernel_tiles<POST, PRE, NORM>),
-                                    dim3(grid), dim3(kThreads), args, 0, st);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&stream_kernel<POST, RM, NORM>), dim3(grid), dim3(kThreads),
+                         args, 0, st);
+}
+template <int RM, bool NORM>
+hipError_t launch_finish_t(const FinishArgs& a, unsigned grid, hipStream_t st) {
+  FinishArgs copy = a;
+  void* args[] = {&copy};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&finish_kernel<RM, NORM>), dim3(grid), dim3(kFinThreads),
+                         args, 0, st);
 }
 
-int launch_split(bool post, bool pre, bool norm, SplitArgs a, void* ws, size_t ws_bytes, int ncu,
-                 hipStream_t st, const char* what) {
-  const WsLayout L = ws_layout(a.n, a.d);
-  if (!ws) return fail(HC_EINVAL, "%s: workspace must not be NULL (need %zu bytes)", what, L.total);
+// s: streams, pre_in, x_out/y_out set; f: split parameters and outputs, gamma set.
+int launch_boundary(bool post, int rm, bool norm, StreamArgs s, FinishArgs f, void* ws, size_t ws_bytes,
+                    hipStream_t st, const char* what) {
+  const size_t need = workspace_bytes(s.n, s.d);
+  if (!ws) return fail(HC_EINVAL, "%s: workspace must not be NULL (need %zu bytes)", what, need);
   if (!aligned16(ws)) return fail(HC_EINVAL, "%s: workspace is not 16-byte aligned", what);
-  if (ws_bytes < L.total) return fail(HC_EINVAL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, L.total);
-  a.S = split_slices(a.n, a.d);
-  a.F = a.d / a.S;
-  a.tiles = (int)((a.n + kTT - 1) / kTT);
-  char* base = static_cast<char*>(ws);
-  a.ws_err = reinterpret_cast<unsigned*>(base + L.err);
-  a.ws_cnt = reinterpret_cast<unsigned*>(base + L.cnt);
-  a.ws_done = reinterpret_cast<unsigned*>(base + L.done);
-  a.ws_part = reinterpret_cast<float*>(base + L.part);
-  {  // the finish gathers the owned tokens' records (and, with RMSNorm, every token's
-     // sum of y^2) into the weight staging area of LDS
-    const int own = (kTT + a.S - 1) / a.S;
-    const size_t gather = ((size_t)own * a.S * kRec + (norm ? (size_t)kTT * a.S : 0)) * 4;
-    if (gather > kWeightStageBytes)
-      return fail(HC_ENOTSUP, "%s: d=%d needs %zu bytes of LDS for the slice exchange (limit %zu)", what, a.d,
-                  gather, kWeightStageBytes);
-  }
-  const int64_t total = (int64_t)a.tiles * a.S;
-  int64_t cap = (int64_t)(ncu / a.S) * a.S;
-  if (cap < a.S) return fail(HC_ENOTSUP, "%s: %d slices need as many resident workgroups, device has %d", what, a.S, ncu);
-  const int grid = (int)std::min<int64_t>(total, cap);
-  const int key = (post ? 4 : 0) | (pre ? 2 : 0) | (norm ? 1 : 0);
+  if (ws_bytes < need) return fail(HC_EINVAL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, need);
+  const int64_t tiles = (s.n + kTT - 1) / kTT;
+  if (tiles * kMaxSlices > INT32_MAX) return fail(HC_ENOTSUP, "%s: n=%lld is too large", what, (long long)s.n);
+  s.S = stream_slices(s.n, s.d);
+  s.F = s.d / s.S;
+  s.tiles = (int)tiles;
+  s.rec = static_cast<float*>(ws);
+  const unsigned grid1 = (unsigned)(tiles * s.S);
   hipError_t e;
-  switch (key) {
-    case 0b000: e = launch_split_t<false, false, false>(a, grid, st); break;
-    case 0b100: e = launch_split_t<true, false, false>(a, grid, st); break;
-    case 0b010: e = launch_split_t<false, true, false>(a, grid, st); break;
-    case 0b011: e = launch_split_t<false, true, true>(a, grid, st); break;
-    case 0b110: e = launch_split_t<true, true, false>(a, grid, st); break;
-    case 0b111: e = launch_split_t<true, true, true>(a, grid, st); break;
+  switch ((post ? 8 : 0) | (rm << 1) | (norm ? 1 : 0)) {
+    case 0x0: e = launch_stream_t<false, kNoRead, false>(s, grid1, st); break;
+    case 0x2: e = launch_stream_t<false, kGivenPre, false>(s, grid1, st); break;
+    case 0x3: e = launch_stream_t<false, kGivenPre, true>(s, grid1, st); break;
+    case 0x4: e = launch_stream_t<false, kFreshPre, false>(s, grid1, st); break;
+    case 0x5: e = launch_stream_t<false, kFreshPre, true>(s, grid1, st); break;
+    case 0xA: e = launch_stream_t<true, kGivenPre, false>(s, grid1, st); break;
+    case 0xB: e = launch_stream_t<true, kGivenPre, true>(s, grid1, st); break;
+    case 0xC: e = launch_stream_t<true, kFreshPre, false>(s, grid1, st); break;
+    case 0xD: e = launch_stream_t<true, kFreshPre, true>(s, grid1, st); break;
     default: return fail(HC_EINVAL, "%s: unsupported stage combination", what);
   }
+  int rc = launched(e, what);
+  if (rc) return rc;
+  const bool read = rm == kFreshPre || (rm == kGivenPre && norm);
+  f.rec = s.rec;
+  f.n = s.n; f.d = s.d; f.S = s.S; f.tiles = s.tiles;
+  f.S2 = read ? read_slices(s.n, s.d) : 1;
+  f.F2 = s.d / f.S2;
+  f.y_out = s.y_out;
+  f.src = rm == kFreshPre ? (post ? s.x_out : s.x) : s.y_out;
+  const unsigned grid2 = (unsigned)(tiles * f.S2);
+  if (rm == kFreshPre) e = norm ? launch_finish_t<kFreshPre, true>(f, grid2, st) : launch_finish_t<kFreshPre, false>(f, grid2, st);
+  else if (rm == kGivenPre && norm) e = launch_finish_t<kGivenPre, true>(f, grid2, st);
+  else e = launch_finish_t<kNoRead, false>(f, grid2, st);
   return launched(e, what);
 }
 
@@ -937,7 +1038,7 @@ int hc_fn_pack(const float* hc_fn, int hc, int d, void* fn_packed, void* stream)
   if (rc) return rc;
   HC_REQ(hc_fn);
   HC_REQ(fn_packed);
-  if ((rc = check_device(nullptr))) return rc;
+  if ((rc = check_device())) return rc;
   const int records = (d / kStepF) * kHC * kNT * 64;
   hipLaunchKernelGGL(pack_kernel, dim3((records + 255) / 256), dim3(256), 0, (hipStream_t)stream, hc_fn, d,
                      reinterpret_cast<u32x4*>(fn_packed), records);
@@ -947,7 +1048,7 @@ int hc_fn_pack(const float* hc_fn, int hc, int d, void* fn_packed, void* stream)
 size_t hc_workspace_bytes(int64_t n, int hc, int d) {
   if (hc != kHC || d <= 0 || d % kCF != 0 || d > kMaxD || n < 0) return 0;
   if (n == 0) return 0;
-  return ws_layout(n, d).total;
+  return workspace_bytes(n, d);
 }
 
 int hc_split_sinkhorn(const float* mixes, const float* hc_scale, const float* hc_base, int64_t n, int hc,
@@ -959,7 +1060,7 @@ int hc_split_sinkhorn(const float* mixes, const float* hc_scale, const float* hc
   if (iters < 1) return fail(HC_EINVAL, "iters=%d: at least one Sinkhorn round is needed", iters);
   HC_REQ(mixes); HC_REQ(hc_scale); HC_REQ(hc_base); HC_REQ(pre); HC_REQ(post); HC_REQ(comb);
   if (n == 0) return HC_OK;
-  if ((rc = check_device(nullptr))) return rc;
+  if ((rc = check_device())) return rc;
   hipLaunchKernelGGL(split_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
                      mixes, hc_scale, hc_base, n, iters, hc_eps, pre, post, comb);
   return launched(hipGetLastError(), "split_kernel");
@@ -981,13 +1082,14 @@ int hc_mixes(const hc_bf16* x, const void* fn_packed, int64_t n, int hc, int d, 
     return fail(HC_EINVAL, "nothing to compute: mixes and pre/post/comb are all NULL");
   }
   if (n == 0) return HC_OK;
-  int ncu = 0;
-  if ((rc = check_device(&ncu))) return rc;
-  SplitArgs a{};
-  a.n = n; a.d = d; a.x = x; a.fn = reinterpret_cast<const u32x4*>(fn_packed); a.mixes_out = mixes;
-  a.norm_eps = norm_eps; a.hc_scale = hc_scale; a.hc_base = hc_base; a.iters = iters; a.hc_eps = hc_eps;
-  if (split) { a.pre_out = pre; a.post_out = post; a.comb_out = comb; }
-  return launch_split(false, false, false, a, workspace, workspace_bytes, ncu, (hipStream_t)stream, "hc_mixes");
+  if ((rc = check_device())) return rc;
+  StreamArgs s{};
+  s.n = n; s.d = d; s.x = x; s.fn = reinterpret_cast<const u32x4*>(fn_packed);
+  FinishArgs f{};
+  f.mixes_out = mixes; f.norm_eps = norm_eps; f.hc_scale = hc_scale; f.hc_base = hc_base; f.iters = iters;
+  f.hc_eps = hc_eps;
+  if (split) { f.pre_out = pre; f.post_out = post; f.comb_out = comb; }
+  return launch_boundary(false, kNoRead, false, s, f, workspace, workspace_bytes, (hipStream_t)stream, "hc_mixes");
 }
 
 int hc_pre(const hc_bf16* x, const float* pre_mix, int64_t n, int hc, int d, hc_bf16* y, void* stream) {
@@ -997,7 +1099,7 @@ int hc_pre(const hc_bf16* x, const float* pre_mix, int64_t n, int hc, int d, hc_
   if ((rc = check_n(n))) return rc;
   HC_REQ(x); HC_REQ(pre_mix); HC_REQ(y);
   if (n == 0) return HC_OK;
-  if ((rc = check_device(nullptr))) return rc;
+  if ((rc = check_device())) return rc;
   RowArgs a{};
   a.n = n; a.d = d; a.x = x; a.pre_in = pre_mix; a.y_out = y;
   return launch_row(false, true, false, a, (hipStream_t)stream, "hc_pre");
@@ -1012,7 +1114,7 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
   HC_REQ(delta); HC_REQ(x); HC_REQ(post); HC_REQ(comb); HC_REQ(x_out);
   if (x_out == x) return fail(HC_EINVAL, "x_out must not alias x");
   if (n == 0) return HC_OK;
-  if ((rc = check_device(nullptr))) return rc;
+  if ((rc = check_device())) return rc;
   RowArgs a{};
   a.n = n; a.d = d; a.delta = delta; a.x = x; a.post_in = post; a.comb_in = comb; a.x_out = x_out;
   return launch_row(true, false, false, a, (hipStream_t)stream, "hc_post");
@@ -1044,8 +1146,7 @@ int hc_boundary(const hc_boundary_args* p, void* stream) {
   if (norm && p->d > kRowChunk * kRowMaxChunks * 2)
     return fail(HC_ENOTSUP, "RMSNorm of the read row supports d <= %d", kRowChunk * kRowMaxChunks * 2);
   if (p->n == 0) return HC_OK;
-  int ncu = 0;
-  if ((rc = check_device(&ncu))) return rc;
+  if ((rc = check_device())) return rc;
   const hipStream_t st = (hipStream_t)stream;
 
   if (!mix) {  // stack exit: write, read (+ norm); no projection
@@ -1054,22 +1155,16 @@ int hc_boundary(const hc_boundary_args* p, void* stream) {
     r.pre_in = p->pre_in; r.gamma = p->gamma; r.x_out = p->x_out; r.y_out = p->y_out; r.rms_eps = p->rms_eps;
     return launch_row(post, true, norm, r, st, "hc_boundary (exit)");
   }
-  SplitArgs a{};
-  a.n = p->n; a.d = p->d; a.x = p->x; a.delta = p->delta; a.post_in = p->post_in; a.comb_in = p->comb_in;
-  a.pre_in = p->pre_in; a.fn = reinterpret_cast<const u32x4*>(p->fn_packed); a.hc_base = p->hc_base;
-  a.hc_scale = p->hc_scale; a.gamma = p->gamma; a.x_out = p->x_out; a.y_out = p->y_out;
-  a.mixes_out = p->mixes_out; a.pre_out = p->pre_out; a.post_out = p->post_out; a.comb_out = p->comb_out;
-  a.iters = p->iters; a.hc_eps = p->hc_eps; a.norm_eps = p->norm_eps; a.rms_eps = p->rms_eps;
-  if (!fresh) return launch_split(post, true, norm, a, p->workspace, p->workspace_bytes, ncu, st, "hc_boundary");
-  // Read with the pre derived in this call: derive (and write), then read.
-  SplitArgs a1 = a;
-  a1.pre_in = nullptr; a1.y_out = nullptr; a1.gamma = nullptr;
-  if ((rc = launch_split(post, false, false, a1, p->workspace, p->workspace_bytes, ncu, st, "hc_boundary (derive)")))
-    return rc;
-  RowArgs r{};
-  r.n = p->n; r.d = p->d; r.x = post ? p->x_out : p->x; r.pre_in = p->pre_out; r.gamma = p->gamma;
-  r.y_out = p->y_out; r.rms_eps = p->rms_eps;
-  return launch_row(false, true, norm, r, st, "hc_boundary (read)");
+  StreamArgs s{};
+  s.n = p->n; s.d = p->d; s.x = p->x; s.delta = p->delta; s.post_in = p->post_in; s.comb_in = p->comb_in;
+  s.pre_in = p->pre_in; s.fn = reinterpret_cast<const u32x4*>(p->fn_packed); s.x_out = p->x_out;
+  s.y_out = p->y_out;
+  FinishArgs f{};
+  f.gamma = p->gamma; f.hc_base = p->hc_base; f.hc_scale = p->hc_scale; f.mixes_out = p->mixes_out;
+  f.pre_out = p->pre_out; f.post_out = p->post_out; f.comb_out = p->comb_out; f.iters = p->iters;
+  f.hc_eps = p->hc_eps; f.norm_eps = p->norm_eps; f.rms_eps = p->rms_eps;
+  return launch_boundary(post, fresh ? kFreshPre : kGivenPre, norm, s, f, p->workspace, p->workspace_bytes, st,
+                         "hc_boundary");
 }
 
 }  // extern "C"

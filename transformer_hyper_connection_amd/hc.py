@@ -97,9 +97,8 @@ _workspaces: dict = {}
 
 
 def workspace(n: int, hc: int, d: int, device) -> torch.Tensor | None:
-    """A zero-filled device workspace of hc_workspace_bytes(n, hc, d) bytes,
-    cached per (device, stream): libhc leaves it zero-filled after every call
-    that completes, so calls on one stream can share it."""
+    """A device workspace of at least hc_workspace_bytes(n, hc, d) bytes,
+    cached per (device, stream): calls on one stream may share it."""
     nbytes = lib().hc_workspace_bytes(n, hc, d)
     if nbytes == 0:
         return None
@@ -107,7 +106,7 @@ def workspace(n: int, hc: int, d: int, device) -> torch.Tensor | None:
     key = (dev, torch.cuda.current_stream(dev).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 
@@ -224,14 +223,12 @@ def hc_post(x, residual, post, comb):
     return out
 
 
-def hc_boundary(x, *, delta=None, post_in=None, comb_in=None, pre_in=None, fn_packed=None,
-                hc_base=None, hc_scale=None, gamma=None, iters: int = 20, hc_eps: float = 1e-6,
-                norm_eps: float = 1e-6, rms_eps: float = 1e-6, out: dict | None = None,
-                want_mixes: bool = False):
-    """One fused sublayer boundary (see include/hc.h).  Returns a dict with
-    x_out (None at a block entry), y, and pre/post/comb (+ mixes) unless
-    fn_packed is None.  ``out`` may hold preallocated outputs under the same
-    keys (and a zero-filled "workspace"); they are used as given."""
+def _prepare_boundary(x, *, delta=None, post_in=None, comb_in=None, pre_in=None, fn_packed=None,
+                      hc_base=None, hc_scale=None, gamma=None, iters: int = 20, hc_eps: float = 1e-6,
+                      norm_eps: float = 1e-6, rms_eps: float = 1e-6, out: dict | None = None,
+                      want_mixes: bool = False):
+    """Checks the arguments of one boundary call, allocates missing outputs and
+    fills the C argument struct.  Returns (struct, outputs)."""
     dev = x.device
     _need(x, "x", torch.bfloat16)
     lead, n, hc, d = _streams_shape(x)
@@ -279,5 +276,36 @@ def hc_boundary(x, *, delta=None, post_in=None, comb_in=None, pre_in=None, fn_pa
             ws = workspace(n, hc, d, dev)
         if ws is not None:
             a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
-    _check(lib().hc_boundary(ctypes.byref(a), _stream(dev)), "hc_boundary")
+            o["workspace"] = ws
+    return a, o
+
+
+def hc_boundary(x, **kw):
+    """One fused sublayer boundary (see include/hc.h).  Keyword arguments:
+    delta, post_in, comb_in, pre_in, fn_packed, hc_base, hc_scale, gamma, iters,
+    hc_eps, norm_eps, rms_eps, out, want_mixes.  Returns a dict with x_out (None
+    at a block entry), y, and pre/post/comb (+ mixes) unless fn_packed is None.
+    ``out`` may hold preallocated outputs under the same keys (and a
+    "workspace"); they are used as given."""
+    a, o = _prepare_boundary(x, **kw)
+    _check(lib().hc_boundary(ctypes.byref(a), _stream(x.device)), "hc_boundary")
     return o
+
+
+class BoundaryCall:
+    """One hc_boundary call on fixed buffers, checked once: run() enqueues it
+    again on the current stream with no per-call checking or allocation (for a
+    loop over the same buffers, such as a serving step).  The tensors given
+    and the outputs in ``outputs`` must stay alive and in place meanwhile."""
+
+    def __init__(self, x, **kw):
+        self._a, self.outputs = _prepare_boundary(x, **kw)
+        self._keep = (x, kw)
+        self._dev = x.device
+        self._fn = lib().hc_boundary
+        self._ref = ctypes.byref(self._a)
+
+    def run(self, stream: int | None = None) -> None:
+        rc = self._fn(self._ref, _stream(self._dev) if stream is None else stream)
+        if rc != HC_OK:
+            _check(rc, "hc_boundary")
