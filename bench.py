@@ -2,14 +2,20 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode fresh|lag] [--no-cpu]
 
-One step = one fused sublayer-boundary call over the whole 4096-token batch:
+One step = one sublayer-boundary call over the whole 4096-token batch (the
+prefill workload: B=1, T=4096, hc=4, d=5120, 20 Sinkhorn rounds, RMSNorm):
 hc_post(delta, X, post, comb) -> hc_mixes on X' -> split/Sinkhorn -> hc_pre ->
-RMSNorm, all inside libhc.  --mode fresh (default) reads X' with the pre this
-call derives; --mode lag reads it with the pre of the previous boundary (the
-data flow of the pages' Block.forward).  Inputs are seeded synthetic tensors
+RMSNorm.  The call is two kernels of libhc (stream_kernel, then
+finish_kernel).  --mode fresh (the default) reads X' with the pre this call
+derives; --mode lag with the pre of the previous boundary (the data flow of
+the pages' Block.forward).  Inputs are seeded synthetic tensors
 (transformer_hyper_connection_amd.synth, workload "prefill"), resident in HBM
-before timing; several input/output buffer sets rotate so that repeated steps
-do not hit in the 256 MB last-level cache.  Prints one JSON line.
+before timing; several input/output buffer sets rotate.  Prints one JSON line.
+
+Timing: W untimed warm-up steps; then K steps timed by the host clock between
+two device synchronisations (value, ms_per_step); then K more steps with
+events on the launch stream around each kernel (the roofline: algorithmic
+bytes of a call / mean event time of a call, and each kernel's share).
 """
 from __future__ import annotations
 
@@ -27,16 +33,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import transformer_hyper_connection_amd as T  # noqa: E402
-from transformer_hyper_connection_amd import synth  # noqa: E402
+from transformer_hyper_connection_amd import profsum, synth  # noqa: E402
 
 N_TOK = synth.WORKLOAD_TOKENS["prefill"]
 HC, D, MIX = 4, 5120, 24
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_boundary_prefill_t4096.json")
 # algorithmic bytes: per token  X 4*d*2 + delta d*2 + X' 4*d*2 + z d*2 (bf16)
-#                               + post_in/comb_in 16+64 (+ pre_in 16 in lag mode) + pre/post/comb out 96
+#                               + post_in/comb_in 16+64 (+ pre_in 16 with a given pre) + pre/post/comb out 96
 #                    per call   hc_fn (fp32) 24*4d*4 + base 96 + scale 12 + gamma d*4
 BYTES_TOKEN_COMMON = 4 * D * 2 + D * 2 + 4 * D * 2 + D * 2 + 16 + 64 + 96
 BYTES_CALL = MIX * 4 * D * 4 + MIX * 4 + 3 * 4 + D * 4
+KERNELS = {"fresh": ("stream_kernel<true, 2, true>", "finish_kernel<2, true>"),
+           "lag": ("stream_kernel<true, 1, true>", "finish_kernel<1, true>")}
 
 
 def algorithmic_bytes(n: int, mode: str) -> int:
@@ -67,52 +76,75 @@ def make_sets(s, dev, n_sets):
 
 
 def time_mode(mode, sets, params, steps, warmup):
-    """Times `steps` boundary calls over the rotating buffer sets.  Returns the
-    wall time, the per-call device times (events on the launch stream around
-    each call) and the host time spent enqueueing the calls."""
     stream = torch.cuda.current_stream()
+    sid = stream.cuda_stream
     calls = [T.BoundaryCall(ins["x"], delta=ins["delta"], post_in=ins["post_in"], comb_in=ins["comb_in"],
                             pre_in=ins["pre_in"] if mode == "lag" else None, out=outs, **params)
              for ins, outs in sets]
-    sid = stream.cuda_stream
     for i in range(warmup):
         calls[i % len(calls)].run(sid)
     torch.cuda.synchronize()
-    # untimed-by-events pass: how long the host takes to enqueue a call
+    # the timed steps: host clock between two synchronisations
     t0 = time.perf_counter()
     for i in range(steps):
         calls[i % len(calls)].run(sid)
-    host = time.perf_counter() - t0
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        ev[i][0].record(stream)
-        calls[(warmup + i) % len(calls)].run(sid)
-        ev[i][1].record(stream)
+    host_enqueue = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_call_ms = [a.elapsed_time(b) for a, b in ev]
-    return wall, per_call_ms, host / steps * 1e6
+    # the same steps again, each kernel bracketed by events on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        c = calls[i % len(calls)]
+        ev[i][0].record(stream)
+        c.begin(sid)
+        ev[i][1].record(stream)
+        c.end(sid)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    k1 = [e[0].elapsed_time(e[1]) for e in ev]
+    k2 = [e[1].elapsed_time(e[2]) for e in ev]
+    call = [e[0].elapsed_time(e[2]) for e in ev]
+    return {"wall_s": wall, "host_enqueue_us_per_call": host_enqueue / steps * 1e6, "call_ms": call,
+            "stream_kernel_ms": k1, "finish_kernel_ms": k2}
 
 
-def copy_bandwidth(dev, nbytes=1 << 30, reps=10):
+def reference_stream(dev, nbytes=1 << 30, reps=10):
+    """A plain streaming kernel over 1 GiB (read 1 GiB, write 1 GiB, one dispatch):
+    the practical HBM ceiling on this device, and the size reference for the
+    traffic counters."""
     a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1)
     b = torch.empty_like(a)
     for _ in range(3):
-        b.copy_(a)
+        torch.mul(a, 1, out=b)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
-        b.copy_(a)
+        torch.mul(a, 1, out=b)
     e1.record()
     torch.cuda.synchronize()
     return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
-def cpu_baseline(s, repeats=2):
+def traffic(mode):
+    """HBM bytes of one call from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None, "no counter summary"
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256") != profsum.source_sha256():
+        return None, "kernel source changed since the counters were taken"
+    total = 0
+    for want in KERNELS[mode]:
+        hit = [v for k, v in t["kernels"].items() if want in k]
+        if not hit:
+            return None, f"{want} not in the counter summary"
+        total += hit[0]["fetch_bytes"] + hit[0]["write_bytes"]
+    return total, os.path.relpath(TRAFFIC_FILE, ROOT)
+
+
+def cpu_baseline(s, repeats):
     """The CPU oracle on the same workload, timed on this host."""
     from oracle import hc_oracle as O
     try:
@@ -128,9 +160,15 @@ def cpu_baseline(s, repeats=2):
         times.append(time.perf_counter() - t0)
     med = statistics.median(times)
     return {"value": round(N_TOK / med, 1), "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"the whole {N_TOK}-token prefill batch, fresh-read boundary, median of {repeats} runs "
-                      f"({med:.2f} s each); float64 BLAS projection on {blas_threads} threads, fp32/fp64 "
-                      f"elementwise NumPy on 1 thread; host has {len(os.sched_getaffinity(0))} usable cores"}
+            "sample": f"the whole {N_TOK}-token prefill batch, fresh-read boundary with the RMSNorm, median of "
+                      f"{repeats} runs ({med:.2f} s each); float64 BLAS projection on {blas_threads} threads, "
+                      f"fp32/fp64 elementwise NumPy on 1 thread; {len(os.sched_getaffinity(0))} usable host "
+                      f"cores, os.cpu_count()={os.cpu_count()}"}
+
+
+def stats(ms):
+    return {"mean": float(np.mean(ms)), "median": float(np.median(ms)), "p10": float(np.percentile(ms, 10)),
+            "p90": float(np.percentile(ms, 90))}
 
 
 def main():
@@ -139,14 +177,15 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--mode", choices=["fresh", "lag"], default="fresh")
+    ap.add_argument("--modes", default="fresh,lag", help="read modes to time (the headline mode is always timed)")
     ap.add_argument("--sets", type=int, default=4, help="rotating input/output buffer sets")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    ap.add_argument("--modes", default="fresh,lag", help="read modes to time (the headline mode is always timed)")
-    ap.add_argument("--no-copy", action="store_true", help="skip the 1 GB device-copy reference")
+    ap.add_argument("--cpu-repeats", type=int, default=3)
+    ap.add_argument("--no-copy", action="store_true", help="skip the 1 GiB reference stream")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; the glue is per-token and would shard over "
-              "tokens with no exchange (see DESIGN.md).  Run with --gpus 1.", file=sys.stderr)
+        print("bench.py: this benchmark runs on one GPU only.  The glue is per token and would shard over "
+              "tokens with no exchange between GPUs; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
     print(f"[bench] generating the {N_TOK}-token prefill workload", file=sys.stderr, flush=True)
@@ -161,24 +200,34 @@ def main():
     modes = [args.mode] + [m for m in args.modes.split(",") if m and m != args.mode]
     for mode in modes:
         print(f"[bench] timing mode={mode}", file=sys.stderr, flush=True)
-        wall, per_call, host_us = time_mode(mode, sets, params, args.steps, args.warmup)
+        r = time_mode(mode, sets, params, args.steps, args.warmup)
         nbytes = algorithmic_bytes(N_TOK, mode)
-        med = statistics.median(per_call)
+        call = stats(r["call_ms"])
         results[mode] = {
-            "wall_s": wall, "ms_per_step": wall / args.steps * 1e3, "call_ms_median": med,
-            "call_ms_p10": float(np.percentile(per_call, 10)), "call_ms_p90": float(np.percentile(per_call, 90)),
-            "call_ms_mean": float(np.mean(per_call)), "algorithmic_bytes": nbytes,
-            "tokens_per_s": N_TOK * args.steps / wall, "gbs_at_median": nbytes / (med * 1e-3) / 1e9,
-            "host_enqueue_us_per_call": host_us,
+            "wall_s": r["wall_s"], "ms_per_step": r["wall_s"] / args.steps * 1e3,
+            "tokens_per_s": N_TOK * args.steps / r["wall_s"], "algorithmic_bytes": nbytes,
+            "call_ms": call, "stream_kernel_ms": stats(r["stream_kernel_ms"]),
+            "finish_kernel_ms": stats(r["finish_kernel_ms"]),
+            "gbs_at_mean_call": nbytes / (call["mean"] * 1e-3) / 1e9,
+            "host_enqueue_us_per_call": r["host_enqueue_us_per_call"],
         }
-    copy_gbs = None if args.no_copy else copy_bandwidth(dev)
+    ref_gbs = None if args.no_copy else reference_stream(dev)
     head = results[args.mode]
-    mean_ms = head["call_ms_mean"]
+    mean_ms = head["call_ms"]["mean"]
     achieved = head["algorithmic_bytes"] / (mean_ms * 1e-3) / 1e9
+    traffic_bytes, traffic_src = traffic(args.mode)
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(s)
+        cpu = cpu_baseline(s, args.cpu_repeats)
+
+    def rnd(v):
+        if isinstance(v, float):
+            return round(v, 5)
+        if isinstance(v, dict):
+            return {k: rnd(x) for k, x in v.items()}
+        return v
+
     line = {
         "metric": "tokens/s of fused HC sublayer boundary (T=4096); HBM GB/s as % of peak",
         "value": round(head["tokens_per_s"], 1),
@@ -190,20 +239,22 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 streams, fp32 arithmetic",
+        "dtype": "bf16 streams, fp32 arithmetic (bf16x3 split-weight MFMA projection)",
         "data": "synthetic (seeded; shapes and distributions of the prefill boundary workload)",
         "config": {"workload": "fused sublayer boundary, prefill B=1 T=4096, hc=4, d=5120, sinkhorn_iters=20, "
                                f"RMSNorm; read with the {'freshly derived' if args.mode == 'fresh' else 'previous'} pre",
                    "tokens": N_TOK, "read_mode": args.mode, "buffer_sets": args.sets},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": "hc_boundary (fused boundary call)",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_bytes,
+                     "kernel": f"hc_boundary = {KERNELS[args.mode][0]} + {KERNELS[args.mode][1]}",
                      "algorithmic_bytes_per_launch": head["algorithmic_bytes"],
-                     "avg_launch_ms": round(mean_ms, 5)},
+                     "avg_launch_ms": round(mean_ms, 5),
+                     "stream_kernel_avg_ms": round(head["stream_kernel_ms"]["mean"], 5),
+                     "finish_kernel_avg_ms": round(head["finish_kernel_ms"]["mean"], 5),
+                     "traffic_source": traffic_src},
         "cpu_baseline": cpu,
-        "modes": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                  for k, v in results.items()},
-        "copy_kernel_gbs": None if copy_gbs is None else round(copy_gbs, 1),
+        "modes": {k: rnd(v) for k, v in results.items()},
+        "reference_stream_gbs": None if ref_gbs is None else round(ref_gbs, 1),
     }
     print(json.dumps(line), flush=True)
 

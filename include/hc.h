@@ -199,6 +199,21 @@ typedef struct hc_boundary_args {
 
 int hc_boundary(const hc_boundary_args* args, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * hc_boundary_begin / hc_boundary_end -- hc_boundary in two halves, for a
+ * caller that places other work between them or times them apart.  With
+ * fn_packed, begin enqueues the streaming pass (x_out; with pre_in, y; the
+ * per-slice partial sums into the workspace) and end the finish (mixes,
+ * pre/post/comb, and the read row where it depends on them).  Without
+ * fn_packed, begin does the whole call and end does nothing.  Call end with
+ * the same arguments, on the same stream or ordered after begin; nothing may
+ * touch the workspace or the outputs in between.  Both validate as
+ * hc_boundary and return its status codes; begin followed by end computes
+ * exactly what hc_boundary does.
+ * ------------------------------------------------------------------------- */
+int hc_boundary_begin(const hc_boundary_args* args, void* stream);
+int hc_boundary_end(const hc_boundary_args* args, void* stream);
+
 /* Workspace bytes hc_boundary needs for n tokens (= hc_workspace_bytes). */
 size_t hc_boundary_workspace_bytes(int64_t n, int hc, int d);
 

@@ -150,6 +150,11 @@ def test_boundary_validation(L):
     assert call(_args(n=0)) == H.HC_OK
     assert call(_args(n=0, delta=None, post_in=None, comb_in=None, x_out=None)) == H.HC_OK
     assert call(_args(d=10304, gamma=P + 0xD00)) == H.HC_ENOTSUP   # RMSNorm row too long
+    for half in (L.hc_boundary_begin, L.hc_boundary_end):          # the halves validate alike
+        assert half(None, S) == H.HC_EINVAL
+        assert half(ctypes.byref(_args(iters=0)), S) == H.HC_EINVAL
+        assert half(ctypes.byref(_args(hc=2)), S) == H.HC_ENOTSUP
+        assert half(ctypes.byref(_args(n=0)), S) == H.HC_OK
 
 
 def test_no_device_reported_without_gpu(L):

@@ -274,6 +274,17 @@ def test_prepared_call_matches_and_repeats():
             if a.dtype == torch.bfloat16:
                 a, b = a.view(torch.int16), b.view(torch.int16)
             assert torch.equal(a, b), f"{k} differs on call {rep}"
+    # the two halves, enqueued apart, give the same bits
+    for k in ("x_out", "y", "pre", "post", "comb", "mixes"):
+        call.outputs[k].fill_(7)
+    call.begin()
+    call.end()
+    torch.cuda.synchronize()
+    for k in ("x_out", "y", "pre", "post", "comb", "mixes"):
+        a, b = call.outputs[k], ref[k]
+        if a.dtype == torch.bfloat16:
+            a, b = a.view(torch.int16), b.view(torch.int16)
+        assert torch.equal(a, b), f"{k} differs after begin/end"
 
 
 # ------------------------------------------------------------------ full size, sampled

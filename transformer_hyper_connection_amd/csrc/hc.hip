@@ -939,8 +939,9 @@ hipError_t launch_finish_t(const FinishArgs& a, unsigned grid, hipStream_t st) {
 }
 
 // s: streams, pre_in, x_out/y_out set; f: split parameters and outputs, gamma set.
+// phases: bit 0 the stream kernel, bit 1 the finish kernel.
 int launch_boundary(bool post, int rm, bool norm, StreamArgs s, FinishArgs f, void* ws, size_t ws_bytes,
-                    hipStream_t st, const char* what) {
+                    hipStream_t st, const char* what, int phases = 3) {
   const size_t need = workspace_bytes(s.n, s.d);
   if (!ws) return fail(HC_EINVAL, "%s: workspace must not be NULL (need %zu bytes)", what, need);
   if (!aligned16(ws)) return fail(HC_EINVAL, "%s: workspace is not 16-byte aligned", what);
@@ -952,8 +953,8 @@ int launch_boundary(bool post, int rm, bool norm, StreamArgs s, FinishArgs f, vo
   s.tiles = (int)tiles;
   s.rec = static_cast<float*>(ws);
   const unsigned grid1 = (unsigned)(tiles * s.S);
-  hipError_t e;
-  switch ((post ? 8 : 0) | (rm << 1) | (norm ? 1 : 0)) {
+  hipError_t e = hipSuccess;
+  if (phases & 1) switch ((post ? 8 : 0) | (rm << 1) | (norm ? 1 : 0)) {
     case 0x0: e = launch_stream_t<false, kNoRead, false>(s, grid1, st); break;
     case 0x2: e = launch_stream_t<false, kGivenPre, false>(s, grid1, st); break;
     case 0x3: e = launch_stream_t<false, kGivenPre, true>(s, grid1, st); break;
@@ -966,7 +967,7 @@ int launch_boundary(bool post, int rm, bool norm, StreamArgs s, FinishArgs f, vo
     default: return fail(HC_EINVAL, "%s: unsupported stage combination", what);
   }
   int rc = launched(e, what);
-  if (rc) return rc;
+  if (rc || !(phases & 2)) return rc;
   const bool read = rm == kFreshPre || (rm == kGivenPre && norm);
   f.rec = s.rec;
   f.n = s.n; f.d = s.d; f.S = s.S; f.tiles = s.tiles;
@@ -1122,7 +1123,7 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
 
 size_t hc_boundary_workspace_bytes(int64_t n, int hc, int d) { return hc_workspace_bytes(n, hc, d); }
 
-int hc_boundary(const hc_boundary_args* p, void* stream) {
+static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) {
   g_err[0] = 0;
   if (!p) return fail(HC_EINVAL, "args must not be NULL");
   if (p->struct_size < sizeof(hc_boundary_args))
@@ -1149,7 +1150,8 @@ int hc_boundary(const hc_boundary_args* p, void* stream) {
   if ((rc = check_device())) return rc;
   const hipStream_t st = (hipStream_t)stream;
 
-  if (!mix) {  // stack exit: write, read (+ norm); no projection
+  if (!mix) {  // stack exit: write, read (+ norm); no projection; one kernel, the first phase
+    if (!(phases & 1)) return HC_OK;
     RowArgs r{};
     r.n = p->n; r.d = p->d; r.x = p->x; r.delta = p->delta; r.post_in = p->post_in; r.comb_in = p->comb_in;
     r.pre_in = p->pre_in; r.gamma = p->gamma; r.x_out = p->x_out; r.y_out = p->y_out; r.rms_eps = p->rms_eps;
@@ -1164,7 +1166,11 @@ int hc_boundary(const hc_boundary_args* p, void* stream) {
   f.pre_out = p->pre_out; f.post_out = p->post_out; f.comb_out = p->comb_out; f.iters = p->iters;
   f.hc_eps = p->hc_eps; f.norm_eps = p->norm_eps; f.rms_eps = p->rms_eps;
   return launch_boundary(post, fresh ? kFreshPre : kGivenPre, norm, s, f, p->workspace, p->workspace_bytes, st,
-                         "hc_boundary");
+                         "hc_boundary", phases);
 }
+
+int hc_boundary(const hc_boundary_args* p, void* stream) { return boundary_phases(p, stream, 3); }
+int hc_boundary_begin(const hc_boundary_args* p, void* stream) { return boundary_phases(p, stream, 1); }
+int hc_boundary_end(const hc_boundary_args* p, void* stream) { return boundary_phases(p, stream, 2); }
 
 }  // extern "C"

@@ -58,6 +58,8 @@ SIGNATURES = {
     "hc_post": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int, c_int, c_void_p,
                         c_void_p]),
     "hc_boundary": (c_int, [ctypes.POINTER(BoundaryArgs), c_void_p]),
+    "hc_boundary_begin": (c_int, [ctypes.POINTER(BoundaryArgs), c_void_p]),
+    "hc_boundary_end": (c_int, [ctypes.POINTER(BoundaryArgs), c_void_p]),
     "hc_boundary_workspace_bytes": (c_size_t, [c_int64, c_int, c_int]),
 }
 
@@ -302,10 +304,23 @@ class BoundaryCall:
         self._a, self.outputs = _prepare_boundary(x, **kw)
         self._keep = (x, kw)
         self._dev = x.device
-        self._fn = lib().hc_boundary
+        L = lib()
+        self._fn, self._begin, self._end = L.hc_boundary, L.hc_boundary_begin, L.hc_boundary_end
         self._ref = ctypes.byref(self._a)
 
-    def run(self, stream: int | None = None) -> None:
-        rc = self._fn(self._ref, _stream(self._dev) if stream is None else stream)
+    def _go(self, fn, stream, what):
+        rc = fn(self._ref, _stream(self._dev) if stream is None else stream)
         if rc != HC_OK:
-            _check(rc, "hc_boundary")
+            _check(rc, what)
+
+    def run(self, stream: int | None = None) -> None:
+        """The whole boundary (hc_boundary)."""
+        self._go(self._fn, stream, "hc_boundary")
+
+    def begin(self, stream: int | None = None) -> None:
+        """The streaming half (hc_boundary_begin)."""
+        self._go(self._begin, stream, "hc_boundary_begin")
+
+    def end(self, stream: int | None = None) -> None:
+        """The finishing half (hc_boundary_end); after begin() on the same stream."""
+        self._go(self._end, stream, "hc_boundary_end")
