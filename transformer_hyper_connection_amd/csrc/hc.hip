@@ -446,6 +446,14 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Slot of A-operand lane L of step st in the LDS A tile.  The 8 lanes that
+// write one token's 64 features hold L = 16*g + c (g = 0..3) for both steps:
+// unswizzled, their 16-byte slots are 256 B apart, all in one bank group.
+// XOR-ing the low 3 bits with (g, st) spreads them over 8 bank groups; per
+// (step, stream) block it is a permutation that keeps each aligned group of
+// 8 lanes together, so the operand reads stay conflict-free too.
+__device__ __forceinline__ int a_swz(int L, int st) { return L ^ (((L >> 4) & 3) | (st << 2)); }
+
 // a store that the finish kernel reads back soon (kept cacheable)
 __device__ __forceinline__ void st_keep(u32x4* p, u32x4 v) { *p = v; }
 
@@ -520,11 +528,11 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
       w_lds[buf][st][k][nt][lane] = wst[i];
     }
   };
-  auto load_stream = [&](int c) {
+  auto load_stream = [&](int c, u32x4 (&dst)[kHC + 1]) {
     const unsigned f = fs + c * kCF + fl;
 #pragma unroll
-    for (int j = 0; j < kHC; ++j) cur[j] = ld_stream(reinterpret_cast<const u32x4*>(xb + (lt * kHC * d + j * d + f)));
-    cur[kHC] = POST ? ld_stream(reinterpret_cast<const u32x4*>(db + (lt * d + f))) : u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < kHC; ++j) dst[j] = ld_stream(reinterpret_cast<const u32x4*>(xb + (lt * kHC * d + j * d + f)));
+    dst[kHC] = POST ? ld_stream(reinterpret_cast<const u32x4*>(db + (lt * d + f))) : u32x4{0u, 0u, 0u, 0u};
   };
   auto stream_phase = [&](int c) {
     const unsigned f = fs + c * kCF + fl;
@@ -549,7 +557,7 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
     for (int k = 0; k < kHC; ++k) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) ssx = dot2_bf16(xp[k][e], xp[k][e], ssx);
-      a_lds[rb][a_st][k][a_lane] = u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]};
+      a_lds[rb][a_st][k][a_swz(a_lane, a_st)] = u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]};
     }
     if constexpr (RM == kGivenPre) {
       u32 yp[4];
@@ -578,27 +586,37 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
   auto matrix_phase = [&](int buf) {
 #pragma unroll
     for (int k = 0; k < kHC; ++k) {
-      const bf16x8 A = __builtin_bit_cast(bf16x8, a_lds[rb][hw][k][lane]);
+      const bf16x8 A = __builtin_bit_cast(bf16x8, a_lds[rb][hw][k][a_swz(lane, hw)]);
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt)
         acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             A, __builtin_bit_cast(bf16x8, w_lds[buf][hw][k][nt][lane]), acc[nt], 0, 0, 0);
     }
   };
-  // one chunk: its streams are in registers; the next chunk's weights (then
-  // streams) are requested before any compute of this one
+  // one chunk: its streams are in registers; the next chunk's weights are
+  // requested before any compute of this one, its streams before (given pre)
+  // or after (fresh pre) the stream phase -- the faster order of each, measured
   auto chunk = [&](int c, bool more) {
-    if (more) load_wst(c + 1);
+    constexpr bool kEarly = RM != kFreshPre;
+    u32x4 nxt[kHC + 1];
+    if (more) {
+      load_wst(c + 1);
+      if (kEarly) load_stream(c + 1, nxt);
+    }
     stream_phase(c);
-    if (more) load_stream(c + 1);
+    if (more && !kEarly) load_stream(c + 1, nxt);
     lds_barrier();                 // A tiles and chunk c's weights in place; previous matrix phase done
     if (more) store_wst((c + 1) & 1);
     matrix_phase(c & 1);
     lds_barrier();                 // matrix phase done before the A tiles are rewritten
+    if (more) {
+#pragma unroll
+      for (int j = 0; j <= kHC; ++j) cur[j] = nxt[j];
+    }
   };
 
   load_wst(0);
-  load_stream(0);
+  load_stream(0, cur);
   store_wst(0);
   lds_barrier();
   for (int c = 0; c + 1 < nch; ++c) chunk(c, true);
@@ -682,6 +700,7 @@ __global__ void __launch_bounds__(kFinThreads) finish_kernel(const FinishArgs a)
   __shared__ float tot[kTT][kRec];          // the tile's records summed over the slices
   __shared__ float s_pre[kTT][kHC];         // derived pre (fresh read)
   __shared__ float s_r[kTT];                // RMSNorm factor of the read row
+  __shared__ float g_lds[NORM ? kMaxNormD : 1];   // gamma of the read slice (F2 <= d <= kMaxNormD)
   constexpr int kUsed = rec_used<RM, NORM>();
   constexpr int kQuads = (kUsed + 3) / 4;
   const int tile = blockIdx.x / a.S2, sl2 = blockIdx.x % a.S2;
@@ -689,6 +708,9 @@ __global__ void __launch_bounds__(kFinThreads) finish_kernel(const FinishArgs a)
   const int valid = (int)min<int64_t>(kTT, a.n - t0);
   const int d = a.d, S = a.S;
 
+  if constexpr (NORM) {
+    for (int i = threadIdx.x; i < a.F2; i += kFinThreads) g_lds[i] = a.gamma[sl2 * a.F2 + i];
+  }
   // ---- sum the tile's records over the slices, in slice order
   const float* rt = a.rec + (size_t)tile * S * kTT * kRec;
   for (int cell = threadIdx.x; cell < valid * kQuads; cell += kFinThreads) {
@@ -806,7 +828,6 @@ __global__ void __launch_bounds__(kFinThreads) finish_kernel(const FinishArgs a)
     constexpr int U = RM == kFreshPre ? 5 : 8;
     for (int cb = nch; cb > 0; cb -= U) {
       u32x4 ld[U][NL];
-      f32x4 gv[U][2];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = cb - 1 - u;
@@ -814,10 +835,6 @@ __global__ void __launch_bounds__(kFinThreads) finish_kernel(const FinishArgs a)
           const unsigned f = fs + c * kCF + fl;
 #pragma unroll
           for (int k = 0; k < NL; ++k) ld[u][k] = ld_stream(reinterpret_cast<const u32x4*>(src + (k * d + f)));
-          if constexpr (NORM) {
-            gv[u][0] = *reinterpret_cast<const f32x4*>(a.gamma + f);
-            gv[u][1] = *reinterpret_cast<const f32x4*>(a.gamma + f + 4);
-          }
         }
       }
 #pragma unroll
@@ -838,8 +855,9 @@ __global__ void __launch_bounds__(kFinThreads) finish_kernel(const FinishArgs a)
             for (int e = 0; e < 4; ++e) yp[e] = ld[u][0][e];
           }
           if constexpr (NORM) {
-            const float gm[8] = {gv[u][0][0], gv[u][0][1], gv[u][0][2], gv[u][0][3],
-                                 gv[u][1][0], gv[u][1][1], gv[u][1][2], gv[u][1][3]};
+            const f32x4 g0 = *reinterpret_cast<const f32x4*>(g_lds + (f - fs));
+            const f32x4 g1 = *reinterpret_cast<const f32x4*>(g_lds + (f - fs) + 4);
+            const float gm[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2)
               yp[e2] = pack_bf16(gm[2 * e2] * (bf_lo(yp[e2]) * r), gm[2 * e2 + 1] * (bf_hi(yp[e2]) * r));
