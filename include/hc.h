@@ -172,7 +172,24 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
  * x_out must not overlap x; y_out must not overlap x, x_out or delta.
  * workspace/workspace_bytes: required when fn_packed != NULL, see
  * hc_workspace_bytes (hc_boundary_workspace_bytes returns the same size).
+ * flags: 0, or HC_BOUNDARY_SINGLE_LAUNCH for the single-launch schedule (below);
+ * a caller built against a header without this field passes the shorter
+ * struct_size and gets 0.
+ *
+ * HC_BOUNDARY_SINGLE_LAUNCH (d a multiple of 512, at least 1024): the whole
+ * call as one persistent launch that keeps X' on chip for the read row instead
+ * of re-reading it, the feature slices of a token tile exchanging per-token
+ * partial sums through the workspace as tagged words.  Its first 8 KB are then
+ * a control block that must be zero before the first such call on a workspace
+ * (each call leaves it valid for the next); byte 4160 holds a sticky error
+ * mask, bit 0 set if a wait for another workgroup's words timed out (the call
+ * then finishes with wrong results instead of hanging).  One call at a time
+ * per workspace.  Same results as the default schedule within the stated
+ * tolerances (the projection is summed over other feature slices).  Measured
+ * slower than the default on MI355X at every n tried (32..4096).
  * ------------------------------------------------------------------------- */
+#define HC_BOUNDARY_SINGLE_LAUNCH 1u
+
 typedef struct hc_boundary_args {
   uint32_t struct_size; /* = sizeof(hc_boundary_args) */
   int32_t hc, d, iters;
@@ -195,6 +212,7 @@ typedef struct hc_boundary_args {
   float* comb_out;         /* [n, hc, hc]  required iff fn_packed != NULL        */
   void* workspace;
   size_t workspace_bytes;
+  uint32_t flags;          /* 0 or HC_BOUNDARY_SINGLE_LAUNCH                     */
 } hc_boundary_args;
 
 int hc_boundary(const hc_boundary_args* args, void* stream);

@@ -66,3 +66,16 @@ def write_floor(delta_bits, x_bits, tol=N.COEF_ABS_TOL):
     D = np.abs(N.bits_to_f64(delta_bits))
     X = np.abs(N.bits_to_f64(x_bits)).sum(axis=-2)
     return (tol * (D + X))[:, None, :] * 1.0001
+
+
+ERR_WORD_BYTE = 4160    # sticky error mask in the workspace control block (bit 0: a wait timed out)
+
+
+def assert_workspace_clean(got):
+    """The single-launch boundary's error mask in the call's workspace is zero."""
+    ws = got.get("workspace") if isinstance(got, dict) else got
+    if ws is None:
+        return
+    torch.cuda.synchronize()
+    mask = int(ws[ERR_WORD_BYTE:ERR_WORD_BYTE + 4].cpu().numpy().view(np.uint32)[0])
+    assert mask == 0, f"workspace error mask {mask:#x}"

@@ -79,10 +79,13 @@ def test_packed_and_workspace_bytes(L):
     assert L.hc_workspace_bytes(0, 4, 5120) == 0
     assert L.hc_workspace_bytes(4096, 3, 5120) == 0
     w = L.hc_workspace_bytes(4096, 4, 5120)
-    # 64 tiles of 64 tokens x 4 slices x 36-float records, plus counters
-    assert 64 * 4 * 64 * 36 * 4 <= w <= 64 * 4 * 64 * 36 * 4 + 4096
+    # 8 KB control block; single-launch records: 256 tiles of 16 tokens x 10 slices x 34 tagged
+    # 8-byte words; two-launch records: 64 tiles of 64 tokens x 4 slices x 36 floats
+    assert w == 8192 + 256 * 10 * 16 * 34 * 8 + 64 * 4 * 64 * 36 * 4
     assert L.hc_boundary_workspace_bytes(4096, 4, 5120) == w
     assert L.hc_workspace_bytes(4097, 4, 5120) > w
+    # widths the single launch does not take (d % 512 != 0): control block + two-launch records only
+    assert L.hc_workspace_bytes(64, 4, 320) == 8192 + 1 * 5 * 64 * 36 * 4
 
 
 @pytest.mark.parametrize("hc,d,code", [(3, 5120, H.HC_ENOTSUP), (8, 5120, H.HC_ENOTSUP), (4, 100, H.HC_ENOTSUP),
@@ -150,6 +153,17 @@ def test_boundary_validation(L):
     assert call(_args(n=0)) == H.HC_OK
     assert call(_args(n=0, delta=None, post_in=None, comb_in=None, x_out=None)) == H.HC_OK
     assert call(_args(d=10304, gamma=P + 0xD00)) == H.HC_ENOTSUP   # RMSNorm row too long
+    # the single-launch schedule flag: unknown bits, shapes it does not take, no halves
+    SL = H.HC_BOUNDARY_SINGLE_LAUNCH
+    assert call(_args(flags=4)) == H.HC_EINVAL
+    assert call(_args(flags=SL)) == H.HC_ENOTSUP                  # d=64: not a multiple of 512
+    assert call(_args(flags=SL, d=512)) == H.HC_ENOTSUP           # at least 1024
+    assert call(_args(flags=SL, d=1024, fn_packed=None, pre_in=P + 0x600)) == H.HC_EINVAL   # needs the mixes
+    assert L.hc_boundary_begin(ctypes.byref(_args(flags=SL, d=1024)), S) == H.HC_EINVAL
+    # a caller of the struct without the trailing flags field (shorter struct_size) gets flags 0
+    short = H.BoundaryArgs.flags.offset
+    assert call(_args(struct_size=short, flags=4)) in (H.HC_ENODEV, H.HC_OK)
+    assert call(_args(struct_size=short - 8)) == H.HC_EINVAL
     for half in (L.hc_boundary_begin, L.hc_boundary_end):          # the halves validate alike
         assert half(None, S) == H.HC_EINVAL
         assert half(ctypes.byref(_args(iters=0)), S) == H.HC_EINVAL

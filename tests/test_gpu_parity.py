@@ -12,7 +12,7 @@ import torch
 from oracle import hc_oracle as O
 from tests import numerics as N
 from tests.gpu_util import (DEV, assert_bf16_close, assert_bits_equal, assert_coef_close, assert_mixes_close,
-                            bf16_dev, f32_dev, host_bits, host_f32, say, write_floor)
+                            assert_workspace_clean, bf16_dev, f32_dev, host_bits, host_f32, say, write_floor)
 from transformer_hyper_connection_amd import hc as H
 from transformer_hyper_connection_amd import synth
 
@@ -39,20 +39,23 @@ def packed(fn):
 # ------------------------------------------------------------------ packing
 @pytest.mark.parametrize("d", [64, 5120])
 def test_pack_terms_reconstruct_weight(d):
+    """Tiles 0/1/2 hold hi/mid/lo of rows 0..15 (column n = row n); tile 3 holds
+    hi of rows 16..23 in columns 0..7 and mid of rows 16..23 in columns 8..15;
+    tile 4 holds lo of rows 16..23 in columns 0..7 and zeros."""
     say(f"[pack] d={d}")
     fn, _, _ = params(d)
     p = packed(fn).cpu().numpy().view(np.uint16)
-    rec = p.reshape(d // 32, 4, 5, 64, 8)             # [step][k][tile][lane][8]
-    W = np.zeros((80, 4 * d), np.float64)
-    for st in range(d // 32):
-        for k in range(4):
-            for nt in range(5):
-                for g in range(4):
-                    rows = nt * 16 + np.arange(16)
-                    cols = k * d + st * 32 + g * 8 + np.arange(8)
-                    W[np.ix_(rows, cols)] = N.bits_to_f64(rec[st, k, nt, g * 16:(g + 1) * 16])
-    assert not W[72:].any()
-    hi, mid, lo = W[:24], W[24:48], W[48:72]
+    rec = N.bits_to_f64(p.reshape(d // 32, 4, 5, 64, 8))   # [step][k][tile][lane][8]
+    # tile[st, k, nt, col, feature-in-step]: lane = 16*g + col holds features 8g..8g+7
+    tile = rec.reshape(d // 32, 4, 5, 4, 16, 8).transpose(0, 1, 2, 4, 3, 5).reshape(d // 32, 4, 5, 16, 32)
+    def rows(nt, cols):                                 # -> [len(cols), 4*d] in feature order k*d + f
+        t = tile[:, :, nt][:, :, cols]                  # [st, k, col, 32]
+        return t.transpose(2, 1, 0, 3).reshape(len(cols), 4 * d)
+    lo8, hi8 = np.arange(8), np.arange(8, 16)
+    hi = np.concatenate([rows(0, np.arange(16)), rows(3, lo8)])
+    mid = np.concatenate([rows(1, np.arange(16)), rows(3, hi8)])
+    lo = np.concatenate([rows(2, np.arange(16)), rows(4, lo8)])
+    assert not rows(4, hi8).any()
     thi = torch.from_numpy(fn).to(torch.bfloat16).float().numpy()
     assert np.array_equal(hi, thi)                      # hi = nearest bf16 of w
     err = np.abs(hi + mid + lo - fn.astype(np.float64))
@@ -142,7 +145,7 @@ def test_step_workload():
 
 
 # ------------------------------------------------------------------ fused boundary
-def _boundary_case(workload, t0, t1, fresh, norm, entry=False, exit_=False, d=None):
+def _boundary_case(workload, t0, t1, fresh, norm, entry=False, exit_=False, d=None, single=False):
     s = synth.boundary_inputs(workload, t0, t1) if d is None else synth.boundary_inputs(workload, t0, t1, d)
     kw = dict(x=s["x"], pre_in=None if fresh else s["pre_in"], gamma=s["gamma"] if norm else None)
     if not entry:
@@ -155,11 +158,12 @@ def _boundary_case(workload, t0, t1, fresh, norm, entry=False, exit_=False, d=No
     if "hc_fn" in kw:
         dev["fn_packed"] = packed(kw["hc_fn"])
     x = dev.pop("x")
-    got = H.hc_boundary(x, **dev, want_mixes=not exit_)
+    got = H.hc_boundary(x, **dev, want_mixes=not exit_, single_launch=single)
     return ref, got, s
 
 
 def _check_boundary(ref, got, s, fresh, norm):
+    assert_workspace_clean(got)
     if ref["x_out"] is not None:
         assert_bits_equal(host_bits(got["x_out"]), ref["x_out"], "x_out")
     if ref["mixes"] is not None:
@@ -187,18 +191,54 @@ def _check_boundary(ref, got, s, fresh, norm):
         assert_bits_equal(y, ref["y"], "y")
 
 
+@pytest.mark.parametrize("single", [False, True])
 @pytest.mark.parametrize("fresh", [False, True])
 @pytest.mark.parametrize("norm", [False, True])
-def test_boundary_small(fresh, norm):
-    say(f"[boundary] prefill tokens 0..40 fresh={fresh} norm={norm}")
-    ref, got, s = _boundary_case("prefill", 0, 40, fresh, norm)
+def test_boundary_small(fresh, norm, single):
+    say(f"[boundary] prefill tokens 0..40 fresh={fresh} norm={norm} single_launch={single}")
+    ref, got, s = _boundary_case("prefill", 0, 40, fresh, norm, single=single)
     _check_boundary(ref, got, s, fresh, norm)
 
 
+@pytest.mark.parametrize("single", [False, True])
+@pytest.mark.parametrize("n,d", [(1, 5120), (17, 1024), (23, 7168), (130, 2048)])
 @pytest.mark.parametrize("fresh", [False, True])
-def test_boundary_entry(fresh):
-    say(f"[boundary entry] fresh={fresh}")
-    ref, got, s = _boundary_case("prefill", 100, 133, fresh, True, entry=True)
+def test_boundary_shapes(n, d, fresh, single):
+    """Other widths and ragged token counts, both schedules."""
+    say(f"[boundary] n={n} d={d} fresh={fresh} single_launch={single}")
+    ref, got, s = _boundary_case("prefill", 0, n, fresh, True, d=d, single=single)
+    _check_boundary(ref, got, s, fresh, True)
+
+
+def test_boundary_repeated_calls_one_workspace():
+    """Consecutive single-launch calls on one workspace (each call advances the
+    call tag the exchange words carry) give the same bits each time, with no
+    wait timed out."""
+    say("[boundary] 5 single-launch calls on one workspace, fresh read")
+    s = synth.boundary_inputs("prefill", 0, 70)
+    dev = dict(delta=bf16_dev(s["delta"]), post_in=f32_dev(s["post_in"]), comb_in=f32_dev(s["comb_in"]),
+               fn_packed=packed(s["hc_fn"]), hc_base=f32_dev(s["hc_base"]), hc_scale=f32_dev(s["hc_scale"]),
+               gamma=f32_dev(s["gamma"]))
+    X = bf16_dev(s["x"])
+    first = None
+    for rep in range(5):
+        got = H.hc_boundary(X, **dev, want_mixes=True, single_launch=True)
+        torch.cuda.synchronize()
+        assert_workspace_clean(got)
+        cur = {k: host_bits(got[k]) if got[k].dtype == torch.bfloat16 else host_f32(got[k])
+               for k in ("x_out", "y", "pre", "post", "comb", "mixes")}
+        if first is None:
+            first = cur
+        else:
+            for k in cur:
+                assert np.array_equal(cur[k], first[k]), f"call {rep}: {k} differs from call 0"
+
+
+@pytest.mark.parametrize("single", [False, True])
+@pytest.mark.parametrize("fresh", [False, True])
+def test_boundary_entry(fresh, single):
+    say(f"[boundary entry] fresh={fresh} single_launch={single}")
+    ref, got, s = _boundary_case("prefill", 100, 133, fresh, True, entry=True, single=single)
     assert got["x_out"] is None
     _check_boundary(ref, got, s, fresh, True)
 
@@ -215,8 +255,9 @@ def test_boundary_stress_outliers_small():
     _check_boundary(ref, got, s, False, True)
 
 
-def test_boundary_deterministic_and_guarded():
-    say("[boundary] determinism + guard bands")
+@pytest.mark.parametrize("single", [False, True])
+def test_boundary_deterministic_and_guarded(single):
+    say(f"[boundary] determinism + guard bands, single_launch={single}")
     s = synth.boundary_inputs("prefill", 0, 33)
     n, d = 33, 5120
     guard = 4096
@@ -242,7 +283,7 @@ def test_boundary_deterministic_and_guarded():
             if b.dtype == torch.int16:
                 v = v.view(torch.bfloat16)
             views[k] = v.view(shapes[k])
-        H.hc_boundary(X, **dev, out=views)
+        H.hc_boundary(X, **dev, out=views, single_launch=single)
         torch.cuda.synchronize()
         for k, b in bufs.items():
             fill = 0x7A7A if b.dtype == torch.int16 else 7.5
@@ -274,17 +315,21 @@ def test_prepared_call_matches_and_repeats():
             if a.dtype == torch.bfloat16:
                 a, b = a.view(torch.int16), b.view(torch.int16)
             assert torch.equal(a, b), f"{k} differs on call {rep}"
-    # the two halves, enqueued apart, give the same bits
+    # the two-launch split (hc_boundary_begin + _end, enqueued apart) sums the
+    # projection over other feature slices: the same X', the other outputs within
+    # the parity bars of the oracle
     for k in ("x_out", "y", "pre", "post", "comb", "mixes"):
         call.outputs[k].fill_(7)
     call.begin()
     call.end()
     torch.cuda.synchronize()
-    for k in ("x_out", "y", "pre", "post", "comb", "mixes"):
-        a, b = call.outputs[k], ref[k]
-        if a.dtype == torch.bfloat16:
-            a, b = a.view(torch.int16), b.view(torch.int16)
-        assert torch.equal(a, b), f"{k} differs after begin/end"
+    assert torch.equal(call.outputs["x_out"].view(torch.int16), ref["x_out"].view(torch.int16))
+    kw = dict(x=s["x"], delta=s["delta"], post_in=s["post_in"], comb_in=s["comb_in"], pre_in=None,
+              hc_fn=s["hc_fn"], hc_base=s["hc_base"], hc_scale=s["hc_scale"], gamma=s["gamma"])
+    oref = O.boundary(**kw)
+    split = dict(call.outputs)
+    split["workspace"] = None
+    _check_boundary(oref, split, s, True, True)
 
 
 # ------------------------------------------------------------------ full size, sampled
@@ -292,8 +337,9 @@ SAMPLE_RANGES = [(0, 3), (15, 18), (2047, 2049), (4093, 4096)]
 
 
 @pytest.mark.parametrize("fresh", [False, True])
-def test_prefill_full_size_sampled(fresh):
-    say(f"[prefill n=4096] fresh={fresh}: generating inputs")
+@pytest.mark.parametrize("single", [False, True])
+def test_prefill_full_size_sampled(fresh, single):
+    say(f"[prefill n=4096] fresh={fresh} single_launch={single}: generating inputs")
     n = 4096
     s = synth.boundary_inputs("prefill")
     X = bf16_dev(s["x"])
@@ -301,8 +347,9 @@ def test_prefill_full_size_sampled(fresh):
                pre_in=None if fresh else f32_dev(s["pre_in"]), fn_packed=packed(s["hc_fn"]),
                hc_base=f32_dev(s["hc_base"]), hc_scale=f32_dev(s["hc_scale"]), gamma=f32_dev(s["gamma"]))
     say("  launching")
-    got = H.hc_boundary(X, **dev, want_mixes=True)
+    got = H.hc_boundary(X, **dev, want_mixes=True, single_launch=single)
     torch.cuda.synchronize()
+    assert_workspace_clean(got)
     for a, b in SAMPLE_RANGES:
         say(f"  oracle tokens {a}..{b}")
         ref = O.boundary(x=s["x"][a:b], delta=s["delta"][a:b], post_in=s["post_in"][a:b],

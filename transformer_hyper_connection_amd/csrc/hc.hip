@@ -25,6 +25,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdint>
+#include <cstddef>
 #include <cstdio>
 
 #include "hc.h"
@@ -33,8 +34,8 @@ namespace {
 
 constexpr int kHC = 4;
 constexpr int kMix = (2 + kHC) * kHC;  // 24 mix numbers
-constexpr int kSplitRows = 3 * kMix;   // 72 = hi | mid | lo rows of the packed weight
-constexpr int kNT = 5;                 // 16-column matrix tiles covering 72 (+8 zero) rows
+constexpr int kNT = 5;                 // packed 16-column weight tiles per 32-feature step and stream
+constexpr int kAcc = 2;                // accumulator tiles: rows 0..15, and rows 16..23 (two halves)
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kFPL = 8;                // features per lane per matrix-core step
@@ -157,13 +158,28 @@ __global__ void __launch_bounds__(256) split_kernel(const float* __restrict__ mi
 }
 
 // ------------------------------------------------------------------ weight pack
+// Each fp32 weight w is split into three bf16 terms, w = hi + mid + lo, each
+// the nearest-even rounding of what is left (exact but for subnormal tails).
 // Packed layout, in 16-byte lane records:
 //   [step = f/32][stream k][tile nt][lane 0..63] -> 8 bf16
-// record (step, k, nt, lane) holds split row qs = 16*nt + lane%16 at features
-// k*d + 32*step + 8*(lane/16) + 0..7.  Split row qs < 24 is the hi term of
-// projection row qs, 24..47 the mid term of row qs-24, 48..71 the lo term of
-// row qs-48, 72..79 zero.  One 1 KB (step, k, nt) block is the B operand of one
-// 16x16x32 matrix-core instruction.
+// record (step, k, nt, lane) holds, for column n = lane%16, the terms of one
+// projection row at features k*d + 32*step + 8*(lane/16) + 0..7:
+//   nt 0/1/2: hi/mid/lo of row n                      (accumulator tile 0)
+//   nt 3:     hi of row 16+n (n < 8), mid of row 8+n  (accumulator tile 1)
+//   nt 4:     lo of row 16+n (n < 8), zero            (accumulator tile 1)
+// so that the three terms of a row meet in one accumulator column (tile 0),
+// or in columns n and n+8 of tile 1 (summed once per token at the end).  One
+// 1 KB (step, k, nt) block is the B operand of one 16x16x32 matrix-core
+// instruction for a 64-lane wave.
+__device__ __forceinline__ float split_term(float x, int part) {
+  const float hi = round_bf16(x);
+  if (part == 0) return hi;
+  const float r1 = x - hi;  // exact
+  const float mid = round_bf16(r1);
+  if (part == 1) return mid;
+  return round_bf16(r1 - mid);  // r1 - mid exact
+}
+
 __global__ void __launch_bounds__(256) pack_kernel(const float* __restrict__ fn, int d,
                                                    u32x4* __restrict__ out, int records) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
@@ -172,30 +188,32 @@ __global__ void __launch_bounds__(256) pack_kernel(const float* __restrict__ fn,
   const int nt = (idx >> 6) % kNT;
   const int k = (idx / (64 * kNT)) % kHC;
   const int step = idx / (64 * kNT * kHC);
-  const int qs = nt * 16 + (lane & 15);
-  const int part = qs / kMix;  // 0 hi, 1 mid, 2 lo, 3 zero
-  const int q = qs % kMix;
+  const int n = lane & 15;
+  int q, part;                       // projection row and split term; q < 0: zero
+  if (nt < 3) { q = n; part = nt; }
+  else if (nt == 3) { q = n < 8 ? 16 + n : 8 + n; part = n < 8 ? 0 : 1; }
+  else { q = n < 8 ? 16 + n : -1; part = 2; }
   const int f0 = step * kStepF + (lane >> 4) * kFPL;
   u32 w[4];
 #pragma unroll
   for (int e2 = 0; e2 < 4; ++e2) {
     float v[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float r = 0.f;
-      if (part < 3) {
-        const float x = fn[(size_t)q * (kHC * d) + (size_t)k * d + f0 + 2 * e2 + h];
-        const float hi = round_bf16(x);
-        const float r1 = x - hi;  // exact
-        const float mid = round_bf16(r1);
-        const float r2 = r1 - mid;  // exact
-        r = part == 0 ? hi : (part == 1 ? mid : round_bf16(r2));
-      }
-      v[h] = r;
-    }
+    for (int h = 0; h < 2; ++h)
+      v[h] = q < 0 ? 0.f : split_term(fn[(size_t)q * (kHC * d) + (size_t)k * d + f0 + 2 * e2 + h], part);
     w[e2] = pack_bf16(v[0], v[1]);
   }
   out[idx] = u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// The matrix-core step for one (A tile, 32-feature step, stream): the five
+// weight tiles into the two accumulator tiles.
+__device__ __forceinline__ void mfma_step(const bf16x8 A, const bf16x8 (&B)[kNT], f32x4 (&acc)[kAcc]) {
+  acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[0], acc[0], 0, 0, 0);
+  acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[1], acc[0], 0, 0, 0);
+  acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[2], acc[0], 0, 0, 0);
+  acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[3], acc[1], 0, 0, 0);
+  acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[4], acc[1], 0, 0, 0);
 }
 
 // ================================================================ row kernel
@@ -503,9 +521,9 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
 
   u32x4 cur[kHC + 1];
   u32x4 wst[kNT];  // this wave's share (5 of 40 blocks) of the next chunk's weight tiles
-  f32x4 acc[kNT];
+  f32x4 acc[kAcc];
 #pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < kAcc; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float ssx = 0.f, ssy = 0.f;
   float gram[kGram];
 #pragma unroll
@@ -587,10 +605,10 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
 #pragma unroll
     for (int k = 0; k < kHC; ++k) {
       const bf16x8 A = __builtin_bit_cast(bf16x8, a_lds[rb][hw][k][a_swz(lane, hw)]);
+      bf16x8 B[kNT];
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt)
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            A, __builtin_bit_cast(bf16x8, w_lds[buf][hw][k][nt][lane]), acc[nt], 0, 0, 0);
+      for (int nt = 0; nt < kNT; ++nt) B[nt] = __builtin_bit_cast(bf16x8, w_lds[buf][hw][k][nt][lane]);
+      mfma_step(A, B, acc);
     }
   };
   // one chunk: its streams are in registers; the next chunk's weights are
@@ -632,13 +650,13 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
       for (int g = 0; g < kGram; ++g) gram[g] += __shfl_xor(gram[g], o);
     }
   }
-  float* red = reinterpret_cast<float*>(&w_lds[0][0][0][0][0]);   // [4 rb][2 steps][16][80] | extra
+  float* red = reinterpret_cast<float*>(&w_lds[0][0][0][0][0]);   // [4 rb][2 steps][16][32] | extra
 #pragma unroll
-  for (int nt = 0; nt < kNT; ++nt)
+  for (int t = 0; t < kAcc; ++t)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
-      red[((rb * 2 + hw) * 16 + 4 * (lane >> 4) + rr) * 80 + nt * 16 + (lane & 15)] = acc[nt][rr];
-  float* extra = red + 4 * 2 * 16 * 80;                            // [kRec - kMix][kTT]
+      red[((rb * 2 + hw) * 16 + 4 * (lane >> 4) + rr) * 32 + t * 16 + (lane & 15)] = acc[t][rr];
+  float* extra = red + 4 * 2 * 16 * 32;                            // [kRec - kMix][kTT]
   if ((lane & 7) == 0) {
     extra[m] = ssx;
     if constexpr (RM == kGivenPre && NORM) extra[kTT + m] = ssy;
@@ -656,9 +674,9 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
     for (int i = 0; i < 4; ++i) {
       const int q = q0 + i;
       if (q < kMix) {
-        const float* r0 = red + ((tm >> 4) * 2 * 16 + (tm & 15)) * 80;   // step 0
-        const float* r1 = r0 + 16 * 80;                                 // step 1
-        v[i] = ((r0[q] + r0[kMix + q]) + r0[2 * kMix + q]) + ((r1[q] + r1[kMix + q]) + r1[2 * kMix + q]);
+        const float* r0 = red + ((tm >> 4) * 2 * 16 + (tm & 15)) * 32;   // step 0
+        const float* r1 = r0 + 16 * 32;                                 // step 1
+        v[i] = q < 16 ? r0[q] + r1[q] : (r0[q] + r0[q + 8]) + (r1[q] + r1[q + 8]);
       } else {
         v[i] = q < kUsed ? extra[(q - kMix) * kTT + tm] : 0.f;
       }
@@ -869,6 +887,608 @@ __global__ void __launch_bounds__(kFinThreads) finish_kernel(const FinishArgs a)
   }
 }
 
+// ======================================================= single-launch boundary
+// fused_kernel<POST, RM, NORM>: the sublayer boundary in one launch, X' written
+// once and read from the chip ("Source layer, pairs pooled": Block.forward).
+//
+// Work items are (tile of kFT = 16 tokens, slice of kFF = 512 features of each
+// stream); the S = d/512 slices of a tile run on different workgroups.  The grid
+// is persistent, one workgroup per compute unit, every workgroup resident, and a
+// multiple of S; it walks the items in rounds, item r*G + w in round r, so the
+// slices of a tile share a round.
+//
+// Segment k of a workgroup (one barrier between segments):
+//   stream waves (8): the read row of item k-2 from its kept X' tile (its
+//     coefficients were derived in segment k-1) -> z; then X' of item k =
+//     hc_post(...) from the loads issued in segment k-1.  The loads of item k+1
+//     go out before any store of item k (one vector-memory counter orders them);
+//     X' is stored, put in the LDS A tile of item k (kept for its read row) and
+//     its Gram entries summed.
+//   matrix waves (4), at the same time: the 24 projection dots of item k-1 on
+//     the matrix cores (weight tiles streamed from L2 into registers); publish
+//     item k-1's per-token record (dots + Gram) for the other slices of its tile;
+//     the outputs (mixes, pre/post, Sinkhorn comb) of the tokens this slice owns
+//     in item k-2 (all 34 words of all S slices, written a segment earlier); the
+//     read coefficients of item k-1: the 14 words the read needs (4 pre dots +
+//     Gram), summed over the S slices in slice order by every slice workgroup of
+//     the tile (the same bits everywhere) -> pre and the RMSNorm factor.
+// Records travel through the workspace as 64-bit words (value, call tag): a word
+// is valid when its tag is this call's, so no ordering between words is needed
+// and no writer waits.  A reader polls until valid, a bounded number of times;
+// a timeout sets an error flag instead of hanging.
+constexpr int kFT = 16;                      // tokens per tile
+constexpr int kFF = 512;                     // features per slice and stream
+constexpr int kFSW = 8;                      // stream waves
+constexpr int kFMW = 4;                      // matrix waves
+constexpr int kFThreads = (kFSW + kFMW) * 64;
+constexpr int kFKS = kFF / kStepF;           // 32-feature steps per slice (16)
+constexpr int kFKB = kFKS * kHC;             // matrix-core K blocks per item (64)
+constexpr int kFKBW = kFKB / kFMW;           // per matrix wave (16)
+constexpr int kFPre = 4;                     // weight blocks in flight per matrix wave
+constexpr int kFRec = 34;                    // record words per token and slice
+constexpr int kFCoef = 5;                    // read coefficients per token: pre[4], RMSNorm factor
+constexpr int kFMinD = 2 * kFF;              // S >= 2: at most 8 owned tokens per slice
+constexpr int kFPollBatch = 10;              // slices polled per batch
+constexpr int kCtrlBytes = 8192;             // control block at the head of the workspace
+constexpr int kEpochCopies = 64;             // epoch word copies, 64 bytes apart
+constexpr int kDoneWord = 1024, kErrWord = 1040;
+constexpr unsigned kPollLimit = 1u << 14;    // polls of one word (about 1 us each) before a wait gives up
+constexpr int64_t kFusedMaxN = (int64_t)1 << 26;   // item indices stay in int
+typedef unsigned long long u64;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+enum : unsigned { kErrPollTimeout = 1u };
+
+struct FusedArgs {
+  const hc_bf16* x;
+  const hc_bf16* delta;
+  const float* post_in;
+  const float* comb_in;
+  const float* pre_in;
+  const u32x4* fn;
+  const float* gamma;
+  const float* hc_base;
+  const float* hc_scale;
+  hc_bf16* x_out;
+  hc_bf16* y_out;
+  float* mixes_out;
+  float* pre_out;
+  float* post_out;
+  float* comb_out;
+  u32* ctrl;          // workspace head (kCtrlBytes)
+  u64* rec;           // [tiles][S][kFT][kFRec] tagged words
+  int64_t n;
+  int d, S, tiles, items, rounds, iters;
+  float hc_eps, norm_eps, rms_eps;
+};
+
+// record word order per read mode: fresh [pre dots 0..3 | Gram 10 | dots 4..23];
+// given pre with RMSNorm [sum y^2 | sum x'^2 | dots]; otherwise [sum x'^2 | dots]
+template <int RM, bool NORM> constexpr int f_fast() { return RM == kFreshPre ? kHC + kGram : (RM == kGivenPre && NORM ? 1 : 0); }
+template <int RM, bool NORM> __device__ __forceinline__ int f_dot(int q) {
+  if constexpr (RM == kFreshPre) return q < kHC ? q : q + kGram;
+  else return q + (NORM && RM == kGivenPre ? 2 : 1);
+}
+template <int RM, bool NORM> constexpr int f_ssx() { return RM == kGivenPre && NORM ? 1 : 0; }   // (not fresh)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, u32 bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld(rsrc_t r, u32 off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2); }
+__device__ __forceinline__ void buf_st(rsrc_t r, u32 off, u32x4 v) { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 2); }
+
+__device__ __forceinline__ u64 tag_word(float v, u32 tag) { return ((u64)tag << 32) | __float_as_uint(v); }
+__device__ __forceinline__ void put_word(u64* p, u64 w) { __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ u64 get_word(const u64* p) { return __hip_atomic_load(const_cast<u64*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+// The word's value once its tag is this call's, polled again as needed.  After
+// a wait of this lane has timed out (dead), no further waiting: the call then
+// finishes quickly with the error flag set rather than polling on.
+__device__ __forceinline__ float settle(const u64* p, u64 w, u32 tag, u32* err, bool& dead) {
+  unsigned polls = 0;
+  while ((u32)(w >> 32) != tag && !dead) {
+    if (++polls > kPollLimit) { atomicOr(err, kErrPollTimeout); dead = true; break; }
+    __builtin_amdgcn_s_sleep(8);
+    w = get_word(p);
+  }
+  return __uint_as_float((u32)w);
+}
+
+// A-tile slot of matrix-core lane L at step parity st: the low 4 bits are
+// XOR-ed with (2*(L/16) | st), a permutation within each 16-slot group, so that
+// the 8 lanes writing one token's 64 features hit 8 different bank groups.
+__device__ __forceinline__ int f_swz(int L, int st) { return (L & 48) | ((L & 15) ^ (((L >> 4) << 1) | st)); }
+
+// One token's mixes / pre / post / comb from its summed record (in LDS, record
+// word order), 4 lanes (one quad) per token, lane j holding comb row j
+// ("Reading weights" kernel panel and reading-weight equation).  All four lanes
+// of the quad call it.
+template <int RM, bool NORM>
+__device__ __forceinline__ void derive_outputs(const float* fs, float rx, int j, const FusedArgs& a, int64_t t) {
+  if (a.mixes_out) {
+#pragma unroll
+    for (int i = 0; i < kMix / kHC; ++i) a.mixes_out[t * kMix + i * kHC + j] = fs[f_dot<RM, NORM>(i * kHC + j)] * rx;
+  }
+  const float s0 = a.hc_scale[0], s1 = a.hc_scale[1], s2 = a.hc_scale[2];
+  const float pre = sigmoidf_((fs[f_dot<RM, NORM>(j)] * rx) * s0 + a.hc_base[j]) + a.hc_eps;
+  const float post = 2.0f * sigmoidf_((fs[f_dot<RM, NORM>(kHC + j)] * rx) * s1 + a.hc_base[kHC + j]);
+  float A[kHC];
+  float mxr = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kHC; ++k) {
+    const int q = 2 * kHC + j * kHC + k;
+    A[k] = (fs[f_dot<RM, NORM>(q)] * rx) * s2 + a.hc_base[q];
+    mxr = fmaxf(mxr, A[k]);
+  }
+  float rsum = 0.f;
+#pragma unroll
+  for (int k = 0; k < kHC; ++k) {
+    A[k] = expf(A[k] - mxr);
+    rsum = rsum + A[k];
+  }
+  const float rinv = __builtin_amdgcn_rcpf(rsum);
+#pragma unroll
+  for (int k = 0; k < kHC; ++k) A[k] = A[k] * rinv + a.hc_eps;
+  auto col_norm = [&]() {
+#pragma unroll
+    for (int k = 0; k < kHC; ++k) A[k] = A[k] * __builtin_amdgcn_rcpf(quad_sum(A[k]) + a.hc_eps);
+  };
+  col_norm();
+  for (int it = 1; it < a.iters; ++it) {
+    const float inv = __builtin_amdgcn_rcpf(((A[0] + A[1]) + A[2]) + A[3] + a.hc_eps);
+#pragma unroll
+    for (int k = 0; k < kHC; ++k) A[k] = A[k] * inv;
+    col_norm();
+  }
+  a.pre_out[t * kHC + j] = pre;
+  a.post_out[t * kHC + j] = post;
+  *reinterpret_cast<f32x4*>(a.comb_out + t * kHC * kHC + j * kHC) = f32x4{A[0], A[1], A[2], A[3]};
+}
+
+template <bool POST, int RM, bool NORM>
+__global__ void __launch_bounds__(kFThreads, 1) fused_kernel(const FusedArgs a) {
+  constexpr bool kFresh = RM == kFreshPre;
+  constexpr bool kKeepY = RM == kGivenPre && NORM;       // y kept (registers) for the RMSNorm
+  constexpr bool kFinish = kFresh || kKeepY;             // a read row is written after the exchange
+  constexpr int kFast = f_fast<RM, NORM>();
+  // LDS
+  __shared__ u32x4 A_lds[2][kHC][kFKS][64];              // X' in matrix-core A layout, items k and k-1 (128 KB)
+  __shared__ float red[kFMW][kFT][kMix];                 // per-matrix-wave partial dots
+  __shared__ float gred[2][4][kFT][kGram + 2];           // per-chunk-pair Gram / sum x'^2 / sum y^2, by item parity
+  __shared__ float cin[2][kFT][kHC + kHC * kHC + kHC];   // post_in, comb_in, pre_in of the streamed item
+  __shared__ float gam[2][NORM ? kFF : 1];               // RMSNorm gain of the item being read
+  __shared__ float coef[2][kFT][kFCoef];                 // read coefficients (pre, RMSNorm factor)
+  __shared__ float fsum[kFMW][kFT / kFMW][kFRec];        // matrix-wave scratch: summed record words
+  __shared__ u32 mcount;                                 // matrix-wave barrier counter
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int G = gridDim.x, w = blockIdx.x, S = a.S, d = a.d;
+  u32* err = a.ctrl + kErrWord;
+  const u32 epoch = __hip_atomic_load(a.ctrl + 16 * (w % kEpochCopies), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const u32 tag = epoch + 1u == 0u ? 1u : epoch + 1u;
+  if (threadIdx.x == 0) mcount = 0;
+
+  // Position of this workgroup in a round: consecutive workgroups land on
+  // different XCDs (round-robin), so they are renumbered XCD by XCD; items are
+  // taken slice-major, position g -> (tile r*TPR + g%TPR, slice g/TPR), TPR = G/S
+  // tiles per round.  A workgroup keeps its slice in every round, and the
+  // workgroups of one XCD share one or two slices: their weight tiles stay in
+  // that XCD's L2.  (Any bijection is correct; this one is for locality.)
+  const int xcd = w & 7, xq = G >> 3, xr = G & 7;
+  const int g_pos = xcd * xq + min(xcd, xr) + (w >> 3);
+  const int TPR = G / S;
+  struct Item { int tile, slice, valid; };
+  auto item_of = [&](int r) {
+    Item it;
+    const int tile = r * TPR + g_pos % TPR;
+    const bool ok = r >= 0 && r < a.rounds && tile < a.tiles;
+    it.tile = ok ? tile : 0;
+    it.slice = g_pos / TPR;
+    it.valid = ok ? (int)min<int64_t>(kFT, a.n - (int64_t)tile * kFT) : 0;
+    return it;
+  };
+  const u32 xrow = (u32)(kHC * d * 2), drow = (u32)(d * 2);
+  const int K = a.rounds + 2;                            // segments: stream k, matrix k-1, read k-2
+
+  if (wave < kFSW) {
+    // ======================================================== stream waves
+    // segment k: the read row of item k-2, then X' of item k
+    const int tg = wave & 1, cp = wave >> 1;
+    const int tl = lane >> 3, p = lane & 7;
+    const int m = 8 * tg + tl;                             // token of the tile
+    struct Res { rsrc_t x, dl, xo, yo; u32 fbyte; };
+    auto res_of = [&](const Item& it) {
+      Res q;
+      const int64_t t0 = (int64_t)it.tile * kFT;
+      q.x = make_rsrc(a.x + t0 * kHC * d, it.valid * xrow);
+      q.dl = make_rsrc(POST ? a.delta + t0 * d : a.x, POST ? it.valid * drow : 0);
+      q.xo = make_rsrc(POST ? a.x_out + t0 * kHC * d : a.x, POST ? it.valid * xrow : 0);
+      q.yo = make_rsrc(a.y_out + t0 * d, it.valid * drow);
+      q.fbyte = (u32)(it.slice * kFF + 2 * cp * 64 + 8 * p) * 2;
+      return q;
+    };
+    u32x4 L[2][kHC + 1];
+    auto issue = [&](const Res& q) {
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const u32 o = (u32)m * xrow + q.fbyte + cc * 128;
+#pragma unroll
+        for (int j = 0; j < kHC; ++j) L[cc][j] = buf_ld(q.x, o + j * drow);
+        L[cc][kHC] = POST ? buf_ld(q.dl, (u32)m * drow + q.fbyte + cc * 128) : u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+    u32 yk1[2][4], yk2[2][4];                            // given pre + RMSNorm: y of items k-1, k-2
+    Res rc = res_of(item_of(0));
+    issue(rc);
+    __syncthreads();                                     // P: cin of item 0 in place
+    for (int k = 0; k < K; ++k) {
+      // ---- the read row of item k-2 (its coefficients arrived with the last barrier)
+      if constexpr (kFinish) {
+        const Res rp = res_of(item_of(k - 2));
+        const int pb = k & 1;                            // (k-2) & 1
+        const float* cf = coef[pb][m];
+        float pr[kHC];
+#pragma unroll
+        for (int j = 0; j < kHC; ++j) pr[j] = cf[j];
+        const float rn = NORM ? cf[kHC] : 1.f;
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          u32 yv[4];
+          if constexpr (kFresh) {
+            const int ks = 2 * (2 * cp + cc) + (p >> 2);
+            const int slot = f_swz(16 * (p & 3) + m, ks & 1);
+            u32 xv[kHC][4];
+#pragma unroll
+            for (int kk = 0; kk < kHC; ++kk) {
+              const u32x4 v = A_lds[pb][kk][ks][slot];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) xv[kk][e] = v[e];
+            }
+            pre_8(xv, pr, yv);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) yv[e] = yk2[cc][e];
+          }
+          if constexpr (NORM) {
+            const float* gm = gam[pb] + (2 * cp + cc) * 64 + 8 * p;
+            const f32x4 g0 = *reinterpret_cast<const f32x4*>(gm);
+            const f32x4 g1 = *reinterpret_cast<const f32x4*>(gm + 4);
+            const float gg[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2)
+              yv[e2] = pack_bf16(gg[2 * e2] * (bf_lo(yv[e2]) * rn), gg[2 * e2 + 1] * (bf_hi(yv[e2]) * rn));
+          }
+          buf_st(rp.yo, (u32)m * drow + rp.fbyte + cc * 128, u32x4{yv[0], yv[1], yv[2], yv[3]});
+        }
+      }
+      // ---- X' of item k
+      const Res rn_ = res_of(item_of(k + 1));
+      const int sl = k & 1;
+      const float* ci = cin[k & 1][m];
+      float cpost[kHC], ccomb[kHC * kHC], cpre[kHC];
+#pragma unroll
+      for (int j = 0; j < kHC; ++j) { cpost[j] = ci[j]; cpre[j] = ci[kHC + kHC * kHC + j]; }
+#pragma unroll
+      for (int j = 0; j < kHC * kHC; ++j) ccomb[j] = ci[kHC + j];
+      u32 xp[2][kHC][4];
+      u32 yp[2][4];
+      float g[kGram + 2];
+#pragma unroll
+      for (int i = 0; i < kGram + 2; ++i) g[i] = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        if constexpr (POST) {
+          post_8(L[cc], cpost, ccomb, xp[cc]);
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < kHC; ++kk)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xp[cc][kk][e] = L[cc][kk][e];
+        }
+        if constexpr (kFresh) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            int gi = 0;
+#pragma unroll
+            for (int j = 0; j < kHC; ++j)
+#pragma unroll
+              for (int l = j; l < kHC; ++l, ++gi) g[gi] = dot2_bf16(xp[cc][j][e], xp[cc][l][e], g[gi]);
+          }
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < kHC; ++kk)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) g[kGram] = dot2_bf16(xp[cc][kk][e], xp[cc][kk][e], g[kGram]);
+          pre_8(xp[cc], cpre, yp[cc]);
+          if constexpr (NORM) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) g[kGram + 1] = dot2_bf16(yp[cc][e], yp[cc][e], g[kGram + 1]);
+          }
+        }
+      }
+      // the loads of item k+1 go out before any store of item k (one vector-memory counter orders them)
+      issue(rn_);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const u32 o = (u32)m * xrow + rc.fbyte + cc * 128;
+        if constexpr (POST) {
+#pragma unroll
+          for (int kk = 0; kk < kHC; ++kk)
+            buf_st(rc.xo, o + kk * drow, u32x4{xp[cc][kk][0], xp[cc][kk][1], xp[cc][kk][2], xp[cc][kk][3]});
+        }
+        if constexpr (RM == kGivenPre && !NORM)
+          buf_st(rc.yo, (u32)m * drow + rc.fbyte + cc * 128, u32x4{yp[cc][0], yp[cc][1], yp[cc][2], yp[cc][3]});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // X' into the A tile of item k: chunk c = 2cp+cc, step ks = 2c + p/4, A lane 16*(p%4) + m
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int ks = 2 * (2 * cp + cc) + (p >> 2);
+        const int slot = f_swz(16 * (p & 3) + m, ks & 1);
+#pragma unroll
+        for (int kk = 0; kk < kHC; ++kk)
+          A_lds[sl][kk][ks][slot] = u32x4{xp[cc][kk][0], xp[cc][kk][1], xp[cc][kk][2], xp[cc][kk][3]};
+      }
+      // per-token sums over the 8 lanes of the token, then one lane writes this chunk pair's share
+#pragma unroll
+      for (int i = 0; i < kGram + 2; ++i) {
+        g[i] += __shfl_xor(g[i], 1);
+        g[i] += __shfl_xor(g[i], 2);
+        g[i] += __shfl_xor(g[i], 4);
+      }
+      if (p == 0) {
+#pragma unroll
+        for (int i = 0; i < kGram + 2; ++i) gred[k & 1][cp][m][i] = g[i];
+      }
+      if constexpr (kKeepY) {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { yk2[cc][e] = yk1[cc][e]; yk1[cc][e] = yp[cc][e]; }
+      }
+      rc = rn_;
+      __syncthreads();                                   // X(k)
+    }
+  } else {
+    // ======================================================== matrix waves
+    // segment k: the dots of item k-1 and its record; the outputs of the tokens
+    // this slice owns in item k-2; the read coefficients of item k-1
+    const int mw = wave - kFSW;
+    const int lt = threadIdx.x - kFSW * 64;              // 0..255
+    u32 mgen = 0;
+    // the four matrix waves meet (LDS counter; bounded)
+    auto mbar = [&]() {
+      ++mgen;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (lane == 0) __hip_atomic_fetch_add(&mcount, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      unsigned spins = 0;
+      while (__hip_atomic_load(&mcount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < kFMW * mgen) {
+        if (++spins > kPollLimit * 64) { if (lane == 0) atomicOr(err, kErrPollTimeout); break; }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    };
+    // weight tiles of this workgroup's slice (the slice is the same in every
+    // round): record (K block kb, tile nt, lane) at ((kb*kNT + nt)*64 + lane)*16 B
+    constexpr u32 kSliceWt = (u32)kFKB * kNT * 64 * 16;
+    const rsrc_t wres = make_rsrc(a.fn + (size_t)item_of(0).slice * (kSliceWt / 16), kSliceWt);
+    const u32 wlane = (u32)lane * 16 + (u32)mw * kFKBW * kNT * 64 * 16;
+    auto wt = [&](int j, int nt) {                     // weight tile nt of K block j of this wave
+      return __builtin_amdgcn_raw_buffer_load_b128(wres, wlane, (j * kNT + nt) * 64 * 16, 0);
+    };
+    constexpr int kCin = kFT * (kHC + kHC * kHC + kHC);  // 384 floats
+    auto cin_val = [&](const Item& it, int i) {
+      const int tm = i / (kHC + kHC * kHC + kHC), q = i % (kHC + kHC * kHC + kHC);
+      const int64_t t = (int64_t)it.tile * kFT + tm;
+      if (tm >= it.valid) return 0.f;
+      if (q < kHC) return POST ? a.post_in[t * kHC + q] : 0.f;
+      if (q < kHC + kHC * kHC) return POST ? a.comb_in[t * kHC * kHC + (q - kHC)] : 0.f;
+      return RM == kGivenPre ? a.pre_in[t * kHC + (q - kHC - kHC * kHC)] : 0.f;
+    };
+    {                                                    // prologue: cin of item 0
+      const Item i0 = item_of(0);
+      for (int i = lt; i < kCin; i += kFMW * 64) cin[0][i / (kCin / kFT)][i % (kCin / kFT)] = cin_val(i0, i);
+    }
+    u32x4 B[kFPre][kNT];
+    {
+      const Item i0 = item_of(0);
+#pragma unroll
+      for (int j = 0; j < kFPre; ++j)
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) B[j][nt] = wt(j, nt);
+    }
+    bool dead = false;
+    __syncthreads();                                     // P
+    for (int k = 0; k < K; ++k) {
+      const Item im = item_of(k - 1), io = item_of(k - 2), in1 = item_of(k + 1);
+      // ---- the dots of item k-1 (A tile k-1, weights prefetched)
+      {
+        const int sl = (k - 1) & 1;
+        f32x4 acc[kAcc];
+#pragma unroll
+        for (int t = 0; t < kAcc; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kFKBW; ++j) {
+          const int kb = mw * kFKBW + j;
+          const int ks = kb >> 2, kk = kb & 3;
+          const bf16x8 Av = __builtin_bit_cast(bf16x8, A_lds[sl][kk][ks][f_swz(lane, ks & 1)]);
+          bf16x8 Bv[kNT];
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt) Bv[nt] = __builtin_bit_cast(bf16x8, B[j % kFPre][nt]);
+          if (j + kFPre < kFKBW) {
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) B[j % kFPre][nt] = wt(j + kFPre, nt);
+          }
+          mfma_step(Av, Bv, acc);
+        }
+        // tile 1: columns c and c+8 hold the (hi+lo) and mid terms of row 16+c
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float o = __shfl_xor(acc[1][i], 8);
+          const int tm = 4 * (lane >> 4) + i, col = lane & 15;
+          red[mw][tm][col] = acc[0][i];
+          if (col < 8) red[mw][tm][16 + col] = acc[1][i] + o;
+        }
+      }
+      // Requests with the weight loads of this segment behind them (one vector-memory
+      // counter: a wait for a weight block waits for everything issued before it):
+      // the staged inputs (stream coefficients of item k+1, RMSNorm gain of item k-1).
+      const u64* ro = a.rec + (size_t)io.tile * S * kFT * kFRec;
+      const int oi0 = mw;                                // first owned token index of this wave
+      u64 ow[kFPollBatch];                               // words of this wave's first owned token, item k-2
+      {
+        const int otm = io.slice + oi0 * S;
+        const bool act = io.valid > 0 && otm < io.valid && lane < kFRec;
+#pragma unroll
+        for (int b = 0; b < kFPollBatch; ++b)
+          ow[b] = (act && b < S) ? get_word(ro + ((size_t)b * kFT + otm) * kFRec + lane) : 0ull;
+      }
+      float cv[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) cv[u] = (lt + u * kFMW * 64 < kCin) ? cin_val(in1, lt + u * kFMW * 64) : 0.f;
+      f32x4 gv = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (NORM) gv = *reinterpret_cast<const f32x4*>(a.gamma + im.slice * kFF + 4 * (lt & (kFF / 4 - 1)));
+      mbar();
+      // ---- publish item k-1's record
+      if (im.valid > 0) {
+        u64* rb = a.rec + ((size_t)im.tile * S + im.slice) * kFT * kFRec;
+        const float(*gr)[kFT][kGram + 2] = gred[(k - 1) & 1];
+        const int tm = lt >> 4;
+#pragma unroll
+        for (int q = lt & 15; q < kFRec; q += 16) {
+          if (tm >= im.valid) break;
+          int qd = -1, gi = -1;
+          if constexpr (kFresh) {
+            if (q < kHC) qd = q;
+            else if (q < kHC + kGram) gi = q - kHC;
+            else qd = q - kGram;
+          } else {
+            const int base = kKeepY ? 2 : 1;
+            if (q >= base + kMix) gi = -2;
+            else if (q >= base) qd = q - base;
+            else gi = (kKeepY && q == 0) ? kGram + 1 : kGram;
+          }
+          float v = 0.f;
+          if (qd >= 0) v = ((red[0][tm][qd] + red[1][tm][qd]) + red[2][tm][qd]) + red[3][tm][qd];
+          else if (gi >= 0) v = ((gr[0][tm][gi] + gr[1][tm][gi]) + gr[2][tm][gi]) + gr[3][tm][gi];
+          put_word(rb + tm * kFRec + q, tag_word(v, tag));
+        }
+      }
+      // ---- read coefficients of item k-1 (words written just now by the other
+      //      slices): requested here, summed after the owned tokens of item k-2
+      const u64* rm = a.rec + (size_t)im.tile * S * kFT * kFRec;
+      const int fi = lane >> 4, fq = lane & 15, ftm = 4 * mw + fi;
+      const bool fast_act = kFast > 0 && im.valid > 0 && fq < kFast && ftm < im.valid;
+      u64 fw[kFPollBatch];
+#pragma unroll
+      for (int b = 0; b < kFPollBatch; ++b)
+        fw[b] = (fast_act && b < S) ? get_word(rm + ((size_t)b * kFT + ftm) * kFRec + fq) : 0ull;
+      // owned tokens: mixes, pre/post, Sinkhorn comb (first owned token from the words above)
+      for (int oi = oi0; io.valid > 0 && io.slice + oi * S < io.valid; oi += kFMW) {
+        const int tm = io.slice + oi * S;
+        const bool act = lane < kFRec;
+        float s = 0.f;
+        for (int s0b = 0; s0b < S; s0b += kFPollBatch) {
+          u64 wv[kFPollBatch];
+#pragma unroll
+          for (int b = 0; b < kFPollBatch; ++b)
+            wv[b] = (oi == oi0 && s0b == 0) ? ow[b]
+                    : ((act && s0b + b < S) ? get_word(ro + ((size_t)(s0b + b) * kFT + tm) * kFRec + lane) : 0ull);
+#pragma unroll
+          for (int b = 0; b < kFPollBatch; ++b)
+            if (act && s0b + b < S) s += settle(ro + ((size_t)(s0b + b) * kFT + tm) * kFRec + lane, wv[b], tag, err, dead);
+        }
+        float* fs = fsum[mw][0];
+        __builtin_amdgcn_wave_barrier();
+        if (act) fs[lane] = s;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float ssx;
+        if constexpr (kFresh) ssx = (fs[kHC + 0] + fs[kHC + 4]) + (fs[kHC + 7] + fs[kHC + 9]);
+        else ssx = fs[f_ssx<RM, NORM>()];
+        const float rx = 1.0f / sqrtf(ssx / (float)(kHC * d) + a.norm_eps);
+        if (lane < kHC) derive_outputs<RM, NORM>(fs, rx, lane, a, (int64_t)io.tile * kFT + tm);
+        __builtin_amdgcn_wave_barrier();
+      }
+      // read coefficients of item k-1: this wave takes tokens 4*mw .. 4*mw+3
+      if constexpr (kFast > 0) {
+        if (im.valid > 0) {
+          float s = 0.f;
+          for (int s0b = 0; s0b < S; s0b += kFPollBatch) {
+            u64 wv[kFPollBatch];
+#pragma unroll
+            for (int b = 0; b < kFPollBatch; ++b)
+              wv[b] = s0b == 0 ? fw[b]
+                               : ((fast_act && s0b + b < S) ? get_word(rm + ((size_t)(s0b + b) * kFT + ftm) * kFRec + fq) : 0ull);
+#pragma unroll
+            for (int b = 0; b < kFPollBatch; ++b)
+              if (fast_act && s0b + b < S) s += settle(rm + ((size_t)(s0b + b) * kFT + ftm) * kFRec + fq, wv[b], tag, err, dead);
+          }
+          __builtin_amdgcn_wave_barrier();
+          if (fast_act) fsum[mw][fi][fq] = s;
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          if (lane < 4 * kHC) {                          // quad per token: lane j of the quad = pre j
+            const int i2 = lane >> 2, j = lane & 3, t2 = 4 * mw + i2;
+            const float* fs = fsum[mw][i2];
+            float pre = 0.f, rnv = 1.f;
+            if constexpr (kFresh) {
+              const float ssx = (fs[kHC + 0] + fs[kHC + 4]) + (fs[kHC + 7] + fs[kHC + 9]);
+              const float rx = 1.0f / sqrtf(ssx / (float)(kHC * d) + a.norm_eps);
+              pre = sigmoidf_((fs[j] * rx) * a.hc_scale[0] + a.hc_base[j]) + a.hc_eps;
+              if constexpr (NORM) {
+                double pd[kHC];
+#pragma unroll
+                for (int l = 0; l < kHC; ++l) pd[l] = (double)__shfl(pre, (lane & ~3) + l);
+                double yy = 0.0;
+                int gi = 0;
+#pragma unroll
+                for (int l = 0; l < kHC; ++l)
+#pragma unroll
+                  for (int l2 = l; l2 < kHC; ++l2, ++gi) yy += (l == l2 ? 1.0 : 2.0) * pd[l] * pd[l2] * (double)fs[kHC + gi];
+                rnv = 1.0f / sqrtf((float)(yy / (double)d) + a.rms_eps);
+              }
+            } else {
+              rnv = 1.0f / sqrtf(fs[0] / (float)d + a.rms_eps);
+            }
+            coef[(k - 1) & 1][t2][j] = pre;
+            if (j == 0) coef[(k - 1) & 1][t2][kHC] = rnv;
+          }
+        }
+      }
+      // ---- staged inputs into LDS; the next item's first weight blocks
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = lt + u * kFMW * 64;
+        if (i < kCin) cin[(k + 1) & 1][i / (kCin / kFT)][i % (kCin / kFT)] = cv[u];
+      }
+      if constexpr (NORM) {
+        if (lt < kFF / 4) *reinterpret_cast<f32x4*>(&gam[(k - 1) & 1][4 * lt]) = gv;
+      }
+      {
+        const Item inext = item_of(k);
+#pragma unroll
+        for (int j = 0; j < kFPre; ++j)
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt) B[j][nt] = wt(j, nt);
+      }
+      __syncthreads();                                   // X(k)
+    }
+  }
+  // ---- the last workgroup out advances the call tag for the next call
+  if (threadIdx.x == 0) {
+    const u32 done = __hip_atomic_fetch_add(a.ctrl + kDoneWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == (u32)G - 1u) {
+      for (int i = 0; i < kEpochCopies; ++i)
+        __hip_atomic_store(a.ctrl + 16 * i, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.ctrl + kDoneWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ host side
 thread_local char g_err[512];
 
@@ -936,10 +1556,18 @@ int read_slices(int64_t n, int d) {
   const int64_t tiles = (n + kTT - 1) / kTT;
   return divisor_at_least(d / kCF, std::min<int64_t>((512 + tiles - 1) / tiles, kMaxSlices));
 }
-size_t workspace_bytes(int64_t n, int d) {
+size_t split_records_bytes(int64_t n, int d) {
   const int64_t tiles = (n + kTT - 1) / kTT;
   return (size_t)tiles * stream_slices(n, d) * kTT * kRec * 4;
 }
+bool fused_shape(int d) { return d % kFF == 0 && d >= kFMinD && d <= kMaxD; }
+size_t fused_records_bytes(int64_t n, int d) {
+  if (!fused_shape(d)) return 0;
+  const int64_t tiles = (n + kFT - 1) / kFT;
+  return (size_t)tiles * (d / kFF) * kFT * kFRec * sizeof(u64);
+}
+// [control block][single-launch records][two-kernel records]
+size_t workspace_bytes(int64_t n, int d) { return kCtrlBytes + fused_records_bytes(n, d) + split_records_bytes(n, d); }
 
 template <bool POST, int RM, bool NORM>
 hipError_t launch_stream_t(const StreamArgs& a, unsigned grid, hipStream_t st) {
@@ -969,7 +1597,7 @@ int launch_boundary(bool post, int rm, bool norm, StreamArgs s, FinishArgs f, vo
   s.S = stream_slices(s.n, s.d);
   s.F = s.d / s.S;
   s.tiles = (int)tiles;
-  s.rec = static_cast<float*>(ws);
+  s.rec = reinterpret_cast<float*>(static_cast<char*>(ws) + kCtrlBytes + fused_records_bytes(s.n, s.d));
   const unsigned grid1 = (unsigned)(tiles * s.S);
   hipError_t e = hipSuccess;
   if (phases & 1) switch ((post ? 8 : 0) | (rm << 1) | (norm ? 1 : 0)) {
@@ -997,6 +1625,78 @@ int launch_boundary(bool post, int rm, bool norm, StreamArgs s, FinishArgs f, vo
   if (rm == kFreshPre) e = norm ? launch_finish_t<kFreshPre, true>(f, grid2, st) : launch_finish_t<kFreshPre, false>(f, grid2, st);
   else if (rm == kGivenPre && norm) e = launch_finish_t<kGivenPre, true>(f, grid2, st);
   else e = launch_finish_t<kNoRead, false>(f, grid2, st);
+  return launched(e, what);
+}
+
+// ---- single-launch boundary
+template <bool POST, int RM, bool NORM>
+hipError_t launch_fused_t(const FusedArgs& a, unsigned grid, hipStream_t st) {
+  FusedArgs copy = a;
+  void* args[] = {&copy};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fused_kernel<POST, RM, NORM>), dim3(grid), dim3(kFThreads),
+                         args, 0, st);
+}
+const void* fused_fn(bool post, int rm, bool norm) {
+  switch ((post ? 4 : 0) | (rm == kFreshPre ? 2 : 0) | (norm ? 1 : 0)) {
+    case 0: return reinterpret_cast<const void*>(&fused_kernel<false, kGivenPre, false>);
+    case 1: return reinterpret_cast<const void*>(&fused_kernel<false, kGivenPre, true>);
+    case 2: return reinterpret_cast<const void*>(&fused_kernel<false, kFreshPre, false>);
+    case 3: return reinterpret_cast<const void*>(&fused_kernel<false, kFreshPre, true>);
+    case 4: return reinterpret_cast<const void*>(&fused_kernel<true, kGivenPre, false>);
+    case 5: return reinterpret_cast<const void*>(&fused_kernel<true, kGivenPre, true>);
+    case 6: return reinterpret_cast<const void*>(&fused_kernel<true, kFreshPre, false>);
+    default: return reinterpret_cast<const void*>(&fused_kernel<true, kFreshPre, true>);
+  }
+}
+// Workgroups of a variant that can be resident at once on the current device
+// (compute units x workgroups per unit), queried once per device and variant.
+int fused_capacity(bool post, int rm, bool norm) {
+  constexpr int kDevs = 64;
+  static int cache[kDevs][8];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 0;
+  const int v = (post ? 4 : 0) | (rm == kFreshPre ? 2 : 0) | (norm ? 1 : 0);
+  int c = __atomic_load_n(&cache[dev][v], __ATOMIC_RELAXED);
+  if (c == 0) {
+    int cus = 0, occ = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fused_fn(post, rm, norm), kFThreads, 0) != hipSuccess)
+      return 0;
+    c = cus * occ > 0 ? cus * occ : -1;
+    __atomic_store_n(&cache[dev][v], c, __ATOMIC_RELAXED);
+  }
+  return c > 0 ? c : 0;
+}
+
+int launch_fused(bool post, int rm, bool norm, FusedArgs f, void* ws, size_t ws_bytes, hipStream_t st,
+                 const char* what) {
+  const size_t need = workspace_bytes(f.n, f.d);
+  if (!ws) return fail(HC_EINVAL, "%s: workspace must not be NULL (need %zu bytes)", what, need);
+  if (!aligned16(ws)) return fail(HC_EINVAL, "%s: workspace is not 16-byte aligned", what);
+  if (ws_bytes < need) return fail(HC_EINVAL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, need);
+  f.S = f.d / kFF;
+  const int64_t tiles = (f.n + kFT - 1) / kFT;
+  const int64_t items = tiles * f.S;
+  const int cap = fused_capacity(post, rm, norm);
+  const int64_t g = std::min<int64_t>(items, (int64_t)(cap / f.S) * f.S);
+  if (g < f.S) return fail(HC_ENOTSUP, "%s: the device holds %d resident workgroups, %d are needed", what, cap, f.S);
+  f.tiles = (int)tiles;
+  f.items = (int)items;
+  f.rounds = (int)((items + g - 1) / g);
+  f.ctrl = static_cast<u32*>(ws);
+  f.rec = reinterpret_cast<u64*>(static_cast<char*>(ws) + kCtrlBytes);
+  const unsigned grid = (unsigned)g;
+  hipError_t e;
+  switch ((post ? 4 : 0) | (rm == kFreshPre ? 2 : 0) | (norm ? 1 : 0)) {
+    case 0: e = launch_fused_t<false, kGivenPre, false>(f, grid, st); break;
+    case 1: e = launch_fused_t<false, kGivenPre, true>(f, grid, st); break;
+    case 2: e = launch_fused_t<false, kFreshPre, false>(f, grid, st); break;
+    case 3: e = launch_fused_t<false, kFreshPre, true>(f, grid, st); break;
+    case 4: e = launch_fused_t<true, kGivenPre, false>(f, grid, st); break;
+    case 5: e = launch_fused_t<true, kGivenPre, true>(f, grid, st); break;
+    case 6: e = launch_fused_t<true, kFreshPre, false>(f, grid, st); break;
+    default: e = launch_fused_t<true, kFreshPre, true>(f, grid, st); break;
+  }
   return launched(e, what);
 }
 
@@ -1144,8 +1844,11 @@ size_t hc_boundary_workspace_bytes(int64_t n, int hc, int d) { return hc_workspa
 static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) {
   g_err[0] = 0;
   if (!p) return fail(HC_EINVAL, "args must not be NULL");
-  if (p->struct_size < sizeof(hc_boundary_args))
+  constexpr size_t kNoFlags = offsetof(hc_boundary_args, flags);   // callers of the field-less struct
+  if (p->struct_size < kNoFlags)
     return fail(HC_EINVAL, "struct_size=%u, expected %zu", p->struct_size, sizeof(hc_boundary_args));
+  const uint32_t flags = p->struct_size >= kNoFlags + sizeof(uint32_t) ? p->flags : 0u;
+  if (flags & ~HC_BOUNDARY_SINGLE_LAUNCH) return fail(HC_EINVAL, "flags=%#x: unknown bits", flags);
   int rc = check_hd(p->hc, p->d);
   if (rc) return rc;
   if ((rc = check_n(p->n))) return rc;
@@ -1164,6 +1867,12 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
   if (fresh && !mix) return fail(HC_EINVAL, "pre_in is NULL but no mixes are derived (fn_packed is NULL)");
   if (norm && p->d > kRowChunk * kRowMaxChunks * 2)
     return fail(HC_ENOTSUP, "RMSNorm of the read row supports d <= %d", kRowChunk * kRowMaxChunks * 2);
+  if (flags & HC_BOUNDARY_SINGLE_LAUNCH) {
+    if (phases != 3) return fail(HC_EINVAL, "the single-launch schedule has no halves (use hc_boundary)");
+    if (!mix) return fail(HC_EINVAL, "the single-launch schedule needs fn_packed");
+    if (!fused_shape(p->d)) return fail(HC_ENOTSUP, "single launch: d=%d must be a multiple of %d, at least %d", p->d, kFF, kFMinD);
+    if (p->n > kFusedMaxN) return fail(HC_ENOTSUP, "single launch: n=%lld is too large", (long long)p->n);
+  }
   if (p->n == 0) return HC_OK;
   if ((rc = check_device())) return rc;
   const hipStream_t st = (hipStream_t)stream;
@@ -1174,6 +1883,16 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
     r.n = p->n; r.d = p->d; r.x = p->x; r.delta = p->delta; r.post_in = p->post_in; r.comb_in = p->comb_in;
     r.pre_in = p->pre_in; r.gamma = p->gamma; r.x_out = p->x_out; r.y_out = p->y_out; r.rms_eps = p->rms_eps;
     return launch_row(post, true, norm, r, st, "hc_boundary (exit)");
+  }
+  if (flags & HC_BOUNDARY_SINGLE_LAUNCH) {
+    FusedArgs f{};
+    f.n = p->n; f.d = p->d; f.x = p->x; f.delta = p->delta; f.post_in = p->post_in; f.comb_in = p->comb_in;
+    f.pre_in = p->pre_in; f.fn = reinterpret_cast<const u32x4*>(p->fn_packed); f.gamma = p->gamma;
+    f.hc_base = p->hc_base; f.hc_scale = p->hc_scale; f.x_out = p->x_out; f.y_out = p->y_out;
+    f.mixes_out = p->mixes_out; f.pre_out = p->pre_out; f.post_out = p->post_out; f.comb_out = p->comb_out;
+    f.iters = p->iters; f.hc_eps = p->hc_eps; f.norm_eps = p->norm_eps; f.rms_eps = p->rms_eps;
+    return launch_fused(post, fresh ? kFreshPre : kGivenPre, norm, f, p->workspace, p->workspace_bytes, st,
+                        "hc_boundary");
   }
   StreamArgs s{};
   s.n = p->n; s.d = p->d; s.x = p->x; s.delta = p->delta; s.post_in = p->post_in; s.comb_in = p->comb_in;

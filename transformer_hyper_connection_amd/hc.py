@@ -20,6 +20,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhc.so")
 
 HC_OK, HC_EINVAL, HC_ENOTSUP, HC_EHIP, HC_ENODEV = 0, -1, -2, -3, -4
+HC_BOUNDARY_SINGLE_LAUNCH = 1
 
 
 class HCError(RuntimeError):
@@ -38,6 +39,7 @@ class BoundaryArgs(ctypes.Structure):
         ("hc_scale", c_void_p), ("gamma", c_void_p), ("x_out", c_void_p), ("y_out", c_void_p),
         ("mixes_out", c_void_p), ("pre_out", c_void_p), ("post_out", c_void_p),
         ("comb_out", c_void_p), ("workspace", c_void_p), ("workspace_bytes", c_size_t),
+        ("flags", c_uint32),
     ]
 
 
@@ -100,6 +102,7 @@ _workspaces: dict = {}
 
 def workspace(n: int, hc: int, d: int, device) -> torch.Tensor | None:
     """A device workspace of at least hc_workspace_bytes(n, hc, d) bytes,
+    zero-filled when allocated (the library keeps it valid from call to call),
     cached per (device, stream): calls on one stream may share it."""
     nbytes = lib().hc_workspace_bytes(n, hc, d)
     if nbytes == 0:
@@ -108,7 +111,7 @@ def workspace(n: int, hc: int, d: int, device) -> torch.Tensor | None:
     key = (dev, torch.cuda.current_stream(dev).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 
@@ -228,7 +231,7 @@ def hc_post(x, residual, post, comb):
 def _prepare_boundary(x, *, delta=None, post_in=None, comb_in=None, pre_in=None, fn_packed=None,
                       hc_base=None, hc_scale=None, gamma=None, iters: int = 20, hc_eps: float = 1e-6,
                       norm_eps: float = 1e-6, rms_eps: float = 1e-6, out: dict | None = None,
-                      want_mixes: bool = False):
+                      want_mixes: bool = False, single_launch: bool = False):
     """Checks the arguments of one boundary call, allocates missing outputs and
     fills the C argument struct.  Returns (struct, outputs)."""
     dev = x.device
@@ -272,6 +275,7 @@ def _prepare_boundary(x, *, delta=None, post_in=None, comb_in=None, pre_in=None,
     a.gamma, a.x_out, a.y_out = _ptr(gamma), _ptr(o.get("x_out")), o["y"].data_ptr()
     a.mixes_out, a.pre_out = _ptr(o.get("mixes")), _ptr(o.get("pre"))
     a.post_out, a.comb_out = _ptr(o.get("post")), _ptr(o.get("comb"))
+    a.flags = HC_BOUNDARY_SINGLE_LAUNCH if single_launch else 0
     if fn_packed is not None:
         ws = o.get("workspace")
         if ws is None:
@@ -285,7 +289,8 @@ def _prepare_boundary(x, *, delta=None, post_in=None, comb_in=None, pre_in=None,
 def hc_boundary(x, **kw):
     """One fused sublayer boundary (see include/hc.h).  Keyword arguments:
     delta, post_in, comb_in, pre_in, fn_packed, hc_base, hc_scale, gamma, iters,
-    hc_eps, norm_eps, rms_eps, out, want_mixes.  Returns a dict with x_out (None
+    hc_eps, norm_eps, rms_eps, out, want_mixes, single_launch (the
+    HC_BOUNDARY_SINGLE_LAUNCH schedule).  Returns a dict with x_out (None
     at a block entry), y, and pre/post/comb (+ mixes) unless fn_packed is None.
     ``out`` may hold preallocated outputs under the same keys (and a
     "workspace"); they are used as given."""
