@@ -166,6 +166,56 @@ def cpu_baseline(s, repeats):
                       f"cores, os.cpu_count()={os.cpu_count()}"}
 
 
+def decode_block(dev, reps=200):
+    """The decode block's glue (B=128, T=1: the entry read with the incoming
+    mix, the boundary, the last write), eager and replayed from a captured
+    graph; mean microseconds per block and per boundary call over reps."""
+    b = synth.block_inputs()
+    (fa, ba, sa), (ff, bf_, sf) = b["attn"], b["ffn"]
+    A = dict(fn_packed=T.hc_fn_pack(f32(fa, dev)), hc_base=f32(ba, dev), hc_scale=f32(sa, dev))
+    F = dict(fn_packed=T.hc_fn_pack(f32(ff, dev)), hc_base=f32(bf_, dev), hc_scale=f32(sf, dev))
+    X, PRE, DA, DF = bf(b["x"], dev), f32(b["pre_in"], dev), bf(b["delta_attn"], dev), bf(b["delta_ffn"], dev)
+    entry = T.BoundaryCall(X, pre_in=PRE, **A)
+    e = entry.outputs
+    bnd = T.BoundaryCall(X, delta=DA, post_in=e["post"], comb_in=e["comb"], pre_in=e["pre"], **F)
+    o = bnd.outputs
+    xo = torch.empty_like(X)
+
+    def glue():
+        entry.run()
+        bnd.run()
+        T.hc_post(DF, o["x_out"], o["post"], o["comb"], out=xo)
+
+    def timed(fn):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    eager = timed(glue)
+    boundary = timed(bnd.run)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        glue()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        glue()
+    graph = timed(g.replay)
+    return {"workload": "decode block glue, B=128 T=1, hc=4, d=5120: entry (incoming mix) + boundary "
+                        "(attention pre) + last write; given pre, no RMSNorm",
+            "tokens": int(X.shape[0]), "block_us_eager": round(eager, 2), "block_us_graph": round(graph, 2),
+            "boundary_call_us": round(boundary, 2)}
+
+
 def stats(ms):
     return {"mean": float(np.mean(ms)), "median": float(np.median(ms)), "p10": float(np.percentile(ms, 10)),
             "p90": float(np.percentile(ms, 90))}
@@ -182,6 +232,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--no-copy", action="store_true", help="skip the 1 GiB reference stream")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode block timing")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this benchmark runs on one GPU only.  The glue is per token and would shard over "
@@ -216,6 +267,7 @@ def main():
     mean_ms = head["call_ms"]["mean"]
     achieved = head["algorithmic_bytes"] / (mean_ms * 1e-3) / 1e9
     traffic_bytes, traffic_src = traffic(args.mode)
+    dec = None if args.no_decode else decode_block(dev)
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -255,6 +307,7 @@ def main():
         "cpu_baseline": cpu,
         "modes": {k: rnd(v) for k, v in results.items()},
         "reference_stream_gbs": None if ref_gbs is None else round(ref_gbs, 1),
+        "decode": dec,
     }
     print(json.dumps(line), flush=True)
 

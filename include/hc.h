@@ -87,10 +87,24 @@ int hc_fn_pack(const float* hc_fn, int hc, int d, void* fn_packed, void* stream)
  * Workspace.  The entry points that derive mixes (hc_mixes, hc_boundary with
  * fn_packed) split the feature range of each token over several workgroups,
  * which leave per-token partial sums in a caller-owned device workspace of
- * hc_workspace_bytes(n, hc, d) bytes (0 for n == 0), 16-byte aligned; a
- * second kernel of the same call reads them.  Its contents before a call do
- * not matter.  Calls that may run concurrently (different streams) need
- * different workspaces; calls on one stream can share one.
+ * hc_workspace_bytes(n, hc, d) bytes (0 for n == 0), 16-byte aligned, for a
+ * later kernel, or the last workgroup to finish, to sum.  The workspace must
+ * be zero before its first use; the calls keep it valid for the next call (a
+ * workspace of the size asked for some (n, d) serves every call that needs no
+ * more).  Calls that may run concurrently (different streams) need different
+ * workspaces; calls on one stream can share one, also when captured in a
+ * graph and replayed.
+ *
+ * Decode schedule.  For n <= 128 with d a multiple of 256, hc_mixes, and
+ * hc_boundary with a given pre_in and no gamma (the pages' data flow at
+ * decode), run as one launch: 16-token tiles by 256-feature slices, each
+ * slice adding its per-token partial sums to the workspace as tagged words
+ * and counting itself in on the tile's arrival word; the last slice of a tile
+ * to arrive sums them in slice order (the same bits whichever slice it is)
+ * and derives mixes, pre/post and the comb ("Reading weights").  No workgroup
+ * waits for another to start.  Byte 4160 of the workspace holds a sticky error
+ * mask, bit 0 set if a word the last slice waited for never became visible
+ * (the call then finishes with wrong results instead of hanging).
  * ------------------------------------------------------------------------- */
 size_t hc_workspace_bytes(int64_t n, int hc, int d);
 
@@ -179,12 +193,11 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
  * HC_BOUNDARY_SINGLE_LAUNCH (d a multiple of 512, at least 1024): the whole
  * call as one persistent launch that keeps X' on chip for the read row instead
  * of re-reading it, the feature slices of a token tile exchanging per-token
- * partial sums through the workspace as tagged words.  Its first 8 KB are then
- * a control block that must be zero before the first such call on a workspace
- * (each call leaves it valid for the next); byte 4160 holds a sticky error
- * mask, bit 0 set if a wait for another workgroup's words timed out (the call
- * then finishes with wrong results instead of hanging).  One call at a time
- * per workspace.  Same results as the default schedule within the stated
+ * partial sums through the workspace as tagged words (the first 8 KB of the
+ * workspace are its control block; byte 4160 holds the sticky error mask, bit
+ * 0 set if a wait for another workgroup's words timed out, the call then
+ * finishing with wrong results instead of hanging).  One call at a time per
+ * workspace.  Same results as the default schedule within the stated
  * tolerances (the projection is summed over other feature slices).  Measured
  * slower than the default on MI355X at every n tried (32..4096).
  * ------------------------------------------------------------------------- */

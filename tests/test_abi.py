@@ -79,9 +79,13 @@ def test_packed_and_workspace_bytes(L):
     assert L.hc_workspace_bytes(0, 4, 5120) == 0
     assert L.hc_workspace_bytes(4096, 3, 5120) == 0
     w = L.hc_workspace_bytes(4096, 4, 5120)
-    # 8 KB control block; single-launch records: 256 tiles of 16 tokens x 10 slices x 34 tagged
-    # 8-byte words; two-launch records: 64 tiles of 64 tokens x 4 slices x 36 floats
-    assert w == 8192 + 256 * 10 * 16 * 34 * 8 + 64 * 4 * 64 * 36 * 4
+    # 8 KB control block; decode region (fixed for d): 256 B of arrival words + 8 tiles x 20 slices
+    # x 16 tokens x 25 tagged 8-byte words; single-launch records: 256 tiles of 16 tokens x 10
+    # slices x 34 tagged words; two-launch records: 64 tiles of 64 tokens x 4 slices x 36 floats
+    decode = 256 + 8 * 20 * 16 * 25 * 8
+    assert w == 8192 + decode + 256 * 10 * 16 * 34 * 8 + 64 * 4 * 64 * 36 * 4
+    # n = 128: 8 single-launch tiles; two-launch: 2 tiles x 40 slices
+    assert L.hc_workspace_bytes(128, 4, 5120) == 8192 + decode + 8 * 10 * 16 * 34 * 8 + 2 * 40 * 64 * 36 * 4
     assert L.hc_boundary_workspace_bytes(4096, 4, 5120) == w
     assert L.hc_workspace_bytes(4097, 4, 5120) > w
     # widths the single launch does not take (d % 512 != 0): control block + two-launch records only

@@ -397,7 +397,9 @@ __global__ void __launch_bounds__(kThreads) row_kernel(const RowArgs a) {
       }
     }
   } else {
-    for (int c = 0; c < nch; ++c) chunk(c);
+    // without the RMSNorm a row need not stay in one workgroup: the chunks of
+    // a row are spread over gridDim.y workgroups (few tokens)
+    for (int c = blockIdx.y; c < nch; c += gridDim.y) chunk(c);
   }
 }
 
@@ -711,6 +713,12 @@ __device__ __forceinline__ float quad_perm(float v) {
 __device__ __forceinline__ float quad_sum(float v) {
   const float u = v + quad_perm<0xB1>(v);      // lanes [1,0,3,2]
   return u + quad_perm<0x4E>(u);               // lanes [2,3,0,1]
+}
+// Sum over the 8 lanes of an aligned group: the two quad sums, each lane
+// adding the other quad's (half-row mirror), the same bits in all 8 lanes.
+__device__ __forceinline__ float oct_sum(float v) {
+  const float u = quad_sum(v);
+  return u + quad_perm<0x141>(u);
 }
 
 template <int RM, bool NORM>
@@ -1489,6 +1497,291 @@ __global__ void __launch_bounds__(kFThreads, 1) fused_kernel(const FusedArgs a) 
   }
 }
 
+// ======================================================= decode boundary
+// decode_kernel<POST, READ>: the boundary for few tokens in one launch, the
+// finalize (split + Sinkhorn) done by the last feature slice of each token tile
+// to finish ("Source layer, pairs pooled": Block.forward at decode, the read
+// taking the given pre; "Reading weights" for the split).  No workgroup waits
+// for another, so the launch needs no co-residency.
+//
+// Work items are (tile of kDT = 16 tokens, slice of kDF = 256 features of each
+// stream), one workgroup each.  A workgroup streams its item (hc_post, X'
+// stored, the read row y = sum_j pre_j X'_j stored), projects X' on the
+// matrix cores with all of its weight tiles loaded into registers at the start,
+// and writes the item's per-token record (24 dots, sum x'^2) to the workspace
+// as tagged words (value, tile epoch).  It then counts itself in on the tile's
+// arrival word; the slice that arrives last sums the S records of each token in
+// slice order (the same bits whichever slice it is), waiting for any word not
+// yet visible, and derives mixes, pre/post and the Sinkhorn comb.
+//
+// Words carry the workspace's call epoch (+1): every workgroup reads it at the
+// start, and it advances only once every tile's last slice is known, so the
+// tags grow from call to call whatever n and d are (a captured graph stays
+// valid across replays).  A tile's arrival word and the tiles-done word are
+// reset by their last arriver, found as the arrival whose count before it is
+// S-1 (tiles-1) modulo S (tiles): exactly one in any run of S (tiles).  The
+// record words must not hold the current tag before the first call: a zeroed
+// workspace never does.
+constexpr int kDT = 16;                      // tokens per tile
+constexpr int kDF = 256;                     // features per slice and stream
+constexpr int kDSteps = kDF / kStepF;        // 32-feature steps per slice (8)
+constexpr int kDThreads = 256;               // 4 waves: 2 steps each in the projection
+constexpr int kDRec = 25;                    // record words per token: 24 dots, sum x'^2
+constexpr int kDMaxN = 128;                  // decode schedule up to this many tokens (measured crossover)
+constexpr int kDTiles = kDMaxN / kDT;        // tiles at most (the region is sized for them)
+constexpr int kDArriveBytes = 256;           // arrival, epoch and tiles-done words: head of the decode region
+static_assert(kDArriveBytes >= (kDTiles + 2) * (int)sizeof(unsigned long long), "arrival words");
+
+struct DecArgs {
+  const hc_bf16* x;
+  const hc_bf16* delta;
+  const float* post_in;
+  const float* comb_in;
+  const float* pre_in;
+  const u32x4* fn;
+  const float* hc_base;
+  const float* hc_scale;
+  hc_bf16* x_out;
+  hc_bf16* y_out;
+  float* mixes_out;
+  float* pre_out;
+  float* post_out;
+  float* comb_out;
+  u64* rec;           // [tiles][S][kDT][kDRec] tagged words
+  u64* arrive;        // [kDTiles] arrival words, then the epoch word and the tiles-done word
+  u32* err;           // sticky error mask (a wait timed out)
+  int tiles;
+  int64_t n;
+  int d, S, iters;
+  float hc_eps, norm_eps;
+};
+
+template <bool POST, bool READ>
+__global__ void __launch_bounds__(kDThreads) decode_kernel(const DecArgs a) {
+  __shared__ u32x4 a_lds[kDSteps][kHC][64];            // X' in A layout (32 KB)
+  __shared__ float red[kDThreads / 64][kDT][32];       // per-wave dots
+  __shared__ float ssq[4][kDT];                        // sum x'^2 per chunk
+  __shared__ float tot[kDT][kDRec];                    // the tile's summed records (last slice)
+  __shared__ u32 s_tag, s_last;
+
+  const int S = a.S, d = a.d;
+  const int tile = blockIdx.x / S, slice = blockIdx.x % S;
+  const int64_t t0 = (int64_t)tile * kDT;
+  const int fs = slice * kDF;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = (threadIdx.x >> 3) & (kDT - 1);        // token of the tile
+  const int fl = (threadIdx.x & 7) * 8;                // first feature within the chunk
+  const int half = threadIdx.x >> 7;                   // chunk 2p + half in pass p
+  const bool tv = t0 + m < a.n;
+  const unsigned lt = tv ? (unsigned)m : 0u;
+
+  // ---- the call's epoch
+  u64* arw = a.arrive + tile;
+  u64* epw = a.arrive + kDTiles;
+  u64* donew = a.arrive + kDTiles + 1;
+  if (threadIdx.x == 0) s_tag = (u32)get_word(epw) + 1u;   // words carry epoch + 1
+
+  // ---- all loads up front: the weight tiles of this wave's two steps, the
+  // streams of both passes and the token's coefficients
+  bf16x8 B[2][kHC][kNT];
+  {
+    const int gstep = fs / kStepF + 2 * wave;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int k = 0; k < kHC; ++k)
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt)
+          B[st][k][nt] = __builtin_bit_cast(bf16x8, a.fn[((size_t)((gstep + st) * kHC + k) * kNT + nt) * 64 + lane]);
+  }
+  u32x4 r[2][kHC + 1];
+  const hc_bf16* xrow = a.x + (t0 + lt) * kHC * d;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int f = fs + (2 * p + half) * kCF + fl;
+#pragma unroll
+    for (int j = 0; j < kHC; ++j) r[p][j] = ld_stream(reinterpret_cast<const u32x4*>(xrow + (j * d + f)));
+    r[p][kHC] = POST ? ld_stream(reinterpret_cast<const u32x4*>(a.delta + (t0 + lt) * d + f)) : u32x4{0u, 0u, 0u, 0u};
+  }
+  float cpost[kHC], ccomb[kHC * kHC], cpre[kHC];
+#pragma unroll
+  for (int j = 0; j < kHC; ++j) {
+    cpost[j] = POST ? a.post_in[(t0 + lt) * kHC + j] : 0.f;
+    cpre[j] = READ ? a.pre_in[(t0 + lt) * kHC + j] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < kHC * kHC; ++j) ccomb[j] = POST ? a.comb_in[(t0 + lt) * kHC * kHC + j] : 0.f;
+
+  // ---- streams: X', the read row, sum x'^2, the A tile
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int c = 2 * p + half;
+    const int f = fs + c * kCF + fl;
+    u32 xp[kHC][4];
+    if constexpr (POST) {
+      post_8(r[p], cpost, ccomb, xp);
+      if (tv) {
+#pragma unroll
+        for (int k = 0; k < kHC; ++k)
+          st_stream(reinterpret_cast<u32x4*>(a.x_out + (t0 + lt) * kHC * d + k * d + f),
+                    u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]});
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kHC; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xp[k][e] = r[p][k][e];
+    }
+    if constexpr (READ) {
+      u32 yp[4];
+      pre_8(xp, cpre, yp);
+      if (tv) st_stream(reinterpret_cast<u32x4*>(a.y_out + (t0 + lt) * d + f), u32x4{yp[0], yp[1], yp[2], yp[3]});
+    }
+    float sx = 0.f;
+#pragma unroll
+    for (int k = 0; k < kHC; ++k) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sx = dot2_bf16(xp[k][e], xp[k][e], sx);
+      // step 2c + fl/32 of the slice; matrix-core lane (fl/8 % 4) * 16 + token
+      a_lds[2 * c + (fl >> 5)][k][((fl >> 3) & 3) * 16 + m] = u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]};
+    }
+    sx = oct_sum(sx);
+    if ((threadIdx.x & 7) == 0) ssq[c][m] = sx;
+  }
+  __syncthreads();
+
+  // ---- projection: wave w takes steps 2w, 2w+1 of the slice
+  f32x4 acc[kAcc];
+#pragma unroll
+  for (int t = 0; t < kAcc; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int k = 0; k < kHC; ++k)
+      mfma_step(__builtin_bit_cast(bf16x8, a_lds[2 * wave + st][k][lane]), B[st][k], acc);
+#pragma unroll
+  for (int t = 0; t < kAcc; ++t)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) red[wave][4 * (lane >> 4) + rr][t * 16 + (lane & 15)] = acc[t][rr];
+  __syncthreads();
+
+  // ---- this slice's record of the tile, then count in
+  const u32 tag = s_tag;
+  u64* rt = a.rec + (size_t)tile * S * kDT * kDRec;
+  for (int idx = threadIdx.x; idx < kDT * kDRec; idx += kDThreads) {
+    const int tm = idx / kDRec, q = idx % kDRec;
+    float v;
+    if (q < kMix) {
+      auto col = [&](int w, int cq) { return cq < 16 ? red[w][tm][cq] : red[w][tm][cq] + red[w][tm][cq + 8]; };
+      v = ((col(0, q) + col(1, q)) + col(2, q)) + col(3, q);
+    } else {
+      v = ((ssq[0][tm] + ssq[1][tm]) + ssq[2][tm]) + ssq[3][tm];
+    }
+    put_word(rt + ((size_t)slice * kDT + tm) * kDRec + q, tag_word(v, tag));
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const u64 before = __hip_atomic_fetch_add(arw, (u64)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = before % (u64)S == (u64)(S - 1);
+    if (s_last) {
+      put_word(arw, 0ull);                       // every slice of the tile has counted in
+      // every workgroup of the call has read the epoch once every tile's last
+      // slice is known: the last of those advances it for the next call
+      const u64 b2 = __hip_atomic_fetch_add(donew, (u64)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (b2 % (u64)a.tiles == (u64)(a.tiles - 1)) {
+        put_word(donew, 0ull);
+        put_word(epw, (u64)s_tag);               // epoch + 1
+      }
+    }
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- the last slice: sum the S records of each token in slice order; a
+  // thread's words of all slices are requested together (one round trip)
+  bool dead = false;
+  constexpr int kPairs = (kDT * kDRec + kDThreads - 1) / kDThreads;   // (token, word) pairs per thread
+  constexpr int kBatch = 32;                                          // slices in flight per pair
+  for (int b0 = 0; b0 < S; b0 += kBatch) {
+    u64 w[kPairs][kBatch];
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i) {
+      const int idx = threadIdx.x + i * kDThreads;
+      const u64* p0 = rt + (size_t)(idx / kDRec) * kDRec + idx % kDRec;   // slice b at + b * kDT * kDRec
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b)
+        w[i][b] = (idx < kDT * kDRec && b0 + b < S) ? get_word(p0 + (size_t)(b0 + b) * kDT * kDRec) : 0ull;
+    }
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i) {
+      const int idx = threadIdx.x + i * kDThreads;
+      if (idx >= kDT * kDRec) continue;
+      const int tm = idx / kDRec, q = idx % kDRec;
+      const u64* p0 = rt + (size_t)tm * kDRec + q;
+      float s = b0 == 0 ? 0.f : tot[tm][q];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b)
+        if (b0 + b < S) {
+          const float v = settle(p0 + (size_t)(b0 + b) * kDT * kDRec, w[i][b], tag, a.err, dead);
+          s = b0 + b == 0 ? v : s + v;
+        }
+      tot[tm][q] = s;
+    }
+  }
+  __syncthreads();
+  // ---- derive: 4 lanes (a quad) per token, lane j holding comb row j
+  if (threadIdx.x < kDT * kHC) {
+    const int tm = threadIdx.x >> 2, j = threadIdx.x & 3;
+    const int64_t t = t0 + tm;
+    const bool valid = t < a.n;
+    const float* rec = tot[tm];
+    const float rx = 1.0f / sqrtf(rec[kMix] / (float)(kHC * d) + a.norm_eps);
+    if (valid && a.mixes_out) {
+#pragma unroll
+      for (int i = 0; i < kMix / kHC; ++i) a.mixes_out[t * kMix + i * kHC + j] = rec[i * kHC + j] * rx;
+    }
+    if (a.pre_out) {
+      const float s0 = a.hc_scale[0], s1 = a.hc_scale[1], s2 = a.hc_scale[2];
+      const float pre = sigmoidf_((rec[j] * rx) * s0 + a.hc_base[j]) + a.hc_eps;
+      const float post = 2.0f * sigmoidf_((rec[kHC + j] * rx) * s1 + a.hc_base[kHC + j]);
+      float A[kHC];
+      float mxr = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < kHC; ++k) {
+        const int q = 2 * kHC + j * kHC + k;
+        A[k] = (rec[q] * rx) * s2 + a.hc_base[q];
+        mxr = fmaxf(mxr, A[k]);
+      }
+      float rsum = 0.f;
+#pragma unroll
+      for (int k = 0; k < kHC; ++k) {
+        A[k] = expf(A[k] - mxr);
+        rsum = rsum + A[k];
+      }
+      const float rinv = __builtin_amdgcn_rcpf(rsum);
+#pragma unroll
+      for (int k = 0; k < kHC; ++k) A[k] = A[k] * rinv + a.hc_eps;
+      auto col_norm = [&]() {
+#pragma unroll
+        for (int k = 0; k < kHC; ++k) A[k] = A[k] * __builtin_amdgcn_rcpf(quad_sum(A[k]) + a.hc_eps);
+      };
+      col_norm();
+      for (int it = 1; it < a.iters; ++it) {
+        const float inv = __builtin_amdgcn_rcpf(((A[0] + A[1]) + A[2]) + A[3] + a.hc_eps);
+#pragma unroll
+        for (int k = 0; k < kHC; ++k) A[k] = A[k] * inv;
+        col_norm();
+      }
+      if (valid) {
+        a.pre_out[t * kHC + j] = pre;
+        a.post_out[t * kHC + j] = post;
+        *reinterpret_cast<f32x4*>(a.comb_out + t * kHC * kHC + j * kHC) = f32x4{A[0], A[1], A[2], A[3]};
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ host side
 thread_local char g_err[512];
 
@@ -1566,8 +1859,18 @@ size_t fused_records_bytes(int64_t n, int d) {
   const int64_t tiles = (n + kFT - 1) / kFT;
   return (size_t)tiles * (d / kFF) * kFT * kFRec * sizeof(u64);
 }
-// [control block][single-launch records][two-kernel records]
-size_t workspace_bytes(int64_t n, int d) { return kCtrlBytes + fused_records_bytes(n, d) + split_records_bytes(n, d); }
+// decode schedule: given pre (or no read), no RMSNorm, few tokens.  Its region
+// has a fixed place and size for a width d (whatever n), so a record slot only
+// ever holds words of the same tile.
+bool decode_shape(int64_t n, int d) { return n <= kDMaxN && d % kDF == 0; }
+size_t decode_region_bytes(int d) {
+  if (d % kDF != 0) return 0;
+  return kDArriveBytes + (size_t)kDTiles * (d / kDF) * kDT * kDRec * sizeof(u64);
+}
+// [control block][decode arrival words + records][single-launch records][two-kernel records]
+size_t workspace_bytes(int64_t n, int d) {
+  return kCtrlBytes + decode_region_bytes(d) + fused_records_bytes(n, d) + split_records_bytes(n, d);
+}
 
 template <bool POST, int RM, bool NORM>
 hipError_t launch_stream_t(const StreamArgs& a, unsigned grid, hipStream_t st) {
@@ -1597,7 +1900,8 @@ int launch_boundary(bool post, int rm, bool norm, StreamArgs s, FinishArgs f, vo
   s.S = stream_slices(s.n, s.d);
   s.F = s.d / s.S;
   s.tiles = (int)tiles;
-  s.rec = reinterpret_cast<float*>(static_cast<char*>(ws) + kCtrlBytes + fused_records_bytes(s.n, s.d));
+  s.rec = reinterpret_cast<float*>(static_cast<char*>(ws) + kCtrlBytes + decode_region_bytes(s.d) +
+                                   fused_records_bytes(s.n, s.d));
   const unsigned grid1 = (unsigned)(tiles * s.S);
   hipError_t e = hipSuccess;
   if (phases & 1) switch ((post ? 8 : 0) | (rm << 1) | (norm ? 1 : 0)) {
@@ -1625,6 +1929,37 @@ int launch_boundary(bool post, int rm, bool norm, StreamArgs s, FinishArgs f, vo
   if (rm == kFreshPre) e = norm ? launch_finish_t<kFreshPre, true>(f, grid2, st) : launch_finish_t<kFreshPre, false>(f, grid2, st);
   else if (rm == kGivenPre && norm) e = launch_finish_t<kGivenPre, true>(f, grid2, st);
   else e = launch_finish_t<kNoRead, false>(f, grid2, st);
+  return launched(e, what);
+}
+
+// ---- decode boundary
+template <bool POST, bool READ>
+hipError_t launch_decode_t(const DecArgs& a, unsigned grid, hipStream_t st) {
+  DecArgs copy = a;
+  void* args[] = {&copy};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<POST, READ>), dim3(grid), dim3(kDThreads), args,
+                         0, st);
+}
+int launch_decode(bool post, bool read, DecArgs a, void* ws, size_t ws_bytes, hipStream_t st, const char* what) {
+  const size_t need = workspace_bytes(a.n, a.d);
+  if (!ws) return fail(HC_EINVAL, "%s: workspace must not be NULL (need %zu bytes)", what, need);
+  if (!aligned16(ws)) return fail(HC_EINVAL, "%s: workspace is not 16-byte aligned", what);
+  if (ws_bytes < need) return fail(HC_EINVAL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, need);
+  a.S = a.d / kDF;
+  const int64_t tiles = (a.n + kDT - 1) / kDT;
+  char* base = static_cast<char*>(ws) + kCtrlBytes;
+  a.arrive = reinterpret_cast<u64*>(base);
+  a.rec = reinterpret_cast<u64*>(base + kDArriveBytes);
+  a.err = static_cast<u32*>(ws) + kErrWord;
+  a.tiles = (int)tiles;
+  const unsigned grid = (unsigned)(tiles * a.S);
+  hipError_t e;
+  switch ((post ? 2 : 0) | (read ? 1 : 0)) {
+    case 0: e = launch_decode_t<false, false>(a, grid, st); break;
+    case 1: e = launch_decode_t<false, true>(a, grid, st); break;
+    case 2: e = launch_decode_t<true, false>(a, grid, st); break;
+    default: e = launch_decode_t<true, true>(a, grid, st); break;
+  }
   return launched(e, what);
 }
 
@@ -1684,7 +2019,7 @@ int launch_fused(bool post, int rm, bool norm, FusedArgs f, void* ws, size_t ws_
   f.items = (int)items;
   f.rounds = (int)((items + g - 1) / g);
   f.ctrl = static_cast<u32*>(ws);
-  f.rec = reinterpret_cast<u64*>(static_cast<char*>(ws) + kCtrlBytes);
+  f.rec = reinterpret_cast<u64*>(static_cast<char*>(ws) + kCtrlBytes + decode_region_bytes(f.d));
   const unsigned grid = (unsigned)g;
   hipError_t e;
   switch ((post ? 4 : 0) | (rm == kFreshPre ? 2 : 0) | (norm ? 1 : 0)) {
@@ -1703,9 +2038,13 @@ int launch_fused(bool post, int rm, bool norm, FusedArgs f, void* ws, size_t ws_
 template <bool POST, bool PRE, bool NORM, int TPW>
 hipError_t launch_row_t(const RowArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)((a.n + kWaves * TPW - 1) / (kWaves * TPW));
+  // without the RMSNorm, few tokens: the 512-feature chunks of a row go to
+  // several workgroups, aiming at about 512 of them
+  const int nch = (a.d + kRowChunk - 1) / kRowChunk;
+  const unsigned gy = NORM ? 1u : (unsigned)std::max(1, std::min<int>(nch, (int)((512 + grid - 1) / grid)));
   RowArgs copy = a;
   void* args[] = {&copy};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&row_kernel<POST, PRE, NORM, TPW>), dim3(grid),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&row_kernel<POST, PRE, NORM, TPW>), dim3(grid, gy),
                          dim3(kThreads), args, 0, st);
 }
 
@@ -1715,10 +2054,11 @@ int launch_row(bool post, bool pre, bool norm, const RowArgs& a, hipStream_t st,
     return fail(HC_ENOTSUP, "%s: RMSNorm of the read row supports d <= %d", what, kRowChunk * kRowMaxChunks * 2);
   const int key = (post ? 4 : 0) | (pre ? 2 : 0) | (norm ? 1 : 0);
   hipError_t e;
+  const bool few = a.n < 2048;                     // one token per wave: more workgroups
   switch (key) {
-    case 0b100: e = launch_row_t<true, false, false, 2>(a, st); break;
-    case 0b010: e = launch_row_t<false, true, false, 2>(a, st); break;
-    case 0b110: e = launch_row_t<true, true, false, 2>(a, st); break;
+    case 0b100: e = few ? launch_row_t<true, false, false, 1>(a, st) : launch_row_t<true, false, false, 2>(a, st); break;
+    case 0b010: e = few ? launch_row_t<false, true, false, 1>(a, st) : launch_row_t<false, true, false, 2>(a, st); break;
+    case 0b110: e = few ? launch_row_t<true, true, false, 1>(a, st) : launch_row_t<true, true, false, 2>(a, st); break;
     case 0b011: e = wide ? launch_row_t<false, true, true, 1>(a, st) : launch_row_t<false, true, true, 2>(a, st); break;
     case 0b111: e = wide ? launch_row_t<true, true, true, 1>(a, st) : launch_row_t<true, true, true, 2>(a, st); break;
     default: return fail(HC_EINVAL, "%s: unsupported stage combination", what);
@@ -1802,6 +2142,13 @@ int hc_mixes(const hc_bf16* x, const void* fn_packed, int64_t n, int hc, int d, 
   }
   if (n == 0) return HC_OK;
   if ((rc = check_device())) return rc;
+  if (decode_shape(n, d)) {
+    DecArgs a{};
+    a.n = n; a.d = d; a.x = x; a.fn = reinterpret_cast<const u32x4*>(fn_packed); a.mixes_out = mixes;
+    a.hc_scale = hc_scale; a.hc_base = hc_base; a.iters = iters; a.hc_eps = hc_eps; a.norm_eps = norm_eps;
+    if (split) { a.pre_out = pre; a.post_out = post; a.comb_out = comb; }
+    return launch_decode(false, false, a, workspace, workspace_bytes, (hipStream_t)stream, "hc_mixes");
+  }
   StreamArgs s{};
   s.n = n; s.d = d; s.x = x; s.fn = reinterpret_cast<const u32x4*>(fn_packed);
   FinishArgs f{};
@@ -1893,6 +2240,15 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
     f.iters = p->iters; f.hc_eps = p->hc_eps; f.norm_eps = p->norm_eps; f.rms_eps = p->rms_eps;
     return launch_fused(post, fresh ? kFreshPre : kGivenPre, norm, f, p->workspace, p->workspace_bytes, st,
                         "hc_boundary");
+  }
+  if (phases == 3 && !fresh && !norm && decode_shape(p->n, p->d)) {
+    DecArgs a{};
+    a.n = p->n; a.d = p->d; a.x = p->x; a.delta = p->delta; a.post_in = p->post_in; a.comb_in = p->comb_in;
+    a.pre_in = p->pre_in; a.fn = reinterpret_cast<const u32x4*>(p->fn_packed); a.hc_base = p->hc_base;
+    a.hc_scale = p->hc_scale; a.x_out = p->x_out; a.y_out = p->y_out; a.mixes_out = p->mixes_out;
+    a.pre_out = p->pre_out; a.post_out = p->post_out; a.comb_out = p->comb_out; a.iters = p->iters;
+    a.hc_eps = p->hc_eps; a.norm_eps = p->norm_eps;
+    return launch_decode(post, true, a, p->workspace, p->workspace_bytes, st, "hc_boundary");
   }
   StreamArgs s{};
   s.n = p->n; s.d = p->d; s.x = p->x; s.delta = p->delta; s.post_in = p->post_in; s.comb_in = p->comb_in;

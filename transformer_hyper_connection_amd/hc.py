@@ -213,16 +213,19 @@ def hc_pre(x, pre_mix):
     return y
 
 
-def hc_post(x, residual, post, comb):
+def hc_post(x, residual, post, comb, out=None):
     """Block.hc_post (argument order as the pages: sublayer output x first,
-    residual streams second) -> [..., hc, d] bf16."""
+    residual streams second) -> [..., hc, d] bf16, into ``out`` if given."""
     dev = residual.device
     _need(residual, "residual", torch.bfloat16)
     lead, n, hc, d = _streams_shape(residual)
     _need(x, "x", torch.bfloat16, dev, (*lead, d))
     _need(post, "post", torch.float32, dev, (*lead, hc))
     _need(comb, "comb", torch.float32, dev, (*lead, hc, hc))
-    out = torch.empty_like(residual)
+    if out is None:
+        out = torch.empty_like(residual)
+    else:
+        _need(out, "out", torch.bfloat16, dev, tuple(residual.shape))
     _check(lib().hc_post(x.data_ptr(), residual.data_ptr(), post.data_ptr(), comb.data_ptr(), n, hc, d,
                          out.data_ptr(), _stream(dev)), "hc_post")
     return out
