@@ -1565,7 +1565,12 @@ __global__ void __launch_bounds__(kDThreads) decode_kernel(const DecArgs a) {
   __shared__ u32 s_tag, s_last;
 
   const int S = a.S, d = a.d;
-  const int tile = blockIdx.x / S, slice = blockIdx.x % S;
+  // XCD-aware numbering: consecutive workgroups land on different XCDs, so
+  // they are renumbered XCD by XCD and taken slice-major, the workgroups of an
+  // XCD sharing few slices (their weight tiles stay in that XCD's L2)
+  const int G = gridDim.x;
+  const int lin = (G & 7) ? blockIdx.x : (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int slice = lin / a.tiles, tile = lin % a.tiles;
   const int64_t t0 = (int64_t)tile * kDT;
   const int fs = slice * kDF;
   const int lane = threadIdx.x & 63;
