@@ -241,12 +241,33 @@ def rms_norm(y: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# Stack entry and the MTP tap -- "Final RMSNorm" (the model driver,
+# Transformer.forward)
+# --------------------------------------------------------------------------
+def expand_streams(h: np.ndarray, hc: int = 4) -> np.ndarray:
+    """The driver's entry: the embedding h [n, d] (bf16 bits) copied into hc
+    identical streams, [n, hc, d]."""
+    h = np.asarray(h, dtype=np.uint16)
+    return np.repeat(h[:, None, :], hc, axis=1)
+
+
+def stream_mean(x: np.ndarray) -> np.ndarray:
+    """The MTP head's tap at its target layers: the mean over the hc streams of
+    a block's input, [n, d], a bf16 tensor mean.  Reading: the exact mean
+    (the sum of hc bf16 values and the division by hc are exact in float64),
+    rounded once to bf16."""
+    v = bf16_to_f32(x).astype(F64)
+    return to_bf16(v.mean(axis=1))
+
+
+# --------------------------------------------------------------------------
 # Compositions -- "Source layer, pairs pooled" (Block.forward) and
 #                 "Final RMSNorm" (the model driver)
 # --------------------------------------------------------------------------
 def boundary(*, x, delta=None, post_in=None, comb_in=None, pre_in=None,
              hc_fn=None, hc_base=None, hc_scale=None, gamma=None,
-             iters=20, hc_eps=1e-6, norm_eps=1e-6, rms_eps=1e-6, hc=4):
+             iters=20, hc_eps=1e-6, norm_eps=1e-6, rms_eps=1e-6, hc=4,
+             x_expanded=False, want_mean=False):
     """One sublayer boundary: write the streams with the previous sublayer's
     (post, comb) and output delta, derive this boundary's (pre, post, comb)
     from the new streams, read the new streams into the next sublayer input.
@@ -257,11 +278,17 @@ def boundary(*, x, delta=None, post_in=None, comb_in=None, pre_in=None,
                       previous boundary produced: the lag ``Block.forward``
                       shows); pre_in None -> read with the pre just derived.
     * gamma given  -> the read row is RMS-normalised (rms_eps) before return.
+    * x_expanded   -> x is [n, d]: the streams are hc copies of it (the
+                      driver's entry expansion).
+    * want_mean    -> also the MTP tap of the new streams (stream_mean).
 
     Returns a dict with x_out (bf16 bits, None on entry), y (bf16 bits:
-    normalised if gamma was given), and mixes/pre/post/comb (None on exit).
+    normalised if gamma was given), mixes/pre/post/comb (None on exit), and
+    x_mean (or None).
     """
     x = np.asarray(x, dtype=np.uint16)
+    if x_expanded:
+        x = expand_streams(x, hc)
     xp = x if delta is None else hc_post(delta, x, post_in, comb_in)
     out = {"x_out": None if delta is None else xp,
            "mixes": None, "pre": None, "post": None, "comb": None}
@@ -274,6 +301,7 @@ def boundary(*, x, delta=None, post_in=None, comb_in=None, pre_in=None,
         raise ValueError("no reading mix: give pre_in or hc_fn")
     y = hc_pre(xp, p)
     out["y"] = rms_norm(y, gamma, rms_eps) if gamma is not None else y
+    out["x_mean"] = stream_mean(xp) if want_mean else None
     return out
 
 

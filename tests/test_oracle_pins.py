@@ -437,3 +437,53 @@ def test_stack_identical_streams_first_read_is_embedding():
     rec = []
     O.stack(h=h, params=params, gammas=gammas, gamma_final=np.ones(d, np.float32), record=rec)
     assert np.array_equal(rec[0][1], O.rms_norm(h, np.ones(d, np.float32), 1e-6))
+
+
+# ------------------------------------------------------------ stack entry and the MTP tap
+def test_expand_streams_copies_the_embedding():
+    h = rand_bf16((5, 32))
+    x = O.expand_streams(h)
+    assert x.shape == (5, 4, 32)
+    for j in range(4):
+        assert np.array_equal(x[:, j], h)
+
+
+def test_stream_mean_of_identical_streams_is_the_stream():
+    h = rand_bf16((6, 96))
+    assert np.array_equal(O.stream_mean(O.expand_streams(h)), h)
+
+
+def test_stream_mean_single_stream_is_a_quarter_exactly():
+    # x/4 is exact in bf16 (a power of two) away from the subnormal range
+    x = np.zeros((3, 4, 64), np.uint16)
+    h = rand_bf16((3, 64))
+    for j in range(4):
+        x[:] = 0
+        x[:, j] = h
+        m = N.bits_to_f64(O.stream_mean(x))
+        assert np.array_equal(m, N.bits_to_f64(h) / 4)
+
+
+def test_stream_mean_exact_rational():
+    x = rand_bf16((2, 4, 16), scale=3.0)
+    m = O.stream_mean(x)
+    X = N.bits_to_f64(x)
+    for t in range(2):
+        for i in range(16):
+            exact = sum(Fraction(X[t, j, i]) for j in range(4)) / 4
+            assert N.bits_to_f64([m[t, i]])[0] == float(N.rne_bf16(exact))
+
+
+def test_boundary_expanded_entry_equals_repeated_streams():
+    hc, d, n = 4, 64, 5
+    h = rand_bf16((n, d))
+    fn = (rng.standard_normal((24, hc * d)) * 0.05).astype(np.float32)
+    base = (rng.standard_normal(24) * 0.1).astype(np.float32)
+    scale = np.array([1.0, 1.5, 0.8], np.float32)
+    pre0 = np.full((n, hc), 0.25, np.float32)
+    a = O.boundary(x=h, pre_in=pre0, hc_fn=fn, hc_base=base, hc_scale=scale, x_expanded=True, want_mean=True)
+    b = O.boundary(x=np.repeat(h[:, None], hc, axis=1), pre_in=pre0, hc_fn=fn, hc_base=base, hc_scale=scale)
+    for k in ("mixes", "pre", "post", "comb", "y"):
+        assert np.array_equal(a[k], b[k])
+    assert np.array_equal(a["y"], h)          # 0.25 on four copies reads the embedding back
+    assert np.array_equal(a["x_mean"], h)     # and the tap of four copies is the embedding
