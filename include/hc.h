@@ -186,9 +186,9 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
  * x_out must not overlap x; y_out must not overlap x, x_out or delta.
  * workspace/workspace_bytes: required when fn_packed != NULL, see
  * hc_workspace_bytes (hc_boundary_workspace_bytes returns the same size).
- * flags: 0, or HC_BOUNDARY_SINGLE_LAUNCH for the single-launch schedule (below);
- * a caller built against a header without this field passes the shorter
- * struct_size and gets 0.
+ * flags: 0, HC_BOUNDARY_SINGLE_LAUNCH for the single-launch schedule (below),
+ * HC_BOUNDARY_X_EXPANDED for an expanded x (below); a caller built against a
+ * header without this field passes the shorter struct_size and gets 0.
  *
  * HC_BOUNDARY_SINGLE_LAUNCH (d a multiple of 512, at least 1024): the whole
  * call as one persistent launch that keeps X' on chip for the read row instead
@@ -202,6 +202,12 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
  * slower than the default on MI355X at every n tried (32..4096).
  * ------------------------------------------------------------------------- */
 #define HC_BOUNDARY_SINGLE_LAUNCH 1u
+/* x is [n, d] and every one of the hc streams is that row: the stack entry
+ * ("Final RMSNorm", the model driver copies the embedding into hc streams)
+ * without materialising the copies.  With delta the call writes the real
+ * streams to x_out; without, it derives the mixes of the copies and reads
+ * them.  Not with HC_BOUNDARY_SINGLE_LAUNCH. */
+#define HC_BOUNDARY_X_EXPANDED 4u
 
 typedef struct hc_boundary_args {
   uint32_t struct_size; /* = sizeof(hc_boundary_args) */
@@ -225,7 +231,13 @@ typedef struct hc_boundary_args {
   float* comb_out;         /* [n, hc, hc]  required iff fn_packed != NULL        */
   void* workspace;
   size_t workspace_bytes;
-  uint32_t flags;          /* 0 or HC_BOUNDARY_SINGLE_LAUNCH                     */
+  uint32_t flags;          /* 0, HC_BOUNDARY_SINGLE_LAUNCH, HC_BOUNDARY_X_EXPANDED */
+  /* [n, d] bf16 or NULL: the mean over the hc streams of the new streams (x_out,
+   * or x at a block entry), the MTP head's tap of a block's input ("Final
+   * RMSNorm", the model driver); (((X'_0 + X'_1) + X'_2) + X'_3) / 4 in fp32,
+   * rounded to bf16.  Not with HC_BOUNDARY_SINGLE_LAUNCH.  A caller built
+   * against a header without this field passes the shorter struct_size. */
+  hc_bf16* x_mean_out;
 } hc_boundary_args;
 
 int hc_boundary(const hc_boundary_args* args, void* stream);

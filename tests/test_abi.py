@@ -158,15 +158,20 @@ def test_boundary_validation(L):
     assert call(_args(n=0, delta=None, post_in=None, comb_in=None, x_out=None)) == H.HC_OK
     assert call(_args(d=10304, gamma=P + 0xD00)) == H.HC_ENOTSUP   # RMSNorm row too long
     # the single-launch schedule flag: unknown bits, shapes it does not take, no halves
-    SL = H.HC_BOUNDARY_SINGLE_LAUNCH
-    assert call(_args(flags=4)) == H.HC_EINVAL
+    SL, XE = H.HC_BOUNDARY_SINGLE_LAUNCH, H.HC_BOUNDARY_X_EXPANDED
+    assert call(_args(flags=8)) == H.HC_EINVAL
+    assert call(_args(flags=SL | XE, d=1024)) == H.HC_ENOTSUP            # no expanded x in the single launch
+    assert call(_args(flags=SL, d=1024, x_mean_out=P + 0xE00)) == H.HC_ENOTSUP   # nor the stream mean
+    assert call(_args(x_mean_out=MIS)) == H.HC_EINVAL                    # misaligned stream-mean output
     assert call(_args(flags=SL)) == H.HC_ENOTSUP                  # d=64: not a multiple of 512
     assert call(_args(flags=SL, d=512)) == H.HC_ENOTSUP           # at least 1024
     assert call(_args(flags=SL, d=1024, fn_packed=None, pre_in=P + 0x600)) == H.HC_EINVAL   # needs the mixes
     assert L.hc_boundary_begin(ctypes.byref(_args(flags=SL, d=1024)), S) == H.HC_EINVAL
     # a caller of the struct without the trailing flags field (shorter struct_size) gets flags 0
     short = H.BoundaryArgs.flags.offset
-    assert call(_args(struct_size=short, flags=4)) in (H.HC_ENODEV, H.HC_OK)
+    assert call(_args(struct_size=short, flags=8)) in (H.HC_ENODEV, H.HC_OK)
+    # ... and without the trailing x_mean_out field, no stream mean
+    assert call(_args(struct_size=H.BoundaryArgs.x_mean_out.offset, x_mean_out=MIS)) in (H.HC_ENODEV, H.HC_OK)
     assert call(_args(struct_size=short - 8)) == H.HC_EINVAL
     for half in (L.hc_boundary_begin, L.hc_boundary_end):          # the halves validate alike
         assert half(None, S) == H.HC_EINVAL

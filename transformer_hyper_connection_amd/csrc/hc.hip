@@ -231,7 +231,9 @@ struct RowArgs {
   const float* gamma;
   hc_bf16* x_out;
   hc_bf16* y_out;
+  hc_bf16* x_mean;    // mean over the streams of X' (MTP tap), or NULL
   int64_t n;
+  int64_t xtok, xstr; // elements per token / per stream of x (hc*d, d; or d, 0 when expanded)
   int d;
   float rms_eps;
 };
@@ -240,10 +242,10 @@ constexpr int kRowChunk = 512;                   // features per wave instructio
 constexpr int kRowMaxChunks = 10;                // per token held in registers (NORM)
 
 template <bool POST>
-__device__ __forceinline__ void row_load(u32x4 (&r)[kHC + 1], const u32x4* xrow, const u32x4* drow, int d,
+__device__ __forceinline__ void row_load(u32x4 (&r)[kHC + 1], const u32x4* xrow, const u32x4* drow, int64_t xstr,
                                          int f) {
 #pragma unroll
-  for (int j = 0; j < kHC; ++j) r[j] = ld_stream(xrow + (j * d + f) / 8);
+  for (int j = 0; j < kHC; ++j) r[j] = ld_stream(xrow + (j * xstr + f) / 8);
   r[kHC] = POST ? ld_stream(drow + f / 8) : u32x4{0u, 0u, 0u, 0u};
 }
 
@@ -273,6 +275,27 @@ __device__ __forceinline__ void post_8(const u32x4 (&r)[kHC + 1], const float* c
       xp[k][e2] = pack_bf16(v[0], v[1]);
     }
   }
+}
+
+// The MTP tap ("Final RMSNorm", the model driver: the mean over the streams of
+// a block's input): (((X'_0 + X'_1) + X'_2) + X'_3) / 4 in fp32, one lane's 8
+// features (the sum of four bf16 values is exact in fp32 but for extreme
+// exponent spreads, and the quarter is exact).
+__device__ __forceinline__ u32x4 mean_8(const u32 (&xp)[kHC][4]) {
+  u32 m[4];
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    float v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float sm = bf_elem(xp[0][e2], h);
+#pragma unroll
+      for (int k = 1; k < kHC; ++k) sm = sm + bf_elem(xp[k][e2], h);
+      v[h] = sm * 0.25f;
+    }
+    m[e2] = pack_bf16(v[0], v[1]);
+  }
+  return u32x4{m[0], m[1], m[2], m[3]};
 }
 
 // y = ((p_0 X'_0 + p_1 X'_1) + p_2 X'_2) + p_3 X'_3, one lane's 8 features
@@ -329,8 +352,8 @@ __global__ void __launch_bounds__(kThreads) row_kernel(const RowArgs a) {
     u32x4 r[TPW][kHC + 1];
 #pragma unroll
     for (int i = 0; i < TPW; ++i)
-      row_load<POST>(r[i], reinterpret_cast<const u32x4*>(a.x + tok[i] * kHC * d),
-                     reinterpret_cast<const u32x4*>(POST ? a.delta + tok[i] * d : a.x), d, f);
+      row_load<POST>(r[i], reinterpret_cast<const u32x4*>(a.x + tok[i] * a.xtok),
+                     reinterpret_cast<const u32x4*>(POST ? a.delta + tok[i] * d : a.x), a.xstr, f);
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const bool st = act && tvalid[i];
@@ -348,6 +371,7 @@ __global__ void __launch_bounds__(kThreads) row_kernel(const RowArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) xp[k][e] = r[i][k][e];
       }
+      if (a.x_mean && st) st_stream(reinterpret_cast<u32x4*>(a.x_mean + tok[i] * d) + f / 8, mean_8(xp));
       if constexpr (PRE) {
         u32 yp[4];
         pre_8(xp, cpre[i], yp);
@@ -455,8 +479,10 @@ struct StreamArgs {
   const u32x4* fn;
   hc_bf16* x_out;
   hc_bf16* y_out;
+  hc_bf16* x_mean;    // mean over the streams of X' (MTP tap), or NULL
   float* rec;         // [tiles][S][kTT][kRec]
   int64_t n;
+  int64_t xtok, xstr; // elements per token / per stream of x (hc*d, d; or d, 0 when expanded)
   int d, S, F, tiles;
 };
 
@@ -507,7 +533,7 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
   const int64_t t0 = (int64_t)tile * kTT;
   const bool tv = t0 + m < a.n;
   const unsigned lt = tv ? (unsigned)m : 0u;   // tokens past n read the tile's first and never store
-  const hc_bf16* xb = a.x + t0 * kHC * d;
+  const hc_bf16* xb = a.x + t0 * a.xtok;
   const hc_bf16* db = POST ? a.delta + t0 * d : a.x;
   hc_bf16* xob = POST ? a.x_out + t0 * kHC * d : nullptr;
   hc_bf16* yb = RM == kGivenPre ? a.y_out + t0 * d : nullptr;
@@ -551,7 +577,7 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
   auto load_stream = [&](int c, u32x4 (&dst)[kHC + 1]) {
     const unsigned f = fs + c * kCF + fl;
 #pragma unroll
-    for (int j = 0; j < kHC; ++j) dst[j] = ld_stream(reinterpret_cast<const u32x4*>(xb + (lt * kHC * d + j * d + f)));
+    for (int j = 0; j < kHC; ++j) dst[j] = ld_stream(reinterpret_cast<const u32x4*>(xb + ((int64_t)lt * a.xtok + j * a.xstr + f)));
     dst[kHC] = POST ? ld_stream(reinterpret_cast<const u32x4*>(db + (lt * d + f))) : u32x4{0u, 0u, 0u, 0u};
   };
   auto stream_phase = [&](int c) {
@@ -573,6 +599,7 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
 #pragma unroll
         for (int e = 0; e < 4; ++e) xp[k][e] = cur[k][e];
     }
+    if (a.x_mean && tv) st_stream(reinterpret_cast<u32x4*>(a.x_mean + (t0 + lt) * d + f), mean_8(xp));
 #pragma unroll
     for (int k = 0; k < kHC; ++k) {
 #pragma unroll
@@ -690,6 +717,7 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
 struct FinishArgs {
   const float* rec;         // [tiles][S][kTT][kRec] from stream_kernel
   const hc_bf16* src;       // fresh pre: X' (or x at a block entry) [n, hc, d]; given pre: y [n, d]
+  int64_t stok, sstr;       // fresh pre: elements per token / per stream of src
   hc_bf16* y_out;
   const float* gamma;
   const float* hc_base;
@@ -846,7 +874,8 @@ __global__ void __launch_bounds__(kFinThreads) finish_kernel(const FinishArgs a)
     for (int j = 0; j < kHC; ++j) p[j] = RM == kFreshPre ? s_pre[lt][j] : 0.f;
     const float r = NORM ? s_r[lt] : 1.f;
     constexpr int NL = RM == kFreshPre ? kHC : 1;
-    const int rstride = RM == kFreshPre ? kHC * d : d;
+    const int64_t rstride = RM == kFreshPre ? a.stok : d;
+    const int64_t sstr = RM == kFreshPre ? a.sstr : 0;
     const hc_bf16* src = a.src + (t0 + lt) * rstride;
     hc_bf16* yrow = a.y_out + (t0 + lt) * d;
     // chunks in batches of U, all loads of a batch in flight at once, last
@@ -860,7 +889,7 @@ __global__ void __launch_bounds__(kFinThreads) finish_kernel(const FinishArgs a)
         if (c >= 0) {
           const unsigned f = fs + c * kCF + fl;
 #pragma unroll
-          for (int k = 0; k < NL; ++k) ld[u][k] = ld_stream(reinterpret_cast<const u32x4*>(src + (k * d + f)));
+          for (int k = 0; k < NL; ++k) ld[u][k] = ld_stream(reinterpret_cast<const u32x4*>(src + (k * sstr + f)));
         }
       }
 #pragma unroll
@@ -1543,10 +1572,12 @@ struct DecArgs {
   const float* hc_scale;
   hc_bf16* x_out;
   hc_bf16* y_out;
+  hc_bf16* x_mean;    // mean over the streams of X' (MTP tap), or NULL
   float* mixes_out;
   float* pre_out;
   float* post_out;
   float* comb_out;
+  int64_t xtok, xstr; // elements per token / per stream of x (hc*d, d; or d, 0 when expanded)
   u64* rec;           // [tiles][S][kDT][kDRec] tagged words
   u64* arrive;        // [kDTiles] arrival words, then the epoch word and the tiles-done word
   u32* err;           // sticky error mask (a wait timed out)
@@ -1601,12 +1632,12 @@ __global__ void __launch_bounds__(kDThreads) decode_kernel(const DecArgs a) {
           B[st][k][nt] = __builtin_bit_cast(bf16x8, a.fn[((size_t)((gstep + st) * kHC + k) * kNT + nt) * 64 + lane]);
   }
   u32x4 r[2][kHC + 1];
-  const hc_bf16* xrow = a.x + (t0 + lt) * kHC * d;
+  const hc_bf16* xrow = a.x + (t0 + lt) * a.xtok;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int f = fs + (2 * p + half) * kCF + fl;
 #pragma unroll
-    for (int j = 0; j < kHC; ++j) r[p][j] = ld_stream(reinterpret_cast<const u32x4*>(xrow + (j * d + f)));
+    for (int j = 0; j < kHC; ++j) r[p][j] = ld_stream(reinterpret_cast<const u32x4*>(xrow + (j * a.xstr + f)));
     r[p][kHC] = POST ? ld_stream(reinterpret_cast<const u32x4*>(a.delta + (t0 + lt) * d + f)) : u32x4{0u, 0u, 0u, 0u};
   }
   float cpost[kHC], ccomb[kHC * kHC], cpre[kHC];
@@ -1638,6 +1669,7 @@ __global__ void __launch_bounds__(kDThreads) decode_kernel(const DecArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) xp[k][e] = r[p][k][e];
     }
+    if (a.x_mean && tv) st_stream(reinterpret_cast<u32x4*>(a.x_mean + (t0 + lt) * d + f), mean_8(xp));
     if constexpr (READ) {
       u32 yp[4];
       pre_8(xp, cpre, yp);
@@ -1930,6 +1962,8 @@ int launch_boundary(bool post, int rm, bool norm, StreamArgs s, FinishArgs f, vo
   f.F2 = s.d / f.S2;
   f.y_out = s.y_out;
   f.src = rm == kFreshPre ? (post ? s.x_out : s.x) : s.y_out;
+  f.stok = post ? (int64_t)kHC * s.d : s.xtok;   // X' as written, or x as given (expanded: stride 0)
+  f.sstr = post ? (int64_t)s.d : s.xstr;
   const unsigned grid2 = (unsigned)(tiles * f.S2);
   if (rm == kFreshPre) e = norm ? launch_finish_t<kFreshPre, true>(f, grid2, st) : launch_finish_t<kFreshPre, false>(f, grid2, st);
   else if (rm == kGivenPre && norm) e = launch_finish_t<kGivenPre, true>(f, grid2, st);
@@ -2150,12 +2184,14 @@ int hc_mixes(const hc_bf16* x, const void* fn_packed, int64_t n, int hc, int d, 
   if (decode_shape(n, d)) {
     DecArgs a{};
     a.n = n; a.d = d; a.x = x; a.fn = reinterpret_cast<const u32x4*>(fn_packed); a.mixes_out = mixes;
+    a.xtok = (int64_t)kHC * d; a.xstr = d;
     a.hc_scale = hc_scale; a.hc_base = hc_base; a.iters = iters; a.hc_eps = hc_eps; a.norm_eps = norm_eps;
     if (split) { a.pre_out = pre; a.post_out = post; a.comb_out = comb; }
     return launch_decode(false, false, a, workspace, workspace_bytes, (hipStream_t)stream, "hc_mixes");
   }
   StreamArgs s{};
   s.n = n; s.d = d; s.x = x; s.fn = reinterpret_cast<const u32x4*>(fn_packed);
+  s.xtok = (int64_t)kHC * d; s.xstr = d;
   FinishArgs f{};
   f.mixes_out = mixes; f.norm_eps = norm_eps; f.hc_scale = hc_scale; f.hc_base = hc_base; f.iters = iters;
   f.hc_eps = hc_eps;
@@ -2172,7 +2208,7 @@ int hc_pre(const hc_bf16* x, const float* pre_mix, int64_t n, int hc, int d, hc_
   if (n == 0) return HC_OK;
   if ((rc = check_device())) return rc;
   RowArgs a{};
-  a.n = n; a.d = d; a.x = x; a.pre_in = pre_mix; a.y_out = y;
+  a.n = n; a.d = d; a.x = x; a.pre_in = pre_mix; a.y_out = y; a.xtok = (int64_t)kHC * d; a.xstr = d;
   return launch_row(false, true, false, a, (hipStream_t)stream, "hc_pre");
 }
 
@@ -2188,6 +2224,7 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
   if ((rc = check_device())) return rc;
   RowArgs a{};
   a.n = n; a.d = d; a.delta = delta; a.x = x; a.post_in = post; a.comb_in = comb; a.x_out = x_out;
+  a.xtok = (int64_t)kHC * d; a.xstr = d;
   return launch_row(true, false, false, a, (hipStream_t)stream, "hc_post");
 }
 
@@ -2200,7 +2237,11 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
   if (p->struct_size < kNoFlags)
     return fail(HC_EINVAL, "struct_size=%u, expected %zu", p->struct_size, sizeof(hc_boundary_args));
   const uint32_t flags = p->struct_size >= kNoFlags + sizeof(uint32_t) ? p->flags : 0u;
-  if (flags & ~HC_BOUNDARY_SINGLE_LAUNCH) return fail(HC_EINVAL, "flags=%#x: unknown bits", flags);
+  constexpr size_t kNoMean = offsetof(hc_boundary_args, x_mean_out);   // callers of the struct without it
+  hc_bf16* const x_mean = p->struct_size >= kNoMean + sizeof(void*) ? p->x_mean_out : nullptr;
+  if (flags & ~(HC_BOUNDARY_SINGLE_LAUNCH | HC_BOUNDARY_X_EXPANDED))
+    return fail(HC_EINVAL, "flags=%#x: unknown bits", flags);
+  const bool expanded = (flags & HC_BOUNDARY_X_EXPANDED) != 0;
   int rc = check_hd(p->hc, p->d);
   if (rc) return rc;
   if ((rc = check_n(p->n))) return rc;
@@ -2208,7 +2249,7 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
   const bool mix = p->fn_packed != nullptr;
   const bool fresh = p->pre_in == nullptr;
   const bool norm = p->gamma != nullptr;
-  HC_REQ(p->x); HC_REQ(p->y_out); HC_OPT(p->delta); HC_OPT(p->pre_in); HC_OPT(p->gamma);
+  HC_REQ(p->x); HC_REQ(p->y_out); HC_OPT(p->delta); HC_OPT(p->pre_in); HC_OPT(p->gamma); HC_OPT(x_mean);
   if (post) { HC_REQ(p->post_in); HC_REQ(p->comb_in); HC_REQ(p->x_out);
     if (p->x_out == p->x) return fail(HC_EINVAL, "x_out must not alias x"); }
   if (mix) {
@@ -2220,6 +2261,7 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
   if (norm && p->d > kRowChunk * kRowMaxChunks * 2)
     return fail(HC_ENOTSUP, "RMSNorm of the read row supports d <= %d", kRowChunk * kRowMaxChunks * 2);
   if (flags & HC_BOUNDARY_SINGLE_LAUNCH) {
+    if (expanded || x_mean) return fail(HC_ENOTSUP, "the single-launch schedule takes neither expanded streams nor x_mean_out");
     if (phases != 3) return fail(HC_EINVAL, "the single-launch schedule has no halves (use hc_boundary)");
     if (!mix) return fail(HC_EINVAL, "the single-launch schedule needs fn_packed");
     if (!fused_shape(p->d)) return fail(HC_ENOTSUP, "single launch: d=%d must be a multiple of %d, at least %d", p->d, kFF, kFMinD);
@@ -2228,12 +2270,15 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
   if (p->n == 0) return HC_OK;
   if ((rc = check_device())) return rc;
   const hipStream_t st = (hipStream_t)stream;
+  const int64_t xtok = expanded ? (int64_t)p->d : (int64_t)kHC * p->d;   // expanded: every stream reads x
+  const int64_t xstr = expanded ? 0 : (int64_t)p->d;
 
   if (!mix) {  // stack exit: write, read (+ norm); no projection; one kernel, the first phase
     if (!(phases & 1)) return HC_OK;
     RowArgs r{};
     r.n = p->n; r.d = p->d; r.x = p->x; r.delta = p->delta; r.post_in = p->post_in; r.comb_in = p->comb_in;
     r.pre_in = p->pre_in; r.gamma = p->gamma; r.x_out = p->x_out; r.y_out = p->y_out; r.rms_eps = p->rms_eps;
+    r.xtok = xtok; r.xstr = xstr; r.x_mean = x_mean;
     return launch_row(post, true, norm, r, st, "hc_boundary (exit)");
   }
   if (flags & HC_BOUNDARY_SINGLE_LAUNCH) {
@@ -2252,13 +2297,13 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
     a.pre_in = p->pre_in; a.fn = reinterpret_cast<const u32x4*>(p->fn_packed); a.hc_base = p->hc_base;
     a.hc_scale = p->hc_scale; a.x_out = p->x_out; a.y_out = p->y_out; a.mixes_out = p->mixes_out;
     a.pre_out = p->pre_out; a.post_out = p->post_out; a.comb_out = p->comb_out; a.iters = p->iters;
-    a.hc_eps = p->hc_eps; a.norm_eps = p->norm_eps;
+    a.hc_eps = p->hc_eps; a.norm_eps = p->norm_eps; a.xtok = xtok; a.xstr = xstr; a.x_mean = x_mean;
     return launch_decode(post, true, a, p->workspace, p->workspace_bytes, st, "hc_boundary");
   }
   StreamArgs s{};
   s.n = p->n; s.d = p->d; s.x = p->x; s.delta = p->delta; s.post_in = p->post_in; s.comb_in = p->comb_in;
   s.pre_in = p->pre_in; s.fn = reinterpret_cast<const u32x4*>(p->fn_packed); s.x_out = p->x_out;
-  s.y_out = p->y_out;
+  s.y_out = p->y_out; s.xtok = xtok; s.xstr = xstr; s.x_mean = x_mean;
   FinishArgs f{};
   f.gamma = p->gamma; f.hc_base = p->hc_base; f.hc_scale = p->hc_scale; f.mixes_out = p->mixes_out;
   f.pre_out = p->pre_out; f.post_out = p->post_out; f.comb_out = p->comb_out; f.iters = p->iters;

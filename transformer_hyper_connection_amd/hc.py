@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhc.so")
 
 HC_OK, HC_EINVAL, HC_ENOTSUP, HC_EHIP, HC_ENODEV = 0, -1, -2, -3, -4
 HC_BOUNDARY_SINGLE_LAUNCH = 1
+HC_BOUNDARY_X_EXPANDED = 4
 
 
 class HCError(RuntimeError):
@@ -39,7 +40,7 @@ class BoundaryArgs(ctypes.Structure):
         ("hc_scale", c_void_p), ("gamma", c_void_p), ("x_out", c_void_p), ("y_out", c_void_p),
         ("mixes_out", c_void_p), ("pre_out", c_void_p), ("post_out", c_void_p),
         ("comb_out", c_void_p), ("workspace", c_void_p), ("workspace_bytes", c_size_t),
-        ("flags", c_uint32),
+        ("flags", c_uint32), ("x_mean_out", c_void_p),
     ]
 
 
@@ -234,12 +235,21 @@ def hc_post(x, residual, post, comb, out=None):
 def _prepare_boundary(x, *, delta=None, post_in=None, comb_in=None, pre_in=None, fn_packed=None,
                       hc_base=None, hc_scale=None, gamma=None, iters: int = 20, hc_eps: float = 1e-6,
                       norm_eps: float = 1e-6, rms_eps: float = 1e-6, out: dict | None = None,
-                      want_mixes: bool = False, single_launch: bool = False):
+                      want_mixes: bool = False, single_launch: bool = False, x_expanded: bool = False,
+                      want_mean: bool = False):
     """Checks the arguments of one boundary call, allocates missing outputs and
     fills the C argument struct.  Returns (struct, outputs)."""
     dev = x.device
     _need(x, "x", torch.bfloat16)
-    lead, n, hc, d = _streams_shape(x)
+    if x_expanded:                   # x [..., d]: every stream is that row
+        if x.dim() < 1:
+            raise ValueError("an expanded x must be [..., d]")
+        lead, d, hc = tuple(x.shape[:-1]), x.shape[-1], 4
+        n = 1
+        for v in lead:
+            n *= v
+    else:
+        lead, n, hc, d = _streams_shape(x)
     mix = (2 + hc) * hc
     o = dict(out or {})
 
@@ -260,6 +270,8 @@ def _prepare_boundary(x, *, delta=None, post_in=None, comb_in=None, pre_in=None,
     if gamma is not None:
         _need(gamma, "gamma", torch.float32, dev, (d,))
     alloc("y", (*lead, d), torch.bfloat16)
+    if want_mean or o.get("x_mean") is not None:
+        alloc("x_mean", (*lead, d), torch.bfloat16)
     if fn_packed is not None:
         _need(fn_packed, "fn_packed", torch.uint8, dev)
         _need(hc_base, "hc_base", torch.float32, dev, (mix,))
@@ -278,7 +290,8 @@ def _prepare_boundary(x, *, delta=None, post_in=None, comb_in=None, pre_in=None,
     a.gamma, a.x_out, a.y_out = _ptr(gamma), _ptr(o.get("x_out")), o["y"].data_ptr()
     a.mixes_out, a.pre_out = _ptr(o.get("mixes")), _ptr(o.get("pre"))
     a.post_out, a.comb_out = _ptr(o.get("post")), _ptr(o.get("comb"))
-    a.flags = HC_BOUNDARY_SINGLE_LAUNCH if single_launch else 0
+    a.flags = (HC_BOUNDARY_SINGLE_LAUNCH if single_launch else 0) | (HC_BOUNDARY_X_EXPANDED if x_expanded else 0)
+    a.x_mean_out = _ptr(o.get("x_mean"))
     if fn_packed is not None:
         ws = o.get("workspace")
         if ws is None:
@@ -293,8 +306,10 @@ def hc_boundary(x, **kw):
     """One fused sublayer boundary (see include/hc.h).  Keyword arguments:
     delta, post_in, comb_in, pre_in, fn_packed, hc_base, hc_scale, gamma, iters,
     hc_eps, norm_eps, rms_eps, out, want_mixes, single_launch (the
-    HC_BOUNDARY_SINGLE_LAUNCH schedule).  Returns a dict with x_out (None
-    at a block entry), y, and pre/post/comb (+ mixes) unless fn_packed is None.
+    HC_BOUNDARY_SINGLE_LAUNCH schedule), x_expanded (x is [..., d], every
+    stream that row: HC_BOUNDARY_X_EXPANDED), want_mean (the mean over the
+    streams, "x_mean").  Returns a dict with x_out (None at a block entry), y,
+    and pre/post/comb (+ mixes) unless fn_packed is None.
     ``out`` may hold preallocated outputs under the same keys (and a
     "workspace"); they are used as given."""
     a, o = _prepare_boundary(x, **kw)
