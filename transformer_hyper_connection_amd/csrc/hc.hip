@@ -233,7 +233,7 @@ struct RowArgs {
   hc_bf16* y_out;
   hc_bf16* x_mean;    // mean over the streams of X' (MTP tap), or NULL
   int64_t n;
-  int64_t xtok, xstr; // elements per token / per stream of x (hc*d, d; or d, 0 when expanded)
+  int xtok, xstr;     // elements per token / per stream of x (hc*d, d; or d, 0 when expanded)
   int d;
   float rms_eps;
 };
@@ -242,7 +242,7 @@ constexpr int kRowChunk = 512;                   // features per wave instructio
 constexpr int kRowMaxChunks = 10;                // per token held in registers (NORM)
 
 template <bool POST>
-__device__ __forceinline__ void row_load(u32x4 (&r)[kHC + 1], const u32x4* xrow, const u32x4* drow, int64_t xstr,
+__device__ __forceinline__ void row_load(u32x4 (&r)[kHC + 1], const u32x4* xrow, const u32x4* drow, int xstr,
                                          int f) {
 #pragma unroll
   for (int j = 0; j < kHC; ++j) r[j] = ld_stream(xrow + (j * xstr + f) / 8);
@@ -482,7 +482,7 @@ struct StreamArgs {
   hc_bf16* x_mean;    // mean over the streams of X' (MTP tap), or NULL
   float* rec;         // [tiles][S][kTT][kRec]
   int64_t n;
-  int64_t xtok, xstr; // elements per token / per stream of x (hc*d, d; or d, 0 when expanded)
+  int xtok, xstr;     // elements per token / per stream of x (hc*d, d; or d, 0 when expanded)
   int d, S, F, tiles;
 };
 
@@ -503,7 +503,9 @@ __device__ __forceinline__ int a_swz(int L, int st) { return L ^ (((L >> 4) & 3)
 // a store that the finish kernel reads back soon (kept cacheable)
 __device__ __forceinline__ void st_keep(u32x4* p, u32x4 v) { *p = v; }
 
-template <bool POST, int RM, bool NORM>
+// MEAN: the stream mean (x_mean) is written; a template parameter so that the
+// calls without it carry none of its registers
+template <bool POST, int RM, bool NORM, bool MEAN>
 __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a) {
   static_assert(!NORM || RM != kNoRead, "RMSNorm needs the read row");
   __shared__ u32x4 w_lds[2][2][kHC][kNT][64];          // weight tiles, double buffered (80 KB)
@@ -577,7 +579,7 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
   auto load_stream = [&](int c, u32x4 (&dst)[kHC + 1]) {
     const unsigned f = fs + c * kCF + fl;
 #pragma unroll
-    for (int j = 0; j < kHC; ++j) dst[j] = ld_stream(reinterpret_cast<const u32x4*>(xb + ((int64_t)lt * a.xtok + j * a.xstr + f)));
+    for (int j = 0; j < kHC; ++j) dst[j] = ld_stream(reinterpret_cast<const u32x4*>(xb + (lt * (unsigned)a.xtok + j * (unsigned)a.xstr + f)));
     dst[kHC] = POST ? ld_stream(reinterpret_cast<const u32x4*>(db + (lt * d + f))) : u32x4{0u, 0u, 0u, 0u};
   };
   auto stream_phase = [&](int c) {
@@ -599,7 +601,9 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
 #pragma unroll
         for (int e = 0; e < 4; ++e) xp[k][e] = cur[k][e];
     }
-    if (a.x_mean && tv) st_stream(reinterpret_cast<u32x4*>(a.x_mean + (t0 + lt) * d + f), mean_8(xp));
+    if constexpr (MEAN) {
+      if (tv) st_stream(reinterpret_cast<u32x4*>(a.x_mean + (t0 + lt) * d + f), mean_8(xp));
+    }
 #pragma unroll
     for (int k = 0; k < kHC; ++k) {
 #pragma unroll
@@ -717,7 +721,7 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
 struct FinishArgs {
   const float* rec;         // [tiles][S][kTT][kRec] from stream_kernel
   const hc_bf16* src;       // fresh pre: X' (or x at a block entry) [n, hc, d]; given pre: y [n, d]
-  int64_t stok, sstr;       // fresh pre: elements per token / per stream of src
+  int stok, sstr;           // fresh pre: elements per token / per stream of src
   hc_bf16* y_out;
   const float* gamma;
   const float* hc_base;
@@ -874,8 +878,8 @@ __global__ void __launch_bounds__(kFinThreads) finish_kernel(const FinishArgs a)
     for (int j = 0; j < kHC; ++j) p[j] = RM == kFreshPre ? s_pre[lt][j] : 0.f;
     const float r = NORM ? s_r[lt] : 1.f;
     constexpr int NL = RM == kFreshPre ? kHC : 1;
-    const int64_t rstride = RM == kFreshPre ? a.stok : d;
-    const int64_t sstr = RM == kFreshPre ? a.sstr : 0;
+    const int rstride = RM == kFreshPre ? a.stok : d;
+    const int sstr = RM == kFreshPre ? a.sstr : 0;
     const hc_bf16* src = a.src + (t0 + lt) * rstride;
     hc_bf16* yrow = a.y_out + (t0 + lt) * d;
     // chunks in batches of U, all loads of a batch in flight at once, last
@@ -1577,7 +1581,7 @@ struct DecArgs {
   float* pre_out;
   float* post_out;
   float* comb_out;
-  int64_t xtok, xstr; // elements per token / per stream of x (hc*d, d; or d, 0 when expanded)
+  int xtok, xstr;     // elements per token / per stream of x (hc*d, d; or d, 0 when expanded)
   u64* rec;           // [tiles][S][kDT][kDRec] tagged words
   u64* arrive;        // [kDTiles] arrival words, then the epoch word and the tiles-done word
   u32* err;           // sticky error mask (a wait timed out)
@@ -1913,7 +1917,9 @@ template <bool POST, int RM, bool NORM>
 hipError_t launch_stream_t(const StreamArgs& a, unsigned grid, hipStream_t st) {
   StreamArgs copy = a;
   void* args[] = {&copy};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&stream_kernel<POST, RM, NORM>), dim3(grid), dim3(kThreads),
+  const void* fn = a.x_mean ? reinterpret_cast<const void*>(&stream_kernel<POST, RM, NORM, true>)
+                            : reinterpret_cast<const void*>(&stream_kernel<POST, RM, NORM, false>);
+  return hipLaunchKernel(fn, dim3(grid), dim3(kThreads),
                          args, 0, st);
 }
 template <int RM, bool NORM>
@@ -1962,8 +1968,8 @@ int launch_boundary(bool post, int rm, bool norm, StreamArgs s, FinishArgs f, vo
   f.F2 = s.d / f.S2;
   f.y_out = s.y_out;
   f.src = rm == kFreshPre ? (post ? s.x_out : s.x) : s.y_out;
-  f.stok = post ? (int64_t)kHC * s.d : s.xtok;   // X' as written, or x as given (expanded: stride 0)
-  f.sstr = post ? (int64_t)s.d : s.xstr;
+  f.stok = post ? kHC * s.d : s.xtok;   // X' as written, or x as given (expanded: stride 0)
+  f.sstr = post ? s.d : s.xstr;
   const unsigned grid2 = (unsigned)(tiles * f.S2);
   if (rm == kFreshPre) e = norm ? launch_finish_t<kFreshPre, true>(f, grid2, st) : launch_finish_t<kFreshPre, false>(f, grid2, st);
   else if (rm == kGivenPre && norm) e = launch_finish_t<kGivenPre, true>(f, grid2, st);
@@ -2184,14 +2190,14 @@ int hc_mixes(const hc_bf16* x, const void* fn_packed, int64_t n, int hc, int d, 
   if (decode_shape(n, d)) {
     DecArgs a{};
     a.n = n; a.d = d; a.x = x; a.fn = reinterpret_cast<const u32x4*>(fn_packed); a.mixes_out = mixes;
-    a.xtok = (int64_t)kHC * d; a.xstr = d;
+    a.xtok = kHC * d; a.xstr = d;
     a.hc_scale = hc_scale; a.hc_base = hc_base; a.iters = iters; a.hc_eps = hc_eps; a.norm_eps = norm_eps;
     if (split) { a.pre_out = pre; a.post_out = post; a.comb_out = comb; }
     return launch_decode(false, false, a, workspace, workspace_bytes, (hipStream_t)stream, "hc_mixes");
   }
   StreamArgs s{};
   s.n = n; s.d = d; s.x = x; s.fn = reinterpret_cast<const u32x4*>(fn_packed);
-  s.xtok = (int64_t)kHC * d; s.xstr = d;
+  s.xtok = kHC * d; s.xstr = d;
   FinishArgs f{};
   f.mixes_out = mixes; f.norm_eps = norm_eps; f.hc_scale = hc_scale; f.hc_base = hc_base; f.iters = iters;
   f.hc_eps = hc_eps;
@@ -2208,7 +2214,7 @@ int hc_pre(const hc_bf16* x, const float* pre_mix, int64_t n, int hc, int d, hc_
   if (n == 0) return HC_OK;
   if ((rc = check_device())) return rc;
   RowArgs a{};
-  a.n = n; a.d = d; a.x = x; a.pre_in = pre_mix; a.y_out = y; a.xtok = (int64_t)kHC * d; a.xstr = d;
+  a.n = n; a.d = d; a.x = x; a.pre_in = pre_mix; a.y_out = y; a.xtok = kHC * d; a.xstr = d;
   return launch_row(false, true, false, a, (hipStream_t)stream, "hc_pre");
 }
 
@@ -2224,7 +2230,7 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
   if ((rc = check_device())) return rc;
   RowArgs a{};
   a.n = n; a.d = d; a.delta = delta; a.x = x; a.post_in = post; a.comb_in = comb; a.x_out = x_out;
-  a.xtok = (int64_t)kHC * d; a.xstr = d;
+  a.xtok = kHC * d; a.xstr = d;
   return launch_row(true, false, false, a, (hipStream_t)stream, "hc_post");
 }
 
@@ -2270,8 +2276,8 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
   if (p->n == 0) return HC_OK;
   if ((rc = check_device())) return rc;
   const hipStream_t st = (hipStream_t)stream;
-  const int64_t xtok = expanded ? (int64_t)p->d : (int64_t)kHC * p->d;   // expanded: every stream reads x
-  const int64_t xstr = expanded ? 0 : (int64_t)p->d;
+  const int xtok = expanded ? p->d : kHC * p->d;   // expanded: every stream reads x
+  const int xstr = expanded ? 0 : p->d;
 
   if (!mix) {  // stack exit: write, read (+ norm); no projection; one kernel, the first phase
     if (!(phases & 1)) return HC_OK;
