@@ -44,8 +44,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_boundary_prefill_t4096.js
 #                    per call   hc_fn (fp32) 24*4d*4 + base 96 + scale 12 + gamma d*4
 BYTES_TOKEN_COMMON = 4 * D * 2 + D * 2 + 4 * D * 2 + D * 2 + 16 + 64 + 96
 BYTES_CALL = MIX * 4 * D * 4 + MIX * 4 + 3 * 4 + D * 4
-KERNELS = {"fresh": ("stream_kernel<true, 2, true>", "finish_kernel<2, true>"),
-           "lag": ("stream_kernel<true, 1, true>", "finish_kernel<1, true>")}
+KERNELS = {"fresh": ("stream_kernel<true, 2, true, false>", "finish_kernel<2, true>"),
+           "lag": ("stream_kernel<true, 1, true, false>", "finish_kernel<1, true>")}
 
 
 def algorithmic_bytes(n: int, mode: str) -> int:
