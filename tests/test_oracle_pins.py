@@ -487,3 +487,53 @@ def test_boundary_expanded_entry_equals_repeated_streams():
         assert np.array_equal(a[k], b[k])
     assert np.array_equal(a["y"], h)          # 0.25 on four copies reads the embedding back
     assert np.array_equal(a["x_mean"], h)     # and the tap of four copies is the embedding
+
+
+# ------------------------------------------------------------ other stream counts (hc = 2, 8)
+def _uniform_closed_form_hc(iters, eps, hc):
+    """Equal logits on an hc x hc comb: a -> a/(hc*a + eps) from a0 = 1/hc + eps,
+    2*iters-1 times; with b = 1/a, b -> hc + eps*b, exact in rationals."""
+    e = Fraction(eps)
+    b = 1 / (Fraction(1, hc) + e)
+    for _ in range(2 * iters - 1):
+        b = hc + e * b
+    return 1 / b
+
+
+@pytest.mark.parametrize("hc", [2, 8])
+@pytest.mark.parametrize("iters", [1, 20])
+def test_sinkhorn_uniform_logits_other_hc(hc, iters):
+    eps = float(np.float32(1e-6))
+    A = O.sinkhorn(np.full((2, hc, hc), -0.3), iters, 1e-6)
+    np.testing.assert_allclose(A, float(_uniform_closed_form_hc(iters, eps, hc)), rtol=1e-14)
+
+
+@pytest.mark.parametrize("hc", [2, 8])
+def test_hc_post_pre_other_hc(hc):
+    n, d = 3, 48
+    x = rand_bf16((n, hc, d)); delta = rand_bf16((n, d))
+    eye = np.broadcast_to(np.eye(hc, dtype=np.float32), (n, hc, hc)).copy()
+    assert np.array_equal(O.hc_post(delta, x, np.zeros((n, hc), np.float32), eye), x)
+    perm = np.roll(np.arange(hc), 1)
+    P = np.zeros((n, hc, hc), np.float32)
+    P[:, np.arange(hc), perm] = 1.0                       # source j -> destination perm[j]
+    out = O.hc_post(delta, x, np.zeros((n, hc), np.float32), P)
+    for j in range(hc):
+        assert np.array_equal(out[:, perm[j]], x[:, j])
+    h = rand_bf16((n, d))
+    same = np.repeat(h[:, None], hc, axis=1)
+    assert np.array_equal(O.hc_pre(same, np.full((n, hc), 1.0 / hc, np.float32)), h)
+
+
+@pytest.mark.parametrize("hc", [2, 8])
+def test_split_slices_other_hc(hc):
+    mix = (2 + hc) * hc
+    m = rng.standard_normal((4, mix)).astype(np.float32)
+    base = (rng.standard_normal(mix) * 0.1).astype(np.float32)
+    scale = np.array([1.0, 1.5, 0.8], np.float32)
+    pre, post, comb = O.hc_split_sinkhorn(m, scale, base, hc, 20, 1e-6)
+    assert pre.shape == (4, hc) and post.shape == (4, hc) and comb.shape == (4, hc, hc)
+    s = lambda u: 1.0 / (1.0 + np.exp(-u))                # noqa: E731
+    np.testing.assert_allclose(pre, s(m[:, :hc].astype(np.float64) * 1.0 + base[:hc]) + 1e-6, rtol=1e-6)
+    np.testing.assert_allclose(post, 2 * s(m[:, hc:2 * hc].astype(np.float64) * 1.5 + base[hc:2 * hc]), rtol=1e-6)
+    np.testing.assert_allclose(comb.sum(axis=1), 1.0, atol=1e-3)   # columns normalised last
