@@ -4,7 +4,8 @@
  *
  * In a Hyper-Connections block the residual is hc parallel copies ("streams")
  * of width d.  Around every sublayer the glue
- *   - derives 24 mix numbers per token from the streams (hc_mixes),
+ *   - derives (2+hc)*hc mix numbers per token from the streams (hc_mixes;
+ *     24 at hc = 4),
  *   - turns them into reading weights pre, writing weights post and a
  *     Sinkhorn-normalised hc x hc combination comb (hc_split_sinkhorn),
  *   - reads the streams into one sublayer input (hc_pre),
@@ -20,9 +21,11 @@
  *     allocates no memory in any compute entry point.
  *   - bf16 tensors are passed as raw bit patterns (hc_bf16) and must be 16-byte
  *     aligned; float tensors must be 16-byte aligned.
- *   - n = number of tokens (batch x positions, flattened).  hc must be 4.
- *     d must be a positive multiple of 64 and at most 32768 (at most 10240
- *     where the read row is RMS-normalised).
+ *   - n = number of tokens (batch x positions, flattened).  hc is 2, 4 or 8;
+ *     hc = 4 (the pages' setting) runs the matrix-core kernels, hc = 2 and 8
+ *     a plainer schedule of separate launches (fp32 multiply-adds for the
+ *     projection, weights unpacked).  d must be a positive multiple of 64
+ *     and at most 32768 (at most 10240 where the read row is RMS-normalised).
  *   - stream is a hipStream_t (NULL = the null stream).  Calls enqueue work on
  *     it and return without synchronising; the current HIP device of the
  *     calling thread is used.  Calls on distinct streams may run concurrently
@@ -50,7 +53,7 @@ typedef uint16_t hc_bf16; /* raw bf16 bit pattern */
 enum hc_status {
   HC_OK = 0,
   HC_EINVAL = -1,  /* NULL or misaligned pointer, negative size, iters < 1, ... */
-  HC_ENOTSUP = -2, /* hc != 4, d not a multiple of 64, or d too large          */
+  HC_ENOTSUP = -2, /* hc not 2/4/8, d not a multiple of 64, or d too large    */
   HC_EHIP = -3,    /* a HIP call or kernel launch failed                        */
   HC_ENODEV = -4   /* no HIP device is visible                                  */
 };
@@ -72,7 +75,8 @@ const char* hc_last_error(void);
  * The compute entry points take it pre-packed: each fp32 weight is split into
  * three bf16 terms hi + mid + lo (each the nearest bf16 to what the previous
  * terms leave), which together hold the fp32 value to about 2^-26 relative,
- * laid out in the tile order of the matrix-core kernels.  Pack once per
+ * laid out in the tile order of the matrix-core kernels (hc = 4).  For hc
+ * = 2 and 8 the packed weight is an fp32 copy of hc_fn.  Pack once per
  * parameter set.
  * ------------------------------------------------------------------------- */
 
@@ -93,9 +97,12 @@ int hc_fn_pack(const float* hc_fn, int hc, int d, void* fn_packed, void* stream)
  * workspace of the size asked for some (n, d) serves every call that needs no
  * more).  Calls that may run concurrently (different streams) need different
  * workspaces; calls on one stream can share one, also when captured in a
- * graph and replayed.
+ * graph and replayed.  For hc = 2 and 8 the workspace only holds the mixes
+ * when the caller passes no mixes output (they are then needed between two
+ * launches); it is placed after the regions an hc = 4 call of the same d
+ * keeps, so one workspace may serve calls of every hc.
  *
- * Decode schedule.  For n <= 128 with d a multiple of 256, hc_mixes, and
+ * Decode schedule (hc = 4).  For n <= 128 with d a multiple of 256, hc_mixes, and
  * hc_boundary with a given pre_in and no gamma (the pages' data flow at
  * decode), run as one launch: 16-token tiles by 256-feature slices, each
  * slice adding its per-token partial sums to the workspace as tagged words
@@ -179,6 +186,9 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
  * the X' streams, i.e. of the y before its bf16 rounding, so that the row
  * need not wait for its own mean square; the two differ by a relative 2^-8 at
  * most (from the rounding of y), which moves z by at most half a bf16 ulp.
+ * (hc = 2 and 8 take the mean square of the bf16 y in every case, running the
+ * write, the projection, the split and the read as separate launches: begin
+ * enqueues the write, and the read when pre_in is given; end the rest.)
  * With pre_in given the call follows the pages' data flow: the streams are
  * read with the reading mix of the previous boundary and the call returns the
  * (pre, post, comb) of this boundary for the next one.  Use delta == NULL at a
@@ -190,7 +200,7 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
  * HC_BOUNDARY_X_EXPANDED for an expanded x (below); a caller built against a
  * header without this field passes the shorter struct_size and gets 0.
  *
- * HC_BOUNDARY_SINGLE_LAUNCH (d a multiple of 512, at least 1024): the whole
+ * HC_BOUNDARY_SINGLE_LAUNCH (hc = 4, d a multiple of 512, at least 1024): the whole
  * call as one persistent launch that keeps X' on chip for the read row instead
  * of re-reading it, the feature slices of a token tile exchanging per-token
  * partial sums through the workspace as tagged words (the first 8 KB of the
@@ -234,9 +244,10 @@ typedef struct hc_boundary_args {
   uint32_t flags;          /* 0, HC_BOUNDARY_SINGLE_LAUNCH, HC_BOUNDARY_X_EXPANDED */
   /* [n, d] bf16 or NULL: the mean over the hc streams of the new streams (x_out,
    * or x at a block entry), the MTP head's tap of a block's input ("Final
-   * RMSNorm", the model driver); (((X'_0 + X'_1) + X'_2) + X'_3) / 4 in fp32,
-   * rounded to bf16.  Not with HC_BOUNDARY_SINGLE_LAUNCH.  A caller built
-   * against a header without this field passes the shorter struct_size. */
+   * RMSNorm", the model driver); the streams summed in fp32 in stream order
+   * (((X'_0 + X'_1) + X'_2) + X'_3 at hc = 4), times 1/hc, rounded to bf16.
+   * Not with HC_BOUNDARY_SINGLE_LAUNCH.  A caller built against a header
+   * without this field passes the shorter struct_size. */
   hc_bf16* x_mean_out;
 } hc_boundary_args;
 

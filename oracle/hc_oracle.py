@@ -266,7 +266,7 @@ def stream_mean(x: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 def boundary(*, x, delta=None, post_in=None, comb_in=None, pre_in=None,
              hc_fn=None, hc_base=None, hc_scale=None, gamma=None,
-             iters=20, hc_eps=1e-6, norm_eps=1e-6, rms_eps=1e-6, hc=4,
+             iters=20, hc_eps=1e-6, norm_eps=1e-6, rms_eps=1e-6, hc=None,
              x_expanded=False, want_mean=False):
     """One sublayer boundary: write the streams with the previous sublayer's
     (post, comb) and output delta, derive this boundary's (pre, post, comb)
@@ -279,7 +279,8 @@ def boundary(*, x, delta=None, post_in=None, comb_in=None, pre_in=None,
                       shows); pre_in None -> read with the pre just derived.
     * gamma given  -> the read row is RMS-normalised (rms_eps) before return.
     * x_expanded   -> x is [n, d]: the streams are hc copies of it (the
-                      driver's entry expansion).
+                      driver's entry expansion; hc defaults to 4).  Otherwise
+                      hc is the stream count of x.
     * want_mean    -> also the MTP tap of the new streams (stream_mean).
 
     Returns a dict with x_out (bf16 bits, None on entry), y (bf16 bits:
@@ -288,7 +289,8 @@ def boundary(*, x, delta=None, post_in=None, comb_in=None, pre_in=None,
     """
     x = np.asarray(x, dtype=np.uint16)
     if x_expanded:
-        x = expand_streams(x, hc)
+        x = expand_streams(x, 4 if hc is None else hc)
+    hc = x.shape[1]
     xp = x if delta is None else hc_post(delta, x, post_in, comb_in)
     out = {"x_out": None if delta is None else xp,
            "mixes": None, "pre": None, "post": None, "comb": None}

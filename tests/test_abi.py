@@ -92,7 +92,22 @@ def test_packed_and_workspace_bytes(L):
     assert L.hc_workspace_bytes(64, 4, 320) == 8192 + 1 * 5 * 64 * 36 * 4
 
 
-@pytest.mark.parametrize("hc,d,code", [(3, 5120, H.HC_ENOTSUP), (8, 5120, H.HC_ENOTSUP), (4, 100, H.HC_ENOTSUP),
+def test_packed_and_workspace_bytes_other_hc(L):
+    # hc = 2 and 8: the packed weight is the fp32 weight itself
+    assert L.hc_fn_packed_bytes(2, 5120) == 8 * 2 * 5120 * 4
+    assert L.hc_fn_packed_bytes(8, 4096) == 80 * 8 * 4096 * 4
+    assert L.hc_fn_packed_bytes(8, 100) == 0
+    assert L.hc_fn_packed_bytes(16, 4096) == 0
+    # the workspace holds the mixes after the hc = 4 control block and decode region of the same d
+    decode = 256 + 8 * 20 * 16 * 25 * 8
+    assert L.hc_workspace_bytes(4096, 8, 5120) == 8192 + decode + 4096 * 80 * 4
+    assert L.hc_workspace_bytes(100, 2, 320) == 8192 + 3328       # 100 x 8 floats, rounded up to 256 B
+    assert L.hc_workspace_bytes(0, 8, 5120) == 0
+    assert L.hc_boundary_workspace_bytes(7, 2, 1024) == L.hc_workspace_bytes(7, 2, 1024)
+
+
+@pytest.mark.parametrize("hc,d,code", [(3, 5120, H.HC_ENOTSUP), (16, 5120, H.HC_ENOTSUP), (1, 64, H.HC_ENOTSUP),
+                                       (4, 100, H.HC_ENOTSUP), (2, 100, H.HC_ENOTSUP), (8, 0, H.HC_ENOTSUP),
                                        (4, 0, H.HC_ENOTSUP), (4, 5152, H.HC_ENOTSUP),
                                        (4, 32832, H.HC_ENOTSUP)])
 def test_unsupported_shapes(L, hc, d, code):
@@ -116,6 +131,10 @@ def test_null_misaligned_negative(L):
     assert L.hc_mixes(P, P, 16, 4, 64, 1e-6, None, P, P, 20, 1e-6, P, None, P, *W, S) == H.HC_EINVAL  # partial split
     assert L.hc_split_sinkhorn(P, P, P, 16, 4, 0, 1e-6, P, P, P, S) == H.HC_EINVAL
     assert L.hc_split_sinkhorn(P, P, P, 16, 3, 20, 1e-6, P, P, P, S) == H.HC_ENOTSUP
+    # hc = 8 without a mixes output keeps the mixes in the workspace: it must hold them
+    assert L.hc_mixes(P, P, 16, 8, 64, 1e-6, None, P, P, 20, 1e-6, P, P, P, P, 4096, S) == H.HC_EINVAL
+    assert b"workspace" in L.hc_last_error()
+    assert L.hc_mixes(P, P, 16, 8, 64, 1e-6, None, P, P, 20, 1e-6, P, P, P, MIS, 1 << 30, S) == H.HC_EINVAL
     assert L.hc_split_sinkhorn(P, P, None, 16, 4, 20, 1e-6, P, P, P, S) == H.HC_EINVAL
 
 
@@ -145,7 +164,7 @@ def test_boundary_validation(L):
     call = lambda a: L.hc_boundary(ctypes.byref(a), S)  # noqa: E731
     assert L.hc_boundary(None, S) == H.HC_EINVAL
     assert call(_args(struct_size=8)) == H.HC_EINVAL
-    assert call(_args(hc=2)) == H.HC_ENOTSUP
+    assert call(_args(hc=3)) == H.HC_ENOTSUP
     assert call(_args(x=None)) == H.HC_EINVAL
     assert call(_args(y_out=None)) == H.HC_EINVAL
     assert call(_args(post_in=None)) == H.HC_EINVAL           # delta given, post_in missing
@@ -166,6 +185,7 @@ def test_boundary_validation(L):
     assert call(_args(flags=SL)) == H.HC_ENOTSUP                  # d=64: not a multiple of 512
     assert call(_args(flags=SL, d=512)) == H.HC_ENOTSUP           # at least 1024
     assert call(_args(flags=SL, d=1024, fn_packed=None, pre_in=P + 0x600)) == H.HC_EINVAL   # needs the mixes
+    assert call(_args(flags=SL, d=1024, hc=8)) == H.HC_ENOTSUP    # hc = 4 only
     assert L.hc_boundary_begin(ctypes.byref(_args(flags=SL, d=1024)), S) == H.HC_EINVAL
     # a caller of the struct without the trailing flags field (shorter struct_size) gets flags 0
     short = H.BoundaryArgs.flags.offset
@@ -176,7 +196,7 @@ def test_boundary_validation(L):
     for half in (L.hc_boundary_begin, L.hc_boundary_end):          # the halves validate alike
         assert half(None, S) == H.HC_EINVAL
         assert half(ctypes.byref(_args(iters=0)), S) == H.HC_EINVAL
-        assert half(ctypes.byref(_args(hc=2)), S) == H.HC_ENOTSUP
+        assert half(ctypes.byref(_args(hc=3)), S) == H.HC_ENOTSUP
         assert half(ctypes.byref(_args(n=0)), S) == H.HC_OK
 
 

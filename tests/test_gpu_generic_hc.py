@@ -1,0 +1,198 @@
+"""GPU parity for hc = 2 and hc = 8 streams (the pages fix hc = 4; the
+Block code is written for any hc, and the projection, split and Sinkhorn
+definitions carry over unchanged).  Every entry point, through the C ABI,
+against the oracle on the same seeded inputs: hc_pre / hc_post bit for bit;
+mixes floored relative error <= 1e-4; pre/post/comb absolute error <= 1e-5;
+the boundary in all its forms (entry, write, fresh or given pre, RMSNorm,
+stream mean, expanded entry, exit, the two halves)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import hc_oracle as O
+from tests import numerics as N
+from tests.gpu_util import (assert_bf16_close, assert_bits_equal, assert_coef_close, assert_mixes_close, bf16_dev,
+                            f32_dev, host_bits, host_f32, say)
+from tests.test_gpu_parity import _check_boundary
+from transformer_hyper_connection_amd import hc as H
+from transformer_hyper_connection_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+HCS = [2, 8]
+
+
+def _inputs(hc, n, d, t0=0):
+    return synth.boundary_inputs("prefill", t0, t0 + n, d, hc=hc)
+
+
+def _dev_params(s):
+    return dict(fn_packed=H.hc_fn_pack(f32_dev(s["hc_fn"]), hc=s["x"].shape[1]), hc_base=f32_dev(s["hc_base"]),
+                hc_scale=f32_dev(s["hc_scale"]))
+
+
+@pytest.mark.parametrize("hc", HCS)
+def test_packed_weight_is_the_weight(hc):
+    say(f"[hc={hc}] pack d=1024")
+    s = _inputs(hc, 1, 1024)
+    p = H.hc_fn_pack(f32_dev(s["hc_fn"]), hc=hc)
+    assert np.array_equal(p.cpu().numpy().view(np.float32).reshape(s["hc_fn"].shape), s["hc_fn"])
+
+
+@pytest.mark.parametrize("hc", HCS)
+@pytest.mark.parametrize("n,d", [(1, 64), (37, 1088), (300, 5120), (2100, 1024)])
+def test_pre_post_bit_exact(hc, n, d):
+    say(f"[hc={hc}] pre/post n={n} d={d}")
+    s = _inputs(hc, n, d)
+    X = bf16_dev(s["x"])
+    y = H.hc_pre(X, f32_dev(s["pre_in"]))
+    assert_bits_equal(host_bits(y), O.hc_pre(s["x"], s["pre_in"]), "hc_pre")
+    xo = H.hc_post(bf16_dev(s["delta"]), X, f32_dev(s["post_in"]), f32_dev(s["comb_in"]))
+    assert_bits_equal(host_bits(xo), O.hc_post(s["delta"], s["x"], s["post_in"], s["comb_in"]), "hc_post")
+
+
+@pytest.mark.parametrize("hc", HCS)
+@pytest.mark.parametrize("n", [1, 255, 300])
+def test_split_sinkhorn(hc, n):
+    say(f"[hc={hc}] split n={n}")
+    s = _inputs(hc, n, 256)
+    m = O.hc_mixes(s["x"], s["hc_fn"], 1e-6).astype(np.float32)
+    pre, post, comb = H.hc_split_sinkhorn(f32_dev(m), f32_dev(s["hc_scale"]), f32_dev(s["hc_base"]), hc_mult=hc)
+    rp, rq, rc = O.hc_split_sinkhorn(m, s["hc_scale"], s["hc_base"], hc)
+    assert_coef_close(host_f32(pre), rp, "pre")
+    assert_coef_close(host_f32(post), rq, "post")
+    assert_coef_close(host_f32(comb), rc, "comb")
+    # every comb column and row of the last round sums to about one
+    c = host_f32(comb).astype(np.float64)
+    assert np.abs(c.sum(axis=1) - 1).max() < 1e-4
+
+
+@pytest.mark.parametrize("hc", HCS)
+@pytest.mark.parametrize("n,d", [(1, 64), (13, 1024), (300, 5120), (4096, 1024)])
+def test_mixes(hc, n, d):
+    say(f"[hc={hc}] mixes n={n} d={d}")
+    s = _inputs(hc, n, d)
+    X = bf16_dev(s["x"])
+    p = _dev_params(s)
+    ref = O.hc_mixes(s["x"], s["hc_fn"], 1e-6)
+    rp, rq, rc = O.hc_split_sinkhorn(ref, s["hc_scale"], s["hc_base"], hc)
+    pre, post, comb, mixes = H.hc_mixes(X, p["fn_packed"], p["hc_scale"], p["hc_base"], return_mixes=True)
+    assert_mixes_close(host_f32(mixes), ref)
+    assert_coef_close(host_f32(pre), rp, "pre")
+    assert_coef_close(host_f32(post), rq, "post")
+    assert_coef_close(host_f32(comb), rc, "comb")
+    # without a mixes output the mixes live in the workspace between the two launches
+    pre2, post2, comb2 = H.hc_mixes(X, p["fn_packed"], p["hc_scale"], p["hc_base"])
+    assert_bits_equal(host_f32(pre2).view(np.uint32), host_f32(pre).view(np.uint32), "pre (workspace mixes)")
+    assert_bits_equal(host_f32(comb2).view(np.uint32), host_f32(comb).view(np.uint32), "comb (workspace mixes)")
+    # mixes only
+    m2 = H.hc_mixes(X, p["fn_packed"])
+    assert_bits_equal(host_f32(m2).view(np.uint32), host_f32(mixes).view(np.uint32), "mixes alone")
+
+
+def _boundary(hc, n, d, fresh, norm, with_delta, want_mean=True, t0=0):
+    s = _inputs(hc, n, d, t0)
+    kw = dict(x=s["x"], pre_in=None if fresh else s["pre_in"], gamma=s["gamma"] if norm else None,
+              hc_fn=s["hc_fn"], hc_base=s["hc_base"], hc_scale=s["hc_scale"], want_mean=want_mean)
+    dev = dict(_dev_params(s), pre_in=None if fresh else f32_dev(s["pre_in"]),
+               gamma=f32_dev(s["gamma"]) if norm else None, want_mean=want_mean)
+    if with_delta:
+        kw.update(delta=s["delta"], post_in=s["post_in"], comb_in=s["comb_in"])
+        dev.update(delta=bf16_dev(s["delta"]), post_in=f32_dev(s["post_in"]), comb_in=f32_dev(s["comb_in"]))
+    return s, kw, dev
+
+
+@pytest.mark.parametrize("hc", HCS)
+@pytest.mark.parametrize("n,d", [(40, 1024), (300, 5120)])
+@pytest.mark.parametrize("fresh,norm", [(False, False), (False, True), (True, False), (True, True)])
+@pytest.mark.parametrize("with_delta", [False, True])
+def test_boundary(hc, n, d, fresh, norm, with_delta):
+    say(f"[hc={hc}] boundary n={n} d={d} fresh={fresh} norm={norm} delta={with_delta}")
+    s, kw, dev = _boundary(hc, n, d, fresh, norm, with_delta)
+    ref = O.boundary(**kw)
+    got = H.hc_boundary(bf16_dev(s["x"]), want_mixes=True, **dev)
+    _check_boundary(ref, got, s, fresh, norm)
+    # the tap: the mean over the new streams (one fp32 rounding of the hc-term sum at most)
+    assert_bf16_close(host_bits(got["x_mean"]), ref["x_mean"], "x_mean")
+
+
+@pytest.mark.parametrize("hc", HCS)
+@pytest.mark.parametrize("fresh", [False, True])
+def test_boundary_halves_and_workspace_mixes(hc, fresh):
+    """begin + end equals the whole call bit for bit, with the mixes kept by
+    the caller or only in the workspace."""
+    say(f"[hc={hc}] boundary halves fresh={fresh}")
+    s, _, dev = _boundary(hc, 130, 2048, fresh, True, True)
+    X = bf16_dev(s["x"])
+    whole = H.hc_boundary(X, want_mixes=True, **dev)
+    a, o = H._prepare_boundary(X, **dev)           # no mixes output: workspace
+    assert o.get("mixes") is None
+    import ctypes
+    st = torch.cuda.current_stream().cuda_stream
+    assert H.lib().hc_boundary_begin(ctypes.byref(a), ctypes.c_void_p(st)) == 0
+    assert H.lib().hc_boundary_end(ctypes.byref(a), ctypes.c_void_p(st)) == 0
+    torch.cuda.synchronize()
+    for k in ("x_out", "y", "x_mean"):
+        assert_bits_equal(host_bits(o[k]), host_bits(whole[k]), k)
+    for k in ("pre", "post", "comb"):
+        assert_bits_equal(host_f32(o[k]).view(np.uint32), host_f32(whole[k]).view(np.uint32), k)
+
+
+@pytest.mark.parametrize("hc", HCS)
+@pytest.mark.parametrize("with_delta", [False, True])
+def test_expanded_entry(hc, with_delta):
+    say(f"[hc={hc}] expanded entry delta={with_delta}")
+    s = _inputs(hc, 100, 1024)
+    h = s["x"][:, 0]
+    kw = dict(x=h, x_expanded=True, hc=hc, want_mean=True, gamma=s["gamma"], hc_fn=s["hc_fn"],
+              hc_base=s["hc_base"], hc_scale=s["hc_scale"])
+    dev = dict(_dev_params(s), gamma=f32_dev(s["gamma"]))
+    if with_delta:
+        kw.update(delta=s["delta"], post_in=s["post_in"], comb_in=s["comb_in"])
+        dev.update(delta=bf16_dev(s["delta"]), post_in=f32_dev(s["post_in"]), comb_in=f32_dev(s["comb_in"]))
+    ref = O.boundary(**kw)
+    got = H.hc_boundary(bf16_dev(h), x_expanded=True, hc_mult=hc, want_mean=True, want_mixes=True, **dev)
+    _check_boundary(ref, got, dict(s, x=O.expand_streams(h, hc)), True, True)
+    assert_bf16_close(host_bits(got["x_mean"]), ref["x_mean"], "x_mean")
+    if not with_delta:
+        assert_bits_equal(host_bits(got["x_mean"]), h, "x_mean of the copies is the embedding")
+
+
+@pytest.mark.parametrize("hc", HCS)
+def test_stack_exit(hc):
+    """Last write, read with the last pre, RMSNorm (eps 1e-20); no mixes."""
+    say(f"[hc={hc}] exit")
+    s = _inputs(hc, 77, 5120)
+    ref = O.boundary(x=s["x"], delta=s["delta"], post_in=s["post_in"], comb_in=s["comb_in"], pre_in=s["pre_in"],
+                     gamma=s["gamma"], rms_eps=1e-20)
+    got = H.hc_boundary(bf16_dev(s["x"]), delta=bf16_dev(s["delta"]), post_in=f32_dev(s["post_in"]),
+                        comb_in=f32_dev(s["comb_in"]), pre_in=f32_dev(s["pre_in"]), gamma=f32_dev(s["gamma"]),
+                        rms_eps=1e-20)
+    assert_bits_equal(host_bits(got["x_out"]), ref["x_out"], "x_out")
+    assert_bf16_close(host_bits(got["y"]), ref["y"], "z")
+
+
+def test_hc4_workspace_survives_other_hc_calls():
+    """A workspace shared with hc = 8 calls (mixes kept in the workspace)
+    keeps the hc = 4 decode schedule's words intact: the hc = 4 decode
+    boundary before and after gives the same bits."""
+    say("[hc=4/8] shared workspace")
+    s4 = synth.boundary_inputs("decode", 0, 64, 1024)
+    s8 = _inputs(8, 64, 1024)
+    ws = torch.zeros(max(H.lib().hc_workspace_bytes(64, 4, 1024), H.lib().hc_workspace_bytes(64, 8, 1024)),
+                     dtype=torch.uint8, device="cuda")
+    dev4 = dict(delta=bf16_dev(s4["delta"]), post_in=f32_dev(s4["post_in"]), comb_in=f32_dev(s4["comb_in"]),
+                pre_in=f32_dev(s4["pre_in"]), fn_packed=H.hc_fn_pack(f32_dev(s4["hc_fn"])),
+                hc_base=f32_dev(s4["hc_base"]), hc_scale=f32_dev(s4["hc_scale"]))
+    X4 = bf16_dev(s4["x"])
+    first = H.hc_boundary(X4, out={"workspace": ws}, **dev4)
+    torch.cuda.synchronize()
+    first = {k: v.clone() for k, v in first.items() if isinstance(v, torch.Tensor) and k != "workspace"}
+    _, _, dev8 = _boundary(8, 64, 1024, True, True, True)
+    for _ in range(3):
+        H.hc_boundary(bf16_dev(s8["x"]), out={"workspace": ws}, **dev8)
+    again = H.hc_boundary(X4, out={"workspace": ws}, **dev4)
+    torch.cuda.synchronize()
+    for k, v in first.items():
+        assert torch.equal(again[k], v), k
+    assert int(ws[4160:4164].cpu().numpy().view(np.uint32)[0]) == 0

@@ -10,16 +10,22 @@
 // is formed implicitly: the stream arithmetic of hc_post / hc_pre is the page's
 // sequence of separately rounded fp32 products and sums, bit for bit).
 //
-// Kernels
-//   tile_kernel<POST, RM, NORM>  everything that derives mixes (hc_mixes, block
-//       entry, sublayer boundary): 64-token tiles x feature slices, about one
-//       workgroup per compute unit; the 24-wide projection on the matrix cores
-//       with the weight tiles shared through LDS; the slices of a tile meet once
-//       in a workspace, then each writes its part of the read row.
-//   row_kernel<POST, PRE, NORM, TPW>  streams only (hc_post, hc_pre, the stack
-//       exit): whole token rows per wave, 1 KB per load or store.
-//   split_kernel    hc_split_sinkhorn, one token per lane.
+// Kernels (hc = 4, the pages' setting)
+//   stream_kernel<POST, RM, NORM, MEAN> + finish_kernel<RM, NORM>  everything
+//       that derives mixes (hc_mixes, block entry, sublayer boundary) at any n:
+//       64-token tiles x feature slices, about one workgroup per compute unit;
+//       the 24-wide projection on the matrix cores with the weight tiles shared
+//       through LDS; the per-slice sums meet in the workspace, and the finish
+//       derives the coefficients and writes the read row.
+//   decode_kernel<POST, READ>  the same for n <= 128 in one launch: the last
+//       slice of a token tile to arrive sums the tile's records.
+//   fused_kernel<POST, RM, NORM>  the single-launch schedule (opt-in).
+//   row_kernel<POST, PRE, NORM, TPW, HC>  streams only (hc_post, hc_pre, the
+//       stack exit): whole token rows per wave, 1 KB per load or store.
+//   split_kernel<HC>  hc_split_sinkhorn, one token per lane.
 //   pack_kernel     fp32 projection weight -> bf16 hi/mid/lo terms in tile order.
+// hc = 2 and 8: row_kernel and split_kernel instantiated for that hc, and
+//   mixes_generic_kernel<GM>, the projection in fp32 multiply-adds.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -80,64 +86,76 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32 w0, u32 w1, u32 w2, u32 w3) {
 // equation.  fp32; the row/column divisions use the hardware reciprocal.
 __device__ __forceinline__ float sigmoidf_(float u) { return __builtin_amdgcn_rcpf(1.0f + expf(-u)); }
 
+template <int HC = kHC>
 __device__ void split_sinkhorn_one(const float* mx, float s0, float s1, float s2, const float* bs,
                                    int iters, float eps, float* pre_o, float* post_o, float* comb_o) {
-  float pre[kHC], post[kHC];
+  float pre[HC], post[HC];
 #pragma unroll
-  for (int j = 0; j < kHC; ++j) {
+  for (int j = 0; j < HC; ++j) {
     pre[j] = sigmoidf_(mx[j] * s0 + bs[j]) + eps;
-    post[j] = 2.0f * sigmoidf_(mx[kHC + j] * s1 + bs[kHC + j]);
+    post[j] = 2.0f * sigmoidf_(mx[HC + j] * s1 + bs[HC + j]);
   }
-  float A[kHC][kHC];
+  float A[HC][HC];
 #pragma unroll
-  for (int j = 0; j < kHC; ++j) {
+  for (int j = 0; j < HC; ++j) {
     float mx_row = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < kHC; ++k) {
-      A[j][k] = mx[2 * kHC + j * kHC + k] * s2 + bs[2 * kHC + j * kHC + k];
+    for (int k = 0; k < HC; ++k) {
+      A[j][k] = mx[2 * HC + j * HC + k] * s2 + bs[2 * HC + j * HC + k];
       mx_row = fmaxf(mx_row, A[j][k]);
     }
     float rs = 0.f;
 #pragma unroll
-    for (int k = 0; k < kHC; ++k) {
+    for (int k = 0; k < HC; ++k) {
       A[j][k] = expf(A[j][k] - mx_row);
       rs = rs + A[j][k];
     }
     const float inv = __builtin_amdgcn_rcpf(rs);
 #pragma unroll
-    for (int k = 0; k < kHC; ++k) A[j][k] = A[j][k] * inv + eps;
+    for (int k = 0; k < HC; ++k) A[j][k] = A[j][k] * inv + eps;
   }
   auto col_norm = [&]() {
 #pragma unroll
-    for (int k = 0; k < kHC; ++k) {
+    for (int k = 0; k < HC; ++k) {
       float cs = A[0][k];
 #pragma unroll
-      for (int j = 1; j < kHC; ++j) cs = cs + A[j][k];
+      for (int j = 1; j < HC; ++j) cs = cs + A[j][k];
       const float inv = __builtin_amdgcn_rcpf(cs + eps);
 #pragma unroll
-      for (int j = 0; j < kHC; ++j) A[j][k] = A[j][k] * inv;
+      for (int j = 0; j < HC; ++j) A[j][k] = A[j][k] * inv;
     }
   };
   col_norm();
   for (int it = 1; it < iters; ++it) {
 #pragma unroll
-    for (int j = 0; j < kHC; ++j) {
+    for (int j = 0; j < HC; ++j) {
       float rs = A[j][0];
 #pragma unroll
-      for (int k = 1; k < kHC; ++k) rs = rs + A[j][k];
+      for (int k = 1; k < HC; ++k) rs = rs + A[j][k];
       const float inv = __builtin_amdgcn_rcpf(rs + eps);
 #pragma unroll
-      for (int k = 0; k < kHC; ++k) A[j][k] = A[j][k] * inv;
+      for (int k = 0; k < HC; ++k) A[j][k] = A[j][k] * inv;
     }
     col_norm();
   }
-  *reinterpret_cast<f32x4*>(pre_o) = f32x4{pre[0], pre[1], pre[2], pre[3]};
-  *reinterpret_cast<f32x4*>(post_o) = f32x4{post[0], post[1], post[2], post[3]};
+  if constexpr (HC == 4) {
+    *reinterpret_cast<f32x4*>(pre_o) = f32x4{pre[0], pre[1], pre[2], pre[3]};
+    *reinterpret_cast<f32x4*>(post_o) = f32x4{post[0], post[1], post[2], post[3]};
 #pragma unroll
-  for (int j = 0; j < kHC; ++j)
-    reinterpret_cast<f32x4*>(comb_o)[j] = f32x4{A[j][0], A[j][1], A[j][2], A[j][3]};
+    for (int j = 0; j < HC; ++j)
+      reinterpret_cast<f32x4*>(comb_o)[j] = f32x4{A[j][0], A[j][1], A[j][2], A[j][3]};
+  } else {
+#pragma unroll
+    for (int j = 0; j < HC; ++j) {
+      pre_o[j] = pre[j];
+      post_o[j] = post[j];
+#pragma unroll
+      for (int k = 0; k < HC; ++k) comb_o[j * HC + k] = A[j][k];
+    }
+  }
 }
 
+template <int HC>
 __global__ void __launch_bounds__(256) split_kernel(const float* __restrict__ mixes,
                                                     const float* __restrict__ scale,
                                                     const float* __restrict__ base, int64_t n, int iters,
@@ -145,16 +163,114 @@ __global__ void __launch_bounds__(256) split_kernel(const float* __restrict__ mi
                                                     float* __restrict__ post, float* __restrict__ comb) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= n) return;
-  float mx[kMix], bs[kMix];
+  constexpr int MIX = (2 + HC) * HC;
+  float mx[MIX], bs[MIX];
 #pragma unroll
-  for (int q = 0; q < kMix; q += 4) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(mixes + t * kMix + q);
+  for (int q = 0; q < MIX; q += 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(mixes + t * MIX + q);
     const f32x4 b = *reinterpret_cast<const f32x4*>(base + q);
     mx[q] = v[0]; mx[q + 1] = v[1]; mx[q + 2] = v[2]; mx[q + 3] = v[3];
     bs[q] = b[0]; bs[q + 1] = b[1]; bs[q + 2] = b[2]; bs[q + 3] = b[3];
   }
-  split_sinkhorn_one(mx, scale[0], scale[1], scale[2], bs, iters, eps, pre + t * kHC, post + t * kHC,
-                     comb + t * kHC * kHC);
+  split_sinkhorn_one<HC>(mx, scale[0], scale[1], scale[2], bs, iters, eps, pre + t * HC, post + t * HC,
+                         comb + t * HC * HC);
+}
+
+// ------------------------------------------- projection for hc other than 4
+// mixes[t, q] = r[t] * sum_c fn[q, c] x[t, c] with r[t] = 1/sqrt(mean_c x^2 +
+// eps) ("Source layer, pairs pooled": the RMS-scaled projection), in plain
+// fp32 multiply-adds on the weights as given (hc_fn_pack copies them for hc
+// other than 4).  A workgroup takes kGT tokens and GM projection rows; the
+// flattened hc*d features are dealt out to its 256 lanes in groups of 8, each
+// lane keeping kGT x GM partial dots and kGT partial sums of squares, which
+// are then summed over the lanes in a fixed order (the same bits every call).
+constexpr int kGT = 8;
+
+struct GenMixArgs {
+  const hc_bf16* x;
+  const float* fn;     // [mix][K] fp32
+  float* mixes;        // [n][mix]
+  int64_t n;
+  int xtok, xstr;      // elements per token / per stream of x (stride 0: expanded)
+  int d, K, mix;
+  float norm_eps;
+};
+
+template <int GM>
+__global__ void __launch_bounds__(256) mixes_generic_kernel(const GenMixArgs a) {
+  const int64_t t0 = (int64_t)blockIdx.x * kGT;
+  const int m0 = blockIdx.y * GM;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float acc[kGT][GM], ss[kGT];
+#pragma unroll
+  for (int tt = 0; tt < kGT; ++tt) {
+    ss[tt] = 0.f;
+#pragma unroll
+    for (int mm = 0; mm < GM; ++mm) acc[tt][mm] = 0.f;
+  }
+  bool mrow[GM];
+#pragma unroll
+  for (int mm = 0; mm < GM; ++mm) mrow[mm] = m0 + mm < a.mix;
+  const int groups = a.K / 8;
+  for (int g = threadIdx.x; g < groups; g += 256) {
+    const int c = g * 8;
+    const int j = c / a.d, i = c - j * a.d;
+    float xv[kGT][8];
+#pragma unroll
+    for (int tt = 0; tt < kGT; ++tt) {
+      const int64_t t = t0 + tt;
+      const u32x4 v = t < a.n ? ld_stream(reinterpret_cast<const u32x4*>(a.x + t * a.xtok + j * a.xstr + i))
+                              : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xv[tt][2 * e] = bf_lo(v[e]);
+        xv[tt][2 * e + 1] = bf_hi(v[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss[tt] = fmaf(xv[tt][e], xv[tt][e], ss[tt]);
+    }
+#pragma unroll
+    for (int mm = 0; mm < GM; ++mm) {
+      if (!mrow[mm]) continue;
+      const f32x4* wp = reinterpret_cast<const f32x4*>(a.fn + (size_t)(m0 + mm) * a.K + c);
+      const f32x4 w0 = wp[0], w1 = wp[1];
+      const float w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+#pragma unroll
+      for (int tt = 0; tt < kGT; ++tt)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[tt][mm] = fmaf(w[e], xv[tt][e], acc[tt][mm]);
+    }
+  }
+  // butterfly sums within each wave (every lane ends with the same bits),
+  // then the four waves in order
+  __shared__ float red[4][kGT * (GM + 1)];
+  auto wave_sum = [&](float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+  };
+#pragma unroll
+  for (int tt = 0; tt < kGT; ++tt) {
+#pragma unroll
+    for (int mm = 0; mm < GM; ++mm) {
+      const float v = wave_sum(acc[tt][mm]);
+      if (lane == 0) red[wave][tt * GM + mm] = v;
+    }
+    const float v = wave_sum(ss[tt]);
+    if (lane == 0) red[wave][kGT * GM + tt] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < kGT * GM) {
+    const int tt = threadIdx.x / GM, mm = threadIdx.x % GM;
+    const int64_t t = t0 + tt;
+    if (t < a.n && m0 + mm < a.mix) {
+      const int q = tt * GM + mm, qs = kGT * GM + tt;
+      const float dot = ((red[0][q] + red[1][q]) + red[2][q]) + red[3][q];
+      const float sq = ((red[0][qs] + red[1][qs]) + red[2][qs]) + red[3][qs];
+      const float r = 1.0f / sqrtf(sq / (float)a.K + a.norm_eps);
+      a.mixes[t * a.mix + m0 + mm] = dot * r;
+    }
+  }
 }
 
 // ------------------------------------------------------------------ weight pack
@@ -241,35 +357,36 @@ struct RowArgs {
 constexpr int kRowChunk = 512;                   // features per wave instruction
 constexpr int kRowMaxChunks = 10;                // per token held in registers (NORM)
 
-template <bool POST>
-__device__ __forceinline__ void row_load(u32x4 (&r)[kHC + 1], const u32x4* xrow, const u32x4* drow, int xstr,
+template <bool POST, int HC = kHC>
+__device__ __forceinline__ void row_load(u32x4 (&r)[HC + 1], const u32x4* xrow, const u32x4* drow, int xstr,
                                          int f) {
 #pragma unroll
-  for (int j = 0; j < kHC; ++j) r[j] = ld_stream(xrow + (j * xstr + f) / 8);
-  r[kHC] = POST ? ld_stream(drow + f / 8) : u32x4{0u, 0u, 0u, 0u};
+  for (int j = 0; j < HC; ++j) r[j] = ld_stream(xrow + (j * xstr + f) / 8);
+  r[HC] = POST ? ld_stream(drow + f / 8) : u32x4{0u, 0u, 0u, 0u};
 }
 
 // X'_k = post_k * delta + ((C_0k X_0 + C_1k X_1) + C_2k X_2) + C_3k X_3, one lane's 8 features
-__device__ __forceinline__ void post_8(const u32x4 (&r)[kHC + 1], const float* cpost, const float* ccomb,
-                                       u32 (&xp)[kHC][4]) {
+template <int HC = kHC>
+__device__ __forceinline__ void post_8(const u32x4 (&r)[HC + 1], const float* cpost, const float* ccomb,
+                                       u32 (&xp)[HC][4]) {
 #pragma unroll
   for (int e2 = 0; e2 < 4; ++e2) {
-    float X[kHC][2], D[2];
+    float X[HC][2], D[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int j = 0; j < kHC; ++j) X[j][h] = bf_elem(r[j][e2], h);
-      D[h] = bf_elem(r[kHC][e2], h);
+      for (int j = 0; j < HC; ++j) X[j][h] = bf_elem(r[j][e2], h);
+      D[h] = bf_elem(r[HC][e2], h);
     }
 #pragma unroll
-    for (int k = 0; k < kHC; ++k) {
+    for (int k = 0; k < HC; ++k) {
       float v[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const float pa = cpost[k] * D[h];
-        float sm = ccomb[0 * kHC + k] * X[0][h];
+        float sm = ccomb[0 * HC + k] * X[0][h];
 #pragma unroll
-        for (int j = 1; j < kHC; ++j) sm = sm + ccomb[j * kHC + k] * X[j][h];
+        for (int j = 1; j < HC; ++j) sm = sm + ccomb[j * HC + k] * X[j][h];
         v[h] = pa + sm;
       }
       xp[k][e2] = pack_bf16(v[0], v[1]);
@@ -281,7 +398,8 @@ __device__ __forceinline__ void post_8(const u32x4 (&r)[kHC + 1], const float* c
 // a block's input): (((X'_0 + X'_1) + X'_2) + X'_3) / 4 in fp32, one lane's 8
 // features (the sum of four bf16 values is exact in fp32 but for extreme
 // exponent spreads, and the quarter is exact).
-__device__ __forceinline__ u32x4 mean_8(const u32 (&xp)[kHC][4]) {
+template <int HC = kHC>
+__device__ __forceinline__ u32x4 mean_8(const u32 (&xp)[HC][4]) {
   u32 m[4];
 #pragma unroll
   for (int e2 = 0; e2 < 4; ++e2) {
@@ -290,8 +408,8 @@ __device__ __forceinline__ u32x4 mean_8(const u32 (&xp)[kHC][4]) {
     for (int h = 0; h < 2; ++h) {
       float sm = bf_elem(xp[0][e2], h);
 #pragma unroll
-      for (int k = 1; k < kHC; ++k) sm = sm + bf_elem(xp[k][e2], h);
-      v[h] = sm * 0.25f;
+      for (int k = 1; k < HC; ++k) sm = sm + bf_elem(xp[k][e2], h);
+      v[h] = sm * (1.0f / HC);
     }
     m[e2] = pack_bf16(v[0], v[1]);
   }
@@ -299,7 +417,8 @@ __device__ __forceinline__ u32x4 mean_8(const u32 (&xp)[kHC][4]) {
 }
 
 // y = ((p_0 X'_0 + p_1 X'_1) + p_2 X'_2) + p_3 X'_3, one lane's 8 features
-__device__ __forceinline__ void pre_8(const u32 (&xp)[kHC][4], const float* cpre, u32 (&yp)[4]) {
+template <int HC = kHC>
+__device__ __forceinline__ void pre_8(const u32 (&xp)[HC][4], const float* cpre, u32 (&yp)[4]) {
 #pragma unroll
   for (int e2 = 0; e2 < 4; ++e2) {
     float v[2];
@@ -307,14 +426,14 @@ __device__ __forceinline__ void pre_8(const u32 (&xp)[kHC][4], const float* cpre
     for (int h = 0; h < 2; ++h) {
       float s = cpre[0] * bf_elem(xp[0][e2], h);
 #pragma unroll
-      for (int k = 1; k < kHC; ++k) s = s + cpre[k] * bf_elem(xp[k][e2], h);
+      for (int k = 1; k < HC; ++k) s = s + cpre[k] * bf_elem(xp[k][e2], h);
       v[h] = s;
     }
     yp[e2] = pack_bf16(v[0], v[1]);
   }
 }
 
-template <bool POST, bool PRE, bool NORM, int TPW>
+template <bool POST, bool PRE, bool NORM, int TPW, int HC = kHC>
 __global__ void __launch_bounds__(kThreads) row_kernel(const RowArgs a) {
   static_assert(!NORM || PRE, "RMSNorm needs the read row");
   constexpr int MAXC = kRowMaxChunks * 2 / TPW;
@@ -325,19 +444,19 @@ __global__ void __launch_bounds__(kThreads) row_kernel(const RowArgs a) {
 
   int64_t tok[TPW];
   bool tvalid[TPW];
-  float cpost[TPW][kHC], ccomb[TPW][kHC * kHC], cpre[TPW][kHC];
+  float cpost[TPW][HC], ccomb[TPW][HC * HC], cpre[TPW][HC];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const int64_t t = (int64_t)blockIdx.x * (kWaves * TPW) + wave * TPW + i;
     tvalid[i] = t < a.n;
     tok[i] = tvalid[i] ? t : 0;
 #pragma unroll
-    for (int j = 0; j < kHC; ++j) {
-      cpost[i][j] = POST ? a.post_in[tok[i] * kHC + j] : 0.f;
-      cpre[i][j] = PRE ? a.pre_in[tok[i] * kHC + j] : 0.f;
+    for (int j = 0; j < HC; ++j) {
+      cpost[i][j] = POST ? a.post_in[tok[i] * HC + j] : 0.f;
+      cpre[i][j] = PRE ? a.pre_in[tok[i] * HC + j] : 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < kHC * kHC; ++j) ccomb[i][j] = POST ? a.comb_in[tok[i] * kHC * kHC + j] : 0.f;
+    for (int j = 0; j < HC * HC; ++j) ccomb[i][j] = POST ? a.comb_in[tok[i] * HC * HC + j] : 0.f;
   }
 
   u32 ykeep[NORM ? TPW : 1][NORM ? MAXC : 1][4];
@@ -349,32 +468,32 @@ __global__ void __launch_bounds__(kThreads) row_kernel(const RowArgs a) {
     const int f0 = c * kRowChunk + lane * 8;
     const bool act = f0 < d;
     const int f = act ? f0 : 0;  // idle lanes of a partial chunk read feature 0 and never store
-    u32x4 r[TPW][kHC + 1];
+    u32x4 r[TPW][HC + 1];
 #pragma unroll
     for (int i = 0; i < TPW; ++i)
-      row_load<POST>(r[i], reinterpret_cast<const u32x4*>(a.x + tok[i] * a.xtok),
+      row_load<POST, HC>(r[i], reinterpret_cast<const u32x4*>(a.x + tok[i] * a.xtok),
                      reinterpret_cast<const u32x4*>(POST ? a.delta + tok[i] * d : a.x), a.xstr, f);
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const bool st = act && tvalid[i];
-      u32 xp[kHC][4];
+      u32 xp[HC][4];
       if constexpr (POST) {
-        post_8(r[i], cpost[i], ccomb[i], xp);
-        u32x4* xo = reinterpret_cast<u32x4*>(a.x_out + tok[i] * kHC * d);
+        post_8<HC>(r[i], cpost[i], ccomb[i], xp);
+        u32x4* xo = reinterpret_cast<u32x4*>(a.x_out + tok[i] * HC * d);
         if (st) {
 #pragma unroll
-          for (int k = 0; k < kHC; ++k) st_stream(xo + (k * d + f) / 8, u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]});
+          for (int k = 0; k < HC; ++k) st_stream(xo + (k * d + f) / 8, u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]});
         }
       } else {
 #pragma unroll
-        for (int k = 0; k < kHC; ++k)
+        for (int k = 0; k < HC; ++k)
 #pragma unroll
           for (int e = 0; e < 4; ++e) xp[k][e] = r[i][k][e];
       }
-      if (a.x_mean && st) st_stream(reinterpret_cast<u32x4*>(a.x_mean + tok[i] * d) + f / 8, mean_8(xp));
+      if (a.x_mean && st) st_stream(reinterpret_cast<u32x4*>(a.x_mean + tok[i] * d) + f / 8, mean_8<HC>(xp));
       if constexpr (PRE) {
         u32 yp[4];
-        pre_8(xp, cpre[i], yp);
+        pre_8<HC>(xp, cpre[i], yp);
         if constexpr (NORM) {
           if (act) {
 #pragma unroll
@@ -1836,8 +1955,11 @@ int fail(int code, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+constexpr int mix_of(int hc) { return (2 + hc) * hc; }
+bool hc_known(int hc) { return hc == 2 || hc == kHC || hc == 8; }
+
 int check_hd(int hc, int d) {
-  if (hc != kHC) return fail(HC_ENOTSUP, "hc=%d: only hc=4 is supported", hc);
+  if (!hc_known(hc)) return fail(HC_ENOTSUP, "hc=%d: hc must be 2, 4 or 8", hc);
   if (d <= 0 || d % kCF != 0 || d > kMaxD)
     return fail(HC_ENOTSUP, "d=%d: d must be a positive multiple of %d, at most %d", d, kCF, kMaxD);
   return HC_OK;
@@ -2080,7 +2202,7 @@ int launch_fused(bool post, int rm, bool norm, FusedArgs f, void* ws, size_t ws_
   return launched(e, what);
 }
 
-template <bool POST, bool PRE, bool NORM, int TPW>
+template <bool POST, bool PRE, bool NORM, int TPW, int HC = kHC>
 hipError_t launch_row_t(const RowArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)((a.n + kWaves * TPW - 1) / (kWaves * TPW));
   // without the RMSNorm, few tokens: the 512-feature chunks of a row go to
@@ -2089,16 +2211,34 @@ hipError_t launch_row_t(const RowArgs& a, hipStream_t st) {
   const unsigned gy = NORM ? 1u : (unsigned)std::max(1, std::min<int>(nch, (int)((512 + grid - 1) / grid)));
   RowArgs copy = a;
   void* args[] = {&copy};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&row_kernel<POST, PRE, NORM, TPW>), dim3(grid, gy),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&row_kernel<POST, PRE, NORM, TPW, HC>), dim3(grid, gy),
                          dim3(kThreads), args, 0, st);
 }
 
-int launch_row(bool post, bool pre, bool norm, const RowArgs& a, hipStream_t st, const char* what) {
+// hc other than 4: one token per wave, every stage combination
+template <int HC>
+hipError_t launch_row_hc(int key, const RowArgs& a, hipStream_t st) {
+  switch (key) {
+    case 0b100: return launch_row_t<true, false, false, 1, HC>(a, st);
+    case 0b010: return launch_row_t<false, true, false, 1, HC>(a, st);
+    case 0b110: return launch_row_t<true, true, false, 1, HC>(a, st);
+    case 0b011: return launch_row_t<false, true, true, 1, HC>(a, st);
+    default: return launch_row_t<true, true, true, 1, HC>(a, st);
+  }
+}
+
+int launch_row(bool post, bool pre, bool norm, const RowArgs& a, hipStream_t st, const char* what, int hc = kHC) {
   const bool wide = norm && a.d > kRowChunk * kRowMaxChunks;
   if (norm && a.d > kRowChunk * kRowMaxChunks * 2)
     return fail(HC_ENOTSUP, "%s: RMSNorm of the read row supports d <= %d", what, kRowChunk * kRowMaxChunks * 2);
   const int key = (post ? 4 : 0) | (pre ? 2 : 0) | (norm ? 1 : 0);
+  if (key != 0b100 && key != 0b010 && key != 0b110 && key != 0b011 && key != 0b111)
+    return fail(HC_EINVAL, "%s: unsupported stage combination", what);
   hipError_t e;
+  if (hc != kHC) {
+    e = hc == 2 ? launch_row_hc<2>(key, a, st) : launch_row_hc<8>(key, a, st);
+    return launched(e, what);
+  }
   const bool few = a.n < 2048;                     // one token per wave: more workgroups
   switch (key) {
     case 0b100: e = few ? launch_row_t<true, false, false, 1>(a, st) : launch_row_t<true, false, false, 2>(a, st); break;
@@ -2109,6 +2249,50 @@ int launch_row(bool post, bool pre, bool norm, const RowArgs& a, hipStream_t st,
     default: return fail(HC_EINVAL, "%s: unsupported stage combination", what);
   }
   return launched(e, what);
+}
+
+// ------------------------------------------------------ hc other than 4
+// workspace of the hc != 4 path: the mixes, when the caller does not keep
+// them, placed after the control block and the decode region of the same d so
+// that a workspace shared with hc = 4 calls keeps their words intact
+size_t generic_mixes_offset(int d) { return kCtrlBytes + decode_region_bytes(d); }
+size_t generic_ws_bytes(int64_t n, int hc, int d) {
+  return generic_mixes_offset(d) + (((size_t)n * mix_of(hc) * 4 + 255) & ~(size_t)255);
+}
+
+int check_generic_ws(int64_t n, int hc, int d, const void* ws, size_t ws_bytes, const char* what) {
+  const size_t need = generic_ws_bytes(n, hc, d);
+  if (!ws) return fail(HC_EINVAL, "%s: workspace must not be NULL (need %zu bytes)", what, need);
+  if (!aligned16(ws)) return fail(HC_EINVAL, "%s: workspace is not 16-byte aligned", what);
+  if (ws_bytes < need) return fail(HC_EINVAL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, need);
+  return HC_OK;
+}
+
+int launch_mixes_generic(int hc, const hc_bf16* x, int xtok, int xstr, const void* fn, int64_t n, int d,
+                         float norm_eps, float* mixes, hipStream_t st, const char* what) {
+  GenMixArgs a{};
+  a.x = x; a.fn = static_cast<const float*>(fn); a.mixes = mixes; a.n = n; a.xtok = xtok; a.xstr = xstr;
+  a.d = d; a.K = hc * d; a.mix = mix_of(hc); a.norm_eps = norm_eps;
+  void* args[] = {&a};
+  const unsigned gx = (unsigned)((n + kGT - 1) / kGT);
+  const hipError_t e =
+      hc == 2 ? hipLaunchKernel(reinterpret_cast<const void*>(&mixes_generic_kernel<8>), dim3(gx, 1), dim3(256),
+                                args, 0, st)
+              : hipLaunchKernel(reinterpret_cast<const void*>(&mixes_generic_kernel<16>),
+                                dim3(gx, (unsigned)((a.mix + 15) / 16)), dim3(256), args, 0, st);
+  return launched(e, what);
+}
+
+int launch_split(int hc, const float* mixes, const float* scale, const float* base, int64_t n, int iters,
+                 float eps, float* pre, float* post, float* comb, hipStream_t st) {
+  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (hc == 2)
+    hipLaunchKernelGGL(split_kernel<2>, grid, block, 0, st, mixes, scale, base, n, iters, eps, pre, post, comb);
+  else if (hc == 8)
+    hipLaunchKernelGGL(split_kernel<8>, grid, block, 0, st, mixes, scale, base, n, iters, eps, pre, post, comb);
+  else
+    hipLaunchKernelGGL(split_kernel<kHC>, grid, block, 0, st, mixes, scale, base, n, iters, eps, pre, post, comb);
+  return launched(hipGetLastError(), "split_kernel");
 }
 
 }  // namespace
@@ -2132,7 +2316,8 @@ const char* hc_strerror(int status) {
 const char* hc_last_error(void) { return g_err; }
 
 size_t hc_fn_packed_bytes(int hc, int d) {
-  if (hc != kHC || d <= 0 || d % kCF != 0 || d > kMaxD) return 0;
+  if (!hc_known(hc) || d <= 0 || d % kCF != 0 || d > kMaxD) return 0;
+  if (hc != kHC) return (size_t)mix_of(hc) * hc * d * 4;   // the fp32 weights as given
   return (size_t)(d / kStepF) * kHC * kNT * 64 * 16;
 }
 
@@ -2143,6 +2328,9 @@ int hc_fn_pack(const float* hc_fn, int hc, int d, void* fn_packed, void* stream)
   HC_REQ(hc_fn);
   HC_REQ(fn_packed);
   if ((rc = check_device())) return rc;
+  if (hc != kHC)
+    return launched(hipMemcpyAsync(fn_packed, hc_fn, hc_fn_packed_bytes(hc, d), hipMemcpyDeviceToDevice,
+                                   (hipStream_t)stream), "hc_fn_pack");
   const int records = (d / kStepF) * kHC * kNT * 64;
   hipLaunchKernelGGL(pack_kernel, dim3((records + 255) / 256), dim3(256), 0, (hipStream_t)stream, hc_fn, d,
                      reinterpret_cast<u32x4*>(fn_packed), records);
@@ -2150,8 +2338,9 @@ int hc_fn_pack(const float* hc_fn, int hc, int d, void* fn_packed, void* stream)
 }
 
 size_t hc_workspace_bytes(int64_t n, int hc, int d) {
-  if (hc != kHC || d <= 0 || d % kCF != 0 || d > kMaxD || n < 0) return 0;
+  if (!hc_known(hc) || d <= 0 || d % kCF != 0 || d > kMaxD || n < 0) return 0;
   if (n == 0) return 0;
+  if (hc != kHC) return generic_ws_bytes(n, hc, d);
   return workspace_bytes(n, d);
 }
 
@@ -2159,15 +2348,13 @@ int hc_split_sinkhorn(const float* mixes, const float* hc_scale, const float* hc
                       int iters, float hc_eps, float* pre, float* post, float* comb, void* stream) {
   g_err[0] = 0;
   int rc;
-  if (hc != kHC) return fail(HC_ENOTSUP, "hc=%d: only hc=4 is supported", hc);
+  if (!hc_known(hc)) return fail(HC_ENOTSUP, "hc=%d: hc must be 2, 4 or 8", hc);
   if ((rc = check_n(n))) return rc;
   if (iters < 1) return fail(HC_EINVAL, "iters=%d: at least one Sinkhorn round is needed", iters);
   HC_REQ(mixes); HC_REQ(hc_scale); HC_REQ(hc_base); HC_REQ(pre); HC_REQ(post); HC_REQ(comb);
   if (n == 0) return HC_OK;
   if ((rc = check_device())) return rc;
-  hipLaunchKernelGGL(split_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
-                     mixes, hc_scale, hc_base, n, iters, hc_eps, pre, post, comb);
-  return launched(hipGetLastError(), "split_kernel");
+  return launch_split(hc, mixes, hc_scale, hc_base, n, iters, hc_eps, pre, post, comb, (hipStream_t)stream);
 }
 
 int hc_mixes(const hc_bf16* x, const void* fn_packed, int64_t n, int hc, int d, float norm_eps, float* mixes,
@@ -2186,7 +2373,14 @@ int hc_mixes(const hc_bf16* x, const void* fn_packed, int64_t n, int hc, int d, 
     return fail(HC_EINVAL, "nothing to compute: mixes and pre/post/comb are all NULL");
   }
   if (n == 0) return HC_OK;
+  if (hc != kHC && !mixes && (rc = check_generic_ws(n, hc, d, workspace, workspace_bytes, "hc_mixes"))) return rc;
   if ((rc = check_device())) return rc;
+  if (hc != kHC) {
+    const hipStream_t st = (hipStream_t)stream;
+    float* mx = mixes ? mixes : reinterpret_cast<float*>(static_cast<char*>(workspace) + generic_mixes_offset(d));
+    if ((rc = launch_mixes_generic(hc, x, hc * d, d, fn_packed, n, d, norm_eps, mx, st, "hc_mixes"))) return rc;
+    return split ? launch_split(hc, mx, hc_scale, hc_base, n, iters, hc_eps, pre, post, comb, st) : HC_OK;
+  }
   if (decode_shape(n, d)) {
     DecArgs a{};
     a.n = n; a.d = d; a.x = x; a.fn = reinterpret_cast<const u32x4*>(fn_packed); a.mixes_out = mixes;
@@ -2214,8 +2408,8 @@ int hc_pre(const hc_bf16* x, const float* pre_mix, int64_t n, int hc, int d, hc_
   if (n == 0) return HC_OK;
   if ((rc = check_device())) return rc;
   RowArgs a{};
-  a.n = n; a.d = d; a.x = x; a.pre_in = pre_mix; a.y_out = y; a.xtok = kHC * d; a.xstr = d;
-  return launch_row(false, true, false, a, (hipStream_t)stream, "hc_pre");
+  a.n = n; a.d = d; a.x = x; a.pre_in = pre_mix; a.y_out = y; a.xtok = hc * d; a.xstr = d;
+  return launch_row(false, true, false, a, (hipStream_t)stream, "hc_pre", hc);
 }
 
 int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const float* comb, int64_t n, int hc,
@@ -2230,8 +2424,8 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
   if ((rc = check_device())) return rc;
   RowArgs a{};
   a.n = n; a.d = d; a.delta = delta; a.x = x; a.post_in = post; a.comb_in = comb; a.x_out = x_out;
-  a.xtok = kHC * d; a.xstr = d;
-  return launch_row(true, false, false, a, (hipStream_t)stream, "hc_post");
+  a.xtok = hc * d; a.xstr = d;
+  return launch_row(true, false, false, a, (hipStream_t)stream, "hc_post", hc);
 }
 
 size_t hc_boundary_workspace_bytes(int64_t n, int hc, int d) { return hc_workspace_bytes(n, hc, d); }
@@ -2267,6 +2461,7 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
   if (norm && p->d > kRowChunk * kRowMaxChunks * 2)
     return fail(HC_ENOTSUP, "RMSNorm of the read row supports d <= %d", kRowChunk * kRowMaxChunks * 2);
   if (flags & HC_BOUNDARY_SINGLE_LAUNCH) {
+    if (p->hc != kHC) return fail(HC_ENOTSUP, "the single-launch schedule needs hc=4");
     if (expanded || x_mean) return fail(HC_ENOTSUP, "the single-launch schedule takes neither expanded streams nor x_mean_out");
     if (phases != 3) return fail(HC_EINVAL, "the single-launch schedule has no halves (use hc_boundary)");
     if (!mix) return fail(HC_EINVAL, "the single-launch schedule needs fn_packed");
@@ -2276,7 +2471,7 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
   if (p->n == 0) return HC_OK;
   if ((rc = check_device())) return rc;
   const hipStream_t st = (hipStream_t)stream;
-  const int xtok = expanded ? p->d : kHC * p->d;   // expanded: every stream reads x
+  const int xtok = expanded ? p->d : p->hc * p->d;   // expanded: every stream reads x
   const int xstr = expanded ? 0 : p->d;
 
   if (!mix) {  // stack exit: write, read (+ norm); no projection; one kernel, the first phase
@@ -2285,7 +2480,7 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
     r.n = p->n; r.d = p->d; r.x = p->x; r.delta = p->delta; r.post_in = p->post_in; r.comb_in = p->comb_in;
     r.pre_in = p->pre_in; r.gamma = p->gamma; r.x_out = p->x_out; r.y_out = p->y_out; r.rms_eps = p->rms_eps;
     r.xtok = xtok; r.xstr = xstr; r.x_mean = x_mean;
-    return launch_row(post, true, norm, r, st, "hc_boundary (exit)");
+    return launch_row(post, true, norm, r, st, "hc_boundary (exit)", p->hc);
   }
   if (flags & HC_BOUNDARY_SINGLE_LAUNCH) {
     FusedArgs f{};
@@ -2296,6 +2491,43 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
     f.iters = p->iters; f.hc_eps = p->hc_eps; f.norm_eps = p->norm_eps; f.rms_eps = p->rms_eps;
     return launch_fused(post, fresh ? kFreshPre : kGivenPre, norm, f, p->workspace, p->workspace_bytes, st,
                         "hc_boundary");
+  }
+  if (p->hc != kHC) {
+    // hc 2 or 8: the write, the projection, the split and the read as separate
+    // launches; begin does the write (and a read from a given pre), end the rest
+    const int hc = p->hc, d = p->d;
+    float* mixes = p->mixes_out;
+    if (!mixes) {
+      if ((rc = check_generic_ws(p->n, hc, d, p->workspace, p->workspace_bytes, "hc_boundary"))) return rc;
+      mixes = reinterpret_cast<float*>(static_cast<char*>(p->workspace) + generic_mixes_offset(d));
+    }
+    RowArgs r{};
+    r.n = p->n; r.d = d; r.x = p->x; r.delta = p->delta; r.post_in = p->post_in; r.comb_in = p->comb_in;
+    r.gamma = p->gamma; r.x_out = p->x_out; r.y_out = p->y_out; r.rms_eps = p->rms_eps;
+    r.xtok = xtok; r.xstr = xstr;
+    if ((phases & 1) && (post || !fresh)) {
+      RowArgs w = r;
+      w.pre_in = fresh ? nullptr : p->pre_in;
+      w.x_mean = x_mean;
+      if ((rc = launch_row(post, !fresh, !fresh && norm, w, st, "hc_boundary (write)", hc))) return rc;
+    }
+    if (phases & 2) {
+      const hc_bf16* src = post ? p->x_out : p->x;    // X'
+      const int stok = post ? hc * d : xtok, sstr = post ? d : xstr;
+      if ((rc = launch_mixes_generic(hc, src, stok, sstr, p->fn_packed, p->n, d, p->norm_eps, mixes, st,
+                                     "hc_boundary")))
+        return rc;
+      if ((rc = launch_split(hc, mixes, p->hc_scale, p->hc_base, p->n, p->iters, p->hc_eps, p->pre_out,
+                             p->post_out, p->comb_out, st)))
+        return rc;
+      if (fresh) {
+        RowArgs rd = r;
+        rd.x = src; rd.xtok = stok; rd.xstr = sstr; rd.delta = nullptr; rd.post_in = nullptr; rd.comb_in = nullptr;
+        rd.x_out = nullptr; rd.pre_in = p->pre_out; rd.x_mean = post ? nullptr : x_mean;
+        return launch_row(false, true, norm, rd, st, "hc_boundary (read)", hc);
+      }
+    }
+    return HC_OK;
   }
   if (phases == 3 && !fresh && !norm && decode_shape(p->n, p->d)) {
     DecArgs a{};

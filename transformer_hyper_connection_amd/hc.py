@@ -163,8 +163,10 @@ def hc_split_sinkhorn(mixes, hc_scale, hc_base, hc_mult: int = 4, sinkhorn_iters
     """mixes [..., (2+hc)*hc] -> (pre [..., hc], post [..., hc], comb [..., hc, hc])."""
     dev = mixes.device
     _need(mixes, "mixes", torch.float32)
-    _need(hc_scale, "hc_scale", torch.float32, dev)
-    _need(hc_base, "hc_base", torch.float32, dev)
+    _need(hc_scale, "hc_scale", torch.float32, dev, (3,))
+    _need(hc_base, "hc_base", torch.float32, dev, ((2 + hc_mult) * hc_mult,))
+    if mixes.dim() < 1 or mixes.shape[-1] != (2 + hc_mult) * hc_mult:
+        raise ValueError(f"mixes: last dimension {tuple(mixes.shape)[-1:]} is not (2+hc)*hc for hc={hc_mult}")
     lead = tuple(mixes.shape[:-1])
     n = mixes.numel() // mixes.shape[-1]
     pre = torch.empty(*lead, hc_mult, dtype=torch.float32, device=dev)
@@ -236,15 +238,16 @@ def _prepare_boundary(x, *, delta=None, post_in=None, comb_in=None, pre_in=None,
                       hc_base=None, hc_scale=None, gamma=None, iters: int = 20, hc_eps: float = 1e-6,
                       norm_eps: float = 1e-6, rms_eps: float = 1e-6, out: dict | None = None,
                       want_mixes: bool = False, single_launch: bool = False, x_expanded: bool = False,
-                      want_mean: bool = False):
+                      want_mean: bool = False, hc_mult: int = 4):
     """Checks the arguments of one boundary call, allocates missing outputs and
-    fills the C argument struct.  Returns (struct, outputs)."""
+    fills the C argument struct.  Returns (struct, outputs).  hc_mult is the
+    number of streams of an expanded x (otherwise x's shape gives it)."""
     dev = x.device
     _need(x, "x", torch.bfloat16)
     if x_expanded:                   # x [..., d]: every stream is that row
         if x.dim() < 1:
             raise ValueError("an expanded x must be [..., d]")
-        lead, d, hc = tuple(x.shape[:-1]), x.shape[-1], 4
+        lead, d, hc = tuple(x.shape[:-1]), x.shape[-1], hc_mult
         n = 1
         for v in lead:
             n *= v
@@ -307,8 +310,8 @@ def hc_boundary(x, **kw):
     delta, post_in, comb_in, pre_in, fn_packed, hc_base, hc_scale, gamma, iters,
     hc_eps, norm_eps, rms_eps, out, want_mixes, single_launch (the
     HC_BOUNDARY_SINGLE_LAUNCH schedule), x_expanded (x is [..., d], every
-    stream that row: HC_BOUNDARY_X_EXPANDED), want_mean (the mean over the
-    streams, "x_mean").  Returns a dict with x_out (None at a block entry), y,
+    stream that row: HC_BOUNDARY_X_EXPANDED; hc_mult then gives the number of
+    streams), want_mean (the mean over the streams, "x_mean").  Returns a dict with x_out (None at a block entry), y,
     and pre/post/comb (+ mixes) unless fn_packed is None.
     ``out`` may hold preallocated outputs under the same keys (and a
     "workspace"); they are used as given."""

@@ -116,23 +116,24 @@ def outlier_columns(workload: str, tensor: int, d: int = D, frac: float = 0.01,
 T_X, T_DELTA, T_FN, T_PRE_IN, T_POST_IN, T_COMB_IN, T_GAMMA, T_OUTLIER, T_DELTA2, T_FN2 = range(10)
 
 
-def boundary_inputs(workload: str, t0: int = 0, t1: int | None = None, d: int = D):
+def boundary_inputs(workload: str, t0: int = 0, t1: int | None = None, d: int = D, hc: int = HC):
     """Inputs of one fused boundary call for tokens [t0, t1).
 
-    Returns a dict: x [t,4,d] u16, delta [t,d] u16, pre_in [t,4], post_in [t,4],
-    comb_in [t,4,4], hc_fn/hc_base/hc_scale, gamma [d] (float32 unless noted).
-    "stress" scales 1% of the feature columns of x by 30 (all four streams).
+    Returns a dict: x [t,hc,d] u16, delta [t,d] u16, pre_in [t,hc], post_in
+    [t,hc], comb_in [t,hc,hc], hc_fn/hc_base/hc_scale, gamma [d] (float32
+    unless noted).  "stress" scales 1% of the feature columns of x by 30 (all
+    streams).  hc other than 4 draws the same distributions at that width.
     """
     n = WORKLOAD_TOKENS[workload]
     t1 = n if t1 is None else t1
     col = outlier_columns(workload, T_OUTLIER, d) if workload == "stress" else None
-    fn, base, scale = hc_params(workload, T_FN, HC, d)
+    fn, base, scale = hc_params(workload, T_FN, hc, d)
     return {
-        "x": token_normal(workload, T_X, (HC, d), t0, t1, col_scale=col),
+        "x": token_normal(workload, T_X, (hc, d), t0, t1, col_scale=col),
         "delta": token_normal(workload, T_DELTA, (d,), t0, t1),
-        "pre_in": token_uniform(workload, T_PRE_IN, HC, 0.0, 1.0, t0, t1),
-        "post_in": token_uniform(workload, T_POST_IN, HC, 0.0, 2.0, t0, t1),
-        "comb_in": token_dirichlet_columns(workload, T_COMB_IN, HC, t0, t1),
+        "pre_in": token_uniform(workload, T_PRE_IN, hc, 0.0, 1.0, t0, t1),
+        "post_in": token_uniform(workload, T_POST_IN, hc, 0.0, 2.0, t0, t1),
+        "comb_in": token_dirichlet_columns(workload, T_COMB_IN, hc, t0, t1),
         "hc_fn": fn, "hc_base": base, "hc_scale": scale,
         "gamma": gamma(workload, T_GAMMA, d),
     }
