@@ -93,15 +93,18 @@ def test_packed_and_workspace_bytes(L):
 
 
 def test_packed_and_workspace_bytes_other_hc(L):
-    # hc = 2 and 8: the packed weight is the fp32 weight itself
-    assert L.hc_fn_packed_bytes(2, 5120) == 8 * 2 * 5120 * 4
-    assert L.hc_fn_packed_bytes(8, 4096) == 80 * 8 * 4096 * 4
+    # hc = 2 and 8: per 32-feature step, 3 terms x ceil(mix/16) tiles of 1 KB (mix = 8 -> 3, 80 -> 15)
+    assert L.hc_fn_packed_bytes(2, 5120) == (2 * 5120 // 32) * 3 * 1024
+    assert L.hc_fn_packed_bytes(8, 4096) == (8 * 4096 // 32) * 15 * 1024
     assert L.hc_fn_packed_bytes(8, 100) == 0
     assert L.hc_fn_packed_bytes(16, 4096) == 0
-    # the workspace holds the mixes after the hc = 4 control block and decode region of the same d
+    # records [S][n][recw] after the hc = 4 control block and decode region of the same d; S is the
+    # largest divisor of hc*d/64 with at most ~512 workgroups of 128 tokens, 64 at most; recw = mix + 1
+    # rounded up to 4 floats (12 at hc = 2, 84 at hc = 8)
     decode = 256 + 8 * 20 * 16 * 25 * 8
-    assert L.hc_workspace_bytes(4096, 8, 5120) == 8192 + decode + 4096 * 80 * 4
-    assert L.hc_workspace_bytes(100, 2, 320) == 8192 + 3328       # 100 x 8 floats, rounded up to 256 B
+    assert L.hc_workspace_bytes(4096, 8, 5120) == 8192 + decode + 16 * 4096 * 84 * 4
+    assert L.hc_workspace_bytes(100, 2, 320) == 8192 + 10 * 100 * 12 * 4     # 10 chunks of 64: S = 10
+    assert L.hc_workspace_bytes(40, 8, 1024) == 8192 + (256 + 8 * 4 * 16 * 25 * 8) + 64 * 40 * 84 * 4
     assert L.hc_workspace_bytes(0, 8, 5120) == 0
     assert L.hc_boundary_workspace_bytes(7, 2, 1024) == L.hc_workspace_bytes(7, 2, 1024)
 
@@ -131,8 +134,8 @@ def test_null_misaligned_negative(L):
     assert L.hc_mixes(P, P, 16, 4, 64, 1e-6, None, P, P, 20, 1e-6, P, None, P, *W, S) == H.HC_EINVAL  # partial split
     assert L.hc_split_sinkhorn(P, P, P, 16, 4, 0, 1e-6, P, P, P, S) == H.HC_EINVAL
     assert L.hc_split_sinkhorn(P, P, P, 16, 3, 20, 1e-6, P, P, P, S) == H.HC_ENOTSUP
-    # hc = 8 without a mixes output keeps the mixes in the workspace: it must hold them
-    assert L.hc_mixes(P, P, 16, 8, 64, 1e-6, None, P, P, 20, 1e-6, P, P, P, P, 4096, S) == H.HC_EINVAL
+    # hc = 8 keeps per-slice records in the workspace: it must hold them
+    assert L.hc_mixes(P, P, 16, 8, 64, 1e-6, P, None, None, 20, 1e-6, None, None, None, P, 4096, S) == H.HC_EINVAL
     assert b"workspace" in L.hc_last_error()
     assert L.hc_mixes(P, P, 16, 8, 64, 1e-6, None, P, P, 20, 1e-6, P, P, P, MIS, 1 << 30, S) == H.HC_EINVAL
     assert L.hc_split_sinkhorn(P, P, None, 16, 4, 20, 1e-6, P, P, P, S) == H.HC_EINVAL

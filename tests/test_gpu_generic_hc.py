@@ -32,11 +32,25 @@ def _dev_params(s):
 
 
 @pytest.mark.parametrize("hc", HCS)
-def test_packed_weight_is_the_weight(hc):
+def test_packed_weight_terms(hc):
+    """Packed column q = 16*tile + lane%16 of a 32-feature step holds term
+    q // mixp (hi, mid, lo) of row q % mixp at features 8*(lane//16)..+7:
+    hi is the nearest bf16 of the weight, hi + mid + lo the weight itself
+    (normal values), and the padding rows are zero."""
     say(f"[hc={hc}] pack d=1024")
-    s = _inputs(hc, 1, 1024)
-    p = H.hc_fn_pack(f32_dev(s["hc_fn"]), hc=hc)
-    assert np.array_equal(p.cpu().numpy().view(np.float32).reshape(s["hc_fn"].shape), s["hc_fn"])
+    d = 1024
+    s = _inputs(hc, 1, d)
+    mix, K = (2 + hc) * hc, hc * d
+    rt = (mix + 15) // 16
+    p = H.hc_fn_pack(f32_dev(s["hc_fn"]), hc=hc).cpu().numpy().view(np.uint16)
+    v = N.bits_to_f64(p.reshape(K // 32, 3 * rt, 4, 16, 8))         # [step][tile][lane//16][lane%16][8]
+    cols = v.transpose(1, 3, 0, 2, 4).reshape(3 * rt * 16, K)         # [packed column][feature]
+    terms = cols.reshape(3, rt * 16, K)
+    assert not terms[:, mix:].any()
+    hi, mid, lo = terms[:, :mix]
+    w = s["hc_fn"].astype(np.float64)
+    assert np.array_equal(hi, torch.from_numpy(s["hc_fn"]).to(torch.bfloat16).double().numpy())
+    assert np.array_equal((hi + mid) + lo, w)
 
 
 @pytest.mark.parametrize("hc", HCS)
@@ -81,7 +95,7 @@ def test_mixes(hc, n, d):
     assert_coef_close(host_f32(pre), rp, "pre")
     assert_coef_close(host_f32(post), rq, "post")
     assert_coef_close(host_f32(comb), rc, "comb")
-    # without a mixes output the mixes live in the workspace between the two launches
+    # without a mixes output: the same coefficients
     pre2, post2, comb2 = H.hc_mixes(X, p["fn_packed"], p["hc_scale"], p["hc_base"])
     assert_bits_equal(host_f32(pre2).view(np.uint32), host_f32(pre).view(np.uint32), "pre (workspace mixes)")
     assert_bits_equal(host_f32(comb2).view(np.uint32), host_f32(comb).view(np.uint32), "comb (workspace mixes)")
@@ -119,8 +133,8 @@ def test_boundary(hc, n, d, fresh, norm, with_delta):
 @pytest.mark.parametrize("hc", HCS)
 @pytest.mark.parametrize("fresh", [False, True])
 def test_boundary_halves_and_workspace_mixes(hc, fresh):
-    """begin + end equals the whole call bit for bit, with the mixes kept by
-    the caller or only in the workspace."""
+    """begin + end equals the whole call bit for bit, with or without a mixes
+    output."""
     say(f"[hc={hc}] boundary halves fresh={fresh}")
     s, _, dev = _boundary(hc, 130, 2048, fresh, True, True)
     X = bf16_dev(s["x"])
@@ -173,8 +187,7 @@ def test_stack_exit(hc):
 
 
 def test_hc4_workspace_survives_other_hc_calls():
-    """A workspace shared with hc = 8 calls (mixes kept in the workspace)
-    keeps the hc = 4 decode schedule's words intact: the hc = 4 decode
+    """A workspace shared with hc = 8 calls (their per-slice records) keeps the hc = 4 decode schedule's words intact: the hc = 4 decode
     boundary before and after gives the same bits."""
     say("[hc=4/8] shared workspace")
     s4 = synth.boundary_inputs("decode", 0, 64, 1024)

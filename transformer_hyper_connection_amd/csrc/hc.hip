@@ -176,103 +176,6 @@ __global__ void __launch_bounds__(256) split_kernel(const float* __restrict__ mi
                          comb + t * HC * HC);
 }
 
-// ------------------------------------------- projection for hc other than 4
-// mixes[t, q] = r[t] * sum_c fn[q, c] x[t, c] with r[t] = 1/sqrt(mean_c x^2 +
-// eps) ("Source layer, pairs pooled": the RMS-scaled projection), in plain
-// fp32 multiply-adds on the weights as given (hc_fn_pack copies them for hc
-// other than 4).  A workgroup takes kGT tokens and GM projection rows; the
-// flattened hc*d features are dealt out to its 256 lanes in groups of 8, each
-// lane keeping kGT x GM partial dots and kGT partial sums of squares, which
-// are then summed over the lanes in a fixed order (the same bits every call).
-constexpr int kGT = 8;
-
-struct GenMixArgs {
-  const hc_bf16* x;
-  const float* fn;     // [mix][K] fp32
-  float* mixes;        // [n][mix]
-  int64_t n;
-  int xtok, xstr;      // elements per token / per stream of x (stride 0: expanded)
-  int d, K, mix;
-  float norm_eps;
-};
-
-template <int GM>
-__global__ void __launch_bounds__(256) mixes_generic_kernel(const GenMixArgs a) {
-  const int64_t t0 = (int64_t)blockIdx.x * kGT;
-  const int m0 = blockIdx.y * GM;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float acc[kGT][GM], ss[kGT];
-#pragma unroll
-  for (int tt = 0; tt < kGT; ++tt) {
-    ss[tt] = 0.f;
-#pragma unroll
-    for (int mm = 0; mm < GM; ++mm) acc[tt][mm] = 0.f;
-  }
-  bool mrow[GM];
-#pragma unroll
-  for (int mm = 0; mm < GM; ++mm) mrow[mm] = m0 + mm < a.mix;
-  const int groups = a.K / 8;
-  for (int g = threadIdx.x; g < groups; g += 256) {
-    const int c = g * 8;
-    const int j = c / a.d, i = c - j * a.d;
-    float xv[kGT][8];
-#pragma unroll
-    for (int tt = 0; tt < kGT; ++tt) {
-      const int64_t t = t0 + tt;
-      const u32x4 v = t < a.n ? ld_stream(reinterpret_cast<const u32x4*>(a.x + t * a.xtok + j * a.xstr + i))
-                              : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        xv[tt][2 * e] = bf_lo(v[e]);
-        xv[tt][2 * e + 1] = bf_hi(v[e]);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss[tt] = fmaf(xv[tt][e], xv[tt][e], ss[tt]);
-    }
-#pragma unroll
-    for (int mm = 0; mm < GM; ++mm) {
-      if (!mrow[mm]) continue;
-      const f32x4* wp = reinterpret_cast<const f32x4*>(a.fn + (size_t)(m0 + mm) * a.K + c);
-      const f32x4 w0 = wp[0], w1 = wp[1];
-      const float w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-#pragma unroll
-      for (int tt = 0; tt < kGT; ++tt)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[tt][mm] = fmaf(w[e], xv[tt][e], acc[tt][mm]);
-    }
-  }
-  // butterfly sums within each wave (every lane ends with the same bits),
-  // then the four waves in order
-  __shared__ float red[4][kGT * (GM + 1)];
-  auto wave_sum = [&](float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-  };
-#pragma unroll
-  for (int tt = 0; tt < kGT; ++tt) {
-#pragma unroll
-    for (int mm = 0; mm < GM; ++mm) {
-      const float v = wave_sum(acc[tt][mm]);
-      if (lane == 0) red[wave][tt * GM + mm] = v;
-    }
-    const float v = wave_sum(ss[tt]);
-    if (lane == 0) red[wave][kGT * GM + tt] = v;
-  }
-  __syncthreads();
-  if (threadIdx.x < kGT * GM) {
-    const int tt = threadIdx.x / GM, mm = threadIdx.x % GM;
-    const int64_t t = t0 + tt;
-    if (t < a.n && m0 + mm < a.mix) {
-      const int q = tt * GM + mm, qs = kGT * GM + tt;
-      const float dot = ((red[0][q] + red[1][q]) + red[2][q]) + red[3][q];
-      const float sq = ((red[0][qs] + red[1][qs]) + red[2][qs]) + red[3][qs];
-      const float r = 1.0f / sqrtf(sq / (float)a.K + a.norm_eps);
-      a.mixes[t * a.mix + m0 + mm] = dot * r;
-    }
-  }
-}
-
 // ------------------------------------------------------------------ weight pack
 // Each fp32 weight w is split into three bf16 terms, w = hi + mid + lo, each
 // the nearest-even rounding of what is left (exact but for subnormal tails).
@@ -320,6 +223,276 @@ __global__ void __launch_bounds__(256) pack_kernel(const float* __restrict__ fn,
     w[e2] = pack_bf16(v[0], v[1]);
   }
   out[idx] = u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// ------------------------------------------- projection for hc other than 4
+// The arithmetic of the hc = 4 kernels (bf16 streams times the three bf16
+// terms of each fp32 weight on the matrix cores, fp32 accumulation) in a
+// plainer schedule: the projection reads the written streams back instead of
+// taking them from the write.  Packed layout for hc other than 4, 16-byte lane
+// records [step = c/32][tile ct][lane 0..63] -> 8 bf16 (c the flattened
+// feature j*d + i): column n = lane%16 of tile ct is packed column q = 16*ct
+// + n, term q / MIXP (hi, mid, lo) of projection row q % MIXP (zero for rows
+// >= MIX), at features 32*step + 8*(lane/16) + 0..7.  The three terms of a
+// row sit in tiles rt, rt + RT, rt + 2 RT at the same column and so meet in
+// the same accumulator register.
+template <int HC>
+struct GShape {
+  static constexpr int MIX = (2 + HC) * HC;
+  static constexpr int RT = (MIX + 15) / 16;        // 16-row tiles per term
+  static constexpr int MIXP = RT * 16;
+  static constexpr int NCT = 3 * RT;                // packed tiles per 32-feature step
+  static constexpr int RECW = (MIX + 1 + 3) & ~3;   // record: MIX dots, sum x^2 (16 B multiple)
+};
+
+template <int HC>
+__global__ void __launch_bounds__(256) gpack_kernel(const float* __restrict__ fn, int K,
+                                                    u32x4* __restrict__ out, int records) {
+  using G = GShape<HC>;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= records) return;
+  const int lane = idx & 63, ct = (idx >> 6) % G::NCT, step = (idx >> 6) / G::NCT;
+  const int q = 16 * ct + (lane & 15), term = q / G::MIXP, row = q % G::MIXP;
+  const float* src = fn + (size_t)row * K + 32 * step + 8 * (lane >> 4);
+  u32 w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a = row < G::MIX ? split_term(src[2 * e], term) : 0.f;
+    const float b = row < G::MIX ? split_term(src[2 * e + 1], term) : 0.f;
+    w[e] = pack_bf16(a, b);
+  }
+  out[idx] = u32x4{w[0], w[1], w[2], w[3]};
+}
+
+constexpr int kGTok = 128;     // tokens per workgroup: 4 waves x 2 row tiles of 16
+constexpr int kGChunk = 64;    // features per pipeline chunk (two 32-feature steps)
+constexpr int kGPD = 2;        // chunks of stream loads in flight ahead of the matrix work
+
+struct GMixArgs {
+  const hc_bf16* x;
+  const u32x4* fn;     // packed as above
+  float* rec;          // [S][n][RECW] per-slice dots and sums of squares
+  int64_t n;
+  int xtok, xstr;      // elements per token / per stream of x (stride 0: expanded)
+  int d, S, Fs;        // slices of the flattened feature range, Fs = hc*d/S features each
+};
+
+// One workgroup: 128 tokens x one feature slice.  Per 64-feature chunk the
+// weight tiles are staged through registers into a double-buffered LDS area
+// shared by the four waves; each wave streams the A tiles of its 32 tokens
+// straight from memory, kGPD chunks ahead.
+template <int HC>
+__global__ void __launch_bounds__(256, 2) gmix_kernel(const GMixArgs a) {
+  using G = GShape<HC>;
+  constexpr int NCT = G::NCT, RT = G::RT;
+  constexpr int BREC = 2 * NCT * 64;            // 16-byte weight records per chunk
+  constexpr int BPT = (BREC + 255) / 256;
+  __shared__ u32x4 w_lds[2][2 * NCT * 64];      // [buffer][step][tile][lane]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // consecutive workgroups go to different XCDs: slice-major so the workgroups
+  // reading one slice of the weights share an XCD (and its L2) where S allows
+  const int slice = blockIdx.x % a.S, group = blockIdx.x / a.S;
+  const int64_t tw = (int64_t)group * kGTok + wave * 32;
+  const hc_bf16* xr[2];
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti) {
+    const int64_t t = tw + 16 * ti + (lane & 15);
+    xr[ti] = a.x + (t < a.n ? t : 0) * a.xtok;    // rows past n read token 0 and are never stored
+  }
+  const int kg = 8 * (lane >> 4);
+  const int c0 = slice * a.Fs;
+  const int nch = a.Fs / kGChunk;
+
+  auto load_a = [&](int ch, u32x4 (&A)[2][2]) {
+    const int c = c0 + ch * kGChunk;              // a chunk never crosses a stream (d % 64 == 0)
+    const int j = c / a.d, i = c - j * a.d + kg;
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) A[ti][st] = ld_stream(reinterpret_cast<const u32x4*>(xr[ti] + j * a.xstr + i + 32 * st));
+  };
+  auto load_b = [&](int ch, u32x4 (&Bs)[BPT]) {
+    const u32x4* src = a.fn + (size_t)((c0 + ch * kGChunk) / 32) * NCT * 64;
+#pragma unroll
+    for (int r = 0; r < BPT; ++r) {
+      const int idx = threadIdx.x + 256 * r;
+      if (idx < BREC) Bs[r] = src[idx];
+    }
+  };
+  auto store_b = [&](int buf, const u32x4 (&Bs)[BPT]) {
+#pragma unroll
+    for (int r = 0; r < BPT; ++r) {
+      const int idx = threadIdx.x + 256 * r;
+      if (idx < BREC) w_lds[buf][idx] = Bs[r];
+    }
+  };
+
+  f32x4 acc[2][NCT];
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[ti][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ss[2] = {0.f, 0.f};
+  // the weight loads of a chunk are issued before the stream loads that run
+  // kGPD chunks ahead, so that waiting for the former (the load counter is in
+  // order) does not wait for the latter
+  u32x4 Aq[kGPD + 1][2][2], Bs[BPT];
+  load_b(0, Bs);
+#pragma unroll
+  for (int p = 0; p < kGPD; ++p)
+    if (p < nch) load_a(p, Aq[p]);
+  store_b(0, Bs);
+  __syncthreads();
+  for (int ch = 0; ch < nch; ++ch) {
+    const bool more = ch + 1 < nch;
+    if (more) load_b(ch + 1, Bs);
+    if (ch + kGPD < nch) load_a(ch + kGPD, Aq[kGPD]);
+    const u32x4* wb = w_lds[ch & 1];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, wb[(st * NCT + ct) * 64 + lane]);
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+          acc[ti][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Aq[0][ti][st]), b,
+                                                                acc[ti][ct], 0, 0, 0);
+      }
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss[ti] = dot2_bf16(Aq[0][ti][st][e], Aq[0][ti][st][e], ss[ti]);
+    if (more) store_b((ch + 1) & 1, Bs);
+    __syncthreads();                              // next weights in place; this chunk's reads done
+#pragma unroll
+    for (int p = 0; p < kGPD; ++p)
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) Aq[p][ti][st] = Aq[p + 1][ti][st];
+  }
+
+  // sums of squares: the four lanes holding one token row (lane, +16, +32, +48)
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti) {
+    ss[ti] += __shfl_xor(ss[ti], 16);
+    ss[ti] += __shfl_xor(ss[ti], 32);
+  }
+  float* rs = a.rec + (size_t)slice * a.n * G::RECW;
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = 16 * rt + (lane & 15);
+      if (row < G::MIX) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t t = tw + 16 * ti + 4 * (lane >> 4) + r;   // accumulator row = token
+          if (t < a.n) rs[t * G::RECW + row] = (acc[ti][rt][r] + acc[ti][rt + RT][r]) + acc[ti][rt + 2 * RT][r];
+        }
+      }
+    }
+    const int64_t t = tw + 16 * ti + lane;
+    if (lane < 16 && t < a.n) rs[t * G::RECW + G::MIX] = ss[ti];
+  }
+}
+
+struct GFinArgs {
+  const float* rec;
+  const float* hc_scale;
+  const float* hc_base;
+  float* mixes_out;    // or NULL
+  float* pre_out;      // pre/post/comb, or all NULL
+  float* post_out;
+  float* comb_out;
+  int64_t n;
+  int S, K, iters;
+  float norm_eps, hc_eps;
+};
+
+// hc lanes per token, lane j owning stream j: the slices' records summed in
+// slice order, the RMS scale applied ("Source layer, pairs pooled":
+// Block.hc_mixes), then the split and the Sinkhorn rounds of "Reading
+// weights" with lane j holding comb row j (column sums across the hc lanes).
+template <int HC>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < HC; o <<= 1) v += __shfl_xor(v, o);   // same bits in every lane of the group
+  return v;
+}
+
+template <int HC>
+__global__ void __launch_bounds__(256) gfinish_kernel(const GFinArgs a) {
+  using G = GShape<HC>;
+  const int j = threadIdx.x % HC;
+  const int64_t tq = (int64_t)blockIdx.x * (256 / HC) + threadIdx.x / HC;
+  const bool valid = tq < a.n;
+  const int64_t t = valid ? tq : 0;   // lanes past n compute on token 0 (they take part in the shuffles)
+  const float* r = a.rec + t * G::RECW;
+  const size_t sstride = (size_t)a.n * G::RECW;
+  float lp = r[j], lq = r[HC + j], ss = r[G::MIX], lc[HC];
+#pragma unroll
+  for (int k = 0; k < HC; ++k) lc[k] = r[2 * HC + j * HC + k];
+#pragma unroll 4
+  for (int s = 1; s < a.S; ++s) {
+    r += sstride;
+    lp = lp + r[j]; lq = lq + r[HC + j]; ss = ss + r[G::MIX];
+#pragma unroll
+    for (int k = 0; k < HC; ++k) lc[k] = lc[k] + r[2 * HC + j * HC + k];
+  }
+  const float rx = 1.0f / sqrtf(ss / (float)a.K + a.norm_eps);
+  lp = lp * rx;
+  lq = lq * rx;
+#pragma unroll
+  for (int k = 0; k < HC; ++k) lc[k] = lc[k] * rx;
+  if (a.mixes_out && valid) {
+    float* m = a.mixes_out + t * G::MIX;
+    m[j] = lp;
+    m[HC + j] = lq;
+#pragma unroll
+    for (int k = 0; k < HC; ++k) m[2 * HC + j * HC + k] = lc[k];
+  }
+  if (!a.pre_out) return;
+  const float s0 = a.hc_scale[0], s1 = a.hc_scale[1], s2 = a.hc_scale[2], eps = a.hc_eps;
+  const float pre = sigmoidf_(lp * s0 + a.hc_base[j]) + eps;
+  const float post = 2.0f * sigmoidf_(lq * s1 + a.hc_base[HC + j]);
+  float A[HC], mxr = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < HC; ++k) {
+    A[k] = lc[k] * s2 + a.hc_base[2 * HC + j * HC + k];
+    mxr = fmaxf(mxr, A[k]);
+  }
+  float rs = 0.f;
+#pragma unroll
+  for (int k = 0; k < HC; ++k) {
+    A[k] = expf(A[k] - mxr);
+    rs = rs + A[k];
+  }
+  const float rinv = __builtin_amdgcn_rcpf(rs);
+#pragma unroll
+  for (int k = 0; k < HC; ++k) A[k] = A[k] * rinv + eps;
+  auto col_norm = [&]() {
+#pragma unroll
+    for (int k = 0; k < HC; ++k) A[k] = A[k] * __builtin_amdgcn_rcpf(group_sum<HC>(A[k]) + eps);
+  };
+  col_norm();
+  for (int it = 1; it < a.iters; ++it) {
+    float r2 = A[0];
+#pragma unroll
+    for (int k = 1; k < HC; ++k) r2 = r2 + A[k];
+    const float inv = __builtin_amdgcn_rcpf(r2 + eps);
+#pragma unroll
+    for (int k = 0; k < HC; ++k) A[k] = A[k] * inv;
+    col_norm();
+  }
+  if (valid) {
+    a.pre_out[t * HC + j] = pre;
+    a.post_out[t * HC + j] = post;
+#pragma unroll
+    for (int k = 0; k < HC; ++k) a.comb_out[t * HC * HC + j * HC + k] = A[k];
+  }
 }
 
 // The matrix-core step for one (A tile, 32-feature step, stream): the five
@@ -2252,12 +2425,28 @@ int launch_row(bool post, bool pre, bool norm, const RowArgs& a, hipStream_t st,
 }
 
 // ------------------------------------------------------ hc other than 4
-// workspace of the hc != 4 path: the mixes, when the caller does not keep
-// them, placed after the control block and the decode region of the same d so
-// that a workspace shared with hc = 4 calls keeps their words intact
-size_t generic_mixes_offset(int d) { return kCtrlBytes + decode_region_bytes(d); }
+int gen_recw(int hc) { return hc == 2 ? GShape<2>::RECW : GShape<8>::RECW; }
+int gen_nct(int hc) { return hc == 2 ? GShape<2>::NCT : GShape<8>::NCT; }
+
+// slices of the flattened feature range: the largest divisor of hc*d/64 (a
+// slice is whole 64-feature chunks) giving at most about 512 workgroups, 64
+// slices at most
+int gen_slices(int64_t n, int hc, int d) {
+  const int64_t groups = (n + kGTok - 1) / kGTok;
+  const int chunks = hc * d / kGChunk;
+  const int64_t want = std::max<int64_t>(1, std::min<int64_t>(64, (512 + groups - 1) / groups));
+  int best = 1;
+  for (int s = 1; s <= want; ++s)
+    if (chunks % s == 0) best = s;
+  return best;
+}
+
+// workspace of the hc != 4 path: the per-slice records, placed after the
+// control block and the decode region of the same d so that a workspace
+// shared with hc = 4 calls keeps their words intact
+size_t gen_rec_offset(int d) { return kCtrlBytes + decode_region_bytes(d); }
 size_t generic_ws_bytes(int64_t n, int hc, int d) {
-  return generic_mixes_offset(d) + (((size_t)n * mix_of(hc) * 4 + 255) & ~(size_t)255);
+  return gen_rec_offset(d) + (size_t)gen_slices(n, hc, d) * n * gen_recw(hc) * 4;
 }
 
 int check_generic_ws(int64_t n, int hc, int d, const void* ws, size_t ws_bytes, const char* what) {
@@ -2265,21 +2454,33 @@ int check_generic_ws(int64_t n, int hc, int d, const void* ws, size_t ws_bytes, 
   if (!ws) return fail(HC_EINVAL, "%s: workspace must not be NULL (need %zu bytes)", what, need);
   if (!aligned16(ws)) return fail(HC_EINVAL, "%s: workspace is not 16-byte aligned", what);
   if (ws_bytes < need) return fail(HC_EINVAL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, need);
+  if ((n + kGTok - 1) / kGTok * gen_slices(n, hc, d) > INT32_MAX)
+    return fail(HC_ENOTSUP, "%s: n=%lld is too large", what, (long long)n);
   return HC_OK;
 }
 
+// projection + split for hc 2 or 8: records into the workspace, then one
+// token per lane sums them and derives mixes / pre, post, comb
 int launch_mixes_generic(int hc, const hc_bf16* x, int xtok, int xstr, const void* fn, int64_t n, int d,
-                         float norm_eps, float* mixes, hipStream_t st, const char* what) {
-  GenMixArgs a{};
-  a.x = x; a.fn = static_cast<const float*>(fn); a.mixes = mixes; a.n = n; a.xtok = xtok; a.xstr = xstr;
-  a.d = d; a.K = hc * d; a.mix = mix_of(hc); a.norm_eps = norm_eps;
-  void* args[] = {&a};
-  const unsigned gx = (unsigned)((n + kGT - 1) / kGT);
-  const hipError_t e =
-      hc == 2 ? hipLaunchKernel(reinterpret_cast<const void*>(&mixes_generic_kernel<8>), dim3(gx, 1), dim3(256),
-                                args, 0, st)
-              : hipLaunchKernel(reinterpret_cast<const void*>(&mixes_generic_kernel<16>),
-                                dim3(gx, (unsigned)((a.mix + 15) / 16)), dim3(256), args, 0, st);
+                         void* ws, GFinArgs f, hipStream_t st, const char* what) {
+  GMixArgs m{};
+  m.x = x; m.fn = static_cast<const u32x4*>(fn); m.n = n; m.xtok = xtok; m.xstr = xstr; m.d = d;
+  m.S = gen_slices(n, hc, d);
+  m.Fs = hc * d / m.S;
+  m.rec = reinterpret_cast<float*>(static_cast<char*>(ws) + gen_rec_offset(d));
+  void* margs[] = {&m};
+  const dim3 mgrid((unsigned)((n + kGTok - 1) / kGTok * m.S));
+  hipError_t e = hipLaunchKernel(hc == 2 ? reinterpret_cast<const void*>(&gmix_kernel<2>)
+                                         : reinterpret_cast<const void*>(&gmix_kernel<8>),
+                                 mgrid, dim3(256), margs, 0, st);
+  int rc = launched(e, what);
+  if (rc) return rc;
+  f.rec = m.rec; f.n = n; f.S = m.S; f.K = hc * d;
+  void* fargs[] = {&f};
+  const int64_t tpb = 256 / hc;                   // tokens per workgroup: hc lanes each
+  e = hipLaunchKernel(hc == 2 ? reinterpret_cast<const void*>(&gfinish_kernel<2>)
+                              : reinterpret_cast<const void*>(&gfinish_kernel<8>),
+                      dim3((unsigned)((n + tpb - 1) / tpb)), dim3(256), fargs, 0, st);
   return launched(e, what);
 }
 
@@ -2317,7 +2518,7 @@ const char* hc_last_error(void) { return g_err; }
 
 size_t hc_fn_packed_bytes(int hc, int d) {
   if (!hc_known(hc) || d <= 0 || d % kCF != 0 || d > kMaxD) return 0;
-  if (hc != kHC) return (size_t)mix_of(hc) * hc * d * 4;   // the fp32 weights as given
+  if (hc != kHC) return (size_t)(hc * d / 32) * gen_nct(hc) * 64 * 16;
   return (size_t)(d / kStepF) * kHC * kNT * 64 * 16;
 }
 
@@ -2328,9 +2529,16 @@ int hc_fn_pack(const float* hc_fn, int hc, int d, void* fn_packed, void* stream)
   HC_REQ(hc_fn);
   HC_REQ(fn_packed);
   if ((rc = check_device())) return rc;
-  if (hc != kHC)
-    return launched(hipMemcpyAsync(fn_packed, hc_fn, hc_fn_packed_bytes(hc, d), hipMemcpyDeviceToDevice,
-                                   (hipStream_t)stream), "hc_fn_pack");
+  if (hc != kHC) {
+    const int recs = (hc * d / 32) * gen_nct(hc) * 64;
+    if (hc == 2)
+      hipLaunchKernelGGL(gpack_kernel<2>, dim3((recs + 255) / 256), dim3(256), 0, (hipStream_t)stream, hc_fn,
+                         hc * d, reinterpret_cast<u32x4*>(fn_packed), recs);
+    else
+      hipLaunchKernelGGL(gpack_kernel<8>, dim3((recs + 255) / 256), dim3(256), 0, (hipStream_t)stream, hc_fn,
+                         hc * d, reinterpret_cast<u32x4*>(fn_packed), recs);
+    return launched(hipGetLastError(), "gpack_kernel");
+  }
   const int records = (d / kStepF) * kHC * kNT * 64;
   hipLaunchKernelGGL(pack_kernel, dim3((records + 255) / 256), dim3(256), 0, (hipStream_t)stream, hc_fn, d,
                      reinterpret_cast<u32x4*>(fn_packed), records);
@@ -2373,13 +2581,15 @@ int hc_mixes(const hc_bf16* x, const void* fn_packed, int64_t n, int hc, int d, 
     return fail(HC_EINVAL, "nothing to compute: mixes and pre/post/comb are all NULL");
   }
   if (n == 0) return HC_OK;
-  if (hc != kHC && !mixes && (rc = check_generic_ws(n, hc, d, workspace, workspace_bytes, "hc_mixes"))) return rc;
+  if (hc != kHC && (rc = check_generic_ws(n, hc, d, workspace, workspace_bytes, "hc_mixes"))) return rc;
   if ((rc = check_device())) return rc;
   if (hc != kHC) {
     const hipStream_t st = (hipStream_t)stream;
-    float* mx = mixes ? mixes : reinterpret_cast<float*>(static_cast<char*>(workspace) + generic_mixes_offset(d));
-    if ((rc = launch_mixes_generic(hc, x, hc * d, d, fn_packed, n, d, norm_eps, mx, st, "hc_mixes"))) return rc;
-    return split ? launch_split(hc, mx, hc_scale, hc_base, n, iters, hc_eps, pre, post, comb, st) : HC_OK;
+    GFinArgs f{};
+    f.hc_scale = hc_scale; f.hc_base = hc_base; f.mixes_out = mixes; f.iters = iters; f.norm_eps = norm_eps;
+    f.hc_eps = hc_eps;
+    if (split) { f.pre_out = pre; f.post_out = post; f.comb_out = comb; }
+    return launch_mixes_generic(hc, x, hc * d, d, fn_packed, n, d, workspace, f, st, "hc_mixes");
   }
   if (decode_shape(n, d)) {
     DecArgs a{};
@@ -2496,11 +2706,7 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
     // hc 2 or 8: the write, the projection, the split and the read as separate
     // launches; begin does the write (and a read from a given pre), end the rest
     const int hc = p->hc, d = p->d;
-    float* mixes = p->mixes_out;
-    if (!mixes) {
-      if ((rc = check_generic_ws(p->n, hc, d, p->workspace, p->workspace_bytes, "hc_boundary"))) return rc;
-      mixes = reinterpret_cast<float*>(static_cast<char*>(p->workspace) + generic_mixes_offset(d));
-    }
+    if ((rc = check_generic_ws(p->n, hc, d, p->workspace, p->workspace_bytes, "hc_boundary"))) return rc;
     RowArgs r{};
     r.n = p->n; r.d = d; r.x = p->x; r.delta = p->delta; r.post_in = p->post_in; r.comb_in = p->comb_in;
     r.gamma = p->gamma; r.x_out = p->x_out; r.y_out = p->y_out; r.rms_eps = p->rms_eps;
@@ -2514,11 +2720,12 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
     if (phases & 2) {
       const hc_bf16* src = post ? p->x_out : p->x;    // X'
       const int stok = post ? hc * d : xtok, sstr = post ? d : xstr;
-      if ((rc = launch_mixes_generic(hc, src, stok, sstr, p->fn_packed, p->n, d, p->norm_eps, mixes, st,
+      GFinArgs f{};
+      f.hc_scale = p->hc_scale; f.hc_base = p->hc_base; f.mixes_out = p->mixes_out; f.pre_out = p->pre_out;
+      f.post_out = p->post_out; f.comb_out = p->comb_out; f.iters = p->iters; f.norm_eps = p->norm_eps;
+      f.hc_eps = p->hc_eps;
+      if ((rc = launch_mixes_generic(hc, src, stok, sstr, p->fn_packed, p->n, d, p->workspace, f, st,
                                      "hc_boundary")))
-        return rc;
-      if ((rc = launch_split(hc, mixes, p->hc_scale, p->hc_base, p->n, p->iters, p->hc_eps, p->pre_out,
-                             p->post_out, p->comb_out, st)))
         return rc;
       if (fresh) {
         RowArgs rd = r;
