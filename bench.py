@@ -12,6 +12,9 @@ the pages' Block.forward).  Inputs are seeded synthetic tensors
 (transformer_hyper_connection_amd.synth, workload "prefill"), resident in HBM
 before timing; several input/output buffer sets rotate.  Prints one JSON line.
 
+Beside the headline line: the decode block's glue (n=128, "decode") and the
+same boundary at hc = 2 and 8 ("other_hc"), each timed by events.
+
 Timing: W untimed warm-up steps; then K steps timed by the host clock between
 two device synchronisations (value, ms_per_step); then K more steps with
 events on the launch stream around each kernel (the roofline: algorithmic
@@ -216,6 +219,42 @@ def decode_block(dev, reps=200):
             "boundary_call_us": round(boundary, 2)}
 
 
+def other_hc(dev, hcs=(2, 8), reps=50):
+    """The same boundary (write, fresh pre, RMSNorm; n=4096, d=5120) at hc = 2
+    and 8, which libhc runs as four plainer launches (row write, matrix-core
+    projection, finish, row read).  Mean microseconds per call by events over
+    reps calls, and the algorithmic bytes of a call."""
+    out = {}
+    for hc in hcs:
+        print(f"[bench] timing hc={hc}", file=sys.stderr, flush=True)
+        s = synth.boundary_inputs("prefill", hc=hc)
+        mix = (2 + hc) * hc
+        call = T.BoundaryCall(bf(s["x"], dev), delta=bf(s["delta"], dev), post_in=f32(s["post_in"], dev),
+                              comb_in=f32(s["comb_in"], dev), fn_packed=T.hc_fn_pack(f32(s["hc_fn"], dev), hc=hc),
+                              hc_base=f32(s["hc_base"], dev), hc_scale=f32(s["hc_scale"], dev),
+                              gamma=f32(s["gamma"], dev))
+        for _ in range(5):
+            call.run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            call.run()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        # per token: X, X' (hc*d bf16 each), delta, z (d bf16 each), post_in, comb_in, pre/post/comb out;
+        # per call: hc_fn (fp32), base, scale, gamma
+        nbytes = N_TOK * (2 * hc * D * 2 + 2 * D * 2 + (hc + hc * hc) * 4 + (2 * hc + hc * hc) * 4) \
+            + mix * hc * D * 4 + mix * 4 + 12 + D * 4
+        out[f"hc{hc}"] = {"call_us": round(us, 2), "algorithmic_bytes": nbytes,
+                          "gbs": round(nbytes / us / 1e3, 1), "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
+        del call
+        torch.cuda.empty_cache()
+    return {"workload": "fused sublayer boundary at other stream counts, B=1 T=4096, d=5120, sinkhorn_iters=20, "
+                        "RMSNorm, read with the freshly derived pre", **out}
+
+
 def stats(ms):
     return {"mean": float(np.mean(ms)), "median": float(np.median(ms)), "p10": float(np.percentile(ms, 10)),
             "p90": float(np.percentile(ms, 90))}
@@ -233,6 +272,7 @@ def main():
     ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--no-copy", action="store_true", help="skip the 1 GiB reference stream")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode block timing")
+    ap.add_argument("--no-other-hc", action="store_true", help="skip the hc = 2 and 8 boundary timing")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this benchmark runs on one GPU only.  The glue is per token and would shard over "
@@ -268,6 +308,7 @@ def main():
     achieved = head["algorithmic_bytes"] / (mean_ms * 1e-3) / 1e9
     traffic_bytes, traffic_src = traffic(args.mode)
     dec = None if args.no_decode else decode_block(dev)
+    ohc = None if args.no_other_hc else other_hc(dev)
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -308,6 +349,7 @@ def main():
         "modes": {k: rnd(v) for k, v in results.items()},
         "reference_stream_gbs": None if ref_gbs is None else round(ref_gbs, 1),
         "decode": dec,
+        "other_hc": ohc,
     }
     print(json.dumps(line), flush=True)
 
