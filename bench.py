@@ -12,8 +12,9 @@ the pages' Block.forward).  Inputs are seeded synthetic tensors
 (transformer_hyper_connection_amd.synth, workload "prefill"), resident in HBM
 before timing; several input/output buffer sets rotate.  Prints one JSON line.
 
-Beside the headline line: the decode block's glue (n=128, "decode") and the
-same boundary at hc = 2 and 8 ("other_hc"), each timed by events.
+Beside the headline line: the decode block's glue (n=128, "decode"), the
+same boundary at hc = 2 and 8 ("other_hc") and at n = 128 ... 32768
+("sweep"), each timed by events.
 
 Timing: W untimed warm-up steps; then K steps timed by the host clock between
 two device synchronisations (value, ms_per_step); then K more steps with
@@ -223,7 +224,7 @@ def other_hc(dev, hcs=(2, 8), reps=50):
     """The same boundary (write, fresh pre, RMSNorm; n=4096, d=5120) at hc = 2
     and 8, which libhc runs as four plainer launches (row write, matrix-core
     projection, finish, row read).  Mean microseconds per call by events over
-    reps calls, and the algorithmic bytes of a call."""
+    at least reps calls after a warm-up, and the algorithmic bytes of a call."""
     out = {}
     for hc in hcs:
         print(f"[bench] timing hc={hc}", file=sys.stderr, flush=True)
@@ -233,16 +234,7 @@ def other_hc(dev, hcs=(2, 8), reps=50):
                               comb_in=f32(s["comb_in"], dev), fn_packed=T.hc_fn_pack(f32(s["hc_fn"], dev), hc=hc),
                               hc_base=f32(s["hc_base"], dev), hc_scale=f32(s["hc_scale"], dev),
                               gamma=f32(s["gamma"], dev))
-        for _ in range(5):
-            call.run()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            call.run()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / reps * 1e3
+        us = timed_calls([call.run], min_reps=reps) * 1e3
         # per token: X, X' (hc*d bf16 each), delta, z (d bf16 each), post_in, comb_in, pre/post/comb out;
         # per call: hc_fn (fp32), base, scale, gamma
         nbytes = N_TOK * (2 * hc * D * 2 + 2 * D * 2 + (hc + hc * hc) * 4 + (2 * hc + hc * hc) * 4) \
@@ -253,6 +245,56 @@ def other_hc(dev, hcs=(2, 8), reps=50):
         torch.cuda.empty_cache()
     return {"workload": "fused sublayer boundary at other stream counts, B=1 T=4096, d=5120, sinkhorn_iters=20, "
                         "RMSNorm, read with the freshly derived pre", **out}
+
+
+def sweep(dev, ns=(128, 512, 4096, 32768), reps=50):
+    """The headline call (write, fresh pre, RMSNorm; hc=4, d=5120) at several
+    token counts: one GPU's share of a batch sharded over tokens.  n=32768 is
+    the channel-outlier stress workload, the others prefixes of the prefill
+    workload.  Event-timed over at least reps calls (after a warm-up) on two
+    rotating buffer sets."""
+    out = {}
+    for n in ns:
+        print(f"[bench] timing n={n}", file=sys.stderr, flush=True)
+        s = synth.boundary_inputs("stress") if n > N_TOK else synth.boundary_inputs("prefill", 0, n)
+        params = dict(fn_packed=T.hc_fn_pack(f32(s["hc_fn"], dev)), hc_base=f32(s["hc_base"], dev),
+                      hc_scale=f32(s["hc_scale"], dev), gamma=f32(s["gamma"], dev))
+        calls = []
+        for i in range(2):
+            ins = {k: (bf(s[k], dev) if k in ("x", "delta") else f32(s[k], dev)) for k in ("x", "delta", "post_in",
+                                                                                          "comb_in")}
+            calls.append((ins, T.BoundaryCall(ins["x"], delta=ins["delta"], post_in=ins["post_in"],
+                                              comb_in=ins["comb_in"], **params)))
+        del s
+        us = timed_calls([c.run for _, c in calls], min_reps=reps) * 1e3
+        nbytes = algorithmic_bytes(n, "fresh")
+        out[str(n)] = {"call_us": round(us, 2), "tokens_per_s": round(n / us * 1e6, 1),
+                       "gbs": round(nbytes / us / 1e3, 1), "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
+        del calls
+        torch.cuda.empty_cache()
+    return {"workload": "fused sublayer boundary, hc=4, d=5120, fresh pre, RMSNorm, at n tokens "
+                        "(n=32768: channel-outlier stress inputs)", **out}
+
+
+def timed_calls(fns, min_s=0.25, min_reps=50):
+    """Mean milliseconds per call of the callables fns (run in rotation),
+    event-timed on the current stream.  Warms up for at least min_s (clocks
+    settle), then times at least min_reps calls and at least min_s."""
+    k, t0 = 0, time.perf_counter()
+    while k < 20 or time.perf_counter() - t0 < min_s:
+        for _ in range(10):
+            fns[k % len(fns)]()
+            k += 1
+        torch.cuda.synchronize()
+    est = (time.perf_counter() - t0) / k
+    reps = max(min_reps, int(min_s / max(est, 1e-6)))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fns[i % len(fns)]()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 def stats(ms):
@@ -273,6 +315,7 @@ def main():
     ap.add_argument("--no-copy", action="store_true", help="skip the 1 GiB reference stream")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode block timing")
     ap.add_argument("--no-other-hc", action="store_true", help="skip the hc = 2 and 8 boundary timing")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the token-count sweep")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this benchmark runs on one GPU only.  The glue is per token and would shard over "
@@ -309,6 +352,7 @@ def main():
     traffic_bytes, traffic_src = traffic(args.mode)
     dec = None if args.no_decode else decode_block(dev)
     ohc = None if args.no_other_hc else other_hc(dev)
+    swp = None if args.no_sweep else sweep(dev)
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -350,6 +394,7 @@ def main():
         "reference_stream_gbs": None if ref_gbs is None else round(ref_gbs, 1),
         "decode": dec,
         "other_hc": ohc,
+        "sweep": swp,
     }
     print(json.dumps(line), flush=True)
 
