@@ -16,10 +16,13 @@ Beside the headline line: the decode block's glue (n=128, "decode"), the
 same boundary at hc = 2 and 8 ("other_hc") and at n = 128 ... 32768
 ("sweep"), each timed by events.
 
-Timing: W untimed warm-up steps; then K steps timed by the host clock between
-two device synchronisations (value, ms_per_step); then K more steps with
-events on the launch stream around each kernel (the roofline: algorithmic
-bytes of a call / mean event time of a call, and each kernel's share).
+Timing: after half a second of plain streaming (GPU clocks settle; the first
+~20 ms after idle run several percent slower), W untimed warm-up steps; then
+K steps timed by the host clock between two device synchronisations (value,
+ms_per_step); then K more steps between two events on the launch stream (the
+roofline: algorithmic bytes of a call / mean event time of a call); then K
+more with events also between the two kernels of each call (each kernel's
+share; those events add a few microseconds per call).
 """
 from __future__ import annotations
 
@@ -95,7 +98,16 @@ def time_mode(mode, sets, params, steps, warmup):
     host_enqueue = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # the same steps again, each kernel bracketed by events on the launch stream
+    # the same steps again between two events on the launch stream: the mean call
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        calls[i % len(calls)].run(sid)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    mean_call = e0.elapsed_time(e1) / steps
+    # and once more with an event before, between and after the two kernels of
+    # each call: their split (the events themselves add a few microseconds)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for i in range(steps):
         c = calls[i % len(calls)]
@@ -108,8 +120,21 @@ def time_mode(mode, sets, params, steps, warmup):
     k1 = [e[0].elapsed_time(e[1]) for e in ev]
     k2 = [e[1].elapsed_time(e[2]) for e in ev]
     call = [e[0].elapsed_time(e[2]) for e in ev]
-    return {"wall_s": wall, "host_enqueue_us_per_call": host_enqueue / steps * 1e6, "call_ms": call,
-            "stream_kernel_ms": k1, "finish_kernel_ms": k2}
+    return {"wall_s": wall, "host_enqueue_us_per_call": host_enqueue / steps * 1e6, "mean_call_ms": mean_call,
+            "call_ms": call, "stream_kernel_ms": k1, "finish_kernel_ms": k2}
+
+
+def settle_clocks(dev, seconds=0.5):
+    """Keep the GPU streaming for a moment before anything is timed: the first
+    ~20 ms of work after idle run several percent slower."""
+    a = torch.empty(1 << 27, dtype=torch.bfloat16, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            torch.mul(a, 1, out=b)
+        torch.cuda.synchronize()
+    del a, b
 
 
 def reference_stream(dev, nbytes=1 << 30, reps=10):
@@ -306,7 +331,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--mode", choices=["fresh", "lag"], default="fresh")
     ap.add_argument("--modes", default="fresh,lag", help="read modes to time (the headline mode is always timed)")
     ap.add_argument("--sets", type=int, default=4, help="rotating input/output buffer sets")
@@ -329,6 +354,7 @@ def main():
                   hc_scale=f32(s["hc_scale"], dev), gamma=f32(s["gamma"], dev), iters=20, hc_eps=1e-6,
                   norm_eps=1e-6, rms_eps=1e-6)
     torch.cuda.synchronize()
+    settle_clocks(dev)
 
     results = {}
     modes = [args.mode] + [m for m in args.modes.split(",") if m and m != args.mode]
@@ -340,14 +366,15 @@ def main():
         results[mode] = {
             "wall_s": r["wall_s"], "ms_per_step": r["wall_s"] / args.steps * 1e3,
             "tokens_per_s": N_TOK * args.steps / r["wall_s"], "algorithmic_bytes": nbytes,
-            "call_ms": call, "stream_kernel_ms": stats(r["stream_kernel_ms"]),
+            "mean_call_ms": r["mean_call_ms"],
+            "split_call_ms": call, "stream_kernel_ms": stats(r["stream_kernel_ms"]),
             "finish_kernel_ms": stats(r["finish_kernel_ms"]),
-            "gbs_at_mean_call": nbytes / (call["mean"] * 1e-3) / 1e9,
+            "gbs_at_mean_call": nbytes / (r["mean_call_ms"] * 1e-3) / 1e9,
             "host_enqueue_us_per_call": r["host_enqueue_us_per_call"],
         }
     ref_gbs = None if args.no_copy else reference_stream(dev)
     head = results[args.mode]
-    mean_ms = head["call_ms"]["mean"]
+    mean_ms = head["mean_call_ms"]
     achieved = head["algorithmic_bytes"] / (mean_ms * 1e-3) / 1e9
     traffic_bytes, traffic_src = traffic(args.mode)
     dec = None if args.no_decode else decode_block(dev)

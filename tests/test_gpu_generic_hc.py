@@ -209,3 +209,19 @@ def test_hc4_workspace_survives_other_hc_calls():
     for k, v in first.items():
         assert torch.equal(again[k], v), k
     assert int(ws[4160:4164].cpu().numpy().view(np.uint32)[0]) == 0
+
+
+@pytest.mark.parametrize("hc,n,d,norm", [(8, 40, 10240, True), (8, 19, 32768, False), (2, 3, 32768, True)])
+def test_boundary_widest_rows(hc, n, d, norm):
+    """The widest rows: d = 10240 with the RMSNorm (its limit) and d = 32768
+    (the library's limit; hc = 2 with the RMSNorm is rejected above 10240)."""
+    if norm and d > 10240:
+        with pytest.raises(H.HCError):
+            H.hc_boundary(bf16_dev(np.zeros((n, hc, d), np.uint16)), gamma=f32_dev(np.ones(d, np.float32)),
+                          **_dev_params(_inputs(hc, 1, d)))
+        return
+    say(f"[hc={hc}] widest rows n={n} d={d} norm={norm}")
+    s, kw, dev = _boundary(hc, n, d, True, norm, True)
+    ref = O.boundary(**kw)
+    got = H.hc_boundary(bf16_dev(s["x"]), want_mixes=True, **dev)
+    _check_boundary(ref, got, s, True, norm)
