@@ -264,7 +264,9 @@ __global__ void __launch_bounds__(256) gpack_kernel(const float* __restrict__ fn
   out[idx] = u32x4{w[0], w[1], w[2], w[3]};
 }
 
-constexpr int kGTok = 128;     // tokens per workgroup: 4 waves x 2 row tiles of 16
+constexpr int kGWaves = 4;                 // waves per workgroup
+constexpr int kGThreads = kGWaves * 64;
+constexpr int kGTok = kGWaves * 32;        // tokens per workgroup: 2 row tiles of 16 per wave
 constexpr int kGChunk = 64;    // features per pipeline chunk (two 32-feature steps)
 constexpr int kGPD = 2;        // chunks of stream loads in flight ahead of the matrix work
 
@@ -277,16 +279,16 @@ struct GMixArgs {
   int d, S, Fs;        // slices of the flattened feature range, Fs = hc*d/S features each
 };
 
-// One workgroup: 128 tokens x one feature slice.  Per 64-feature chunk the
-// weight tiles are staged through registers into a double-buffered LDS area
-// shared by the four waves; each wave streams the A tiles of its 32 tokens
+// One workgroup: 32 tokens per wave x one feature slice.  Per 64-feature chunk
+// the weight tiles are staged through registers into a double-buffered LDS
+// area shared by the waves; each wave streams the A tiles of its 32 tokens
 // straight from memory, kGPD chunks ahead.
 template <int HC>
-__global__ void __launch_bounds__(256, 2) gmix_kernel(const GMixArgs a) {
+__global__ void __launch_bounds__(kGThreads, 2) gmix_kernel(const GMixArgs a) {
   using G = GShape<HC>;
   constexpr int NCT = G::NCT, RT = G::RT;
   constexpr int BREC = 2 * NCT * 64;            // 16-byte weight records per chunk
-  constexpr int BPT = (BREC + 255) / 256;
+  constexpr int BPT = (BREC + kGThreads - 1) / kGThreads;
   __shared__ u32x4 w_lds[2][2 * NCT * 64];      // [buffer][step][tile][lane]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // consecutive workgroups go to different XCDs: slice-major so the workgroups
@@ -315,14 +317,14 @@ __global__ void __launch_bounds__(256, 2) gmix_kernel(const GMixArgs a) {
     const u32x4* src = a.fn + (size_t)((c0 + ch * kGChunk) / 32) * NCT * 64;
 #pragma unroll
     for (int r = 0; r < BPT; ++r) {
-      const int idx = threadIdx.x + 256 * r;
+      const int idx = threadIdx.x + kGThreads * r;
       if (idx < BREC) Bs[r] = src[idx];
     }
   };
   auto store_b = [&](int buf, const u32x4 (&Bs)[BPT]) {
 #pragma unroll
     for (int r = 0; r < BPT; ++r) {
-      const int idx = threadIdx.x + 256 * r;
+      const int idx = threadIdx.x + kGThreads * r;
       if (idx < BREC) w_lds[buf][idx] = Bs[r];
     }
   };
@@ -2472,7 +2474,7 @@ int launch_mixes_generic(int hc, const hc_bf16* x, int xtok, int xstr, const voi
   const dim3 mgrid((unsigned)((n + kGTok - 1) / kGTok * m.S));
   hipError_t e = hipLaunchKernel(hc == 2 ? reinterpret_cast<const void*>(&gmix_kernel<2>)
                                          : reinterpret_cast<const void*>(&gmix_kernel<8>),
-                                 mgrid, dim3(256), margs, 0, st);
+                                 mgrid, dim3(kGThreads), margs, 0, st);
   int rc = launched(e, what);
   if (rc) return rc;
   f.rec = m.rec; f.n = n; f.S = m.S; f.K = hc * d;
