@@ -22,10 +22,11 @@
  *   - bf16 tensors are passed as raw bit patterns (hc_bf16) and must be 16-byte
  *     aligned; float tensors must be 16-byte aligned.
  *   - n = number of tokens (batch x positions, flattened).  hc is 2, 4 or 8;
- *     hc = 4 (the pages' setting) runs the matrix-core kernels, hc = 2 and 8
- *     a plainer schedule of separate launches (fp32 multiply-adds for the
- *     projection, weights unpacked).  d must be a positive multiple of 64
- *     and at most 32768 (at most 10240 where the read row is RMS-normalised).
+ *     hc = 4 (the pages' setting) runs the fused kernels, hc = 2 and 8 a
+ *     plainer schedule of separate launches (the write, the projection, the
+ *     split, the read), with the same arithmetic.  d must be a positive
+ *     multiple of 64 and at most 32768 (at most 10240 where the read row is
+ *     RMS-normalised).
  *   - stream is a hipStream_t (NULL = the null stream).  Calls enqueue work on
  *     it and return without synchronising; the current HIP device of the
  *     calling thread is used.  Calls on distinct streams may run concurrently
@@ -75,9 +76,8 @@ const char* hc_last_error(void);
  * The compute entry points take it pre-packed: each fp32 weight is split into
  * three bf16 terms hi + mid + lo (each the nearest bf16 to what the previous
  * terms leave), which together hold the fp32 value to about 2^-26 relative,
- * laid out in the tile order of the matrix-core kernels (hc = 4).  For hc
- * = 2 and 8 the packed weight is an fp32 copy of hc_fn.  Pack once per
- * parameter set.
+ * laid out in the tile order of the matrix-core kernels (one order for hc =
+ * 4, another for hc = 2 and 8).  Pack once per parameter set.
  * ------------------------------------------------------------------------- */
 
 /* Bytes of the packed weight for (hc, d); 0 if (hc, d) is not supported. */
@@ -97,10 +97,9 @@ int hc_fn_pack(const float* hc_fn, int hc, int d, void* fn_packed, void* stream)
  * workspace of the size asked for some (n, d) serves every call that needs no
  * more).  Calls that may run concurrently (different streams) need different
  * workspaces; calls on one stream can share one, also when captured in a
- * graph and replayed.  For hc = 2 and 8 the workspace only holds the mixes
- * when the caller passes no mixes output (they are then needed between two
- * launches); it is placed after the regions an hc = 4 call of the same d
- * keeps, so one workspace may serve calls of every hc.
+ * graph and replayed.  For hc = 2 and 8 the per-slice sums are placed after
+ * the regions an hc = 4 call of the same d keeps, so one workspace may serve
+ * calls of every hc.
  *
  * Decode schedule (hc = 4).  For n <= 128 with d a multiple of 256, hc_mixes, and
  * hc_boundary with a given pre_in and no gamma (the pages' data flow at

@@ -11,7 +11,8 @@ token range can be regenerated without drawing the rest.  Draws are float64,
 rounded to float32 (nearest-even) and, for bf16 tensors, to bf16
 (nearest-even); bf16 tensors are returned as uint16 bit patterns.
 
-Workloads (n = tokens, hc = 4 streams, d = 5120, 24 mix numbers):
+Workloads (n = tokens, hc = 4 streams, d = 5120, 24 mix numbers; boundary_inputs
+also draws the same distributions at hc = 2 or 8):
   "step"    n=32     one sublayer step (mixes, read, write)
   "decode"  n=128    one block's glue at decode, two parameter sets
   "prefill" n=4096   fused sublayer boundary
