@@ -225,3 +225,57 @@ def test_boundary_widest_rows(hc, n, d, norm):
     ref = O.boundary(**kw)
     got = H.hc_boundary(bf16_dev(s["x"]), want_mixes=True, **dev)
     _check_boundary(ref, got, s, True, norm)
+
+
+@pytest.mark.parametrize("hc", HCS)
+def test_graph_replay_and_determinism(hc):
+    """The four-launch boundary captured in a graph and replayed on changing
+    inputs (eager work and synchronisations between the replays): every replay
+    equals the eager call on the same inputs bit for bit, and two eager calls
+    agree bit for bit."""
+    say(f"[hc={hc}] graph replay")
+    s0 = _inputs(hc, 300, 1024)
+    s1 = _inputs(hc, 300, 1024, t0=300)
+    dev = _dev_params(s0)
+    X, D = bf16_dev(s0["x"]), bf16_dev(s0["delta"])
+    P, C, G = f32_dev(s0["post_in"]), f32_dev(s0["comb_in"]), f32_dev(s0["gamma"])
+    call = H.BoundaryCall(X, delta=D, post_in=P, comb_in=C, gamma=G, want_mixes=True, want_mean=True, **dev)
+    o = call.outputs
+
+    def load(s):
+        X.copy_(bf16_dev(s["x"]))
+        D.copy_(bf16_dev(s["delta"]))
+        P.copy_(f32_dev(s["post_in"]))
+        C.copy_(f32_dev(s["comb_in"]))
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return {k: (host_bits(v) if v.dtype == torch.bfloat16 else host_f32(v).view(np.uint32))
+                for k, v in o.items() if isinstance(v, torch.Tensor) and k != "workspace"}
+
+    eager = []
+    for s in (s0, s1):
+        load(s)
+        call.run()
+        first = snapshot()
+        call.run()
+        again = snapshot()
+        for k in first:
+            assert np.array_equal(first[k], again[k]), f"{k}: two eager calls differ"
+        eager.append(first)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call.run()
+    for rep, i in enumerate((0, 1, 1, 0)):
+        load((s0, s1)[i])
+        torch.cuda.synchronize()
+        g.replay()
+        got = snapshot()
+        for k in got:
+            assert np.array_equal(got[k], eager[i][k]), f"replay {rep}: {k} differs from the eager call"
