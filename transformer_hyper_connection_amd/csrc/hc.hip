@@ -1082,13 +1082,20 @@ __global__ void __launch_bounds__(kFinThreads) finish_kernel(const FinishArgs a)
   }
   __syncthreads();
 
-  // ---- derive: 4 lanes per token, lane j holds comb row j
-  if (threadIdx.x < kTT * kHC) {
-    const int tm = threadIdx.x >> 2, j = threadIdx.x & 3;
+  // ---- derive: 4 lanes per token, lane j of token dtm holds stream j.  The
+  // read needs only pre and the RMSNorm factor of every token; the Sinkhorn
+  // comb is needed only for the tokens this workgroup owns (writes) and runs
+  // later, while the first reads of X' are in flight.
+  const bool dthr = threadIdx.x < kTT * kHC;
+  const int dtm = (threadIdx.x >> 2) & (kTT - 1), dj = threadIdx.x & 3;
+  const bool own = dthr && dtm < valid && dtm % a.S2 == sl2;
+  float d_pre = 0.f, d_post = 0.f, d_rx = 0.f;
+  if (dthr) {
+    const int tm = dtm, j = dj;
     const int64_t t = t0 + tm;
-    const bool own = tm < valid && tm % a.S2 == sl2;
     const float* rec = tot[tm];
     const float rx = 1.0f / sqrtf(rec[kMix] / (float)(kHC * d) + a.norm_eps);
+    d_rx = rx;
     if (own && a.mixes_out) {
       const f32x4 v = *reinterpret_cast<const f32x4*>(rec + 4 * j);
       *reinterpret_cast<f32x4*>(a.mixes_out + t * kMix + 4 * j) = f32x4{v[0] * rx, v[1] * rx, v[2] * rx, v[3] * rx};
@@ -1099,42 +1106,9 @@ __global__ void __launch_bounds__(kFinThreads) finish_kernel(const FinishArgs a)
       }
     }
     if (a.pre_out) {
-      const float s0 = a.hc_scale[0], s1 = a.hc_scale[1], s2 = a.hc_scale[2];
-      const float pre = sigmoidf_((rec[j] * rx) * s0 + a.hc_base[j]) + a.hc_eps;
-      const float post = 2.0f * sigmoidf_((rec[kHC + j] * rx) * s1 + a.hc_base[kHC + j]);
-      float A[kHC];
-      float mxr = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < kHC; ++k) {
-        const int q = 2 * kHC + j * kHC + k;
-        A[k] = (rec[q] * rx) * s2 + a.hc_base[q];
-        mxr = fmaxf(mxr, A[k]);
-      }
-      float rsum = 0.f;
-#pragma unroll
-      for (int k = 0; k < kHC; ++k) {
-        A[k] = expf(A[k] - mxr);
-        rsum = rsum + A[k];
-      }
-      const float rinv = __builtin_amdgcn_rcpf(rsum);
-#pragma unroll
-      for (int k = 0; k < kHC; ++k) A[k] = A[k] * rinv + a.hc_eps;
-      auto col_norm = [&]() {
-#pragma unroll
-        for (int k = 0; k < kHC; ++k) A[k] = A[k] * __builtin_amdgcn_rcpf(quad_sum(A[k]) + a.hc_eps);
-      };
-      col_norm();
-      for (int it = 1; it < a.iters; ++it) {
-        const float inv = __builtin_amdgcn_rcpf(((A[0] + A[1]) + A[2]) + A[3] + a.hc_eps);
-#pragma unroll
-        for (int k = 0; k < kHC; ++k) A[k] = A[k] * inv;
-        col_norm();
-      }
-      if (own) {
-        a.pre_out[t * kHC + j] = pre;
-        a.post_out[t * kHC + j] = post;
-        *reinterpret_cast<f32x4*>(a.comb_out + t * kHC * kHC + j * kHC) = f32x4{A[0], A[1], A[2], A[3]};
-      }
+      const float pre = sigmoidf_((rec[j] * rx) * a.hc_scale[0] + a.hc_base[j]) + a.hc_eps;
+      d_pre = pre;
+      d_post = 2.0f * sigmoidf_((rec[kHC + j] * rx) * a.hc_scale[1] + a.hc_base[kHC + j]);
       if constexpr (RM == kFreshPre) {
         s_pre[tm][j] = pre;
         if constexpr (NORM) {
@@ -1157,6 +1131,46 @@ __global__ void __launch_bounds__(kFinThreads) finish_kernel(const FinishArgs a)
       if (j == 0) s_r[tm] = 1.0f / sqrtf(rec[kMix + 1] / (float)d + a.rms_eps);
     }
   }
+  // the owned tokens' comb (whole quads take part: ownership is per token)
+  auto sinkhorn_owned = [&]() {
+    if (!(own && a.pre_out)) return;
+    const int tm = dtm, j = dj;
+    const int64_t t = t0 + tm;
+    const float* rec = tot[tm];
+    const float s2 = a.hc_scale[2];
+    float A[kHC];
+    float mxr = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kHC; ++k) {
+      const int q = 2 * kHC + j * kHC + k;
+      A[k] = (rec[q] * d_rx) * s2 + a.hc_base[q];
+      mxr = fmaxf(mxr, A[k]);
+    }
+    float rsum = 0.f;
+#pragma unroll
+    for (int k = 0; k < kHC; ++k) {
+      A[k] = expf(A[k] - mxr);
+      rsum = rsum + A[k];
+    }
+    const float rinv = __builtin_amdgcn_rcpf(rsum);
+#pragma unroll
+    for (int k = 0; k < kHC; ++k) A[k] = A[k] * rinv + a.hc_eps;
+    auto col_norm = [&]() {
+#pragma unroll
+      for (int k = 0; k < kHC; ++k) A[k] = A[k] * __builtin_amdgcn_rcpf(quad_sum(A[k]) + a.hc_eps);
+    };
+    col_norm();
+    for (int it = 1; it < a.iters; ++it) {
+      const float inv = __builtin_amdgcn_rcpf(((A[0] + A[1]) + A[2]) + A[3] + a.hc_eps);
+#pragma unroll
+      for (int k = 0; k < kHC; ++k) A[k] = A[k] * inv;
+      col_norm();
+    }
+    a.pre_out[t * kHC + j] = d_pre;
+    a.post_out[t * kHC + j] = d_post;
+    *reinterpret_cast<f32x4*>(a.comb_out + t * kHC * kHC + j * kHC) = f32x4{A[0], A[1], A[2], A[3]};
+  };
+  if constexpr (!(RM == kFreshPre || (RM == kGivenPre && NORM))) sinkhorn_owned();
 
   // ---- this workgroup's slice of the read row
   if constexpr (RM == kFreshPre || (RM == kGivenPre && NORM)) {
@@ -1190,6 +1204,7 @@ __global__ void __launch_bounds__(kFinThreads) finish_kernel(const FinishArgs a)
           for (int k = 0; k < NL; ++k) ld[u][k] = ld_stream(reinterpret_cast<const u32x4*>(src + (k * sstr + f)));
         }
       }
+      if (cb == nch) sinkhorn_owned();   // while the first batch is in flight
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = cb - 1 - u;
