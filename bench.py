@@ -14,7 +14,8 @@ before timing; several input/output buffer sets rotate.  Prints one JSON line.
 
 Beside the headline line: the decode block's glue (n=128, "decode"), the
 same boundary at hc = 2 and 8 ("other_hc") and at n = 128 ... 32768
-("sweep"), each timed by events.
+("sweep"), and the calls at the stand-in stack's two ends ("stack_ends"),
+each timed by events.
 
 Timing: after half a second of plain streaming (GPU clocks settle; the first
 ~20 ms after idle run several percent slower), W untimed warm-up steps; then
@@ -301,6 +302,37 @@ def sweep(dev, ns=(128, 512, 4096, 32768), reps=50):
                         "(n=32768: channel-outlier stress inputs)", **out}
 
 
+def stack_ends(dev, reps=50):
+    """The calls at the two ends of the stand-in stack (n = 8192, hc = 4,
+    d = 5120): the entry (x the embedding [n, d], read by all four streams;
+    first pre 0.25 given; mixes derived; the MTP tap of the block input), a
+    boundary with the tap, and the exit (last write, read with the last pre,
+    RMSNorm with eps 1e-20; no mixes).  Mean microseconds per call by events."""
+    st = synth.stack_inputs(2)
+    n = st["h"].shape[0]
+    (fn, base, scale), (fn2, base2, scale2) = st["params"]
+    h = bf(st["h"], dev)
+    g = f32(st["gammas"][0], dev)
+    pre0 = torch.full((n, HC), 0.25, dtype=torch.float32, device=dev)
+    entry = T.BoundaryCall(h, x_expanded=True, pre_in=pre0, fn_packed=T.hc_fn_pack(f32(fn, dev)),
+                           hc_base=f32(base, dev), hc_scale=f32(scale, dev), gamma=g, want_mean=True)
+    e = entry.outputs
+    x = h.view(n, 1, D).expand(n, HC, D).contiguous()
+    delta = e["y"].clone()                                   # a stand-in sublayer output
+    bnd = T.BoundaryCall(x, delta=delta, post_in=e["post"], comb_in=e["comb"], pre_in=e["pre"],
+                         fn_packed=T.hc_fn_pack(f32(fn2, dev)), hc_base=f32(base2, dev),
+                         hc_scale=f32(scale2, dev), gamma=g, want_mean=True)
+    ex = T.BoundaryCall(x, delta=delta, post_in=e["post"], comb_in=e["comb"], pre_in=e["pre"],
+                        gamma=f32(st["gamma_final"], dev), rms_eps=1e-20)
+    out = {}
+    for name, c in (("entry_us", entry), ("boundary_with_tap_us", bnd), ("exit_us", ex)):
+        print(f"[bench] timing the stack's {name[:-3]}", file=sys.stderr, flush=True)
+        out[name] = round(timed_calls([c.run], min_reps=reps) * 1e3, 2)
+    return {"workload": "stand-in stack ends, B=2 T=4096 (n=8192), hc=4, d=5120: expanded entry with the "
+                        "MTP tap; a given-pre boundary with RMSNorm and the tap; the exit (no mixes, "
+                        "RMSNorm eps 1e-20)", "tokens": n, **out}
+
+
 def timed_calls(fns, min_s=0.25, min_reps=50):
     """Mean milliseconds per call of the callables fns (run in rotation),
     event-timed on the current stream.  Warms up for at least min_s (clocks
@@ -341,6 +373,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode block timing")
     ap.add_argument("--no-other-hc", action="store_true", help="skip the hc = 2 and 8 boundary timing")
     ap.add_argument("--no-sweep", action="store_true", help="skip the token-count sweep")
+    ap.add_argument("--no-stack-ends", action="store_true", help="skip the stack entry / exit timing")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this benchmark runs on one GPU only.  The glue is per token and would shard over "
@@ -380,6 +413,7 @@ def main():
     dec = None if args.no_decode else decode_block(dev)
     ohc = None if args.no_other_hc else other_hc(dev)
     swp = None if args.no_sweep else sweep(dev)
+    ends = None if args.no_stack_ends else stack_ends(dev)
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -422,6 +456,7 @@ def main():
         "decode": dec,
         "other_hc": ohc,
         "sweep": swp,
+        "stack_ends": ends,
     }
     print(json.dumps(line), flush=True)
 
