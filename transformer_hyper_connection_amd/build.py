@@ -29,6 +29,8 @@ HIPCC_FLAGS = [
     "-ffp-contract=off",
     # no packed-fp32 instructions are generated
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+    "-Wextra",
     "-Wno-unused-command-line-argument",
 ]
 

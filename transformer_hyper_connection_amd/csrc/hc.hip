@@ -76,10 +76,6 @@ __device__ __forceinline__ float dot2_bf16(u32 a, u32 b, float c) {
 __device__ __forceinline__ u32x4 ld_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32 w0, u32 w1, u32 w2, u32 w3) {
-  u32x4 v = {w0, w1, w2, w3};
-  return __builtin_bit_cast(bf16x8, v);
-}
 
 // ------------------------------------------------------------- split / Sinkhorn
 // One token: "Reading weights" split/Sinkhorn kernel panel and reading-weight
@@ -1641,13 +1637,10 @@ __global__ void __launch_bounds__(kFThreads, 1) fused_kernel(const FusedArgs a) 
       for (int i = lt; i < kCin; i += kFMW * 64) cin[0][i / (kCin / kFT)][i % (kCin / kFT)] = cin_val(i0, i);
     }
     u32x4 B[kFPre][kNT];
-    {
-      const Item i0 = item_of(0);
 #pragma unroll
-      for (int j = 0; j < kFPre; ++j)
+    for (int j = 0; j < kFPre; ++j)
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) B[j][nt] = wt(j, nt);
-    }
+      for (int nt = 0; nt < kNT; ++nt) B[j][nt] = wt(j, nt);
     bool dead = false;
     __syncthreads();                                     // P
     for (int k = 0; k < K; ++k) {
@@ -1818,13 +1811,10 @@ __global__ void __launch_bounds__(kFThreads, 1) fused_kernel(const FusedArgs a) 
       if constexpr (NORM) {
         if (lt < kFF / 4) *reinterpret_cast<f32x4*>(&gam[(k - 1) & 1][4 * lt]) = gv;
       }
-      {
-        const Item inext = item_of(k);
 #pragma unroll
-        for (int j = 0; j < kFPre; ++j)
+      for (int j = 0; j < kFPre; ++j)
 #pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) B[j][nt] = wt(j, nt);
-      }
+        for (int nt = 0; nt < kNT; ++nt) B[j][nt] = wt(j, nt);
       __syncthreads();                                   // X(k)
     }
   }
@@ -2145,7 +2135,6 @@ int fail(int code, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-constexpr int mix_of(int hc) { return (2 + hc) * hc; }
 bool hc_known(int hc) { return hc == 2 || hc == kHC || hc == 8; }
 
 int check_hd(int hc, int d) {
