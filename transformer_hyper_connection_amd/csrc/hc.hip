@@ -1896,9 +1896,14 @@ __global__ void __launch_bounds__(kDThreads) decode_kernel(const DecArgs a) {
   __shared__ float red[kDThreads / 64][kDT][32];       // per-wave dots
   __shared__ float ssq[4][kDT];                        // sum x'^2 per chunk
   __shared__ float tot[kDT][kDRec];                    // the tile's summed records (last slice)
+  __shared__ float s_cf[kMix + 3];                     // hc_base, hc_scale (read by the last slice)
   __shared__ u32 s_tag, s_last;
 
   const int S = a.S, d = a.d;
+  // the split's parameters, requested now so that the last slice's derive does
+  // not wait for them
+  if (a.pre_out && threadIdx.x < kMix + 3)
+    s_cf[threadIdx.x] = threadIdx.x < kMix ? a.hc_base[threadIdx.x] : a.hc_scale[threadIdx.x - kMix];
   // XCD-aware numbering: consecutive workgroups land on different XCDs, so
   // they are renumbered XCD by XCD and taken slice-major, the workgroups of an
   // XCD sharing few slices (their weight tiles stay in that XCD's L2)
@@ -2082,15 +2087,15 @@ __global__ void __launch_bounds__(kDThreads) decode_kernel(const DecArgs a) {
       for (int i = 0; i < kMix / kHC; ++i) a.mixes_out[t * kMix + i * kHC + j] = rec[i * kHC + j] * rx;
     }
     if (a.pre_out) {
-      const float s0 = a.hc_scale[0], s1 = a.hc_scale[1], s2 = a.hc_scale[2];
-      const float pre = sigmoidf_((rec[j] * rx) * s0 + a.hc_base[j]) + a.hc_eps;
-      const float post = 2.0f * sigmoidf_((rec[kHC + j] * rx) * s1 + a.hc_base[kHC + j]);
+      const float s0 = s_cf[kMix], s1 = s_cf[kMix + 1], s2 = s_cf[kMix + 2];
+      const float pre = sigmoidf_((rec[j] * rx) * s0 + s_cf[j]) + a.hc_eps;
+      const float post = 2.0f * sigmoidf_((rec[kHC + j] * rx) * s1 + s_cf[kHC + j]);
       float A[kHC];
       float mxr = -INFINITY;
 #pragma unroll
       for (int k = 0; k < kHC; ++k) {
         const int q = 2 * kHC + j * kHC + k;
-        A[k] = (rec[q] * rx) * s2 + a.hc_base[q];
+        A[k] = (rec[q] * rx) * s2 + s_cf[q];
         mxr = fmaxf(mxr, A[k]);
       }
       float rsum = 0.f;
