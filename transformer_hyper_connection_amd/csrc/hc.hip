@@ -264,7 +264,6 @@ constexpr int kGWaves = 4;                 // waves per workgroup
 constexpr int kGThreads = kGWaves * 64;
 constexpr int kGTok = kGWaves * 32;        // tokens per workgroup: 2 row tiles of 16 per wave
 constexpr int kGChunk = 64;    // features per pipeline chunk (two 32-feature steps)
-constexpr int kGPD = 2;        // chunks of stream loads in flight ahead of the matrix work
 
 struct GMixArgs {
   const hc_bf16* x;
@@ -278,7 +277,7 @@ struct GMixArgs {
 // One workgroup: 32 tokens per wave x one feature slice.  Per 64-feature chunk
 // the weight tiles are staged through registers into a double-buffered LDS
 // area shared by the waves; each wave streams the A tiles of its 32 tokens
-// straight from memory, kGPD chunks ahead.
+// straight from memory, two chunks ahead.
 template <int HC>
 __global__ void __launch_bounds__(kGThreads, 2) gmix_kernel(const GMixArgs a) {
   using G = GShape<HC>;
@@ -331,20 +330,16 @@ __global__ void __launch_bounds__(kGThreads, 2) gmix_kernel(const GMixArgs a) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) acc[ti][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   float ss[2] = {0.f, 0.f};
-  // the weight loads of a chunk are issued before the stream loads that run
-  // kGPD chunks ahead, so that waiting for the former (the load counter is in
-  // order) does not wait for the latter
-  u32x4 Aq[kGPD + 1][2][2], Bs[BPT];
-  load_b(0, Bs);
-#pragma unroll
-  for (int p = 0; p < kGPD; ++p)
-    if (p < nch) load_a(p, Aq[p]);
-  store_b(0, Bs);
-  __syncthreads();
-  for (int ch = 0; ch < nch; ++ch) {
+  // The stream tiles run two chunks ahead in three register sets used in
+  // rotation by a loop unrolled three times (a copy between sets would wait for
+  // the loads in flight).  A chunk's weight loads are issued before its stream
+  // loads, so that waiting for the former (the load counter is in order) does
+  // not wait for the latter.
+  u32x4 A0[2][2], A1[2][2], A2[2][2], Bs[BPT];
+  auto step = [&](int ch, const u32x4 (&Ac)[2][2], u32x4 (&An)[2][2]) {
     const bool more = ch + 1 < nch;
     if (more) load_b(ch + 1, Bs);
-    if (ch + kGPD < nch) load_a(ch + kGPD, Aq[kGPD]);
+    if (ch + 2 < nch) load_a(ch + 2, An);
     const u32x4* wb = w_lds[ch & 1];
 #pragma unroll
     for (int st = 0; st < 2; ++st)
@@ -353,7 +348,7 @@ __global__ void __launch_bounds__(kGThreads, 2) gmix_kernel(const GMixArgs a) {
         const bf16x8 b = __builtin_bit_cast(bf16x8, wb[(st * NCT + ct) * 64 + lane]);
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti)
-          acc[ti][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Aq[0][ti][st]), b,
+          acc[ti][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Ac[ti][st]), b,
                                                                 acc[ti][ct], 0, 0, 0);
       }
 #pragma unroll
@@ -361,15 +356,19 @@ __global__ void __launch_bounds__(kGThreads, 2) gmix_kernel(const GMixArgs a) {
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ss[ti] = dot2_bf16(Aq[0][ti][st][e], Aq[0][ti][st][e], ss[ti]);
+        for (int e = 0; e < 4; ++e) ss[ti] = dot2_bf16(Ac[ti][st][e], Ac[ti][st][e], ss[ti]);
     if (more) store_b((ch + 1) & 1, Bs);
     __syncthreads();                              // next weights in place; this chunk's reads done
-#pragma unroll
-    for (int p = 0; p < kGPD; ++p)
-#pragma unroll
-      for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-        for (int st = 0; st < 2; ++st) Aq[p][ti][st] = Aq[p + 1][ti][st];
+  };
+  load_b(0, Bs);
+  load_a(0, A0);
+  if (nch > 1) load_a(1, A1);
+  store_b(0, Bs);
+  __syncthreads();
+  for (int ch = 0; ch < nch; ch += 3) {
+    step(ch, A0, A2);
+    if (ch + 1 < nch) step(ch + 1, A1, A0);
+    if (ch + 2 < nch) step(ch + 2, A2, A1);
   }
 
   // sums of squares: the four lanes holding one token row (lane, +16, +32, +48)
