@@ -14,8 +14,8 @@ before timing; several input/output buffer sets rotate.  Prints one JSON line.
 
 Beside the headline line: the decode block's glue (n=128, "decode"), the
 same boundary at hc = 2 and 8 ("other_hc") and at n = 128 ... 32768
-("sweep"), and the calls at the stand-in stack's two ends ("stack_ends"),
-each timed by events.
+("sweep"), the calls at the stand-in stack's two ends ("stack_ends") and
+the standalone entry points ("entry_points"), each timed by events.
 
 Timing: after half a second of plain streaming (GPU clocks settle; the first
 ~20 ms after idle run several percent slower), W untimed warm-up steps; then
@@ -302,6 +302,48 @@ def sweep(dev, ns=(128, 512, 4096, 32768), reps=50):
                         "(n=32768: channel-outlier stress inputs)", **out}
 
 
+def entry_points(dev, s, reps=50):
+    """The standalone entry points on the prefill workload (n = 4096, hc = 4,
+    d = 5120), each by events: hc_post, hc_pre, hc_mixes (projection + split),
+    hc_split_sinkhorn.  Algorithmic bytes of each as it runs alone."""
+    n = N_TOK
+    X, Dl = bf(s["x"], dev), bf(s["delta"], dev)
+    post, comb, pre = f32(s["post_in"], dev), f32(s["comb_in"], dev), f32(s["pre_in"], dev)
+    fn = T.hc_fn_pack(f32(s["hc_fn"], dev))
+    base, scale = f32(s["hc_base"], dev), f32(s["hc_scale"], dev)
+    xo, y = torch.empty_like(X), torch.empty(n, D, dtype=torch.bfloat16, device=dev)
+    mixes = T.hc_mixes(X, fn)
+    calls = {
+        "hc_post": (lambda: T.hc_post(Dl, X, post, comb, out=xo), n * (4 * D * 2 * 2 + D * 2 + 80)),
+        "hc_pre": (lambda: T.hc_pre(X, pre), n * (4 * D * 2 + D * 2 + 16)),
+        "hc_mixes": (lambda: T.hc_mixes(X, fn, scale, base), n * (4 * D * 2 + 96) + BYTES_CALL - D * 4),
+        "hc_split_sinkhorn": (lambda: T.hc_split_sinkhorn(mixes, scale, base), n * (MIX * 4 + 96)),
+    }
+    out = {}
+    per_graph = 20
+    for name, (fn_call, nbytes) in calls.items():
+        print(f"[bench] timing {name}", file=sys.stderr, flush=True)
+        # the Python binding costs more per call than the small kernels take, so
+        # the calls are captured in a graph (20 per replay) and the replays timed
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn_call()                                    # workspace and allocator warm on this stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(per_graph):
+                fn_call()
+        us = timed_calls([g.replay], min_reps=max(1, reps // per_graph)) * 1e3 / per_graph
+        out[name] = {"call_us": round(us, 2), "algorithmic_bytes": nbytes, "gbs": round(nbytes / us / 1e3, 1),
+                     "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
+        del g
+    del y
+    return {"workload": "standalone entry points, prefill B=1 T=4096, hc=4, d=5120; 20 calls per captured "
+                        "graph, replays timed by events", **out}
+
+
 def stack_ends(dev, reps=50):
     """The calls at the two ends of the stand-in stack (n = 8192, hc = 4,
     d = 5120): the entry (x the embedding [n, d], read by all four streams;
@@ -374,6 +416,7 @@ def main():
     ap.add_argument("--no-other-hc", action="store_true", help="skip the hc = 2 and 8 boundary timing")
     ap.add_argument("--no-sweep", action="store_true", help="skip the token-count sweep")
     ap.add_argument("--no-stack-ends", action="store_true", help="skip the stack entry / exit timing")
+    ap.add_argument("--no-entry-points", action="store_true", help="skip the standalone entry-point timing")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this benchmark runs on one GPU only.  The glue is per token and would shard over "
@@ -414,6 +457,7 @@ def main():
     ohc = None if args.no_other_hc else other_hc(dev)
     swp = None if args.no_sweep else sweep(dev)
     ends = None if args.no_stack_ends else stack_ends(dev)
+    eps = None if args.no_entry_points else entry_points(dev, s)
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -457,6 +501,7 @@ def main():
         "other_hc": ohc,
         "sweep": swp,
         "stack_ends": ends,
+        "entry_points": eps,
     }
     print(json.dumps(line), flush=True)
 

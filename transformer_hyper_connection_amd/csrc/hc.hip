@@ -78,98 +78,101 @@ __device__ __forceinline__ void st_stream(u32x4* p, u32x4 v) { __builtin_nontemp
 
 
 // ------------------------------------------------------------- split / Sinkhorn
-// One token: "Reading weights" split/Sinkhorn kernel panel and reading-weight
-// equation.  fp32; the row/column divisions use the hardware reciprocal.
+// "Reading weights" split/Sinkhorn kernel panel and reading-weight equation.
+// fp32; the row/column divisions use the hardware reciprocal.
 __device__ __forceinline__ float sigmoidf_(float u) { return __builtin_amdgcn_rcpf(1.0f + expf(-u)); }
 
-template <int HC = kHC>
-__device__ void split_sinkhorn_one(const float* mx, float s0, float s1, float s2, const float* bs,
-                                   int iters, float eps, float* pre_o, float* post_o, float* comb_o) {
-  float pre[HC], post[HC];
+// Lane-group sums by DPP, within the group (no LDS round trip).  Butterfly
+// order: every lane of a group gets the same bits; for a quad (v0 + v1) +
+// (v2 + v3) up to commutation.
+template <int CTRL>
+__device__ __forceinline__ float quad_perm(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  const float u = v + quad_perm<0xB1>(v);      // lanes [1,0,3,2]
+  return u + quad_perm<0x4E>(u);               // lanes [2,3,0,1]
+}
+// Sum over the 8 lanes of an aligned group: the two quad sums, each lane
+// adding the other quad's (half-row mirror), the same bits in all 8 lanes.
+__device__ __forceinline__ float oct_sum(float v) {
+  const float u = quad_sum(v);
+  return u + quad_perm<0x141>(u);
+}
+template <int HC>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (HC == 2) return v + quad_perm<0xB1>(v);
+  else if constexpr (HC == 4) return quad_sum(v);
+  else return oct_sum(v);
+}
+
+// The split and the Sinkhorn of "Reading weights" for one token, hc lanes per
+// token: lane j holds mixes pre_j (mp), post_j (mq) and comb row j (mc), and
+// writes pre_j, post_j and comb row j.  The column sums run across the lanes
+// of the token.  Every lane of the group calls it (lanes of a token past n
+// with valid false: they compute and store nothing).
+template <int HC>
+__device__ __forceinline__ void split_lanes(float mp, float mq, const float (&mc)[HC], const float* scale,
+                                            const float* base, int iters, float eps, int j, bool valid,
+                                            float* pre_o, float* post_o, float* comb_o) {
+  const float s0 = scale[0], s1 = scale[1], s2 = scale[2];
+  const float pre = sigmoidf_(mp * s0 + base[j]) + eps;
+  const float post = 2.0f * sigmoidf_(mq * s1 + base[HC + j]);
+  float A[HC], mxr = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < HC; ++j) {
-    pre[j] = sigmoidf_(mx[j] * s0 + bs[j]) + eps;
-    post[j] = 2.0f * sigmoidf_(mx[HC + j] * s1 + bs[HC + j]);
+  for (int k = 0; k < HC; ++k) {
+    A[k] = mc[k] * s2 + base[2 * HC + j * HC + k];
+    mxr = fmaxf(mxr, A[k]);
   }
-  float A[HC][HC];
+  float rs = 0.f;
 #pragma unroll
-  for (int j = 0; j < HC; ++j) {
-    float mx_row = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < HC; ++k) {
-      A[j][k] = mx[2 * HC + j * HC + k] * s2 + bs[2 * HC + j * HC + k];
-      mx_row = fmaxf(mx_row, A[j][k]);
-    }
-    float rs = 0.f;
-#pragma unroll
-    for (int k = 0; k < HC; ++k) {
-      A[j][k] = expf(A[j][k] - mx_row);
-      rs = rs + A[j][k];
-    }
-    const float inv = __builtin_amdgcn_rcpf(rs);
-#pragma unroll
-    for (int k = 0; k < HC; ++k) A[j][k] = A[j][k] * inv + eps;
+  for (int k = 0; k < HC; ++k) {
+    A[k] = expf(A[k] - mxr);
+    rs = rs + A[k];
   }
+  const float rinv = __builtin_amdgcn_rcpf(rs);
+#pragma unroll
+  for (int k = 0; k < HC; ++k) A[k] = A[k] * rinv + eps;
   auto col_norm = [&]() {
 #pragma unroll
-    for (int k = 0; k < HC; ++k) {
-      float cs = A[0][k];
-#pragma unroll
-      for (int j = 1; j < HC; ++j) cs = cs + A[j][k];
-      const float inv = __builtin_amdgcn_rcpf(cs + eps);
-#pragma unroll
-      for (int j = 0; j < HC; ++j) A[j][k] = A[j][k] * inv;
-    }
+    for (int k = 0; k < HC; ++k) A[k] = A[k] * __builtin_amdgcn_rcpf(group_sum<HC>(A[k]) + eps);
   };
   col_norm();
   for (int it = 1; it < iters; ++it) {
+    float r2 = A[0];
 #pragma unroll
-    for (int j = 0; j < HC; ++j) {
-      float rs = A[j][0];
+    for (int k = 1; k < HC; ++k) r2 = r2 + A[k];
+    const float inv = __builtin_amdgcn_rcpf(r2 + eps);
 #pragma unroll
-      for (int k = 1; k < HC; ++k) rs = rs + A[j][k];
-      const float inv = __builtin_amdgcn_rcpf(rs + eps);
-#pragma unroll
-      for (int k = 0; k < HC; ++k) A[j][k] = A[j][k] * inv;
-    }
+    for (int k = 0; k < HC; ++k) A[k] = A[k] * inv;
     col_norm();
   }
-  if constexpr (HC == 4) {
-    *reinterpret_cast<f32x4*>(pre_o) = f32x4{pre[0], pre[1], pre[2], pre[3]};
-    *reinterpret_cast<f32x4*>(post_o) = f32x4{post[0], post[1], post[2], post[3]};
+  if (valid) {
+    pre_o[j] = pre;
+    post_o[j] = post;
 #pragma unroll
-    for (int j = 0; j < HC; ++j)
-      reinterpret_cast<f32x4*>(comb_o)[j] = f32x4{A[j][0], A[j][1], A[j][2], A[j][3]};
-  } else {
-#pragma unroll
-    for (int j = 0; j < HC; ++j) {
-      pre_o[j] = pre[j];
-      post_o[j] = post[j];
-#pragma unroll
-      for (int k = 0; k < HC; ++k) comb_o[j * HC + k] = A[j][k];
-    }
+    for (int k = 0; k < HC; ++k) comb_o[j * HC + k] = A[k];
   }
 }
 
+// hc_split_sinkhorn: hc lanes per token.
 template <int HC>
 __global__ void __launch_bounds__(256) split_kernel(const float* __restrict__ mixes,
                                                     const float* __restrict__ scale,
                                                     const float* __restrict__ base, int64_t n, int iters,
                                                     float eps, float* __restrict__ pre,
                                                     float* __restrict__ post, float* __restrict__ comb) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= n) return;
   constexpr int MIX = (2 + HC) * HC;
-  float mx[MIX], bs[MIX];
+  const int j = threadIdx.x % HC;
+  const int64_t tq = (int64_t)blockIdx.x * (256 / HC) + threadIdx.x / HC;
+  const bool valid = tq < n;
+  const int64_t t = valid ? tq : 0;   // lanes past n compute on token 0 (they take part in the sums)
+  const float* m = mixes + t * MIX;
+  float mc[HC];
 #pragma unroll
-  for (int q = 0; q < MIX; q += 4) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(mixes + t * MIX + q);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(base + q);
-    mx[q] = v[0]; mx[q + 1] = v[1]; mx[q + 2] = v[2]; mx[q + 3] = v[3];
-    bs[q] = b[0]; bs[q + 1] = b[1]; bs[q + 2] = b[2]; bs[q + 3] = b[3];
-  }
-  split_sinkhorn_one<HC>(mx, scale[0], scale[1], scale[2], bs, iters, eps, pre + t * HC, post + t * HC,
-                         comb + t * HC * HC);
+  for (int k = 0; k < HC; ++k) mc[k] = m[2 * HC + j * HC + k];
+  split_lanes<HC>(m[j], m[HC + j], mc, scale, base, iters, eps, j, valid, pre + t * HC, post + t * HC,
+                  comb + t * HC * HC);
 }
 
 // ------------------------------------------------------------------ weight pack
@@ -413,12 +416,6 @@ struct GFinArgs {
 // slice order, the RMS scale applied ("Source layer, pairs pooled":
 // Block.hc_mixes), then the split and the Sinkhorn rounds of "Reading
 // weights" with lane j holding comb row j (column sums across the hc lanes).
-template <int HC>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = 1; o < HC; o <<= 1) v += __shfl_xor(v, o);   // same bits in every lane of the group
-  return v;
-}
 
 template <int HC>
 __global__ void __launch_bounds__(256) gfinish_kernel(const GFinArgs a) {
@@ -452,44 +449,8 @@ __global__ void __launch_bounds__(256) gfinish_kernel(const GFinArgs a) {
     for (int k = 0; k < HC; ++k) m[2 * HC + j * HC + k] = lc[k];
   }
   if (!a.pre_out) return;
-  const float s0 = a.hc_scale[0], s1 = a.hc_scale[1], s2 = a.hc_scale[2], eps = a.hc_eps;
-  const float pre = sigmoidf_(lp * s0 + a.hc_base[j]) + eps;
-  const float post = 2.0f * sigmoidf_(lq * s1 + a.hc_base[HC + j]);
-  float A[HC], mxr = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < HC; ++k) {
-    A[k] = lc[k] * s2 + a.hc_base[2 * HC + j * HC + k];
-    mxr = fmaxf(mxr, A[k]);
-  }
-  float rs = 0.f;
-#pragma unroll
-  for (int k = 0; k < HC; ++k) {
-    A[k] = expf(A[k] - mxr);
-    rs = rs + A[k];
-  }
-  const float rinv = __builtin_amdgcn_rcpf(rs);
-#pragma unroll
-  for (int k = 0; k < HC; ++k) A[k] = A[k] * rinv + eps;
-  auto col_norm = [&]() {
-#pragma unroll
-    for (int k = 0; k < HC; ++k) A[k] = A[k] * __builtin_amdgcn_rcpf(group_sum<HC>(A[k]) + eps);
-  };
-  col_norm();
-  for (int it = 1; it < a.iters; ++it) {
-    float r2 = A[0];
-#pragma unroll
-    for (int k = 1; k < HC; ++k) r2 = r2 + A[k];
-    const float inv = __builtin_amdgcn_rcpf(r2 + eps);
-#pragma unroll
-    for (int k = 0; k < HC; ++k) A[k] = A[k] * inv;
-    col_norm();
-  }
-  if (valid) {
-    a.pre_out[t * HC + j] = pre;
-    a.post_out[t * HC + j] = post;
-#pragma unroll
-    for (int k = 0; k < HC; ++k) a.comb_out[t * HC * HC + j * HC + k] = A[k];
-  }
+  split_lanes<HC>(lp, lq, lc, a.hc_scale, a.hc_base, a.iters, a.hc_eps, j, valid, a.pre_out + t * HC,
+                  a.post_out + t * HC, a.comb_out + t * HC * HC);
 }
 
 // The matrix-core step for one (A tile, 32-feature step, stream): the five
@@ -1023,24 +984,6 @@ struct FinishArgs {
   int d, S, S2, F2, tiles, iters;
   float hc_eps, norm_eps, rms_eps;
 };
-
-// Sum over the 4 lanes of a token's quad, by lane permutation within the
-// quad (no LDS round trip).  Butterfly order: every lane of the quad obtains
-// the same bits, (v0 + v1) + (v2 + v3) up to commutation.
-template <int CTRL>
-__device__ __forceinline__ float quad_perm(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float quad_sum(float v) {
-  const float u = v + quad_perm<0xB1>(v);      // lanes [1,0,3,2]
-  return u + quad_perm<0x4E>(u);               // lanes [2,3,0,1]
-}
-// Sum over the 8 lanes of an aligned group: the two quad sums, each lane
-// adding the other quad's (half-row mirror), the same bits in all 8 lanes.
-__device__ __forceinline__ float oct_sum(float v) {
-  const float u = quad_sum(v);
-  return u + quad_perm<0x141>(u);
-}
 
 template <int RM, bool NORM>
 __global__ void __launch_bounds__(kFinThreads) finish_kernel(const FinishArgs a) {
@@ -2496,7 +2439,8 @@ int launch_mixes_generic(int hc, const hc_bf16* x, int xtok, int xstr, const voi
 
 int launch_split(int hc, const float* mixes, const float* scale, const float* base, int64_t n, int iters,
                  float eps, float* pre, float* post, float* comb, hipStream_t st) {
-  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  const int64_t tpb = 256 / hc;                   // tokens per workgroup: hc lanes each
+  const dim3 grid((unsigned)((n + tpb - 1) / tpb)), block(256);
   if (hc == 2)
     hipLaunchKernelGGL(split_kernel<2>, grid, block, 0, st, mixes, scale, base, n, iters, eps, pre, post, comb);
   else if (hc == 8)
