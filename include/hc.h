@@ -217,6 +217,19 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
  * streams to x_out; without, it derives the mixes of the copies and reads
  * them.  Not with HC_BOUNDARY_SINGLE_LAUNCH. */
 #define HC_BOUNDARY_X_EXPANDED 4u
+/* HC_BOUNDARY_SLICE_RESIDENT (hc = 4, d = 5120, delta and fn_packed given,
+ * pre_in NULL): the whole call as one launch of one workgroup per compute unit
+ * (it needs all 256 compute units of an MI355X, else HC_ENOTSUP), every
+ * workgroup keeping one 160-feature slice of the projection weights in LDS and
+ * the new streams of its last token tiles in registers, so X and delta are read
+ * once and X' is never read back.  The slices of a token tile exchange
+ * per-token partial sums through the workspace (a fixed region after the
+ * control block and the decode region; bounded waits: a timeout sets bit 0 of
+ * the error mask at byte 4160 and the call finishes with wrong values instead
+ * of hanging).  One call at a time per workspace.  Same results as the default
+ * schedule within the stated tolerances (the projection is summed over other
+ * feature slices).  Not with HC_BOUNDARY_SINGLE_LAUNCH. */
+#define HC_BOUNDARY_SLICE_RESIDENT 8u
 
 typedef struct hc_boundary_args {
   uint32_t struct_size; /* = sizeof(hc_boundary_args) */
@@ -240,7 +253,7 @@ typedef struct hc_boundary_args {
   float* comb_out;         /* [n, hc, hc]  required iff fn_packed != NULL        */
   void* workspace;
   size_t workspace_bytes;
-  uint32_t flags;          /* 0, HC_BOUNDARY_SINGLE_LAUNCH, HC_BOUNDARY_X_EXPANDED */
+  uint32_t flags;          /* 0, or HC_BOUNDARY_* bits (above)                    */
   /* [n, d] bf16 or NULL: the mean over the hc streams of the new streams (x_out,
    * or x at a block entry), the MTP head's tap of a block's input ("Final
    * RMSNorm", the model driver); the streams summed in fp32 in stream order

@@ -80,12 +80,16 @@ def test_packed_and_workspace_bytes(L):
     assert L.hc_workspace_bytes(4096, 3, 5120) == 0
     w = L.hc_workspace_bytes(4096, 4, 5120)
     # 8 KB control block; decode region (fixed for d): 256 B of arrival words + 8 tiles x 20 slices
-    # x 16 tokens x 25 tagged 8-byte words; single-launch records: 256 tiles of 16 tokens x 10
-    # slices x 34 tagged words; two-launch records: 64 tiles of 64 tokens x 4 slices x 36 floats
+    # x 16 tokens x 25 tagged 8-byte words; slice-resident ring (d = 5120 only): 8 XCDs x 16 slots
+    # x 32 slices x 16 tokens x 36 tagged record words, and 8 XCDs x 16 slots x 16 tokens x 8
+    # read-coefficient words; single-launch records: 256 tiles of
+    # 16 tokens x 10 slices x 34 tagged words; two-launch records: 64 tiles of 64 tokens x 4 slices
+    # x 36 floats
     decode = 256 + 8 * 20 * 16 * 25 * 8
-    assert w == 8192 + decode + 256 * 10 * 16 * 34 * 8 + 64 * 4 * 64 * 36 * 4
+    ring = 8 * 16 * 32 * 16 * 36 * 8 + 8 * 16 * 16 * 8 * 8
+    assert w == 8192 + decode + ring + 256 * 10 * 16 * 34 * 8 + 64 * 4 * 64 * 36 * 4
     # n = 128: 8 single-launch tiles; two-launch: 2 tiles x 40 slices
-    assert L.hc_workspace_bytes(128, 4, 5120) == 8192 + decode + 8 * 10 * 16 * 34 * 8 + 2 * 40 * 64 * 36 * 4
+    assert L.hc_workspace_bytes(128, 4, 5120) == 8192 + decode + ring + 8 * 10 * 16 * 34 * 8 + 2 * 40 * 64 * 36 * 4
     assert L.hc_boundary_workspace_bytes(4096, 4, 5120) == w
     assert L.hc_workspace_bytes(4097, 4, 5120) > w
     # widths the single launch does not take (d % 512 != 0): control block + two-launch records only
@@ -102,7 +106,8 @@ def test_packed_and_workspace_bytes_other_hc(L):
     # largest divisor of hc*d/64 with at most ~512 workgroups of 128 tokens, 64 at most; recw = mix + 1
     # rounded up to 4 floats (12 at hc = 2, 84 at hc = 8)
     decode = 256 + 8 * 20 * 16 * 25 * 8
-    assert L.hc_workspace_bytes(4096, 8, 5120) == 8192 + decode + 16 * 4096 * 84 * 4
+    ring = 8 * 16 * 32 * 16 * 36 * 8 + 8 * 16 * 16 * 8 * 8   # slice-resident ring at d = 5120
+    assert L.hc_workspace_bytes(4096, 8, 5120) == 8192 + decode + ring + 16 * 4096 * 84 * 4
     assert L.hc_workspace_bytes(100, 2, 320) == 8192 + 10 * 100 * 12 * 4     # 10 chunks of 64: S = 10
     assert L.hc_workspace_bytes(40, 8, 1024) == 8192 + (256 + 8 * 4 * 16 * 25 * 8) + 64 * 40 * 84 * 4
     assert L.hc_workspace_bytes(0, 8, 5120) == 0
@@ -181,7 +186,7 @@ def test_boundary_validation(L):
     assert call(_args(d=10304, gamma=P + 0xD00)) == H.HC_ENOTSUP   # RMSNorm row too long
     # the single-launch schedule flag: unknown bits, shapes it does not take, no halves
     SL, XE = H.HC_BOUNDARY_SINGLE_LAUNCH, H.HC_BOUNDARY_X_EXPANDED
-    assert call(_args(flags=8)) == H.HC_EINVAL
+    assert call(_args(flags=16)) == H.HC_EINVAL
     assert call(_args(flags=SL | XE, d=1024)) == H.HC_ENOTSUP            # no expanded x in the single launch
     assert call(_args(flags=SL, d=1024, x_mean_out=P + 0xE00)) == H.HC_ENOTSUP   # nor the stream mean
     assert call(_args(x_mean_out=MIS)) == H.HC_EINVAL                    # misaligned stream-mean output
@@ -190,9 +195,21 @@ def test_boundary_validation(L):
     assert call(_args(flags=SL, d=1024, fn_packed=None, pre_in=P + 0x600)) == H.HC_EINVAL   # needs the mixes
     assert call(_args(flags=SL, d=1024, hc=8)) == H.HC_ENOTSUP    # hc = 4 only
     assert L.hc_boundary_begin(ctypes.byref(_args(flags=SL, d=1024)), S) == H.HC_EINVAL
+    # the slice-resident schedule: hc = 4, d = 5120, a write, the mixes, the fresh pre; one launch
+    SR = H.HC_BOUNDARY_SLICE_RESIDENT
+    assert call(_args(flags=SR | SL, d=5120, pre_in=None)) == H.HC_EINVAL        # one schedule at a time
+    assert call(_args(flags=SR, d=1024, pre_in=None)) == H.HC_ENOTSUP            # d = 5120 only
+    assert call(_args(flags=SR, d=5120, hc=8, pre_in=None)) == H.HC_ENOTSUP      # hc = 4 only
+    assert call(_args(flags=SR, d=5120)) == H.HC_ENOTSUP                         # a given pre
+    assert call(_args(flags=SR, d=5120, pre_in=None, delta=None, post_in=None, comb_in=None,
+                      x_out=None)) == H.HC_ENOTSUP                               # a block entry
+    assert call(_args(flags=SR, d=5120, pre_in=None, x_mean_out=P + 0xE00)) == H.HC_ENOTSUP
+    assert call(_args(flags=SR | XE, d=5120, pre_in=None)) == H.HC_ENOTSUP
+    assert L.hc_boundary_begin(ctypes.byref(_args(flags=SR, d=5120, pre_in=None)), S) == H.HC_EINVAL
+    assert call(_args(flags=SR, d=5120, pre_in=None, n=0)) == H.HC_OK
     # a caller of the struct without the trailing flags field (shorter struct_size) gets flags 0
     short = H.BoundaryArgs.flags.offset
-    assert call(_args(struct_size=short, flags=8)) in (H.HC_ENODEV, H.HC_OK)
+    assert call(_args(struct_size=short, flags=16)) in (H.HC_ENODEV, H.HC_OK)
     # ... and without the trailing x_mean_out field, no stream mean
     assert call(_args(struct_size=H.BoundaryArgs.x_mean_out.offset, x_mean_out=MIS)) in (H.HC_ENODEV, H.HC_OK)
     assert call(_args(struct_size=short - 8)) == H.HC_EINVAL

@@ -53,6 +53,7 @@ typedef unsigned int u32;
 typedef u32 u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -1771,6 +1772,544 @@ __global__ void __launch_bounds__(kFThreads, 1) fused_kernel(const FusedArgs a) 
   }
 }
 
+// ======================================================= slice-resident boundary
+// sweep_kernel<NORM>: the boundary with the freshly derived pre -- hc_post,
+// hc_mixes on X', split and Sinkhorn, hc_pre with that pre (+ RMSNorm) -- in
+// one launch that reads X and delta once and never reads X' back ("Source
+// layer, pairs pooled": Block.forward; "Reading weights": the split kernel
+// panel; "Final RMSNorm").  Built for the pages' width, d = 5120, at hc = 4.
+//
+// The width is cut into 32 slices of 160 features of each stream.  Token tiles
+// (16 tokens) are dealt to the eight XCDs round robin (tile T to XCD T % 8);
+// on an XCD every tile passes through all 32 workgroups, workgroup p taking
+// slice p.  So a workgroup keeps one slice for the whole call and holds that
+// slice's packed projection weights (the B operands of the matrix cores) in
+// LDS, loaded once.  The grid is one workgroup per compute unit, all resident.
+//
+// Eight waves, two per SIMD: five stream waves (one lane per token and 8
+// features of the slice), the projection wave, and exchange waves A and B.
+// The stream waves never wait on global memory; the others never stream.
+// Interval k, one workgroup barrier per interval (tile indices local to the
+// XCD):
+//   stream waves: the read row (y, or z with the RMSNorm) of tile k-7 from its
+//     X' kept in registers (eight sets) and its coefficients in LDS; X' of
+//     tile k+1 from the loads of two intervals ago, stored and put in the LDS
+//     A tile; the loads of tile k+3.
+//   projection wave: the 24 dots of tile k on the matrix cores, published as
+//     words 0..23 of each token's record.
+//   wave A: sum x'^2 and the 10 Gram entries of tile k from the A tile,
+//     record words 24..35; the read coefficients of tile k-6 (requested an
+//     interval earlier) into LDS; post_in and comb_in of tile k+2.
+//   wave B (owner of one token of every other tile): sums the records of its
+//     token of tile k-3 over the 32 slices (requested an interval earlier),
+//     derives and publishes the read coefficients (pre, and the RMSNorm factor
+//     from p^T G p) with mixes, pre and post; or requests the records of tile
+//     k-2 and runs the Sinkhorn comb of its token of tile k-4.
+// Exchange words are 64-bit (value, tag) stored and loaded with device scope;
+// tags are the call epoch plus the tile index, so no ring slot needs clearing
+// and no store waits.  Every request is issued at the start of an interval
+// (ahead of the stream waves' burst in the compute unit's memory pipeline) and
+// used an interval later.  Waits are bounded: a timeout sets the error mask and
+// the call finishes with wrong values instead of hanging.  The last workgroup
+// to finish advances the epoch.
+constexpr int kWT = 16;                      // tokens per tile
+constexpr int kWX = 8;                       // XCDs: tile T goes to XCD T % 8
+constexpr int kWS = 32;                      // slices = workgroups per XCD
+constexpr int kWD = 5120;                    // the width the schedule is built for
+constexpr int kWF = kWD / kWS;               // 160 features per slice and stream
+constexpr int kWG8 = kWF / 8;                // 20 lanes per token
+constexpr int kWSt = kWF / kStepF;           // 5 matrix-core K steps per stream
+constexpr int kWSW = kWT * kWG8 / 64;        // 5 stream waves
+constexpr int kWThreads = (kWSW + 3) * 64;   // + exchange waves A, B and the projection wave
+constexpr int kWGrid = kWX * kWS;            // 256 workgroups
+constexpr int kWLag = 7;                     // read row of tile k - 7 in interval k
+constexpr int kWXS = kWLag + 1;              // X' register sets, tile % 8
+constexpr int kWRR = 16;                     // ring slots (records, read coefficients)
+constexpr int kWRec = 36;                    // record floats: 24 dots, sum x'^2, 10 Gram, pad
+constexpr int kWCin = kHC + kHC * kHC;       // post_in, comb_in per token
+constexpr int kWCoefW = 8;                   // read-coefficient words per token (5 used)
+constexpr int kWEpochWord = 1152;            // control block: 8 epoch copies, 64 bytes apart
+constexpr int kWDoneWord = 1280;
+constexpr int kWaitLds = 0xC07F;             // s_waitcnt lgkmcnt(0) only (vmcnt 63, expcnt 7 untouched)
+constexpr size_t kWRecBytes = sizeof(unsigned long long) * kWX * kWRR * kWS * kWT * kWRec;
+constexpr size_t kWCoefBytes = sizeof(unsigned long long) * kWX * kWRR * kWT * kWCoefW;
+static_assert(kWSW * 64 == kWT * kWG8, "stream lanes cover the tile");
+static_assert(kWF % kStepF == 0, "slice is whole matrix-core steps");
+
+struct SweepArgs {
+  const hc_bf16* x;
+  const hc_bf16* delta;
+  const float* post_in;
+  const float* comb_in;
+  const u32x4* fn;
+  const float* gamma;
+  const float* hc_base;
+  const float* hc_scale;
+  hc_bf16* x_out;
+  hc_bf16* y_out;
+  float* mixes_out;
+  float* pre_out;
+  float* post_out;
+  float* comb_out;
+  u32* ctrl;          // workspace head (kCtrlBytes)
+  u64* rec;           // [kWX][kWRR][kWS][kWT][kWRec] tagged words
+  u64* coef;          // [kWX][kWRR][kWT][kWCoefW]
+  int64_t n;
+  int ntiles, maxcnt, iters;
+  float hc_eps, norm_eps, rms_eps;
+};
+
+template <int N> struct IC { static constexpr int v = N; };
+
+// Sum over the 4 lanes c, c+4, c+8, c+12 of a row of 16 (one column of a 4x4
+// block held one element per lane, lane 4j + c).  Rotating a row by 8 pairs
+// lane l with l^8; the pair sums are then rotated by 4, which lands in the
+// other pair whichever way the rotation runs: each lane adds the same two
+// pair sums, so all four lanes get the same bits.
+template <int CTRL>
+__device__ __forceinline__ float row_dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float col4_sum(float v) {
+  const float u = v + row_dpp<0x128>(v);          // row_ror:8
+  return u + row_dpp<0x124>(u);                   // row_ror:4
+}
+__device__ __forceinline__ float quad_max(float v) {
+  const float u = fmaxf(v, quad_perm<0xB1>(v));
+  return fmaxf(u, quad_perm<0x4E>(u));
+}
+
+template <bool NORM>
+__global__ void __launch_bounds__(kWThreads, 1) sweep_kernel(const SweepArgs a) {
+  __shared__ u32x4 w_lds[kWSt][kHC][kNT][64];      // the slice's weight tiles (100 KB)
+  __shared__ u32x4 a_lds[2][kWSt][kHC][64];        // X' in A layout, by tile parity (40 KB)
+  __shared__ float cin[2][kWT][kWCin];             // post_in, comb_in, by tile parity
+  __shared__ float bcl[2][kWT][kHC + 1];           // pre and RMSNorm factor, by tile parity
+  __shared__ float gsc[kWS][kWRec];                // owner: one token's records of all slices
+  __shared__ float tot[2][kWRec];                  // owner: summed, by tile parity
+
+  constexpr int d = kWD;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int x = blockIdx.x % kWX, p = blockIdx.x / kWX;
+  const int cnt = a.ntiles > x ? (a.ntiles - x + kWX - 1) / kWX : 0;   // tiles of this XCD
+  const int K = cnt > 0 ? cnt + kWLag : 0;                            // the last interval's k
+  // intervals k = -1 .. J-2: K + 1 of them, padded to a multiple of 8 (the
+  // stream waves' loop is unrolled eight times with no early exit)
+  const int J = (K + 1 + kWXS - 1) / kWXS * kWXS;
+  u32* err = a.ctrl + kErrWord;
+  const u32 epoch = __hip_atomic_load(a.ctrl + kWEpochWord + 16 * x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  auto tag_of = [&](int i) __attribute__((always_inline)) { return epoch + 1u + (u32)i; };
+  auto tok0 = [&](int i) __attribute__((always_inline)) { return (int64_t)(x + kWX * i) * kWT; };   // first token of local tile i
+  const int fs = p * kWF;                          // first feature of the slice (per stream)
+
+  // ---- the slice's weight tiles into LDS (once)
+  for (int idx = threadIdx.x; idx < kWSt * kHC * kNT * 64; idx += kWThreads) {
+    const int l = idx & 63, nt = (idx >> 6) % kNT, k = (idx / (64 * kNT)) % kHC, s = idx / (64 * kNT * kHC);
+    const int gstep = fs / kStepF + s;
+    w_lds[s][k][nt][l] = a.fn[((size_t)(gstep * kHC + k) * kNT + nt) * 64 + l];
+  }
+
+  if (wave < kWSW) {
+    // ======================================================== stream waves
+    // Every memory access goes through a buffer resource sized to the tile's
+    // valid tokens (0 for a tile past the end): tokens past n read zeros and
+    // store nothing, with no branch, so every interval issues the same memory
+    // instructions and the loads of the next two tiles stay in flight.
+    const int u = wave * 64 + lane;
+    const int tau = u / kWG8, g = u % kWG8;
+    const int f = fs + 8 * g;                      // this lane's first feature (per stream)
+    const int a_s = g >> 2, a_lane = (g & 3) * 16 + tau;
+    const u32 xoff = (u32)((tau * kHC * d + f) * 2), doff = (u32)((tau * d + f) * 2);
+    float gm[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gm[e] = NORM ? a.gamma[f + e] : 1.f;
+    u32x4 LS[2][kHC + 1];                          // loads in flight, by tile parity
+    u32 XS[kWXS][kHC][4] = {};                     // X' kept for the read row, tile % 8
+    auto valid_of = [&](int i) __attribute__((always_inline)) -> u32 {
+      if (i < 0 || i >= cnt) return 0u;
+      const int64_t left = a.n - tok0(i);
+      return (u32)(left < kWT ? left : kWT);
+    };
+    auto issue = [&](int i, u32x4 (&L)[kHC + 1]) __attribute__((always_inline)) {
+      const u32 v = valid_of(i);
+      const int64_t t0 = v ? tok0(i) : 0;
+      const rsrc_t rx = make_rsrc(a.x + t0 * kHC * d, v * (u32)(kHC * d * 2));
+      const rsrc_t rd = make_rsrc(a.delta + t0 * d, v * (u32)(d * 2));
+#pragma unroll
+      for (int j = 0; j < kHC; ++j) L[j] = buf_ld(rx, xoff + (u32)(j * d * 2));
+      L[kHC] = buf_ld(rd, doff);
+    };
+    // X' of tile i: stored, and into the A tile
+    auto stream = [&](int i, const u32x4 (&L)[kHC + 1], u32 (&xp)[kHC][4]) __attribute__((always_inline)) {
+      const u32 v = valid_of(i);
+      const rsrc_t ro = make_rsrc(a.x_out + (v ? tok0(i) : 0) * kHC * d, v * (u32)(kHC * d * 2));
+      const float* c = cin[i & 1][tau];
+      float cpost[kHC], ccomb[kHC * kHC];
+#pragma unroll
+      for (int j = 0; j < kHC; ++j) cpost[j] = c[j];
+#pragma unroll
+      for (int j = 0; j < kHC * kHC; ++j) ccomb[j] = c[kHC + j];
+      post_8(L, cpost, ccomb, xp);
+#pragma unroll
+      for (int k = 0; k < kHC; ++k) buf_st(ro, xoff + (u32)(k * d * 2), u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]});
+#pragma unroll
+      for (int k = 0; k < kHC; ++k)
+        a_lds[i & 1][a_s][k][a_swz(a_lane, a_s & 1)] = u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]};
+    };
+    // the read row of tile i from its kept X'
+    auto read_row = [&](int i, const u32 (&xp)[kHC][4]) __attribute__((always_inline)) {
+      const u32 v = valid_of(i);
+      const rsrc_t ry = make_rsrc(a.y_out + (v ? tok0(i) : 0) * d, v * (u32)(d * 2));
+      const float* cf = bcl[i & 1][tau];
+      float pr[kHC];
+#pragma unroll
+      for (int j = 0; j < kHC; ++j) pr[j] = cf[j];
+      u32 yp[4];
+      pre_8(xp, pr, yp);
+      if constexpr (NORM) {
+        const float r = cf[kHC];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2)
+          yp[e2] = pack_bf16(gm[2 * e2] * (bf_lo(yp[e2]) * r), gm[2 * e2 + 1] * (bf_hi(yp[e2]) * r));
+      }
+      buf_st(ry, doff, u32x4{yp[0], yp[1], yp[2], yp[3]});
+    };
+
+    issue(0, LS[0]);
+    issue(1, LS[1]);
+    lds_barrier();                                 // weights, cin of tile 0 in place
+    // interval k = j - 1, j = r (mod 8): the register sets are compile-time indices
+    auto interval = [&](int j, auto R) __attribute__((always_inline)) {
+      constexpr int r = decltype(R)::v;
+      read_row(j - 1 - kWLag, XS[r]);
+      stream(j, LS[r & 1], XS[r]);
+      issue(j + 2, LS[r & 1]);
+      lds_barrier();
+    };
+    for (int j0 = 0; j0 < J; j0 += kWXS) {
+      interval(j0, IC<0>{});
+      interval(j0 + 1, IC<1>{});
+      interval(j0 + 2, IC<2>{});
+      interval(j0 + 3, IC<3>{});
+      interval(j0 + 4, IC<4>{});
+      interval(j0 + 5, IC<5>{});
+      interval(j0 + 6, IC<6>{});
+      interval(j0 + 7, IC<7>{});
+    }
+  } else if (wave == kWSW) {
+    // ======================================================== exchange wave A
+    // Each interval: the read coefficients of tile k-6 (from their owners)
+    // into LDS, post_in and comb_in of tile k+2, and the sums of squares and
+    // Gram entries of tile k (record words 24..35).  Its global loads are
+    // issued an interval before their data is used: in the compute unit's
+    // memory pipeline they queue behind the stream waves' loads.
+    bool dead = false;
+    // post_in and comb_in of tile i: issued early, written to LDS late
+    auto cin_load = [&](int i, float (&cv)[5]) __attribute__((always_inline)) {
+      const int64_t t0 = tok0(i);
+      const int tp = lane >> 2;                      // post_in: lane -> (token lane/4, stream lane%4)
+      cv[0] = t0 + tp < a.n ? a.post_in[t0 * kHC + lane] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {                  // comb_in: 256 floats, 4 per lane
+        const int e = lane + 64 * r;
+        cv[1 + r] = t0 + e / (kHC * kHC) < a.n ? a.comb_in[t0 * kHC * kHC + e] : 0.f;
+      }
+    };
+    auto cin_store = [&](int i, const float (&v)[5]) __attribute__((always_inline)) {
+      cin[i & 1][lane >> 2][lane & 3] = v[0];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = lane + 64 * r;
+        cin[i & 1][e / (kHC * kHC)][kHC + e % (kHC * kHC)] = v[1 + r];
+      }
+    };
+    const rsrc_t rrec = make_rsrc(a.rec, (u32)kWRecBytes);
+    // the read-coefficient words of tile i: lane w holds words w and w + 64 of
+    // the tile's 80 (token w / 5, word w % 5)
+    const int w0 = lane, w1 = lane + 64;
+    auto coef_ok = [&](int i, int w) __attribute__((always_inline)) {
+      return i >= 0 && i < cnt && w < kWT * (kHC + 1) && tok0(i) + w / (kHC + 1) < a.n;
+    };
+    auto coef_ptr = [&](int i, int w) __attribute__((always_inline)) -> const u64* {
+      return a.coef + ((size_t)(x * kWRR + (i >= 0 ? i % kWRR : 0)) * kWT + w / (kHC + 1)) * kWCoefW + w % (kHC + 1);
+    };
+    // requests alternate between two register sets (the loop below is unrolled
+    // twice), so that nothing waits for a load before the interval that uses it
+    u64 cw[2][2] = {{0, 0}, {0, 0}};
+    float cvv[2][5];
+    if (cnt > 0) { cin_load(0, cvv[0]); cin_store(0, cvv[0]); }
+    if (cnt > 1) cin_load(1, cvv[1]);
+    lds_barrier();
+    auto xa_interval = [&](int k, auto B) __attribute__((always_inline)) {
+      constexpr int b = decltype(B)::v;              // this interval's request set; 1 - b holds the last
+      const int ic = k - (kWLag - 1);                // consumed now; ic + 1 requested
+      // ---- this interval's requests first (ahead of the stream waves' loads
+      // in the CU's memory pipeline), used in the next interval: the read
+      // coefficients of tile k-5, post_in and comb_in of tile k+3
+      if (coef_ok(ic + 1, w0)) cw[b][0] = get_word(coef_ptr(ic + 1, w0));
+      if (coef_ok(ic + 1, w1)) cw[b][1] = get_word(coef_ptr(ic + 1, w1));
+      if (k + 3 < cnt) cin_load(k + 3, cvv[b]);
+      // ---- last interval's requests: the read coefficients of tile k-6 into
+      // LDS (a word not there yet is polled), post_in and comb_in of tile k+2
+      if (ic >= 0 && ic < cnt) {
+        const u32 tg = tag_of(ic);
+        if (coef_ok(ic, w0))
+          bcl[ic & 1][w0 / (kHC + 1)][w0 % (kHC + 1)] = settle(coef_ptr(ic, w0), cw[1 - b][0], tg, err, dead);
+        if (coef_ok(ic, w1))
+          bcl[ic & 1][w1 / (kHC + 1)][w1 % (kHC + 1)] = settle(coef_ptr(ic, w1), cw[1 - b][1], tg, err, dead);
+      }
+      if (k + 2 < cnt) cin_store(k + 2, cvv[1 - b]);
+      // ---- tile k: sum x'^2 and the Gram entries of each token from the A tile
+      // (X' of tile k), words 24..35 of its record.  Lane 4*tau + c takes the
+      // feature groups c, c+4, .., c+16 of token tau (all four streams each);
+      // the four lanes of a token then sum by DPP.
+      if (k >= 0 && k < cnt) {
+        const int tau = lane >> 2, c = lane & 3;
+        float sq[kGram + 1];
+#pragma unroll
+        for (int q = 0; q <= kGram; ++q) sq[q] = 0.f;
+#pragma unroll
+        for (int m = 0; m < kWG8 / 4; ++m) {
+          const int g = c + 4 * m, gs = g >> 2, gl = (g & 3) * 16 + tau;
+          u32x4 xv[kHC];
+#pragma unroll
+          for (int kk = 0; kk < kHC; ++kk) xv[kk] = a_lds[k & 1][gs][kk][a_swz(gl, gs & 1)];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+#pragma unroll
+            for (int kk = 0; kk < kHC; ++kk) sq[0] = dot2_bf16(xv[kk][e], xv[kk][e], sq[0]);
+            int q = 1;
+#pragma unroll
+            for (int j2 = 0; j2 < kHC; ++j2)
+#pragma unroll
+              for (int l2 = j2; l2 < kHC; ++l2, ++q) sq[q] = dot2_bf16(xv[j2][e], xv[l2][e], sq[q]);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q <= kGram; ++q) sq[q] = quad_sum(sq[q]);
+        // lane c of the token stores words 24 + 3c .. 26 + 3c (word 35: pad)
+        const u32 tg = tag_of(k);
+        const u32 base = (u32)(((((x * kWRR + k % kWRR) * kWS + p) * kWT + tau) * kWRec + kMix) * sizeof(u64));
+#pragma unroll
+        for (int e = 0; e < 3; ++e) {
+          const int q = 3 * c + e;
+          float v = 0.f;
+#pragma unroll
+          for (int qq = 0; qq <= kGram; ++qq) v = q == qq ? sq[qq] : v;
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, tag_word(v, tg)), rrec,
+                                                base + (u32)(q * sizeof(u64)), 0, 16 /* device scope */);
+        }
+      }
+      lds_barrier();
+    };
+    // intervals k = -1 .. J-2 (J is even): request set 0 at odd k, 1 at even k
+    for (int k = -1; k < J - 1; k += 2) {
+      xa_interval(k, IC<0>{});
+      xa_interval(k + 1, IC<1>{});
+    }
+  } else if (wave == kWSW + 2) {
+    // ======================================================== projection wave
+    // Interval k: the 24 dots of tile k on the matrix cores (X' in the LDS A
+    // tile, written by the stream waves in interval k-1; the slice's weight
+    // tiles resident in LDS), K-outer so that each A operand is read once;
+    // then the tile's dots are published, words 0..23 of the token records
+    // (tagged).  It never waits on global memory.
+    const rsrc_t rrec = make_rsrc(a.rec, (u32)kWRecBytes);
+    const int col = lane & 15, grp = lane >> 4;
+    lds_barrier();
+    for (int k = -1; k < J - 1; ++k) {
+      if (k >= 0 && k < cnt) {
+        f32x4 acc[kNT][2];
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) acc[nt][0] = acc[nt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // K step st = 4*s + kk; its A and five B operands are read from LDS two
+        // steps ahead of their matrix-core instructions (scheduling barriers
+        // keep the reads there)
+        constexpr int kSteps = kWSt * kHC, kAhead = 2;
+        u32x4 Ab[kAhead + 1], Bb[kAhead + 1][kNT];
+        auto fetch = [&](int st, u32x4& Ao, u32x4 (&Bo)[kNT]) __attribute__((always_inline)) {
+          const int s = st / kHC, kk = st % kHC;
+          Ao = a_lds[k & 1][s][kk][a_swz(lane, s & 1)];
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt) Bo[nt] = w_lds[s][kk][nt][lane];
+        };
+#pragma unroll
+        for (int st = 0; st < kAhead; ++st) fetch(st, Ab[st], Bb[st]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) {
+          if (st + kAhead < kSteps) fetch(st + kAhead, Ab[(st + kAhead) % (kAhead + 1)], Bb[(st + kAhead) % (kAhead + 1)]);
+          __builtin_amdgcn_sched_barrier(0);
+          const int b = st % (kAhead + 1), h = st & 1;
+          const bf16x8 A = __builtin_bit_cast(bf16x8, Ab[b]);
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt)
+            acc[nt][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, Bb[b][nt]), acc[nt][h], 0,
+                                                                0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        const u32 tg = tag_of(k);
+        const u32 slot_base = (u32)((((x * kWRR + k % kWRR) * kWS + p) * kWT) * kWRec * sizeof(u64));
+        auto put = [&](int tau, int q, float v) __attribute__((always_inline)) {
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, tag_word(v, tg)), rrec,
+                                                slot_base + (u32)((tau * kWRec + q) * sizeof(u64)), 0,
+                                                16 /* device scope */);
+        };
+        // dots: lane holds rows (tokens) 4*grp + r of column col of each weight tile
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float t0 = acc[0][0][r] + acc[0][1][r], t1 = acc[1][0][r] + acc[1][1][r];
+          const float t2 = acc[2][0][r] + acc[2][1][r], t3 = acc[3][0][r] + acc[3][1][r];
+          const float t4 = acc[4][0][r] + acc[4][1][r];
+          const float d0 = (t0 + t1) + t2;                      // row col: hi + mid + lo
+          const float d1 = (t3 + row_dpp<0x128>(t3)) + t4;      // row 16 + col (col < 8): hi, mid, lo
+          put(4 * grp + r, col, d0);
+          if (col < 8) put(4 * grp + r, 16 + col, d1);
+        }
+      }
+      lds_barrier();
+    }
+  } else {
+    // ======================================================== exchange wave B (owner)
+    // A slice owns one token of every other tile.  Interval k, owner of a token
+    // of tile k-3: its records from all 32 slices (published three intervals
+    // ago, requested at the start of the last interval) are checked and summed
+    // in slice order, and the read coefficients (pre and the RMSNorm factor)
+    // are derived and published at once, with the mixes, pre and post.
+    // Interval k, owner of a token of tile k-2 and k-4: the records of tile k-2
+    // are requested, and the Sinkhorn comb of the token of tile k-4 runs (only
+    // an output, nothing in the call waits for it).
+    bool dead = false;
+    const rsrc_t rrec = make_rsrc(a.rec, (u32)kWRecBytes);
+    auto owned = [&](int i) __attribute__((always_inline)) -> int {   // token of tile i this slice owns, or -1
+      const int tau = p - kWT * (i & 1);
+      if (i < 0 || i >= cnt || tau < 0 || tau >= kWT || tok0(i) + tau >= a.n) return -1;
+      return tau;
+    };
+    constexpr int kGL = kWS * kWRec / 2 / 64;        // 16-byte loads per lane (9)
+    static_assert(kGL * 64 * 2 == kWS * kWRec, "gather covers all record words");
+    // the split parameters, loaded once: no later parameter load waits behind
+    // this wave's device-scope stores (one in-order counter covers both)
+    const float s0 = a.hc_scale[0], s1 = a.hc_scale[1], s2 = a.hc_scale[2];
+    const float base_m = lane < kMix ? a.hc_base[lane] : 0.f;                  // base[lane]
+    const float base_c = lane < kHC * kHC ? a.hc_base[2 * kHC + lane] : 0.f;   // base[8 + lane]
+    auto base_at = [&](int q) __attribute__((always_inline)) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, base_m), q));
+    };
+    // the records of the owned token of tile i, lane: words 2c, 2c+1, c = lane + 64r
+    auto goff = [&](int i, int tau, int r) __attribute__((always_inline)) -> u32 {
+      const int c = lane + 64 * r, s = (2 * c) / kWRec, q = (2 * c) % kWRec;
+      return (u32)(((((x * kWRR + i % kWRR) * kWS + s) * kWT + tau) * kWRec + q) * sizeof(u64));
+    };
+    u32x4 gv[kGL];                                   // requested at the start of the interval before
+    lds_barrier();
+    for (int k = -1; k < J - 1; ++k) {
+      // ---- request the records of tile k-2 (published two intervals ago),
+      // first in the interval: summed in the next one
+      const int in = k - 2, tn = owned(in);
+      if (tn >= 0) {
+#pragma unroll
+        for (int r = 0; r < kGL; ++r) gv[r] = __builtin_amdgcn_raw_buffer_load_b128(rrec, goff(in, tn, r), 0, 16);
+      }
+      // ---- tile k-3: check the records, sum, read coefficients, mixes, pre, post
+      const int ig = k - 3, tg_tau = owned(ig);
+      if (tg_tau >= 0) {
+        const u32 tg = tag_of(ig);
+        unsigned polls = 0;
+        while (!dead) {
+          bool ok = true;
+#pragma unroll
+          for (int r = 0; r < kGL; ++r) ok = ok && gv[r][1] == tg && gv[r][3] == tg;
+          if (__all(ok)) break;
+          if (++polls > kPollLimit) { if (lane == 0) atomicOr(err, kErrPollTimeout); dead = true; break; }
+          __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+          for (int r = 0; r < kGL; ++r) gv[r] = __builtin_amdgcn_raw_buffer_load_b128(rrec, goff(ig, tg_tau, r), 0, 16);
+        }
+#pragma unroll
+        for (int r = 0; r < kGL; ++r) {
+          const int c = lane + 64 * r;
+          *reinterpret_cast<f32x2*>(&gsc[(2 * c) / kWRec][(2 * c) % kWRec]) =
+              f32x2{__uint_as_float(gv[r][0]), __uint_as_float(gv[r][2])};
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_s_waitcnt(kWaitLds);
+        // lane q < 36 sums word q over the slices in slice order (all reads first)
+        float sacc = 0.f;
+        if (lane < kWRec) {
+          float v[kWS];
+#pragma unroll
+          for (int s = 0; s < kWS; ++s) v[s] = gsc[s][lane];
+          sacc = v[0];
+#pragma unroll
+          for (int s = 1; s < kWS; ++s) sacc = sacc + v[s];
+          tot[ig & 1][lane] = sacc;                  // for the comb, next interval
+        }
+        // the words the read needs, as wave-uniform values
+        auto word = [&](int q) __attribute__((always_inline)) {
+          return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sacc), q));
+        };
+        const int64_t t = tok0(ig) + tg_tau;
+        const float rx = 1.0f / sqrtf(word(kMix) / (float)(kHC * d) + a.norm_eps);
+        float pre[kHC];
+#pragma unroll
+        for (int l = 0; l < kHC; ++l) pre[l] = sigmoidf_((word(l) * rx) * s0 + base_at(l)) + a.hc_eps;
+        float rn = 1.f;
+        if constexpr (NORM) {
+          // sum_i y_i^2 = p^T G p over the whole row
+          double yy = 0.0;
+          int q = 0;
+#pragma unroll
+          for (int l = 0; l < kHC; ++l)
+#pragma unroll
+            for (int l2 = l; l2 < kHC; ++l2, ++q)
+              yy += (l == l2 ? 1.0 : 2.0) * (double)pre[l] * (double)pre[l2] * (double)word(kMix + 1 + q);
+          rn = 1.0f / sqrtf((float)(yy / (double)d) + a.rms_eps);
+        }
+        u64* cw = a.coef + ((size_t)(x * kWRR + ig % kWRR) * kWT + tg_tau) * kWCoefW;
+        if (lane <= kHC) put_word(cw + lane, tag_word(lane == 0 ? pre[0] : lane == 1 ? pre[1] : lane == 2 ? pre[2]
+                                                        : lane == 3 ? pre[3] : rn, tg));
+        if (a.mixes_out && lane < kMix) a.mixes_out[t * kMix + lane] = sacc * rx;
+        if (lane < kHC) {
+          const float pj = lane == 0 ? pre[0] : lane == 1 ? pre[1] : lane == 2 ? pre[2] : pre[3];
+          a.pre_out[t * kHC + lane] = pj;
+        } else if (lane < 2 * kHC) {
+          a.post_out[t * kHC + lane - kHC] = 2.0f * sigmoidf_((sacc * rx) * s1 + base_m);
+        }
+      }
+      // ---- tile k-4: the comb, softmax (+eps) along the rows, a column step,
+      // then iters-1 rounds of (row, column)
+      const int ih = k - 4, th = owned(ih);
+      if (th >= 0 && lane < kHC * kHC) {
+        const float* rc = tot[ih & 1];
+        const float rx = 1.0f / sqrtf(rc[kMix] / (float)(kHC * d) + a.norm_eps);
+        float A = (rc[2 * kHC + lane] * rx) * s2 + base_c;
+        const float mxr = quad_max(A);
+        A = expf(A - mxr);
+        A = A * __builtin_amdgcn_rcpf(quad_sum(A)) + a.hc_eps;
+        A = A * __builtin_amdgcn_rcpf(col4_sum(A) + a.hc_eps);
+        for (int it = 1; it < a.iters; ++it) {
+          A = A * __builtin_amdgcn_rcpf(quad_sum(A) + a.hc_eps);
+          A = A * __builtin_amdgcn_rcpf(col4_sum(A) + a.hc_eps);
+        }
+        a.comb_out[(tok0(ih) + th) * kHC * kHC + lane] = A;
+      }
+      lds_barrier();
+    }
+  }
+  // ---- the last workgroup out advances the epoch for the next call
+  if (threadIdx.x == 0) {
+    const u32 done = __hip_atomic_fetch_add(a.ctrl + kWDoneWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == (u32)kWGrid - 1u) {
+      for (int i = 0; i < kWX; ++i)
+        __hip_atomic_store(a.ctrl + kWEpochWord + 16 * i, epoch + 2u + (u32)a.maxcnt, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.ctrl + kWDoneWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // ======================================================= decode boundary
 // decode_kernel<POST, READ>: the boundary for few tokens in one launch, the
 // finalize (split + Sinkhorn) done by the last feature slice of each token tile
@@ -2156,9 +2695,14 @@ size_t decode_region_bytes(int d) {
   if (d % kDF != 0) return 0;
   return kDArriveBytes + (size_t)kDTiles * (d / kDF) * kDT * kDRec * sizeof(u64);
 }
-// [control block][decode arrival words + records][single-launch records][two-kernel records]
+// slice-resident schedule (hc = 4, d = 5120): record ring, flags, read-coefficient words.
+// Its region has a fixed place for a width d and nothing else writes there.
+bool sweep_shape(int d) { return d == kWD; }
+size_t sweep_region_bytes(int d) { return sweep_shape(d) ? kWRecBytes + kWCoefBytes : 0; }
+size_t fixed_region_bytes(int d) { return kCtrlBytes + decode_region_bytes(d) + sweep_region_bytes(d); }
+// [control block][decode arrival words + records][slice-resident ring][single-launch records][two-kernel records]
 size_t workspace_bytes(int64_t n, int d) {
-  return kCtrlBytes + decode_region_bytes(d) + fused_records_bytes(n, d) + split_records_bytes(n, d);
+  return fixed_region_bytes(d) + fused_records_bytes(n, d) + split_records_bytes(n, d);
 }
 
 template <bool POST, int RM, bool NORM>
@@ -2191,8 +2735,7 @@ int launch_boundary(bool post, int rm, bool norm, StreamArgs s, FinishArgs f, vo
   s.S = stream_slices(s.n, s.d);
   s.F = s.d / s.S;
   s.tiles = (int)tiles;
-  s.rec = reinterpret_cast<float*>(static_cast<char*>(ws) + kCtrlBytes + decode_region_bytes(s.d) +
-                                   fused_records_bytes(s.n, s.d));
+  s.rec = reinterpret_cast<float*>(static_cast<char*>(ws) + fixed_region_bytes(s.d) + fused_records_bytes(s.n, s.d));
   const unsigned grid1 = (unsigned)(tiles * s.S);
   hipError_t e = hipSuccess;
   if (phases & 1) switch ((post ? 8 : 0) | (rm << 1) | (norm ? 1 : 0)) {
@@ -2312,7 +2855,7 @@ int launch_fused(bool post, int rm, bool norm, FusedArgs f, void* ws, size_t ws_
   f.items = (int)items;
   f.rounds = (int)((items + g - 1) / g);
   f.ctrl = static_cast<u32*>(ws);
-  f.rec = reinterpret_cast<u64*>(static_cast<char*>(ws) + kCtrlBytes + decode_region_bytes(f.d));
+  f.rec = reinterpret_cast<u64*>(static_cast<char*>(ws) + fixed_region_bytes(f.d));
   const unsigned grid = (unsigned)g;
   hipError_t e;
   switch ((post ? 4 : 0) | (rm == kFreshPre ? 2 : 0) | (norm ? 1 : 0)) {
@@ -2326,6 +2869,48 @@ int launch_fused(bool post, int rm, bool norm, FusedArgs f, void* ws, size_t ws_
     default: e = launch_fused_t<true, kFreshPre, true>(f, grid, st); break;
   }
   return launched(e, what);
+}
+
+// The slice-resident schedule needs its whole grid resident: one workgroup on
+// each of the 256 compute units (8 XCDs x 32).  Checked once per device.
+bool sweep_device_ok(bool norm) {
+  constexpr int kDevs = 64;
+  static int cache[kDevs][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return false;
+  int c = __atomic_load_n(&cache[dev][norm], __ATOMIC_RELAXED);
+  if (c == 0) {
+    int cus = 0, occ = 0;
+    const void* fn = norm ? reinterpret_cast<const void*>(&sweep_kernel<true>)
+                          : reinterpret_cast<const void*>(&sweep_kernel<false>);
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kWThreads, 0) != hipSuccess)
+      return false;
+    c = (cus == kWGrid && occ >= 1) ? 1 : -1;
+    __atomic_store_n(&cache[dev][norm], c, __ATOMIC_RELAXED);
+  }
+  return c > 0;
+}
+
+int launch_sweep(bool norm, SweepArgs a, void* ws, size_t ws_bytes, hipStream_t st, const char* what) {
+  const size_t need = workspace_bytes(a.n, kWD);
+  if (!ws) return fail(HC_EINVAL, "%s: workspace must not be NULL (need %zu bytes)", what, need);
+  if (!aligned16(ws)) return fail(HC_EINVAL, "%s: workspace is not 16-byte aligned", what);
+  if (ws_bytes < need) return fail(HC_EINVAL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, need);
+  if (!sweep_device_ok(norm))
+    return fail(HC_ENOTSUP, "%s: the slice-resident schedule needs %d resident workgroups (one per compute unit)",
+                what, kWGrid);
+  const int64_t tiles = (a.n + kWT - 1) / kWT;
+  a.ntiles = (int)tiles;
+  a.maxcnt = (int)((tiles + kWX - 1) / kWX);
+  char* base = static_cast<char*>(ws);
+  a.ctrl = static_cast<u32*>(ws);
+  a.rec = reinterpret_cast<u64*>(base + kCtrlBytes + decode_region_bytes(kWD));
+  a.coef = reinterpret_cast<u64*>(reinterpret_cast<char*>(a.rec) + kWRecBytes);
+  void* args[] = {&a};
+  const void* fn = norm ? reinterpret_cast<const void*>(&sweep_kernel<true>)
+                        : reinterpret_cast<const void*>(&sweep_kernel<false>);
+  return launched(hipLaunchKernel(fn, dim3(kWGrid), dim3(kWThreads), args, 0, st), what);
 }
 
 template <bool POST, bool PRE, bool NORM, int TPW, int HC = kHC>
@@ -2397,7 +2982,7 @@ int gen_slices(int64_t n, int hc, int d) {
 // workspace of the hc != 4 path: the per-slice records, placed after the
 // control block and the decode region of the same d so that a workspace
 // shared with hc = 4 calls keeps their words intact
-size_t gen_rec_offset(int d) { return kCtrlBytes + decode_region_bytes(d); }
+size_t gen_rec_offset(int d) { return fixed_region_bytes(d); }
 size_t generic_ws_bytes(int64_t n, int hc, int d) {
   return gen_rec_offset(d) + (size_t)gen_slices(n, hc, d) * n * gen_recw(hc) * 4;
 }
@@ -2603,8 +3188,10 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
   const uint32_t flags = p->struct_size >= kNoFlags + sizeof(uint32_t) ? p->flags : 0u;
   constexpr size_t kNoMean = offsetof(hc_boundary_args, x_mean_out);   // callers of the struct without it
   hc_bf16* const x_mean = p->struct_size >= kNoMean + sizeof(void*) ? p->x_mean_out : nullptr;
-  if (flags & ~(HC_BOUNDARY_SINGLE_LAUNCH | HC_BOUNDARY_X_EXPANDED))
+  if (flags & ~(HC_BOUNDARY_SINGLE_LAUNCH | HC_BOUNDARY_X_EXPANDED | HC_BOUNDARY_SLICE_RESIDENT))
     return fail(HC_EINVAL, "flags=%#x: unknown bits", flags);
+  if ((flags & HC_BOUNDARY_SINGLE_LAUNCH) && (flags & HC_BOUNDARY_SLICE_RESIDENT))
+    return fail(HC_EINVAL, "flags=%#x: pick one schedule", flags);
   const bool expanded = (flags & HC_BOUNDARY_X_EXPANDED) != 0;
   int rc = check_hd(p->hc, p->d);
   if (rc) return rc;
@@ -2632,6 +3219,15 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
     if (!fused_shape(p->d)) return fail(HC_ENOTSUP, "single launch: d=%d must be a multiple of %d, at least %d", p->d, kFF, kFMinD);
     if (p->n > kFusedMaxN) return fail(HC_ENOTSUP, "single launch: n=%lld is too large", (long long)p->n);
   }
+  if (flags & HC_BOUNDARY_SLICE_RESIDENT) {
+    if (p->hc != kHC || !sweep_shape(p->d))
+      return fail(HC_ENOTSUP, "the slice-resident schedule needs hc=4 and d=%d", kWD);
+    if (expanded || x_mean) return fail(HC_ENOTSUP, "the slice-resident schedule takes neither expanded streams nor x_mean_out");
+    if (phases != 3) return fail(HC_EINVAL, "the slice-resident schedule has no halves (use hc_boundary)");
+    if (!mix || !post || !fresh)
+      return fail(HC_ENOTSUP, "the slice-resident schedule needs delta and fn_packed, and pre_in NULL");
+    if (p->n > kFusedMaxN) return fail(HC_ENOTSUP, "slice-resident: n=%lld is too large", (long long)p->n);
+  }
   if (p->n == 0) return HC_OK;
   if ((rc = check_device())) return rc;
   const hipStream_t st = (hipStream_t)stream;
@@ -2645,6 +3241,15 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
     r.pre_in = p->pre_in; r.gamma = p->gamma; r.x_out = p->x_out; r.y_out = p->y_out; r.rms_eps = p->rms_eps;
     r.xtok = xtok; r.xstr = xstr; r.x_mean = x_mean;
     return launch_row(post, true, norm, r, st, "hc_boundary (exit)", p->hc);
+  }
+  if (flags & HC_BOUNDARY_SLICE_RESIDENT) {
+    SweepArgs w{};
+    w.n = p->n; w.x = p->x; w.delta = p->delta; w.post_in = p->post_in; w.comb_in = p->comb_in;
+    w.fn = reinterpret_cast<const u32x4*>(p->fn_packed); w.gamma = p->gamma; w.hc_base = p->hc_base;
+    w.hc_scale = p->hc_scale; w.x_out = p->x_out; w.y_out = p->y_out; w.mixes_out = p->mixes_out;
+    w.pre_out = p->pre_out; w.post_out = p->post_out; w.comb_out = p->comb_out; w.iters = p->iters;
+    w.hc_eps = p->hc_eps; w.norm_eps = p->norm_eps; w.rms_eps = p->rms_eps;
+    return launch_sweep(norm, w, p->workspace, p->workspace_bytes, st, "hc_boundary");
   }
   if (flags & HC_BOUNDARY_SINGLE_LAUNCH) {
     FusedArgs f{};

@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhc.so")
 HC_OK, HC_EINVAL, HC_ENOTSUP, HC_EHIP, HC_ENODEV = 0, -1, -2, -3, -4
 HC_BOUNDARY_SINGLE_LAUNCH = 1
 HC_BOUNDARY_X_EXPANDED = 4
+HC_BOUNDARY_SLICE_RESIDENT = 8
 
 
 class HCError(RuntimeError):
@@ -238,7 +239,7 @@ def _prepare_boundary(x, *, delta=None, post_in=None, comb_in=None, pre_in=None,
                       hc_base=None, hc_scale=None, gamma=None, iters: int = 20, hc_eps: float = 1e-6,
                       norm_eps: float = 1e-6, rms_eps: float = 1e-6, out: dict | None = None,
                       want_mixes: bool = False, single_launch: bool = False, x_expanded: bool = False,
-                      want_mean: bool = False, hc_mult: int = 4):
+                      want_mean: bool = False, hc_mult: int = 4, slice_resident: bool = False):
     """Checks the arguments of one boundary call, allocates missing outputs and
     fills the C argument struct.  Returns (struct, outputs).  hc_mult is the
     number of streams of an expanded x (otherwise x's shape gives it)."""
@@ -293,7 +294,8 @@ def _prepare_boundary(x, *, delta=None, post_in=None, comb_in=None, pre_in=None,
     a.gamma, a.x_out, a.y_out = _ptr(gamma), _ptr(o.get("x_out")), o["y"].data_ptr()
     a.mixes_out, a.pre_out = _ptr(o.get("mixes")), _ptr(o.get("pre"))
     a.post_out, a.comb_out = _ptr(o.get("post")), _ptr(o.get("comb"))
-    a.flags = (HC_BOUNDARY_SINGLE_LAUNCH if single_launch else 0) | (HC_BOUNDARY_X_EXPANDED if x_expanded else 0)
+    a.flags = ((HC_BOUNDARY_SINGLE_LAUNCH if single_launch else 0) | (HC_BOUNDARY_X_EXPANDED if x_expanded else 0)
+               | (HC_BOUNDARY_SLICE_RESIDENT if slice_resident else 0))
     a.x_mean_out = _ptr(o.get("x_mean"))
     if fn_packed is not None:
         ws = o.get("workspace")
@@ -309,7 +311,8 @@ def hc_boundary(x, **kw):
     """One fused sublayer boundary (see include/hc.h).  Keyword arguments:
     delta, post_in, comb_in, pre_in, fn_packed, hc_base, hc_scale, gamma, iters,
     hc_eps, norm_eps, rms_eps, out, want_mixes, single_launch (the
-    HC_BOUNDARY_SINGLE_LAUNCH schedule), x_expanded (x is [..., d], every
+    HC_BOUNDARY_SINGLE_LAUNCH schedule), slice_resident (the
+    HC_BOUNDARY_SLICE_RESIDENT schedule), x_expanded (x is [..., d], every
     stream that row: HC_BOUNDARY_X_EXPANDED; hc_mult then gives the number of
     streams), want_mean (the mean over the streams, "x_mean").  Returns a dict with x_out (None at a block entry), y,
     and pre/post/comb (+ mixes) unless fn_packed is None.
