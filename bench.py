@@ -14,8 +14,9 @@ before timing; several input/output buffer sets rotate.  Prints one JSON line.
 
 Beside the headline line: the decode block's glue (n=128, "decode"), the
 same boundary at hc = 2 and 8 ("other_hc") and at n = 128 ... 32768
-("sweep"), the calls at the stand-in stack's two ends ("stack_ends") and
-the standalone entry points ("entry_points"), each timed by events.
+("sweep"), the calls at the stand-in stack's two ends ("stack_ends"), the
+standalone entry points ("entry_points") and the headline call on the two
+opt-in one-launch schedules ("other_schedules"), each timed by events.
 
 Timing: after half a second of plain streaming (GPU clocks settle; the first
 ~20 ms after idle run several percent slower), W untimed warm-up steps; then
@@ -302,6 +303,31 @@ def sweep(dev, ns=(128, 512, 4096, 32768), reps=50):
                         "(n=32768: channel-outlier stress inputs)", **out}
 
 
+def other_schedules(dev, s, reps=50):
+    """The headline call (write, fresh pre, RMSNorm; n = 4096, hc = 4, d = 5120)
+    on libhc's two opt-in one-launch schedules: HC_BOUNDARY_SINGLE_LAUNCH and
+    HC_BOUNDARY_SLICE_RESIDENT (each workgroup keeps a feature slice of the
+    weights in LDS and X' of its last tiles in registers; no X' read-back).
+    Event-timed like the sweep; the default two-launch schedule beside them."""
+    out = {}
+    ins = {k: (bf(s[k], dev) if k in ("x", "delta") else f32(s[k], dev)) for k in ("x", "delta", "post_in", "comb_in")}
+    params = dict(fn_packed=T.hc_fn_pack(f32(s["hc_fn"], dev)), hc_base=f32(s["hc_base"], dev),
+                  hc_scale=f32(s["hc_scale"], dev), gamma=f32(s["gamma"], dev))
+    nbytes = algorithmic_bytes(N_TOK, "fresh")
+    for name, kw in (("two_launch", {}), ("single_launch", {"single_launch": True}),
+                     ("slice_resident", {"slice_resident": True})):
+        print(f"[bench] timing the {name} schedule", file=sys.stderr, flush=True)
+        call = T.BoundaryCall(ins["x"], delta=ins["delta"], post_in=ins["post_in"], comb_in=ins["comb_in"],
+                              **params, **kw)
+        us = timed_calls([call.run], min_reps=reps) * 1e3
+        out[name] = {"call_us": round(us, 2), "gbs": round(nbytes / us / 1e3, 1),
+                     "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
+        del call
+    torch.cuda.empty_cache()
+    return {"workload": "fused sublayer boundary, prefill B=1 T=4096, hc=4, d=5120, fresh pre, RMSNorm, by schedule",
+            **out}
+
+
 def entry_points(dev, s, reps=50):
     """The standalone entry points on the prefill workload (n = 4096, hc = 4,
     d = 5120), each by events: hc_post, hc_pre, hc_mixes (projection + split),
@@ -417,6 +443,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the token-count sweep")
     ap.add_argument("--no-stack-ends", action="store_true", help="skip the stack entry / exit timing")
     ap.add_argument("--no-entry-points", action="store_true", help="skip the standalone entry-point timing")
+    ap.add_argument("--no-schedules", action="store_true", help="skip the one-launch schedules' timing")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this benchmark runs on one GPU only.  The glue is per token and would shard over "
@@ -458,6 +485,7 @@ def main():
     swp = None if args.no_sweep else sweep(dev)
     ends = None if args.no_stack_ends else stack_ends(dev)
     eps = None if args.no_entry_points else entry_points(dev, s)
+    sch = None if args.no_schedules else other_schedules(dev, s)
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -502,6 +530,7 @@ def main():
         "sweep": swp,
         "stack_ends": ends,
         "entry_points": eps,
+        "other_schedules": sch,
     }
     print(json.dumps(line), flush=True)
 
