@@ -81,12 +81,12 @@ def test_packed_and_workspace_bytes(L):
     w = L.hc_workspace_bytes(4096, 4, 5120)
     # 8 KB control block; decode region (fixed for d): 256 B of arrival words + 8 tiles x 20 slices
     # x 16 tokens x 25 tagged 8-byte words; slice-resident ring (d = 5120 only): 8 XCDs x 16 slots
-    # x 32 slices x 16 tokens x 36 tagged record words, and 8 XCDs x 16 slots x 16 tokens x 8
+    # x 32 slices x 16 tokens x 48 tagged record words (36 used), and 8 XCDs x 16 slots x 16 tokens x 8
     # read-coefficient words; single-launch records: 256 tiles of
     # 16 tokens x 10 slices x 34 tagged words; two-launch records: 64 tiles of 64 tokens x 4 slices
     # x 36 floats
     decode = 256 + 8 * 20 * 16 * 25 * 8
-    ring = 8 * 16 * 32 * 16 * 36 * 8 + 8 * 16 * 16 * 8 * 8
+    ring = 8 * 16 * 32 * 16 * 48 * 8 + 8 * 16 * 16 * 8 * 8
     assert w == 8192 + decode + ring + 256 * 10 * 16 * 34 * 8 + 64 * 4 * 64 * 36 * 4
     # n = 128: 8 single-launch tiles; two-launch: 2 tiles x 40 slices
     assert L.hc_workspace_bytes(128, 4, 5120) == 8192 + decode + ring + 8 * 10 * 16 * 34 * 8 + 2 * 40 * 64 * 36 * 4
@@ -106,7 +106,7 @@ def test_packed_and_workspace_bytes_other_hc(L):
     # largest divisor of hc*d/64 with at most ~512 workgroups of 128 tokens, 64 at most; recw = mix + 1
     # rounded up to 4 floats (12 at hc = 2, 84 at hc = 8)
     decode = 256 + 8 * 20 * 16 * 25 * 8
-    ring = 8 * 16 * 32 * 16 * 36 * 8 + 8 * 16 * 16 * 8 * 8   # slice-resident ring at d = 5120
+    ring = 8 * 16 * 32 * 16 * 48 * 8 + 8 * 16 * 16 * 8 * 8   # slice-resident ring at d = 5120
     assert L.hc_workspace_bytes(4096, 8, 5120) == 8192 + decode + ring + 16 * 4096 * 84 * 4
     assert L.hc_workspace_bytes(100, 2, 320) == 8192 + 10 * 100 * 12 * 4     # 10 chunks of 64: S = 10
     assert L.hc_workspace_bytes(40, 8, 1024) == 8192 + (256 + 8 * 4 * 16 * 25 * 8) + 64 * 40 * 84 * 4

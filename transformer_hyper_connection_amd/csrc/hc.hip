@@ -1825,13 +1825,16 @@ constexpr int kWGrid = kWX * kWS;            // 256 workgroups
 constexpr int kWLag = 7;                     // read row of tile k - 7 in interval k
 constexpr int kWXS = kWLag + 1;              // X' register sets, tile % 8
 constexpr int kWRR = 16;                     // ring slots (records, read coefficients)
-constexpr int kWRec = 36;                    // record floats: 24 dots, sum x'^2, 10 Gram, pad
+constexpr int kWRec = 36;                    // record words used: 24 dots, sum x'^2, 10 Gram, pad
+constexpr int kWRecS = 48;                   // record stride (384 B, three 128-byte lines): dots in
+                                             // words 0..23, sum x'^2 / Gram / pad in words 32..43
+constexpr int kWSq = 32;                     // first sum-of-squares word
 constexpr int kWCin = kHC + kHC * kHC;       // post_in, comb_in per token
 constexpr int kWCoefW = 8;                   // read-coefficient words per token (5 used)
 constexpr int kWEpochWord = 1152;            // control block: 8 epoch copies, 64 bytes apart
 constexpr int kWDoneWord = 1280;
 constexpr int kWaitLds = 0xC07F;             // s_waitcnt lgkmcnt(0) only (vmcnt 63, expcnt 7 untouched)
-constexpr size_t kWRecBytes = sizeof(unsigned long long) * kWX * kWRR * kWS * kWT * kWRec;
+constexpr size_t kWRecBytes = sizeof(unsigned long long) * kWX * kWRR * kWS * kWT * kWRecS;
 constexpr size_t kWCoefBytes = sizeof(unsigned long long) * kWX * kWRR * kWT * kWCoefW;
 static_assert(kWSW * 64 == kWT * kWG8, "stream lanes cover the tile");
 static_assert(kWF % kStepF == 0, "slice is whole matrix-core steps");
@@ -1852,7 +1855,7 @@ struct SweepArgs {
   float* post_out;
   float* comb_out;
   u32* ctrl;          // workspace head (kCtrlBytes)
-  u64* rec;           // [kWX][kWRR][kWS][kWT][kWRec] tagged words
+  u64* rec;           // [kWX][kWRR][kWS][kWT][kWRecS] tagged words
   u64* coef;          // [kWX][kWRR][kWT][kWCoefW]
   int64_t n;
   int ntiles, maxcnt, iters;
@@ -2088,18 +2091,23 @@ __global__ void __launch_bounds__(kWThreads, 1) sweep_kernel(const SweepArgs a) 
         }
 #pragma unroll
         for (int q = 0; q <= kGram; ++q) sq[q] = quad_sum(sq[q]);
-        // lane c of the token stores words 24 + 3c .. 26 + 3c (word 35: pad)
+        // the token's 12 words (sum x'^2, 10 Gram entries, a pad) in two runs of
+        // 16-byte stores: lanes c = 0..3 words 2c, 2c+1, then lanes c = 0, 1
+        // words 8 + 2c, 9 + 2c (every lane of a token holds all the sums)
         const u32 tg = tag_of(k);
-        const u32 base = (u32)(((((x * kWRR + k % kWRR) * kWS + p) * kWT + tau) * kWRec + kMix) * sizeof(u64));
-#pragma unroll
-        for (int e = 0; e < 3; ++e) {
-          const int q = 3 * c + e;
+        const u32 base = (u32)(((((x * kWRR + k % kWRR) * kWS + p) * kWT + tau) * kWRecS + kWSq) * sizeof(u64));
+        auto sq_at = [&](int q) __attribute__((always_inline)) {
           float v = 0.f;
 #pragma unroll
           for (int qq = 0; qq <= kGram; ++qq) v = q == qq ? sq[qq] : v;
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, tag_word(v, tg)), rrec,
-                                                base + (u32)(q * sizeof(u64)), 0, 16 /* device scope */);
-        }
+          return v;
+        };
+        auto put2 = [&](int q) __attribute__((always_inline)) {
+          __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(sq_at(q)), tg, __float_as_uint(sq_at(q + 1)), tg},
+                                                 rrec, base + (u32)(q * sizeof(u64)), 0, 16 /* device scope */);
+        };
+        put2(2 * c);
+        if (c < 2) put2(8 + 2 * c);
       }
       lds_barrier();
     };
@@ -2150,10 +2158,10 @@ __global__ void __launch_bounds__(kWThreads, 1) sweep_kernel(const SweepArgs a) 
           __builtin_amdgcn_sched_barrier(0);
         }
         const u32 tg = tag_of(k);
-        const u32 slot_base = (u32)((((x * kWRR + k % kWRR) * kWS + p) * kWT) * kWRec * sizeof(u64));
+        const u32 slot_base = (u32)((((x * kWRR + k % kWRR) * kWS + p) * kWT) * kWRecS * sizeof(u64));
         auto put = [&](int tau, int q, float v) __attribute__((always_inline)) {
           __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, tag_word(v, tg)), rrec,
-                                                slot_base + (u32)((tau * kWRec + q) * sizeof(u64)), 0,
+                                                slot_base + (u32)((tau * kWRecS + q) * sizeof(u64)), 0,
                                                 16 /* device scope */);
         };
         // dots: lane holds rows (tokens) 4*grp + r of column col of each weight tile
@@ -2189,6 +2197,12 @@ __global__ void __launch_bounds__(kWThreads, 1) sweep_kernel(const SweepArgs a) 
     };
     constexpr int kGL = kWS * kWRec / 2 / 64;        // 16-byte loads per lane (9)
     static_assert(kGL * 64 * 2 == kWS * kWRec, "gather covers all record words");
+    // chunk c: slice c / 18, compact words 2h, 2h+1 (h = c % 18) at record word
+    // 2h (dots, h < 12) or kWSq + 2(h - 12) (the sums)
+    auto cword = [&](int c) __attribute__((always_inline)) {
+      const int h = c % (kWRec / 2);
+      return h < kMix / 2 ? 2 * h : kWSq + 2 * (h - kMix / 2);
+    };
     // the split parameters, loaded once: no later parameter load waits behind
     // this wave's device-scope stores (one in-order counter covers both)
     const float s0 = a.hc_scale[0], s1 = a.hc_scale[1], s2 = a.hc_scale[2];
@@ -2199,8 +2213,8 @@ __global__ void __launch_bounds__(kWThreads, 1) sweep_kernel(const SweepArgs a) 
     };
     // the records of the owned token of tile i, lane: words 2c, 2c+1, c = lane + 64r
     auto goff = [&](int i, int tau, int r) __attribute__((always_inline)) -> u32 {
-      const int c = lane + 64 * r, s = (2 * c) / kWRec, q = (2 * c) % kWRec;
-      return (u32)(((((x * kWRR + i % kWRR) * kWS + s) * kWT + tau) * kWRec + q) * sizeof(u64));
+      const int c = lane + 64 * r, s = c / (kWRec / 2);
+      return (u32)(((((x * kWRR + i % kWRR) * kWS + s) * kWT + tau) * kWRecS + cword(c)) * sizeof(u64));
     };
     u32x4 gv[kGL];                                   // requested at the start of the interval before
     lds_barrier();
