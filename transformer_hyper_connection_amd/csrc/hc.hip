@@ -754,6 +754,8 @@ __device__ __forceinline__ int a_swz(int L, int st) { return L ^ (((L >> 4) & 3)
 // a store that the finish kernel reads back soon (kept cacheable)
 __device__ __forceinline__ void st_keep(u32x4* p, u32x4 v) { *p = v; }
 
+template <int N> struct IC { static constexpr int v = N; };
+
 // MEAN: the stream mean (x_mean) is written; a template parameter so that the
 // calls without it carry none of its registers
 template <bool POST, int RM, bool NORM, bool MEAN>
@@ -785,7 +787,7 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
 
   const int64_t t0 = (int64_t)tile * kTT;
   const bool tv = t0 + m < a.n;
-  const unsigned lt = tv ? (unsigned)m : 0u;   // tokens past n read the tile's first and never store
+  const unsigned lt = tv ? (unsigned)m : 0u;   // tokens past n read the tile's first token
   const hc_bf16* xb = a.x + t0 * a.xtok;
   const hc_bf16* db = POST ? a.delta + t0 * d : a.x;
   hc_bf16* xob = POST ? a.x_out + t0 * kHC * d : nullptr;
@@ -810,21 +812,21 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
 #pragma unroll
   for (int g = 0; g < kGram; ++g) gram[g] = 0.f;
 
-  auto load_wst = [&](int c) {
+  auto load_wst = [&](int c, u32x4 (&dst)[kNT]) {
     const int gstep = (fs + c * kCF) / 32;
 #pragma unroll
     for (int i = 0; i < kNT; ++i) {
       const int blk = wave + i * kWaves;          // (st, k, nt) = blk / 20, (blk / 5) % 4, blk % 5
       const int st = blk / (kHC * kNT), k = (blk / kNT) % kHC, nt = blk % kNT;
-      wst[i] = a.fn[((size_t)((gstep + st) * kHC + k) * kNT + nt) * 64 + lane];
+      dst[i] = a.fn[((size_t)((gstep + st) * kHC + k) * kNT + nt) * 64 + lane];
     }
   };
-  auto store_wst = [&](int buf) {
+  auto store_wst = [&](int buf, const u32x4 (&src)[kNT]) {
 #pragma unroll
     for (int i = 0; i < kNT; ++i) {
       const int blk = wave + i * kWaves;
       const int st = blk / (kHC * kNT), k = (blk / kNT) % kHC, nt = blk % kNT;
-      w_lds[buf][st][k][nt][lane] = wst[i];
+      w_lds[buf][st][k][nt][lane] = src[i];
     }
   };
   auto load_stream = [&](int c, u32x4 (&dst)[kHC + 1]) {
@@ -833,11 +835,11 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
     for (int j = 0; j < kHC; ++j) dst[j] = ld_stream(reinterpret_cast<const u32x4*>(xb + (lt * (unsigned)a.xtok + j * (unsigned)a.xstr + f)));
     dst[kHC] = POST ? ld_stream(reinterpret_cast<const u32x4*>(db + (lt * d + f))) : u32x4{0u, 0u, 0u, 0u};
   };
-  auto stream_phase = [&](int c) {
+  auto stream_phase = [&](int c, const u32x4 (&src)[kHC + 1]) {
     const unsigned f = fs + c * kCF + fl;
     u32 xp[kHC][4];
     if constexpr (POST) {
-      post_8(cur, cpost, ccomb, xp);
+      post_8(src, cpost, ccomb, xp);
       if (tv) {
 #pragma unroll
         for (int k = 0; k < kHC; ++k) {
@@ -850,11 +852,12 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
 #pragma unroll
       for (int k = 0; k < kHC; ++k)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) xp[k][e] = cur[k][e];
+        for (int e = 0; e < 4; ++e) xp[k][e] = src[k][e];
     }
-    if constexpr (MEAN) {
-      if (tv) st_stream(reinterpret_cast<u32x4*>(a.x_mean + (t0 + lt) * d + f), mean_8(xp));
-    }
+    // unconditional: a lane past n works on the tile's first token (lt = 0) and
+    // stores the same bits as that token's lane; with no branch the wait counts
+    // of the two-chunk loop need not assume a skipped store
+    if constexpr (MEAN) st_stream(reinterpret_cast<u32x4*>(a.x_mean + (t0 + lt) * d + f), mean_8(xp));
 #pragma unroll
     for (int k = 0; k < kHC; ++k) {
 #pragma unroll
@@ -902,13 +905,13 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
     constexpr bool kEarly = RM != kFreshPre;
     u32x4 nxt[kHC + 1];
     if (more) {
-      load_wst(c + 1);
+      load_wst(c + 1, wst);
       if (kEarly) load_stream(c + 1, nxt);
     }
-    stream_phase(c);
+    stream_phase(c, cur);
     if (more && !kEarly) load_stream(c + 1, nxt);
     lds_barrier();                 // A tiles and chunk c's weights in place; previous matrix phase done
-    if (more) store_wst((c + 1) & 1);
+    if (more) store_wst((c + 1) & 1, wst);
     matrix_phase(c & 1);
     lds_barrier();                 // matrix phase done before the A tiles are rewritten
     if (more) {
@@ -916,13 +919,68 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
       for (int j = 0; j <= kHC; ++j) cur[j] = nxt[j];
     }
   };
+  // Two chunks in flight (the kernels that store no X'): while chunk c is
+  // consumed, c+1 is arriving, and c+2 is requested as soon as c's stream
+  // registers are free.  Each chunk's weights are requested before its streams,
+  // so the wait for the weights (one chunk later) never waits for younger
+  // stream loads.  Register sets alternate with the chunk's parity (loop
+  // unrolled by two: no copies of loaded registers).  Measured at n = 4096:
+  // hc_mixes' kernel 41.5 -> 38.4 us; with hc_post (X' stored) the same loop
+  // is slower, 70.5 -> 71.9 us, so those keep one chunk in flight.
+  auto deep_step = [&](int c, auto ISSUE, auto STORE, u32x4 (&s)[kHC + 1], u32x4 (&wfree)[kNT],
+                       const u32x4 (&wnext)[kNT]) {
+    __builtin_amdgcn_sched_barrier(0);             // nothing of chunk c moves into chunk c-1
+    stream_phase(c, s);
+    if constexpr (decltype(ISSUE)::v) {
+      __builtin_amdgcn_sched_barrier(0);           // keep the issue order: weights, then streams
+      load_wst(c + 2, wfree);
+      __builtin_amdgcn_sched_barrier(0);
+      load_stream(c + 2, s);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lds_barrier();
+    if constexpr (decltype(STORE)::v) store_wst((c + 1) & 1, wnext);
+    matrix_phase(c & 1);
+    lds_barrier();
+  };
 
-  load_wst(0);
-  load_stream(0, cur);
-  store_wst(0);
-  lds_barrier();
-  for (int c = 0; c + 1 < nch; ++c) chunk(c, true);
-  chunk(nch - 1, false);
+  if constexpr (!POST) {
+    u32x4 sB[kHC + 1], wB[kNT];
+    const int c1 = nch > 1 ? 1 : 0;                // a single chunk loads chunk 0 twice (unused)
+    load_wst(0, wst);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stream(0, cur);
+    __builtin_amdgcn_sched_barrier(0);
+    load_wst(c1, wB);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stream(c1, sB);
+    __builtin_amdgcn_sched_barrier(0);
+    store_wst(0, wst);
+    lds_barrier();
+    int c = 0;
+    for (; c + 3 < nch; c += 2) {
+      deep_step(c, IC<1>{}, IC<1>{}, cur, wst, wB);
+      deep_step(c + 1, IC<1>{}, IC<1>{}, sB, wB, wst);
+    }
+    const int left = nch - c;                       // 1..3: chunk c in cur, c+1 in sB
+    if (left == 3) {
+      deep_step(c, IC<1>{}, IC<1>{}, cur, wst, wB);
+      deep_step(c + 1, IC<0>{}, IC<1>{}, sB, wB, wst);
+      deep_step(c + 2, IC<0>{}, IC<0>{}, cur, wst, wB);
+    } else if (left == 2) {
+      deep_step(c, IC<0>{}, IC<1>{}, cur, wst, wB);
+      deep_step(c + 1, IC<0>{}, IC<0>{}, sB, wB, wst);
+    } else {
+      deep_step(c, IC<0>{}, IC<0>{}, cur, wst, wB);
+    }
+  } else {
+    load_wst(0, wst);
+    load_stream(0, cur);
+    store_wst(0, wst);
+    lds_barrier();
+    for (int c = 0; c + 1 < nch; ++c) chunk(c, true);
+    chunk(nch - 1, false);
+  }
 
   // ---- per-token records of this slice
 #pragma unroll
@@ -1862,7 +1920,6 @@ struct SweepArgs {
   float hc_eps, norm_eps, rms_eps;
 };
 
-template <int N> struct IC { static constexpr int v = N; };
 
 // Sum over the 4 lanes c, c+4, c+8, c+12 of a row of 16 (one column of a 4x4
 // block held one element per lane, lane 4j + c).  Rotating a row by 8 pairs
