@@ -1052,7 +1052,11 @@ __global__ void __launch_bounds__(kFinThreads) finish_kernel(const FinishArgs a)
   __shared__ float g_lds[NORM ? kMaxNormD : 1];   // gamma of the read slice (F2 <= d <= kMaxNormD)
   constexpr int kUsed = rec_used<RM, NORM>();
   constexpr int kQuads = (kUsed + 3) / 4;
-  const int tile = blockIdx.x / a.S2, sl2 = blockIdx.x % a.S2;
+  // XCD-aware: consecutive blocks land on different XCDs.  Renumbered so that
+  // each XCD holds a contiguous run, the S2 workgroups of a tile share an XCD
+  // and its L2, and the tile's records cross the fabric once instead of S2 times.
+  const int lin = (gridDim.x & 7) ? blockIdx.x : (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int tile = lin / a.S2, sl2 = lin % a.S2;
   const int64_t t0 = (int64_t)tile * kTT;
   const int valid = (int)min<int64_t>(kTT, a.n - t0);
   const int d = a.d, S = a.S;
