@@ -109,7 +109,11 @@ def test_identities_on_gpu():
 
 
 # ------------------------------------------------------------------ hc_mixes
-@pytest.mark.parametrize("n,d", [(32, 5120), (45, 5120), (16, 64), (3, 1024), (19, 7168)])
+# chunks of 64 features per workgroup slice: 2 at (32 | 45, 5120) and (19, 7168),
+# 1 at d = 64 and 1024, 5 at (1000, 5120) and 10 at (2048, 5120) -- every tail of
+# the projection loop, which keeps two chunks in flight and is unrolled by two
+@pytest.mark.parametrize("n,d", [(32, 5120), (45, 5120), (16, 64), (3, 1024), (19, 7168), (1000, 5120),
+                                 (2048, 5120)])
 def test_hc_mixes_end_to_end(n, d):
     say(f"[hc_mixes] n={n} d={d}")
     x = rand_bits((n, 4, d))
