@@ -439,6 +439,153 @@ def test_stack_identical_streams_first_read_is_embedding():
     assert np.array_equal(rec[0][1], O.rms_norm(h, np.ones(d, np.float32), 1e-6))
 
 
+# ------------------------------------------------------------ comb routing
+def _comb_one_round(m, s, b, row_of, scale_index):
+    """The comb after one Sinkhorn round with eps = 0, in 40-digit arithmetic:
+    logits L[j][k] = s[scale_index] * m[8 + row_of(j, k)] + b[8 + row_of(j, k)],
+    a softmax along each row, then each column divided by its sum."""
+    mpmath.mp.dps = 40
+    L = [[mpmath.mpf(float(s[scale_index])) * mpmath.mpf(float(m[8 + row_of(j, k)]))
+          + mpmath.mpf(float(b[8 + row_of(j, k)])) for k in range(4)] for j in range(4)]
+    E = [[mpmath.exp(v) for v in row] for row in L]
+    A = [[E[j][k] / mpmath.fsum(E[j]) for k in range(4)] for j in range(4)]
+    col = [mpmath.fsum(A[j][k] for j in range(4)) for k in range(4)]
+    return np.array([[float(A[j][k] / col[k]) for k in range(4)] for j in range(4)])
+
+
+def test_comb_routing_index_orientation_and_scale():
+    """"Reading weights", split/Sinkhorn kernel panel: the comb logit of (row j,
+    column k) is hc_scale[2] * m[2hc + j*hc + k] + hc_base[2hc + j*hc + k].
+    With one round and eps = 0 the comb is that row softmax followed by one
+    column normalisation (closed form, 40 digits).  Every (j, k) gets its own
+    logit and offset, and the three scales differ, so the transposed routing
+    or either other scale lands far from the oracle."""
+    # logits with no additive (row + column) part, which a row softmax followed
+    # by a column normalisation would cancel
+    m = np.zeros((1, 24), np.float32)
+    b = np.zeros(24, np.float32)
+    m[0, 8:] = [0.9, -1.3, 0.2, 1.7, -0.4, 1.1, -1.8, 0.6, 1.4, -0.7, 0.3, -1.5, 0.8, -0.1, 1.9, -1.1]
+    for j in range(4):
+        for k in range(4):
+            b[8 + 4 * j + k] = 0.05 * ((3 * j + 5 * k) % 7)
+    s = np.array([0.5, 1.25, 2.0], np.float32)
+    _, _, comb = O.hc_split_sinkhorn(m, s, b, 4, iters=1, eps=0.0)
+    want = _comb_one_round(m[0], s, b, lambda j, k: 4 * j + k, 2)
+    np.testing.assert_allclose(comb[0], want, rtol=0, atol=1e-7)
+    # the routing the pages do not use is told apart by far more than the tolerance
+    wrong = [_comb_one_round(m[0], s, b, lambda j, k: 4 * k + j, 2),      # transposed logits
+             _comb_one_round(m[0], s, b, lambda j, k: 4 * j + k, 0),      # hc_scale[0]
+             _comb_one_round(m[0], s, b, lambda j, k: 4 * j + k, 1)]      # hc_scale[1]
+    for w in wrong:
+        assert np.abs(w - comb[0]).max() > 1e-2
+    # the final step normalises columns: each column of the comb sums to 1 (eps = 0)
+    np.testing.assert_allclose(comb[0].sum(axis=0), np.ones(4), atol=1e-6)
+
+
+# ------------------------------------------------------------ the reading-mix lag
+def _forcing_params(d, read_next, rng_, post_base=None):
+    """A parameter set whose pre is one-hot on stream read_next to within
+    sigmoid(-50) (offsets +-50 on the pre slice, far beyond any s0 * m here);
+    post offsets -3, -1, 1, 3 (or post_base for all) and a comb near the
+    identity (offsets +-10), so that the streams a write leaves stay distinct."""
+    fn = (rng_.standard_normal((24, 4 * d)) * 0.02).astype(np.float32)
+    base = np.zeros(24, np.float32)
+    base[:4] = -50.0
+    base[read_next] = 50.0
+    base[4:8] = [-3.0, -1.0, 1.0, 3.0] if post_base is None else post_base
+    base[8:] = np.where(np.eye(4, dtype=bool), 10.0, -10.0).reshape(16)
+    scale = np.array([1.0, 1.5, 0.8], np.float32)
+    return fn, base, scale
+
+
+def test_block_attention_reads_incoming_pre_ffn_reads_attention_pre():
+    """"Source layer, pairs pooled", Block.forward: attention reads the streams
+    with the incoming mix; the feed-forward reads the attention's new streams
+    with the pre the attention's hc_mixes produced (from the old streams);
+    the block hands on the feed-forward's own pre.  With the incoming mix on
+    stream 0, the attention's pre forced onto stream 1 and the feed-forward's
+    onto stream 2: the attention read is stream 0 bit for bit, the feed-forward
+    read is stream 1 of X' (to eps * sum_j |X'_j| and a bf16 ulp), and the block
+    hands on pre = e_2 + eps."""
+    g = np.random.default_rng(31)
+    n, d = 6, 64
+    x = synth.f64_to_bf16_bits(g.standard_normal((n, 4, d)))
+    da = synth.f64_to_bf16_bits(g.standard_normal((n, d)))
+    df = synth.f64_to_bf16_bits(g.standard_normal((n, d)))
+    pre0 = np.zeros((n, 4), np.float32)
+    pre0[:, 0] = 1.0
+    attn, ffn = _forcing_params(d, 1, g), _forcing_params(d, 2, g)
+    out = O.block(x=x, pre_in=pre0, delta_attn=da, delta_ffn=df, attn=attn, ffn=ffn)
+    assert np.array_equal(out["attn"]["y"], x[:, 0])
+    eps = float(np.float32(1e-6))
+    np.testing.assert_allclose(out["attn"]["pre"], np.tile([eps, 1 + eps, eps, eps], (n, 1)), atol=2e-7)
+    xp = out["ffn"]["x_out"]
+    assert np.array_equal(xp, O.hc_post(da, x, out["attn"]["post"], out["attn"]["comb"]))
+    yf = N.bits_to_f64(out["ffn"]["y"])
+    X = N.bits_to_f64(xp)
+    tol = N.bf16_ulp(X[:, 1]) + 1.1e-6 * np.abs(X).sum(axis=1)
+    assert (np.abs(yf - X[:, 1]) <= tol).all()
+    for other in (0, 2, 3):                         # any other lag reads another stream
+        assert (np.abs(yf - X[:, other]) > tol).any()
+    np.testing.assert_allclose(out["pre_out"], np.tile([eps, eps, 1 + eps, eps], (n, 1)), atol=2e-7)
+
+
+def _norm_close(got_bits, xs, col, gamma, eps, X):
+    """|got - RMSNorm(stream col of xs)| within the bound of a read that is
+    stream col to eps * sum_j |X_j| and an ulp, carried through the norm."""
+    want = N.bits_to_f64(O.rms_norm(xs[:, col], gamma, eps))
+    r = 1 / np.sqrt((X[:, col] ** 2).mean(axis=-1, keepdims=True) + float(np.float32(eps)))
+    tol = 2 * N.bf16_ulp(want) + (N.bf16_ulp(X[:, col]) + 1.1e-6 * np.abs(X).sum(axis=1)) * r * np.abs(gamma) * 1.01
+    return np.abs(N.bits_to_f64(got_bits) - want) <= tol
+
+
+def test_stack_lag_over_depth_and_exit():
+    """"Final RMSNorm", Transformer.forward, with the stand-in sublayer: the
+    entry reads the four copies with 0.25 each (the embedding); sublayer s >= 1
+    reads its new streams with the pre of sublayer s-1; the exit writes, then
+    reads with the last sublayer's pre.  Each sublayer's pre is forced onto
+    stream s+1, so sublayer s reads stream s of its new streams and the exit
+    stream 3 of the final ones; any other lag reads another stream."""
+    g = np.random.default_rng(47)
+    n, d, depth = 5, 64, 3
+    h = synth.f64_to_bf16_bits(g.standard_normal((n, d)))
+    params = [_forcing_params(d, (s + 1) % 4, g) for s in range(depth)]
+    gammas = [(1 + g.standard_normal(d) * 0.1).astype(np.float32) for _ in range(depth)]
+    gf = (1 + g.standard_normal(d) * 0.1).astype(np.float32)
+    rec = []
+    out = O.stack(h=h, params=params, gammas=gammas, gamma_final=gf, record=rec)
+    assert np.array_equal(rec[0][1], O.rms_norm(h, gammas[0], 1e-6))
+    for s in range(1, depth):
+        xs, ys = rec[s][0], rec[s][1]
+        X = N.bits_to_f64(xs)
+        assert _norm_close(ys, xs, s, gammas[s], 1e-6, X).all(), s
+        for other in set(range(4)) - {s}:
+            assert not _norm_close(ys, xs, other, gammas[s], 1e-6, X).all(), (s, other)
+    xf = out["x_out"]
+    X = N.bits_to_f64(xf)
+    assert _norm_close(out["z"], xf, 3, gf, 1e-20, X).all()
+    for other in (0, 1, 2):
+        assert not _norm_close(out["z"], xf, other, gf, 1e-20, X).all()
+
+
+def test_stack_exit_norm_eps():
+    """The exit's RMSNorm takes eps 1e-20 ("Final RMSNorm" equation): with a tiny
+    embedding (2^-20 scale) and the write offsets making post ~ 1e-22, the
+    streams stay tiny to the end, and the final row still comes out at unit
+    RMS (eps 1e-6 would shrink it to ~1e-6)."""
+    g = np.random.default_rng(53)
+    n, d, depth = 4, 64, 3
+    h = synth.f64_to_bf16_bits(g.standard_normal((n, d)) * 2.0 ** -20)
+    params = [_forcing_params(d, (s + 1) % 4, g, post_base=-50.0) for s in range(depth)]
+    gammas = [(1 + g.standard_normal(d) * 0.1).astype(np.float32) for _ in range(depth)]
+    gf = (1 + g.standard_normal(d) * 0.1).astype(np.float32)
+    out = O.stack(h=h, params=params, gammas=gammas, gamma_final=gf)
+    assert np.abs(N.bits_to_f64(out["x_out"])).max() < 2.0 ** -10
+    z = N.bits_to_f64(out["z"])
+    ms = ((z / gf.astype(np.float64)) ** 2).mean(axis=-1)
+    np.testing.assert_allclose(ms, 1.0, rtol=2e-2)
+
+
 # ------------------------------------------------------------ stack entry and the MTP tap
 def test_expand_streams_copies_the_embedding():
     h = rand_bf16((5, 32))
