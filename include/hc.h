@@ -108,11 +108,33 @@ int hc_fn_pack(const float* hc_fn, int hc, int d, void* fn_packed, void* stream)
  * and counting itself in on the tile's arrival word; the last slice of a tile
  * to arrive sums them in slice order (the same bits whichever slice it is)
  * and derives mixes, pre/post and the comb ("Reading weights").  No workgroup
- * waits for another to start.  Byte 4160 of the workspace holds a sticky error
- * mask, bit 0 set if a word the last slice waited for never became visible
- * (the call then finishes with wrong results instead of hanging).
+ * waits for another to start.  A word the last slice waits for that never
+ * becomes visible sets bit 0 of the workspace's error mask (see
+ * hc_workspace_status); the call then finishes with wrong results instead of
+ * hanging.  The workspace holds a control block (the error mask and the
+ * schedules' call counters), the decode schedule's words and the read-row
+ * exchange's words at the same place whatever (n, hc, d), then the per-slice
+ * sums of the two-launch schedule (or of hc = 2, 8).
  * ------------------------------------------------------------------------- */
 size_t hc_workspace_bytes(int64_t n, int hc, int d);
+
+/* The workspace's regions for a call of shape (n, hc, d), as byte offsets and
+ * sizes in regions[0..7]: the control block, the decode schedule's tagged
+ * words, the read-row exchange's tagged words (these three at the same place
+ * and size for every shape, so that no call writes another schedule's
+ * persistent words), then the per-slice sums of this shape.  Their end is
+ * hc_workspace_bytes (for n > 0).  HC_EINVAL / HC_ENOTSUP as hc_workspace_bytes
+ * would return 0. */
+int hc_workspace_layout(int64_t n, int hc, int d, size_t regions[8]);
+
+/* Reads a workspace's sticky error mask into *mask (host memory), after the
+ * work already enqueued on stream has finished (the call synchronises the
+ * stream): bit 0 set means that some earlier call on this workspace waited for
+ * another workgroup's words until its bound and then finished with wrong
+ * values.  With clear != 0 the mask is then reset to zero by work enqueued on
+ * stream.  HC_EINVAL for a NULL or misaligned workspace, fewer than 8192 bytes,
+ * or a NULL mask; HC_EHIP if the copy fails. */
+int hc_workspace_status(void* workspace, size_t workspace_bytes, int clear, uint32_t* mask, void* stream);
 
 /* ---------------------------------------------------------------------------
  * hc_mixes -- "Source layer, pairs pooled", Block.hc_mixes.
@@ -195,41 +217,32 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
  * x_out must not overlap x; y_out must not overlap x, x_out or delta.
  * workspace/workspace_bytes: required when fn_packed != NULL, see
  * hc_workspace_bytes (hc_boundary_workspace_bytes returns the same size).
- * flags: 0, HC_BOUNDARY_SINGLE_LAUNCH for the single-launch schedule (below),
- * HC_BOUNDARY_X_EXPANDED for an expanded x (below); a caller built against a
- * header without this field passes the shorter struct_size and gets 0.
+ * flags: 0, or HC_BOUNDARY_* bits (below); a caller built against a header
+ * without this field passes the shorter struct_size and gets 0.
  *
- * HC_BOUNDARY_SINGLE_LAUNCH (hc = 4, d a multiple of 512, at least 1024): the whole
- * call as one persistent launch that keeps X' on chip for the read row instead
- * of re-reading it, the feature slices of a token tile exchanging per-token
- * partial sums through the workspace as tagged words (the first 8 KB of the
- * workspace are its control block; byte 4160 holds the sticky error mask, bit
- * 0 set if a wait for another workgroup's words timed out, the call then
- * finishing with wrong results instead of hanging).  One call at a time per
- * workspace.  Same results as the default schedule within the stated
- * tolerances (the projection is summed over other feature slices).  Measured
- * slower than the default on MI355X at every n tried (32..4096).
+ * Schedules (hc = 4).  With a given pre_in and gamma, when the feature slices
+ * of a token tile are 640 or 1280 features wide (d = 5120 with n from 2048
+ * to 4096, or in general d / S for the slice count S the call picks), the call
+ * is one launch: each slice keeps its read row on chip, the slices of a tile
+ * exchange their per-token sums through the workspace as tagged words, and the
+ * RMSNorm is applied without writing y first.  Otherwise, with a given pre_in
+ * and no gamma and n <= 128, the decode schedule of hc_workspace_bytes runs;
+ * and in every other case two launches: a streaming pass (X', the read row of
+ * a given pre, per-slice sums) and a finish (mixes, pre/post/comb, and the read
+ * row where it depends on them or on its RMSNorm).  A wait for another
+ * workgroup's words that times out sets bit 0 of the workspace's error mask
+ * (hc_workspace_status) and the call finishes with wrong values instead of
+ * hanging; one call at a time per workspace.
  * ------------------------------------------------------------------------- */
-#define HC_BOUNDARY_SINGLE_LAUNCH 1u
 /* x is [n, d] and every one of the hc streams is that row: the stack entry
  * ("Final RMSNorm", the model driver copies the embedding into hc streams)
  * without materialising the copies.  With delta the call writes the real
  * streams to x_out; without, it derives the mixes of the copies and reads
- * them.  Not with HC_BOUNDARY_SINGLE_LAUNCH. */
+ * them. */
 #define HC_BOUNDARY_X_EXPANDED 4u
-/* HC_BOUNDARY_SLICE_RESIDENT (hc = 4, d = 5120, delta and fn_packed given,
- * pre_in NULL): the whole call as one launch of one workgroup per compute unit
- * (it needs all 256 compute units of an MI355X, else HC_ENOTSUP), every
- * workgroup keeping one 160-feature slice of the projection weights in LDS and
- * the new streams of its last token tiles in registers, so X and delta are read
- * once and X' is never read back.  The slices of a token tile exchange
- * per-token partial sums through the workspace (a fixed region after the
- * control block and the decode region; bounded waits: a timeout sets bit 0 of
- * the error mask at byte 4160 and the call finishes with wrong values instead
- * of hanging).  One call at a time per workspace.  Same results as the default
- * schedule within the stated tolerances (the projection is summed over other
- * feature slices).  Not with HC_BOUNDARY_SINGLE_LAUNCH. */
-#define HC_BOUNDARY_SLICE_RESIDENT 8u
+/* Always the two-launch schedule (the one hc_boundary_begin / _end run):
+ * never the decode schedule nor the one-launch read-row exchange. */
+#define HC_BOUNDARY_TWO_LAUNCH 16u
 
 typedef struct hc_boundary_args {
   uint32_t struct_size; /* = sizeof(hc_boundary_args) */
@@ -258,7 +271,7 @@ typedef struct hc_boundary_args {
    * or x at a block entry), the MTP head's tap of a block's input ("Final
    * RMSNorm", the model driver); the streams summed in fp32 in stream order
    * (((X'_0 + X'_1) + X'_2) + X'_3 at hc = 4), times 1/hc, rounded to bf16.
-   * Not with HC_BOUNDARY_SINGLE_LAUNCH.  A caller built against a header
+   * A caller built against a header
    * without this field passes the shorter struct_size. */
   hc_bf16* x_mean_out;
 } hc_boundary_args;

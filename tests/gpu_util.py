@@ -68,14 +68,12 @@ def write_floor(delta_bits, x_bits, tol=N.COEF_ABS_TOL):
     return (tol * (D + X))[:, None, :] * 1.0001
 
 
-ERR_WORD_BYTE = 4160    # sticky error mask in the workspace control block (bit 0: a wait timed out)
-
-
 def assert_workspace_clean(got):
-    """The single-launch boundary's error mask in the call's workspace is zero."""
+    """The error mask of the call's workspace (hc_workspace_status) is zero: no
+    wait for another workgroup's words ran into its bound."""
+    from transformer_hyper_connection_amd import hc as H
     ws = got.get("workspace") if isinstance(got, dict) else got
     if ws is None:
         return
-    torch.cuda.synchronize()
-    mask = int(ws[ERR_WORD_BYTE:ERR_WORD_BYTE + 4].cpu().numpy().view(np.uint32)[0])
+    mask = H.workspace_status(ws)
     assert mask == 0, f"workspace error mask {mask:#x}"

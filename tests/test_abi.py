@@ -79,21 +79,57 @@ def test_packed_and_workspace_bytes(L):
     assert L.hc_workspace_bytes(0, 4, 5120) == 0
     assert L.hc_workspace_bytes(4096, 3, 5120) == 0
     w = L.hc_workspace_bytes(4096, 4, 5120)
-    # 8 KB control block; decode region (fixed for d): 256 B of arrival words + 8 tiles x 20 slices
-    # x 16 tokens x 25 tagged 8-byte words; slice-resident ring (d = 5120 only): 8 XCDs x 16 slots
-    # x 32 slices x 16 tokens x 48 tagged record words (36 used), and 8 XCDs x 16 slots x 16 tokens x 8
-    # read-coefficient words; single-launch records: 256 tiles of
-    # 16 tokens x 10 slices x 34 tagged words; two-launch records: 64 tiles of 64 tokens x 4 slices
-    # x 36 floats
-    decode = 256 + 8 * 20 * 16 * 25 * 8
-    ring = 8 * 16 * 32 * 16 * 48 * 8 + 8 * 16 * 16 * 8 * 8
-    assert w == 8192 + decode + ring + 256 * 10 * 16 * 34 * 8 + 64 * 4 * 64 * 36 * 4
-    # n = 128: 8 single-launch tiles; two-launch: 2 tiles x 40 slices
-    assert L.hc_workspace_bytes(128, 4, 5120) == 8192 + decode + ring + 8 * 10 * 16 * 34 * 8 + 2 * 40 * 64 * 36 * 4
+    # 8 KB control block; decode words: 8 tiles x (8192/256) slices x 16 tokens x 25 tagged 8-byte words;
+    # read-row exchange words: 256 groups x 64 tokens x 26 tagged words; then the two-launch records:
+    # 64 tiles of 64 tokens x 4 slices x 36 floats
+    fixed = 8192 + 8 * 32 * 16 * 25 * 8 + 256 * 64 * 26 * 8
+    assert w == fixed + 64 * 4 * 64 * 36 * 4
+    # n = 128: 2 tiles x 40 slices
+    assert L.hc_workspace_bytes(128, 4, 5120) == fixed + 2 * 40 * 64 * 36 * 4
     assert L.hc_boundary_workspace_bytes(4096, 4, 5120) == w
     assert L.hc_workspace_bytes(4097, 4, 5120) > w
-    # widths the single launch does not take (d % 512 != 0): control block + two-launch records only
-    assert L.hc_workspace_bytes(64, 4, 320) == 8192 + 1 * 5 * 64 * 36 * 4
+    assert L.hc_workspace_bytes(64, 4, 320) == fixed + 1 * 5 * 64 * 36 * 4
+
+
+def _layout(L, n, hc, d):
+    r = (ctypes.c_size_t * 8)()
+    assert L.hc_workspace_layout(n, hc, d, r) == H.HC_OK
+    return list(r)
+
+
+def test_workspace_layout_regions_never_overlap(L):
+    """Every shape's workspace: the control block, the decode words and the
+    exchange words sit at one place and size whatever (n, hc, d), so no call's
+    per-slice sums (or any other region) can lie on another schedule's
+    persistent words; the regions are disjoint and end at hc_workspace_bytes."""
+    base = _layout(L, 1, 4, 64)[:6]
+    assert base[0] == 0 and base[1] == 8192
+    # the decode words hold 8 tiles x (8192/256) slices x 16 tokens x 25 words; the
+    # exchange words 256 groups x 64 tokens x 26 words
+    assert base[3] >= 8 * (8192 // 256) * 16 * 25 * 8
+    assert base[5] >= 256 * 64 * 26 * 8
+    ns = (1, 17, 128, 129, 2048, 3000, 4096, 4097, 32768)
+    for hc in (2, 4, 8):
+        for d in range(64, 32768 + 1, 64):
+            for n in ns if d % 1024 == 0 else (1, 4096):
+                r = _layout(L, n, hc, d)
+                assert r[:6] == base, (n, hc, d)
+                spans = sorted((r[i], r[i] + r[i + 1]) for i in range(0, 8, 2))
+                for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
+                    assert a1 <= b0, (n, hc, d, spans)
+                assert r[6] + r[7] == L.hc_workspace_bytes(n, hc, d), (n, hc, d)
+    bad = (ctypes.c_size_t * 8)()
+    assert L.hc_workspace_layout(16, 3, 5120, bad) == H.HC_ENOTSUP
+    assert L.hc_workspace_layout(-1, 4, 5120, bad) == H.HC_EINVAL
+    assert L.hc_workspace_layout(16, 4, 5120, None) == H.HC_EINVAL
+
+
+def test_workspace_status_validates(L):
+    mask = ctypes.c_uint32(7)
+    assert L.hc_workspace_status(None, 1 << 20, 0, ctypes.byref(mask), S) == H.HC_EINVAL
+    assert L.hc_workspace_status(MIS, 1 << 20, 0, ctypes.byref(mask), S) == H.HC_EINVAL
+    assert L.hc_workspace_status(P, 4096, 0, ctypes.byref(mask), S) == H.HC_EINVAL      # smaller than the control block
+    assert L.hc_workspace_status(P, 1 << 20, 0, None, S) == H.HC_EINVAL
 
 
 def test_packed_and_workspace_bytes_other_hc(L):
@@ -102,29 +138,11 @@ def test_packed_and_workspace_bytes_other_hc(L):
     assert L.hc_fn_packed_bytes(8, 4096) == (8 * 4096 // 32) * 15 * 1024
     assert L.hc_fn_packed_bytes(8, 100) == 0
     assert L.hc_fn_packed_bytes(16, 4096) == 0
-    # records [S][n][recw] after the hc = 4 control block and decode region of the same d; S is the
-    # largest divisor of hc*d/64 with at most ~512 workgroups of 128 tokens, 64 at most; recw = mix + 1
-    # rounded up to 4 floats (12 at hc = 2, 84 at hc = 8)
-    decode = 256 + 8 * 20 * 16 * 25 * 8
-    ring = 8 * 16 * 32 * 16 * 48 * 8 + 8 * 16 * 16 * 8 * 8   # slice-resident ring at d = 5120
-    assert L.hc_workspace_bytes(4096, 8, 5120) == 8192 + decode + ring + 16 * 4096 * 84 * 4
-    assert L.hc_workspace_bytes(100, 2, 320) == 8192 + 10 * 100 * 12 * 4     # 10 chunks of 64: S = 10
-    assert L.hc_workspace_bytes(40, 8, 1024) == 8192 + (256 + 8 * 4 * 16 * 25 * 8) + 64 * 40 * 84 * 4
-    assert L.hc_workspace_bytes(0, 8, 5120) == 0
-    assert L.hc_boundary_workspace_bytes(7, 2, 1024) == L.hc_workspace_bytes(7, 2, 1024)
-
-
-@pytest.mark.parametrize("hc,d,code", [(3, 5120, H.HC_ENOTSUP), (16, 5120, H.HC_ENOTSUP), (1, 64, H.HC_ENOTSUP),
-                                       (4, 100, H.HC_ENOTSUP), (2, 100, H.HC_ENOTSUP), (8, 0, H.HC_ENOTSUP),
-                                       (4, 0, H.HC_ENOTSUP), (4, 5152, H.HC_ENOTSUP),
-                                       (4, 32832, H.HC_ENOTSUP)])
-def test_unsupported_shapes(L, hc, d, code):
-    assert L.hc_pre(P, P, 16, hc, d, P, S) == code
-    assert L.hc_post(P, P, P, P, 16, hc, d, P, S) == code
-    assert L.hc_mixes(P, P, 16, hc, d, 1e-6, P, None, None, 20, 1e-6, None, None, None, P, 1 << 30, S) == code
-    assert L.hc_fn_pack(P, hc, d, P, S) == code
-    assert L.hc_last_error()
-
+    # records [S][n][recw] after the fixed regions; S is the largest divisor of hc*d/64 with at most
+    # ~512 workgroups of 128 tokens, 64 at most; recw = mix + 1 rounded up to 4 floats (12 at hc = 2,
+    # 84 at hc = 8)
+    fixed = 8192 + 8 * 32 * 16 * 25 * 8 + 256 * 64 * 26 * 8
+    assert L.hc_workspace_bytes(4096, 8, 5120) == fixed + 16 * 4096 * 84 * 4
 
 def test_null_misaligned_negative(L):
     assert L.hc_pre(None, P, 16, 4, 64, P, S) == H.HC_EINVAL
@@ -158,11 +176,13 @@ def _args(**kw):
     a.struct_size = ctypes.sizeof(H.BoundaryArgs)
     a.hc, a.d, a.iters, a.n = 4, 64, 20, 16
     a.hc_eps = a.norm_eps = a.rms_eps = 1e-6
-    a.x, a.y_out = P, P + 0x100
-    a.delta, a.post_in, a.comb_in, a.x_out = P + 0x200, P + 0x300, P + 0x400, P + 0x500
-    a.pre_in = P + 0x600
-    a.fn_packed, a.hc_base, a.hc_scale = P + 0x700, P + 0x800, P + 0x900
-    a.pre_out, a.post_out, a.comb_out = P + 0xA00, P + 0xB00, P + 0xC00
+    # the streams far apart (no overlap at the test shapes), the small tensors after them
+    a.x, a.y_out = P, P + 0x400000
+    a.delta, a.x_out = P + 0x800000, P + 0xC00000
+    a.post_in, a.comb_in = P + 0x1000000, P + 0x1001000
+    a.pre_in = P + 0x1002000
+    a.fn_packed, a.hc_base, a.hc_scale = P + 0x1003000, P + 0x1004000, P + 0x1005000
+    a.pre_out, a.post_out, a.comb_out = P + 0x1006000, P + 0x1007000, P + 0x1008000
     for k, v in kw.items():
         setattr(a, k, v)
     return a
@@ -184,32 +204,34 @@ def test_boundary_validation(L):
     assert call(_args(n=0)) == H.HC_OK
     assert call(_args(n=0, delta=None, post_in=None, comb_in=None, x_out=None)) == H.HC_OK
     assert call(_args(d=10304, gamma=P + 0xD00)) == H.HC_ENOTSUP   # RMSNorm row too long
-    # the single-launch schedule flag: unknown bits, shapes it does not take, no halves
-    SL, XE = H.HC_BOUNDARY_SINGLE_LAUNCH, H.HC_BOUNDARY_X_EXPANDED
-    assert call(_args(flags=16)) == H.HC_EINVAL
-    assert call(_args(flags=SL | XE, d=1024)) == H.HC_ENOTSUP            # no expanded x in the single launch
-    assert call(_args(flags=SL, d=1024, x_mean_out=P + 0xE00)) == H.HC_ENOTSUP   # nor the stream mean
+    # flags: the expanded-x bit and the two-launch bit; every other bit is rejected, the
+    # bits of the schedules this library no longer has included
+    XE, TL = H.HC_BOUNDARY_X_EXPANDED, H.HC_BOUNDARY_TWO_LAUNCH
+    for bad in (1, 2, 8, 32, 1 << 31):
+        assert call(_args(flags=bad)) == H.HC_EINVAL
+    assert call(_args(flags=XE | TL, n=0)) == H.HC_OK
     assert call(_args(x_mean_out=MIS)) == H.HC_EINVAL                    # misaligned stream-mean output
-    assert call(_args(flags=SL)) == H.HC_ENOTSUP                  # d=64: not a multiple of 512
-    assert call(_args(flags=SL, d=512)) == H.HC_ENOTSUP           # at least 1024
-    assert call(_args(flags=SL, d=1024, fn_packed=None, pre_in=P + 0x600)) == H.HC_EINVAL   # needs the mixes
-    assert call(_args(flags=SL, d=1024, hc=8)) == H.HC_ENOTSUP    # hc = 4 only
-    assert L.hc_boundary_begin(ctypes.byref(_args(flags=SL, d=1024)), S) == H.HC_EINVAL
-    # the slice-resident schedule: hc = 4, d = 5120, a write, the mixes, the fresh pre; one launch
-    SR = H.HC_BOUNDARY_SLICE_RESIDENT
-    assert call(_args(flags=SR | SL, d=5120, pre_in=None)) == H.HC_EINVAL        # one schedule at a time
-    assert call(_args(flags=SR, d=1024, pre_in=None)) == H.HC_ENOTSUP            # d = 5120 only
-    assert call(_args(flags=SR, d=5120, hc=8, pre_in=None)) == H.HC_ENOTSUP      # hc = 4 only
-    assert call(_args(flags=SR, d=5120)) == H.HC_ENOTSUP                         # a given pre
-    assert call(_args(flags=SR, d=5120, pre_in=None, delta=None, post_in=None, comb_in=None,
-                      x_out=None)) == H.HC_ENOTSUP                               # a block entry
-    assert call(_args(flags=SR, d=5120, pre_in=None, x_mean_out=P + 0xE00)) == H.HC_ENOTSUP
-    assert call(_args(flags=SR | XE, d=5120, pre_in=None)) == H.HC_ENOTSUP
-    assert L.hc_boundary_begin(ctypes.byref(_args(flags=SR, d=5120, pre_in=None)), S) == H.HC_EINVAL
-    assert call(_args(flags=SR, d=5120, pre_in=None, n=0)) == H.HC_OK
+    # outputs overlapping the streams they are formed from, or each other, by any range
+    n, d = 16, 64
+    xb, rb = n * 4 * d * 2, n * d * 2                                   # x / x_out bytes, delta / y bytes
+    X0, XO, Y0, D0 = P, P + 0x100000, P + 0x200000, P + 0x300000
+    ok = dict(x=X0, x_out=XO, y_out=Y0, delta=D0)
+    assert call(_args(**ok, n=0)) == H.HC_OK
+    assert call(_args(**{**ok, "x_out": X0 + xb - 16})) == H.HC_EINVAL   # x_out's head on x's tail
+    assert call(_args(**{**ok, "x_out": X0 - xb + 16})) == H.HC_EINVAL   # x_out's tail on x's head
+    assert call(_args(**{**ok, "x_out": D0 + 16})) == H.HC_EINVAL        # x_out on delta
+    assert call(_args(**{**ok, "y_out": X0 + 32})) == H.HC_EINVAL        # y_out inside x
+    assert call(_args(**{**ok, "y_out": XO + xb - 16})) == H.HC_EINVAL   # y_out on x_out's tail
+    assert call(_args(**{**ok, "y_out": D0 + rb - 16})) == H.HC_EINVAL   # y_out on delta
+    assert call(_args(**{**ok, "x_mean_out": Y0 + 16})) == H.HC_EINVAL   # the stream mean on y_out
+    assert call(_args(**{**ok, "x_out": X0 + xb})) in (H.HC_ENODEV, H.HC_OK)      # adjacent is fine
+    assert call(_args(**{**ok, "y_out": XO + xb})) in (H.HC_ENODEV, H.HC_OK)
+    # expanded x is [n, d]: an x_out right after it does not overlap
+    assert call(_args(**{**ok, "x_out": X0 + rb}, flags=XE)) in (H.HC_ENODEV, H.HC_OK)
+    assert call(_args(**{**ok, "x_out": X0 + rb - 16}, flags=XE)) == H.HC_EINVAL
     # a caller of the struct without the trailing flags field (shorter struct_size) gets flags 0
     short = H.BoundaryArgs.flags.offset
-    assert call(_args(struct_size=short, flags=16)) in (H.HC_ENODEV, H.HC_OK)
+    assert call(_args(struct_size=short, flags=1)) in (H.HC_ENODEV, H.HC_OK)
     # ... and without the trailing x_mean_out field, no stream mean
     assert call(_args(struct_size=H.BoundaryArgs.x_mean_out.offset, x_mean_out=MIS)) in (H.HC_ENODEV, H.HC_OK)
     assert call(_args(struct_size=short - 8)) == H.HC_EINVAL
@@ -224,4 +246,4 @@ def test_no_device_reported_without_gpu(L):
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is visible")
-    assert L.hc_pre(P, P, 16, 4, 64, P + 0x100, S) == H.HC_ENODEV
+    assert L.hc_pre(P, P + 0x400000, 16, 4, 64, P + 0x800000, S) == H.HC_ENODEV

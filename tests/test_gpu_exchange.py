@@ -1,0 +1,137 @@
+"""GPU parity of the one-launch boundary with a given pre and the RMSNorm
+(the read-row exchange: each feature slice keeps its read row on chip and the
+slices of a token tile exchange their per-token sums through the workspace),
+against the oracle on every token; the workspace's call epoch, its sharing with
+the other schedules, and its error mask (hc_workspace_status)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import hc_oracle as O
+from tests.gpu_util import (DEV, assert_bits_equal, assert_coef_close, assert_mixes_close, assert_workspace_clean,
+                            bf16_dev, f32_dev, host_bits, host_f32, say)
+from tests.test_gpu_parity import _check_boundary, packed
+from transformer_hyper_connection_amd import hc as H
+from transformer_hyper_connection_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+CTL_X_EPOCH = 16          # u64 index of the exchange's call epoch in the workspace control block
+
+
+def _inputs(n, entry=False):
+    s = synth.boundary_inputs("prefill", 0, n)
+    kw = dict(x=s["x"], pre_in=s["pre_in"], gamma=s["gamma"], hc_fn=s["hc_fn"], hc_base=s["hc_base"],
+              hc_scale=s["hc_scale"])
+    if not entry:
+        kw.update(delta=s["delta"], post_in=s["post_in"], comb_in=s["comb_in"])
+    dev = {k: (bf16_dev(v) if v.dtype == np.uint16 else f32_dev(v)) for k, v in kw.items() if k != "hc_fn"}
+    dev["fn_packed"] = packed(kw["hc_fn"])
+    return s, kw, dev
+
+
+def _epoch(ws):
+    torch.cuda.synchronize()
+    return int(ws[8 * CTL_X_EPOCH:8 * CTL_X_EPOCH + 8].cpu().numpy().view(np.uint64)[0])
+
+
+# n = 2048 and 3000: slices of 640 features (8 per tile; 3000 leaves a ragged
+# last tile); 4096: slices of 1280 (4 per tile); 4097: 65 tiles x 4 slices,
+# more groups than the exchange holds, so the two launches run instead
+@pytest.mark.parametrize("n", [2048, 3000, 4096, 4097])
+def test_exchange_every_token(n):
+    say(f"[exchange] n={n}: every token")
+    s, kw, dev = _inputs(n)
+    x = dev.pop("x")
+    got = H.hc_boundary(x, **dev, want_mixes=True, want_mean=True)
+    torch.cuda.synchronize()
+    assert_workspace_clean(got)
+    ref = O.boundary(**kw, want_mean=True)
+    _check_boundary(ref, got, s, False, True)
+    assert_bits_equal(host_bits(got["x_mean"]), ref["x_mean"], "stream mean")
+
+
+@pytest.mark.parametrize("expanded", [False, True])
+def test_exchange_block_entry(expanded):
+    """The block entry (no write) in one launch, the streams as given or the
+    embedding expanded to four streams."""
+    say(f"[exchange] entry n=4096 expanded={expanded}")
+    s, kw, dev = _inputs(4096, entry=True)
+    x = dev.pop("x")
+    if expanded:
+        h = s["x"][:, 0]
+        kw["x"], x = h, bf16_dev(h)
+        got = H.hc_boundary(x, **dev, want_mixes=True, x_expanded=True)
+        ref = O.boundary(**kw, x_expanded=True)
+    else:
+        got = H.hc_boundary(x, **dev, want_mixes=True)
+        ref = O.boundary(**kw)
+    torch.cuda.synchronize()
+    assert got["x_out"] is None
+    assert_workspace_clean(got)
+    _check_boundary(ref, got, {"x": O.expand_streams(kw["x"]) if expanded else s["x"], "gamma": s["gamma"]},
+                    False, True)
+
+
+def test_exchange_matches_two_launches():
+    """The same call in one launch and in two: identical streams and read row
+    (the same sum y^2 per slice, summed in the same slice order); the mixes and
+    coefficients within the parity bars of each other (the two launches add
+    each chunk's projection partial sums in fp64, the one launch in fp32)."""
+    say("[exchange] one launch vs two, n=2048")
+    s, kw, dev = _inputs(2048)
+    x = dev.pop("x")
+    one = H.hc_boundary(x, **dev, want_mixes=True)
+    two = H.hc_boundary(x, **dev, want_mixes=True, two_launch=True)
+    torch.cuda.synchronize()
+    for k in ("x_out", "y"):
+        assert_bits_equal(host_bits(one[k]), host_bits(two[k]), k)
+    assert_mixes_close(host_f32(one["mixes"]), host_f32(two["mixes"]).astype(np.float64))
+    for k in ("pre", "post", "comb"):
+        assert_coef_close(host_f32(one[k]), host_f32(two[k]), k)
+
+
+def test_exchange_repeated_calls_and_shared_workspace():
+    """Calls on one workspace: each one-launch call advances the exchange's call
+    epoch by one and gives the same bits; decode, two-launch and other-width
+    calls in between leave it intact."""
+    say("[exchange] repeated calls, shared workspace")
+    s, kw, dev = _inputs(4096)
+    x = dev.pop("x")
+    ref = O.boundary(**kw)
+    ws = torch.zeros(H.lib().hc_workspace_bytes(4096, 4, 5120), dtype=torch.uint8, device=DEV)
+    first, e0 = None, _epoch(ws)
+    small, skw, sdev = _inputs(64)
+    sx = sdev.pop("x")
+    for rep in range(4):
+        got = H.hc_boundary(x, **dev, want_mixes=True, out={"workspace": ws})
+        assert _epoch(ws) == e0 + rep + 1
+        cur = {k: host_bits(got[k]) if got[k].dtype == torch.bfloat16 else host_f32(got[k])
+               for k in ("x_out", "y", "pre", "post", "comb", "mixes")}
+        if first is None:
+            first = cur
+            _check_boundary(ref, got, s, False, True)
+        else:
+            for k in cur:
+                assert np.array_equal(cur[k], first[k]), f"call {rep}: {k} differs from call 0"
+        # other schedules on the same workspace: the decode schedule (n = 64, no RMSNorm),
+        # the two launches (fresh read) and another width
+        g1 = H.hc_boundary(sx, **{**sdev, "gamma": None}, want_mixes=True, out={"workspace": ws})
+        r1 = O.boundary(**{**skw, "gamma": None})
+        _check_boundary(r1, g1, small, False, False)
+        g2 = H.hc_boundary(sx, **{**sdev, "pre_in": None}, want_mixes=True, out={"workspace": ws})
+        r2 = O.boundary(**{**skw, "pre_in": None})
+        _check_boundary(r2, g2, small, True, True)
+    assert_workspace_clean(ws)
+
+
+def test_workspace_status_reads_and_clears():
+    """The error mask round trip through hc_workspace_status: a word set from
+    the host is read back, and cleared on request."""
+    say("[workspace status]")
+    ws = torch.zeros(H.lib().hc_workspace_bytes(64, 4, 5120), dtype=torch.uint8, device=DEV)
+    assert H.workspace_status(ws) == 0
+    ws[4160:4164] = torch.tensor([5, 0, 0, 0], dtype=torch.uint8, device=DEV)
+    assert H.workspace_status(ws) == 5
+    assert H.workspace_status(ws, clear=True) == 5
+    assert H.workspace_status(ws) == 0

@@ -149,7 +149,7 @@ def test_step_workload():
 
 
 # ------------------------------------------------------------------ fused boundary
-def _boundary_case(workload, t0, t1, fresh, norm, entry=False, exit_=False, d=None, single=False):
+def _boundary_case(workload, t0, t1, fresh, norm, entry=False, exit_=False, d=None, two=False):
     s = synth.boundary_inputs(workload, t0, t1) if d is None else synth.boundary_inputs(workload, t0, t1, d)
     kw = dict(x=s["x"], pre_in=None if fresh else s["pre_in"], gamma=s["gamma"] if norm else None)
     if not entry:
@@ -162,7 +162,7 @@ def _boundary_case(workload, t0, t1, fresh, norm, entry=False, exit_=False, d=No
     if "hc_fn" in kw:
         dev["fn_packed"] = packed(kw["hc_fn"])
     x = dev.pop("x")
-    got = H.hc_boundary(x, **dev, want_mixes=not exit_, single_launch=single)
+    got = H.hc_boundary(x, **dev, want_mixes=not exit_, two_launch=two)
     return ref, got, s
 
 
@@ -195,54 +195,28 @@ def _check_boundary(ref, got, s, fresh, norm):
         assert_bits_equal(y, ref["y"], "y")
 
 
-@pytest.mark.parametrize("single", [False, True])
+@pytest.mark.parametrize("two", [False, True])
 @pytest.mark.parametrize("fresh", [False, True])
 @pytest.mark.parametrize("norm", [False, True])
-def test_boundary_small(fresh, norm, single):
-    say(f"[boundary] prefill tokens 0..40 fresh={fresh} norm={norm} single_launch={single}")
-    ref, got, s = _boundary_case("prefill", 0, 40, fresh, norm, single=single)
+def test_boundary_small(fresh, norm, two):
+    say(f"[boundary] prefill tokens 0..40 fresh={fresh} norm={norm} two_launch={two}")
+    ref, got, s = _boundary_case("prefill", 0, 40, fresh, norm, two=two)
     _check_boundary(ref, got, s, fresh, norm)
 
 
-@pytest.mark.parametrize("single", [False, True])
 @pytest.mark.parametrize("n,d", [(1, 5120), (17, 1024), (23, 7168), (130, 2048)])
 @pytest.mark.parametrize("fresh", [False, True])
-def test_boundary_shapes(n, d, fresh, single):
-    """Other widths and ragged token counts, both schedules."""
-    say(f"[boundary] n={n} d={d} fresh={fresh} single_launch={single}")
-    ref, got, s = _boundary_case("prefill", 0, n, fresh, True, d=d, single=single)
+def test_boundary_shapes(n, d, fresh):
+    """Other widths and ragged token counts."""
+    say(f"[boundary] n={n} d={d} fresh={fresh}")
+    ref, got, s = _boundary_case("prefill", 0, n, fresh, True, d=d)
     _check_boundary(ref, got, s, fresh, True)
 
 
-def test_boundary_repeated_calls_one_workspace():
-    """Consecutive single-launch calls on one workspace (each call advances the
-    call tag the exchange words carry) give the same bits each time, with no
-    wait timed out."""
-    say("[boundary] 5 single-launch calls on one workspace, fresh read")
-    s = synth.boundary_inputs("prefill", 0, 70)
-    dev = dict(delta=bf16_dev(s["delta"]), post_in=f32_dev(s["post_in"]), comb_in=f32_dev(s["comb_in"]),
-               fn_packed=packed(s["hc_fn"]), hc_base=f32_dev(s["hc_base"]), hc_scale=f32_dev(s["hc_scale"]),
-               gamma=f32_dev(s["gamma"]))
-    X = bf16_dev(s["x"])
-    first = None
-    for rep in range(5):
-        got = H.hc_boundary(X, **dev, want_mixes=True, single_launch=True)
-        torch.cuda.synchronize()
-        assert_workspace_clean(got)
-        cur = {k: host_bits(got[k]) if got[k].dtype == torch.bfloat16 else host_f32(got[k])
-               for k in ("x_out", "y", "pre", "post", "comb", "mixes")}
-        if first is None:
-            first = cur
-        else:
-            for k in cur:
-                assert np.array_equal(cur[k], first[k]), f"call {rep}: {k} differs from call 0"
-
-
-@pytest.mark.parametrize("single", [False, True])
 @pytest.mark.parametrize("fresh", [False, True])
-def test_boundary_entry(fresh, single):
-    say(f"[boundary entry] fresh={fresh} single_launch={single}")
-    ref, got, s = _boundary_case("prefill", 100, 133, fresh, True, entry=True, single=single)
+def test_boundary_entry(fresh):
+    say(f"[boundary entry] fresh={fresh}")
+    ref, got, s = _boundary_case("prefill", 100, 133, fresh, True, entry=True)
     assert got["x_out"] is None
     _check_boundary(ref, got, s, fresh, True)
 
@@ -259,9 +233,9 @@ def test_boundary_stress_outliers_small():
     _check_boundary(ref, got, s, False, True)
 
 
-@pytest.mark.parametrize("single", [False, True])
-def test_boundary_deterministic_and_guarded(single):
-    say(f"[boundary] determinism + guard bands, single_launch={single}")
+@pytest.mark.parametrize("two", [False, True])
+def test_boundary_deterministic_and_guarded(two):
+    say(f"[boundary] determinism + guard bands, two_launch={two}")
     s = synth.boundary_inputs("prefill", 0, 33)
     n, d = 33, 5120
     guard = 4096
@@ -287,7 +261,7 @@ def test_boundary_deterministic_and_guarded(single):
             if b.dtype == torch.int16:
                 v = v.view(torch.bfloat16)
             views[k] = v.view(shapes[k])
-        H.hc_boundary(X, **dev, out=views, single_launch=single)
+        H.hc_boundary(X, **dev, out=views, two_launch=two)
         torch.cuda.synchronize()
         for k, b in bufs.items():
             fill = 0x7A7A if b.dtype == torch.int16 else 7.5
@@ -336,54 +310,57 @@ def test_prepared_call_matches_and_repeats():
     _check_boundary(oref, split, s, True, True)
 
 
-# ------------------------------------------------------------------ full size, sampled
-SAMPLE_RANGES = [(0, 3), (15, 18), (2047, 2049), (4093, 4096)]
+# ------------------------------------------------------------------ full size, every token
+FULL_CHUNK = 1024      # tokens per oracle call (bounds the oracle's temporaries)
 
 
-@pytest.mark.parametrize("fresh", [False, True])
-@pytest.mark.parametrize("single", [False, True])
-def test_prefill_full_size_sampled(fresh, single):
-    say(f"[prefill n=4096] fresh={fresh} single_launch={single}: generating inputs")
-    n = 4096
-    s = synth.boundary_inputs("prefill")
+def _host(got):
+    return {k: (v.detach().cpu() if isinstance(v, torch.Tensor) else v) for k, v in got.items() if k != "workspace"}
+
+
+def _compare_every_token(s, got, fresh, tag):
+    n = s["x"].shape[0]
+    host = _host(got)
+    for a in range(0, n, FULL_CHUNK):
+        b = min(n, a + FULL_CHUNK)
+        say(f"  {tag}: oracle tokens {a}..{b}")
+        ref = O.boundary(x=s["x"][a:b], delta=s["delta"][a:b], post_in=s["post_in"][a:b],
+                         comb_in=s["comb_in"][a:b], pre_in=None if fresh else s["pre_in"][a:b],
+                         hc_fn=s["hc_fn"], hc_base=s["hc_base"], hc_scale=s["hc_scale"], gamma=s["gamma"])
+        sub = {k: (v[a:b] if v is not None else None) for k, v in host.items()}
+        _check_boundary(ref, sub, {"x": s["x"][a:b], "gamma": s["gamma"]}, fresh, True)
+
+
+def _full_size(workload, fresh, two):
+    s = synth.boundary_inputs(workload)
     X = bf16_dev(s["x"])
     dev = dict(delta=bf16_dev(s["delta"]), post_in=f32_dev(s["post_in"]), comb_in=f32_dev(s["comb_in"]),
                pre_in=None if fresh else f32_dev(s["pre_in"]), fn_packed=packed(s["hc_fn"]),
                hc_base=f32_dev(s["hc_base"]), hc_scale=f32_dev(s["hc_scale"]), gamma=f32_dev(s["gamma"]))
     say("  launching")
-    got = H.hc_boundary(X, **dev, want_mixes=True, single_launch=single)
+    got = H.hc_boundary(X, **dev, want_mixes=True, two_launch=two)
     torch.cuda.synchronize()
     assert_workspace_clean(got)
-    for a, b in SAMPLE_RANGES:
-        say(f"  oracle tokens {a}..{b}")
-        ref = O.boundary(x=s["x"][a:b], delta=s["delta"][a:b], post_in=s["post_in"][a:b],
-                         comb_in=s["comb_in"][a:b], pre_in=None if fresh else s["pre_in"][a:b],
-                         hc_fn=s["hc_fn"], hc_base=s["hc_base"], hc_scale=s["hc_scale"], gamma=s["gamma"])
-        sub = {k: (v[a:b] if v is not None else None) for k, v in got.items() if k != "workspace"}
-        _check_boundary(ref, sub, {"x": s["x"][a:b], "gamma": s["gamma"]}, fresh, True)
-    assert got["y"].shape == (n, 5120)
+    del X, dev
+    return s, got
 
 
-STRESS_RANGES = [(0, 2), (8191, 8193), (20001, 20003), (32766, 32768)]
+@pytest.mark.parametrize("fresh,two", [(True, False), (False, False), (False, True)])
+def test_prefill_full_size_every_token(fresh, two):
+    """The benchmark's call (B=1, T=4096, d=5120, RMSNorm) compared with the
+    oracle on every token: the fresh read (two launches), the given read in one
+    launch (the read-row exchange) and the given read in two launches."""
+    say(f"[prefill n=4096] fresh={fresh} two_launch={two}: generating inputs")
+    s, got = _full_size("prefill", fresh, two)
+    assert got["y"].shape == (4096, 5120)
+    _compare_every_token(s, got, fresh, "prefill")
 
 
-def test_stress_full_size_sampled():
+@pytest.mark.parametrize("fresh", [True, False])
+def test_stress_full_size_every_token(fresh):
     """The bandwidth-stress boundary: B=4 T=8192 (32768 tokens, X = 1.34 GB),
-    heavy-tailed streams (1% of features x30), fresh read with the RMSNorm.
-    More tiles than workgroups per launch; sampled tokens across the batch."""
-    say("[stress n=32768] generating inputs")
-    s = synth.boundary_inputs("stress")
-    X = bf16_dev(s["x"])
-    dev = dict(delta=bf16_dev(s["delta"]), post_in=f32_dev(s["post_in"]), comb_in=f32_dev(s["comb_in"]),
-               fn_packed=packed(s["hc_fn"]), hc_base=f32_dev(s["hc_base"]), hc_scale=f32_dev(s["hc_scale"]),
-               gamma=f32_dev(s["gamma"]))
-    say("  launching")
-    got = H.hc_boundary(X, **dev, want_mixes=True)
-    torch.cuda.synchronize()
-    for a, b in STRESS_RANGES:
-        say(f"  oracle tokens {a}..{b}")
-        ref = O.boundary(x=s["x"][a:b], delta=s["delta"][a:b], post_in=s["post_in"][a:b],
-                         comb_in=s["comb_in"][a:b], pre_in=None, hc_fn=s["hc_fn"], hc_base=s["hc_base"],
-                         hc_scale=s["hc_scale"], gamma=s["gamma"])
-        sub = {k: (v[a:b] if v is not None else None) for k, v in got.items() if k != "workspace"}
-        _check_boundary(ref, sub, {"x": s["x"][a:b], "gamma": s["gamma"]}, True, True)
+    heavy-tailed streams (1% of features x30), RMSNorm, both reads; every
+    token against the oracle."""
+    say(f"[stress n=32768] fresh={fresh}: generating inputs")
+    s, got = _full_size("stress", fresh, False)
+    _compare_every_token(s, got, fresh, "stress")

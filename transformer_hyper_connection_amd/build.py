@@ -22,7 +22,7 @@ ARCH = "gfx950"
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
-    "-std=c++17",
+    "-std=c++20",
     "-fPIC",
     "-shared",
     # the stream arithmetic is a fixed sequence of separately rounded fp32 ops

@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <utility>
 #include <cstdarg>
 #include <cstdint>
 #include <cstddef>
@@ -678,6 +679,95 @@ __global__ void __launch_bounds__(kThreads) row_kernel(const RowArgs a) {
   }
 }
 
+// ======================================================= workgroup exchange
+// Words that one workgroup leaves for another travel through the workspace as
+// 64-bit (tag, value) pairs written and read with device scope: a word is valid
+// when its tag is the current call's, so no ordering between words is needed.
+// A reader polls a bounded number of times; a timeout sets a sticky bit in the
+// workspace's error mask (read back by hc_workspace_status) instead of hanging.
+typedef unsigned long long u64;
+constexpr int kCtrlBytes = 8192;             // control block at the head of the workspace
+constexpr int kErrWord = 1040;               // u32 index: sticky error mask (byte 4160)
+constexpr int kCtlDecArrive = 0;             // u64 index: decode arrival words [kDTiles]
+constexpr int kCtlDecEpoch = 8;              // u64 index: decode call epoch
+constexpr int kCtlDecDone = 9;               // u64 index: decode tiles-done count
+constexpr int kCtlXEpoch = 16;               // u64 index: read-row exchange call epoch
+constexpr int kCtlXDone = 17;                // u64 index: read-row exchange workgroups-done count
+constexpr unsigned kPollLimit = 1u << 14;    // polls of one word (about 1 us each) before a wait gives up
+enum : unsigned { kErrPollTimeout = 1u };
+
+__device__ __forceinline__ u64 tag_word(float v, u32 tag) { return ((u64)tag << 32) | __float_as_uint(v); }
+__device__ __forceinline__ void put_word(u64* p, u64 w) { __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ u64 get_word(const u64* p) { return __hip_atomic_load(const_cast<u64*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+// The word's value once its tag is this call's, polled again as needed.  After
+// a wait of this lane has timed out (dead), no further waiting: the call then
+// finishes quickly with the error flag set rather than polling on.
+__device__ __forceinline__ float settle(const u64* p, u64 w, u32 tag, u32* err, bool& dead) {
+  unsigned polls = 0;
+  while ((u32)(w >> 32) != tag && !dead) {
+    if (++polls > kPollLimit) { atomicOr(err, kErrPollTimeout); dead = true; break; }
+    __builtin_amdgcn_s_sleep(8);
+    w = get_word(p);
+  }
+  return __uint_as_float((u32)w);
+}
+
+// The split and Sinkhorn of one token, 4 lanes (a quad) per token, lane j
+// holding pre_j, post_j and comb row j (column sums by DPP quad sums), from the
+// token's dots (summed in a fixed order) and its RMS factor rx ("Reading
+// weights" kernel panel and reading-weight equation).  Every lane of the quad
+// calls it; the outputs are written if valid (pre/post/comb only if pre_out).
+__device__ __forceinline__ void derive_quad(float dpre, float dpost, const float (&dcomb)[4], float rx, int j,
+                                            bool valid, int64_t t, const float* hc_scale, const float* hc_base,
+                                            int iters, float eps, float* mixes_out, float* pre_out,
+                                            float* post_out, float* comb_out) {
+  constexpr int HC = 4, MIX = 24;
+  const float mp = dpre * rx, mq = dpost * rx;
+  float mc[HC];
+#pragma unroll
+  for (int k = 0; k < HC; ++k) mc[k] = dcomb[k] * rx;
+  if (valid && mixes_out) {
+    mixes_out[t * MIX + j] = mp;
+    mixes_out[t * MIX + HC + j] = mq;
+    *reinterpret_cast<f32x4*>(mixes_out + t * MIX + 2 * HC + j * HC) = f32x4{mc[0], mc[1], mc[2], mc[3]};
+  }
+  if (!pre_out) return;
+  const float pre = sigmoidf_(mp * hc_scale[0] + hc_base[j]) + eps;
+  const float post = 2.0f * sigmoidf_(mq * hc_scale[1] + hc_base[HC + j]);
+  const float s2 = hc_scale[2];
+  float A[HC];
+  float mxr = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < HC; ++k) {
+    A[k] = mc[k] * s2 + hc_base[2 * HC + j * HC + k];
+    mxr = fmaxf(mxr, A[k]);
+  }
+  float rsum = 0.f;
+#pragma unroll
+  for (int k = 0; k < HC; ++k) {
+    A[k] = expf(A[k] - mxr);
+    rsum = rsum + A[k];
+  }
+  const float rinv = __builtin_amdgcn_rcpf(rsum);
+#pragma unroll
+  for (int k = 0; k < HC; ++k) A[k] = A[k] * rinv + eps;
+  auto col_norm = [&]() {
+#pragma unroll
+    for (int k = 0; k < HC; ++k) A[k] = A[k] * __builtin_amdgcn_rcpf(quad_sum(A[k]) + eps);
+  };
+  col_norm();
+  for (int it = 1; it < iters; ++it) {
+    const float inv = __builtin_amdgcn_rcpf(((A[0] + A[1]) + A[2]) + A[3] + eps);
+#pragma unroll
+    for (int k = 0; k < HC; ++k) A[k] = A[k] * inv;
+    col_norm();
+  }
+  if (!valid) return;
+  pre_out[t * HC + j] = pre;
+  post_out[t * HC + j] = post;
+  *reinterpret_cast<f32x4*>(comb_out + t * HC * HC + j * HC) = f32x4{A[0], A[1], A[2], A[3]};
+}
+
 // ====================================================== boundary: two kernels
 // Everything that derives mixes (hc_mixes, block entry, sublayer boundary)
 // runs as two ordinary launches; the boundary between them is the only
@@ -735,7 +825,21 @@ struct StreamArgs {
   int64_t n;
   int xtok, xstr;     // elements per token / per stream of x (hc*d, d; or d, 0 when expanded)
   int d, S, F, tiles;
+  // the read-row exchange (given pre + RMSNorm in one launch, YK > 0)
+  u64* ctl;           // workspace control block (epoch, done count)
+  u64* xw;            // [tiles * S][kTT][kXW] tagged words
+  u32* err;           // sticky error mask
+  const float* gamma;
+  const float* hc_base;
+  const float* hc_scale;
+  float* mixes_out;
+  float* pre_out;
+  float* post_out;
+  float* comb_out;
+  int iters;
+  float hc_eps, norm_eps, rms_eps;
 };
+constexpr int kXW = kMix + 2;            // exchanged words per token and slice: 24 dots, sum x'^2, sum y^2
 
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -757,10 +861,24 @@ __device__ __forceinline__ void st_keep(u32x4* p, u32x4 v) { *p = v; }
 template <int N> struct IC { static constexpr int v = N; };
 
 // MEAN: the stream mean (x_mean) is written; a template parameter so that the
-// calls without it carry none of its registers
-template <bool POST, int RM, bool NORM, bool MEAN>
-__global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a) {
+// calls without it carry none of its registers.
+// YK > 0 (a given pre with the RMSNorm, the slice exactly YK chunks wide): the
+// whole boundary in this one launch.  Each lane keeps its read row in
+// registers instead of storing it; at the end every workgroup publishes its
+// per-token sums (24 dots, sum x'^2, sum y^2) as tagged words, sums the S
+// slices' sum y^2 of each of its tokens in slice order (the same bits in every
+// slice) and writes z = gamma * (y * r); the owner slice of each token (token
+// m % S == slice) sums the token's records in slice order and derives mixes,
+// pre/post and the comb.  A wait never depends on a workgroup dispatched later
+// than the first of its tile on every XCD, so no co-residency is assumed; a
+// wait that times out sets the error mask.
+// (Its 112 KB of LDS allow one workgroup, two waves per SIMD, per compute
+// unit; the register budget says so, else the compiler aims at three.)
+template <bool POST, int RM, bool NORM, bool MEAN, int YK = 0>
+__global__ void __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 2)))
+stream_kernel(const StreamArgs a) {
   static_assert(!NORM || RM != kNoRead, "RMSNorm needs the read row");
+  static_assert(YK == 0 || (RM == kGivenPre && NORM), "the read-row exchange is for a given pre with the RMSNorm");
   __shared__ u32x4 w_lds[2][2][kHC][kNT][64];          // weight tiles, double buffered (80 KB)
   __shared__ u32x4 a_lds[4][2][kHC][64];               // X' in A layout per row block (32 KB)
 
@@ -807,12 +925,38 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
   f32x4 acc[kAcc];
 #pragma unroll
   for (int t = 0; t < kAcc; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the projection's running sums: each chunk's matrix-core partial sums (fp32)
+  // are added here in fp64 and the fp32 accumulators restart, so fp32 rounding
+  // builds up over one chunk only, whatever the slice width (a slice can be the
+  // whole 20480-long row, and the dot of a heavy-tailed row cancels strongly).
+  // The one-launch read-row exchange (YK) has slices of at most 20 chunks and
+  // keeps its read row in these registers instead.
+  double acc64[kAcc][4];
+#pragma unroll
+  for (int t = 0; t < kAcc; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc64[t][i] = 0.0;
+  auto flush = [&]() __attribute__((always_inline)) {
+    if constexpr (YK == 0) {
+#pragma unroll
+      for (int t = 0; t < kAcc; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc64[t][i] += (double)acc[t][i];
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
   float ssx = 0.f, ssy = 0.f;
+  u32 ykeep[YK > 0 ? YK : 1][4];               // YK: this lane's read row, chunk by chunk
+  __shared__ u32 s_tag;
+  if constexpr (YK > 0) {
+    if (threadIdx.x == 0) s_tag = (u32)get_word(a.ctl + kCtlXEpoch) + 1u;   // words carry epoch + 1
+  }
   float gram[kGram];
 #pragma unroll
   for (int g = 0; g < kGram; ++g) gram[g] = 0.f;
 
-  auto load_wst = [&](int c, u32x4 (&dst)[kNT]) {
+  auto load_wst = [&](int c, u32x4 (&dst)[kNT]) __attribute__((always_inline)) {
     const int gstep = (fs + c * kCF) / 32;
 #pragma unroll
     for (int i = 0; i < kNT; ++i) {
@@ -821,7 +965,7 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
       dst[i] = a.fn[((size_t)((gstep + st) * kHC + k) * kNT + nt) * 64 + lane];
     }
   };
-  auto store_wst = [&](int buf, const u32x4 (&src)[kNT]) {
+  auto store_wst = [&](int buf, const u32x4 (&src)[kNT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kNT; ++i) {
       const int blk = wave + i * kWaves;
@@ -829,13 +973,13 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
       w_lds[buf][st][k][nt][lane] = src[i];
     }
   };
-  auto load_stream = [&](int c, u32x4 (&dst)[kHC + 1]) {
+  auto load_stream = [&](int c, u32x4 (&dst)[kHC + 1]) __attribute__((always_inline)) {
     const unsigned f = fs + c * kCF + fl;
 #pragma unroll
     for (int j = 0; j < kHC; ++j) dst[j] = ld_stream(reinterpret_cast<const u32x4*>(xb + (lt * (unsigned)a.xtok + j * (unsigned)a.xstr + f)));
     dst[kHC] = POST ? ld_stream(reinterpret_cast<const u32x4*>(db + (lt * d + f))) : u32x4{0u, 0u, 0u, 0u};
   };
-  auto stream_phase = [&](int c, const u32x4 (&src)[kHC + 1]) {
+  auto stream_phase = [&](int c, const u32x4 (&src)[kHC + 1]) __attribute__((always_inline)) {
     const unsigned f = fs + c * kCF + fl;
     u32 xp[kHC][4];
     if constexpr (POST) {
@@ -871,7 +1015,10 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
 #pragma unroll
         for (int e = 0; e < 4; ++e) ssy = dot2_bf16(yp[e], yp[e], ssy);
       }
-      if (tv) {
+      if constexpr (YK > 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ykeep[c][e] = yp[e];
+      } else if (tv) {
         u32x4* p = reinterpret_cast<u32x4*>(yb + (lt * d + f));
         const u32x4 v = u32x4{yp[0], yp[1], yp[2], yp[3]};
         if constexpr (NORM) st_keep(p, v); else st_stream(p, v);
@@ -888,7 +1035,7 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
       }
     }
   };
-  auto matrix_phase = [&](int buf) {
+  auto matrix_phase = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < kHC; ++k) {
       const bf16x8 A = __builtin_bit_cast(bf16x8, a_lds[rb][hw][k][a_swz(lane, hw)]);
@@ -901,7 +1048,7 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
   // one chunk: its streams are in registers; the next chunk's weights are
   // requested before any compute of this one, its streams before (given pre)
   // or after (fresh pre) the stream phase -- the faster order of each, measured
-  auto chunk = [&](int c, bool more) {
+  auto chunk = [&](int c, bool more) __attribute__((always_inline)) {
     constexpr bool kEarly = RM != kFreshPre;
     u32x4 nxt[kHC + 1];
     if (more) {
@@ -913,6 +1060,7 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
     lds_barrier();                 // A tiles and chunk c's weights in place; previous matrix phase done
     if (more) store_wst((c + 1) & 1, wst);
     matrix_phase(c & 1);
+    flush();
     lds_barrier();                 // matrix phase done before the A tiles are rewritten
     if (more) {
 #pragma unroll
@@ -941,10 +1089,21 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
     lds_barrier();
     if constexpr (decltype(STORE)::v) store_wst((c + 1) & 1, wnext);
     matrix_phase(c & 1);
+    flush();
     lds_barrier();
   };
 
-  if constexpr (!POST) {
+  if constexpr (YK > 0) {
+    // the slice is YK chunks wide: the loop unrolled, each chunk's read row in
+    // registers of its own
+    load_wst(0, wst);
+    load_stream(0, cur);
+    store_wst(0, wst);
+    lds_barrier();
+    [&]<int... C>(std::integer_sequence<int, C...>) __attribute__((always_inline)) {
+      (chunk(C, C + 1 < YK), ...);
+    }(std::make_integer_sequence<int, YK>{});
+  } else if constexpr (!POST) {
     u32x4 sB[kHC + 1], wB[kNT];
     const int c1 = nch > 1 ? 1 : 0;                // a single chunk loads chunk 0 twice (unused)
     load_wst(0, wst);
@@ -997,7 +1156,7 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
   for (int t = 0; t < kAcc; ++t)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
-      red[((rb * 2 + hw) * 16 + 4 * (lane >> 4) + rr) * 32 + t * 16 + (lane & 15)] = acc[t][rr];
+      red[((rb * 2 + hw) * 16 + 4 * (lane >> 4) + rr) * 32 + t * 16 + (lane & 15)] = (YK == 0 ? (float)acc64[t][rr] : acc[t][rr]);
   float* extra = red + 4 * 2 * 16 * 32;                            // [kRec - kMix][kTT]
   if ((lane & 7) == 0) {
     extra[m] = ssx;
@@ -1008,6 +1167,95 @@ __global__ void __launch_bounds__(kThreads, 1) stream_kernel(const StreamArgs a)
     }
   }
   lds_barrier();
+  if constexpr (YK > 0) {
+    constexpr int kXS = 8;                         // slices at most on this path (S = d / (64 YK))
+    const u32 tag = s_tag;
+    u64* tilew = a.xw + (size_t)tile * S * kTT * kXW;
+    // publish this slice's sums of every token of the tile
+    u64* mine = tilew + (size_t)slice * kTT * kXW;
+    for (int idx = threadIdx.x; idx < kTT * kXW; idx += kThreads) {
+      const int tm = idx / kXW, q = idx % kXW;
+      float v;
+      if (q < kMix) {
+        const float* r0 = red + ((tm >> 4) * 2 * 16 + (tm & 15)) * 32;   // step 0
+        const float* r1 = r0 + 16 * 32;                                 // step 1
+        v = q < 16 ? r0[q] + r1[q] : (r0[q] + r0[q + 8]) + (r1[q] + r1[q + 8]);
+      } else {
+        v = extra[(q - kMix) * kTT + tm];                               // sum x'^2, sum y^2
+      }
+      put_word(mine + idx, tag_word(v, tag));
+    }
+    // one round trip for every word this workgroup waits for: each thread
+    // requests the sum y^2 of its token from every slice, and, for one
+    // (owned token, word) pair, that word from every slice; each is summed in
+    // slice order (every slice of the tile forms the same bits)
+    bool dead = false;
+    const int nown = (kTT - slice + S - 1) / S;          // owned tokens: slice, slice + S, ...
+    const int pr = threadIdx.x;                          // (owned token, word) pair of this thread
+    const bool has_pair = pr < nown * kXW;
+    const int ptm = has_pair ? slice + S * (pr / kXW) : 0, pq = has_pair ? pr % kXW : 0;
+    u64 wy[kXS], wr[kXS];
+#pragma unroll
+    for (int s2 = 0; s2 < kXS; ++s2) {
+      wy[s2] = s2 < S ? get_word(tilew + ((size_t)s2 * kTT + m) * kXW + kMix + 1) : 0ull;
+      wr[s2] = s2 < S && has_pair ? get_word(tilew + ((size_t)s2 * kTT + ptm) * kXW + pq) : 0ull;
+    }
+    float* tot = reinterpret_cast<float*>(&a_lds[0][0][0][0]);   // [owned token][kXW] (A tiles are free)
+    {
+      float ty = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < kXS; ++s2)
+        if (s2 < S) {
+          const float v = settle(tilew + ((size_t)s2 * kTT + m) * kXW + kMix + 1, wy[s2], tag, a.err, dead);
+          ty = s2 == 0 ? v : ty + v;
+        }
+      const float ry = 1.0f / sqrtf(ty / (float)d + a.rms_eps);
+      // z = gamma * (y * r) from the kept read row
+#pragma unroll
+      for (int c = 0; c < YK; ++c) {
+        const int f = fs + c * kCF + fl;
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(a.gamma + f);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(a.gamma + f + 4);
+        const float gm[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+        u32 zp[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2)
+          zp[e2] = pack_bf16(gm[2 * e2] * (bf_lo(ykeep[c][e2]) * ry), gm[2 * e2 + 1] * (bf_hi(ykeep[c][e2]) * ry));
+        if (tv) st_stream(reinterpret_cast<u32x4*>(yb + (lt * d + f)), u32x4{zp[0], zp[1], zp[2], zp[3]});
+      }
+      if (has_pair) {
+        float tr = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < kXS; ++s2)
+          if (s2 < S) {
+            const float v = settle(tilew + ((size_t)s2 * kTT + ptm) * kXW + pq, wr[s2], tag, a.err, dead);
+            tr = s2 == 0 ? v : tr + v;
+          }
+        tot[pr] = tr;
+      }
+    }
+    __syncthreads();
+    // the owned tokens' mixes, pre/post and comb: 4 lanes per token
+    if ((int)threadIdx.x < 4 * nown) {
+      const int k = threadIdx.x >> 2, j = threadIdx.x & 3;
+      const int tm = slice + S * k;
+      const float* r = tot + k * kXW;
+      const float rx = 1.0f / sqrtf(r[kMix] / (float)(kHC * d) + a.norm_eps);
+      const float dc[kHC] = {r[2 * kHC + 4 * j], r[2 * kHC + 4 * j + 1], r[2 * kHC + 4 * j + 2], r[2 * kHC + 4 * j + 3]};
+      derive_quad(r[j], r[kHC + j], dc, rx, j, t0 + tm < a.n, t0 + tm, a.hc_scale, a.hc_base, a.iters,
+                  a.hc_eps, a.mixes_out, a.pre_out, a.post_out, a.comb_out);
+    }
+    // every word of this call read: the last workgroup advances the epoch
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const u64 before = __hip_atomic_fetch_add(a.ctl + kCtlXDone, (u64)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (before % (u64)gridDim.x == (u64)(gridDim.x - 1)) {
+        put_word(a.ctl + kCtlXDone, 0ull);
+        put_word(a.ctl + kCtlXEpoch, (u64)tag);
+      }
+    }
+    return;
+  }
   float* rec = a.rec + ((size_t)tile * S + slice) * kTT * kRec;
   for (int idx = threadIdx.x; idx < kTT * kQuads; idx += kThreads) {
     const int tm = idx / kQuads, q0 = (idx % kQuads) * 4;
@@ -1238,1153 +1486,6 @@ __global__ void __launch_bounds__(kFinThreads) finish_kernel(const FinishArgs a)
   }
 }
 
-// ======================================================= single-launch boundary
-// fused_kernel<POST, RM, NORM>: the sublayer boundary in one launch, X' written
-// once and read from the chip ("Source layer, pairs pooled": Block.forward).
-//
-// Work items are (tile of kFT = 16 tokens, slice of kFF = 512 features of each
-// stream); the S = d/512 slices of a tile run on different workgroups.  The grid
-// is persistent, one workgroup per compute unit, every workgroup resident, and a
-// multiple of S; it walks the items in rounds, item r*G + w in round r, so the
-// slices of a tile share a round.
-//
-// Segment k of a workgroup (one barrier between segments):
-//   stream waves (8): the read row of item k-2 from its kept X' tile (its
-//     coefficients were derived in segment k-1) -> z; then X' of item k =
-//     hc_post(...) from the loads issued in segment k-1.  The loads of item k+1
-//     go out before any store of item k (one vector-memory counter orders them);
-//     X' is stored, put in the LDS A tile of item k (kept for its read row) and
-//     its Gram entries summed.
-//   matrix waves (4), at the same time: the 24 projection dots of item k-1 on
-//     the matrix cores (weight tiles streamed from L2 into registers); publish
-//     item k-1's per-token record (dots + Gram) for the other slices of its tile;
-//     the outputs (mixes, pre/post, Sinkhorn comb) of the tokens this slice owns
-//     in item k-2 (all 34 words of all S slices, written a segment earlier); the
-//     read coefficients of item k-1: the 14 words the read needs (4 pre dots +
-//     Gram), summed over the S slices in slice order by every slice workgroup of
-//     the tile (the same bits everywhere) -> pre and the RMSNorm factor.
-// Records travel through the workspace as 64-bit words (value, call tag): a word
-// is valid when its tag is this call's, so no ordering between words is needed
-// and no writer waits.  A reader polls until valid, a bounded number of times;
-// a timeout sets an error flag instead of hanging.
-constexpr int kFT = 16;                      // tokens per tile
-constexpr int kFF = 512;                     // features per slice and stream
-constexpr int kFSW = 8;                      // stream waves
-constexpr int kFMW = 4;                      // matrix waves
-constexpr int kFThreads = (kFSW + kFMW) * 64;
-constexpr int kFKS = kFF / kStepF;           // 32-feature steps per slice (16)
-constexpr int kFKB = kFKS * kHC;             // matrix-core K blocks per item (64)
-constexpr int kFKBW = kFKB / kFMW;           // per matrix wave (16)
-constexpr int kFPre = 4;                     // weight blocks in flight per matrix wave
-constexpr int kFRec = 34;                    // record words per token and slice
-constexpr int kFCoef = 5;                    // read coefficients per token: pre[4], RMSNorm factor
-constexpr int kFMinD = 2 * kFF;              // S >= 2: at most 8 owned tokens per slice
-constexpr int kFPollBatch = 10;              // slices polled per batch
-constexpr int kCtrlBytes = 8192;             // control block at the head of the workspace
-constexpr int kEpochCopies = 64;             // epoch word copies, 64 bytes apart
-constexpr int kDoneWord = 1024, kErrWord = 1040;
-constexpr unsigned kPollLimit = 1u << 14;    // polls of one word (about 1 us each) before a wait gives up
-constexpr int64_t kFusedMaxN = (int64_t)1 << 26;   // item indices stay in int
-typedef unsigned long long u64;
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-enum : unsigned { kErrPollTimeout = 1u };
-
-struct FusedArgs {
-  const hc_bf16* x;
-  const hc_bf16* delta;
-  const float* post_in;
-  const float* comb_in;
-  const float* pre_in;
-  const u32x4* fn;
-  const float* gamma;
-  const float* hc_base;
-  const float* hc_scale;
-  hc_bf16* x_out;
-  hc_bf16* y_out;
-  float* mixes_out;
-  float* pre_out;
-  float* post_out;
-  float* comb_out;
-  u32* ctrl;          // workspace head (kCtrlBytes)
-  u64* rec;           // [tiles][S][kFT][kFRec] tagged words
-  int64_t n;
-  int d, S, tiles, items, rounds, iters;
-  float hc_eps, norm_eps, rms_eps;
-};
-
-// record word order per read mode: fresh [pre dots 0..3 | Gram 10 | dots 4..23];
-// given pre with RMSNorm [sum y^2 | sum x'^2 | dots]; otherwise [sum x'^2 | dots]
-template <int RM, bool NORM> constexpr int f_fast() { return RM == kFreshPre ? kHC + kGram : (RM == kGivenPre && NORM ? 1 : 0); }
-template <int RM, bool NORM> __device__ __forceinline__ int f_dot(int q) {
-  if constexpr (RM == kFreshPre) return q < kHC ? q : q + kGram;
-  else return q + (NORM && RM == kGivenPre ? 2 : 1);
-}
-template <int RM, bool NORM> constexpr int f_ssx() { return RM == kGivenPre && NORM ? 1 : 0; }   // (not fresh)
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* p, u32 bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 buf_ld(rsrc_t r, u32 off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2); }
-__device__ __forceinline__ void buf_st(rsrc_t r, u32 off, u32x4 v) { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 2); }
-
-__device__ __forceinline__ u64 tag_word(float v, u32 tag) { return ((u64)tag << 32) | __float_as_uint(v); }
-__device__ __forceinline__ void put_word(u64* p, u64 w) { __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ __forceinline__ u64 get_word(const u64* p) { return __hip_atomic_load(const_cast<u64*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-// The word's value once its tag is this call's, polled again as needed.  After
-// a wait of this lane has timed out (dead), no further waiting: the call then
-// finishes quickly with the error flag set rather than polling on.
-__device__ __forceinline__ float settle(const u64* p, u64 w, u32 tag, u32* err, bool& dead) {
-  unsigned polls = 0;
-  while ((u32)(w >> 32) != tag && !dead) {
-    if (++polls > kPollLimit) { atomicOr(err, kErrPollTimeout); dead = true; break; }
-    __builtin_amdgcn_s_sleep(8);
-    w = get_word(p);
-  }
-  return __uint_as_float((u32)w);
-}
-
-// A-tile slot of matrix-core lane L at step parity st: the low 4 bits are
-// XOR-ed with (2*(L/16) | st), a permutation within each 16-slot group, so that
-// the 8 lanes writing one token's 64 features hit 8 different bank groups.
-__device__ __forceinline__ int f_swz(int L, int st) { return (L & 48) | ((L & 15) ^ (((L >> 4) << 1) | st)); }
-
-// One token's mixes / pre / post / comb from its summed record (in LDS, record
-// word order), 4 lanes (one quad) per token, lane j holding comb row j
-// ("Reading weights" kernel panel and reading-weight equation).  All four lanes
-// of the quad call it.
-template <int RM, bool NORM>
-__device__ __forceinline__ void derive_outputs(const float* fs, float rx, int j, const FusedArgs& a, int64_t t) {
-  if (a.mixes_out) {
-#pragma unroll
-    for (int i = 0; i < kMix / kHC; ++i) a.mixes_out[t * kMix + i * kHC + j] = fs[f_dot<RM, NORM>(i * kHC + j)] * rx;
-  }
-  const float s0 = a.hc_scale[0], s1 = a.hc_scale[1], s2 = a.hc_scale[2];
-  const float pre = sigmoidf_((fs[f_dot<RM, NORM>(j)] * rx) * s0 + a.hc_base[j]) + a.hc_eps;
-  const float post = 2.0f * sigmoidf_((fs[f_dot<RM, NORM>(kHC + j)] * rx) * s1 + a.hc_base[kHC + j]);
-  float A[kHC];
-  float mxr = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < kHC; ++k) {
-    const int q = 2 * kHC + j * kHC + k;
-    A[k] = (fs[f_dot<RM, NORM>(q)] * rx) * s2 + a.hc_base[q];
-    mxr = fmaxf(mxr, A[k]);
-  }
-  float rsum = 0.f;
-#pragma unroll
-  for (int k = 0; k < kHC; ++k) {
-    A[k] = expf(A[k] - mxr);
-    rsum = rsum + A[k];
-  }
-  const float rinv = __builtin_amdgcn_rcpf(rsum);
-#pragma unroll
-  for (int k = 0; k < kHC; ++k) A[k] = A[k] * rinv + a.hc_eps;
-  auto col_norm = [&]() {
-#pragma unroll
-    for (int k = 0; k < kHC; ++k) A[k] = A[k] * __builtin_amdgcn_rcpf(quad_sum(A[k]) + a.hc_eps);
-  };
-  col_norm();
-  for (int it = 1; it < a.iters; ++it) {
-    const float inv = __builtin_amdgcn_rcpf(((A[0] + A[1]) + A[2]) + A[3] + a.hc_eps);
-#pragma unroll
-    for (int k = 0; k < kHC; ++k) A[k] = A[k] * inv;
-    col_norm();
-  }
-  a.pre_out[t * kHC + j] = pre;
-  a.post_out[t * kHC + j] = post;
-  *reinterpret_cast<f32x4*>(a.comb_out + t * kHC * kHC + j * kHC) = f32x4{A[0], A[1], A[2], A[3]};
-}
-
-template <bool POST, int RM, bool NORM>
-__global__ void __launch_bounds__(kFThreads, 1) fused_kernel(const FusedArgs a) {
-  constexpr bool kFresh = RM == kFreshPre;
-  constexpr bool kKeepY = RM == kGivenPre && NORM;       // y kept (registers) for the RMSNorm
-  constexpr bool kFinish = kFresh || kKeepY;             // a read row is written after the exchange
-  constexpr int kFast = f_fast<RM, NORM>();
-  // LDS
-  __shared__ u32x4 A_lds[2][kHC][kFKS][64];              // X' in matrix-core A layout, items k and k-1 (128 KB)
-  __shared__ float red[kFMW][kFT][kMix];                 // per-matrix-wave partial dots
-  __shared__ float gred[2][4][kFT][kGram + 2];           // per-chunk-pair Gram / sum x'^2 / sum y^2, by item parity
-  __shared__ float cin[2][kFT][kHC + kHC * kHC + kHC];   // post_in, comb_in, pre_in of the streamed item
-  __shared__ float gam[2][NORM ? kFF : 1];               // RMSNorm gain of the item being read
-  __shared__ float coef[2][kFT][kFCoef];                 // read coefficients (pre, RMSNorm factor)
-  __shared__ float fsum[kFMW][kFT / kFMW][kFRec];        // matrix-wave scratch: summed record words
-  __shared__ u32 mcount;                                 // matrix-wave barrier counter
-
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int G = gridDim.x, w = blockIdx.x, S = a.S, d = a.d;
-  u32* err = a.ctrl + kErrWord;
-  const u32 epoch = __hip_atomic_load(a.ctrl + 16 * (w % kEpochCopies), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const u32 tag = epoch + 1u == 0u ? 1u : epoch + 1u;
-  if (threadIdx.x == 0) mcount = 0;
-
-  // Position of this workgroup in a round: consecutive workgroups land on
-  // different XCDs (round-robin), so they are renumbered XCD by XCD; items are
-  // taken slice-major, position g -> (tile r*TPR + g%TPR, slice g/TPR), TPR = G/S
-  // tiles per round.  A workgroup keeps its slice in every round, and the
-  // workgroups of one XCD share one or two slices: their weight tiles stay in
-  // that XCD's L2.  (Any bijection is correct; this one is for locality.)
-  const int xcd = w & 7, xq = G >> 3, xr = G & 7;
-  const int g_pos = xcd * xq + min(xcd, xr) + (w >> 3);
-  const int TPR = G / S;
-  struct Item { int tile, slice, valid; };
-  auto item_of = [&](int r) {
-    Item it;
-    const int tile = r * TPR + g_pos % TPR;
-    const bool ok = r >= 0 && r < a.rounds && tile < a.tiles;
-    it.tile = ok ? tile : 0;
-    it.slice = g_pos / TPR;
-    it.valid = ok ? (int)min<int64_t>(kFT, a.n - (int64_t)tile * kFT) : 0;
-    return it;
-  };
-  const u32 xrow = (u32)(kHC * d * 2), drow = (u32)(d * 2);
-  const int K = a.rounds + 2;                            // segments: stream k, matrix k-1, read k-2
-
-  if (wave < kFSW) {
-    // ======================================================== stream waves
-    // segment k: the read row of item k-2, then X' of item k
-    const int tg = wave & 1, cp = wave >> 1;
-    const int tl = lane >> 3, p = lane & 7;
-    const int m = 8 * tg + tl;                             // token of the tile
-    struct Res { rsrc_t x, dl, xo, yo; u32 fbyte; };
-    auto res_of = [&](const Item& it) {
-      Res q;
-      const int64_t t0 = (int64_t)it.tile * kFT;
-      q.x = make_rsrc(a.x + t0 * kHC * d, it.valid * xrow);
-      q.dl = make_rsrc(POST ? a.delta + t0 * d : a.x, POST ? it.valid * drow : 0);
-      q.xo = make_rsrc(POST ? a.x_out + t0 * kHC * d : a.x, POST ? it.valid * xrow : 0);
-      q.yo = make_rsrc(a.y_out + t0 * d, it.valid * drow);
-      q.fbyte = (u32)(it.slice * kFF + 2 * cp * 64 + 8 * p) * 2;
-      return q;
-    };
-    u32x4 L[2][kHC + 1];
-    auto issue = [&](const Res& q) {
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const u32 o = (u32)m * xrow + q.fbyte + cc * 128;
-#pragma unroll
-        for (int j = 0; j < kHC; ++j) L[cc][j] = buf_ld(q.x, o + j * drow);
-        L[cc][kHC] = POST ? buf_ld(q.dl, (u32)m * drow + q.fbyte + cc * 128) : u32x4{0u, 0u, 0u, 0u};
-      }
-    };
-    u32 yk1[2][4], yk2[2][4];                            // given pre + RMSNorm: y of items k-1, k-2
-    Res rc = res_of(item_of(0));
-    issue(rc);
-    __syncthreads();                                     // P: cin of item 0 in place
-    for (int k = 0; k < K; ++k) {
-      // ---- the read row of item k-2 (its coefficients arrived with the last barrier)
-      if constexpr (kFinish) {
-        const Res rp = res_of(item_of(k - 2));
-        const int pb = k & 1;                            // (k-2) & 1
-        const float* cf = coef[pb][m];
-        float pr[kHC];
-#pragma unroll
-        for (int j = 0; j < kHC; ++j) pr[j] = cf[j];
-        const float rn = NORM ? cf[kHC] : 1.f;
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          u32 yv[4];
-          if constexpr (kFresh) {
-            const int ks = 2 * (2 * cp + cc) + (p >> 2);
-            const int slot = f_swz(16 * (p & 3) + m, ks & 1);
-            u32 xv[kHC][4];
-#pragma unroll
-            for (int kk = 0; kk < kHC; ++kk) {
-              const u32x4 v = A_lds[pb][kk][ks][slot];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) xv[kk][e] = v[e];
-            }
-            pre_8(xv, pr, yv);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) yv[e] = yk2[cc][e];
-          }
-          if constexpr (NORM) {
-            const float* gm = gam[pb] + (2 * cp + cc) * 64 + 8 * p;
-            const f32x4 g0 = *reinterpret_cast<const f32x4*>(gm);
-            const f32x4 g1 = *reinterpret_cast<const f32x4*>(gm + 4);
-            const float gg[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2)
-              yv[e2] = pack_bf16(gg[2 * e2] * (bf_lo(yv[e2]) * rn), gg[2 * e2 + 1] * (bf_hi(yv[e2]) * rn));
-          }
-          buf_st(rp.yo, (u32)m * drow + rp.fbyte + cc * 128, u32x4{yv[0], yv[1], yv[2], yv[3]});
-        }
-      }
-      // ---- X' of item k
-      const Res rn_ = res_of(item_of(k + 1));
-      const int sl = k & 1;
-      const float* ci = cin[k & 1][m];
-      float cpost[kHC], ccomb[kHC * kHC], cpre[kHC];
-#pragma unroll
-      for (int j = 0; j < kHC; ++j) { cpost[j] = ci[j]; cpre[j] = ci[kHC + kHC * kHC + j]; }
-#pragma unroll
-      for (int j = 0; j < kHC * kHC; ++j) ccomb[j] = ci[kHC + j];
-      u32 xp[2][kHC][4];
-      u32 yp[2][4];
-      float g[kGram + 2];
-#pragma unroll
-      for (int i = 0; i < kGram + 2; ++i) g[i] = 0.f;
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        if constexpr (POST) {
-          post_8(L[cc], cpost, ccomb, xp[cc]);
-        } else {
-#pragma unroll
-          for (int kk = 0; kk < kHC; ++kk)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) xp[cc][kk][e] = L[cc][kk][e];
-        }
-        if constexpr (kFresh) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            int gi = 0;
-#pragma unroll
-            for (int j = 0; j < kHC; ++j)
-#pragma unroll
-              for (int l = j; l < kHC; ++l, ++gi) g[gi] = dot2_bf16(xp[cc][j][e], xp[cc][l][e], g[gi]);
-          }
-        } else {
-#pragma unroll
-          for (int kk = 0; kk < kHC; ++kk)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) g[kGram] = dot2_bf16(xp[cc][kk][e], xp[cc][kk][e], g[kGram]);
-          pre_8(xp[cc], cpre, yp[cc]);
-          if constexpr (NORM) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) g[kGram + 1] = dot2_bf16(yp[cc][e], yp[cc][e], g[kGram + 1]);
-          }
-        }
-      }
-      // the loads of item k+1 go out before any store of item k (one vector-memory counter orders them)
-      issue(rn_);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const u32 o = (u32)m * xrow + rc.fbyte + cc * 128;
-        if constexpr (POST) {
-#pragma unroll
-          for (int kk = 0; kk < kHC; ++kk)
-            buf_st(rc.xo, o + kk * drow, u32x4{xp[cc][kk][0], xp[cc][kk][1], xp[cc][kk][2], xp[cc][kk][3]});
-        }
-        if constexpr (RM == kGivenPre && !NORM)
-          buf_st(rc.yo, (u32)m * drow + rc.fbyte + cc * 128, u32x4{yp[cc][0], yp[cc][1], yp[cc][2], yp[cc][3]});
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // X' into the A tile of item k: chunk c = 2cp+cc, step ks = 2c + p/4, A lane 16*(p%4) + m
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int ks = 2 * (2 * cp + cc) + (p >> 2);
-        const int slot = f_swz(16 * (p & 3) + m, ks & 1);
-#pragma unroll
-        for (int kk = 0; kk < kHC; ++kk)
-          A_lds[sl][kk][ks][slot] = u32x4{xp[cc][kk][0], xp[cc][kk][1], xp[cc][kk][2], xp[cc][kk][3]};
-      }
-      // per-token sums over the 8 lanes of the token, then one lane writes this chunk pair's share
-#pragma unroll
-      for (int i = 0; i < kGram + 2; ++i) {
-        g[i] += __shfl_xor(g[i], 1);
-        g[i] += __shfl_xor(g[i], 2);
-        g[i] += __shfl_xor(g[i], 4);
-      }
-      if (p == 0) {
-#pragma unroll
-        for (int i = 0; i < kGram + 2; ++i) gred[k & 1][cp][m][i] = g[i];
-      }
-      if constexpr (kKeepY) {
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { yk2[cc][e] = yk1[cc][e]; yk1[cc][e] = yp[cc][e]; }
-      }
-      rc = rn_;
-      __syncthreads();                                   // X(k)
-    }
-  } else {
-    // ======================================================== matrix waves
-    // segment k: the dots of item k-1 and its record; the outputs of the tokens
-    // this slice owns in item k-2; the read coefficients of item k-1
-    const int mw = wave - kFSW;
-    const int lt = threadIdx.x - kFSW * 64;              // 0..255
-    u32 mgen = 0;
-    // the four matrix waves meet (LDS counter; bounded)
-    auto mbar = [&]() {
-      ++mgen;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      if (lane == 0) __hip_atomic_fetch_add(&mcount, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      unsigned spins = 0;
-      while (__hip_atomic_load(&mcount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < kFMW * mgen) {
-        if (++spins > kPollLimit * 64) { if (lane == 0) atomicOr(err, kErrPollTimeout); break; }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    };
-    // weight tiles of this workgroup's slice (the slice is the same in every
-    // round): record (K block kb, tile nt, lane) at ((kb*kNT + nt)*64 + lane)*16 B
-    constexpr u32 kSliceWt = (u32)kFKB * kNT * 64 * 16;
-    const rsrc_t wres = make_rsrc(a.fn + (size_t)item_of(0).slice * (kSliceWt / 16), kSliceWt);
-    const u32 wlane = (u32)lane * 16 + (u32)mw * kFKBW * kNT * 64 * 16;
-    auto wt = [&](int j, int nt) {                     // weight tile nt of K block j of this wave
-      return __builtin_amdgcn_raw_buffer_load_b128(wres, wlane, (j * kNT + nt) * 64 * 16, 0);
-    };
-    constexpr int kCin = kFT * (kHC + kHC * kHC + kHC);  // 384 floats
-    auto cin_val = [&](const Item& it, int i) {
-      const int tm = i / (kHC + kHC * kHC + kHC), q = i % (kHC + kHC * kHC + kHC);
-      const int64_t t = (int64_t)it.tile * kFT + tm;
-      if (tm >= it.valid) return 0.f;
-      if (q < kHC) return POST ? a.post_in[t * kHC + q] : 0.f;
-      if (q < kHC + kHC * kHC) return POST ? a.comb_in[t * kHC * kHC + (q - kHC)] : 0.f;
-      return RM == kGivenPre ? a.pre_in[t * kHC + (q - kHC - kHC * kHC)] : 0.f;
-    };
-    {                                                    // prologue: cin of item 0
-      const Item i0 = item_of(0);
-      for (int i = lt; i < kCin; i += kFMW * 64) cin[0][i / (kCin / kFT)][i % (kCin / kFT)] = cin_val(i0, i);
-    }
-    u32x4 B[kFPre][kNT];
-#pragma unroll
-    for (int j = 0; j < kFPre; ++j)
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) B[j][nt] = wt(j, nt);
-    bool dead = false;
-    __syncthreads();                                     // P
-    for (int k = 0; k < K; ++k) {
-      const Item im = item_of(k - 1), io = item_of(k - 2), in1 = item_of(k + 1);
-      // ---- the dots of item k-1 (A tile k-1, weights prefetched)
-      {
-        const int sl = (k - 1) & 1;
-        f32x4 acc[kAcc];
-#pragma unroll
-        for (int t = 0; t < kAcc; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < kFKBW; ++j) {
-          const int kb = mw * kFKBW + j;
-          const int ks = kb >> 2, kk = kb & 3;
-          const bf16x8 Av = __builtin_bit_cast(bf16x8, A_lds[sl][kk][ks][f_swz(lane, ks & 1)]);
-          bf16x8 Bv[kNT];
-#pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) Bv[nt] = __builtin_bit_cast(bf16x8, B[j % kFPre][nt]);
-          if (j + kFPre < kFKBW) {
-#pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) B[j % kFPre][nt] = wt(j + kFPre, nt);
-          }
-          mfma_step(Av, Bv, acc);
-        }
-        // tile 1: columns c and c+8 hold the (hi+lo) and mid terms of row 16+c
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float o = __shfl_xor(acc[1][i], 8);
-          const int tm = 4 * (lane >> 4) + i, col = lane & 15;
-          red[mw][tm][col] = acc[0][i];
-          if (col < 8) red[mw][tm][16 + col] = acc[1][i] + o;
-        }
-      }
-      // Requests with the weight loads of this segment behind them (one vector-memory
-      // counter: a wait for a weight block waits for everything issued before it):
-      // the staged inputs (stream coefficients of item k+1, RMSNorm gain of item k-1).
-      const u64* ro = a.rec + (size_t)io.tile * S * kFT * kFRec;
-      const int oi0 = mw;                                // first owned token index of this wave
-      u64 ow[kFPollBatch];                               // words of this wave's first owned token, item k-2
-      {
-        const int otm = io.slice + oi0 * S;
-        const bool act = io.valid > 0 && otm < io.valid && lane < kFRec;
-#pragma unroll
-        for (int b = 0; b < kFPollBatch; ++b)
-          ow[b] = (act && b < S) ? get_word(ro + ((size_t)b * kFT + otm) * kFRec + lane) : 0ull;
-      }
-      float cv[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) cv[u] = (lt + u * kFMW * 64 < kCin) ? cin_val(in1, lt + u * kFMW * 64) : 0.f;
-      f32x4 gv = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (NORM) gv = *reinterpret_cast<const f32x4*>(a.gamma + im.slice * kFF + 4 * (lt & (kFF / 4 - 1)));
-      mbar();
-      // ---- publish item k-1's record
-      if (im.valid > 0) {
-        u64* rb = a.rec + ((size_t)im.tile * S + im.slice) * kFT * kFRec;
-        const float(*gr)[kFT][kGram + 2] = gred[(k - 1) & 1];
-        const int tm = lt >> 4;
-#pragma unroll
-        for (int q = lt & 15; q < kFRec; q += 16) {
-          if (tm >= im.valid) break;
-          int qd = -1, gi = -1;
-          if constexpr (kFresh) {
-            if (q < kHC) qd = q;
-            else if (q < kHC + kGram) gi = q - kHC;
-            else qd = q - kGram;
-          } else {
-            const int base = kKeepY ? 2 : 1;
-            if (q >= base + kMix) gi = -2;
-            else if (q >= base) qd = q - base;
-            else gi = (kKeepY && q == 0) ? kGram + 1 : kGram;
-          }
-          float v = 0.f;
-          if (qd >= 0) v = ((red[0][tm][qd] + red[1][tm][qd]) + red[2][tm][qd]) + red[3][tm][qd];
-          else if (gi >= 0) v = ((gr[0][tm][gi] + gr[1][tm][gi]) + gr[2][tm][gi]) + gr[3][tm][gi];
-          put_word(rb + tm * kFRec + q, tag_word(v, tag));
-        }
-      }
-      // ---- read coefficients of item k-1 (words written just now by the other
-      //      slices): requested here, summed after the owned tokens of item k-2
-      const u64* rm = a.rec + (size_t)im.tile * S * kFT * kFRec;
-      const int fi = lane >> 4, fq = lane & 15, ftm = 4 * mw + fi;
-      const bool fast_act = kFast > 0 && im.valid > 0 && fq < kFast && ftm < im.valid;
-      u64 fw[kFPollBatch];
-#pragma unroll
-      for (int b = 0; b < kFPollBatch; ++b)
-        fw[b] = (fast_act && b < S) ? get_word(rm + ((size_t)b * kFT + ftm) * kFRec + fq) : 0ull;
-      // owned tokens: mixes, pre/post, Sinkhorn comb (first owned token from the words above)
-      for (int oi = oi0; io.valid > 0 && io.slice + oi * S < io.valid; oi += kFMW) {
-        const int tm = io.slice + oi * S;
-        const bool act = lane < kFRec;
-        float s = 0.f;
-        for (int s0b = 0; s0b < S; s0b += kFPollBatch) {
-          u64 wv[kFPollBatch];
-#pragma unroll
-          for (int b = 0; b < kFPollBatch; ++b)
-            wv[b] = (oi == oi0 && s0b == 0) ? ow[b]
-                    : ((act && s0b + b < S) ? get_word(ro + ((size_t)(s0b + b) * kFT + tm) * kFRec + lane) : 0ull);
-#pragma unroll
-          for (int b = 0; b < kFPollBatch; ++b)
-            if (act && s0b + b < S) s += settle(ro + ((size_t)(s0b + b) * kFT + tm) * kFRec + lane, wv[b], tag, err, dead);
-        }
-        float* fs = fsum[mw][0];
-        __builtin_amdgcn_wave_barrier();
-        if (act) fs[lane] = s;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        float ssx;
-        if constexpr (kFresh) ssx = (fs[kHC + 0] + fs[kHC + 4]) + (fs[kHC + 7] + fs[kHC + 9]);
-        else ssx = fs[f_ssx<RM, NORM>()];
-        const float rx = 1.0f / sqrtf(ssx / (float)(kHC * d) + a.norm_eps);
-        if (lane < kHC) derive_outputs<RM, NORM>(fs, rx, lane, a, (int64_t)io.tile * kFT + tm);
-        __builtin_amdgcn_wave_barrier();
-      }
-      // read coefficients of item k-1: this wave takes tokens 4*mw .. 4*mw+3
-      if constexpr (kFast > 0) {
-        if (im.valid > 0) {
-          float s = 0.f;
-          for (int s0b = 0; s0b < S; s0b += kFPollBatch) {
-            u64 wv[kFPollBatch];
-#pragma unroll
-            for (int b = 0; b < kFPollBatch; ++b)
-              wv[b] = s0b == 0 ? fw[b]
-                               : ((fast_act && s0b + b < S) ? get_word(rm + ((size_t)(s0b + b) * kFT + ftm) * kFRec + fq) : 0ull);
-#pragma unroll
-            for (int b = 0; b < kFPollBatch; ++b)
-              if (fast_act && s0b + b < S) s += settle(rm + ((size_t)(s0b + b) * kFT + ftm) * kFRec + fq, wv[b], tag, err, dead);
-          }
-          __builtin_amdgcn_wave_barrier();
-          if (fast_act) fsum[mw][fi][fq] = s;
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          if (lane < 4 * kHC) {                          // quad per token: lane j of the quad = pre j
-            const int i2 = lane >> 2, j = lane & 3, t2 = 4 * mw + i2;
-            const float* fs = fsum[mw][i2];
-            float pre = 0.f, rnv = 1.f;
-            if constexpr (kFresh) {
-              const float ssx = (fs[kHC + 0] + fs[kHC + 4]) + (fs[kHC + 7] + fs[kHC + 9]);
-              const float rx = 1.0f / sqrtf(ssx / (float)(kHC * d) + a.norm_eps);
-              pre = sigmoidf_((fs[j] * rx) * a.hc_scale[0] + a.hc_base[j]) + a.hc_eps;
-              if constexpr (NORM) {
-                double pd[kHC];
-#pragma unroll
-                for (int l = 0; l < kHC; ++l) pd[l] = (double)__shfl(pre, (lane & ~3) + l);
-                double yy = 0.0;
-                int gi = 0;
-#pragma unroll
-                for (int l = 0; l < kHC; ++l)
-#pragma unroll
-                  for (int l2 = l; l2 < kHC; ++l2, ++gi) yy += (l == l2 ? 1.0 : 2.0) * pd[l] * pd[l2] * (double)fs[kHC + gi];
-                rnv = 1.0f / sqrtf((float)(yy / (double)d) + a.rms_eps);
-              }
-            } else {
-              rnv = 1.0f / sqrtf(fs[0] / (float)d + a.rms_eps);
-            }
-            coef[(k - 1) & 1][t2][j] = pre;
-            if (j == 0) coef[(k - 1) & 1][t2][kHC] = rnv;
-          }
-        }
-      }
-      // ---- staged inputs into LDS; the next item's first weight blocks
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int i = lt + u * kFMW * 64;
-        if (i < kCin) cin[(k + 1) & 1][i / (kCin / kFT)][i % (kCin / kFT)] = cv[u];
-      }
-      if constexpr (NORM) {
-        if (lt < kFF / 4) *reinterpret_cast<f32x4*>(&gam[(k - 1) & 1][4 * lt]) = gv;
-      }
-#pragma unroll
-      for (int j = 0; j < kFPre; ++j)
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) B[j][nt] = wt(j, nt);
-      __syncthreads();                                   // X(k)
-    }
-  }
-  // ---- the last workgroup out advances the call tag for the next call
-  if (threadIdx.x == 0) {
-    const u32 done = __hip_atomic_fetch_add(a.ctrl + kDoneWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (done == (u32)G - 1u) {
-      for (int i = 0; i < kEpochCopies; ++i)
-        __hip_atomic_store(a.ctrl + 16 * i, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.ctrl + kDoneWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-}
-
-// ======================================================= slice-resident boundary
-// sweep_kernel<NORM>: the boundary with the freshly derived pre -- hc_post,
-// hc_mixes on X', split and Sinkhorn, hc_pre with that pre (+ RMSNorm) -- in
-// one launch that reads X and delta once and never reads X' back ("Source
-// layer, pairs pooled": Block.forward; "Reading weights": the split kernel
-// panel; "Final RMSNorm").  Built for the pages' width, d = 5120, at hc = 4.
-//
-// The width is cut into 32 slices of 160 features of each stream.  Token tiles
-// (16 tokens) are dealt to the eight XCDs round robin (tile T to XCD T % 8);
-// on an XCD every tile passes through all 32 workgroups, workgroup p taking
-// slice p.  So a workgroup keeps one slice for the whole call and holds that
-// slice's packed projection weights (the B operands of the matrix cores) in
-// LDS, loaded once.  The grid is one workgroup per compute unit, all resident.
-//
-// Eight waves, two per SIMD: five stream waves (one lane per token and 8
-// features of the slice), the projection wave, and exchange waves A and B.
-// The stream waves never wait on global memory; the others never stream.
-// Interval k, one workgroup barrier per interval (tile indices local to the
-// XCD):
-//   stream waves: the read row (y, or z with the RMSNorm) of tile k-7 from its
-//     X' kept in registers (eight sets) and its coefficients in LDS; X' of
-//     tile k+1 from the loads of two intervals ago, stored and put in the LDS
-//     A tile; the loads of tile k+3.
-//   projection wave: the 24 dots of tile k on the matrix cores, published as
-//     words 0..23 of each token's record.
-//   wave A: sum x'^2 and the 10 Gram entries of tile k from the A tile,
-//     record words 24..35; the read coefficients of tile k-6 (requested an
-//     interval earlier) into LDS; post_in and comb_in of tile k+2.
-//   wave B (owner of one token of every other tile): sums the records of its
-//     token of tile k-3 over the 32 slices (requested an interval earlier),
-//     derives and publishes the read coefficients (pre, and the RMSNorm factor
-//     from p^T G p) with mixes, pre and post; or requests the records of tile
-//     k-2 and runs the Sinkhorn comb of its token of tile k-4.
-// Exchange words are 64-bit (value, tag) stored and loaded with device scope;
-// tags are the call epoch plus the tile index, so no ring slot needs clearing
-// and no store waits.  Every request is issued at the start of an interval
-// (ahead of the stream waves' burst in the compute unit's memory pipeline) and
-// used an interval later.  Waits are bounded: a timeout sets the error mask and
-// the call finishes with wrong values instead of hanging.  The last workgroup
-// to finish advances the epoch.
-constexpr int kWT = 16;                      // tokens per tile
-constexpr int kWX = 8;                       // XCDs: tile T goes to XCD T % 8
-constexpr int kWS = 32;                      // slices = workgroups per XCD
-constexpr int kWD = 5120;                    // the width the schedule is built for
-constexpr int kWF = kWD / kWS;               // 160 features per slice and stream
-constexpr int kWG8 = kWF / 8;                // 20 lanes per token
-constexpr int kWSt = kWF / kStepF;           // 5 matrix-core K steps per stream
-constexpr int kWSW = kWT * kWG8 / 64;        // 5 stream waves
-constexpr int kWThreads = (kWSW + 3) * 64;   // + exchange waves A, B and the projection wave
-constexpr int kWGrid = kWX * kWS;            // 256 workgroups
-constexpr int kWLag = 7;                     // read row of tile k - 7 in interval k
-constexpr int kWXS = kWLag + 1;              // X' register sets, tile % 8
-constexpr int kWRR = 16;                     // ring slots (records, read coefficients)
-constexpr int kWRec = 36;                    // record words used: 24 dots, sum x'^2, 10 Gram, pad
-constexpr int kWRecS = 48;                   // record stride (384 B, three 128-byte lines): dots in
-                                             // words 0..23, sum x'^2 / Gram / pad in words 32..43
-constexpr int kWSq = 32;                     // first sum-of-squares word
-constexpr int kWCin = kHC + kHC * kHC;       // post_in, comb_in per token
-constexpr int kWCoefW = 8;                   // read-coefficient words per token (5 used)
-constexpr int kWEpochWord = 1152;            // control block: 8 epoch copies, 64 bytes apart
-constexpr int kWDoneWord = 1280;
-constexpr int kWaitLds = 0xC07F;             // s_waitcnt lgkmcnt(0) only (vmcnt 63, expcnt 7 untouched)
-constexpr size_t kWRecBytes = sizeof(unsigned long long) * kWX * kWRR * kWS * kWT * kWRecS;
-constexpr size_t kWCoefBytes = sizeof(unsigned long long) * kWX * kWRR * kWT * kWCoefW;
-static_assert(kWSW * 64 == kWT * kWG8, "stream lanes cover the tile");
-static_assert(kWF % kStepF == 0, "slice is whole matrix-core steps");
-
-struct SweepArgs {
-  const hc_bf16* x;
-  const hc_bf16* delta;
-  const float* post_in;
-  const float* comb_in;
-  const u32x4* fn;
-  const float* gamma;
-  const float* hc_base;
-  const float* hc_scale;
-  hc_bf16* x_out;
-  hc_bf16* y_out;
-  float* mixes_out;
-  float* pre_out;
-  float* post_out;
-  float* comb_out;
-  u32* ctrl;          // workspace head (kCtrlBytes)
-  u64* rec;           // [kWX][kWRR][kWS][kWT][kWRecS] tagged words
-  u64* coef;          // [kWX][kWRR][kWT][kWCoefW]
-  int64_t n;
-  int ntiles, maxcnt, iters;
-  float hc_eps, norm_eps, rms_eps;
-};
-
-
-// Sum over the 4 lanes c, c+4, c+8, c+12 of a row of 16 (one column of a 4x4
-// block held one element per lane, lane 4j + c).  Rotating a row by 8 pairs
-// lane l with l^8; the pair sums are then rotated by 4, which lands in the
-// other pair whichever way the rotation runs: each lane adds the same two
-// pair sums, so all four lanes get the same bits.
-template <int CTRL>
-__device__ __forceinline__ float row_dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float col4_sum(float v) {
-  const float u = v + row_dpp<0x128>(v);          // row_ror:8
-  return u + row_dpp<0x124>(u);                   // row_ror:4
-}
-__device__ __forceinline__ float quad_max(float v) {
-  const float u = fmaxf(v, quad_perm<0xB1>(v));
-  return fmaxf(u, quad_perm<0x4E>(u));
-}
-
-template <bool NORM>
-__global__ void __launch_bounds__(kWThreads, 1) sweep_kernel(const SweepArgs a) {
-  __shared__ u32x4 w_lds[kWSt][kHC][kNT][64];      // the slice's weight tiles (100 KB)
-  __shared__ u32x4 a_lds[2][kWSt][kHC][64];        // X' in A layout, by tile parity (40 KB)
-  __shared__ float cin[2][kWT][kWCin];             // post_in, comb_in, by tile parity
-  __shared__ float bcl[2][kWT][kHC + 1];           // pre and RMSNorm factor, by tile parity
-  __shared__ float gsc[kWS][kWRec];                // owner: one token's records of all slices
-  __shared__ float tot[2][kWRec];                  // owner: summed, by tile parity
-
-  constexpr int d = kWD;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int x = blockIdx.x % kWX, p = blockIdx.x / kWX;
-  const int cnt = a.ntiles > x ? (a.ntiles - x + kWX - 1) / kWX : 0;   // tiles of this XCD
-  const int K = cnt > 0 ? cnt + kWLag : 0;                            // the last interval's k
-  // intervals k = -1 .. J-2: K + 1 of them, padded to a multiple of 8 (the
-  // stream waves' loop is unrolled eight times with no early exit)
-  const int J = (K + 1 + kWXS - 1) / kWXS * kWXS;
-  u32* err = a.ctrl + kErrWord;
-  const u32 epoch = __hip_atomic_load(a.ctrl + kWEpochWord + 16 * x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  auto tag_of = [&](int i) __attribute__((always_inline)) { return epoch + 1u + (u32)i; };
-  auto tok0 = [&](int i) __attribute__((always_inline)) { return (int64_t)(x + kWX * i) * kWT; };   // first token of local tile i
-  const int fs = p * kWF;                          // first feature of the slice (per stream)
-
-  // ---- the slice's weight tiles into LDS (once)
-  for (int idx = threadIdx.x; idx < kWSt * kHC * kNT * 64; idx += kWThreads) {
-    const int l = idx & 63, nt = (idx >> 6) % kNT, k = (idx / (64 * kNT)) % kHC, s = idx / (64 * kNT * kHC);
-    const int gstep = fs / kStepF + s;
-    w_lds[s][k][nt][l] = a.fn[((size_t)(gstep * kHC + k) * kNT + nt) * 64 + l];
-  }
-
-  if (wave < kWSW) {
-    // ======================================================== stream waves
-    // Every memory access goes through a buffer resource sized to the tile's
-    // valid tokens (0 for a tile past the end): tokens past n read zeros and
-    // store nothing, with no branch, so every interval issues the same memory
-    // instructions and the loads of the next two tiles stay in flight.
-    const int u = wave * 64 + lane;
-    const int tau = u / kWG8, g = u % kWG8;
-    const int f = fs + 8 * g;                      // this lane's first feature (per stream)
-    const int a_s = g >> 2, a_lane = (g & 3) * 16 + tau;
-    const u32 xoff = (u32)((tau * kHC * d + f) * 2), doff = (u32)((tau * d + f) * 2);
-    float gm[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) gm[e] = NORM ? a.gamma[f + e] : 1.f;
-    u32x4 LS[2][kHC + 1];                          // loads in flight, by tile parity
-    u32 XS[kWXS][kHC][4] = {};                     // X' kept for the read row, tile % 8
-    auto valid_of = [&](int i) __attribute__((always_inline)) -> u32 {
-      if (i < 0 || i >= cnt) return 0u;
-      const int64_t left = a.n - tok0(i);
-      return (u32)(left < kWT ? left : kWT);
-    };
-    auto issue = [&](int i, u32x4 (&L)[kHC + 1]) __attribute__((always_inline)) {
-      const u32 v = valid_of(i);
-      const int64_t t0 = v ? tok0(i) : 0;
-      const rsrc_t rx = make_rsrc(a.x + t0 * kHC * d, v * (u32)(kHC * d * 2));
-      const rsrc_t rd = make_rsrc(a.delta + t0 * d, v * (u32)(d * 2));
-#pragma unroll
-      for (int j = 0; j < kHC; ++j) L[j] = buf_ld(rx, xoff + (u32)(j * d * 2));
-      L[kHC] = buf_ld(rd, doff);
-    };
-    // X' of tile i: stored, and into the A tile
-    auto stream = [&](int i, const u32x4 (&L)[kHC + 1], u32 (&xp)[kHC][4]) __attribute__((always_inline)) {
-      const u32 v = valid_of(i);
-      const rsrc_t ro = make_rsrc(a.x_out + (v ? tok0(i) : 0) * kHC * d, v * (u32)(kHC * d * 2));
-      const float* c = cin[i & 1][tau];
-      float cpost[kHC], ccomb[kHC * kHC];
-#pragma unroll
-      for (int j = 0; j < kHC; ++j) cpost[j] = c[j];
-#pragma unroll
-      for (int j = 0; j < kHC * kHC; ++j) ccomb[j] = c[kHC + j];
-      post_8(L, cpost, ccomb, xp);
-#pragma unroll
-      for (int k = 0; k < kHC; ++k) buf_st(ro, xoff + (u32)(k * d * 2), u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]});
-#pragma unroll
-      for (int k = 0; k < kHC; ++k)
-        a_lds[i & 1][a_s][k][a_swz(a_lane, a_s & 1)] = u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]};
-    };
-    // the read row of tile i from its kept X'
-    auto read_row = [&](int i, const u32 (&xp)[kHC][4]) __attribute__((always_inline)) {
-      const u32 v = valid_of(i);
-      const rsrc_t ry = make_rsrc(a.y_out + (v ? tok0(i) : 0) * d, v * (u32)(d * 2));
-      const float* cf = bcl[i & 1][tau];
-      float pr[kHC];
-#pragma unroll
-      for (int j = 0; j < kHC; ++j) pr[j] = cf[j];
-      u32 yp[4];
-      pre_8(xp, pr, yp);
-      if constexpr (NORM) {
-        const float r = cf[kHC];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2)
-          yp[e2] = pack_bf16(gm[2 * e2] * (bf_lo(yp[e2]) * r), gm[2 * e2 + 1] * (bf_hi(yp[e2]) * r));
-      }
-      buf_st(ry, doff, u32x4{yp[0], yp[1], yp[2], yp[3]});
-    };
-
-    issue(0, LS[0]);
-    issue(1, LS[1]);
-    lds_barrier();                                 // weights, cin of tile 0 in place
-    // interval k = j - 1, j = r (mod 8): the register sets are compile-time indices
-    auto interval = [&](int j, auto R) __attribute__((always_inline)) {
-      constexpr int r = decltype(R)::v;
-      read_row(j - 1 - kWLag, XS[r]);
-      stream(j, LS[r & 1], XS[r]);
-      issue(j + 2, LS[r & 1]);
-      lds_barrier();
-    };
-    for (int j0 = 0; j0 < J; j0 += kWXS) {
-      interval(j0, IC<0>{});
-      interval(j0 + 1, IC<1>{});
-      interval(j0 + 2, IC<2>{});
-      interval(j0 + 3, IC<3>{});
-      interval(j0 + 4, IC<4>{});
-      interval(j0 + 5, IC<5>{});
-      interval(j0 + 6, IC<6>{});
-      interval(j0 + 7, IC<7>{});
-    }
-  } else if (wave == kWSW) {
-    // ======================================================== exchange wave A
-    // Each interval: the read coefficients of tile k-6 (from their owners)
-    // into LDS, post_in and comb_in of tile k+2, and the sums of squares and
-    // Gram entries of tile k (record words 24..35).  Its global loads are
-    // issued an interval before their data is used: in the compute unit's
-    // memory pipeline they queue behind the stream waves' loads.
-    bool dead = false;
-    // post_in and comb_in of tile i: issued early, written to LDS late
-    auto cin_load = [&](int i, float (&cv)[5]) __attribute__((always_inline)) {
-      const int64_t t0 = tok0(i);
-      const int tp = lane >> 2;                      // post_in: lane -> (token lane/4, stream lane%4)
-      cv[0] = t0 + tp < a.n ? a.post_in[t0 * kHC + lane] : 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {                  // comb_in: 256 floats, 4 per lane
-        const int e = lane + 64 * r;
-        cv[1 + r] = t0 + e / (kHC * kHC) < a.n ? a.comb_in[t0 * kHC * kHC + e] : 0.f;
-      }
-    };
-    auto cin_store = [&](int i, const float (&v)[5]) __attribute__((always_inline)) {
-      cin[i & 1][lane >> 2][lane & 3] = v[0];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int e = lane + 64 * r;
-        cin[i & 1][e / (kHC * kHC)][kHC + e % (kHC * kHC)] = v[1 + r];
-      }
-    };
-    const rsrc_t rrec = make_rsrc(a.rec, (u32)kWRecBytes);
-    // the read-coefficient words of tile i: lane w holds words w and w + 64 of
-    // the tile's 80 (token w / 5, word w % 5)
-    const int w0 = lane, w1 = lane + 64;
-    auto coef_ok = [&](int i, int w) __attribute__((always_inline)) {
-      return i >= 0 && i < cnt && w < kWT * (kHC + 1) && tok0(i) + w / (kHC + 1) < a.n;
-    };
-    auto coef_ptr = [&](int i, int w) __attribute__((always_inline)) -> const u64* {
-      return a.coef + ((size_t)(x * kWRR + (i >= 0 ? i % kWRR : 0)) * kWT + w / (kHC + 1)) * kWCoefW + w % (kHC + 1);
-    };
-    // requests alternate between two register sets (the loop below is unrolled
-    // twice), so that nothing waits for a load before the interval that uses it
-    u64 cw[2][2] = {{0, 0}, {0, 0}};
-    float cvv[2][5];
-    if (cnt > 0) { cin_load(0, cvv[0]); cin_store(0, cvv[0]); }
-    if (cnt > 1) cin_load(1, cvv[1]);
-    lds_barrier();
-    auto xa_interval = [&](int k, auto B) __attribute__((always_inline)) {
-      constexpr int b = decltype(B)::v;              // this interval's request set; 1 - b holds the last
-      const int ic = k - (kWLag - 1);                // consumed now; ic + 1 requested
-      // ---- this interval's requests first (ahead of the stream waves' loads
-      // in the CU's memory pipeline), used in the next interval: the read
-      // coefficients of tile k-5, post_in and comb_in of tile k+3
-      if (coef_ok(ic + 1, w0)) cw[b][0] = get_word(coef_ptr(ic + 1, w0));
-      if (coef_ok(ic + 1, w1)) cw[b][1] = get_word(coef_ptr(ic + 1, w1));
-      if (k + 3 < cnt) cin_load(k + 3, cvv[b]);
-      // ---- last interval's requests: the read coefficients of tile k-6 into
-      // LDS (a word not there yet is polled), post_in and comb_in of tile k+2
-      if (ic >= 0 && ic < cnt) {
-        const u32 tg = tag_of(ic);
-        if (coef_ok(ic, w0))
-          bcl[ic & 1][w0 / (kHC + 1)][w0 % (kHC + 1)] = settle(coef_ptr(ic, w0), cw[1 - b][0], tg, err, dead);
-        if (coef_ok(ic, w1))
-          bcl[ic & 1][w1 / (kHC + 1)][w1 % (kHC + 1)] = settle(coef_ptr(ic, w1), cw[1 - b][1], tg, err, dead);
-      }
-      if (k + 2 < cnt) cin_store(k + 2, cvv[1 - b]);
-      // ---- tile k: sum x'^2 and the Gram entries of each token from the A tile
-      // (X' of tile k), words 24..35 of its record.  Lane 4*tau + c takes the
-      // feature groups c, c+4, .., c+16 of token tau (all four streams each);
-      // the four lanes of a token then sum by DPP.
-      if (k >= 0 && k < cnt) {
-        const int tau = lane >> 2, c = lane & 3;
-        float sq[kGram + 1];
-#pragma unroll
-        for (int q = 0; q <= kGram; ++q) sq[q] = 0.f;
-#pragma unroll
-        for (int m = 0; m < kWG8 / 4; ++m) {
-          const int g = c + 4 * m, gs = g >> 2, gl = (g & 3) * 16 + tau;
-          u32x4 xv[kHC];
-#pragma unroll
-          for (int kk = 0; kk < kHC; ++kk) xv[kk] = a_lds[k & 1][gs][kk][a_swz(gl, gs & 1)];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-#pragma unroll
-            for (int kk = 0; kk < kHC; ++kk) sq[0] = dot2_bf16(xv[kk][e], xv[kk][e], sq[0]);
-            int q = 1;
-#pragma unroll
-            for (int j2 = 0; j2 < kHC; ++j2)
-#pragma unroll
-              for (int l2 = j2; l2 < kHC; ++l2, ++q) sq[q] = dot2_bf16(xv[j2][e], xv[l2][e], sq[q]);
-          }
-        }
-#pragma unroll
-        for (int q = 0; q <= kGram; ++q) sq[q] = quad_sum(sq[q]);
-        // the token's 12 words (sum x'^2, 10 Gram entries, a pad) in two runs of
-        // 16-byte stores: lanes c = 0..3 words 2c, 2c+1, then lanes c = 0, 1
-        // words 8 + 2c, 9 + 2c (every lane of a token holds all the sums)
-        const u32 tg = tag_of(k);
-        const u32 base = (u32)(((((x * kWRR + k % kWRR) * kWS + p) * kWT + tau) * kWRecS + kWSq) * sizeof(u64));
-        auto sq_at = [&](int q) __attribute__((always_inline)) {
-          float v = 0.f;
-#pragma unroll
-          for (int qq = 0; qq <= kGram; ++qq) v = q == qq ? sq[qq] : v;
-          return v;
-        };
-        auto put2 = [&](int q) __attribute__((always_inline)) {
-          __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(sq_at(q)), tg, __float_as_uint(sq_at(q + 1)), tg},
-                                                 rrec, base + (u32)(q * sizeof(u64)), 0, 16 /* device scope */);
-        };
-        put2(2 * c);
-        if (c < 2) put2(8 + 2 * c);
-      }
-      lds_barrier();
-    };
-    // intervals k = -1 .. J-2 (J is even): request set 0 at odd k, 1 at even k
-    for (int k = -1; k < J - 1; k += 2) {
-      xa_interval(k, IC<0>{});
-      xa_interval(k + 1, IC<1>{});
-    }
-  } else if (wave == kWSW + 2) {
-    // ======================================================== projection wave
-    // Interval k: the 24 dots of tile k on the matrix cores (X' in the LDS A
-    // tile, written by the stream waves in interval k-1; the slice's weight
-    // tiles resident in LDS), K-outer so that each A operand is read once;
-    // then the tile's dots are published, words 0..23 of the token records
-    // (tagged).  It never waits on global memory.
-    const rsrc_t rrec = make_rsrc(a.rec, (u32)kWRecBytes);
-    const int col = lane & 15, grp = lane >> 4;
-    lds_barrier();
-    for (int k = -1; k < J - 1; ++k) {
-      if (k >= 0 && k < cnt) {
-        f32x4 acc[kNT][2];
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) acc[nt][0] = acc[nt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // K step st = 4*s + kk; its A and five B operands are read from LDS two
-        // steps ahead of their matrix-core instructions (scheduling barriers
-        // keep the reads there)
-        constexpr int kSteps = kWSt * kHC, kAhead = 2;
-        u32x4 Ab[kAhead + 1], Bb[kAhead + 1][kNT];
-        auto fetch = [&](int st, u32x4& Ao, u32x4 (&Bo)[kNT]) __attribute__((always_inline)) {
-          const int s = st / kHC, kk = st % kHC;
-          Ao = a_lds[k & 1][s][kk][a_swz(lane, s & 1)];
-#pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) Bo[nt] = w_lds[s][kk][nt][lane];
-        };
-#pragma unroll
-        for (int st = 0; st < kAhead; ++st) fetch(st, Ab[st], Bb[st]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int st = 0; st < kSteps; ++st) {
-          if (st + kAhead < kSteps) fetch(st + kAhead, Ab[(st + kAhead) % (kAhead + 1)], Bb[(st + kAhead) % (kAhead + 1)]);
-          __builtin_amdgcn_sched_barrier(0);
-          const int b = st % (kAhead + 1), h = st & 1;
-          const bf16x8 A = __builtin_bit_cast(bf16x8, Ab[b]);
-#pragma unroll
-          for (int nt = 0; nt < kNT; ++nt)
-            acc[nt][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, Bb[b][nt]), acc[nt][h], 0,
-                                                                0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        const u32 tg = tag_of(k);
-        const u32 slot_base = (u32)((((x * kWRR + k % kWRR) * kWS + p) * kWT) * kWRecS * sizeof(u64));
-        auto put = [&](int tau, int q, float v) __attribute__((always_inline)) {
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, tag_word(v, tg)), rrec,
-                                                slot_base + (u32)((tau * kWRecS + q) * sizeof(u64)), 0,
-                                                16 /* device scope */);
-        };
-        // dots: lane holds rows (tokens) 4*grp + r of column col of each weight tile
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float t0 = acc[0][0][r] + acc[0][1][r], t1 = acc[1][0][r] + acc[1][1][r];
-          const float t2 = acc[2][0][r] + acc[2][1][r], t3 = acc[3][0][r] + acc[3][1][r];
-          const float t4 = acc[4][0][r] + acc[4][1][r];
-          const float d0 = (t0 + t1) + t2;                      // row col: hi + mid + lo
-          const float d1 = (t3 + row_dpp<0x128>(t3)) + t4;      // row 16 + col (col < 8): hi, mid, lo
-          put(4 * grp + r, col, d0);
-          if (col < 8) put(4 * grp + r, 16 + col, d1);
-        }
-      }
-      lds_barrier();
-    }
-  } else {
-    // ======================================================== exchange wave B (owner)
-    // A slice owns one token of every other tile.  Interval k, owner of a token
-    // of tile k-3: its records from all 32 slices (published three intervals
-    // ago, requested at the start of the last interval) are checked and summed
-    // in slice order, and the read coefficients (pre and the RMSNorm factor)
-    // are derived and published at once, with the mixes, pre and post.
-    // Interval k, owner of a token of tile k-2 and k-4: the records of tile k-2
-    // are requested, and the Sinkhorn comb of the token of tile k-4 runs (only
-    // an output, nothing in the call waits for it).
-    bool dead = false;
-    const rsrc_t rrec = make_rsrc(a.rec, (u32)kWRecBytes);
-    auto owned = [&](int i) __attribute__((always_inline)) -> int {   // token of tile i this slice owns, or -1
-      const int tau = p - kWT * (i & 1);
-      if (i < 0 || i >= cnt || tau < 0 || tau >= kWT || tok0(i) + tau >= a.n) return -1;
-      return tau;
-    };
-    constexpr int kGL = kWS * kWRec / 2 / 64;        // 16-byte loads per lane (9)
-    static_assert(kGL * 64 * 2 == kWS * kWRec, "gather covers all record words");
-    // chunk c: slice c / 18, compact words 2h, 2h+1 (h = c % 18) at record word
-    // 2h (dots, h < 12) or kWSq + 2(h - 12) (the sums)
-    auto cword = [&](int c) __attribute__((always_inline)) {
-      const int h = c % (kWRec / 2);
-      return h < kMix / 2 ? 2 * h : kWSq + 2 * (h - kMix / 2);
-    };
-    // the split parameters, loaded once: no later parameter load waits behind
-    // this wave's device-scope stores (one in-order counter covers both)
-    const float s0 = a.hc_scale[0], s1 = a.hc_scale[1], s2 = a.hc_scale[2];
-    const float base_m = lane < kMix ? a.hc_base[lane] : 0.f;                  // base[lane]
-    const float base_c = lane < kHC * kHC ? a.hc_base[2 * kHC + lane] : 0.f;   // base[8 + lane]
-    auto base_at = [&](int q) __attribute__((always_inline)) {
-      return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, base_m), q));
-    };
-    // the records of the owned token of tile i, lane: words 2c, 2c+1, c = lane + 64r
-    auto goff = [&](int i, int tau, int r) __attribute__((always_inline)) -> u32 {
-      const int c = lane + 64 * r, s = c / (kWRec / 2);
-      return (u32)(((((x * kWRR + i % kWRR) * kWS + s) * kWT + tau) * kWRecS + cword(c)) * sizeof(u64));
-    };
-    u32x4 gv[kGL];                                   // requested at the start of the interval before
-    lds_barrier();
-    for (int k = -1; k < J - 1; ++k) {
-      // ---- request the records of tile k-2 (published two intervals ago),
-      // first in the interval: summed in the next one
-      const int in = k - 2, tn = owned(in);
-      if (tn >= 0) {
-#pragma unroll
-        for (int r = 0; r < kGL; ++r) gv[r] = __builtin_amdgcn_raw_buffer_load_b128(rrec, goff(in, tn, r), 0, 16);
-      }
-      // ---- tile k-3: check the records, sum, read coefficients, mixes, pre, post
-      const int ig = k - 3, tg_tau = owned(ig);
-      if (tg_tau >= 0) {
-        const u32 tg = tag_of(ig);
-        unsigned polls = 0;
-        while (!dead) {
-          bool ok = true;
-#pragma unroll
-          for (int r = 0; r < kGL; ++r) ok = ok && gv[r][1] == tg && gv[r][3] == tg;
-          if (__all(ok)) break;
-          if (++polls > kPollLimit) { if (lane == 0) atomicOr(err, kErrPollTimeout); dead = true; break; }
-          __builtin_amdgcn_s_sleep(2);
-#pragma unroll
-          for (int r = 0; r < kGL; ++r) gv[r] = __builtin_amdgcn_raw_buffer_load_b128(rrec, goff(ig, tg_tau, r), 0, 16);
-        }
-#pragma unroll
-        for (int r = 0; r < kGL; ++r) {
-          const int c = lane + 64 * r;
-          *reinterpret_cast<f32x2*>(&gsc[(2 * c) / kWRec][(2 * c) % kWRec]) =
-              f32x2{__uint_as_float(gv[r][0]), __uint_as_float(gv[r][2])};
-        }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_s_waitcnt(kWaitLds);
-        // lane q < 36 sums word q over the slices in slice order (all reads first)
-        float sacc = 0.f;
-        if (lane < kWRec) {
-          float v[kWS];
-#pragma unroll
-          for (int s = 0; s < kWS; ++s) v[s] = gsc[s][lane];
-          sacc = v[0];
-#pragma unroll
-          for (int s = 1; s < kWS; ++s) sacc = sacc + v[s];
-          tot[ig & 1][lane] = sacc;                  // for the comb, next interval
-        }
-        // the words the read needs, as wave-uniform values
-        auto word = [&](int q) __attribute__((always_inline)) {
-          return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sacc), q));
-        };
-        const int64_t t = tok0(ig) + tg_tau;
-        const float rx = 1.0f / sqrtf(word(kMix) / (float)(kHC * d) + a.norm_eps);
-        float pre[kHC];
-#pragma unroll
-        for (int l = 0; l < kHC; ++l) pre[l] = sigmoidf_((word(l) * rx) * s0 + base_at(l)) + a.hc_eps;
-        float rn = 1.f;
-        if constexpr (NORM) {
-          // sum_i y_i^2 = p^T G p over the whole row
-          double yy = 0.0;
-          int q = 0;
-#pragma unroll
-          for (int l = 0; l < kHC; ++l)
-#pragma unroll
-            for (int l2 = l; l2 < kHC; ++l2, ++q)
-              yy += (l == l2 ? 1.0 : 2.0) * (double)pre[l] * (double)pre[l2] * (double)word(kMix + 1 + q);
-          rn = 1.0f / sqrtf((float)(yy / (double)d) + a.rms_eps);
-        }
-        u64* cw = a.coef + ((size_t)(x * kWRR + ig % kWRR) * kWT + tg_tau) * kWCoefW;
-        if (lane <= kHC) put_word(cw + lane, tag_word(lane == 0 ? pre[0] : lane == 1 ? pre[1] : lane == 2 ? pre[2]
-                                                        : lane == 3 ? pre[3] : rn, tg));
-        if (a.mixes_out && lane < kMix) a.mixes_out[t * kMix + lane] = sacc * rx;
-        if (lane < kHC) {
-          const float pj = lane == 0 ? pre[0] : lane == 1 ? pre[1] : lane == 2 ? pre[2] : pre[3];
-          a.pre_out[t * kHC + lane] = pj;
-        } else if (lane < 2 * kHC) {
-          a.post_out[t * kHC + lane - kHC] = 2.0f * sigmoidf_((sacc * rx) * s1 + base_m);
-        }
-      }
-      // ---- tile k-4: the comb, softmax (+eps) along the rows, a column step,
-      // then iters-1 rounds of (row, column)
-      const int ih = k - 4, th = owned(ih);
-      if (th >= 0 && lane < kHC * kHC) {
-        const float* rc = tot[ih & 1];
-        const float rx = 1.0f / sqrtf(rc[kMix] / (float)(kHC * d) + a.norm_eps);
-        float A = (rc[2 * kHC + lane] * rx) * s2 + base_c;
-        const float mxr = quad_max(A);
-        A = expf(A - mxr);
-        A = A * __builtin_amdgcn_rcpf(quad_sum(A)) + a.hc_eps;
-        A = A * __builtin_amdgcn_rcpf(col4_sum(A) + a.hc_eps);
-        for (int it = 1; it < a.iters; ++it) {
-          A = A * __builtin_amdgcn_rcpf(quad_sum(A) + a.hc_eps);
-          A = A * __builtin_amdgcn_rcpf(col4_sum(A) + a.hc_eps);
-        }
-        a.comb_out[(tok0(ih) + th) * kHC * kHC + lane] = A;
-      }
-      lds_barrier();
-    }
-  }
-  // ---- the last workgroup out advances the epoch for the next call
-  if (threadIdx.x == 0) {
-    const u32 done = __hip_atomic_fetch_add(a.ctrl + kWDoneWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (done == (u32)kWGrid - 1u) {
-      for (int i = 0; i < kWX; ++i)
-        __hip_atomic_store(a.ctrl + kWEpochWord + 16 * i, epoch + 2u + (u32)a.maxcnt, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.ctrl + kWDoneWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-}
-
 // ======================================================= decode boundary
 // decode_kernel<POST, READ>: the boundary for few tokens in one launch, the
 // finalize (split + Sinkhorn) done by the last feature slice of each token tile
@@ -2417,8 +1518,8 @@ constexpr int kDThreads = 256;               // 4 waves: 2 steps each in the pro
 constexpr int kDRec = 25;                    // record words per token: 24 dots, sum x'^2
 constexpr int kDMaxN = 128;                  // decode schedule up to this many tokens (measured crossover)
 constexpr int kDTiles = kDMaxN / kDT;        // tiles at most (the region is sized for them)
-constexpr int kDArriveBytes = 256;           // arrival, epoch and tiles-done words: head of the decode region
-static_assert(kDArriveBytes >= (kDTiles + 2) * (int)sizeof(unsigned long long), "arrival words");
+constexpr int kDMaxD = 8192;                 // widest row of the decode schedule (the region is sized for it)
+static_assert(kCtlDecArrive + kDTiles <= kCtlDecEpoch, "decode arrival words fit before the epoch word");
 
 struct DecArgs {
   const hc_bf16* x;
@@ -2438,7 +1539,7 @@ struct DecArgs {
   float* comb_out;
   int xtok, xstr;     // elements per token / per stream of x (hc*d, d; or d, 0 when expanded)
   u64* rec;           // [tiles][S][kDT][kDRec] tagged words
-  u64* arrive;        // [kDTiles] arrival words, then the epoch word and the tiles-done word
+  u64* ctl;           // the workspace's control block (arrival, epoch and tiles-done words)
   u32* err;           // sticky error mask (a wait timed out)
   int tiles;
   int64_t n;
@@ -2477,9 +1578,9 @@ __global__ void __launch_bounds__(kDThreads) decode_kernel(const DecArgs a) {
   const unsigned lt = tv ? (unsigned)m : 0u;
 
   // ---- the call's epoch
-  u64* arw = a.arrive + tile;
-  u64* epw = a.arrive + kDTiles;
-  u64* donew = a.arrive + kDTiles + 1;
+  u64* arw = a.ctl + kCtlDecArrive + tile;
+  u64* epw = a.ctl + kCtlDecEpoch;
+  u64* donew = a.ctl + kCtlDecDone;
   if (threadIdx.x == 0) s_tag = (u32)get_word(epw) + 1u;   // words carry epoch + 1
 
   // ---- all loads up front: the weight tiles of this wave's two steps, the
@@ -2683,6 +1784,12 @@ __global__ void __launch_bounds__(kDThreads) decode_kernel(const DecArgs a) {
   }
 }
 
+// one 32-bit word set to zero (a kernel rather than a memset, so that it may
+// sit in a captured graph)
+__global__ void clear_word_kernel(u32* w) {
+  if (threadIdx.x == 0) *w = 0u;
+}
+
 // ------------------------------------------------------------------ host side
 thread_local char g_err[512];
 
@@ -2695,6 +1802,13 @@ int fail(int code, const char* fmt, ...) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a + na) and [b, b + nb) share a byte (both non-empty)
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
 
 bool hc_known(int hc) { return hc == 2 || hc == kHC || hc == 8; }
 
@@ -2756,29 +1870,26 @@ size_t split_records_bytes(int64_t n, int d) {
   const int64_t tiles = (n + kTT - 1) / kTT;
   return (size_t)tiles * stream_slices(n, d) * kTT * kRec * 4;
 }
-bool fused_shape(int d) { return d % kFF == 0 && d >= kFMinD && d <= kMaxD; }
-size_t fused_records_bytes(int64_t n, int d) {
-  if (!fused_shape(d)) return 0;
-  const int64_t tiles = (n + kFT - 1) / kFT;
-  return (size_t)tiles * (d / kFF) * kFT * kFRec * sizeof(u64);
-}
-// decode schedule: given pre (or no read), no RMSNorm, few tokens.  Its region
-// has a fixed place and size for a width d (whatever n), so a record slot only
-// ever holds words of the same tile.
-bool decode_shape(int64_t n, int d) { return n <= kDMaxN && d % kDF == 0; }
-size_t decode_region_bytes(int d) {
-  if (d % kDF != 0) return 0;
-  return kDArriveBytes + (size_t)kDTiles * (d / kDF) * kDT * kDRec * sizeof(u64);
-}
-// slice-resident schedule (hc = 4, d = 5120): record ring, flags, read-coefficient words.
-// Its region has a fixed place for a width d and nothing else writes there.
-bool sweep_shape(int d) { return d == kWD; }
-size_t sweep_region_bytes(int d) { return sweep_shape(d) ? kWRecBytes + kWCoefBytes : 0; }
-size_t fixed_region_bytes(int d) { return kCtrlBytes + decode_region_bytes(d) + sweep_region_bytes(d); }
-// [control block][decode arrival words + records][slice-resident ring][single-launch records][two-kernel records]
-size_t workspace_bytes(int64_t n, int d) {
-  return fixed_region_bytes(d) + fused_records_bytes(n, d) + split_records_bytes(n, d);
-}
+// Workspace layout, the same for every (n, hc, d), so that one workspace
+// serves calls of any shape and no region of one call lies on the persistent
+// words of another:
+//   [control block, kCtrlBytes]  error mask, the decode schedule's arrival /
+//                                epoch / tiles-done words, the read-row
+//                                exchange's epoch and done words
+//   [decode records]             [kDTiles][kDMaxD/kDF][kDT][kDRec] tagged words
+//   [read-row exchange words]    [kXMaxGroups][kTT] tagged words
+//   [per-slice records]          two-launch schedule (hc = 4) or hc = 2, 8;
+//                                plain floats, rewritten by every call
+// Tagged words carry their schedule's call epoch + 1; the epochs only grow, so
+// a word left by an earlier call (of any shape) never holds a current tag.
+bool decode_shape(int64_t n, int d) { return n <= kDMaxN && d % kDF == 0 && d <= kDMaxD; }
+constexpr size_t kDecRegionBytes = (size_t)kDTiles * (kDMaxD / kDF) * kDT * kDRec * sizeof(u64);
+constexpr int kXMaxGroups = 256;             // workgroups of one read-row exchange at most
+constexpr size_t kXRegionBytes = (size_t)kXMaxGroups * kTT * kXW * sizeof(u64);
+constexpr size_t kDecOffset = kCtrlBytes;
+constexpr size_t kXOffset = kDecOffset + kDecRegionBytes;
+constexpr size_t kRecOffset = kXOffset + kXRegionBytes;
+size_t workspace_bytes(int64_t n, int d) { return kRecOffset + split_records_bytes(n, d); }
 
 template <bool POST, int RM, bool NORM>
 hipError_t launch_stream_t(const StreamArgs& a, unsigned grid, hipStream_t st) {
@@ -2788,6 +1899,24 @@ hipError_t launch_stream_t(const StreamArgs& a, unsigned grid, hipStream_t st) {
                             : reinterpret_cast<const void*>(&stream_kernel<POST, RM, NORM, false>);
   return hipLaunchKernel(fn, dim3(grid), dim3(kThreads),
                          args, 0, st);
+}
+// the given-pre boundary with the RMSNorm in one launch (read row kept, slice YK chunks wide)
+template <bool POST, int YK>
+hipError_t launch_exchange_t(const StreamArgs& a, unsigned grid, hipStream_t st) {
+  StreamArgs copy = a;
+  void* args[] = {&copy};
+  const void* fn = a.x_mean ? reinterpret_cast<const void*>(&stream_kernel<POST, kGivenPre, true, true, YK>)
+                            : reinterpret_cast<const void*>(&stream_kernel<POST, kGivenPre, true, false, YK>);
+  return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, st);
+}
+// The read-row exchange takes slices of 10 or 20 chunks (640 or 1280 features),
+// at most 8 slices and kXMaxGroups workgroups.
+int exchange_chunks(int64_t n, int d) {
+  const int64_t tiles = (n + kTT - 1) / kTT;
+  const int S = stream_slices(n, d);
+  const int yk = d / S / kCF;
+  if ((yk != 10 && yk != 20) || S > 8 || tiles * S > kXMaxGroups) return 0;
+  return yk;
 }
 template <int RM, bool NORM>
 hipError_t launch_finish_t(const FinishArgs& a, unsigned grid, hipStream_t st) {
@@ -2800,7 +1929,7 @@ hipError_t launch_finish_t(const FinishArgs& a, unsigned grid, hipStream_t st) {
 // s: streams, pre_in, x_out/y_out set; f: split parameters and outputs, gamma set.
 // phases: bit 0 the stream kernel, bit 1 the finish kernel.
 int launch_boundary(bool post, int rm, bool norm, StreamArgs s, FinishArgs f, void* ws, size_t ws_bytes,
-                    hipStream_t st, const char* what, int phases = 3) {
+                    hipStream_t st, const char* what, int phases = 3, bool exchange = false) {
   const size_t need = workspace_bytes(s.n, s.d);
   if (!ws) return fail(HC_EINVAL, "%s: workspace must not be NULL (need %zu bytes)", what, need);
   if (!aligned16(ws)) return fail(HC_EINVAL, "%s: workspace is not 16-byte aligned", what);
@@ -2810,9 +1939,24 @@ int launch_boundary(bool post, int rm, bool norm, StreamArgs s, FinishArgs f, vo
   s.S = stream_slices(s.n, s.d);
   s.F = s.d / s.S;
   s.tiles = (int)tiles;
-  s.rec = reinterpret_cast<float*>(static_cast<char*>(ws) + fixed_region_bytes(s.d) + fused_records_bytes(s.n, s.d));
+  s.rec = reinterpret_cast<float*>(static_cast<char*>(ws) + kRecOffset);
   const unsigned grid1 = (unsigned)(tiles * s.S);
   hipError_t e = hipSuccess;
+  const int yk = exchange && phases == 3 && rm == kGivenPre && norm ? exchange_chunks(s.n, s.d) : 0;
+  if (yk) {
+    // the words of every (tile, slice) group stay inside the exchange region
+    if ((size_t)tiles * s.S * kTT * kXW * sizeof(u64) > kXRegionBytes)
+      return fail(HC_ENOTSUP, "%s: %lld exchange groups exceed the region", what, (long long)(tiles * s.S));
+    s.ctl = static_cast<u64*>(ws);
+    s.xw = reinterpret_cast<u64*>(static_cast<char*>(ws) + kXOffset);
+    s.err = static_cast<u32*>(ws) + kErrWord;
+    s.gamma = f.gamma; s.hc_base = f.hc_base; s.hc_scale = f.hc_scale; s.mixes_out = f.mixes_out;
+    s.pre_out = f.pre_out; s.post_out = f.post_out; s.comb_out = f.comb_out; s.iters = f.iters;
+    s.hc_eps = f.hc_eps; s.norm_eps = f.norm_eps; s.rms_eps = f.rms_eps;
+    if (post) e = yk == 20 ? launch_exchange_t<true, 20>(s, grid1, st) : launch_exchange_t<true, 10>(s, grid1, st);
+    else e = yk == 20 ? launch_exchange_t<false, 20>(s, grid1, st) : launch_exchange_t<false, 10>(s, grid1, st);
+    return launched(e, what);
+  }
   if (phases & 1) switch ((post ? 8 : 0) | (rm << 1) | (norm ? 1 : 0)) {
     case 0x0: e = launch_stream_t<false, kNoRead, false>(s, grid1, st); break;
     case 0x2: e = launch_stream_t<false, kGivenPre, false>(s, grid1, st); break;
@@ -2858,9 +2002,10 @@ int launch_decode(bool post, bool read, DecArgs a, void* ws, size_t ws_bytes, hi
   if (ws_bytes < need) return fail(HC_EINVAL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, need);
   a.S = a.d / kDF;
   const int64_t tiles = (a.n + kDT - 1) / kDT;
-  char* base = static_cast<char*>(ws) + kCtrlBytes;
-  a.arrive = reinterpret_cast<u64*>(base);
-  a.rec = reinterpret_cast<u64*>(base + kDArriveBytes);
+  a.ctl = static_cast<u64*>(ws);
+  a.rec = reinterpret_cast<u64*>(static_cast<char*>(ws) + kDecOffset);
+  if ((size_t)((a.n + kDT - 1) / kDT) * (a.d / kDF) * kDT * kDRec * sizeof(u64) > kDecRegionBytes)
+    return fail(HC_ENOTSUP, "%s: the decode records exceed their region", what);
   a.err = static_cast<u32*>(ws) + kErrWord;
   a.tiles = (int)tiles;
   const unsigned grid = (unsigned)(tiles * a.S);
@@ -2872,120 +2017,6 @@ int launch_decode(bool post, bool read, DecArgs a, void* ws, size_t ws_bytes, hi
     default: e = launch_decode_t<true, true>(a, grid, st); break;
   }
   return launched(e, what);
-}
-
-// ---- single-launch boundary
-template <bool POST, int RM, bool NORM>
-hipError_t launch_fused_t(const FusedArgs& a, unsigned grid, hipStream_t st) {
-  FusedArgs copy = a;
-  void* args[] = {&copy};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fused_kernel<POST, RM, NORM>), dim3(grid), dim3(kFThreads),
-                         args, 0, st);
-}
-const void* fused_fn(bool post, int rm, bool norm) {
-  switch ((post ? 4 : 0) | (rm == kFreshPre ? 2 : 0) | (norm ? 1 : 0)) {
-    case 0: return reinterpret_cast<const void*>(&fused_kernel<false, kGivenPre, false>);
-    case 1: return reinterpret_cast<const void*>(&fused_kernel<false, kGivenPre, true>);
-    case 2: return reinterpret_cast<const void*>(&fused_kernel<false, kFreshPre, false>);
-    case 3: return reinterpret_cast<const void*>(&fused_kernel<false, kFreshPre, true>);
-    case 4: return reinterpret_cast<const void*>(&fused_kernel<true, kGivenPre, false>);
-    case 5: return reinterpret_cast<const void*>(&fused_kernel<true, kGivenPre, true>);
-    case 6: return reinterpret_cast<const void*>(&fused_kernel<true, kFreshPre, false>);
-    default: return reinterpret_cast<const void*>(&fused_kernel<true, kFreshPre, true>);
-  }
-}
-// Workgroups of a variant that can be resident at once on the current device
-// (compute units x workgroups per unit), queried once per device and variant.
-int fused_capacity(bool post, int rm, bool norm) {
-  constexpr int kDevs = 64;
-  static int cache[kDevs][8];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 0;
-  const int v = (post ? 4 : 0) | (rm == kFreshPre ? 2 : 0) | (norm ? 1 : 0);
-  int c = __atomic_load_n(&cache[dev][v], __ATOMIC_RELAXED);
-  if (c == 0) {
-    int cus = 0, occ = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fused_fn(post, rm, norm), kFThreads, 0) != hipSuccess)
-      return 0;
-    c = cus * occ > 0 ? cus * occ : -1;
-    __atomic_store_n(&cache[dev][v], c, __ATOMIC_RELAXED);
-  }
-  return c > 0 ? c : 0;
-}
-
-int launch_fused(bool post, int rm, bool norm, FusedArgs f, void* ws, size_t ws_bytes, hipStream_t st,
-                 const char* what) {
-  const size_t need = workspace_bytes(f.n, f.d);
-  if (!ws) return fail(HC_EINVAL, "%s: workspace must not be NULL (need %zu bytes)", what, need);
-  if (!aligned16(ws)) return fail(HC_EINVAL, "%s: workspace is not 16-byte aligned", what);
-  if (ws_bytes < need) return fail(HC_EINVAL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, need);
-  f.S = f.d / kFF;
-  const int64_t tiles = (f.n + kFT - 1) / kFT;
-  const int64_t items = tiles * f.S;
-  const int cap = fused_capacity(post, rm, norm);
-  const int64_t g = std::min<int64_t>(items, (int64_t)(cap / f.S) * f.S);
-  if (g < f.S) return fail(HC_ENOTSUP, "%s: the device holds %d resident workgroups, %d are needed", what, cap, f.S);
-  f.tiles = (int)tiles;
-  f.items = (int)items;
-  f.rounds = (int)((items + g - 1) / g);
-  f.ctrl = static_cast<u32*>(ws);
-  f.rec = reinterpret_cast<u64*>(static_cast<char*>(ws) + fixed_region_bytes(f.d));
-  const unsigned grid = (unsigned)g;
-  hipError_t e;
-  switch ((post ? 4 : 0) | (rm == kFreshPre ? 2 : 0) | (norm ? 1 : 0)) {
-    case 0: e = launch_fused_t<false, kGivenPre, false>(f, grid, st); break;
-    case 1: e = launch_fused_t<false, kGivenPre, true>(f, grid, st); break;
-    case 2: e = launch_fused_t<false, kFreshPre, false>(f, grid, st); break;
-    case 3: e = launch_fused_t<false, kFreshPre, true>(f, grid, st); break;
-    case 4: e = launch_fused_t<true, kGivenPre, false>(f, grid, st); break;
-    case 5: e = launch_fused_t<true, kGivenPre, true>(f, grid, st); break;
-    case 6: e = launch_fused_t<true, kFreshPre, false>(f, grid, st); break;
-    default: e = launch_fused_t<true, kFreshPre, true>(f, grid, st); break;
-  }
-  return launched(e, what);
-}
-
-// The slice-resident schedule needs its whole grid resident: one workgroup on
-// each of the 256 compute units (8 XCDs x 32).  Checked once per device.
-bool sweep_device_ok(bool norm) {
-  constexpr int kDevs = 64;
-  static int cache[kDevs][2];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return false;
-  int c = __atomic_load_n(&cache[dev][norm], __ATOMIC_RELAXED);
-  if (c == 0) {
-    int cus = 0, occ = 0;
-    const void* fn = norm ? reinterpret_cast<const void*>(&sweep_kernel<true>)
-                          : reinterpret_cast<const void*>(&sweep_kernel<false>);
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kWThreads, 0) != hipSuccess)
-      return false;
-    c = (cus == kWGrid && occ >= 1) ? 1 : -1;
-    __atomic_store_n(&cache[dev][norm], c, __ATOMIC_RELAXED);
-  }
-  return c > 0;
-}
-
-int launch_sweep(bool norm, SweepArgs a, void* ws, size_t ws_bytes, hipStream_t st, const char* what) {
-  const size_t need = workspace_bytes(a.n, kWD);
-  if (!ws) return fail(HC_EINVAL, "%s: workspace must not be NULL (need %zu bytes)", what, need);
-  if (!aligned16(ws)) return fail(HC_EINVAL, "%s: workspace is not 16-byte aligned", what);
-  if (ws_bytes < need) return fail(HC_EINVAL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, need);
-  if (!sweep_device_ok(norm))
-    return fail(HC_ENOTSUP, "%s: the slice-resident schedule needs %d resident workgroups (one per compute unit)",
-                what, kWGrid);
-  const int64_t tiles = (a.n + kWT - 1) / kWT;
-  a.ntiles = (int)tiles;
-  a.maxcnt = (int)((tiles + kWX - 1) / kWX);
-  char* base = static_cast<char*>(ws);
-  a.ctrl = static_cast<u32*>(ws);
-  a.rec = reinterpret_cast<u64*>(base + kCtrlBytes + decode_region_bytes(kWD));
-  a.coef = reinterpret_cast<u64*>(reinterpret_cast<char*>(a.rec) + kWRecBytes);
-  void* args[] = {&a};
-  const void* fn = norm ? reinterpret_cast<const void*>(&sweep_kernel<true>)
-                        : reinterpret_cast<const void*>(&sweep_kernel<false>);
-  return launched(hipLaunchKernel(fn, dim3(kWGrid), dim3(kWThreads), args, 0, st), what);
 }
 
 template <bool POST, bool PRE, bool NORM, int TPW, int HC = kHC>
@@ -3057,7 +2088,7 @@ int gen_slices(int64_t n, int hc, int d) {
 // workspace of the hc != 4 path: the per-slice records, placed after the
 // control block and the decode region of the same d so that a workspace
 // shared with hc = 4 calls keeps their words intact
-size_t gen_rec_offset(int d) { return fixed_region_bytes(d); }
+size_t gen_rec_offset(int) { return kRecOffset; }
 size_t generic_ws_bytes(int64_t n, int hc, int d) {
   return gen_rec_offset(d) + (size_t)gen_slices(n, hc, d) * n * gen_recw(hc) * 4;
 }
@@ -3229,6 +2260,7 @@ int hc_pre(const hc_bf16* x, const float* pre_mix, int64_t n, int hc, int d, hc_
   if (rc) return rc;
   if ((rc = check_n(n))) return rc;
   HC_REQ(x); HC_REQ(pre_mix); HC_REQ(y);
+  if (overlap(y, (size_t)n * d * 2, x, (size_t)n * hc * d * 2)) return fail(HC_EINVAL, "y overlaps x");
   if (n == 0) return HC_OK;
   if ((rc = check_device())) return rc;
   RowArgs a{};
@@ -3243,7 +2275,11 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
   if (rc) return rc;
   if ((rc = check_n(n))) return rc;
   HC_REQ(delta); HC_REQ(x); HC_REQ(post); HC_REQ(comb); HC_REQ(x_out);
-  if (x_out == x) return fail(HC_EINVAL, "x_out must not alias x");
+  {
+    const size_t sb = (size_t)n * hc * d * 2, rb = (size_t)n * d * 2;
+    if (overlap(x_out, sb, x, sb)) return fail(HC_EINVAL, "x_out overlaps x");
+    if (overlap(x_out, sb, delta, rb)) return fail(HC_EINVAL, "x_out overlaps delta");
+  }
   if (n == 0) return HC_OK;
   if ((rc = check_device())) return rc;
   RowArgs a{};
@@ -3254,6 +2290,40 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
 
 size_t hc_boundary_workspace_bytes(int64_t n, int hc, int d) { return hc_workspace_bytes(n, hc, d); }
 
+int hc_workspace_layout(int64_t n, int hc, int d, size_t regions[8]) {
+  g_err[0] = 0;
+  if (!regions) return fail(HC_EINVAL, "regions must not be NULL");
+  int rc = check_hd(hc, d);
+  if (rc) return rc;
+  if ((rc = check_n(n))) return rc;
+  regions[0] = 0;            regions[1] = kCtrlBytes;
+  regions[2] = kDecOffset;   regions[3] = kDecRegionBytes;
+  regions[4] = kXOffset;     regions[5] = kXRegionBytes;
+  regions[6] = kRecOffset;
+  regions[7] = n == 0 ? 0 : (hc == kHC ? split_records_bytes(n, d) : generic_ws_bytes(n, hc, d) - kRecOffset);
+  return HC_OK;
+}
+
+int hc_workspace_status(void* workspace, size_t workspace_bytes, int clear, uint32_t* mask, void* stream) {
+  g_err[0] = 0;
+  HC_REQ(workspace);
+  if (!mask) return fail(HC_EINVAL, "mask must not be NULL");
+  if (workspace_bytes < (size_t)kCtrlBytes)
+    return fail(HC_EINVAL, "workspace has %zu bytes, the control block alone is %d", workspace_bytes, kCtrlBytes);
+  int rc;
+  if ((rc = check_device())) return rc;
+  const hipStream_t st = (hipStream_t)stream;
+  u32* word = static_cast<u32*>(workspace) + kErrWord;
+  hipError_t e = hipMemcpyAsync(mask, word, sizeof(u32), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(HC_EHIP, "reading the error mask: %s", hipGetErrorName(e));
+  if (clear) {
+    hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(64), 0, st, word);
+    return launched(hipGetLastError(), "clear_word_kernel");
+  }
+  return HC_OK;
+}
+
 static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) {
   g_err[0] = 0;
   if (!p) return fail(HC_EINVAL, "args must not be NULL");
@@ -3263,10 +2333,8 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
   const uint32_t flags = p->struct_size >= kNoFlags + sizeof(uint32_t) ? p->flags : 0u;
   constexpr size_t kNoMean = offsetof(hc_boundary_args, x_mean_out);   // callers of the struct without it
   hc_bf16* const x_mean = p->struct_size >= kNoMean + sizeof(void*) ? p->x_mean_out : nullptr;
-  if (flags & ~(HC_BOUNDARY_SINGLE_LAUNCH | HC_BOUNDARY_X_EXPANDED | HC_BOUNDARY_SLICE_RESIDENT))
+  if (flags & ~(HC_BOUNDARY_X_EXPANDED | HC_BOUNDARY_TWO_LAUNCH))
     return fail(HC_EINVAL, "flags=%#x: unknown bits", flags);
-  if ((flags & HC_BOUNDARY_SINGLE_LAUNCH) && (flags & HC_BOUNDARY_SLICE_RESIDENT))
-    return fail(HC_EINVAL, "flags=%#x: pick one schedule", flags);
   const bool expanded = (flags & HC_BOUNDARY_X_EXPANDED) != 0;
   int rc = check_hd(p->hc, p->d);
   if (rc) return rc;
@@ -3276,8 +2344,7 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
   const bool fresh = p->pre_in == nullptr;
   const bool norm = p->gamma != nullptr;
   HC_REQ(p->x); HC_REQ(p->y_out); HC_OPT(p->delta); HC_OPT(p->pre_in); HC_OPT(p->gamma); HC_OPT(x_mean);
-  if (post) { HC_REQ(p->post_in); HC_REQ(p->comb_in); HC_REQ(p->x_out);
-    if (p->x_out == p->x) return fail(HC_EINVAL, "x_out must not alias x"); }
+  if (post) { HC_REQ(p->post_in); HC_REQ(p->comb_in); HC_REQ(p->x_out); }
   if (mix) {
     HC_REQ(p->fn_packed); HC_REQ(p->hc_base); HC_REQ(p->hc_scale);
     HC_REQ(p->pre_out); HC_REQ(p->post_out); HC_REQ(p->comb_out); HC_OPT(p->mixes_out);
@@ -3286,22 +2353,17 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
   if (fresh && !mix) return fail(HC_EINVAL, "pre_in is NULL but no mixes are derived (fn_packed is NULL)");
   if (norm && p->d > kRowChunk * kRowMaxChunks * 2)
     return fail(HC_ENOTSUP, "RMSNorm of the read row supports d <= %d", kRowChunk * kRowMaxChunks * 2);
-  if (flags & HC_BOUNDARY_SINGLE_LAUNCH) {
-    if (p->hc != kHC) return fail(HC_ENOTSUP, "the single-launch schedule needs hc=4");
-    if (expanded || x_mean) return fail(HC_ENOTSUP, "the single-launch schedule takes neither expanded streams nor x_mean_out");
-    if (phases != 3) return fail(HC_EINVAL, "the single-launch schedule has no halves (use hc_boundary)");
-    if (!mix) return fail(HC_EINVAL, "the single-launch schedule needs fn_packed");
-    if (!fused_shape(p->d)) return fail(HC_ENOTSUP, "single launch: d=%d must be a multiple of %d, at least %d", p->d, kFF, kFMinD);
-    if (p->n > kFusedMaxN) return fail(HC_ENOTSUP, "single launch: n=%lld is too large", (long long)p->n);
-  }
-  if (flags & HC_BOUNDARY_SLICE_RESIDENT) {
-    if (p->hc != kHC || !sweep_shape(p->d))
-      return fail(HC_ENOTSUP, "the slice-resident schedule needs hc=4 and d=%d", kWD);
-    if (expanded || x_mean) return fail(HC_ENOTSUP, "the slice-resident schedule takes neither expanded streams nor x_mean_out");
-    if (phases != 3) return fail(HC_EINVAL, "the slice-resident schedule has no halves (use hc_boundary)");
-    if (!mix || !post || !fresh)
-      return fail(HC_ENOTSUP, "the slice-resident schedule needs delta and fn_packed, and pre_in NULL");
-    if (p->n > kFusedMaxN) return fail(HC_ENOTSUP, "slice-resident: n=%lld is too large", (long long)p->n);
+  {  // the outputs may not overlap the streams they are formed from, nor each other
+    const size_t n = (size_t)p->n, hc = (size_t)p->hc, d = (size_t)p->d;
+    const size_t xb = n * (expanded ? 1 : hc) * d * 2, sb = n * hc * d * 2, rb = n * d * 2;
+    if (post && overlap(p->x_out, sb, p->x, xb)) return fail(HC_EINVAL, "x_out overlaps x");
+    if (post && overlap(p->x_out, sb, p->delta, rb)) return fail(HC_EINVAL, "x_out overlaps delta");
+    if (overlap(p->y_out, rb, p->x, xb)) return fail(HC_EINVAL, "y_out overlaps x");
+    if (post && overlap(p->y_out, rb, p->x_out, sb)) return fail(HC_EINVAL, "y_out overlaps x_out");
+    if (overlap(p->y_out, rb, p->delta, rb)) return fail(HC_EINVAL, "y_out overlaps delta");
+    if (x_mean && overlap(x_mean, rb, p->y_out, rb)) return fail(HC_EINVAL, "x_mean_out overlaps y_out");
+    if (x_mean && overlap(x_mean, rb, p->x, xb)) return fail(HC_EINVAL, "x_mean_out overlaps x");
+    if (x_mean && post && overlap(x_mean, rb, p->x_out, sb)) return fail(HC_EINVAL, "x_mean_out overlaps x_out");
   }
   if (p->n == 0) return HC_OK;
   if ((rc = check_device())) return rc;
@@ -3316,25 +2378,6 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
     r.pre_in = p->pre_in; r.gamma = p->gamma; r.x_out = p->x_out; r.y_out = p->y_out; r.rms_eps = p->rms_eps;
     r.xtok = xtok; r.xstr = xstr; r.x_mean = x_mean;
     return launch_row(post, true, norm, r, st, "hc_boundary (exit)", p->hc);
-  }
-  if (flags & HC_BOUNDARY_SLICE_RESIDENT) {
-    SweepArgs w{};
-    w.n = p->n; w.x = p->x; w.delta = p->delta; w.post_in = p->post_in; w.comb_in = p->comb_in;
-    w.fn = reinterpret_cast<const u32x4*>(p->fn_packed); w.gamma = p->gamma; w.hc_base = p->hc_base;
-    w.hc_scale = p->hc_scale; w.x_out = p->x_out; w.y_out = p->y_out; w.mixes_out = p->mixes_out;
-    w.pre_out = p->pre_out; w.post_out = p->post_out; w.comb_out = p->comb_out; w.iters = p->iters;
-    w.hc_eps = p->hc_eps; w.norm_eps = p->norm_eps; w.rms_eps = p->rms_eps;
-    return launch_sweep(norm, w, p->workspace, p->workspace_bytes, st, "hc_boundary");
-  }
-  if (flags & HC_BOUNDARY_SINGLE_LAUNCH) {
-    FusedArgs f{};
-    f.n = p->n; f.d = p->d; f.x = p->x; f.delta = p->delta; f.post_in = p->post_in; f.comb_in = p->comb_in;
-    f.pre_in = p->pre_in; f.fn = reinterpret_cast<const u32x4*>(p->fn_packed); f.gamma = p->gamma;
-    f.hc_base = p->hc_base; f.hc_scale = p->hc_scale; f.x_out = p->x_out; f.y_out = p->y_out;
-    f.mixes_out = p->mixes_out; f.pre_out = p->pre_out; f.post_out = p->post_out; f.comb_out = p->comb_out;
-    f.iters = p->iters; f.hc_eps = p->hc_eps; f.norm_eps = p->norm_eps; f.rms_eps = p->rms_eps;
-    return launch_fused(post, fresh ? kFreshPre : kGivenPre, norm, f, p->workspace, p->workspace_bytes, st,
-                        "hc_boundary");
   }
   if (p->hc != kHC) {
     // hc 2 or 8: the write, the projection, the split and the read as separate
@@ -3370,7 +2413,8 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
     }
     return HC_OK;
   }
-  if (phases == 3 && !fresh && !norm && decode_shape(p->n, p->d)) {
+  const bool two = (flags & HC_BOUNDARY_TWO_LAUNCH) != 0;
+  if (phases == 3 && !two && !fresh && !norm && decode_shape(p->n, p->d)) {
     DecArgs a{};
     a.n = p->n; a.d = p->d; a.x = p->x; a.delta = p->delta; a.post_in = p->post_in; a.comb_in = p->comb_in;
     a.pre_in = p->pre_in; a.fn = reinterpret_cast<const u32x4*>(p->fn_packed); a.hc_base = p->hc_base;
@@ -3388,7 +2432,7 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
   f.pre_out = p->pre_out; f.post_out = p->post_out; f.comb_out = p->comb_out; f.iters = p->iters;
   f.hc_eps = p->hc_eps; f.norm_eps = p->norm_eps; f.rms_eps = p->rms_eps;
   return launch_boundary(post, fresh ? kFreshPre : kGivenPre, norm, s, f, p->workspace, p->workspace_bytes, st,
-                         "hc_boundary", phases);
+                         "hc_boundary", phases, !two);
 }
 
 int hc_boundary(const hc_boundary_args* p, void* stream) { return boundary_phases(p, stream, 3); }

@@ -20,9 +20,8 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhc.so")
 
 HC_OK, HC_EINVAL, HC_ENOTSUP, HC_EHIP, HC_ENODEV = 0, -1, -2, -3, -4
-HC_BOUNDARY_SINGLE_LAUNCH = 1
 HC_BOUNDARY_X_EXPANDED = 4
-HC_BOUNDARY_SLICE_RESIDENT = 8
+HC_BOUNDARY_TWO_LAUNCH = 16
 
 
 class HCError(RuntimeError):
@@ -65,6 +64,8 @@ SIGNATURES = {
     "hc_boundary_begin": (c_int, [ctypes.POINTER(BoundaryArgs), c_void_p]),
     "hc_boundary_end": (c_int, [ctypes.POINTER(BoundaryArgs), c_void_p]),
     "hc_boundary_workspace_bytes": (c_size_t, [c_int64, c_int, c_int]),
+    "hc_workspace_status": (c_int, [c_void_p, c_size_t, c_int, ctypes.POINTER(c_uint32), c_void_p]),
+    "hc_workspace_layout": (c_int, [c_int64, c_int, c_int, ctypes.POINTER(c_size_t)]),
 }
 
 _lib = None
@@ -116,6 +117,16 @@ def workspace(n: int, hc: int, d: int, device) -> torch.Tensor | None:
         ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
+
+
+def workspace_status(ws: torch.Tensor, clear: bool = False) -> int:
+    """The sticky error mask of a workspace (hc_workspace_status): bit 0 set if
+    a call on it waited for another workgroup's words until its bound.
+    Synchronises the current stream; with clear, resets the mask."""
+    mask = c_uint32(0)
+    _check(lib().hc_workspace_status(ws.data_ptr(), ws.numel(), 1 if clear else 0, ctypes.byref(mask),
+                                     _stream(ws.device)), "hc_workspace_status")
+    return int(mask.value)
 
 
 def _need(t, name, dtype, device=None, shape=None):
@@ -238,8 +249,8 @@ def hc_post(x, residual, post, comb, out=None):
 def _prepare_boundary(x, *, delta=None, post_in=None, comb_in=None, pre_in=None, fn_packed=None,
                       hc_base=None, hc_scale=None, gamma=None, iters: int = 20, hc_eps: float = 1e-6,
                       norm_eps: float = 1e-6, rms_eps: float = 1e-6, out: dict | None = None,
-                      want_mixes: bool = False, single_launch: bool = False, x_expanded: bool = False,
-                      want_mean: bool = False, hc_mult: int = 4, slice_resident: bool = False):
+                      want_mixes: bool = False, x_expanded: bool = False, want_mean: bool = False,
+                      hc_mult: int = 4, two_launch: bool = False):
     """Checks the arguments of one boundary call, allocates missing outputs and
     fills the C argument struct.  Returns (struct, outputs).  hc_mult is the
     number of streams of an expanded x (otherwise x's shape gives it)."""
@@ -294,8 +305,7 @@ def _prepare_boundary(x, *, delta=None, post_in=None, comb_in=None, pre_in=None,
     a.gamma, a.x_out, a.y_out = _ptr(gamma), _ptr(o.get("x_out")), o["y"].data_ptr()
     a.mixes_out, a.pre_out = _ptr(o.get("mixes")), _ptr(o.get("pre"))
     a.post_out, a.comb_out = _ptr(o.get("post")), _ptr(o.get("comb"))
-    a.flags = ((HC_BOUNDARY_SINGLE_LAUNCH if single_launch else 0) | (HC_BOUNDARY_X_EXPANDED if x_expanded else 0)
-               | (HC_BOUNDARY_SLICE_RESIDENT if slice_resident else 0))
+    a.flags = (HC_BOUNDARY_X_EXPANDED if x_expanded else 0) | (HC_BOUNDARY_TWO_LAUNCH if two_launch else 0)
     a.x_mean_out = _ptr(o.get("x_mean"))
     if fn_packed is not None:
         ws = o.get("workspace")
@@ -310,10 +320,9 @@ def _prepare_boundary(x, *, delta=None, post_in=None, comb_in=None, pre_in=None,
 def hc_boundary(x, **kw):
     """One fused sublayer boundary (see include/hc.h).  Keyword arguments:
     delta, post_in, comb_in, pre_in, fn_packed, hc_base, hc_scale, gamma, iters,
-    hc_eps, norm_eps, rms_eps, out, want_mixes, single_launch (the
-    HC_BOUNDARY_SINGLE_LAUNCH schedule), slice_resident (the
-    HC_BOUNDARY_SLICE_RESIDENT schedule), x_expanded (x is [..., d], every
-    stream that row: HC_BOUNDARY_X_EXPANDED; hc_mult then gives the number of
+    hc_eps, norm_eps, rms_eps, out, want_mixes, two_launch (the
+    HC_BOUNDARY_TWO_LAUNCH schedule), x_expanded (x is [..., d], every stream
+    that row: HC_BOUNDARY_X_EXPANDED; hc_mult then gives the number of
     streams), want_mean (the mean over the streams, "x_mean").  Returns a dict with x_out (None at a block entry), y,
     and pre/post/comb (+ mixes) unless fn_packed is None.
     ``out`` may hold preallocated outputs under the same keys (and a
