@@ -279,6 +279,21 @@ typedef struct hc_boundary_args {
 int hc_boundary(const hc_boundary_args* args, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * hc_boundary_static -- hc_boundary for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same call, but args->workspace and workspace_bytes
+ * are ignored and the library's own static device workspace is used instead
+ * (16 MiB on each GPU the library runs on, held until the process ends; zero
+ * when the library is loaded).  It allocates nothing.  Shapes whose workspace
+ * (hc_workspace_bytes) exceeds 16 MiB return HC_ENOTSUP -- hc = 4 fits up to
+ * about 80 000 tokens at d = 5120.  Every call on one GPU shares that GPU's
+ * static workspace, which keeps the last call's contents: calls that may
+ * overlap on one GPU (different streams, different threads) race and must be
+ * serialised by the caller.  Same status codes as hc_boundary.
+ * ------------------------------------------------------------------------- */
+int hc_boundary_static(const hc_boundary_args* args, void* stream);
+
+/* ---------------------------------------------------------------------------
  * hc_boundary_begin / hc_boundary_end -- hc_boundary in two halves, for a
  * caller that places other work between them or times them apart.  With
  * fn_packed, begin enqueues the streaming pass (x_out; with pre_in, y; the

@@ -29,11 +29,13 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <utility>
 #include <cstdarg>
 #include <cstdint>
 #include <cstddef>
 #include <cstdio>
+#include <cstring>
 
 #include "hc.h"
 
@@ -1784,6 +1786,14 @@ __global__ void __launch_bounds__(kDThreads) decode_kernel(const DecArgs a) {
   }
 }
 
+// The library's own workspace for hc_boundary_static, one copy per GPU the
+// library runs on (held until the process ends).  Zero when the code object
+// is loaded, as a fresh caller workspace must be; every call leaves it valid
+// for the next (the tagged words' call epochs only grow).  Host code uses the
+// per-device address from hipGetSymbolAddress, never the name itself.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
 // one 32-bit word set to zero (a kernel rather than a memset, so that it may
 // sit in a captured graph)
 __global__ void clear_word_kernel(u32* w) {
@@ -1793,12 +1803,37 @@ __global__ void clear_word_kernel(u32* w) {
 // ------------------------------------------------------------------ host side
 thread_local char g_err[512];
 
+
 int fail(int code, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
   vsnprintf(g_err, sizeof g_err, fmt, ap);
   va_end(ap);
   return code;
+}
+
+// The device address of the static scratch on the current device, looked up
+// once per device (nullptr and HC_EHIP detail on failure).
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+void* static_scratch(int* rc) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *rc = fail(HC_ENODEV, "no current HIP device: %s", hipGetErrorName(e));
+    return nullptr;
+  }
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *rc = fail(HC_EHIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorName(e));
+      return nullptr;
+    }
+    g_scratch[dev].store(p, std::memory_order_release);   // the same value whichever thread wins
+  }
+  *rc = HC_OK;
+  return p;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -2436,6 +2471,29 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
 }
 
 int hc_boundary(const hc_boundary_args* p, void* stream) { return boundary_phases(p, stream, 3); }
+
+int hc_boundary_static(const hc_boundary_args* p, void* stream) {
+  g_err[0] = 0;
+  if (!p) return fail(HC_EINVAL, "args must not be NULL");
+  if (p->struct_size < offsetof(hc_boundary_args, flags))
+    return fail(HC_EINVAL, "struct_size=%u, expected %zu", p->struct_size, sizeof(hc_boundary_args));
+  hc_boundary_args a{};
+  memcpy(&a, p, std::min<size_t>(p->struct_size, sizeof a));
+  a.struct_size = (uint32_t)std::min<size_t>(p->struct_size, sizeof a);
+  int rc = check_hd(a.hc, a.d);
+  if (rc) return rc;
+  if ((rc = check_n(a.n))) return rc;
+  const size_t need = hc_workspace_bytes(a.n, a.hc, a.d);
+  if (a.fn_packed && need > kStaticScratchBytes)
+    return fail(HC_ENOTSUP, "n=%lld, hc=%d, d=%d needs %zu workspace bytes; the static workspace holds %zu",
+                (long long)a.n, a.hc, a.d, need, kStaticScratchBytes);
+  if (a.n == 0) return boundary_phases(&a, stream, 3);
+  if ((rc = check_device())) return rc;
+  a.workspace = static_scratch(&rc);
+  if (!a.workspace) return rc;
+  a.workspace_bytes = kStaticScratchBytes;
+  return boundary_phases(&a, stream, 3);
+}
 int hc_boundary_begin(const hc_boundary_args* p, void* stream) { return boundary_phases(p, stream, 1); }
 int hc_boundary_end(const hc_boundary_args* p, void* stream) { return boundary_phases(p, stream, 2); }
 

@@ -61,6 +61,7 @@ SIGNATURES = {
     "hc_post": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int, c_int, c_void_p,
                         c_void_p]),
     "hc_boundary": (c_int, [ctypes.POINTER(BoundaryArgs), c_void_p]),
+    "hc_boundary_static": (c_int, [ctypes.POINTER(BoundaryArgs), c_void_p]),
     "hc_boundary_begin": (c_int, [ctypes.POINTER(BoundaryArgs), c_void_p]),
     "hc_boundary_end": (c_int, [ctypes.POINTER(BoundaryArgs), c_void_p]),
     "hc_boundary_workspace_bytes": (c_size_t, [c_int64, c_int, c_int]),
@@ -250,7 +251,7 @@ def _prepare_boundary(x, *, delta=None, post_in=None, comb_in=None, pre_in=None,
                       hc_base=None, hc_scale=None, gamma=None, iters: int = 20, hc_eps: float = 1e-6,
                       norm_eps: float = 1e-6, rms_eps: float = 1e-6, out: dict | None = None,
                       want_mixes: bool = False, x_expanded: bool = False, want_mean: bool = False,
-                      hc_mult: int = 4, two_launch: bool = False):
+                      hc_mult: int = 4, two_launch: bool = False, own_workspace: bool = True):
     """Checks the arguments of one boundary call, allocates missing outputs and
     fills the C argument struct.  Returns (struct, outputs).  hc_mult is the
     number of streams of an expanded x (otherwise x's shape gives it)."""
@@ -307,7 +308,7 @@ def _prepare_boundary(x, *, delta=None, post_in=None, comb_in=None, pre_in=None,
     a.post_out, a.comb_out = _ptr(o.get("post")), _ptr(o.get("comb"))
     a.flags = (HC_BOUNDARY_X_EXPANDED if x_expanded else 0) | (HC_BOUNDARY_TWO_LAUNCH if two_launch else 0)
     a.x_mean_out = _ptr(o.get("x_mean"))
-    if fn_packed is not None:
+    if fn_packed is not None and own_workspace:
         ws = o.get("workspace")
         if ws is None:
             ws = workspace(n, hc, d, dev)
@@ -329,6 +330,15 @@ def hc_boundary(x, **kw):
     "workspace"); they are used as given."""
     a, o = _prepare_boundary(x, **kw)
     _check(lib().hc_boundary(ctypes.byref(a), _stream(x.device)), "hc_boundary")
+    return o
+
+
+def hc_boundary_static(x, **kw):
+    """hc_boundary on the library's static device workspace (include/hc.h,
+    hc_boundary_static): the same keyword arguments, no workspace allocated
+    or passed.  Returns the output dict of hc_boundary (without a workspace)."""
+    a, o = _prepare_boundary(x, **kw, own_workspace=False)
+    _check(lib().hc_boundary_static(ctypes.byref(a), _stream(x.device)), "hc_boundary_static")
     return o
 
 
