@@ -5,26 +5,28 @@
 One step = one sublayer-boundary call over the whole 4096-token batch (the
 prefill workload: B=1, T=4096, hc=4, d=5120, 20 Sinkhorn rounds, RMSNorm):
 hc_post(delta, X, post, comb) -> hc_mixes on X' -> split/Sinkhorn -> hc_pre ->
-RMSNorm.  The call is two kernels of libhc (stream_kernel, then
-finish_kernel).  --mode fresh (the default) reads X' with the pre this call
-derives; --mode lag with the pre of the previous boundary (the data flow of
-the pages' Block.forward).  Inputs are seeded synthetic tensors
+RMSNorm.  --mode fresh (the default) reads X' with the pre this call
+derives: two kernels of libhc (stream_kernel, then finish_kernel, which reads
+X' back).  --mode lag reads with the pre of the previous boundary (the data
+flow of the pages' Block.forward): one kernel, X read once, the workgroups of
+a token tile exchanging their per-slice sums on chip.  Both modes are timed
+and reported; --mode picks the headline.  Inputs are seeded synthetic tensors
 (transformer_hyper_connection_amd.synth, workload "prefill"), resident in HBM
 before timing; several input/output buffer sets rotate.  Prints one JSON line.
 
 Beside the headline line: the decode block's glue (n=128, "decode"), the
 same boundary at hc = 2 and 8 ("other_hc") and at n = 128 ... 32768
 ("sweep"), the calls at the stand-in stack's two ends ("stack_ends"), the
-standalone entry points ("entry_points") and the headline call on the two
-opt-in one-launch schedules ("other_schedules"), each timed by events.
+standalone entry points ("entry_points") and the given-pre call on its two
+schedules, one launch and two ("schedules"), each timed by events.
 
 Timing: after half a second of plain streaming (GPU clocks settle; the first
 ~20 ms after idle run several percent slower), W untimed warm-up steps; then
 K steps timed by the host clock between two device synchronisations (value,
 ms_per_step); then K more steps between two events on the launch stream (the
-roofline: algorithmic bytes of a call / mean event time of a call); then K
-more with events also between the two kernels of each call (each kernel's
-share; those events add a few microseconds per call).
+roofline: algorithmic bytes of a call / mean event time of a call); then, for
+a two-kernel call, K more with events also between its two kernels (each
+kernel's share; those events add a few microseconds per call).
 """
 from __future__ import annotations
 
@@ -53,8 +55,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_boundary_prefill_t4096.js
 #                    per call   hc_fn (fp32) 24*4d*4 + base 96 + scale 12 + gamma d*4
 BYTES_TOKEN_COMMON = 4 * D * 2 + D * 2 + 4 * D * 2 + D * 2 + 16 + 64 + 96
 BYTES_CALL = MIX * 4 * D * 4 + MIX * 4 + 3 * 4 + D * 4
-KERNELS = {"fresh": ("stream_kernel<true, 2, true, false>", "finish_kernel<2, true>"),
-           "lag": ("stream_kernel<true, 1, true, false>", "finish_kernel<1, true>")}
+# the kernels of one call as rocprofv3 names them (the last template argument of
+# stream_kernel is the read-row exchange's slice width in chunks, 0 for none)
+KERNELS = {"fresh": ("stream_kernel<true, 2, true, false, 0>", "finish_kernel<2, true>"),
+           "lag": ("stream_kernel<true, 1, true, false, 20>",)}
 
 
 def algorithmic_bytes(n: int, mode: str) -> int:
@@ -108,6 +112,9 @@ def time_mode(mode, sets, params, steps, warmup):
     e1.record(stream)
     torch.cuda.synchronize()
     mean_call = e0.elapsed_time(e1) / steps
+    out = {"wall_s": wall, "host_enqueue_us_per_call": host_enqueue / steps * 1e6, "mean_call_ms": mean_call}
+    if len(KERNELS[mode]) == 1:
+        return out
     # and once more with an event before, between and after the two kernels of
     # each call: their split (the events themselves add a few microseconds)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
@@ -122,8 +129,7 @@ def time_mode(mode, sets, params, steps, warmup):
     k1 = [e[0].elapsed_time(e[1]) for e in ev]
     k2 = [e[1].elapsed_time(e[2]) for e in ev]
     call = [e[0].elapsed_time(e[2]) for e in ev]
-    return {"wall_s": wall, "host_enqueue_us_per_call": host_enqueue / steps * 1e6, "mean_call_ms": mean_call,
-            "call_ms": call, "stream_kernel_ms": k1, "finish_kernel_ms": k2}
+    return {**out, "call_ms": call, "stream_kernel_ms": k1, "finish_kernel_ms": k2}
 
 
 def settle_clocks(dev, seconds=0.5):
@@ -303,29 +309,30 @@ def sweep(dev, ns=(128, 512, 4096, 32768), reps=50):
                         "(n=32768: channel-outlier stress inputs)", **out}
 
 
-def other_schedules(dev, s, reps=50):
-    """The headline call (write, fresh pre, RMSNorm; n = 4096, hc = 4, d = 5120)
-    on libhc's two opt-in one-launch schedules: HC_BOUNDARY_SINGLE_LAUNCH and
-    HC_BOUNDARY_SLICE_RESIDENT (each workgroup keeps a feature slice of the
-    weights in LDS and X' of its last tiles in registers; no X' read-back).
-    Event-timed like the sweep; the default two-launch schedule beside them."""
+def schedules(dev, s, reps=50):
+    """The given-pre call (write, read with the previous boundary's pre,
+    RMSNorm; n = 4096, hc = 4, d = 5120) on its two schedules: one launch (the
+    default: the workgroups of a token tile exchange their per-slice sums on
+    chip, y stays in registers until its mean square is known) and two
+    launches (HC_BOUNDARY_TWO_LAUNCH: per-slice records, y written and read
+    back by the finishing kernel).  Event-timed like the sweep."""
     out = {}
-    ins = {k: (bf(s[k], dev) if k in ("x", "delta") else f32(s[k], dev)) for k in ("x", "delta", "post_in", "comb_in")}
+    ins = {k: (bf(s[k], dev) if k in ("x", "delta") else f32(s[k], dev))
+           for k in ("x", "delta", "post_in", "comb_in", "pre_in")}
     params = dict(fn_packed=T.hc_fn_pack(f32(s["hc_fn"], dev)), hc_base=f32(s["hc_base"], dev),
                   hc_scale=f32(s["hc_scale"], dev), gamma=f32(s["gamma"], dev))
-    nbytes = algorithmic_bytes(N_TOK, "fresh")
-    for name, kw in (("two_launch", {}), ("single_launch", {"single_launch": True}),
-                     ("slice_resident", {"slice_resident": True})):
-        print(f"[bench] timing the {name} schedule", file=sys.stderr, flush=True)
+    nbytes = algorithmic_bytes(N_TOK, "lag")
+    for name, kw in (("one_launch", {}), ("two_launch", {"two_launch": True})):
+        print(f"[bench] timing the given-pre call, {name}", file=sys.stderr, flush=True)
         call = T.BoundaryCall(ins["x"], delta=ins["delta"], post_in=ins["post_in"], comb_in=ins["comb_in"],
-                              **params, **kw)
+                              pre_in=ins["pre_in"], **params, **kw)
         us = timed_calls([call.run], min_reps=reps) * 1e3
         out[name] = {"call_us": round(us, 2), "gbs": round(nbytes / us / 1e3, 1),
                      "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
         del call
     torch.cuda.empty_cache()
-    return {"workload": "fused sublayer boundary, prefill B=1 T=4096, hc=4, d=5120, fresh pre, RMSNorm, by schedule",
-            **out}
+    return {"workload": "fused sublayer boundary, prefill B=1 T=4096, hc=4, d=5120, given pre, RMSNorm, "
+                        "by schedule", **out}
 
 
 def entry_points(dev, s, reps=50):
@@ -443,7 +450,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the token-count sweep")
     ap.add_argument("--no-stack-ends", action="store_true", help="skip the stack entry / exit timing")
     ap.add_argument("--no-entry-points", action="store_true", help="skip the standalone entry-point timing")
-    ap.add_argument("--no-schedules", action="store_true", help="skip the one-launch schedules' timing")
+    ap.add_argument("--no-schedules", action="store_true", help="skip the given-pre schedules' timing")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this benchmark runs on one GPU only.  The glue is per token and would shard over "
@@ -465,16 +472,18 @@ def main():
         print(f"[bench] timing mode={mode}", file=sys.stderr, flush=True)
         r = time_mode(mode, sets, params, args.steps, args.warmup)
         nbytes = algorithmic_bytes(N_TOK, mode)
-        call = stats(r["call_ms"])
         results[mode] = {
             "wall_s": r["wall_s"], "ms_per_step": r["wall_s"] / args.steps * 1e3,
             "tokens_per_s": N_TOK * args.steps / r["wall_s"], "algorithmic_bytes": nbytes,
-            "mean_call_ms": r["mean_call_ms"],
-            "split_call_ms": call, "stream_kernel_ms": stats(r["stream_kernel_ms"]),
-            "finish_kernel_ms": stats(r["finish_kernel_ms"]),
+            "mean_call_ms": r["mean_call_ms"], "kernels": list(KERNELS[mode]),
             "gbs_at_mean_call": nbytes / (r["mean_call_ms"] * 1e-3) / 1e9,
+            "frac_at_mean_call": nbytes / (r["mean_call_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "host_enqueue_us_per_call": r["host_enqueue_us_per_call"],
         }
+        if "call_ms" in r:
+            results[mode].update({"split_call_ms": stats(r["call_ms"]),
+                                  "stream_kernel_ms": stats(r["stream_kernel_ms"]),
+                                  "finish_kernel_ms": stats(r["finish_kernel_ms"])})
     ref_gbs = None if args.no_copy else reference_stream(dev)
     head = results[args.mode]
     mean_ms = head["mean_call_ms"]
@@ -485,7 +494,7 @@ def main():
     swp = None if args.no_sweep else sweep(dev)
     ends = None if args.no_stack_ends else stack_ends(dev)
     eps = None if args.no_entry_points else entry_points(dev, s)
-    sch = None if args.no_schedules else other_schedules(dev, s)
+    sch = None if args.no_schedules else schedules(dev, s)
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -516,11 +525,12 @@ def main():
                    "tokens": N_TOK, "read_mode": args.mode, "buffer_sets": args.sets},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_bytes,
-                     "kernel": f"hc_boundary = {KERNELS[args.mode][0]} + {KERNELS[args.mode][1]}",
+                     "kernel": "hc_boundary = " + " + ".join(KERNELS[args.mode]),
                      "algorithmic_bytes_per_launch": head["algorithmic_bytes"],
                      "avg_launch_ms": round(mean_ms, 5),
-                     "stream_kernel_avg_ms": round(head["stream_kernel_ms"]["mean"], 5),
-                     "finish_kernel_avg_ms": round(head["finish_kernel_ms"]["mean"], 5),
+                     **({"stream_kernel_avg_ms": round(head["stream_kernel_ms"]["mean"], 5),
+                         "finish_kernel_avg_ms": round(head["finish_kernel_ms"]["mean"], 5)}
+                        if "stream_kernel_ms" in head else {}),
                      "traffic_source": traffic_src},
         "cpu_baseline": cpu,
         "modes": {k: rnd(v) for k, v in results.items()},
@@ -530,7 +540,7 @@ def main():
         "sweep": swp,
         "stack_ends": ends,
         "entry_points": eps,
-        "other_schedules": sch,
+        "schedules": sch,
     }
     print(json.dumps(line), flush=True)
 

@@ -51,6 +51,19 @@ def test_exchange_every_token(n):
     assert_bits_equal(host_bits(got["x_mean"]), ref["x_mean"], "stream mean")
 
 
+# Shapes whose tiles get fewer than 4 slices (n = 8192, d = 1280: 128 tiles x
+# 2 slices of 640 features; n = 16384, d = 640: 256 tiles x 1 slice) have more
+# (owned token, word) pairs per workgroup than threads: they take the two
+# launches, and must still match the oracle on every token.
+@pytest.mark.parametrize("n,d", [(8192, 1280), (16384, 640)])
+def test_few_slices_every_token(n, d):
+    say(f"[exchange] few slices n={n} d={d}: every token")
+    from tests.test_gpu_parity import _boundary_case
+    ref, got, s = _boundary_case("stress", 0, n, False, True, d=d)
+    torch.cuda.synchronize()
+    _check_boundary(ref, got, s, False, True)
+
+
 @pytest.mark.parametrize("expanded", [False, True])
 def test_exchange_block_entry(expanded):
     """The block entry (no write) in one launch, the streams as given or the

@@ -1945,12 +1945,14 @@ hipError_t launch_exchange_t(const StreamArgs& a, unsigned grid, hipStream_t st)
   return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, st);
 }
 // The read-row exchange takes slices of 10 or 20 chunks (640 or 1280 features),
-// at most 8 slices and kXMaxGroups workgroups.
+// at most 8 slices and kXMaxGroups workgroups, and enough slices that the
+// (owned token, word) pairs of a workgroup fit its threads (S >= 4).
 int exchange_chunks(int64_t n, int d) {
   const int64_t tiles = (n + kTT - 1) / kTT;
   const int S = stream_slices(n, d);
   const int yk = d / S / kCF;
   if ((yk != 10 && yk != 20) || S > 8 || tiles * S > kXMaxGroups) return 0;
+  if ((kTT + S - 1) / S * kXW > kThreads) return 0;
   return yk;
 }
 template <int RM, bool NORM>
