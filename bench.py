@@ -1,16 +1,16 @@
 """Benchmark: fused HC sublayer boundary, prefill T=4096, on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode fresh|lag] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode lag|fresh] [--no-cpu]
 
 One step = one sublayer-boundary call over the whole 4096-token batch (the
 prefill workload: B=1, T=4096, hc=4, d=5120, 20 Sinkhorn rounds, RMSNorm):
 hc_post(delta, X, post, comb) -> hc_mixes on X' -> split/Sinkhorn -> hc_pre ->
-RMSNorm.  --mode fresh (the default) reads X' with the pre this call
-derives: two kernels of libhc (stream_kernel, then finish_kernel, which reads
-X' back).  --mode lag reads with the pre of the previous boundary (the data
-flow of the pages' Block.forward): one kernel, X read once, the workgroups of
-a token tile exchanging their per-slice sums on chip.  Both modes are timed
-and reported; --mode picks the headline.  Inputs are seeded synthetic tensors
+RMSNorm.  --mode lag (the default) reads with the pre of the previous
+boundary, the data flow of the pages' Block.forward: one kernel of libhc, X
+read once, the workgroups of a token tile exchanging their per-slice sums on
+chip.  --mode fresh reads X' with the pre this call derives: two kernels
+(stream_kernel, then finish_kernel, which reads X' back).  Both modes are
+timed and reported; --mode picks the headline.  Inputs are seeded synthetic tensors
 (transformer_hyper_connection_amd.synth, workload "prefill"), resident in HBM
 before timing; several input/output buffer sets rotate.  Prints one JSON line.
 
@@ -181,8 +181,9 @@ def traffic(mode):
     return total, os.path.relpath(TRAFFIC_FILE, ROOT)
 
 
-def cpu_baseline(s, repeats):
-    """The CPU oracle on the same workload, timed on this host."""
+def cpu_baseline(s, repeats, mode):
+    """The CPU oracle on the same workload (the headline read mode), timed on
+    this host."""
     from oracle import hc_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -192,12 +193,14 @@ def cpu_baseline(s, repeats):
     times = []
     for _ in range(repeats):
         t0 = time.perf_counter()
-        O.boundary(x=s["x"], delta=s["delta"], post_in=s["post_in"], comb_in=s["comb_in"], pre_in=None,
+        O.boundary(x=s["x"], delta=s["delta"], post_in=s["post_in"], comb_in=s["comb_in"],
+                   pre_in=s["pre_in"] if mode == "lag" else None,
                    hc_fn=s["hc_fn"], hc_base=s["hc_base"], hc_scale=s["hc_scale"], gamma=s["gamma"])
         times.append(time.perf_counter() - t0)
     med = statistics.median(times)
     return {"value": round(N_TOK / med, 1), "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"the whole {N_TOK}-token prefill batch, fresh-read boundary with the RMSNorm, median of "
+            "sample": f"the whole {N_TOK}-token prefill batch, {'given' if mode == 'lag' else 'fresh'}-pre "
+                      f"boundary with the RMSNorm, median of "
                       f"{repeats} runs ({med:.2f} s each); float64 BLAS projection on {blas_threads} threads, "
                       f"fp32/fp64 elementwise NumPy on 1 thread; {len(os.sched_getaffinity(0))} usable host "
                       f"cores, os.cpu_count()={os.cpu_count()}"}
@@ -281,32 +284,34 @@ def other_hc(dev, hcs=(2, 8), reps=50):
 
 
 def sweep(dev, ns=(128, 512, 4096, 32768), reps=50):
-    """The headline call (write, fresh pre, RMSNorm; hc=4, d=5120) at several
-    token counts: one GPU's share of a batch sharded over tokens.  n=32768 is
-    the channel-outlier stress workload, the others prefixes of the prefill
-    workload.  Event-timed over at least reps calls (after a warm-up) on two
-    rotating buffer sets."""
+    """The boundary (write, RMSNorm; hc=4, d=5120) at several token counts,
+    in both read modes: one GPU's share of a batch sharded over tokens.
+    n=32768 is the channel-outlier stress workload, the others prefixes of
+    the prefill workload.  Event-timed over at least reps calls (after a
+    warm-up) on two rotating buffer sets."""
     out = {}
     for n in ns:
         print(f"[bench] timing n={n}", file=sys.stderr, flush=True)
         s = synth.boundary_inputs("stress") if n > N_TOK else synth.boundary_inputs("prefill", 0, n)
         params = dict(fn_packed=T.hc_fn_pack(f32(s["hc_fn"], dev)), hc_base=f32(s["hc_base"], dev),
                       hc_scale=f32(s["hc_scale"], dev), gamma=f32(s["gamma"], dev))
-        calls = []
-        for i in range(2):
-            ins = {k: (bf(s[k], dev) if k in ("x", "delta") else f32(s[k], dev)) for k in ("x", "delta", "post_in",
-                                                                                          "comb_in")}
-            calls.append((ins, T.BoundaryCall(ins["x"], delta=ins["delta"], post_in=ins["post_in"],
-                                              comb_in=ins["comb_in"], **params)))
+        sets = [{k: (bf(s[k], dev) if k in ("x", "delta") else f32(s[k], dev))
+                 for k in ("x", "delta", "post_in", "comb_in", "pre_in")} for _ in range(2)]
         del s
-        us = timed_calls([c.run for _, c in calls], min_reps=reps) * 1e3
-        nbytes = algorithmic_bytes(n, "fresh")
-        out[str(n)] = {"call_us": round(us, 2), "tokens_per_s": round(n / us * 1e6, 1),
-                       "gbs": round(nbytes / us / 1e3, 1), "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
-        del calls
+        out[str(n)] = {}
+        for mode in ("lag", "fresh"):
+            calls = [T.BoundaryCall(ins["x"], delta=ins["delta"], post_in=ins["post_in"], comb_in=ins["comb_in"],
+                                    pre_in=ins["pre_in"] if mode == "lag" else None, **params) for ins in sets]
+            us = timed_calls([c.run for c in calls], min_reps=reps) * 1e3
+            nbytes = algorithmic_bytes(n, mode)
+            out[str(n)][mode] = {"call_us": round(us, 2), "tokens_per_s": round(n / us * 1e6, 1),
+                                 "gbs": round(nbytes / us / 1e3, 1),
+                                 "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
+            del calls
+        del sets
         torch.cuda.empty_cache()
-    return {"workload": "fused sublayer boundary, hc=4, d=5120, fresh pre, RMSNorm, at n tokens "
-                        "(n=32768: channel-outlier stress inputs)", **out}
+    return {"workload": "fused sublayer boundary, hc=4, d=5120, RMSNorm, at n tokens, given pre (lag) and fresh "
+                        "pre (n=32768: channel-outlier stress inputs)", **out}
 
 
 def schedules(dev, s, reps=50):
@@ -439,8 +444,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--mode", choices=["fresh", "lag"], default="fresh")
-    ap.add_argument("--modes", default="fresh,lag", help="read modes to time (the headline mode is always timed)")
+    ap.add_argument("--mode", choices=["lag", "fresh"], default="lag")
+    ap.add_argument("--modes", default="lag,fresh", help="read modes to time (the headline mode is always timed)")
     ap.add_argument("--sets", type=int, default=4, help="rotating input/output buffer sets")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-repeats", type=int, default=3)
@@ -498,7 +503,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(s, args.cpu_repeats)
+        cpu = cpu_baseline(s, args.cpu_repeats, args.mode)
 
     def rnd(v):
         if isinstance(v, float):

@@ -221,9 +221,9 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
  * without this field passes the shorter struct_size and gets 0.
  *
  * Schedules (hc = 4).  With a given pre_in and gamma, when the feature slices
- * of a token tile are 640 or 1280 features wide (d = 5120 with n from 2048
- * to 4096, or in general d / S for the slice count S the call picks), the call
- * is one launch: each slice keeps its read row on chip, the slices of a tile
+ * of a token tile are 640 or 1280 features wide and a tile has 4 to 8 of them
+ * (d = 5120 with n from 2048 to 4096, or in general d / S for the slice count
+ * S the call picks), the call is one launch: each slice keeps its read row on chip, the slices of a tile
  * exchange their per-token sums through the workspace as tagged words, and the
  * RMSNorm is applied without writing y first.  Otherwise, with a given pre_in
  * and no gamma and n <= 128, the decode schedule of hc_workspace_bytes runs;
