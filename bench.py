@@ -56,9 +56,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_boundary_prefill_t4096.js
 BYTES_TOKEN_COMMON = 4 * D * 2 + D * 2 + 4 * D * 2 + D * 2 + 16 + 64 + 96
 BYTES_CALL = MIX * 4 * D * 4 + MIX * 4 + 3 * 4 + D * 4
 # the kernels of one call as rocprofv3 names them (the last template argument of
-# stream_kernel is the read-row exchange's slice width in chunks, 0 for none)
-KERNELS = {"fresh": ("stream_kernel<true, 2, true, false, 0>", "finish_kernel<2, true>"),
-           "lag": ("stream_kernel<true, 1, true, false, 20>",)}
+# exchange_kernel is the slice width in 64-feature chunks)
+KERNELS = {"fresh": ("stream_kernel<true, 2, true, false>", "finish_kernel<2, true>"),
+           "lag": ("exchange_kernel<true, false, 20>",)}
 
 
 def algorithmic_bytes(n: int, mode: str) -> int:

@@ -827,9 +827,9 @@ struct StreamArgs {
   int64_t n;
   int xtok, xstr;     // elements per token / per stream of x (hc*d, d; or d, 0 when expanded)
   int d, S, F, tiles;
-  // the read-row exchange (given pre + RMSNorm in one launch, YK > 0)
+  // the read-row exchange (exchange_kernel: given pre + RMSNorm in one launch)
   u64* ctl;           // workspace control block (epoch, done count)
-  u64* xw;            // [tiles * S][kTT][kXW] tagged words
+  u64* xw;            // [tiles][S][kTT][kXW] tagged words
   u32* err;           // sticky error mask
   const float* gamma;
   const float* hc_base;
@@ -864,23 +864,12 @@ template <int N> struct IC { static constexpr int v = N; };
 
 // MEAN: the stream mean (x_mean) is written; a template parameter so that the
 // calls without it carry none of its registers.
-// YK > 0 (a given pre with the RMSNorm, the slice exactly YK chunks wide): the
-// whole boundary in this one launch.  Each lane keeps its read row in
-// registers instead of storing it; at the end every workgroup publishes its
-// per-token sums (24 dots, sum x'^2, sum y^2) as tagged words, sums the S
-// slices' sum y^2 of each of its tokens in slice order (the same bits in every
-// slice) and writes z = gamma * (y * r); the owner slice of each token (token
-// m % S == slice) sums the token's records in slice order and derives mixes,
-// pre/post and the comb.  A wait never depends on a workgroup dispatched later
-// than the first of its tile on every XCD, so no co-residency is assumed; a
-// wait that times out sets the error mask.
 // (Its 112 KB of LDS allow one workgroup, two waves per SIMD, per compute
 // unit; the register budget says so, else the compiler aims at three.)
-template <bool POST, int RM, bool NORM, bool MEAN, int YK = 0>
+template <bool POST, int RM, bool NORM, bool MEAN>
 __global__ void __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 2)))
 stream_kernel(const StreamArgs a) {
   static_assert(!NORM || RM != kNoRead, "RMSNorm needs the read row");
-  static_assert(YK == 0 || (RM == kGivenPre && NORM), "the read-row exchange is for a given pre with the RMSNorm");
   __shared__ u32x4 w_lds[2][2][kHC][kNT][64];          // weight tiles, double buffered (80 KB)
   __shared__ u32x4 a_lds[4][2][kHC][64];               // X' in A layout per row block (32 KB)
 
@@ -931,29 +920,20 @@ stream_kernel(const StreamArgs a) {
   // are added here in fp64 and the fp32 accumulators restart, so fp32 rounding
   // builds up over one chunk only, whatever the slice width (a slice can be the
   // whole 20480-long row, and the dot of a heavy-tailed row cancels strongly).
-  // The one-launch read-row exchange (YK) has slices of at most 20 chunks and
-  // keeps its read row in these registers instead.
   double acc64[kAcc][4];
 #pragma unroll
   for (int t = 0; t < kAcc; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc64[t][i] = 0.0;
   auto flush = [&]() __attribute__((always_inline)) {
-    if constexpr (YK == 0) {
 #pragma unroll
-      for (int t = 0; t < kAcc; ++t) {
+    for (int t = 0; t < kAcc; ++t) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc64[t][i] += (double)acc[t][i];
-        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int i = 0; i < 4; ++i) acc64[t][i] += (double)acc[t][i];
+      acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
   float ssx = 0.f, ssy = 0.f;
-  u32 ykeep[YK > 0 ? YK : 1][4];               // YK: this lane's read row, chunk by chunk
-  __shared__ u32 s_tag;
-  if constexpr (YK > 0) {
-    if (threadIdx.x == 0) s_tag = (u32)get_word(a.ctl + kCtlXEpoch) + 1u;   // words carry epoch + 1
-  }
   float gram[kGram];
 #pragma unroll
   for (int g = 0; g < kGram; ++g) gram[g] = 0.f;
@@ -1017,10 +997,7 @@ stream_kernel(const StreamArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) ssy = dot2_bf16(yp[e], yp[e], ssy);
       }
-      if constexpr (YK > 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ykeep[c][e] = yp[e];
-      } else if (tv) {
+      if (tv) {
         u32x4* p = reinterpret_cast<u32x4*>(yb + (lt * d + f));
         const u32x4 v = u32x4{yp[0], yp[1], yp[2], yp[3]};
         if constexpr (NORM) st_keep(p, v); else st_stream(p, v);
@@ -1095,17 +1072,7 @@ stream_kernel(const StreamArgs a) {
     lds_barrier();
   };
 
-  if constexpr (YK > 0) {
-    // the slice is YK chunks wide: the loop unrolled, each chunk's read row in
-    // registers of its own
-    load_wst(0, wst);
-    load_stream(0, cur);
-    store_wst(0, wst);
-    lds_barrier();
-    [&]<int... C>(std::integer_sequence<int, C...>) __attribute__((always_inline)) {
-      (chunk(C, C + 1 < YK), ...);
-    }(std::make_integer_sequence<int, YK>{});
-  } else if constexpr (!POST) {
+  if constexpr (!POST) {
     u32x4 sB[kHC + 1], wB[kNT];
     const int c1 = nch > 1 ? 1 : 0;                // a single chunk loads chunk 0 twice (unused)
     load_wst(0, wst);
@@ -1158,7 +1125,7 @@ stream_kernel(const StreamArgs a) {
   for (int t = 0; t < kAcc; ++t)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
-      red[((rb * 2 + hw) * 16 + 4 * (lane >> 4) + rr) * 32 + t * 16 + (lane & 15)] = (YK == 0 ? (float)acc64[t][rr] : acc[t][rr]);
+      red[((rb * 2 + hw) * 16 + 4 * (lane >> 4) + rr) * 32 + t * 16 + (lane & 15)] = (float)acc64[t][rr];
   float* extra = red + 4 * 2 * 16 * 32;                            // [kRec - kMix][kTT]
   if ((lane & 7) == 0) {
     extra[m] = ssx;
@@ -1169,95 +1136,6 @@ stream_kernel(const StreamArgs a) {
     }
   }
   lds_barrier();
-  if constexpr (YK > 0) {
-    constexpr int kXS = 8;                         // slices at most on this path (S = d / (64 YK))
-    const u32 tag = s_tag;
-    u64* tilew = a.xw + (size_t)tile * S * kTT * kXW;
-    // publish this slice's sums of every token of the tile
-    u64* mine = tilew + (size_t)slice * kTT * kXW;
-    for (int idx = threadIdx.x; idx < kTT * kXW; idx += kThreads) {
-      const int tm = idx / kXW, q = idx % kXW;
-      float v;
-      if (q < kMix) {
-        const float* r0 = red + ((tm >> 4) * 2 * 16 + (tm & 15)) * 32;   // step 0
-        const float* r1 = r0 + 16 * 32;                                 // step 1
-        v = q < 16 ? r0[q] + r1[q] : (r0[q] + r0[q + 8]) + (r1[q] + r1[q + 8]);
-      } else {
-        v = extra[(q - kMix) * kTT + tm];                               // sum x'^2, sum y^2
-      }
-      put_word(mine + idx, tag_word(v, tag));
-    }
-    // one round trip for every word this workgroup waits for: each thread
-    // requests the sum y^2 of its token from every slice, and, for one
-    // (owned token, word) pair, that word from every slice; each is summed in
-    // slice order (every slice of the tile forms the same bits)
-    bool dead = false;
-    const int nown = (kTT - slice + S - 1) / S;          // owned tokens: slice, slice + S, ...
-    const int pr = threadIdx.x;                          // (owned token, word) pair of this thread
-    const bool has_pair = pr < nown * kXW;
-    const int ptm = has_pair ? slice + S * (pr / kXW) : 0, pq = has_pair ? pr % kXW : 0;
-    u64 wy[kXS], wr[kXS];
-#pragma unroll
-    for (int s2 = 0; s2 < kXS; ++s2) {
-      wy[s2] = s2 < S ? get_word(tilew + ((size_t)s2 * kTT + m) * kXW + kMix + 1) : 0ull;
-      wr[s2] = s2 < S && has_pair ? get_word(tilew + ((size_t)s2 * kTT + ptm) * kXW + pq) : 0ull;
-    }
-    float* tot = reinterpret_cast<float*>(&a_lds[0][0][0][0]);   // [owned token][kXW] (A tiles are free)
-    {
-      float ty = 0.f;
-#pragma unroll
-      for (int s2 = 0; s2 < kXS; ++s2)
-        if (s2 < S) {
-          const float v = settle(tilew + ((size_t)s2 * kTT + m) * kXW + kMix + 1, wy[s2], tag, a.err, dead);
-          ty = s2 == 0 ? v : ty + v;
-        }
-      const float ry = 1.0f / sqrtf(ty / (float)d + a.rms_eps);
-      // z = gamma * (y * r) from the kept read row
-#pragma unroll
-      for (int c = 0; c < YK; ++c) {
-        const int f = fs + c * kCF + fl;
-        const f32x4 g0 = *reinterpret_cast<const f32x4*>(a.gamma + f);
-        const f32x4 g1 = *reinterpret_cast<const f32x4*>(a.gamma + f + 4);
-        const float gm[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
-        u32 zp[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2)
-          zp[e2] = pack_bf16(gm[2 * e2] * (bf_lo(ykeep[c][e2]) * ry), gm[2 * e2 + 1] * (bf_hi(ykeep[c][e2]) * ry));
-        if (tv) st_stream(reinterpret_cast<u32x4*>(yb + (lt * d + f)), u32x4{zp[0], zp[1], zp[2], zp[3]});
-      }
-      if (has_pair) {
-        float tr = 0.f;
-#pragma unroll
-        for (int s2 = 0; s2 < kXS; ++s2)
-          if (s2 < S) {
-            const float v = settle(tilew + ((size_t)s2 * kTT + ptm) * kXW + pq, wr[s2], tag, a.err, dead);
-            tr = s2 == 0 ? v : tr + v;
-          }
-        tot[pr] = tr;
-      }
-    }
-    __syncthreads();
-    // the owned tokens' mixes, pre/post and comb: 4 lanes per token
-    if ((int)threadIdx.x < 4 * nown) {
-      const int k = threadIdx.x >> 2, j = threadIdx.x & 3;
-      const int tm = slice + S * k;
-      const float* r = tot + k * kXW;
-      const float rx = 1.0f / sqrtf(r[kMix] / (float)(kHC * d) + a.norm_eps);
-      const float dc[kHC] = {r[2 * kHC + 4 * j], r[2 * kHC + 4 * j + 1], r[2 * kHC + 4 * j + 2], r[2 * kHC + 4 * j + 3]};
-      derive_quad(r[j], r[kHC + j], dc, rx, j, t0 + tm < a.n, t0 + tm, a.hc_scale, a.hc_base, a.iters,
-                  a.hc_eps, a.mixes_out, a.pre_out, a.post_out, a.comb_out);
-    }
-    // every word of this call read: the last workgroup advances the epoch
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const u64 before = __hip_atomic_fetch_add(a.ctl + kCtlXDone, (u64)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (before % (u64)gridDim.x == (u64)(gridDim.x - 1)) {
-        put_word(a.ctl + kCtlXDone, 0ull);
-        put_word(a.ctl + kCtlXEpoch, (u64)tag);
-      }
-    }
-    return;
-  }
   float* rec = a.rec + ((size_t)tile * S + slice) * kTT * kRec;
   for (int idx = threadIdx.x; idx < kTT * kQuads; idx += kThreads) {
     const int tm = idx / kQuads, q0 = (idx % kQuads) * 4;
@@ -1274,6 +1152,264 @@ stream_kernel(const StreamArgs a) {
       }
     }
     *reinterpret_cast<f32x4*>(rec + tm * kRec + q0) = f32x4{v[0], v[1], v[2], v[3]};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// exchange_kernel: the boundary with a given pre and the RMSNorm in one launch
+// ("Source layer, pairs pooled", Block.forward; "Final RMSNorm").  The RMSNorm
+// of the read row needs sum y^2 over the whole row, which the S feature slices
+// of a token tile each hold a part of.  Each lane keeps its slice of y in
+// registers (the chunk loop unrolled at compile time) instead of storing it;
+// the slices of a tile exchange their per-token sums (24 dots, sum x'^2,
+// sum y^2) as tagged words in the workspace; every slice sums the S parts of
+// sum y^2 of each of its tokens in slice order (the same bits in every slice)
+// and writes z = gamma * (y * r); the owner slice of a token (token m with
+// m % S == slice) sums all of the token's words in slice order and derives
+// its mixes, pre/post and comb.  The owners' words are summed first, so that
+// the derive (one wave) runs while the other waves' z stores drain.
+// Per 64-feature chunk the streaming is that of the stream kernel (X' stored,
+// its A tile and the matrix-core projection, sum x'^2 and sum y^2).  Every
+// workgroup of a call must be resident at once (one per compute unit, at most
+// 256); a wait that times out sets the error mask instead of hanging.
+constexpr int kXS = 8;                    // slices per tile at most on this path
+
+template <bool POST, bool MEAN, int YK>
+__global__ void __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 2)))
+exchange_kernel(const StreamArgs a) {
+  __shared__ u32x4 w_lds[2][2][kHC][kNT][64];          // weight tiles, double buffered (80 KB)
+  __shared__ u32x4 a_lds[4][2][kHC][64];               // X' in A layout per row block (32 KB)
+  __shared__ float red[4][2][16][32];                  // projection sums per (row block, step) (16 KB)
+  __shared__ float ssum[2][kTT];                       // sum x'^2, sum y^2 per token
+  __shared__ float tot[kTT / 4 * kXW];                 // the owned tokens' words, summed over the slices
+  __shared__ f32x4 g_slice[YK * kCF / 4];              // gamma of the slice
+  __shared__ u32 s_tag;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rb = wave >> 1, hw = wave & 1;   // row block, half (stream phase) / step (matrix phase)
+  const int d = a.d, S = a.S;
+  // XCD-aware: consecutive blocks land on different XCDs; renumbered so that
+  // each XCD holds a contiguous run, slice-major (an XCD's L2 holds the
+  // weights of few slices)
+  const int lin = (gridDim.x & 7) ? blockIdx.x : (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int slice = lin / a.tiles, tile = lin % a.tiles;
+  const int fs = slice * (YK * kCF);
+  const int hl = lane >> 3, fl = (lane & 7) * 8;
+  const int m = rb * 16 + hw * 8 + hl;          // token within the tile
+  const int a_st = fl >> 5, a_g = (fl >> 3) & 3;
+  const int a_lane = a_g * 16 + hw * 8 + hl;
+  const int nown = (kTT - slice + S - 1) / S;   // owned tokens: slice, slice + S, ... (S >= 4: at most 16)
+  const int pr = threadIdx.x;                   // (owned token, word) pair of this thread
+  const bool has_pair = pr < nown * kXW;
+  const int ptm = has_pair ? slice + S * (pr / kXW) : 0, pq = has_pair ? pr % kXW : 0;
+
+  if (threadIdx.x == 0) s_tag = (u32)get_word(a.ctl + kCtlXEpoch) + 1u;   // words carry epoch + 1
+  if (threadIdx.x < YK * kCF / 4) g_slice[threadIdx.x] = reinterpret_cast<const f32x4*>(a.gamma + fs)[threadIdx.x];
+
+  const int64_t t0 = (int64_t)tile * kTT;
+  const bool tv = t0 + m < a.n;
+  const unsigned lt = tv ? (unsigned)m : 0u;   // a token past n reads the tile's first token
+  const hc_bf16* xb = a.x + t0 * a.xtok;
+  float cpost[kHC], ccomb[kHC * kHC], cpre[kHC];
+#pragma unroll
+  for (int j = 0; j < kHC; ++j) {
+    cpost[j] = POST ? a.post_in[(t0 + lt) * kHC + j] : 0.f;
+    cpre[j] = a.pre_in[(t0 + lt) * kHC + j];
+  }
+#pragma unroll
+  for (int j = 0; j < kHC * kHC; ++j) ccomb[j] = POST ? a.comb_in[(t0 + lt) * kHC * kHC + j] : 0.f;
+
+  auto load_wst = [&](int c, u32x4 (&dst)[kNT]) __attribute__((always_inline)) {
+    const int gstep = (fs + c * kCF) / 32;
+#pragma unroll
+    for (int i = 0; i < kNT; ++i) {
+      const int blk = wave + i * kWaves;          // (st, k, nt) = blk / 20, (blk / 5) % 4, blk % 5
+      const int st = blk / (kHC * kNT), kk = (blk / kNT) % kHC, nt = blk % kNT;
+      dst[i] = a.fn[((size_t)((gstep + st) * kHC + kk) * kNT + nt) * 64 + lane];
+    }
+  };
+  auto store_wst = [&](int buf, const u32x4 (&src)[kNT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kNT; ++i) {
+      const int blk = wave + i * kWaves;
+      const int st = blk / (kHC * kNT), kk = (blk / kNT) % kHC, nt = blk % kNT;
+      w_lds[buf][st][kk][nt][lane] = src[i];
+    }
+  };
+  auto load_stream = [&](int c, u32x4 (&dst)[kHC + 1]) __attribute__((always_inline)) {
+    const unsigned f = fs + c * kCF + fl;
+#pragma unroll
+    for (int j = 0; j < kHC; ++j)
+      dst[j] = ld_stream(reinterpret_cast<const u32x4*>(xb + (lt * (unsigned)a.xtok + j * (unsigned)a.xstr + f)));
+    dst[kHC] = POST ? ld_stream(reinterpret_cast<const u32x4*>(a.delta + (t0 + lt) * d + f)) : u32x4{0u, 0u, 0u, 0u};
+  };
+  float ssx = 0.f, ssy = 0.f;
+  f32x4 acc[kAcc];
+#pragma unroll
+  for (int t = 0; t < kAcc; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32 ykeep[YK][4];                             // this lane's read row, chunk by chunk
+  auto stream_phase = [&](int c, const u32x4 (&src)[kHC + 1]) __attribute__((always_inline)) {
+    const unsigned f = fs + c * kCF + fl;
+    u32 xp[kHC][4];
+    if constexpr (POST) {
+      post_8(src, cpost, ccomb, xp);
+      if (tv) {
+        hc_bf16* xob = a.x_out + (t0 + lt) * kHC * d;
+#pragma unroll
+        for (int j = 0; j < kHC; ++j)
+          st_stream(reinterpret_cast<u32x4*>(xob + (j * d + f)), u32x4{xp[j][0], xp[j][1], xp[j][2], xp[j][3]});
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kHC; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xp[j][e] = src[j][e];
+    }
+    // unconditional: a lane past n stores the same bits as its tile's first token
+    if constexpr (MEAN) st_stream(reinterpret_cast<u32x4*>(a.x_mean + (t0 + lt) * d + f), mean_8(xp));
+#pragma unroll
+    for (int j = 0; j < kHC; ++j) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ssx = dot2_bf16(xp[j][e], xp[j][e], ssx);
+      a_lds[rb][a_st][j][a_swz(a_lane, a_st)] = u32x4{xp[j][0], xp[j][1], xp[j][2], xp[j][3]};
+    }
+    u32 yp[4];
+    pre_8(xp, cpre, yp);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ssy = dot2_bf16(yp[e], yp[e], ssy);
+      ykeep[c][e] = yp[e];
+    }
+  };
+  auto matrix_phase = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kHC; ++j) {
+      const bf16x8 A = __builtin_bit_cast(bf16x8, a_lds[rb][hw][j][a_swz(lane, hw)]);
+      bf16x8 B[kNT];
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) B[nt] = __builtin_bit_cast(bf16x8, w_lds[buf][hw][j][nt][lane]);
+      mfma_step(A, B, acc);
+    }
+  };
+
+  // the chunks: the next chunk's weights, then its streams, are requested
+  // before this chunk's work; two barriers (A tiles and weights in place; the
+  // matrix phase done before the A tiles are rewritten)
+  u32x4 cur[kHC + 1], wst[kNT];
+  load_wst(0, wst);
+  load_stream(0, cur);
+  store_wst(0, wst);
+  lds_barrier();
+  auto chunk = [&]<int C>(IC<C>) __attribute__((always_inline)) {
+    constexpr bool kMore = C + 1 < YK;
+    u32x4 nxt[kHC + 1];
+    if constexpr (kMore) {
+      load_wst(C + 1, wst);
+      load_stream(C + 1, nxt);
+    }
+    stream_phase(C, cur);
+    lds_barrier();
+    if constexpr (kMore) store_wst((C + 1) & 1, wst);
+    matrix_phase(C & 1);
+    lds_barrier();
+    if constexpr (kMore) {
+#pragma unroll
+      for (int j = 0; j <= kHC; ++j) cur[j] = nxt[j];
+    }
+  };
+  [&]<int... C>(std::integer_sequence<int, C...>) __attribute__((always_inline)) {
+    (chunk(IC<C>{}), ...);
+  }(std::make_integer_sequence<int, YK>{});
+
+  // ---- this slice's sums of every token of the tile, as tagged words
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+    ssx += __shfl_xor(ssx, o);
+    ssy += __shfl_xor(ssy, o);
+  }
+#pragma unroll
+  for (int t = 0; t < kAcc; ++t)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) red[rb][hw][4 * (lane >> 4) + rr][t * 16 + (lane & 15)] = acc[t][rr];
+  if ((lane & 7) == 0) {
+    ssum[0][m] = ssx;
+    ssum[1][m] = ssy;
+  }
+  lds_barrier();
+  const u32 tag = s_tag;
+  u64* tilew = a.xw + (size_t)tile * S * kTT * kXW;
+  u64* mine = tilew + (size_t)slice * kTT * kXW;
+  for (int idx = threadIdx.x; idx < kTT * kXW; idx += kThreads) {
+    const int tm = idx / kXW, q = idx % kXW;
+    float v;
+    if (q < kMix) {
+      const float* r0 = red[tm >> 4][0][tm & 15];
+      const float* r1 = red[tm >> 4][1][tm & 15];
+      v = q < 16 ? r0[q] + r1[q] : (r0[q] + r0[q + 8]) + (r1[q] + r1[q + 8]);
+    } else {
+      v = ssum[q - kMix][tm];
+    }
+    put_word(mine + idx, tag_word(v, tag));
+  }
+  // ---- every word this workgroup waits for, in one round trip: sum y^2 of
+  // this lane's token and, for the owned (token, word) pair of this thread,
+  // that word, from every slice; each summed in slice order
+  u64 wy[kXS], wr[kXS];
+#pragma unroll
+  for (int s2 = 0; s2 < kXS; ++s2) {
+    wy[s2] = s2 < S ? get_word(tilew + ((size_t)s2 * kTT + m) * kXW + kMix + 1) : 0ull;
+    wr[s2] = s2 < S && has_pair ? get_word(tilew + ((size_t)s2 * kTT + ptm) * kXW + pq) : 0ull;
+  }
+  bool dead = false;
+  if (has_pair) {
+    float tr = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < kXS; ++s2)
+      if (s2 < S) {
+        const float v = settle(tilew + ((size_t)s2 * kTT + ptm) * kXW + pq, wr[s2], tag, a.err, dead);
+        tr = s2 == 0 ? v : tr + v;
+      }
+    tot[pr] = tr;
+  }
+  float ty = 0.f;
+#pragma unroll
+  for (int s2 = 0; s2 < kXS; ++s2)
+    if (s2 < S) {
+      const float v = settle(tilew + ((size_t)s2 * kTT + m) * kXW + kMix + 1, wy[s2], tag, a.err, dead);
+      ty = s2 == 0 ? v : ty + v;
+    }
+  const float ry = 1.0f / sqrtf(ty / (float)d + a.rms_eps);
+  __syncthreads();
+  if (threadIdx.x == 0) {   // every word of this call read: the last workgroup advances the epoch
+    const u64 before = __hip_atomic_fetch_add(a.ctl + kCtlXDone, (u64)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (before % (u64)gridDim.x == (u64)(gridDim.x - 1)) {
+      put_word(a.ctl + kCtlXDone, 0ull);
+      put_word(a.ctl + kCtlXEpoch, (u64)tag);
+    }
+  }
+  // ---- the owned tokens' mixes, pre/post and comb: 4 lanes per token (one wave)
+  if ((int)threadIdx.x < 4 * nown) {
+    const int k = threadIdx.x >> 2, j = threadIdx.x & 3;
+    const int tm = slice + S * k;
+    const float* r = &tot[k * kXW];
+    const float rx = 1.0f / sqrtf(r[kMix] / (float)(kHC * d) + a.norm_eps);
+    const float dc[kHC] = {r[2 * kHC + 4 * j], r[2 * kHC + 4 * j + 1], r[2 * kHC + 4 * j + 2], r[2 * kHC + 4 * j + 3]};
+    derive_quad(r[j], r[kHC + j], dc, rx, j, t0 + tm < a.n, t0 + tm, a.hc_scale, a.hc_base, a.iters, a.hc_eps,
+                a.mixes_out, a.pre_out, a.post_out, a.comb_out);
+  }
+  // ---- z = gamma * (y * r) from the kept read row
+#pragma unroll
+  for (int c = 0; c < YK; ++c) {
+    const int f = fs + c * kCF + fl;
+    const f32x4 g0 = g_slice[(c * kCF + fl) / 4];
+    const f32x4 g1 = g_slice[(c * kCF + fl) / 4 + 1];
+    const float gm[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+    u32 zp[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2)
+      zp[e2] = pack_bf16(gm[2 * e2] * (bf_lo(ykeep[c][e2]) * ry), gm[2 * e2 + 1] * (bf_hi(ykeep[c][e2]) * ry));
+    if (tv) st_stream(reinterpret_cast<u32x4*>(a.y_out + (t0 + lt) * d + f), u32x4{zp[0], zp[1], zp[2], zp[3]});
   }
 }
 
@@ -1912,14 +2048,14 @@ size_t split_records_bytes(int64_t n, int d) {
 //                                epoch / tiles-done words, the read-row
 //                                exchange's epoch and done words
 //   [decode records]             [kDTiles][kDMaxD/kDF][kDT][kDRec] tagged words
-//   [read-row exchange words]    [kXMaxGroups][kTT] tagged words
+//   [read-row exchange words]    [kXMaxGroups][kTT][kXW] tagged words
 //   [per-slice records]          two-launch schedule (hc = 4) or hc = 2, 8;
 //                                plain floats, rewritten by every call
 // Tagged words carry their schedule's call epoch + 1; the epochs only grow, so
 // a word left by an earlier call (of any shape) never holds a current tag.
 bool decode_shape(int64_t n, int d) { return n <= kDMaxN && d % kDF == 0 && d <= kDMaxD; }
 constexpr size_t kDecRegionBytes = (size_t)kDTiles * (kDMaxD / kDF) * kDT * kDRec * sizeof(u64);
-constexpr int kXMaxGroups = 256;             // workgroups of one read-row exchange at most
+constexpr int kXMaxGroups = 256;             // (tile, slice) groups (= workgroups) of one read-row exchange at most
 constexpr size_t kXRegionBytes = (size_t)kXMaxGroups * kTT * kXW * sizeof(u64);
 constexpr size_t kDecOffset = kCtrlBytes;
 constexpr size_t kXOffset = kDecOffset + kDecRegionBytes;
@@ -1940,19 +2076,19 @@ template <bool POST, int YK>
 hipError_t launch_exchange_t(const StreamArgs& a, unsigned grid, hipStream_t st) {
   StreamArgs copy = a;
   void* args[] = {&copy};
-  const void* fn = a.x_mean ? reinterpret_cast<const void*>(&stream_kernel<POST, kGivenPre, true, true, YK>)
-                            : reinterpret_cast<const void*>(&stream_kernel<POST, kGivenPre, true, false, YK>);
+  const void* fn = a.x_mean ? reinterpret_cast<const void*>(&exchange_kernel<POST, true, YK>)
+                            : reinterpret_cast<const void*>(&exchange_kernel<POST, false, YK>);
   return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, st);
 }
-// The read-row exchange takes slices of 10 or 20 chunks (640 or 1280 features),
-// at most 8 slices and kXMaxGroups workgroups, and enough slices that the
-// (owned token, word) pairs of a workgroup fit its threads (S >= 4).
+// The read-row exchange: slices of 10 or 20 chunks (640 or 1280 features), 4
+// to kXS slices per tile (the owned (token, word) pairs of a workgroup fit its
+// threads), and every workgroup resident at once (at most 256, one per
+// compute unit); 0 if the shape has no such split.
 int exchange_chunks(int64_t n, int d) {
   const int64_t tiles = (n + kTT - 1) / kTT;
   const int S = stream_slices(n, d);
-  const int yk = d / S / kCF;
-  if ((yk != 10 && yk != 20) || S > 8 || tiles * S > kXMaxGroups) return 0;
-  if ((kTT + S - 1) / S * kXW > kThreads) return 0;
+  const int yk = d / kCF / S;
+  if ((yk != 10 && yk != 20) || S < 4 || S > kXS || tiles * S > kXMaxGroups) return 0;
   return yk;
 }
 template <int RM, bool NORM>
