@@ -102,14 +102,16 @@ int hc_fn_pack(const float* hc_fn, int hc, int d, void* fn_packed, void* stream)
  * calls of every hc.
  *
  * Decode schedule (hc = 4).  For n <= 128 with d a multiple of 256, hc_mixes, and
- * hc_boundary with a given pre_in and no gamma (the pages' data flow at
- * decode), run as one launch: 16-token tiles by 256-feature slices, each
- * slice adding its per-token partial sums to the workspace as tagged words
- * and counting itself in on the tile's arrival word; the last slice of a tile
- * to arrive sums them in slice order (the same bits whichever slice it is)
- * and derives mixes, pre/post and the comb ("Reading weights").  No workgroup
- * waits for another to start.  A word the last slice waits for that never
- * becomes visible sets bit 0 of the workspace's error mask (see
+ * hc_boundary with a given pre_in (the pages' data flow at decode; with or
+ * without gamma), run as one launch: 16-token tiles by 256-feature slices,
+ * each slice adding its per-token partial sums to the workspace as tagged
+ * words and counting itself in on the tile's arrival word; the last slice of a
+ * tile to arrive sums them in slice order (the same bits whichever slice it
+ * is) and derives mixes, pre/post and the comb ("Reading weights").  Without
+ * gamma no workgroup waits for another to start; with gamma every slice sums
+ * the slices' sum y^2 of its tokens and writes its part of z, so all of the
+ * launch's workgroups (at most 256) must be resident at once.  A word a slice
+ * waits for that never becomes visible sets bit 0 of the workspace's error mask (see
  * hc_workspace_status); the call then finishes with wrong results instead of
  * hanging.  The workspace holds a control block (the error mask and the
  * schedules' call counters), the decode schedule's words and the read-row
@@ -223,10 +225,11 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
  * Schedules (hc = 4).  With a given pre_in and gamma, when the feature slices
  * of a token tile are 640 or 1280 features wide and a tile has 4 to 8 of them
  * (d = 5120 with n from 2048 to 4096, or in general d / S for the slice count
- * S the call picks), the call is one launch: each slice keeps its read row on chip, the slices of a tile
- * exchange their per-token sums through the workspace as tagged words, and the
+ * S the call picks), the call is one launch: each slice keeps its read row on
+ * chip, the slices of a tile exchange their per-token sums through the
+ * workspace as tagged words, and the
  * RMSNorm is applied without writing y first.  Otherwise, with a given pre_in
- * and no gamma and n <= 128, the decode schedule of hc_workspace_bytes runs;
+ * and n <= 128, the decode schedule of hc_workspace_bytes runs;
  * and in every other case two launches: a streaming pass (X', the read row of
  * a given pre, per-slice sums) and a finish (mixes, pre/post/comb, and the read
  * row where it depends on them or on its RMSNorm).  A wait for another

@@ -79,10 +79,10 @@ def test_packed_and_workspace_bytes(L):
     assert L.hc_workspace_bytes(0, 4, 5120) == 0
     assert L.hc_workspace_bytes(4096, 3, 5120) == 0
     w = L.hc_workspace_bytes(4096, 4, 5120)
-    # 8 KB control block; decode words: 8 tiles x (8192/256) slices x 16 tokens x 25 tagged 8-byte words;
+    # 8 KB control block; decode words: 8 tiles x (8192/256) slices x 16 tokens x 26 tagged 8-byte words;
     # read-row exchange words: 256 groups x 64 tokens x 26 tagged words; then the two-launch records:
     # 64 tiles of 64 tokens x 4 slices x 36 floats
-    fixed = 8192 + 8 * 32 * 16 * 25 * 8 + 256 * 64 * 26 * 8
+    fixed = 8192 + 8 * 32 * 16 * 26 * 8 + 256 * 64 * 26 * 8
     assert w == fixed + 64 * 4 * 64 * 36 * 4
     # n = 128: 2 tiles x 40 slices
     assert L.hc_workspace_bytes(128, 4, 5120) == fixed + 2 * 40 * 64 * 36 * 4
@@ -104,9 +104,9 @@ def test_workspace_layout_regions_never_overlap(L):
     persistent words; the regions are disjoint and end at hc_workspace_bytes."""
     base = _layout(L, 1, 4, 64)[:6]
     assert base[0] == 0 and base[1] == 8192
-    # the decode words hold 8 tiles x (8192/256) slices x 16 tokens x 25 words; the
+    # the decode words hold 8 tiles x (8192/256) slices x 16 tokens x 26 words; the
     # exchange words 256 groups x 64 tokens x 26 words
-    assert base[3] >= 8 * (8192 // 256) * 16 * 25 * 8
+    assert base[3] >= 8 * (8192 // 256) * 16 * 26 * 8
     assert base[5] >= 256 * 64 * 26 * 8
     ns = (1, 17, 128, 129, 2048, 3000, 4096, 4097, 32768)
     for hc in (2, 4, 8):
@@ -141,7 +141,7 @@ def test_packed_and_workspace_bytes_other_hc(L):
     # records [S][n][recw] after the fixed regions; S is the largest divisor of hc*d/64 with at most
     # ~512 workgroups of 128 tokens, 64 at most; recw = mix + 1 rounded up to 4 floats (12 at hc = 2,
     # 84 at hc = 8)
-    fixed = 8192 + 8 * 32 * 16 * 25 * 8 + 256 * 64 * 26 * 8
+    fixed = 8192 + 8 * 32 * 16 * 26 * 8 + 256 * 64 * 26 * 8
     assert L.hc_workspace_bytes(4096, 8, 5120) == fixed + 16 * 4096 * 84 * 4
 
 def test_null_misaligned_negative(L):

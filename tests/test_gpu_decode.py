@@ -1,8 +1,10 @@
-"""GPU parity of the decode schedule: hc_boundary with a given pre and no
-RMSNorm, and hc_mixes, for n <= 128 run as one launch whose last-arriving
-feature slice of each token tile sums the slices' partial sums and derives
-the coefficients ("Source layer, pairs pooled": Block.forward at decode;
-"Reading weights").  Checked against the oracle on ragged token counts and
+"""GPU parity of the decode schedule: hc_boundary with a given pre (with and
+without the RMSNorm of the read row), and hc_mixes, for n <= 128 run as one
+launch whose last-arriving feature slice of each token tile sums the slices'
+partial sums and derives the coefficients ("Source layer, pairs pooled":
+Block.forward at decode; "Reading weights"; with the RMSNorm every slice
+sums the slices' sum y^2 of its tokens and writes its part of z, "Final
+RMSNorm").  Checked against the oracle on ragged token counts and
 widths whose slice count spans one and two gather batches; on one workspace
 reused across calls of changing n and inputs (the tile epochs carried in the
 workspace); and captured in a graph with the decode block's other calls and
@@ -28,6 +30,39 @@ def test_decode_boundary(n, d, entry):
     say(f"[decode] n={n} d={d} entry={entry}")
     ref, got, s = T._boundary_case("prefill", 0, n, False, False, entry=entry, d=d)
     T._check_boundary(ref, got, s, False, False)
+
+
+# with the RMSNorm: every slice waits for the others' sum y^2 (d = 8192 at
+# n = 128 is 8 tiles x 32 slices = 256 workgroups, the most the schedule takes)
+@pytest.mark.parametrize("n,d", [(1, 5120), (17, 5120), (128, 5120), (129, 5120), (45, 7168), (128, 8192),
+                                 (70, 10240)])
+@pytest.mark.parametrize("entry", [False, True])
+def test_decode_boundary_norm(n, d, entry):
+    say(f"[decode norm] n={n} d={d} entry={entry}")
+    ref, got, s = T._boundary_case("prefill", 0, n, False, True, entry=entry, d=d)
+    T._check_boundary(ref, got, s, False, True)
+
+
+def test_decode_norm_repeated_and_against_two_launches():
+    """The decode schedule with the RMSNorm on one workspace, called again on
+    new inputs (the call epoch advances) and beside the two launches of the
+    same call (bit-equal streams); every call against the oracle."""
+    ws = torch.zeros(H.lib().hc_workspace_bytes(128, 4, 5120), dtype=torch.uint8, device="cuda:0")
+    for i, (t0, n) in enumerate(((0, 128), (500, 100), (0, 128))):
+        say(f"[decode norm repeat] call {i}: tokens {t0}..{t0 + n}")
+        s, dev = _inputs(t0, t0 + n)
+        dev["gamma"] = f32_dev(s["gamma"])
+        fn = H.hc_fn_pack(f32_dev(s["hc_fn"]))
+        x = bf16_dev(s["x"])
+        one = H.hc_boundary(x, fn_packed=fn, want_mixes=True, out={"workspace": ws}, **dev)
+        two = H.hc_boundary(x, fn_packed=fn, want_mixes=True, two_launch=True, **dev)
+        torch.cuda.synchronize()
+        assert_workspace_clean(ws)
+        assert np.array_equal(host_bits(one["x_out"]), host_bits(two["x_out"]))
+        ref = O.boundary(x=s["x"], delta=s["delta"], post_in=s["post_in"], comb_in=s["comb_in"],
+                         pre_in=s["pre_in"], hc_fn=s["hc_fn"], hc_base=s["hc_base"], hc_scale=s["hc_scale"],
+                         gamma=s["gamma"])
+        T._check_boundary(ref, one, s, False, True)
 
 
 def _inputs(t0, t1, d=5120):

@@ -17,15 +17,18 @@
 //       the 24-wide projection on the matrix cores with the weight tiles shared
 //       through LDS; the per-slice sums meet in the workspace, and the finish
 //       derives the coefficients and writes the read row.
-//   decode_kernel<POST, READ>  the same for n <= 128 in one launch: the last
+//   exchange_kernel<POST, MEAN, YK>  a given pre with the RMSNorm in one launch
+//       (tiles of 4 to 8 slices of YK chunks): the slices of a tile exchange
+//       their per-token sums as tagged words; the read row stays in registers.
+//   decode_kernel<POST, READ, NORM>  the same for n <= 128 in one launch: the last
 //       slice of a token tile to arrive sums the tile's records.
-//   fused_kernel<POST, RM, NORM>  the single-launch schedule (opt-in).
 //   row_kernel<POST, PRE, NORM, TPW, HC>  streams only (hc_post, hc_pre, the
 //       stack exit): whole token rows per wave, 1 KB per load or store.
 //   split_kernel<HC>  hc_split_sinkhorn, one token per lane.
 //   pack_kernel     fp32 projection weight -> bf16 hi/mid/lo terms in tile order.
 // hc = 2 and 8: row_kernel and split_kernel instantiated for that hc, and
-//   mixes_generic_kernel<GM>, the projection in fp32 multiply-adds.
+//   gpack_kernel / gmix_kernel / gfinish_kernel<HC>, the projection on the
+//   matrix cores with per-slice records and their finish.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -1625,11 +1628,15 @@ __global__ void __launch_bounds__(kFinThreads) finish_kernel(const FinishArgs a)
 }
 
 // ======================================================= decode boundary
-// decode_kernel<POST, READ>: the boundary for few tokens in one launch, the
-// finalize (split + Sinkhorn) done by the last feature slice of each token tile
-// to finish ("Source layer, pairs pooled": Block.forward at decode, the read
-// taking the given pre; "Reading weights" for the split).  No workgroup waits
-// for another, so the launch needs no co-residency.
+// decode_kernel<POST, READ, NORM>: the boundary for few tokens in one launch,
+// the finalize (split + Sinkhorn) done by the last feature slice of each token
+// tile to finish ("Source layer, pairs pooled": Block.forward at decode, the
+// read taking the given pre; "Reading weights" for the split).  Without the
+// RMSNorm no workgroup waits for another, so the launch needs no co-residency;
+// with it ("Final RMSNorm") each slice keeps its part of the read row in
+// registers, adds sum y^2 to its record, and scales the row once the S
+// slices' sums of its tokens are visible (the last slice takes them from its
+// gather), so every workgroup of the launch must be resident.
 //
 // Work items are (tile of kDT = 16 tokens, slice of kDF = 256 features of each
 // stream), one workgroup each.  A workgroup streams its item (hc_post, X'
@@ -1653,7 +1660,8 @@ constexpr int kDT = 16;                      // tokens per tile
 constexpr int kDF = 256;                     // features per slice and stream
 constexpr int kDSteps = kDF / kStepF;        // 32-feature steps per slice (8)
 constexpr int kDThreads = 256;               // 4 waves: 2 steps each in the projection
-constexpr int kDRec = 25;                    // record words per token: 24 dots, sum x'^2
+constexpr int kDRec = 25;                    // record words per token the last slice sums: 24 dots, sum x'^2
+constexpr int kDRecW = kDRec + 1;            // words per token in the layout: + sum y^2 (with the RMSNorm)
 constexpr int kDMaxN = 128;                  // decode schedule up to this many tokens (measured crossover)
 constexpr int kDTiles = kDMaxN / kDT;        // tiles at most (the region is sized for them)
 constexpr int kDMaxD = 8192;                 // widest row of the decode schedule (the region is sized for it)
@@ -1676,7 +1684,9 @@ struct DecArgs {
   float* post_out;
   float* comb_out;
   int xtok, xstr;     // elements per token / per stream of x (hc*d, d; or d, 0 when expanded)
-  u64* rec;           // [tiles][S][kDT][kDRec] tagged words
+  u64* rec;           // [tiles][S][kDT][kDRecW] tagged words
+  const float* gamma; // RMSNorm gain of the read row (NORM)
+  float rms_eps;
   u64* ctl;           // the workspace's control block (arrival, epoch and tiles-done words)
   u32* err;           // sticky error mask (a wait timed out)
   int tiles;
@@ -1685,12 +1695,14 @@ struct DecArgs {
   float hc_eps, norm_eps;
 };
 
-template <bool POST, bool READ>
+template <bool POST, bool READ, bool NORM>
 __global__ void __launch_bounds__(kDThreads) decode_kernel(const DecArgs a) {
+  static_assert(!NORM || READ, "the RMSNorm is of the read row");
   __shared__ u32x4 a_lds[kDSteps][kHC][64];            // X' in A layout (32 KB)
   __shared__ float red[kDThreads / 64][kDT][32];       // per-wave dots
   __shared__ float ssq[4][kDT];                        // sum x'^2 per chunk
-  __shared__ float tot[kDT][kDRec];                    // the tile's summed records (last slice)
+  __shared__ float ssy[NORM ? 4 : 1][kDT];             // sum y^2 per chunk (NORM)
+  __shared__ float tot[kDT][kDRecW];                   // the tile's summed records (last slice)
   __shared__ float s_cf[kMix + 3];                     // hc_base, hc_scale (read by the last slice)
   __shared__ u32 s_tag, s_last;
 
@@ -1752,6 +1764,22 @@ __global__ void __launch_bounds__(kDThreads) decode_kernel(const DecArgs a) {
 #pragma unroll
   for (int j = 0; j < kHC * kHC; ++j) ccomb[j] = POST ? a.comb_in[(t0 + lt) * kHC * kHC + j] : 0.f;
 
+  // the RMSNorm gain of this lane's features (NORM)
+  float gm[NORM ? 2 : 1][8];
+  if constexpr (NORM) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const f32x4* g = reinterpret_cast<const f32x4*>(a.gamma + fs + (2 * p + half) * kCF + fl);
+      const f32x4 g0 = g[0], g1 = g[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gm[p][e] = g0[e];
+        gm[p][4 + e] = g1[e];
+      }
+    }
+  }
+  u32 ykeep[NORM ? 2 : 1][4];                          // the read row (NORM: kept until its factor is known)
+
   // ---- streams: X', the read row, sum x'^2, the A tile
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
@@ -1776,7 +1804,18 @@ __global__ void __launch_bounds__(kDThreads) decode_kernel(const DecArgs a) {
     if constexpr (READ) {
       u32 yp[4];
       pre_8(xp, cpre, yp);
-      if (tv) st_stream(reinterpret_cast<u32x4*>(a.y_out + (t0 + lt) * d + f), u32x4{yp[0], yp[1], yp[2], yp[3]});
+      if constexpr (NORM) {
+        float sy = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sy = dot2_bf16(yp[e], yp[e], sy);
+          ykeep[p][e] = yp[e];
+        }
+        sy = oct_sum(sy);
+        if ((threadIdx.x & 7) == 0) ssy[c][m] = sy;
+      } else if (tv) {
+        st_stream(reinterpret_cast<u32x4*>(a.y_out + (t0 + lt) * d + f), u32x4{yp[0], yp[1], yp[2], yp[3]});
+      }
     }
     float sx = 0.f;
 #pragma unroll
@@ -1808,17 +1847,20 @@ __global__ void __launch_bounds__(kDThreads) decode_kernel(const DecArgs a) {
 
   // ---- this slice's record of the tile, then count in
   const u32 tag = s_tag;
-  u64* rt = a.rec + (size_t)tile * S * kDT * kDRec;
-  for (int idx = threadIdx.x; idx < kDT * kDRec; idx += kDThreads) {
-    const int tm = idx / kDRec, q = idx % kDRec;
+  u64* rt = a.rec + (size_t)tile * S * kDT * kDRecW;
+  constexpr int kPut = NORM ? kDRecW : kDRec;         // + sum y^2 with the RMSNorm
+  for (int idx = threadIdx.x; idx < kDT * kPut; idx += kDThreads) {
+    const int tm = idx / kPut, q = idx % kPut;
     float v;
     if (q < kMix) {
       auto col = [&](int w, int cq) { return cq < 16 ? red[w][tm][cq] : red[w][tm][cq] + red[w][tm][cq + 8]; };
       v = ((col(0, q) + col(1, q)) + col(2, q)) + col(3, q);
-    } else {
+    } else if (q == kMix) {
       v = ((ssq[0][tm] + ssq[1][tm]) + ssq[2][tm]) + ssq[3][tm];
+    } else {
+      v = ((ssy[0][tm] + ssy[1][tm]) + ssy[2][tm]) + ssy[NORM ? 3 : 0][tm];
     }
-    put_word(rt + ((size_t)slice * kDT + tm) * kDRec + q, tag_word(v, tag));
+    put_word(rt + ((size_t)slice * kDT + tm) * kDRecW + q, tag_word(v, tag));
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -1836,40 +1878,74 @@ __global__ void __launch_bounds__(kDThreads) decode_kernel(const DecArgs a) {
     }
   }
   __syncthreads();
+  bool dead = false;
+  // z = gamma * (y * r) of this lane's features from the kept read row
+  auto store_z = [&](float ry) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int f = fs + (2 * p + half) * kCF + fl;
+      u32 zp[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2)
+        zp[e2] = pack_bf16(gm[p][2 * e2] * (bf_lo(ykeep[p][e2]) * ry), gm[p][2 * e2 + 1] * (bf_hi(ykeep[p][e2]) * ry));
+      if (tv) st_stream(reinterpret_cast<u32x4*>(a.y_out + (t0 + lt) * d + f), u32x4{zp[0], zp[1], zp[2], zp[3]});
+    }
+  };
+  if (NORM && !s_last) {
+    // the other slices: the S slices' sum y^2 of this lane's token, summed in
+    // slice order (the same factor in every slice; the last slice sums them in
+    // its gather), then this slice's z.  They wait for the others' words here,
+    // so the launch needs all of its workgroups resident (at most
+    // kDTiles * kDMaxD / kDF = 256).
+    u64 w[kDMaxD / kDF];
+    const u64* p0 = rt + (size_t)m * kDRecW + kDRec;   // slice b at + b * kDT * kDRecW
+#pragma unroll
+    for (int b = 0; b < kDMaxD / kDF; ++b) w[b] = b < S ? get_word(p0 + (size_t)b * kDT * kDRecW) : 0ull;
+    float ty = 0.f;
+#pragma unroll
+    for (int b = 0; b < kDMaxD / kDF; ++b)
+      if (b < S) {
+        const float v = settle(p0 + (size_t)b * kDT * kDRecW, w[b], tag, a.err, dead);
+        ty = b == 0 ? v : ty + v;
+      }
+    store_z(1.0f / sqrtf(ty / (float)d + a.rms_eps));
+  }
   if (!s_last) return;
 
   // ---- the last slice: sum the S records of each token in slice order; a
   // thread's words of all slices are requested together (one round trip)
-  bool dead = false;
-  constexpr int kPairs = (kDT * kDRec + kDThreads - 1) / kDThreads;   // (token, word) pairs per thread
+  constexpr int kGath = NORM ? kDRecW : kDRec;                        // words summed per token (+ sum y^2)
+  constexpr int kPairs = (kDT * kGath + kDThreads - 1) / kDThreads;   // (token, word) pairs per thread
   constexpr int kBatch = 32;                                          // slices in flight per pair
   for (int b0 = 0; b0 < S; b0 += kBatch) {
     u64 w[kPairs][kBatch];
 #pragma unroll
     for (int i = 0; i < kPairs; ++i) {
       const int idx = threadIdx.x + i * kDThreads;
-      const u64* p0 = rt + (size_t)(idx / kDRec) * kDRec + idx % kDRec;   // slice b at + b * kDT * kDRec
+      const u64* p0 = rt + (size_t)(idx / kGath) * kDRecW + idx % kGath;   // slice b at + b * kDT * kDRecW
 #pragma unroll
       for (int b = 0; b < kBatch; ++b)
-        w[i][b] = (idx < kDT * kDRec && b0 + b < S) ? get_word(p0 + (size_t)(b0 + b) * kDT * kDRec) : 0ull;
+        w[i][b] = (idx < kDT * kGath && b0 + b < S) ? get_word(p0 + (size_t)(b0 + b) * kDT * kDRecW) : 0ull;
     }
 #pragma unroll
     for (int i = 0; i < kPairs; ++i) {
       const int idx = threadIdx.x + i * kDThreads;
-      if (idx >= kDT * kDRec) continue;
-      const int tm = idx / kDRec, q = idx % kDRec;
-      const u64* p0 = rt + (size_t)tm * kDRec + q;
+      if (idx >= kDT * kGath) continue;
+      const int tm = idx / kGath, q = idx % kGath;
+      const u64* p0 = rt + (size_t)tm * kDRecW + q;
       float s = b0 == 0 ? 0.f : tot[tm][q];
 #pragma unroll
       for (int b = 0; b < kBatch; ++b)
         if (b0 + b < S) {
-          const float v = settle(p0 + (size_t)(b0 + b) * kDT * kDRec, w[i][b], tag, a.err, dead);
+          const float v = settle(p0 + (size_t)(b0 + b) * kDT * kDRecW, w[i][b], tag, a.err, dead);
           s = b0 + b == 0 ? v : s + v;
         }
       tot[tm][q] = s;
     }
   }
   __syncthreads();
+  // the last slice's own z first (its stores drain while wave 0 derives)
+  if constexpr (NORM) store_z(1.0f / sqrtf(tot[m][kDRec] / (float)d + a.rms_eps));
   // ---- derive: 4 lanes (a quad) per token, lane j holding comb row j
   if (threadIdx.x < kDT * kHC) {
     const int tm = threadIdx.x >> 2, j = threadIdx.x & 3;
@@ -2047,14 +2123,14 @@ size_t split_records_bytes(int64_t n, int d) {
 //   [control block, kCtrlBytes]  error mask, the decode schedule's arrival /
 //                                epoch / tiles-done words, the read-row
 //                                exchange's epoch and done words
-//   [decode records]             [kDTiles][kDMaxD/kDF][kDT][kDRec] tagged words
+//   [decode records]             [kDTiles][kDMaxD/kDF][kDT][kDRecW] tagged words
 //   [read-row exchange words]    [kXMaxGroups][kTT][kXW] tagged words
 //   [per-slice records]          two-launch schedule (hc = 4) or hc = 2, 8;
 //                                plain floats, rewritten by every call
 // Tagged words carry their schedule's call epoch + 1; the epochs only grow, so
 // a word left by an earlier call (of any shape) never holds a current tag.
 bool decode_shape(int64_t n, int d) { return n <= kDMaxN && d % kDF == 0 && d <= kDMaxD; }
-constexpr size_t kDecRegionBytes = (size_t)kDTiles * (kDMaxD / kDF) * kDT * kDRec * sizeof(u64);
+constexpr size_t kDecRegionBytes = (size_t)kDTiles * (kDMaxD / kDF) * kDT * kDRecW * sizeof(u64);
 constexpr int kXMaxGroups = 256;             // (tile, slice) groups (= workgroups) of one read-row exchange at most
 constexpr size_t kXRegionBytes = (size_t)kXMaxGroups * kTT * kXW * sizeof(u64);
 constexpr size_t kDecOffset = kCtrlBytes;
@@ -2161,13 +2237,14 @@ int launch_boundary(bool post, int rm, bool norm, StreamArgs s, FinishArgs f, vo
 }
 
 // ---- decode boundary
-template <bool POST, bool READ>
+template <bool POST, bool READ, bool NORM = false>
 hipError_t launch_decode_t(const DecArgs& a, unsigned grid, hipStream_t st) {
   DecArgs copy = a;
   void* args[] = {&copy};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<POST, READ>), dim3(grid), dim3(kDThreads), args,
-                         0, st);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<POST, READ, NORM>), dim3(grid), dim3(kDThreads),
+                         args, 0, st);
 }
+// a.gamma set: the read row's RMSNorm (read must be set)
 int launch_decode(bool post, bool read, DecArgs a, void* ws, size_t ws_bytes, hipStream_t st, const char* what) {
   const size_t need = workspace_bytes(a.n, a.d);
   if (!ws) return fail(HC_EINVAL, "%s: workspace must not be NULL (need %zu bytes)", what, need);
@@ -2177,17 +2254,20 @@ int launch_decode(bool post, bool read, DecArgs a, void* ws, size_t ws_bytes, hi
   const int64_t tiles = (a.n + kDT - 1) / kDT;
   a.ctl = static_cast<u64*>(ws);
   a.rec = reinterpret_cast<u64*>(static_cast<char*>(ws) + kDecOffset);
-  if ((size_t)((a.n + kDT - 1) / kDT) * (a.d / kDF) * kDT * kDRec * sizeof(u64) > kDecRegionBytes)
+  if ((size_t)((a.n + kDT - 1) / kDT) * (a.d / kDF) * kDT * kDRecW * sizeof(u64) > kDecRegionBytes)
     return fail(HC_ENOTSUP, "%s: the decode records exceed their region", what);
   a.err = static_cast<u32*>(ws) + kErrWord;
   a.tiles = (int)tiles;
   const unsigned grid = (unsigned)(tiles * a.S);
   hipError_t e;
-  switch ((post ? 2 : 0) | (read ? 1 : 0)) {
+  const bool norm = read && a.gamma != nullptr;
+  switch ((norm ? 4 : 0) | (post ? 2 : 0) | (read ? 1 : 0)) {
     case 0: e = launch_decode_t<false, false>(a, grid, st); break;
     case 1: e = launch_decode_t<false, true>(a, grid, st); break;
     case 2: e = launch_decode_t<true, false>(a, grid, st); break;
-    default: e = launch_decode_t<true, true>(a, grid, st); break;
+    case 3: e = launch_decode_t<true, true>(a, grid, st); break;
+    case 5: e = launch_decode_t<false, true, true>(a, grid, st); break;
+    default: e = launch_decode_t<true, true, true>(a, grid, st); break;
   }
   return launched(e, what);
 }
@@ -2587,13 +2667,14 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
     return HC_OK;
   }
   const bool two = (flags & HC_BOUNDARY_TWO_LAUNCH) != 0;
-  if (phases == 3 && !two && !fresh && !norm && decode_shape(p->n, p->d)) {
+  if (phases == 3 && !two && !fresh && decode_shape(p->n, p->d)) {
     DecArgs a{};
     a.n = p->n; a.d = p->d; a.x = p->x; a.delta = p->delta; a.post_in = p->post_in; a.comb_in = p->comb_in;
     a.pre_in = p->pre_in; a.fn = reinterpret_cast<const u32x4*>(p->fn_packed); a.hc_base = p->hc_base;
     a.hc_scale = p->hc_scale; a.x_out = p->x_out; a.y_out = p->y_out; a.mixes_out = p->mixes_out;
     a.pre_out = p->pre_out; a.post_out = p->post_out; a.comb_out = p->comb_out; a.iters = p->iters;
     a.hc_eps = p->hc_eps; a.norm_eps = p->norm_eps; a.xtok = xtok; a.xstr = xstr; a.x_mean = x_mean;
+    a.gamma = p->gamma; a.rms_eps = p->rms_eps;
     return launch_decode(post, true, a, p->workspace, p->workspace_bytes, st, "hc_boundary");
   }
   StreamArgs s{};
