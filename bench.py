@@ -256,6 +256,58 @@ def decode_block(dev, reps=200):
             "boundary_call_us": round(boundary, 2)}
 
 
+def decode_stack(dev, sublayers=80, reps=20):
+    """A decode stack's glue (B=128, T=1): the entry (read with the incoming
+    mix), then one boundary per sublayer (write with the previous post/comb,
+    mixes, read with the previous pre, RMSNorm), the attention and
+    feed-forward parameter sets alternating and a given stand-in sublayer
+    output; eager (each call enqueued by the binding) and replayed from one
+    captured graph.  Mean microseconds per sublayer."""
+    b = synth.block_inputs()
+    sets = [dict(fn_packed=T.hc_fn_pack(f32(fn, dev)), hc_base=f32(base, dev), hc_scale=f32(scale, dev))
+            for fn, base, scale in (b["attn"], b["ffn"])]
+    g = torch.ones(D, dtype=torch.float32, device=dev)
+    X, PRE = bf(b["x"], dev), f32(b["pre_in"], dev)
+    DL = bf(b["delta_attn"], dev)
+    calls = [T.BoundaryCall(X, pre_in=PRE, gamma=g, **sets[0])]
+    for i in range(sublayers):
+        o = calls[-1].outputs
+        x_in = X if i == 0 else o["x_out"]
+        calls.append(T.BoundaryCall(x_in, delta=DL, post_in=o["post"], comb_in=o["comb"], pre_in=o["pre"], gamma=g,
+                                    **sets[(i + 1) % 2]))
+
+    def stack():
+        for c in calls:
+            c.run()
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3 / len(calls)
+
+    eager = timed(stack)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        stack()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        stack()
+    replay = timed(graph.replay)
+    return {"workload": f"decode stack glue, B=128 T=1, hc=4, d=5120: the entry and {sublayers} sublayer "
+                        "boundaries (given pre, RMSNorm), eager and from one captured graph",
+            "calls": len(calls), "per_call_us_eager": round(eager, 2), "per_call_us_graph": round(replay, 2)}
+
+
 def other_hc(dev, hcs=(2, 8), reps=50):
     """The same boundary (write, fresh pre, RMSNorm; n=4096, d=5120) at hc = 2
     and 8, which libhc runs as four plainer launches (row write, matrix-core
@@ -494,7 +546,7 @@ def main():
     mean_ms = head["mean_call_ms"]
     achieved = head["algorithmic_bytes"] / (mean_ms * 1e-3) / 1e9
     traffic_bytes, traffic_src = traffic(args.mode)
-    dec = None if args.no_decode else decode_block(dev)
+    dec = None if args.no_decode else {**decode_block(dev), "stack": decode_stack(dev)}
     ohc = None if args.no_other_hc else other_hc(dev)
     swp = None if args.no_sweep else sweep(dev)
     ends = None if args.no_stack_ends else stack_ends(dev)

@@ -109,11 +109,13 @@ def test_identities_on_gpu():
 
 
 # ------------------------------------------------------------------ hc_mixes
-# chunks of 64 features per workgroup slice: 2 at (32 | 45, 5120) and (19, 7168),
-# 1 at d = 64 and 1024, 5 at (1000, 5120) and 10 at (2048, 5120) -- every tail of
-# the projection loop, which keeps two chunks in flight and is unrolled by two
+# n <= 128 (d a multiple of 256) runs the decode schedule; above, the stream
+# kernel (two chunks in flight, loop unrolled by two) with 64-feature chunks
+# per workgroup slice: 1 at d = 64, 2 at (300, 5120), 5 at (1000, 5120), 10 at
+# (2048, 5120), 20 at 4096 and 4097 (a ragged last tile), 4 at (5000, 1024):
+# every tail of the unrolled loop
 @pytest.mark.parametrize("n,d", [(32, 5120), (45, 5120), (16, 64), (3, 1024), (19, 7168), (1000, 5120),
-                                 (2048, 5120)])
+                                 (2048, 5120), (300, 5120), (4096, 5120), (4097, 5120), (5000, 1024)])
 def test_hc_mixes_end_to_end(n, d):
     say(f"[hc_mixes] n={n} d={d}")
     x = rand_bits((n, 4, d))
@@ -128,6 +130,29 @@ def test_hc_mixes_end_to_end(n, d):
     assert_coef_close(host_f32(comb), rc, "comb")
     only = H.hc_mixes(bf16_dev(x), packed(fn))
     assert torch.equal(only, mixes)
+
+
+def test_hc_mixes_stress_full_size_every_token():
+    """hc_mixes on the channel-outlier stress workload (n = 32768: 512 tiles x
+    one slice of 80 chunks, whose per-chunk sums are carried in fp64), every
+    token against the oracle, in chunks."""
+    say("[hc_mixes stress] n=32768, every token")
+    s = synth.boundary_inputs("stress")
+    X = bf16_dev(s["x"])
+    pre, post, comb, mixes = H.hc_mixes(X, packed(s["hc_fn"]), f32_dev(s["hc_scale"]), f32_dev(s["hc_base"]),
+                                        return_mixes=True)
+    torch.cuda.synchronize()
+    del X
+    got = {k: host_f32(v) for k, v in (("pre", pre), ("post", post), ("comb", comb), ("mixes", mixes))}
+    for a in range(0, s["x"].shape[0], 4 * FULL_CHUNK):
+        b = a + 4 * FULL_CHUNK
+        say(f"  oracle tokens {a}..{b}")
+        rm = O.hc_mixes(s["x"][a:b], s["hc_fn"], 1e-6)
+        assert_mixes_close(got["mixes"][a:b], rm)
+        rp, rq, rc = O.hc_split_sinkhorn(rm, s["hc_scale"], s["hc_base"])
+        assert_coef_close(got["pre"][a:b], rp, "pre")
+        assert_coef_close(got["post"][a:b], rq, "post")
+        assert_coef_close(got["comb"][a:b], rc, "comb")
 
 
 # ------------------------------------------------------------------ one sublayer step (n=32)
