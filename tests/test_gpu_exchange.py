@@ -35,10 +35,11 @@ def _epoch(ws):
     return int(ws[8 * CTL_X_EPOCH:8 * CTL_X_EPOCH + 8].cpu().numpy().view(np.uint64)[0])
 
 
-# n = 2048 and 3000: slices of 640 features (8 per tile; 3000 leaves a ragged
-# last tile); 4096: slices of 1280 (4 per tile); 4097: 65 tiles x 4 slices,
-# more groups than the exchange holds, so the two launches run instead
-@pytest.mark.parametrize("n", [2048, 3000, 4096, 4097])
+# n = 1300 (21 tiles, the last ragged), 1536 and 2048: slices of 640 features
+# (8 per tile); 4096: slices of 1280 (4 per tile); 3000 (47 tiles x 8 slices)
+# and 4097 (65 tiles x 4 slices): more groups than the exchange holds, so the
+# two launches run instead
+@pytest.mark.parametrize("n", [1300, 1536, 2048, 3000, 4096, 4097])
 def test_exchange_every_token(n):
     say(f"[exchange] n={n}: every token")
     s, kw, dev = _inputs(n)

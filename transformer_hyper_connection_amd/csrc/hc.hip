@@ -2159,13 +2159,20 @@ hipError_t launch_exchange_t(const StreamArgs& a, unsigned grid, hipStream_t st)
 // The read-row exchange: slices of 10 or 20 chunks (640 or 1280 features), 4
 // to kXS slices per tile (the owned (token, word) pairs of a workgroup fit its
 // threads), and every workgroup resident at once (at most 256, one per
-// compute unit); 0 if the shape has no such split.
-int exchange_chunks(int64_t n, int d) {
+// compute unit).  The slices are the two-launch schedule's where those fit;
+// else, from 20 tiles up (fewer leave too many compute units idle; measured
+// at n = 1024 and 1536), slices of 10 chunks.  Returns the slice count, 0 if
+// the shape has no such split.
+int exchange_slices(int64_t n, int d) {
   const int64_t tiles = (n + kTT - 1) / kTT;
+  auto fits = [&](int S) {
+    const int yk = S > 0 && d / kCF % S == 0 ? d / kCF / S : 0;
+    return (yk == 10 || yk == 20) && S >= 4 && S <= kXS && tiles * S <= kXMaxGroups;
+  };
   const int S = stream_slices(n, d);
-  const int yk = d / kCF / S;
-  if ((yk != 10 && yk != 20) || S < 4 || S > kXS || tiles * S > kXMaxGroups) return 0;
-  return yk;
+  if (fits(S)) return S;
+  if (d / kCF % 10 == 0 && fits(d / kCF / 10) && tiles >= 20) return d / kCF / 10;
+  return 0;
 }
 template <int RM, bool NORM>
 hipError_t launch_finish_t(const FinishArgs& a, unsigned grid, hipStream_t st) {
@@ -2191,8 +2198,11 @@ int launch_boundary(bool post, int rm, bool norm, StreamArgs s, FinishArgs f, vo
   s.rec = reinterpret_cast<float*>(static_cast<char*>(ws) + kRecOffset);
   const unsigned grid1 = (unsigned)(tiles * s.S);
   hipError_t e = hipSuccess;
-  const int yk = exchange && phases == 3 && rm == kGivenPre && norm ? exchange_chunks(s.n, s.d) : 0;
-  if (yk) {
+  const int xs = exchange && phases == 3 && rm == kGivenPre && norm ? exchange_slices(s.n, s.d) : 0;
+  if (xs) {
+    const int yk = s.d / kCF / xs;
+    s.S = xs;
+    s.F = s.d / xs;
     // the words of every (tile, slice) group stay inside the exchange region
     if ((size_t)tiles * s.S * kTT * kXW * sizeof(u64) > kXRegionBytes)
       return fail(HC_ENOTSUP, "%s: %lld exchange groups exceed the region", what, (long long)(tiles * s.S));
@@ -2202,8 +2212,9 @@ int launch_boundary(bool post, int rm, bool norm, StreamArgs s, FinishArgs f, vo
     s.gamma = f.gamma; s.hc_base = f.hc_base; s.hc_scale = f.hc_scale; s.mixes_out = f.mixes_out;
     s.pre_out = f.pre_out; s.post_out = f.post_out; s.comb_out = f.comb_out; s.iters = f.iters;
     s.hc_eps = f.hc_eps; s.norm_eps = f.norm_eps; s.rms_eps = f.rms_eps;
-    if (post) e = yk == 20 ? launch_exchange_t<true, 20>(s, grid1, st) : launch_exchange_t<true, 10>(s, grid1, st);
-    else e = yk == 20 ? launch_exchange_t<false, 20>(s, grid1, st) : launch_exchange_t<false, 10>(s, grid1, st);
+    const unsigned grid = (unsigned)(tiles * s.S);
+    if (post) e = yk == 20 ? launch_exchange_t<true, 20>(s, grid, st) : launch_exchange_t<true, 10>(s, grid, st);
+    else e = yk == 20 ? launch_exchange_t<false, 20>(s, grid, st) : launch_exchange_t<false, 10>(s, grid, st);
     return launched(e, what);
   }
   if (phases & 1) switch ((post ? 8 : 0) | (rm << 1) | (norm ? 1 : 0)) {
