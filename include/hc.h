@@ -224,12 +224,14 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
  *
  * Schedules (hc = 4).  With a given pre_in and gamma, when the feature slices
  * of a token tile are 640 or 1280 features wide and a tile has 4 to 8 of them
- * (d = 5120 with n from 2048 to 4096, or in general d / S for the slice count
- * S the call picks), the call is one launch: each slice keeps its read row on
- * chip, the slices of a tile exchange their per-token sums through the
- * workspace as tagged words, and the
- * RMSNorm is applied without writing y first.  Otherwise, with a given pre_in
- * and n <= 128, the decode schedule of hc_workspace_bytes runs;
+ * (d = 5120 with n from about 1300 to 4096, or in general d / S for the slice
+ * count S the call picks), the call is one launch: each slice keeps its read
+ * row on chip, the slices of a tile exchange their per-token sums through the
+ * workspace as tagged words, and the RMSNorm is applied without writing y
+ * first; beyond 4096 tokens (when 4096 tokens take that form) the call runs
+ * as consecutive such calls of 4096 tokens and a last one for the rest.
+ * Otherwise, with a given pre_in and n <= 128, the decode schedule of
+ * hc_workspace_bytes runs;
  * and in every other case two launches: a streaming pass (X', the read row of
  * a given pre, per-slice sums) and a finish (mixes, pre/post/comb, and the read
  * row where it depends on them or on its RMSNorm).  A wait for another

@@ -20,7 +20,7 @@ CTL_X_EPOCH = 16          # u64 index of the exchange's call epoch in the worksp
 
 
 def _inputs(n, entry=False):
-    s = synth.boundary_inputs("prefill", 0, n)
+    s = synth.boundary_inputs("prefill" if n <= 4096 else "stress", 0, n)
     kw = dict(x=s["x"], pre_in=s["pre_in"], gamma=s["gamma"], hc_fn=s["hc_fn"], hc_base=s["hc_base"],
               hc_scale=s["hc_scale"])
     if not entry:
@@ -36,10 +36,11 @@ def _epoch(ws):
 
 
 # n = 1300 (21 tiles, the last ragged), 1536 and 2048: slices of 640 features
-# (8 per tile); 4096: slices of 1280 (4 per tile); 3000 (47 tiles x 8 slices)
-# and 4097 (65 tiles x 4 slices): more groups than the exchange holds, so the
-# two launches run instead
-@pytest.mark.parametrize("n", [1300, 1536, 2048, 3000, 4096, 4097])
+# (8 per tile); 4096: slices of 1280 (4 per tile); 3000 (47 tiles x 8 slices):
+# more groups than the exchange holds, so the two launches run instead; 4097,
+# 8192 and 9000: consecutive one-launch calls of 4096 tokens, the rest (1
+# token: the decode schedule; 808 tokens: two launches) as its own call
+@pytest.mark.parametrize("n", [1300, 1536, 2048, 3000, 4096, 4097, 8192, 9000])
 def test_exchange_every_token(n):
     say(f"[exchange] n={n}: every token")
     s, kw, dev = _inputs(n)

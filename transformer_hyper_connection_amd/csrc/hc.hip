@@ -2163,6 +2163,7 @@ hipError_t launch_exchange_t(const StreamArgs& a, unsigned grid, hipStream_t st)
 // else, from 20 tiles up (fewer leave too many compute units idle; measured
 // at n = 1024 and 1536), slices of 10 chunks.  Returns the slice count, 0 if
 // the shape has no such split.
+constexpr int64_t kXPart = (int64_t)kXMaxGroups / 4 * kTT;   // tokens of the largest exchange (4 slices a tile)
 int exchange_slices(int64_t n, int d) {
   const int64_t tiles = (n + kTT - 1) / kTT;
   auto fits = [&](int S) {
@@ -2678,6 +2679,34 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
     return HC_OK;
   }
   const bool two = (flags & HC_BOUNDARY_TWO_LAUNCH) != 0;
+  if (phases == 3 && !two && !fresh && norm && p->n > kXPart && exchange_slices(kXPart, p->d)) {
+    // a given pre with the RMSNorm beyond one exchange's reach: consecutive
+    // calls on parts of kXPart tokens (one launch each), then the rest as its
+    // own call (whatever schedule suits it)
+    hc_boundary_args q{};
+    memcpy(&q, p, std::min<size_t>(p->struct_size, sizeof q));
+    q.struct_size = sizeof q;
+    q.x_mean_out = x_mean;
+    q.flags = flags;
+    for (int64_t t0 = 0; t0 < p->n; t0 += kXPart) {
+      const int64_t m = std::min<int64_t>(kXPart, p->n - t0);
+      q.n = m;
+      q.x = p->x + t0 * xtok;
+      q.delta = post ? p->delta + t0 * p->d : nullptr;
+      q.post_in = post ? p->post_in + t0 * kHC : nullptr;
+      q.comb_in = post ? p->comb_in + t0 * kHC * kHC : nullptr;
+      q.pre_in = p->pre_in + t0 * kHC;
+      q.x_out = post ? p->x_out + t0 * kHC * p->d : nullptr;
+      q.y_out = p->y_out + t0 * p->d;
+      q.x_mean_out = x_mean ? x_mean + t0 * p->d : nullptr;
+      q.mixes_out = p->mixes_out ? p->mixes_out + t0 * kMix : nullptr;
+      q.pre_out = p->pre_out + t0 * kHC;
+      q.post_out = p->post_out + t0 * kHC;
+      q.comb_out = p->comb_out + t0 * kHC * kHC;
+      if ((rc = boundary_phases(&q, stream, 3))) return rc;
+    }
+    return HC_OK;
+  }
   if (phases == 3 && !two && !fresh && decode_shape(p->n, p->d)) {
     DecArgs a{};
     a.n = p->n; a.d = p->d; a.x = p->x; a.delta = p->delta; a.post_in = p->post_in; a.comb_in = p->comb_in;
