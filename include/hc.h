@@ -84,7 +84,11 @@ const char* hc_last_error(void);
 size_t hc_fn_packed_bytes(int hc, int d);
 
 /* hc_fn [(2+hc)*hc, hc*d] float32 -> fn_packed (hc_fn_packed_bytes(hc, d)
- * bytes, 16-byte aligned). */
+ * bytes, 16-byte aligned): each fp32 weight split exactly into three bf16
+ * terms, laid out as the matrix cores' operand tiles; at hc = 4 followed by the
+ * same tiles of the weight summed over the four stream blocks (the projection
+ * of four identical streams, used by the block entry from the expanded
+ * embedding).  Pack once per parameter set. */
 int hc_fn_pack(const float* hc_fn, int hc, int d, void* fn_packed, void* stream);
 
 /* ---------------------------------------------------------------------------

@@ -71,10 +71,11 @@ def test_strerror_and_version(L):
 
 
 def test_packed_and_workspace_bytes(L):
-    assert L.hc_fn_packed_bytes(4, 5120) == 80 * 4 * 5120 * 2  # 72 split rows + 8 zero rows, bf16
+    # 72 split rows + 8 zero rows, bf16, for the four stream blocks and their sum
+    assert L.hc_fn_packed_bytes(4, 5120) == 80 * 5 * 5120 * 2
     assert L.hc_fn_packed_bytes(3, 5120) == 0
     assert L.hc_fn_packed_bytes(4, 100) == 0
-    assert L.hc_fn_packed_bytes(4, 5184) == 80 * 4 * 5184 * 2
+    assert L.hc_fn_packed_bytes(4, 5184) == 80 * 5 * 5184 * 2
     assert L.hc_fn_packed_bytes(4, 32832) == 0
     assert L.hc_workspace_bytes(0, 4, 5120) == 0
     assert L.hc_workspace_bytes(4096, 3, 5120) == 0

@@ -45,21 +45,34 @@ def test_pack_terms_reconstruct_weight(d):
     say(f"[pack] d={d}")
     fn, _, _ = params(d)
     p = packed(fn).cpu().numpy().view(np.uint16)
-    rec = N.bits_to_f64(p.reshape(d // 32, 4, 5, 64, 8))   # [step][k][tile][lane][8]
-    # tile[st, k, nt, col, feature-in-step]: lane = 16*g + col holds features 8g..8g+7
-    tile = rec.reshape(d // 32, 4, 5, 4, 16, 8).transpose(0, 1, 2, 4, 3, 5).reshape(d // 32, 4, 5, 16, 32)
-    def rows(nt, cols):                                 # -> [len(cols), 4*d] in feature order k*d + f
-        t = tile[:, :, nt][:, :, cols]                  # [st, k, col, 32]
-        return t.transpose(2, 1, 0, 3).reshape(len(cols), 4 * d)
-    lo8, hi8 = np.arange(8), np.arange(8, 16)
-    hi = np.concatenate([rows(0, np.arange(16)), rows(3, lo8)])
-    mid = np.concatenate([rows(1, np.arange(16)), rows(3, hi8)])
-    lo = np.concatenate([rows(2, np.arange(16)), rows(4, lo8)])
-    assert not rows(4, hi8).any()
+    main = (d // 32) * 4 * 5 * 64 * 8
+    assert p.size == main * 5 // 4                       # the four stream blocks, then their sum
+
+    def terms(rec, blocks):
+        # tile[st, k, nt, col, feature-in-step]: lane = 16*g + col holds features 8g..8g+7
+        tile = rec.reshape(d // 32, blocks, 5, 4, 16, 8).transpose(0, 1, 2, 4, 3, 5).reshape(d // 32, blocks, 5, 16,
+                                                                                            32)
+
+        def rows(nt, cols):                             # -> [len(cols), blocks*d] in feature order k*d + f
+            t = tile[:, :, nt][:, :, cols]              # [st, k, col, 32]
+            return t.transpose(2, 1, 0, 3).reshape(len(cols), blocks * d)
+        lo8, hi8 = np.arange(8), np.arange(8, 16)
+        assert not rows(4, hi8).any()
+        return (np.concatenate([rows(0, np.arange(16)), rows(3, lo8)]),
+                np.concatenate([rows(1, np.arange(16)), rows(3, hi8)]),
+                np.concatenate([rows(2, np.arange(16)), rows(4, lo8)]))
+
+    hi, mid, lo = terms(N.bits_to_f64(p[:main]), 4)
     thi = torch.from_numpy(fn).to(torch.bfloat16).float().numpy()
     assert np.array_equal(hi, thi)                      # hi = nearest bf16 of w
     err = np.abs(hi + mid + lo - fn.astype(np.float64))
     assert (err <= 2.0 ** -25 * np.abs(fn) + 1e-45).all()
+    # the stream-summed block: the same split of the fp32 rounding of the fp64 sum over the four blocks
+    ws = fn.astype(np.float64).reshape(24, 4, d).sum(axis=1).astype(np.float32)
+    shi, smid, slo = terms(N.bits_to_f64(p[main:]), 1)
+    assert np.array_equal(shi, torch.from_numpy(ws).to(torch.bfloat16).float().numpy())
+    serr = np.abs(shi + smid + slo - ws.astype(np.float64))
+    assert (serr <= 2.0 ** -25 * np.abs(ws) + 1e-45).all()
 
 
 # ------------------------------------------------------------------ split / Sinkhorn

@@ -205,14 +205,21 @@ __device__ __forceinline__ float split_term(float x, int part) {
   return round_bf16(r1 - mid);  // r1 - mid exact
 }
 
+// records [d/32 steps][kHC streams][kNT tiles][64 lanes] of the weight, then
+// [d/32 steps][kNT tiles][64 lanes] of the weight summed over the four stream
+// blocks (the projection of four identical streams, the expanded block entry:
+// the sum taken in fp64 and rounded to fp32 once, then split the same way)
 __global__ void __launch_bounds__(256) pack_kernel(const float* __restrict__ fn, int d,
                                                    u32x4* __restrict__ out, int records) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= records) return;
-  const int lane = idx & 63;
-  const int nt = (idx >> 6) % kNT;
-  const int k = (idx / (64 * kNT)) % kHC;
-  const int step = idx / (64 * kNT * kHC);
+  const int main_records = (d / kStepF) * kHC * kNT * 64;
+  const bool summed = idx >= main_records;
+  const int ridx = summed ? idx - main_records : idx;
+  const int lane = ridx & 63;
+  const int nt = (ridx >> 6) % kNT;
+  const int k = summed ? 0 : (ridx / (64 * kNT)) % kHC;
+  const int step = summed ? ridx / (64 * kNT) : ridx / (64 * kNT * kHC);
   const int n = lane & 15;
   int q, part;                       // projection row and split term; q < 0: zero
   if (nt < 3) { q = n; part = nt; }
@@ -224,8 +231,18 @@ __global__ void __launch_bounds__(256) pack_kernel(const float* __restrict__ fn,
   for (int e2 = 0; e2 < 4; ++e2) {
     float v[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      v[h] = q < 0 ? 0.f : split_term(fn[(size_t)q * (kHC * d) + (size_t)k * d + f0 + 2 * e2 + h], part);
+    for (int h = 0; h < 2; ++h) {
+      float x = 0.f;
+      if (q >= 0 && summed) {
+        double sum = 0.0;
+#pragma unroll
+        for (int kk = 0; kk < kHC; ++kk) sum += (double)fn[(size_t)q * (kHC * d) + (size_t)kk * d + f0 + 2 * e2 + h];
+        x = (float)sum;
+      } else if (q >= 0) {
+        x = fn[(size_t)q * (kHC * d) + (size_t)k * d + f0 + 2 * e2 + h];
+      }
+      v[h] = q < 0 ? 0.f : split_term(x, part);
+    }
     w[e2] = pack_bf16(v[0], v[1]);
   }
   out[idx] = u32x4{w[0], w[1], w[2], w[3]};
@@ -1177,9 +1194,15 @@ stream_kernel(const StreamArgs a) {
 // 256); a wait that times out sets the error mask instead of hanging.
 constexpr int kXS = 8;                    // slices per tile at most on this path
 
-template <bool POST, bool MEAN, int YK>
+// SUMW (the block entry from the expanded embedding: no write, four identical
+// streams): each lane loads its row once, and the projection takes the
+// weight summed over the stream blocks (the tiles hc_fn_pack appends) against
+// one stream's A tile, a quarter of the weight tiles and matrix-core work.
+template <bool POST, bool MEAN, int YK, bool SUMW = false>
 __global__ void __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 2)))
 exchange_kernel(const StreamArgs a) {
+  static_assert(!(SUMW && POST), "summed weights only for four identical streams (no write)");
+  constexpr int kPK = SUMW ? 1 : kHC;           // stream blocks of the projection
   __shared__ u32x4 w_lds[2][2][kHC][kNT][64];          // weight tiles, double buffered (80 KB)
   __shared__ u32x4 a_lds[4][2][kHC][64];               // X' in A layout per row block (32 KB)
   __shared__ float red[4][2][16][32];                  // projection sums per (row block, step) (16 KB)
@@ -1223,28 +1246,41 @@ exchange_kernel(const StreamArgs a) {
 #pragma unroll
   for (int j = 0; j < kHC * kHC; ++j) ccomb[j] = POST ? a.comb_in[(t0 + lt) * kHC * kHC + j] : 0.f;
 
+  // the chunk's 2 x kPK x kNT weight tiles, kPK x kNT / 4 per wave
+  constexpr int kWB = (2 * kPK * kNT + kWaves - 1) / kWaves;
+  const u32x4* fsum = SUMW ? a.fn + (size_t)(d / kStepF) * kHC * kNT * 64 : nullptr;   // stream-summed tiles
   auto load_wst = [&](int c, u32x4 (&dst)[kNT]) __attribute__((always_inline)) {
     const int gstep = (fs + c * kCF) / 32;
 #pragma unroll
-    for (int i = 0; i < kNT; ++i) {
-      const int blk = wave + i * kWaves;          // (st, k, nt) = blk / 20, (blk / 5) % 4, blk % 5
-      const int st = blk / (kHC * kNT), kk = (blk / kNT) % kHC, nt = blk % kNT;
-      dst[i] = a.fn[((size_t)((gstep + st) * kHC + kk) * kNT + nt) * 64 + lane];
+    for (int i = 0; i < kWB; ++i) {
+      const int blk = wave + i * kWaves;          // (st, k, nt) = blk / (5 kPK), (blk / 5) % kPK, blk % 5
+      const int st = blk / (kPK * kNT), kk = (blk / kNT) % kPK, nt = blk % kNT;
+      if constexpr (SUMW) {
+        if (blk < 2 * kPK * kNT) dst[i] = fsum[((size_t)(gstep + st) * kNT + nt) * 64 + lane];
+      } else {
+        dst[i] = a.fn[((size_t)((gstep + st) * kHC + kk) * kNT + nt) * 64 + lane];   // 40 blocks, 5 per wave
+      }
     }
   };
   auto store_wst = [&](int buf, const u32x4 (&src)[kNT]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kNT; ++i) {
+    for (int i = 0; i < kWB; ++i) {
       const int blk = wave + i * kWaves;
-      const int st = blk / (kHC * kNT), kk = (blk / kNT) % kHC, nt = blk % kNT;
-      w_lds[buf][st][kk][nt][lane] = src[i];
+      const int st = blk / (kPK * kNT), kk = (blk / kNT) % kPK, nt = blk % kNT;
+      if (!SUMW || blk < 2 * kPK * kNT) w_lds[buf][st][kk][nt][lane] = src[i];
     }
   };
   auto load_stream = [&](int c, u32x4 (&dst)[kHC + 1]) __attribute__((always_inline)) {
     const unsigned f = fs + c * kCF + fl;
+    if constexpr (SUMW) {
+      dst[0] = ld_stream(reinterpret_cast<const u32x4*>(xb + (lt * (unsigned)a.xtok + f)));
 #pragma unroll
-    for (int j = 0; j < kHC; ++j)
-      dst[j] = ld_stream(reinterpret_cast<const u32x4*>(xb + (lt * (unsigned)a.xtok + j * (unsigned)a.xstr + f)));
+      for (int j = 1; j < kHC; ++j) dst[j] = dst[0];
+    } else {
+#pragma unroll
+      for (int j = 0; j < kHC; ++j)
+        dst[j] = ld_stream(reinterpret_cast<const u32x4*>(xb + (lt * (unsigned)a.xtok + j * (unsigned)a.xstr + f)));
+    }
     dst[kHC] = POST ? ld_stream(reinterpret_cast<const u32x4*>(a.delta + (t0 + lt) * d + f)) : u32x4{0u, 0u, 0u, 0u};
   };
   float ssx = 0.f, ssy = 0.f;
@@ -1275,7 +1311,7 @@ exchange_kernel(const StreamArgs a) {
     for (int j = 0; j < kHC; ++j) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) ssx = dot2_bf16(xp[j][e], xp[j][e], ssx);
-      a_lds[rb][a_st][j][a_swz(a_lane, a_st)] = u32x4{xp[j][0], xp[j][1], xp[j][2], xp[j][3]};
+      if (j < kPK) a_lds[rb][a_st][j][a_swz(a_lane, a_st)] = u32x4{xp[j][0], xp[j][1], xp[j][2], xp[j][3]};
     }
     u32 yp[4];
     pre_8(xp, cpre, yp);
@@ -1287,7 +1323,7 @@ exchange_kernel(const StreamArgs a) {
   };
   auto matrix_phase = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < kHC; ++j) {
+    for (int j = 0; j < kPK; ++j) {
       const bf16x8 A = __builtin_bit_cast(bf16x8, a_lds[rb][hw][j][a_swz(lane, hw)]);
       bf16x8 B[kNT];
 #pragma unroll
@@ -2152,8 +2188,17 @@ template <bool POST, int YK>
 hipError_t launch_exchange_t(const StreamArgs& a, unsigned grid, hipStream_t st) {
   StreamArgs copy = a;
   void* args[] = {&copy};
-  const void* fn = a.x_mean ? reinterpret_cast<const void*>(&exchange_kernel<POST, true, YK>)
-                            : reinterpret_cast<const void*>(&exchange_kernel<POST, false, YK>);
+  const void* fn;
+  if constexpr (POST) {
+    fn = a.x_mean ? reinterpret_cast<const void*>(&exchange_kernel<true, true, YK>)
+                  : reinterpret_cast<const void*>(&exchange_kernel<true, false, YK>);
+  } else if (a.xstr == 0) {   // the four streams are one row: the stream-summed weight
+    fn = a.x_mean ? reinterpret_cast<const void*>(&exchange_kernel<false, true, YK, true>)
+                  : reinterpret_cast<const void*>(&exchange_kernel<false, false, YK, true>);
+  } else {
+    fn = a.x_mean ? reinterpret_cast<const void*>(&exchange_kernel<false, true, YK>)
+                  : reinterpret_cast<const void*>(&exchange_kernel<false, false, YK>);
+  }
   return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, st);
 }
 // The read-row exchange: slices of 10 or 20 chunks (640 or 1280 features), 4
@@ -2429,7 +2474,7 @@ const char* hc_last_error(void) { return g_err; }
 size_t hc_fn_packed_bytes(int hc, int d) {
   if (!hc_known(hc) || d <= 0 || d % kCF != 0 || d > kMaxD) return 0;
   if (hc != kHC) return (size_t)(hc * d / 32) * gen_nct(hc) * 64 * 16;
-  return (size_t)(d / kStepF) * kHC * kNT * 64 * 16;
+  return (size_t)(d / kStepF) * (kHC + 1) * kNT * 64 * 16;   // + the stream-summed tiles
 }
 
 int hc_fn_pack(const float* hc_fn, int hc, int d, void* fn_packed, void* stream) {
@@ -2449,7 +2494,7 @@ int hc_fn_pack(const float* hc_fn, int hc, int d, void* fn_packed, void* stream)
                          hc * d, reinterpret_cast<u32x4*>(fn_packed), recs);
     return launched(hipGetLastError(), "gpack_kernel");
   }
-  const int records = (d / kStepF) * kHC * kNT * 64;
+  const int records = (d / kStepF) * (kHC + 1) * kNT * 64;
   hipLaunchKernelGGL(pack_kernel, dim3((records + 255) / 256), dim3(256), 0, (hipStream_t)stream, hc_fn, d,
                      reinterpret_cast<u32x4*>(fn_packed), records);
   return launched(hipGetLastError(), "pack_kernel");
