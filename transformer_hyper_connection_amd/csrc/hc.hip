@@ -1335,31 +1335,70 @@ exchange_kernel(const StreamArgs a) {
   // the chunks: the next chunk's weights, then its streams, are requested
   // before this chunk's work; two barriers (A tiles and weights in place; the
   // matrix phase done before the A tiles are rewritten)
-  u32x4 cur[kHC + 1], wst[kNT];
-  load_wst(0, wst);
-  load_stream(0, cur);
-  store_wst(0, wst);
-  lds_barrier();
-  auto chunk = [&]<int C>(IC<C>) __attribute__((always_inline)) {
-    constexpr bool kMore = C + 1 < YK;
-    u32x4 nxt[kHC + 1];
-    if constexpr (kMore) {
-      load_wst(C + 1, wst);
-      load_stream(C + 1, nxt);
-    }
-    stream_phase(C, cur);
-    lds_barrier();
-    if constexpr (kMore) store_wst((C + 1) & 1, wst);
-    matrix_phase(C & 1);
-    lds_barrier();
-    if constexpr (kMore) {
+  if constexpr (SUMW) {
+    // little to load per chunk (one row, a quarter of the weight tiles): the
+    // row kP chunks ahead and the weight tiles two chunks ahead, in rings
+    // indexed by the (compile-time) chunk number, so the chunks do not wait
+    // on a memory round trip each
+    constexpr int kP = 4;
+    u32x4 hq[kP], wq[2][kNT];
+    load_wst(0, wq[0]);
 #pragma unroll
-      for (int j = 0; j <= kHC; ++j) cur[j] = nxt[j];
+    for (int c = 0; c < kP && c < YK; ++c) {
+      u32x4 t[kHC + 1];
+      load_stream(c, t);
+      hq[c] = t[0];
     }
-  };
-  [&]<int... C>(std::integer_sequence<int, C...>) __attribute__((always_inline)) {
-    (chunk(IC<C>{}), ...);
-  }(std::make_integer_sequence<int, YK>{});
+    store_wst(0, wq[0]);
+    if constexpr (YK > 1) load_wst(1, wq[1]);
+    lds_barrier();
+    auto chunk = [&]<int C>(IC<C>) __attribute__((always_inline)) {
+      if constexpr (C + 2 < YK) load_wst(C + 2, wq[C & 1]);   // its slot's tiles were stored a chunk ago
+      u32x4 src[kHC + 1];
+#pragma unroll
+      for (int j = 0; j < kHC; ++j) src[j] = hq[C % kP];
+      src[kHC] = u32x4{0u, 0u, 0u, 0u};
+      stream_phase(C, src);
+      if constexpr (C + kP < YK) {
+        u32x4 t[kHC + 1];
+        load_stream(C + kP, t);
+        hq[C % kP] = t[0];
+      }
+      lds_barrier();
+      if constexpr (C + 1 < YK) store_wst((C + 1) & 1, wq[(C + 1) & 1]);
+      matrix_phase(C & 1);
+      lds_barrier();
+    };
+    [&]<int... C>(std::integer_sequence<int, C...>) __attribute__((always_inline)) {
+      (chunk(IC<C>{}), ...);
+    }(std::make_integer_sequence<int, YK>{});
+  } else {
+    u32x4 cur[kHC + 1], wst[kNT];
+    load_wst(0, wst);
+    load_stream(0, cur);
+    store_wst(0, wst);
+    lds_barrier();
+    auto chunk = [&]<int C>(IC<C>) __attribute__((always_inline)) {
+      constexpr bool kMore = C + 1 < YK;
+      u32x4 nxt[kHC + 1];
+      if constexpr (kMore) {
+        load_wst(C + 1, wst);
+        load_stream(C + 1, nxt);
+      }
+      stream_phase(C, cur);
+      lds_barrier();
+      if constexpr (kMore) store_wst((C + 1) & 1, wst);
+      matrix_phase(C & 1);
+      lds_barrier();
+      if constexpr (kMore) {
+#pragma unroll
+        for (int j = 0; j <= kHC; ++j) cur[j] = nxt[j];
+      }
+    };
+    [&]<int... C>(std::integer_sequence<int, C...>) __attribute__((always_inline)) {
+      (chunk(IC<C>{}), ...);
+    }(std::make_integer_sequence<int, YK>{});
+  }
 
   // ---- this slice's sums of every token of the tile, as tagged words
 #pragma unroll
