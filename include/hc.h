@@ -233,7 +233,8 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
  * row on chip, the slices of a tile exchange their per-token sums through the
  * workspace as tagged words, and the RMSNorm is applied without writing y
  * first; beyond 4096 tokens (when 4096 tokens take that form) the call runs
- * as consecutive such calls of 4096 tokens and a last one for the rest.
+ * as consecutive such calls of 4096 tokens and a last one for the rest (so
+ * does a call with a fresh pre from 16384 tokens on).
  * Otherwise, with a given pre_in and n <= 128, the decode schedule of
  * hc_workspace_bytes runs;
  * and in every other case two launches: a streaming pass (X', the read row of
