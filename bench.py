@@ -56,9 +56,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_boundary_prefill_t4096.js
 BYTES_TOKEN_COMMON = 4 * D * 2 + D * 2 + 4 * D * 2 + D * 2 + 16 + 64 + 96
 BYTES_CALL = MIX * 4 * D * 4 + MIX * 4 + 3 * 4 + D * 4
 # the kernels of one call as rocprofv3 names them (the last template argument of
-# exchange_kernel is the slice width in 64-feature chunks)
+# exchange_kernel is whether the weight is stream-summed, the one before it
+# the slice width in 64-feature chunks)
 KERNELS = {"fresh": ("stream_kernel<true, 2, true, false>", "finish_kernel<2, true>"),
-           "lag": ("exchange_kernel<true, false, 20>",)}
+           "lag": ("exchange_kernel<true, false, 20, false>",)}
 
 
 def algorithmic_bytes(n: int, mode: str) -> int:
