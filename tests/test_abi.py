@@ -248,3 +248,16 @@ def test_no_device_reported_without_gpu(L):
     if torch.cuda.is_available():
         pytest.skip("a GPU is visible")
     assert L.hc_pre(P, P + 0x400000, 16, 4, 64, P + 0x800000, S) == H.HC_ENODEV
+
+
+def test_workspace_covers_the_parts_of_a_long_call(L):
+    """A call beyond 4096 tokens may run as 4096-token parts and a rest: the
+    workspace asked for its n covers the parts and any rest (whose slices can
+    be more than the whole call's)."""
+    for d in (1024, 2560, 5120, 10240):
+        for n in list(range(4097, 4096 + 4097, 61)) + [8712, 32768 + 520]:
+            w = L.hc_workspace_bytes(n, 4, d)
+            assert w >= L.hc_workspace_bytes(4096, 4, d), (n, d)
+            r = n % 4096
+            if r:
+                assert w >= L.hc_workspace_bytes(r, 4, d), (n, d, r)

@@ -2211,7 +2211,17 @@ constexpr size_t kXRegionBytes = (size_t)kXMaxGroups * kTT * kXW * sizeof(u64);
 constexpr size_t kDecOffset = kCtrlBytes;
 constexpr size_t kXOffset = kDecOffset + kDecRegionBytes;
 constexpr size_t kRecOffset = kXOffset + kXRegionBytes;
-size_t workspace_bytes(int64_t n, int d) { return kRecOffset + split_records_bytes(n, d); }
+constexpr int64_t kXPart = (int64_t)kXMaxGroups / 4 * kTT;   // tokens of the largest exchange (4 slices a tile)
+// The per-slice records a call of n tokens can need: its own, and, since a
+// call beyond kXPart tokens may run as parts of kXPart tokens and a rest (any
+// shorter count, whose slices can be more), those of every shorter call.
+size_t records_bytes(int64_t n, int d) {
+  size_t b = split_records_bytes(n, d);
+  if (n > kXPart)
+    for (int64_t t = 1; t <= kXPart / kTT; ++t) b = std::max(b, split_records_bytes(t * kTT, d));
+  return b;
+}
+size_t workspace_bytes(int64_t n, int d) { return kRecOffset + records_bytes(n, d); }
 
 template <bool POST, int RM, bool NORM>
 hipError_t launch_stream_t(const StreamArgs& a, unsigned grid, hipStream_t st) {
@@ -2247,7 +2257,6 @@ hipError_t launch_exchange_t(const StreamArgs& a, unsigned grid, hipStream_t st)
 // else, from 20 tiles up (fewer leave too many compute units idle; measured
 // at n = 1024 and 1536), slices of 10 chunks.  Returns the slice count, 0 if
 // the shape has no such split.
-constexpr int64_t kXPart = (int64_t)kXMaxGroups / 4 * kTT;   // tokens of the largest exchange (4 slices a tile)
 int exchange_slices(int64_t n, int d) {
   const int64_t tiles = (n + kTT - 1) / kTT;
   auto fits = [&](int S) {
@@ -2649,7 +2658,7 @@ int hc_workspace_layout(int64_t n, int hc, int d, size_t regions[8]) {
   regions[2] = kDecOffset;   regions[3] = kDecRegionBytes;
   regions[4] = kXOffset;     regions[5] = kXRegionBytes;
   regions[6] = kRecOffset;
-  regions[7] = n == 0 ? 0 : (hc == kHC ? split_records_bytes(n, d) : generic_ws_bytes(n, hc, d) - kRecOffset);
+  regions[7] = n == 0 ? 0 : (hc == kHC ? records_bytes(n, d) : generic_ws_bytes(n, hc, d) - kRecOffset);
   return HC_OK;
 }
 
