@@ -68,3 +68,52 @@ def test_random_boundary(case):
     _check_boundary(ref, got, {"x": streams, "gamma": s["gamma"]}, fresh, norm)
     if mean:
         assert_bits_equal(host_bits(got["x_mean"]), ref["x_mean"], "stream mean")
+
+
+def _entry_cases(count=20, seed=7):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        hc = int(rng.choice([2, 4, 8]))
+        n = int(rng.integers(1, 5001))
+        d = int(rng.choice([64, 320, 1024, 5120] if hc != 8 else [64, 320, 1024, 2048]))
+        out.append((i, hc, n, d, str(rng.choice(["mixes", "pre", "post", "boundary", "static"]))))
+    return out
+
+
+@pytest.mark.parametrize("case", _entry_cases(), ids=lambda c: "e%d-hc%d-n%d-d%d-%s" % c)
+def test_random_entry_points(case):
+    """The standalone entry points, the boundary at hc = 2 and 8, and the
+    boundary on the library's static workspace, on seeded random shapes."""
+    i, hc, n, d, what = case
+    say(f"[random entry {i}] hc={hc} n={n} d={d} {what}")
+    from tests.gpu_util import assert_coef_close, assert_mixes_close, host_f32
+    s = synth.boundary_inputs("prefill", 0, n, d, hc=hc)
+    X = bf16_dev(s["x"])
+    if what == "mixes":
+        fn = H.hc_fn_pack(f32_dev(s["hc_fn"]), hc=hc)
+        pre, post, comb, mixes = H.hc_mixes(X, fn, f32_dev(s["hc_scale"]), f32_dev(s["hc_base"]), return_mixes=True)
+        rm = O.hc_mixes(s["x"], s["hc_fn"], 1e-6)
+        assert_mixes_close(host_f32(mixes), rm)
+        rp, rq, rc = O.hc_split_sinkhorn(rm, s["hc_scale"], s["hc_base"], hc)
+        assert_coef_close(host_f32(pre), rp, "pre")
+        assert_coef_close(host_f32(post), rq, "post")
+        assert_coef_close(host_f32(comb), rc, "comb")
+    elif what == "pre":
+        assert_bits_equal(host_bits(H.hc_pre(X, f32_dev(s["pre_in"]))), O.hc_pre(s["x"], s["pre_in"]), "hc_pre")
+    elif what == "post":
+        got = H.hc_post(bf16_dev(s["delta"]), X, f32_dev(s["post_in"]), f32_dev(s["comb_in"]))
+        assert_bits_equal(host_bits(got), O.hc_post(s["delta"], s["x"], s["post_in"], s["comb_in"]), "hc_post")
+    else:
+        kw = dict(x=s["x"], delta=s["delta"], post_in=s["post_in"], comb_in=s["comb_in"], pre_in=s["pre_in"],
+                  hc_fn=s["hc_fn"], hc_base=s["hc_base"], hc_scale=s["hc_scale"], gamma=s["gamma"])
+        dev = {k: (bf16_dev(v) if v.dtype == np.uint16 else f32_dev(v)) for k, v in kw.items() if k not in ("x",
+                                                                                                         "hc_fn")}
+        dev["fn_packed"] = H.hc_fn_pack(f32_dev(s["hc_fn"]), hc=hc)
+        if what == "static" and hc == 4 and H.lib().hc_boundary_workspace_bytes(n, hc, d) <= 16 << 20:
+            got = H.hc_boundary_static(X, **dev, want_mixes=True)
+        else:
+            got = H.hc_boundary(X, **dev, want_mixes=True)
+        torch.cuda.synchronize()
+        ref = O.boundary(**kw, hc=hc)
+        _check_boundary(ref, got, {"x": s["x"], "gamma": s["gamma"]}, False, True)
