@@ -58,7 +58,7 @@ BYTES_CALL = MIX * 4 * D * 4 + MIX * 4 + 3 * 4 + D * 4
 # the kernels of one call as rocprofv3 names them (the last template argument of
 # exchange_kernel is whether the weight is stream-summed, the one before it
 # the slice width in 64-feature chunks)
-KERNELS = {"fresh": ("stream_kernel<true, 2, true, false>", "finish_kernel<2, true>"),
+KERNELS = {"fresh": ("stream_kernel<2, true, false>", "finish_kernel<2, true>"),
            "lag": ("exchange_kernel<true, false, 20, false>",)}
 
 

@@ -81,10 +81,11 @@ def test_packed_and_workspace_bytes(L):
     assert L.hc_workspace_bytes(4096, 3, 5120) == 0
     w = L.hc_workspace_bytes(4096, 4, 5120)
     # 8 KB control block; decode words: 8 tiles x (8192/256) slices x 16 tokens x 26 tagged 8-byte words;
-    # read-row exchange words: 256 groups x 64 tokens x 26 tagged words; then the two-launch records:
-    # 64 tiles of 64 tokens x 4 slices x 36 floats
+    # read-row exchange words: 256 groups x 64 tokens x 26 tagged words; then the per-slice records:
+    # 64 tiles of 64 tokens x 36 floats x the larger slice count of the two first kernels (the stream
+    # kernel's 64 tiles take 4 slices, the projection kernel's 32 workgroups of 128 tokens 8)
     fixed = 8192 + 8 * 32 * 16 * 26 * 8 + 256 * 64 * 26 * 8
-    assert w == fixed + 64 * 4 * 64 * 36 * 4
+    assert w == fixed + 64 * 8 * 64 * 36 * 4
     # n = 128: 2 tiles x 40 slices
     assert L.hc_workspace_bytes(128, 4, 5120) == fixed + 2 * 40 * 64 * 36 * 4
     assert L.hc_boundary_workspace_bytes(4096, 4, 5120) == w

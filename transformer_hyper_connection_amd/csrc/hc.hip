@@ -11,12 +11,15 @@
 // sequence of separately rounded fp32 products and sums, bit for bit).
 //
 // Kernels (hc = 4, the pages' setting)
-//   stream_kernel<POST, RM, NORM, MEAN> + finish_kernel<RM, NORM>  everything
-//       that derives mixes (hc_mixes, block entry, sublayer boundary) at any n:
-//       64-token tiles x feature slices, about one workgroup per compute unit;
-//       the 24-wide projection on the matrix cores with the weight tiles shared
+//   stream_kernel<RM, NORM, MEAN> + finish_kernel<RM, NORM>  everything that
+//       derives mixes and writes X' (the sublayer boundary) at any n: 64-token
+//       tiles x feature slices, about one workgroup per compute unit; the
+//       24-wide projection on the matrix cores with the weight tiles shared
 //       through LDS; the per-slice sums meet in the workspace, and the finish
 //       derives the coefficients and writes the read row.
+//   proj_kernel<RM, NORM, MEAN> + finish_kernel<RM, NORM>  the same with no
+//       write (hc_mixes, block entry): 128-token workgroups, half the weight
+//       traffic per token.
 //   exchange_kernel<POST, MEAN, YK>  a given pre with the RMSNorm in one launch
 //       (tiles of 4 to 8 slices of YK chunks): the slices of a tile exchange
 //       their per-token sums as tagged words; the read row stays in registers.
@@ -792,8 +795,10 @@ __device__ __forceinline__ void derive_quad(float dpre, float dpost, const float
 
 // ====================================================== boundary: two kernels
 // Everything that derives mixes (hc_mixes, block entry, sublayer boundary)
-// runs as two ordinary launches; the boundary between them is the only
-// device-wide synchronisation.
+// can run as two ordinary launches; the boundary between them is the only
+// device-wide synchronisation.  The first is the stream kernel when X' is
+// written, else the projection kernel (proj_kernel, below: the same records
+// from 128-token workgroups).
 //
 // stream_kernel: tokens form tiles of 64 (4 row blocks of 16); the features
 // of each stream are cut into S slices of F = d/S (a multiple of 64), S chosen
@@ -886,7 +891,7 @@ template <int N> struct IC { static constexpr int v = N; };
 // calls without it carry none of its registers.
 // (Its 112 KB of LDS allow one workgroup, two waves per SIMD, per compute
 // unit; the register budget says so, else the compiler aims at three.)
-template <bool POST, int RM, bool NORM, bool MEAN>
+template <int RM, bool NORM, bool MEAN>
 __global__ void __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 2)))
 stream_kernel(const StreamArgs a) {
   static_assert(!NORM || RM != kNoRead, "RMSNorm needs the read row");
@@ -918,18 +923,18 @@ stream_kernel(const StreamArgs a) {
   const bool tv = t0 + m < a.n;
   const unsigned lt = tv ? (unsigned)m : 0u;   // tokens past n read the tile's first token
   const hc_bf16* xb = a.x + t0 * a.xtok;
-  const hc_bf16* db = POST ? a.delta + t0 * d : a.x;
-  hc_bf16* xob = POST ? a.x_out + t0 * kHC * d : nullptr;
+  const hc_bf16* db = a.delta + t0 * d;
+  hc_bf16* xob = a.x_out + t0 * kHC * d;
   hc_bf16* yb = RM == kGivenPre ? a.y_out + t0 * d : nullptr;
 
   float cpost[kHC], ccomb[kHC * kHC], cpre[kHC];
 #pragma unroll
   for (int j = 0; j < kHC; ++j) {
-    cpost[j] = POST ? a.post_in[(t0 + lt) * kHC + j] : 0.f;
+    cpost[j] = a.post_in[(t0 + lt) * kHC + j];
     cpre[j] = RM == kGivenPre ? a.pre_in[(t0 + lt) * kHC + j] : 0.f;
   }
 #pragma unroll
-  for (int j = 0; j < kHC * kHC; ++j) ccomb[j] = POST ? a.comb_in[(t0 + lt) * kHC * kHC + j] : 0.f;
+  for (int j = 0; j < kHC * kHC; ++j) ccomb[j] = a.comb_in[(t0 + lt) * kHC * kHC + j];
 
   u32x4 cur[kHC + 1];
   u32x4 wst[kNT];  // this wave's share (5 of 40 blocks) of the next chunk's weight tiles
@@ -979,30 +984,22 @@ stream_kernel(const StreamArgs a) {
     const unsigned f = fs + c * kCF + fl;
 #pragma unroll
     for (int j = 0; j < kHC; ++j) dst[j] = ld_stream(reinterpret_cast<const u32x4*>(xb + (lt * (unsigned)a.xtok + j * (unsigned)a.xstr + f)));
-    dst[kHC] = POST ? ld_stream(reinterpret_cast<const u32x4*>(db + (lt * d + f))) : u32x4{0u, 0u, 0u, 0u};
+    dst[kHC] = ld_stream(reinterpret_cast<const u32x4*>(db + (lt * d + f)));
   };
   auto stream_phase = [&](int c, const u32x4 (&src)[kHC + 1]) __attribute__((always_inline)) {
     const unsigned f = fs + c * kCF + fl;
     u32 xp[kHC][4];
-    if constexpr (POST) {
-      post_8(src, cpost, ccomb, xp);
-      if (tv) {
+    post_8(src, cpost, ccomb, xp);
+    if (tv) {
 #pragma unroll
-        for (int k = 0; k < kHC; ++k) {
-          u32x4* p = reinterpret_cast<u32x4*>(xob + (lt * kHC * d + k * d + f));
-          const u32x4 v = u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]};
-          if constexpr (RM == kFreshPre) st_keep(p, v); else st_stream(p, v);
-        }
+      for (int k = 0; k < kHC; ++k) {
+        u32x4* p = reinterpret_cast<u32x4*>(xob + (lt * kHC * d + k * d + f));
+        const u32x4 v = u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]};
+        if constexpr (RM == kFreshPre) st_keep(p, v); else st_stream(p, v);
       }
-    } else {
-#pragma unroll
-      for (int k = 0; k < kHC; ++k)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) xp[k][e] = src[k][e];
     }
     // unconditional: a lane past n works on the tile's first token (lt = 0) and
-    // stores the same bits as that token's lane; with no branch the wait counts
-    // of the two-chunk loop need not assume a skipped store
+    // stores the same bits as that token's lane
     if constexpr (MEAN) st_stream(reinterpret_cast<u32x4*>(a.x_mean + (t0 + lt) * d + f), mean_8(xp));
 #pragma unroll
     for (int k = 0; k < kHC; ++k) {
@@ -1066,69 +1063,12 @@ stream_kernel(const StreamArgs a) {
       for (int j = 0; j <= kHC; ++j) cur[j] = nxt[j];
     }
   };
-  // Two chunks in flight (the kernels that store no X'): while chunk c is
-  // consumed, c+1 is arriving, and c+2 is requested as soon as c's stream
-  // registers are free.  Each chunk's weights are requested before its streams,
-  // so the wait for the weights (one chunk later) never waits for younger
-  // stream loads.  Register sets alternate with the chunk's parity (loop
-  // unrolled by two: no copies of loaded registers).  Measured at n = 4096:
-  // hc_mixes' kernel 41.5 -> 38.4 us; with hc_post (X' stored) the same loop
-  // is slower, 70.5 -> 71.9 us, so those keep one chunk in flight.
-  auto deep_step = [&](int c, auto ISSUE, auto STORE, u32x4 (&s)[kHC + 1], u32x4 (&wfree)[kNT],
-                       const u32x4 (&wnext)[kNT]) {
-    __builtin_amdgcn_sched_barrier(0);             // nothing of chunk c moves into chunk c-1
-    stream_phase(c, s);
-    if constexpr (decltype(ISSUE)::v) {
-      __builtin_amdgcn_sched_barrier(0);           // keep the issue order: weights, then streams
-      load_wst(c + 2, wfree);
-      __builtin_amdgcn_sched_barrier(0);
-      load_stream(c + 2, s);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    lds_barrier();
-    if constexpr (decltype(STORE)::v) store_wst((c + 1) & 1, wnext);
-    matrix_phase(c & 1);
-    flush();
-    lds_barrier();
-  };
-
-  if constexpr (!POST) {
-    u32x4 sB[kHC + 1], wB[kNT];
-    const int c1 = nch > 1 ? 1 : 0;                // a single chunk loads chunk 0 twice (unused)
-    load_wst(0, wst);
-    __builtin_amdgcn_sched_barrier(0);
-    load_stream(0, cur);
-    __builtin_amdgcn_sched_barrier(0);
-    load_wst(c1, wB);
-    __builtin_amdgcn_sched_barrier(0);
-    load_stream(c1, sB);
-    __builtin_amdgcn_sched_barrier(0);
-    store_wst(0, wst);
-    lds_barrier();
-    int c = 0;
-    for (; c + 3 < nch; c += 2) {
-      deep_step(c, IC<1>{}, IC<1>{}, cur, wst, wB);
-      deep_step(c + 1, IC<1>{}, IC<1>{}, sB, wB, wst);
-    }
-    const int left = nch - c;                       // 1..3: chunk c in cur, c+1 in sB
-    if (left == 3) {
-      deep_step(c, IC<1>{}, IC<1>{}, cur, wst, wB);
-      deep_step(c + 1, IC<0>{}, IC<1>{}, sB, wB, wst);
-      deep_step(c + 2, IC<0>{}, IC<0>{}, cur, wst, wB);
-    } else if (left == 2) {
-      deep_step(c, IC<0>{}, IC<1>{}, cur, wst, wB);
-      deep_step(c + 1, IC<0>{}, IC<0>{}, sB, wB, wst);
-    } else {
-      deep_step(c, IC<0>{}, IC<0>{}, cur, wst, wB);
-    }
-  } else {
-    load_wst(0, wst);
-    load_stream(0, cur);
-    store_wst(0, wst);
-    lds_barrier();
-    for (int c = 0; c + 1 < nch; ++c) chunk(c, true);
-    chunk(nch - 1, false);
-  }
+  load_wst(0, wst);
+  load_stream(0, cur);
+  store_wst(0, wst);
+  lds_barrier();
+  for (int c = 0; c + 1 < nch; ++c) chunk(c, true);
+  chunk(nch - 1, false);
 
   // ---- per-token records of this slice
 #pragma unroll
@@ -1172,6 +1112,266 @@ stream_kernel(const StreamArgs a) {
       }
     }
     *reinterpret_cast<f32x4*>(rec + tm * kRec + q0) = f32x4{v[0], v[1], v[2], v[3]};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// proj_kernel: the stream kernel's work when nothing is written back (hc_mixes,
+// the block entry): per-slice records of the projection dots, sum x^2 and the
+// norm sums, in the stream kernel's record layout, for the finish kernel.
+// Its cost is the weight tiles, not the streams: every workgroup reads its
+// slice's tiles (from L2) once, so a workgroup takes 128 tokens (two record
+// tiles), half the weight traffic per token of a 64-token tile.  Wave w owns
+// row block w (16 tokens) in both phases:
+//   stream phase: two groups of 8 tokens, 8 lanes a token, 8 features a lane;
+//     the row block's A tiles are written to LDS, where only wave w reads
+//     them; the sums accumulate in registers;
+//   matrix phase: both 32-feature steps x 4 streams x 5 tiles against the
+//     chunk's weight tiles, which all waves stage (double buffered), so one
+//     barrier per chunk.
+// Streams and weights run two chunks ahead in register pairs.  Each chunk's
+// fp32 matrix-core sums are added in fp64, rounded once at the end.
+constexpr int kPTT = 128;                 // tokens per workgroup
+
+template <int RM, bool NORM, bool MEAN>
+__global__ void __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 2)))
+proj_kernel(const StreamArgs a) {
+  static_assert(!NORM || RM != kNoRead, "RMSNorm needs the read row");
+  __shared__ u32x4 w_lds[2][2][kHC][kNT][64];          // weight tiles, double buffered (80 KB)
+  __shared__ u32x4 a_lds[kWaves][2][kHC][64];          // A tiles per row block (64 KB)
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // = row block
+  const int d = a.d, S = a.S, F = a.F;
+  const int nch = F / kCF;
+  const int tiles2 = (a.tiles + 1) / 2;
+  const int lin = (gridDim.x & 7) ? blockIdx.x : (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int slice = lin / tiles2;
+  const int tile2 = lin % tiles2;
+  const int fs = slice * F;
+
+  const int hl = lane >> 3;
+  const int fl = (lane & 7) * 8;
+  const int a_st = fl >> 5, a_g = (fl >> 3) & 3;
+  constexpr int kUsed = rec_used<RM, NORM>();
+  constexpr int kQuads = (kUsed + 3) / 4;
+
+  const int64_t t0 = (int64_t)tile2 * kPTT;           // < n: the first token of the workgroup is real
+  bool tv[2];
+  int64_t tm64[2];
+  const hc_bf16* xr[2];
+  float cpre[2][kHC];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int m = wave * 16 + p * 8 + hl;
+    tv[p] = t0 + m < a.n;
+    tm64[p] = t0 + m;
+    const int64_t tr = tv[p] ? t0 + m : t0;          // a token past n reads the first token
+    xr[p] = a.x + tr * a.xtok;
+#pragma unroll
+    for (int j = 0; j < kHC; ++j) cpre[p][j] = RM == kGivenPre ? a.pre_in[tr * kHC + j] : 0.f;
+  }
+
+  f32x4 acc[kAcc];
+  double acc64[kAcc][4];
+#pragma unroll
+  for (int t = 0; t < kAcc; ++t) {
+    acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc64[t][i] = 0.0;
+  }
+  float ssx[2] = {0.f, 0.f}, ssy[2] = {0.f, 0.f};
+  float gram[2][kGram];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int g = 0; g < kGram; ++g) gram[p][g] = 0.f;
+
+  auto load_wst = [&](int c, u32x4 (&dst)[kNT]) __attribute__((always_inline)) {
+    const int gstep = (fs + c * kCF) / 32;
+#pragma unroll
+    for (int i = 0; i < kNT; ++i) {
+      const int blk = wave + i * kWaves;          // (st, k, nt) = blk / 20, (blk / 5) % 4, blk % 5
+      const int st = blk / (kHC * kNT), k = (blk / kNT) % kHC, nt = blk % kNT;
+      dst[i] = a.fn[((size_t)((gstep + st) * kHC + k) * kNT + nt) * 64 + lane];
+    }
+  };
+  auto store_wst = [&](int buf, const u32x4 (&src)[kNT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kNT; ++i) {
+      const int blk = wave + i * kWaves;
+      const int st = blk / (kHC * kNT), k = (blk / kNT) % kHC, nt = blk % kNT;
+      w_lds[buf][st][k][nt][lane] = src[i];
+    }
+  };
+  auto load_stream = [&](int c, u32x4 (&dst)[2][kHC]) __attribute__((always_inline)) {
+    const unsigned f = fs + c * kCF + fl;
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int j = 0; j < kHC; ++j) dst[p][j] = ld_stream(reinterpret_cast<const u32x4*>(xr[p] + (j * (unsigned)a.xstr + f)));
+  };
+  auto stream_phase = [&](int c, const u32x4 (&src)[2][kHC]) __attribute__((always_inline)) {
+    const unsigned f = fs + c * kCF + fl;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      u32 xp[kHC][4];
+#pragma unroll
+      for (int k = 0; k < kHC; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xp[k][e] = src[p][k][e];
+      if constexpr (MEAN) {
+        if (tv[p]) st_stream(reinterpret_cast<u32x4*>(a.x_mean + tm64[p] * d + f), mean_8(xp));
+      }
+      const int a_lane = a_g * 16 + p * 8 + hl;
+#pragma unroll
+      for (int k = 0; k < kHC; ++k) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ssx[p] = dot2_bf16(xp[k][e], xp[k][e], ssx[p]);
+        a_lds[wave][a_st][k][a_swz(a_lane, a_st)] = u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]};
+      }
+      if constexpr (RM == kGivenPre) {
+        u32 yp[4];
+        pre_8(xp, cpre[p], yp);
+        if constexpr (NORM) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ssy[p] = dot2_bf16(yp[e], yp[e], ssy[p]);
+        }
+        if (tv[p]) {
+          u32x4* q = reinterpret_cast<u32x4*>(a.y_out + tm64[p] * d + f);
+          const u32x4 v = u32x4{yp[0], yp[1], yp[2], yp[3]};
+          if constexpr (NORM) st_keep(q, v); else st_stream(q, v);
+        }
+      }
+      if constexpr (RM == kFreshPre && NORM) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          int g = 0;
+#pragma unroll
+          for (int j = 0; j < kHC; ++j)
+#pragma unroll
+            for (int l = j; l < kHC; ++l, ++g) gram[p][g] = dot2_bf16(xp[j][e], xp[l][e], gram[p][g]);
+        }
+      }
+    }
+  };
+  auto matrix_phase = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int k = 0; k < kHC; ++k) {
+        const bf16x8 A = __builtin_bit_cast(bf16x8, a_lds[wave][st][k][a_swz(lane, st)]);
+        bf16x8 B[kNT];
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) B[nt] = __builtin_bit_cast(bf16x8, w_lds[buf][st][k][nt][lane]);
+        mfma_step(A, B, acc);
+      }
+#pragma unroll
+    for (int t = 0; t < kAcc; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc64[t][i] += (double)acc[t][i];
+      acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  // one chunk: chunk c+1's weights were requested two chunks ago and go to
+  // LDS after the barrier (which also ends every wave's reads of that buffer,
+  // chunk c-1's); chunk c+2's weights, then its streams, are requested once
+  // chunk c's stream registers are free
+  auto step = [&](int c, auto ISSUE, auto STORE, u32x4 (&s)[2][kHC], u32x4 (&wfree)[kNT],
+                  const u32x4 (&wnext)[kNT]) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    stream_phase(c, s);
+    if constexpr (decltype(ISSUE)::v) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_wst(c + 2, wfree);
+      __builtin_amdgcn_sched_barrier(0);
+      load_stream(c + 2, s);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lds_barrier();
+    if constexpr (decltype(STORE)::v) store_wst((c + 1) & 1, wnext);
+    matrix_phase(c & 1);
+  };
+
+  {
+    u32x4 sA[2][kHC], sB[2][kHC], wA[kNT], wB[kNT];
+    const int c1 = nch > 1 ? 1 : 0;                   // a single chunk loads chunk 0 twice (unused)
+    load_wst(0, wA);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stream(0, sA);
+    __builtin_amdgcn_sched_barrier(0);
+    load_wst(c1, wB);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stream(c1, sB);
+    __builtin_amdgcn_sched_barrier(0);
+    store_wst(0, wA);
+    int c = 0;
+    for (; c + 3 < nch; c += 2) {
+      step(c, IC<1>{}, IC<1>{}, sA, wA, wB);
+      step(c + 1, IC<1>{}, IC<1>{}, sB, wB, wA);
+    }
+    const int left = nch - c;                         // 1..3: chunk c in sA, c+1 in sB
+    if (left == 3) {
+      step(c, IC<1>{}, IC<1>{}, sA, wA, wB);
+      step(c + 1, IC<0>{}, IC<1>{}, sB, wB, wA);
+      step(c + 2, IC<0>{}, IC<0>{}, sA, wA, wB);
+    } else if (left == 2) {
+      step(c, IC<0>{}, IC<1>{}, sA, wA, wB);
+      step(c + 1, IC<0>{}, IC<0>{}, sB, wB, wA);
+    } else {
+      step(c, IC<0>{}, IC<0>{}, sA, wA, wB);
+    }
+  }
+
+  // ---- per-token records of this slice, in the two record tiles of the workgroup
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      ssx[p] += __shfl_xor(ssx[p], o);
+      if constexpr (RM == kGivenPre && NORM) ssy[p] += __shfl_xor(ssy[p], o);
+      if constexpr (RM == kFreshPre && NORM) {
+#pragma unroll
+        for (int g = 0; g < kGram; ++g) gram[p][g] += __shfl_xor(gram[p][g], o);
+      }
+    }
+  lds_barrier();                                      // every wave's last matrix phase done: the weight area is reused
+  double* red64 = reinterpret_cast<double*>(&w_lds[0][0][0][0][0]);   // [row block][acc tile][4 rows][64 lanes]
+#pragma unroll
+  for (int t = 0; t < kAcc; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red64[((wave * kAcc + t) * 4 + i) * 64 + lane] = acc64[t][i];
+  float* extra = reinterpret_cast<float*>(red64 + kWaves * kAcc * 4 * 64);   // [kRec - kMix][kPTT]
+  if ((lane & 7) == 0) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int m = wave * 16 + p * 8 + hl;
+      extra[m] = ssx[p];
+      if constexpr (RM == kGivenPre && NORM) extra[kPTT + m] = ssy[p];
+      if constexpr (RM == kFreshPre && NORM) {
+#pragma unroll
+        for (int g = 0; g < kGram; ++g) extra[(1 + g) * kPTT + m] = gram[p][g];
+      }
+    }
+  }
+  lds_barrier();
+  for (int idx = threadIdx.x; idx < kPTT * kQuads; idx += kThreads) {
+    const int tm = idx / kQuads, q0 = (idx % kQuads) * 4;
+    const int tile = 2 * tile2 + (tm >> 6);
+    if (tile >= a.tiles) continue;                    // the second record tile of a call's last 64 tokens
+    // token tm's accumulator element: row block tm / 16, row tm % 4 of lanes 16 ((tm % 16) / 4) + column;
+    // rows 16..23 sit in columns q - 16 and q - 8 of the second tile
+    const double* e = red64 + ((tm >> 4) * kAcc * 4 + (tm & 3)) * 64 + 16 * ((tm & 15) >> 2);
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = q0 + i;
+      if (q < 16) v[i] = (float)e[q];
+      else if (q < kMix) v[i] = (float)(e[4 * 64 + q - 16] + e[4 * 64 + q - 8]);
+      else v[i] = q < kUsed ? extra[(q - kMix) * kPTT + tm] : 0.f;
+    }
+    float* rec = a.rec + (((size_t)tile * S + slice) * kTT + (tm & 63)) * kRec;
+    *reinterpret_cast<f32x4*>(rec + q0) = f32x4{v[0], v[1], v[2], v[3]};
   }
 }
 
@@ -2184,13 +2384,18 @@ int stream_slices(int64_t n, int d) {
   const int64_t tiles = (n + kTT - 1) / kTT;
   return divisor_at_least(d / kCF, std::min<int64_t>((256 + tiles - 1) / tiles, kMaxSlices));
 }
+// slices of the projection kernel (128-token workgroups)
+int proj_slices(int64_t n, int d) {
+  const int64_t tiles2 = (n + 2 * kTT - 1) / (2 * kTT);
+  return divisor_at_least(d / kCF, std::min<int64_t>((256 + tiles2 - 1) / tiles2, kMaxSlices));
+}
 int read_slices(int64_t n, int d) {
   const int64_t tiles = (n + kTT - 1) / kTT;
   return divisor_at_least(d / kCF, std::min<int64_t>((512 + tiles - 1) / tiles, kMaxSlices));
 }
 size_t split_records_bytes(int64_t n, int d) {
   const int64_t tiles = (n + kTT - 1) / kTT;
-  return (size_t)tiles * stream_slices(n, d) * kTT * kRec * 4;
+  return (size_t)tiles * std::max(stream_slices(n, d), proj_slices(n, d)) * kTT * kRec * 4;
 }
 // Workspace layout, the same for every (n, hc, d), so that one workspace
 // serves calls of any shape and no region of one call lies on the persistent
@@ -2223,14 +2428,20 @@ size_t records_bytes(int64_t n, int d) {
 }
 size_t workspace_bytes(int64_t n, int d) { return kRecOffset + records_bytes(n, d); }
 
+// without POST the 128-token projection kernel, with it the stream kernel
 template <bool POST, int RM, bool NORM>
 hipError_t launch_stream_t(const StreamArgs& a, unsigned grid, hipStream_t st) {
   StreamArgs copy = a;
   void* args[] = {&copy};
-  const void* fn = a.x_mean ? reinterpret_cast<const void*>(&stream_kernel<POST, RM, NORM, true>)
-                            : reinterpret_cast<const void*>(&stream_kernel<POST, RM, NORM, false>);
-  return hipLaunchKernel(fn, dim3(grid), dim3(kThreads),
-                         args, 0, st);
+  const void* fn;
+  if constexpr (POST) {
+    fn = a.x_mean ? reinterpret_cast<const void*>(&stream_kernel<RM, NORM, true>)
+                  : reinterpret_cast<const void*>(&stream_kernel<RM, NORM, false>);
+  } else {
+    fn = a.x_mean ? reinterpret_cast<const void*>(&proj_kernel<RM, NORM, true>)
+                  : reinterpret_cast<const void*>(&proj_kernel<RM, NORM, false>);
+  }
+  return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, st);
 }
 // the given-pre boundary with the RMSNorm in one launch (read row kept, slice YK chunks wide)
 template <bool POST, int YK>
@@ -2311,12 +2522,17 @@ int launch_boundary(bool post, int rm, bool norm, StreamArgs s, FinishArgs f, vo
     else e = yk == 20 ? launch_exchange_t<false, 20>(s, grid, st) : launch_exchange_t<false, 10>(s, grid, st);
     return launched(e, what);
   }
+  if (!post) {                                    // the projection kernel: 128-token workgroups
+    s.S = proj_slices(s.n, s.d);
+    s.F = s.d / s.S;
+  }
+  const unsigned gridp = (unsigned)((tiles + 1) / 2 * s.S);
   if (phases & 1) switch ((post ? 8 : 0) | (rm << 1) | (norm ? 1 : 0)) {
-    case 0x0: e = launch_stream_t<false, kNoRead, false>(s, grid1, st); break;
-    case 0x2: e = launch_stream_t<false, kGivenPre, false>(s, grid1, st); break;
-    case 0x3: e = launch_stream_t<false, kGivenPre, true>(s, grid1, st); break;
-    case 0x4: e = launch_stream_t<false, kFreshPre, false>(s, grid1, st); break;
-    case 0x5: e = launch_stream_t<false, kFreshPre, true>(s, grid1, st); break;
+    case 0x0: e = launch_stream_t<false, kNoRead, false>(s, gridp, st); break;
+    case 0x2: e = launch_stream_t<false, kGivenPre, false>(s, gridp, st); break;
+    case 0x3: e = launch_stream_t<false, kGivenPre, true>(s, gridp, st); break;
+    case 0x4: e = launch_stream_t<false, kFreshPre, false>(s, gridp, st); break;
+    case 0x5: e = launch_stream_t<false, kFreshPre, true>(s, gridp, st); break;
     case 0xA: e = launch_stream_t<true, kGivenPre, false>(s, grid1, st); break;
     case 0xB: e = launch_stream_t<true, kGivenPre, true>(s, grid1, st); break;
     case 0xC: e = launch_stream_t<true, kFreshPre, false>(s, grid1, st); break;
