@@ -269,6 +269,30 @@ def test_boundary_entry(fresh):
     _check_boundary(ref, got, s, fresh, True)
 
 
+# The block entry from the streams as given stores no X': the 128-token
+# projection kernel, whose last workgroup's second 64-token record tile lies
+# past n when the count of 64-token tiles is odd (n = 191: 3 tiles; 4160: 65,
+# where the given pre with the RMSNorm runs as a 4096-token exchange and a
+# 64-token decode call instead).  Every token, with the stream mean.
+@pytest.mark.parametrize("n", [191, 4160])
+@pytest.mark.parametrize("fresh,norm", [(True, True), (True, False), (False, True), (False, False)])
+def test_entry_odd_tile_counts(n, fresh, norm):
+    say(f"[entry] n={n} fresh={fresh} norm={norm}: every token, with the stream mean")
+    s = synth.boundary_inputs("prefill", 0, n)
+    kw = dict(x=s["x"], pre_in=None if fresh else s["pre_in"], gamma=s["gamma"] if norm else None,
+              hc_fn=s["hc_fn"], hc_base=s["hc_base"], hc_scale=s["hc_scale"])
+    ref = O.boundary(**kw, want_mean=True)
+    dev = {k: (bf16_dev(v) if v.dtype == np.uint16 else f32_dev(v)) for k, v in kw.items()
+           if v is not None and k != "hc_fn"}
+    dev["fn_packed"] = packed(s["hc_fn"])
+    x = dev.pop("x")
+    got = H.hc_boundary(x, **dev, want_mixes=True, want_mean=True)
+    torch.cuda.synchronize()
+    assert got["x_out"] is None
+    _check_boundary(ref, got, s, fresh, norm)
+    assert_bits_equal(host_bits(got["x_mean"]), ref["x_mean"], "stream mean")
+
+
 def test_boundary_exit():
     say("[boundary exit]")
     ref, got, s = _boundary_case("prefill", 7, 30, False, True, exit_=True)

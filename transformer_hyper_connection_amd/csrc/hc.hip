@@ -330,13 +330,18 @@ __global__ void __launch_bounds__(kGThreads, 2) gmix_kernel(const GMixArgs a) {
   const int c0 = slice * a.Fs;
   const int nch = a.Fs / kGChunk;
 
+  // The A operand comes straight from memory in the matrix-core layout: 64
+  // bytes of each of 16 token rows per instruction, the two steps' halves of
+  // a 128-byte line back to back.  Plain (cached) loads, so that the two
+  // halves meet in L2 as one line fill; nontemporal ones measured slower
+  // (hc = 8: 314 against 306 us per boundary).
   auto load_a = [&](int ch, u32x4 (&A)[2][2]) {
     const int c = c0 + ch * kGChunk;              // a chunk never crosses a stream (d % 64 == 0)
     const int j = c / a.d, i = c - j * a.d + kg;
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-      for (int st = 0; st < 2; ++st) A[ti][st] = ld_stream(reinterpret_cast<const u32x4*>(xr[ti] + j * a.xstr + i + 32 * st));
+      for (int st = 0; st < 2; ++st) A[ti][st] = *reinterpret_cast<const u32x4*>(xr[ti] + j * a.xstr + i + 32 * st);
   };
   auto load_b = [&](int ch, u32x4 (&Bs)[BPT]) {
     const u32x4* src = a.fn + (size_t)((c0 + ch * kGChunk) / 32) * NCT * 64;
