@@ -798,6 +798,58 @@ __device__ __forceinline__ void derive_quad(float dpre, float dpost, const float
   *reinterpret_cast<f32x4*>(comb_out + t * HC * HC + j * HC) = f32x4{A[0], A[1], A[2], A[3]};
 }
 
+// Lane exchanges inside a 16-lane row for the 16-lanes-per-token derive: lane
+// i <- lane i ^ 4 (reverse the quad, then mirror the half row) and lane i <-
+// lane i ^ 8 (rotate the row by 8).
+__device__ __forceinline__ float xor4_16(float v) { return quad_perm<0x141>(quad_perm<0x1B>(v)); }
+__device__ __forceinline__ float xor8_16(float v) { return quad_perm<0x128>(v); }
+// Sum over the lanes k, k+4, k+8, k+12 of a 16-lane row (a comb column): a
+// butterfly, so every lane of the column gets the same bits.
+__device__ __forceinline__ float col_sum16(float v) {
+  const float u = v + xor4_16(v);
+  return u + xor8_16(u);
+}
+
+// The split and Sinkhorn of one token, 16 lanes per token ("Reading weights"
+// kernel panel and reading-weight equation): lane 4j+k of the token's 16-lane
+// row holds comb element (j, k), so a Sinkhorn row sum is a quad sum and a
+// column sum a butterfly over the four quads, one element per lane (a short
+// dependency chain: the derive is on the critical path of the one-launch
+// exchange).  Lanes k = 0 and k = 1 of quad j also form pre_j and post_j.  r
+// points at the token's summed words (24 dots, sum x'^2).  Every lane of the
+// row calls it; the outputs are written if valid (pre/post/comb only if
+// pre_out).
+__device__ __forceinline__ void derive_16(const float* r, float rx, int j, int k, bool valid, int64_t t,
+                                          const float* hc_scale, const float* hc_base, int iters, float eps,
+                                          float* mixes_out, float* pre_out, float* post_out, float* comb_out) {
+  constexpr int HC = 4, MIX = 24;
+  const bool odd = k & 1;
+  const float mpq = r[odd ? HC + j : j] * rx;           // lane k = 0: pre mix j; k = 1: post mix j
+  const float mc = r[2 * HC + 4 * j + k] * rx;
+  if (valid && mixes_out) {
+    mixes_out[t * MIX + 2 * HC + 4 * j + k] = mc;
+    if (k < 2) mixes_out[t * MIX + k * HC + j] = mpq;
+  }
+  if (!pre_out) return;
+  const float u = odd ? mpq * hc_scale[1] + hc_base[HC + j] : mpq * hc_scale[0] + hc_base[j];
+  const float sg = sigmoidf_(u);
+  const float g = odd ? 2.0f * sg : sg + eps;           // post_j / pre_j
+  float a = mc * hc_scale[2] + hc_base[2 * HC + 4 * j + k];
+  float mx = fmaxf(a, quad_perm<0xB1>(a));
+  mx = fmaxf(mx, quad_perm<0x4E>(mx));
+  a = expf(a - mx);
+  a = a * __builtin_amdgcn_rcpf(quad_sum(a)) + eps;     // row softmax + eps
+  a = a * __builtin_amdgcn_rcpf(col_sum16(a) + eps);    // column step
+  for (int it = 1; it < iters; ++it) {
+    a = a * __builtin_amdgcn_rcpf(quad_sum(a) + eps);
+    a = a * __builtin_amdgcn_rcpf(col_sum16(a) + eps);
+  }
+  if (!valid) return;
+  if (k == 0) pre_out[t * HC + j] = g;
+  if (k == 1) post_out[t * HC + j] = g;
+  comb_out[t * HC * HC + 4 * j + k] = a;
+}
+
 // ====================================================== boundary: two kernels
 // Everything that derives mixes (hc_mixes, block entry, sublayer boundary)
 // can run as two ordinary launches; the boundary between them is the only
@@ -1411,7 +1463,7 @@ exchange_kernel(const StreamArgs a) {
   __shared__ u32x4 w_lds[2][2][kHC][kNT][64];          // weight tiles, double buffered (80 KB)
   __shared__ u32x4 a_lds[4][2][kHC][64];               // X' in A layout per row block (32 KB)
   __shared__ float red[4][2][16][32];                  // projection sums per (row block, step) (16 KB)
-  __shared__ float ssum[2][kTT];                       // sum x'^2, sum y^2 per token
+  __shared__ float ssum[kTT];                          // sum x'^2 per token
   __shared__ float tot[kTT / 4 * kXW];                 // the owned tokens' words, summed over the slices
   __shared__ f32x4 g_slice[YK * kCF / 4];              // gamma of the slice
   __shared__ u32 s_tag;
@@ -1493,16 +1545,28 @@ exchange_kernel(const StreamArgs a) {
 #pragma unroll
   for (int t = 0; t < kAcc; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   u32 ykeep[YK][4];                             // this lane's read row, chunk by chunk
+  u32 xlast[kHC][4];                            // X' of the last chunk, stored after the sums are published
+  auto store_x = [&](int c, const u32 (&xp)[kHC][4]) __attribute__((always_inline)) {
+    const unsigned f = fs + c * kCF + fl;
+    if (tv) {
+      hc_bf16* xob = a.x_out + (t0 + lt) * kHC * d;
+#pragma unroll
+      for (int j = 0; j < kHC; ++j)
+        st_stream(reinterpret_cast<u32x4*>(xob + (j * d + f)), u32x4{xp[j][0], xp[j][1], xp[j][2], xp[j][3]});
+    }
+  };
   auto stream_phase = [&](int c, const u32x4 (&src)[kHC + 1]) __attribute__((always_inline)) {
     const unsigned f = fs + c * kCF + fl;
     u32 xp[kHC][4];
     if constexpr (POST) {
       post_8(src, cpost, ccomb, xp);
-      if (tv) {
-        hc_bf16* xob = a.x_out + (t0 + lt) * kHC * d;
+      if (c + 1 < YK) {
+        store_x(c, xp);
+      } else {
 #pragma unroll
         for (int j = 0; j < kHC; ++j)
-          st_stream(reinterpret_cast<u32x4*>(xob + (j * d + f)), u32x4{xp[j][0], xp[j][1], xp[j][2], xp[j][3]});
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xlast[j][e] = xp[j][e];
       }
     } else {
 #pragma unroll
@@ -1605,36 +1669,38 @@ exchange_kernel(const StreamArgs a) {
     }(std::make_integer_sequence<int, YK>{});
   }
 
-  // ---- this slice's sums of every token of the tile, as tagged words
+  // ---- this slice's sums of every token of the tile, as tagged words: sum y^2
+  // (every slice of the tile waits for it) straight from the lanes, the rest
+  // through LDS, then the last chunk's X'
+  const u32 tag = s_tag;
+  u64* tilew = a.xw + (size_t)tile * S * kTT * kXW;
+  u64* mine = tilew + (size_t)slice * kTT * kXW;
 #pragma unroll
   for (int o = 1; o < 8; o <<= 1) {
     ssx += __shfl_xor(ssx, o);
     ssy += __shfl_xor(ssy, o);
   }
+  if ((lane & 7) == 0) put_word(mine + m * kXW + kMix + 1, tag_word(ssy, tag));
 #pragma unroll
   for (int t = 0; t < kAcc; ++t)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) red[rb][hw][4 * (lane >> 4) + rr][t * 16 + (lane & 15)] = acc[t][rr];
-  if ((lane & 7) == 0) {
-    ssum[0][m] = ssx;
-    ssum[1][m] = ssy;
-  }
+  if ((lane & 7) == 0) ssum[m] = ssx;
   lds_barrier();
-  const u32 tag = s_tag;
-  u64* tilew = a.xw + (size_t)tile * S * kTT * kXW;
-  u64* mine = tilew + (size_t)slice * kTT * kXW;
-  for (int idx = threadIdx.x; idx < kTT * kXW; idx += kThreads) {
-    const int tm = idx / kXW, q = idx % kXW;
+  for (int i = threadIdx.x; i < kTT * (kXW - 1); i += kThreads) {
+    const int tm = i / (kXW - 1), q = i % (kXW - 1);
+    const int idx = tm * kXW + q;
     float v;
     if (q < kMix) {
       const float* r0 = red[tm >> 4][0][tm & 15];
       const float* r1 = red[tm >> 4][1][tm & 15];
       v = q < 16 ? r0[q] + r1[q] : (r0[q] + r0[q + 8]) + (r1[q] + r1[q + 8]);
     } else {
-      v = ssum[q - kMix][tm];
+      v = ssum[tm];
     }
     put_word(mine + idx, tag_word(v, tag));
   }
+  if constexpr (POST) store_x(YK - 1, xlast);
   // ---- every word this workgroup waits for, in one round trip: sum y^2 of
   // this lane's token and, for the owned (token, word) pair of this thread,
   // that word, from every slice; each summed in slice order
@@ -1664,22 +1730,22 @@ exchange_kernel(const StreamArgs a) {
     }
   const float ry = 1.0f / sqrtf(ty / (float)d + a.rms_eps);
   __syncthreads();
-  if (threadIdx.x == 0) {   // every word of this call read: the last workgroup advances the epoch
-    const u64 before = __hip_atomic_fetch_add(a.ctl + kCtlXDone, (u64)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (before % (u64)gridDim.x == (u64)(gridDim.x - 1)) {
-      put_word(a.ctl + kCtlXDone, 0ull);
-      put_word(a.ctl + kCtlXEpoch, (u64)tag);
-    }
-  }
-  // ---- the owned tokens' mixes, pre/post and comb: 4 lanes per token (one wave)
-  if ((int)threadIdx.x < 4 * nown) {
-    const int k = threadIdx.x >> 2, j = threadIdx.x & 3;
+  // every word of this call read: count this workgroup done.  A thread of the
+  // last wave (no derive work) issues it, and awaits the count only at its end.
+  constexpr int kDoneThread = kThreads - 1;
+  u64 before = 0;
+  if (threadIdx.x == kDoneThread)
+    before = __hip_atomic_fetch_add(a.ctl + kCtlXDone, (u64)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // ---- the owned tokens' mixes, pre/post and comb: 16 lanes per token (up to
+  // four waves, which write their part of z after it, while the others' z stores
+  // drain)
+  if ((int)threadIdx.x < 16 * nown) {
+    const int k = threadIdx.x >> 4, q = threadIdx.x & 15;
     const int tm = slice + S * k;
     const float* r = &tot[k * kXW];
     const float rx = 1.0f / sqrtf(r[kMix] / (float)(kHC * d) + a.norm_eps);
-    const float dc[kHC] = {r[2 * kHC + 4 * j], r[2 * kHC + 4 * j + 1], r[2 * kHC + 4 * j + 2], r[2 * kHC + 4 * j + 3]};
-    derive_quad(r[j], r[kHC + j], dc, rx, j, t0 + tm < a.n, t0 + tm, a.hc_scale, a.hc_base, a.iters, a.hc_eps,
-                a.mixes_out, a.pre_out, a.post_out, a.comb_out);
+    derive_16(r, rx, q >> 2, q & 3, t0 + tm < a.n, t0 + tm, a.hc_scale, a.hc_base, a.iters, a.hc_eps,
+              a.mixes_out, a.pre_out, a.post_out, a.comb_out);
   }
   // ---- z = gamma * (y * r) from the kept read row
 #pragma unroll
@@ -1693,6 +1759,11 @@ exchange_kernel(const StreamArgs a) {
     for (int e2 = 0; e2 < 4; ++e2)
       zp[e2] = pack_bf16(gm[2 * e2] * (bf_lo(ykeep[c][e2]) * ry), gm[2 * e2 + 1] * (bf_hi(ykeep[c][e2]) * ry));
     if (tv) st_stream(reinterpret_cast<u32x4*>(a.y_out + (t0 + lt) * d + f), u32x4{zp[0], zp[1], zp[2], zp[3]});
+  }
+  // the last workgroup to count itself done advances the call epoch
+  if (threadIdx.x == kDoneThread && before % (u64)gridDim.x == (u64)(gridDim.x - 1)) {
+    put_word(a.ctl + kCtlXDone, 0ull);
+    put_word(a.ctl + kCtlXEpoch, (u64)tag);
   }
 }
 
