@@ -1,10 +1,13 @@
-"""GPU parity of the decode schedule: hc_boundary with a given pre (with and
+"""GPU parity of the decode schedules: hc_boundary with a given pre (with and
 without the RMSNorm of the read row), and hc_mixes, for n <= 128 run as one
-launch whose last-arriving feature slice of each token tile sums the slices'
-partial sums and derives the coefficients ("Source layer, pairs pooled":
-Block.forward at decode; "Reading weights"; with the RMSNorm every slice
-sums the slices' sum y^2 of its tokens and writes its part of z, "Final
-RMSNorm").  Checked against the oracle on ragged token counts and
+launch ("Source layer, pairs pooled": Block.forward at decode; "Reading
+weights"; "Final RMSNorm").  From d = 1024 to 8192 that is the few-token
+exchange (64-token tiles, one 64-feature chunk per workgroup; the owner slice
+of a token sums its words over the slices, derives its coefficients and, with
+the RMSNorm, publishes the token's factor r for the other slices); at other
+widths (multiples of 256) the decode kernel, whose last-arriving feature slice
+of each 16-token tile sums the slices' partial sums and derives the
+coefficients.  Checked against the oracle on ragged token counts and
 widths whose slice count spans one and two gather batches; on one workspace
 reused across calls of changing n and inputs (the tile epochs carried in the
 workspace); and captured in a graph with the decode block's other calls and
@@ -23,8 +26,14 @@ from transformer_hyper_connection_amd import synth
 pytestmark = pytest.mark.gpu
 
 
+# widths from 1024 to 8192 run the few-token schedule (one 64-feature chunk
+# per workgroup: S = d / 64 slices, an owner slice per token); 1088 and 1344
+# (17 and 21 slices) give a slice up to four owned tokens, 2112 (33) two; n =
+# 65 leaves one valid token in the second tile; 512 and 768 run the decode
+# kernel
 @pytest.mark.parametrize("n,d", [(1, 5120), (16, 5120), (17, 5120), (100, 5120), (128, 5120), (129, 5120),
-                                 (45, 7168), (70, 10240)])
+                                 (45, 7168), (70, 10240), (65, 1088), (128, 1344), (100, 2112), (3, 1024),
+                                 (20, 512), (128, 768)])
 @pytest.mark.parametrize("entry", [False, True])
 def test_decode_boundary(n, d, entry):
     say(f"[decode] n={n} d={d} entry={entry}")
@@ -32,9 +41,11 @@ def test_decode_boundary(n, d, entry):
     T._check_boundary(ref, got, s, False, False)
 
 
-# with the RMSNorm: every slice waits for the others' sum y^2 (d = 8192 at
-# n = 128 is 8 tiles x 32 slices = 256 workgroups, the most the schedule takes)
+# with the RMSNorm: each token's owner slice publishes its factor r for every
+# slice of the tile (d = 8192 at n = 128 is 2 tiles x 128 slices = 256
+# workgroups, the most the schedule takes)
 @pytest.mark.parametrize("n,d", [(1, 5120), (17, 5120), (128, 5120), (129, 5120), (45, 7168), (128, 8192),
+                                 (65, 1088), (128, 1344), (100, 2112), (3, 1024), (20, 512), (128, 768),
                                  (70, 10240)])
 @pytest.mark.parametrize("entry", [False, True])
 def test_decode_boundary_norm(n, d, entry):

@@ -108,19 +108,20 @@ def test_exchange_matches_two_launches():
 
 def test_exchange_repeated_calls_and_shared_workspace():
     """Calls on one workspace: each one-launch call advances the exchange's call
-    epoch by one and gives the same bits; decode, two-launch and other-width
-    calls in between leave it intact."""
+    epoch by one and gives the same bits; few-token (one-launch as well),
+    two-launch and other-width calls in between leave its results intact."""
     say("[exchange] repeated calls, shared workspace")
     s, kw, dev = _inputs(4096)
     x = dev.pop("x")
     ref = O.boundary(**kw)
     ws = torch.zeros(H.lib().hc_workspace_bytes(4096, 4, 5120), dtype=torch.uint8, device=DEV)
-    first, e0 = None, _epoch(ws)
+    first = None
     small, skw, sdev = _inputs(64)
     sx = sdev.pop("x")
     for rep in range(4):
+        e0 = _epoch(ws)
         got = H.hc_boundary(x, **dev, want_mixes=True, out={"workspace": ws})
-        assert _epoch(ws) == e0 + rep + 1
+        assert _epoch(ws) == e0 + 1
         cur = {k: host_bits(got[k]) if got[k].dtype == torch.bfloat16 else host_f32(got[k])
                for k in ("x_out", "y", "pre", "post", "comb", "mixes")}
         if first is None:
@@ -129,8 +130,8 @@ def test_exchange_repeated_calls_and_shared_workspace():
         else:
             for k in cur:
                 assert np.array_equal(cur[k], first[k]), f"call {rep}: {k} differs from call 0"
-        # other schedules on the same workspace: the decode schedule (n = 64, no RMSNorm),
-        # the two launches (fresh read) and another width
+        # other schedules on the same workspace: the few-token schedule (n = 64, no RMSNorm,
+        # advancing the same epoch), the two launches (fresh read) and another width
         g1 = H.hc_boundary(sx, **{**sdev, "gamma": None}, want_mixes=True, out={"workspace": ws})
         r1 = O.boundary(**{**skw, "gamma": None})
         _check_boundary(r1, g1, small, False, False)

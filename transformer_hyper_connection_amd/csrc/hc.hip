@@ -742,6 +742,30 @@ __device__ __forceinline__ float settle(const u64* p, u64 w, u32 tag, u32* err, 
   return __uint_as_float((u32)w);
 }
 
+// Batched form of settle for the words w[i] at ptr(i) with use(i): every
+// round checks all of them and reloads all the stale ones at once, so the wait
+// ends one round trip after the last of them became visible (polling them one
+// after another costs a round trip per stale word).  Gives up after
+// kPollLimit rounds like settle (dead, error mask).
+template <int N, typename P, typename U>
+__device__ __forceinline__ void settle_all(u64 (&w)[N], P ptr, U use, u32 tag, u32* err, bool& dead) {
+  for (unsigned polls = 0; !dead; ++polls) {
+    bool stale = false;
+#pragma unroll
+    for (int i = 0; i < N; ++i) stale |= use(i) && (u32)(w[i] >> 32) != tag;
+    if (!stale) break;
+    if (polls >= kPollLimit) {
+      atomicOr(err, kErrPollTimeout);
+      dead = true;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(8);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (use(i) && (u32)(w[i] >> 32) != tag) w[i] = get_word(ptr(i));
+  }
+}
+
 // The split and Sinkhorn of one token, 4 lanes (a quad) per token, lane j
 // holding pre_j, post_j and comb row j (column sums by DPP quad sums), from the
 // token's dots (summed in a fixed order) and its RMS factor rx ("Reading
@@ -1466,6 +1490,7 @@ exchange_kernel(const StreamArgs a) {
   __shared__ float ssum[kTT];                          // sum x'^2 per token
   __shared__ float tot[kTT / 4 * kXW];                 // the owned tokens' words, summed over the slices
   __shared__ f32x4 g_slice[YK * kCF / 4];              // gamma of the slice
+  __shared__ float s_cf[kMix + 3];                     // hc_base, hc_scale (read by the derive)
   __shared__ u32 s_tag;
 
   const int lane = threadIdx.x & 63;
@@ -1489,6 +1514,11 @@ exchange_kernel(const StreamArgs a) {
 
   if (threadIdx.x == 0) s_tag = (u32)get_word(a.ctl + kCtlXEpoch) + 1u;   // words carry epoch + 1
   if (threadIdx.x < YK * kCF / 4) g_slice[threadIdx.x] = reinterpret_cast<const f32x4*>(a.gamma + fs)[threadIdx.x];
+  // the split's parameters, requested now so that the derive does not wait for them
+  if (a.pre_out && threadIdx.x >= kThreads - (kMix + 3)) {
+    const int i = threadIdx.x - (kThreads - (kMix + 3));
+    s_cf[i] = i < kMix ? a.hc_base[i] : a.hc_scale[i - kMix];
+  }
 
   const int64_t t0 = (int64_t)tile * kTT;
   const bool tv = t0 + m < a.n;
@@ -1704,19 +1734,22 @@ exchange_kernel(const StreamArgs a) {
   // ---- every word this workgroup waits for, in one round trip: sum y^2 of
   // this lane's token and, for the owned (token, word) pair of this thread,
   // that word, from every slice; each summed in slice order
-  u64 wy[kXS], wr[kXS];
+  // words 0 .. kXS-1: sum y^2 of this lane's token; kXS ..: the owned pair
+  auto wptr = [&](int i) {
+    return i < kXS ? tilew + ((size_t)i * kTT + m) * kXW + kMix + 1 : tilew + ((size_t)(i - kXS) * kTT + ptm) * kXW + pq;
+  };
+  auto wuse = [&](int i) { return i < kXS ? i < S : has_pair && i - kXS < S; };
+  u64 wv[2 * kXS];
 #pragma unroll
-  for (int s2 = 0; s2 < kXS; ++s2) {
-    wy[s2] = s2 < S ? get_word(tilew + ((size_t)s2 * kTT + m) * kXW + kMix + 1) : 0ull;
-    wr[s2] = s2 < S && has_pair ? get_word(tilew + ((size_t)s2 * kTT + ptm) * kXW + pq) : 0ull;
-  }
+  for (int i = 0; i < 2 * kXS; ++i) wv[i] = wuse(i) ? get_word(wptr(i)) : 0ull;
   bool dead = false;
+  settle_all(wv, wptr, wuse, tag, a.err, dead);
   if (has_pair) {
     float tr = 0.f;
 #pragma unroll
     for (int s2 = 0; s2 < kXS; ++s2)
       if (s2 < S) {
-        const float v = settle(tilew + ((size_t)s2 * kTT + ptm) * kXW + pq, wr[s2], tag, a.err, dead);
+        const float v = __uint_as_float((u32)wv[kXS + s2]);
         tr = s2 == 0 ? v : tr + v;
       }
     tot[pr] = tr;
@@ -1725,7 +1758,7 @@ exchange_kernel(const StreamArgs a) {
 #pragma unroll
   for (int s2 = 0; s2 < kXS; ++s2)
     if (s2 < S) {
-      const float v = settle(tilew + ((size_t)s2 * kTT + m) * kXW + kMix + 1, wy[s2], tag, a.err, dead);
+      const float v = __uint_as_float((u32)wv[s2]);
       ty = s2 == 0 ? v : ty + v;
     }
   const float ry = 1.0f / sqrtf(ty / (float)d + a.rms_eps);
@@ -1744,7 +1777,7 @@ exchange_kernel(const StreamArgs a) {
     const int tm = slice + S * k;
     const float* r = &tot[k * kXW];
     const float rx = 1.0f / sqrtf(r[kMix] / (float)(kHC * d) + a.norm_eps);
-    derive_16(r, rx, q >> 2, q & 3, t0 + tm < a.n, t0 + tm, a.hc_scale, a.hc_base, a.iters, a.hc_eps,
+    derive_16(r, rx, q >> 2, q & 3, t0 + tm < a.n, t0 + tm, s_cf + kMix, s_cf, a.iters, a.hc_eps,
               a.mixes_out, a.pre_out, a.post_out, a.comb_out);
   }
   // ---- z = gamma * (y * r) from the kept read row
@@ -1764,6 +1797,260 @@ exchange_kernel(const StreamArgs a) {
   if (threadIdx.x == kDoneThread && before % (u64)gridDim.x == (u64)(gridDim.x - 1)) {
     put_word(a.ctl + kCtlXDone, 0ull);
     put_word(a.ctl + kCtlXEpoch, (u64)tag);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// xdec_kernel: the boundary for few tokens (decode: n <= 128) in one launch,
+// the read-row exchange taken to one chunk per workgroup ("Source layer, pairs
+// pooled", Block.forward; "Final RMSNorm"; "Reading weights" for the split).
+// A workgroup owns (64-token tile, one 64-feature chunk of every stream): S =
+// d / 64 slices per tile, at most two tiles, so the packed weight is read once
+// per tile.  The streaming, the matrix-core projection and the per-token words
+// (24 dots, sum x'^2, with the RMSNorm sum y^2) are those of exchange_kernel
+// for one chunk.  The owner slice of a token (token m with m % S == slice)
+// sums each of the token's words over the slices in G interleaved groups
+// (slices g, g + G, ...) and then the G group sums in order, derives the
+// mixes, pre/post and comb with 16 lanes (derive_16) and, with the RMSNorm,
+// publishes the token's factor r = rsqrt(mean y^2 + eps) as one more tagged
+// word; every slice then scales its part of the read row by the r of its
+// tokens (two hops, but a slice reads 64 words instead of 64 x S).  Without
+// the RMSNorm the read row is stored as it is formed, and without a read
+// (READ false: the mixes alone) there is none.  Tokens of a tile past n take no
+// part in the exchange.  Every workgroup of a call must be resident at once
+// (at most 256, one per compute unit); a wait that times out sets the error
+// mask instead of hanging.
+constexpr int kXDMaxN = 128;                 // tokens at most on this schedule
+constexpr int kXDMinD = 1024, kXDMaxD = 8192;   // S = d / 64 from 16 to 128 slices
+constexpr int kXDGroups = 20;                // partial sums per owned word at most
+constexpr int kXDOLoads = 8;                 // owned words per thread at most (S <= 8 G for every S)
+constexpr int kCtlXdR = 64;                  // u64 index: the RMS factor words [kXDMaxN] (tile-major)
+static_assert(kCtlXdR + kXDMaxN <= kErrWord / 2, "the RMS factor words fit below the error mask");
+
+template <bool POST, bool MEAN, bool READ, bool NORM>
+__global__ void __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 2)))
+xdec_kernel(const StreamArgs a) {
+  static_assert(!NORM || READ, "the RMSNorm is of the read row");
+  constexpr int kOW = NORM ? kXW : kXW - 1;             // owned words per token: 24 dots, sum x'^2 (, sum y^2)
+  __shared__ u32x4 w_lds[2][kHC][kNT][64];             // the chunk's weight tiles (40 KB)
+  __shared__ u32x4 a_lds[4][2][kHC][64];               // X' in A layout per row block (32 KB)
+  __shared__ float red[4][2][16][32];                  // projection sums per (row block, step) (16 KB)
+  __shared__ float ssum[2][kTT];                       // sum x'^2, sum y^2 per token
+  __shared__ float part[4][kXW][kXDGroups];            // owned words: group sums
+  __shared__ float tot[4][kXW];                        // owned words summed over the slices
+  __shared__ float s_cf[kMix + 3];                     // hc_base, hc_scale (read by the derive)
+  __shared__ u32 s_tag;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rb = wave >> 1, hw = wave & 1;
+  const int d = a.d, S = a.S;
+  // XCD-aware: renumbered so that each XCD holds a contiguous run, slice-major
+  // (the tiles of a slice share its weight tiles in one L2)
+  const int lin = (gridDim.x & 7) ? blockIdx.x : (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int slice = lin / a.tiles, tile = lin % a.tiles;
+  const int fs = slice * kCF;
+  const int hl = lane >> 3, fl = (lane & 7) * 8;
+  const int m = rb * 16 + hw * 8 + hl;                 // token within the tile
+  const int a_st = fl >> 5, a_g = (fl >> 3) & 3;
+  const int a_lane = a_g * 16 + hw * 8 + hl;
+
+  if (threadIdx.x == 0) s_tag = (u32)get_word(a.ctl + kCtlXEpoch) + 1u;   // words carry epoch + 1
+  // the split's parameters, requested now so that the derive does not wait for them
+  if (a.pre_out && threadIdx.x >= kThreads - (kMix + 3)) {
+    const int i = threadIdx.x - (kThreads - (kMix + 3));
+    s_cf[i] = i < kMix ? a.hc_base[i] : a.hc_scale[i - kMix];
+  }
+  const int64_t t0 = (int64_t)tile * kTT;
+  const int nval = (int)min<int64_t>(kTT, a.n - t0);  // valid tokens of the tile
+  const bool tv = m < nval;
+  const unsigned lt = tv ? (unsigned)m : 0u;           // a token past n reads the tile's first token
+  // the chunk's 2 x 4 x 5 weight tiles, 5 per wave, then the streams
+  const int gstep = fs / kStepF;
+  u32x4 wst[kNT];
+#pragma unroll
+  for (int i = 0; i < kNT; ++i) {
+    const int blk = wave + i * kWaves;
+    const int st = blk / (kHC * kNT), kk = (blk / kNT) % kHC, nt = blk % kNT;
+    wst[i] = a.fn[((size_t)((gstep + st) * kHC + kk) * kNT + nt) * 64 + lane];
+  }
+  const hc_bf16* xr = a.x + (t0 + lt) * a.xtok + fs + fl;
+  u32x4 src[kHC + 1];
+#pragma unroll
+  for (int j = 0; j < kHC; ++j) src[j] = ld_stream(reinterpret_cast<const u32x4*>(xr + j * a.xstr));
+  src[kHC] = POST ? ld_stream(reinterpret_cast<const u32x4*>(a.delta + (t0 + lt) * d + fs + fl))
+                  : u32x4{0u, 0u, 0u, 0u};
+  float cpost[kHC], ccomb[kHC * kHC], cpre[kHC];
+#pragma unroll
+  for (int j = 0; j < kHC; ++j) {
+    cpost[j] = POST ? a.post_in[(t0 + lt) * kHC + j] : 0.f;
+    cpre[j] = READ ? a.pre_in[(t0 + lt) * kHC + j] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < kHC * kHC; ++j) ccomb[j] = POST ? a.comb_in[(t0 + lt) * kHC * kHC + j] : 0.f;
+  float gm[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) gm[e] = NORM ? a.gamma[fs + fl + e] : 0.f;
+#pragma unroll
+  for (int i = 0; i < kNT; ++i) {
+    const int blk = wave + i * kWaves;
+    w_lds[blk / (kHC * kNT)][(blk / kNT) % kHC][blk % kNT][lane] = wst[i];
+  }
+
+  // ---- the chunk: X' (stored), its A tile, sum x'^2, the read row and sum y^2
+  u32 xp[kHC][4];
+  if constexpr (POST) {
+    post_8(src, cpost, ccomb, xp);
+    if (tv) {
+      hc_bf16* xob = a.x_out + (t0 + lt) * kHC * d + fs + fl;
+#pragma unroll
+      for (int j = 0; j < kHC; ++j)
+        st_stream(reinterpret_cast<u32x4*>(xob + j * d), u32x4{xp[j][0], xp[j][1], xp[j][2], xp[j][3]});
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kHC; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xp[j][e] = src[j][e];
+  }
+  if constexpr (MEAN) {
+    if (tv) st_stream(reinterpret_cast<u32x4*>(a.x_mean + (t0 + lt) * d + fs + fl), mean_8(xp));
+  }
+  float ssx = 0.f, ssy = 0.f;
+#pragma unroll
+  for (int j = 0; j < kHC; ++j) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ssx = dot2_bf16(xp[j][e], xp[j][e], ssx);
+    a_lds[rb][a_st][j][a_swz(a_lane, a_st)] = u32x4{xp[j][0], xp[j][1], xp[j][2], xp[j][3]};
+  }
+  u32 yp[4] = {0u, 0u, 0u, 0u};
+  if constexpr (READ) {
+    pre_8(xp, cpre, yp);
+    if constexpr (NORM) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ssy = dot2_bf16(yp[e], yp[e], ssy);
+    } else if (tv) {
+      st_stream(reinterpret_cast<u32x4*>(a.y_out + (t0 + lt) * d + fs + fl), u32x4{yp[0], yp[1], yp[2], yp[3]});
+    }
+  }
+  lds_barrier();
+  f32x4 acc[kAcc];
+#pragma unroll
+  for (int t = 0; t < kAcc; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kHC; ++j) {
+    const bf16x8 A = __builtin_bit_cast(bf16x8, a_lds[rb][hw][j][a_swz(lane, hw)]);
+    bf16x8 B[kNT];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) B[nt] = __builtin_bit_cast(bf16x8, w_lds[hw][j][nt][lane]);
+    mfma_step(A, B, acc);
+  }
+
+  // ---- the words of the valid tokens, through LDS
+  const u32 tag = s_tag;
+  u64* tilew = a.xw + (size_t)tile * S * kTT * kXW;
+  u64* mine = tilew + (size_t)slice * kTT * kXW;
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+    ssx += __shfl_xor(ssx, o);
+    if constexpr (NORM) ssy += __shfl_xor(ssy, o);
+  }
+#pragma unroll
+  for (int t = 0; t < kAcc; ++t)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) red[rb][hw][4 * (lane >> 4) + rr][t * 16 + (lane & 15)] = acc[t][rr];
+  if ((lane & 7) == 0) {
+    ssum[0][m] = ssx;
+    ssum[1][m] = ssy;
+  }
+  lds_barrier();
+  for (int i = threadIdx.x; i < nval * kOW; i += kThreads) {
+    const int tm = i / kOW, q = i % kOW;
+    float v;
+    if (q < kMix) {
+      const float* r0 = red[tm >> 4][0][tm & 15];
+      const float* r1 = red[tm >> 4][1][tm & 15];
+      v = q < 16 ? r0[q] + r1[q] : (r0[q] + r0[q + 8]) + (r1[q] + r1[q + 8]);
+    } else {
+      v = ssum[q - kMix][tm];
+    }
+    put_word(mine + tm * kXW + q, tag_word(v, tag));
+  }
+
+  // ---- the owned tokens' words from every slice, in one round trip
+  const int nown = slice < nval ? (nval - 1 - slice) / S + 1 : 0;   // owned tokens slice, slice + S, ...
+  const int npairs = nown * kOW;
+  const int G = npairs ? min(kXDGroups, kThreads / npairs) : 1;
+  const bool has_o = (int)threadIdx.x < npairs * G;
+  const int opr = has_o ? threadIdx.x / G : 0, og = has_o ? threadIdx.x % G : 0;
+  const int ok = opr / kOW, oq = opr % kOW;
+  const int otm = slice + S * ok;
+  auto wptr = [&](int i) { return tilew + ((size_t)(og + G * i) * kTT + otm) * kXW + oq; };
+  auto wuse = [&](int i) { return has_o && og + G * i < S; };
+  u64 wv[kXDOLoads];
+#pragma unroll
+  for (int i = 0; i < kXDOLoads; ++i) wv[i] = wuse(i) ? get_word(wptr(i)) : 0ull;
+  bool dead = false;
+  settle_all(wv, wptr, wuse, tag, a.err, dead);
+  if (has_o) {
+    float po = 0.f;
+#pragma unroll
+    for (int i = 0; i < kXDOLoads; ++i)
+      if (og + G * i < S) {
+        const float v = __uint_as_float((u32)wv[i]);
+        po = i == 0 ? v : po + v;
+      }
+    part[ok][oq][og] = po;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < npairs) {
+    const int k = threadIdx.x / kOW, q = threadIdx.x % kOW;
+    float v = part[k][q][0];
+    for (int g = 1; g < G; ++g) v += part[k][q][g];
+    tot[k][q] = v;
+  }
+  __syncthreads();
+  // every word of this call read but the factors: count this workgroup done
+  // (a thread of the last wave, awaited at its end; the factor words are
+  // read before the count can complete, see below)
+  constexpr int kDoneThread = kThreads - 1;
+  u64* rword = a.ctl + kCtlXdR + t0;
+  if constexpr (NORM) {   // the owned tokens' factors, for every slice of the tile
+    if ((int)threadIdx.x < nown) {
+      const int tm = slice + S * threadIdx.x;
+      put_word(rword + tm, tag_word(1.0f / sqrtf(tot[threadIdx.x][kXW - 1] / (float)d + a.rms_eps), tag));
+    }
+  }
+  // ---- the owned tokens' mixes, pre/post and comb: 16 lanes per token
+  if ((int)threadIdx.x < 16 * nown) {
+    const int k = threadIdx.x >> 4, q = threadIdx.x & 15;
+    const int tm = slice + S * k;
+    const float* r = tot[k];
+    const float rx = 1.0f / sqrtf(r[kMix] / (float)(kHC * d) + a.norm_eps);
+    derive_16(r, rx, q >> 2, q & 3, true, t0 + tm, s_cf + kMix, s_cf, a.iters, a.hc_eps,
+              a.mixes_out, a.pre_out, a.post_out, a.comb_out);
+  }
+  // ---- z = gamma * (y * r) for the chunk, r from the token's owner
+  if constexpr (NORM) {
+    u64 rv[1] = {tv ? get_word(rword + m) : 0ull};
+    settle_all(rv, [&](int) { return rword + m; }, [&](int) { return tv; }, tag, a.err, dead);
+    if (tv) {
+      const float ry = __uint_as_float((u32)rv[0]);
+      u32 zp[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2)
+        zp[e2] = pack_bf16(gm[2 * e2] * (bf_lo(yp[e2]) * ry), gm[2 * e2 + 1] * (bf_hi(yp[e2]) * ry));
+      st_stream(reinterpret_cast<u32x4*>(a.y_out + (t0 + lt) * d + fs + fl), u32x4{zp[0], zp[1], zp[2], zp[3]});
+    }
+    __syncthreads();   // every factor word of this workgroup read before it counts itself done
+  }
+  // the last workgroup to count itself done advances the call epoch
+  if (threadIdx.x == kDoneThread) {
+    const u64 before = __hip_atomic_fetch_add(a.ctl + kCtlXDone, (u64)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (before % (u64)gridDim.x == (u64)(gridDim.x - 1)) {
+      put_word(a.ctl + kCtlXDone, 0ull);
+      put_word(a.ctl + kCtlXEpoch, (u64)tag);
+    }
   }
 }
 
@@ -2537,6 +2824,16 @@ hipError_t launch_exchange_t(const StreamArgs& a, unsigned grid, hipStream_t st)
   }
   return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, st);
 }
+// the given-pre boundary with the RMSNorm for few tokens: one chunk per workgroup
+template <bool POST, bool READ, bool NORM>
+hipError_t launch_xdec_t(const StreamArgs& a, unsigned grid, hipStream_t st) {
+  StreamArgs copy = a;
+  void* args[] = {&copy};
+  const void* fn = a.x_mean ? reinterpret_cast<const void*>(&xdec_kernel<POST, true, READ, NORM>)
+                            : reinterpret_cast<const void*>(&xdec_kernel<POST, false, READ, NORM>);
+  return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, st);
+}
+bool xdec_shape(int64_t n, int d) { return n <= kXDMaxN && d % kCF == 0 && d >= kXDMinD && d <= kXDMaxD; }
 // The read-row exchange: slices of 10 or 20 chunks (640 or 1280 features), 4
 // to kXS slices per tile (the owned (token, word) pairs of a workgroup fit its
 // threads), and every workgroup resident at once (at most 256, one per
@@ -2579,6 +2876,24 @@ int launch_boundary(bool post, int rm, bool norm, StreamArgs s, FinishArgs f, vo
   s.rec = reinterpret_cast<float*>(static_cast<char*>(ws) + kRecOffset);
   const unsigned grid1 = (unsigned)(tiles * s.S);
   hipError_t e = hipSuccess;
+  if (exchange && phases == 3 && rm != kFreshPre && xdec_shape(s.n, s.d)) {
+    // few tokens: one 64-feature chunk per workgroup, the tile's slices exchanging their words
+    s.S = s.d / kCF;
+    s.F = kCF;
+    s.ctl = static_cast<u64*>(ws);
+    s.xw = reinterpret_cast<u64*>(static_cast<char*>(ws) + kXOffset);
+    s.err = static_cast<u32*>(ws) + kErrWord;
+    s.gamma = f.gamma; s.hc_base = f.hc_base; s.hc_scale = f.hc_scale; s.mixes_out = f.mixes_out;
+    s.pre_out = f.pre_out; s.post_out = f.post_out; s.comb_out = f.comb_out; s.iters = f.iters;
+    s.hc_eps = f.hc_eps; s.norm_eps = f.norm_eps; s.rms_eps = f.rms_eps;
+    static_assert((size_t)(kXDMaxN / kTT) * (kXDMaxD / kCF) * kTT * kXW * sizeof(u64) <= kXRegionBytes,
+                  "the few-token exchange's words fit the exchange region");
+    const unsigned grid = (unsigned)(tiles * s.S);
+    if (rm == kNoRead) e = launch_xdec_t<false, false, false>(s, grid, st);
+    else if (post) e = norm ? launch_xdec_t<true, true, true>(s, grid, st) : launch_xdec_t<true, true, false>(s, grid, st);
+    else e = norm ? launch_xdec_t<false, true, true>(s, grid, st) : launch_xdec_t<false, true, false>(s, grid, st);
+    return launched(e, what);
+  }
   const int xs = exchange && phases == 3 && rm == kGivenPre && norm ? exchange_slices(s.n, s.d) : 0;
   if (xs) {
     const int yk = s.d / kCF / xs;
@@ -2886,7 +3201,7 @@ int hc_mixes(const hc_bf16* x, const void* fn_packed, int64_t n, int hc, int d, 
     if (split) { f.pre_out = pre; f.post_out = post; f.comb_out = comb; }
     return launch_mixes_generic(hc, x, hc * d, d, fn_packed, n, d, workspace, f, st, "hc_mixes");
   }
-  if (decode_shape(n, d)) {
+  if (decode_shape(n, d) && !xdec_shape(n, d)) {
     DecArgs a{};
     a.n = n; a.d = d; a.x = x; a.fn = reinterpret_cast<const u32x4*>(fn_packed); a.mixes_out = mixes;
     a.xtok = kHC * d; a.xstr = d;
@@ -2901,7 +3216,8 @@ int hc_mixes(const hc_bf16* x, const void* fn_packed, int64_t n, int hc, int d, 
   f.mixes_out = mixes; f.norm_eps = norm_eps; f.hc_scale = hc_scale; f.hc_base = hc_base; f.iters = iters;
   f.hc_eps = hc_eps;
   if (split) { f.pre_out = pre; f.post_out = post; f.comb_out = comb; }
-  return launch_boundary(false, kNoRead, false, s, f, workspace, workspace_bytes, (hipStream_t)stream, "hc_mixes");
+  return launch_boundary(false, kNoRead, false, s, f, workspace, workspace_bytes, (hipStream_t)stream, "hc_mixes", 3,
+                         xdec_shape(n, d));
 }
 
 int hc_pre(const hc_bf16* x, const float* pre_mix, int64_t n, int hc, int d, hc_bf16* y, void* stream) {
@@ -3096,7 +3412,7 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
     }
     return HC_OK;
   }
-  if (phases == 3 && !two && !fresh && decode_shape(p->n, p->d)) {
+  if (phases == 3 && !two && !fresh && decode_shape(p->n, p->d) && !xdec_shape(p->n, p->d)) {
     DecArgs a{};
     a.n = p->n; a.d = p->d; a.x = p->x; a.delta = p->delta; a.post_in = p->post_in; a.comb_in = p->comb_in;
     a.pre_in = p->pre_in; a.fn = reinterpret_cast<const u32x4*>(p->fn_packed); a.hc_base = p->hc_base;
