@@ -1801,61 +1801,64 @@ exchange_kernel(const StreamArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// xdec_kernel: the boundary for few tokens (decode: n <= 128) in one launch,
-// the read-row exchange taken to one chunk per workgroup ("Source layer, pairs
-// pooled", Block.forward; "Final RMSNorm"; "Reading weights" for the split).
-// A workgroup owns (64-token tile, one 64-feature chunk of every stream): S =
-// d / 64 slices per tile, at most two tiles, so the packed weight is read once
-// per tile.  The streaming, the matrix-core projection and the per-token words
-// (24 dots, sum x'^2, with the RMSNorm sum y^2) are those of exchange_kernel
-// for one chunk.  The owner slice of a token (token m with m % S == slice)
-// sums each of the token's words over the slices in G interleaved groups
-// (slices g, g + G, ...) and then the G group sums in order, derives the
-// mixes, pre/post and comb with 16 lanes (derive_16) and, with the RMSNorm,
-// publishes the token's factor r = rsqrt(mean y^2 + eps) as one more tagged
-// word; every slice then scales its part of the read row by the r of its
-// tokens (two hops, but a slice reads 64 words instead of 64 x S).  Without
-// the RMSNorm the read row is stored as it is formed, and without a read
-// (READ false: the mixes alone) there is none.  Tokens of a tile past n take no
-// part in the exchange.  Every workgroup of a call must be resident at once
-// (at most 256, one per compute unit); a wait that times out sets the error
-// mask instead of hanging.
-constexpr int kXDMaxN = 128;                 // tokens at most on this schedule
-constexpr int kXDMinD = 1024, kXDMaxD = 8192;   // S = d / 64 from 16 to 128 slices
-constexpr int kXDGroups = 20;                // partial sums per owned word at most
-constexpr int kXDOLoads = 8;                 // owned words per thread at most (S <= 8 G for every S)
-constexpr int kCtlXdR = 64;                  // u64 index: the RMS factor words [kXDMaxN] (tile-major)
-static_assert(kCtlXdR + kXDMaxN <= kErrWord / 2, "the RMS factor words fit below the error mask");
+// xfew_kernel: the boundary for few token tiles (decode, short prefill) in one
+// launch ("Source layer, pairs pooled", Block.forward; "Final RMSNorm";
+// "Reading weights" for the split).  A workgroup owns (64-token tile, slice of
+// YK 64-feature chunks of every stream), with YK from 1 up so small that the
+// tiles x slices workgroups fill the compute units (S = d / 64 / YK slices per
+// tile, at least 8).  Per chunk the streaming and the matrix-core projection
+// are those of exchange_kernel (X' stored, the read row kept in registers).
+// The owner slice of a token (token m with m % S == slice) sums each of the
+// token's words (24 dots, sum x'^2, with the RMSNorm sum y^2) over the slices
+// in G interleaved groups (slices g, g + G, ...) and then the G group sums in
+// order, derives its mixes, pre/post and comb with 16 lanes (derive_16) and,
+// with the RMSNorm, publishes the token's factor r = rsqrt(mean y^2 + eps) as
+// one more tagged word (in the slot of its own sum y^2 word of the token,
+// which only it reads, with the complement of the call's tag); every slice
+// then scales its part of the read row by the r of its tokens (two hops, but
+// a slice reads 64 words instead of 64 x S).  Without the RMSNorm the read row is stored as it is formed, and without
+// a read (READ false: the mixes alone) there is none.  Tokens of a tile past n
+// take no part in the exchange.  Every workgroup of a call must be resident
+// at once (at most 256, one per compute unit); a wait that times out sets the
+// error mask instead of hanging.
+constexpr int kXFMinD = 1024, kXFMaxD = 8192;   // widths of the schedule
+constexpr int kXFMinS = 8;                   // slices per tile at least
+constexpr int kXFMaxOwn = kTT / kXFMinS;     // owned tokens per slice at most (8)
+constexpr int kXFGroups = 20;                // partial sums per owned word at most
+constexpr int kXFOLoads = 8;                 // owned words per thread at most (S <= 8 G for every S)
+constexpr int kXFMixesMaxN = 128;            // hc_mixes takes the schedule up to this many tokens
 
-template <bool POST, bool MEAN, bool READ, bool NORM>
+template <bool POST, bool MEAN, bool READ, bool NORM, int YK>
 __global__ void __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 2)))
-xdec_kernel(const StreamArgs a) {
+xfew_kernel(const StreamArgs a) {
   static_assert(!NORM || READ, "the RMSNorm is of the read row");
   constexpr int kOW = NORM ? kXW : kXW - 1;             // owned words per token: 24 dots, sum x'^2 (, sum y^2)
-  __shared__ u32x4 w_lds[2][kHC][kNT][64];             // the chunk's weight tiles (40 KB)
+  __shared__ u32x4 w_lds[2][2][kHC][kNT][64];          // weight tiles, double buffered (80 KB)
   __shared__ u32x4 a_lds[4][2][kHC][64];               // X' in A layout per row block (32 KB)
   __shared__ float red[4][2][16][32];                  // projection sums per (row block, step) (16 KB)
   __shared__ float ssum[2][kTT];                       // sum x'^2, sum y^2 per token
-  __shared__ float part[4][kXW][kXDGroups];            // owned words: group sums
-  __shared__ float tot[4][kXW];                        // owned words summed over the slices
+  __shared__ float part[kXFMaxOwn][kXW][kXFGroups];    // owned words: group sums (16.6 KB)
+  __shared__ float tot[kXFMaxOwn][kXW];                // owned words summed over the slices
+  __shared__ f32x4 g_slice[NORM ? YK * kCF / 4 : 1];   // gamma of the slice
   __shared__ float s_cf[kMix + 3];                     // hc_base, hc_scale (read by the derive)
   __shared__ u32 s_tag;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rb = wave >> 1, hw = wave & 1;
+  const int rb = wave >> 1, hw = wave & 1;   // row block, half (stream phase) / step (matrix phase)
   const int d = a.d, S = a.S;
   // XCD-aware: renumbered so that each XCD holds a contiguous run, slice-major
   // (the tiles of a slice share its weight tiles in one L2)
   const int lin = (gridDim.x & 7) ? blockIdx.x : (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
   const int slice = lin / a.tiles, tile = lin % a.tiles;
-  const int fs = slice * kCF;
+  const int fs = slice * (YK * kCF);
   const int hl = lane >> 3, fl = (lane & 7) * 8;
   const int m = rb * 16 + hw * 8 + hl;                 // token within the tile
   const int a_st = fl >> 5, a_g = (fl >> 3) & 3;
   const int a_lane = a_g * 16 + hw * 8 + hl;
 
   if (threadIdx.x == 0) s_tag = (u32)get_word(a.ctl + kCtlXEpoch) + 1u;   // words carry epoch + 1
+  if (NORM && threadIdx.x < YK * kCF / 4) g_slice[threadIdx.x] = reinterpret_cast<const f32x4*>(a.gamma + fs)[threadIdx.x];
   // the split's parameters, requested now so that the derive does not wait for them
   if (a.pre_out && threadIdx.x >= kThreads - (kMix + 3)) {
     const int i = threadIdx.x - (kThreads - (kMix + 3));
@@ -1865,21 +1868,7 @@ xdec_kernel(const StreamArgs a) {
   const int nval = (int)min<int64_t>(kTT, a.n - t0);  // valid tokens of the tile
   const bool tv = m < nval;
   const unsigned lt = tv ? (unsigned)m : 0u;           // a token past n reads the tile's first token
-  // the chunk's 2 x 4 x 5 weight tiles, 5 per wave, then the streams
-  const int gstep = fs / kStepF;
-  u32x4 wst[kNT];
-#pragma unroll
-  for (int i = 0; i < kNT; ++i) {
-    const int blk = wave + i * kWaves;
-    const int st = blk / (kHC * kNT), kk = (blk / kNT) % kHC, nt = blk % kNT;
-    wst[i] = a.fn[((size_t)((gstep + st) * kHC + kk) * kNT + nt) * 64 + lane];
-  }
-  const hc_bf16* xr = a.x + (t0 + lt) * a.xtok + fs + fl;
-  u32x4 src[kHC + 1];
-#pragma unroll
-  for (int j = 0; j < kHC; ++j) src[j] = ld_stream(reinterpret_cast<const u32x4*>(xr + j * a.xstr));
-  src[kHC] = POST ? ld_stream(reinterpret_cast<const u32x4*>(a.delta + (t0 + lt) * d + fs + fl))
-                  : u32x4{0u, 0u, 0u, 0u};
+  const hc_bf16* xb = a.x + t0 * a.xtok;
   float cpost[kHC], ccomb[kHC * kHC], cpre[kHC];
 #pragma unroll
   for (int j = 0; j < kHC; ++j) {
@@ -1888,62 +1877,115 @@ xdec_kernel(const StreamArgs a) {
   }
 #pragma unroll
   for (int j = 0; j < kHC * kHC; ++j) ccomb[j] = POST ? a.comb_in[(t0 + lt) * kHC * kHC + j] : 0.f;
-  float gm[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) gm[e] = NORM ? a.gamma[fs + fl + e] : 0.f;
-#pragma unroll
-  for (int i = 0; i < kNT; ++i) {
-    const int blk = wave + i * kWaves;
-    w_lds[blk / (kHC * kNT)][(blk / kNT) % kHC][blk % kNT][lane] = wst[i];
-  }
 
-  // ---- the chunk: X' (stored), its A tile, sum x'^2, the read row and sum y^2
-  u32 xp[kHC][4];
-  if constexpr (POST) {
-    post_8(src, cpost, ccomb, xp);
-    if (tv) {
-      hc_bf16* xob = a.x_out + (t0 + lt) * kHC * d + fs + fl;
+  // the chunk's 2 x 4 x 5 weight tiles, 5 per wave
+  auto load_wst = [&](int c, u32x4 (&dst)[kNT]) __attribute__((always_inline)) {
+    const int gstep = (fs + c * kCF) / kStepF;
 #pragma unroll
-      for (int j = 0; j < kHC; ++j)
-        st_stream(reinterpret_cast<u32x4*>(xob + j * d), u32x4{xp[j][0], xp[j][1], xp[j][2], xp[j][3]});
+    for (int i = 0; i < kNT; ++i) {
+      const int blk = wave + i * kWaves;
+      const int st = blk / (kHC * kNT), kk = (blk / kNT) % kHC, nt = blk % kNT;
+      dst[i] = a.fn[((size_t)((gstep + st) * kHC + kk) * kNT + nt) * 64 + lane];
     }
-  } else {
+  };
+  auto store_wst = [&](int buf, const u32x4 (&src)[kNT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kNT; ++i) {
+      const int blk = wave + i * kWaves;
+      w_lds[buf][blk / (kHC * kNT)][(blk / kNT) % kHC][blk % kNT][lane] = src[i];
+    }
+  };
+  auto load_stream = [&](int c, u32x4 (&dst)[kHC + 1]) __attribute__((always_inline)) {
+    const unsigned f = fs + c * kCF + fl;
 #pragma unroll
     for (int j = 0; j < kHC; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) xp[j][e] = src[j][e];
-  }
-  if constexpr (MEAN) {
-    if (tv) st_stream(reinterpret_cast<u32x4*>(a.x_mean + (t0 + lt) * d + fs + fl), mean_8(xp));
-  }
+      dst[j] = ld_stream(reinterpret_cast<const u32x4*>(xb + (lt * (unsigned)a.xtok + j * (unsigned)a.xstr + f)));
+    dst[kHC] = POST ? ld_stream(reinterpret_cast<const u32x4*>(a.delta + (t0 + lt) * d + f)) : u32x4{0u, 0u, 0u, 0u};
+  };
   float ssx = 0.f, ssy = 0.f;
-#pragma unroll
-  for (int j = 0; j < kHC; ++j) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ssx = dot2_bf16(xp[j][e], xp[j][e], ssx);
-    a_lds[rb][a_st][j][a_swz(a_lane, a_st)] = u32x4{xp[j][0], xp[j][1], xp[j][2], xp[j][3]};
-  }
-  u32 yp[4] = {0u, 0u, 0u, 0u};
-  if constexpr (READ) {
-    pre_8(xp, cpre, yp);
-    if constexpr (NORM) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ssy = dot2_bf16(yp[e], yp[e], ssy);
-    } else if (tv) {
-      st_stream(reinterpret_cast<u32x4*>(a.y_out + (t0 + lt) * d + fs + fl), u32x4{yp[0], yp[1], yp[2], yp[3]});
-    }
-  }
-  lds_barrier();
   f32x4 acc[kAcc];
 #pragma unroll
   for (int t = 0; t < kAcc; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32 ykeep[NORM ? YK : 1][4];                         // the read row, chunk by chunk (RMSNorm)
+  auto stream_phase = [&](int c, const u32x4 (&src)[kHC + 1]) __attribute__((always_inline)) {
+    const unsigned f = fs + c * kCF + fl;
+    u32 xp[kHC][4];
+    if constexpr (POST) {
+      post_8(src, cpost, ccomb, xp);
+      if (tv) {
+        hc_bf16* xob = a.x_out + (t0 + lt) * kHC * d;
 #pragma unroll
-  for (int j = 0; j < kHC; ++j) {
-    const bf16x8 A = __builtin_bit_cast(bf16x8, a_lds[rb][hw][j][a_swz(lane, hw)]);
-    bf16x8 B[kNT];
+        for (int j = 0; j < kHC; ++j)
+          st_stream(reinterpret_cast<u32x4*>(xob + (j * d + f)), u32x4{xp[j][0], xp[j][1], xp[j][2], xp[j][3]});
+      }
+    } else {
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) B[nt] = __builtin_bit_cast(bf16x8, w_lds[hw][j][nt][lane]);
-    mfma_step(A, B, acc);
+      for (int j = 0; j < kHC; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xp[j][e] = src[j][e];
+    }
+    if constexpr (MEAN) {
+      if (tv) st_stream(reinterpret_cast<u32x4*>(a.x_mean + (t0 + lt) * d + f), mean_8(xp));
+    }
+#pragma unroll
+    for (int j = 0; j < kHC; ++j) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ssx = dot2_bf16(xp[j][e], xp[j][e], ssx);
+      a_lds[rb][a_st][j][a_swz(a_lane, a_st)] = u32x4{xp[j][0], xp[j][1], xp[j][2], xp[j][3]};
+    }
+    if constexpr (READ) {
+      u32 yp[4];
+      pre_8(xp, cpre, yp);
+      if constexpr (NORM) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ssy = dot2_bf16(yp[e], yp[e], ssy);
+          ykeep[c][e] = yp[e];
+        }
+      } else if (tv) {
+        st_stream(reinterpret_cast<u32x4*>(a.y_out + (t0 + lt) * d + f), u32x4{yp[0], yp[1], yp[2], yp[3]});
+      }
+    }
+  };
+  auto matrix_phase = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kHC; ++j) {
+      const bf16x8 A = __builtin_bit_cast(bf16x8, a_lds[rb][hw][j][a_swz(lane, hw)]);
+      bf16x8 B[kNT];
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) B[nt] = __builtin_bit_cast(bf16x8, w_lds[buf][hw][j][nt][lane]);
+      mfma_step(A, B, acc);
+    }
+  };
+  // the chunks: the next chunk's weights, then its streams, are requested
+  // before this chunk's work; two barriers (A tiles and weights in place; the
+  // matrix phase done before the A tiles are rewritten)
+  {
+    u32x4 cur[kHC + 1], wst[kNT];
+    load_wst(0, wst);
+    load_stream(0, cur);
+    store_wst(0, wst);
+    lds_barrier();
+    auto chunk = [&]<int C>(IC<C>) __attribute__((always_inline)) {
+      constexpr bool kMore = C + 1 < YK;
+      u32x4 nxt[kHC + 1];
+      if constexpr (kMore) {
+        load_wst(C + 1, wst);
+        load_stream(C + 1, nxt);
+      }
+      stream_phase(C, cur);
+      lds_barrier();
+      if constexpr (kMore) store_wst((C + 1) & 1, wst);
+      matrix_phase(C & 1);
+      if constexpr (kMore) {
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j <= kHC; ++j) cur[j] = nxt[j];
+      }
+    };
+    [&]<int... C>(std::integer_sequence<int, C...>) __attribute__((always_inline)) {
+      (chunk(IC<C>{}), ...);
+    }(std::make_integer_sequence<int, YK>{});
   }
 
   // ---- the words of the valid tokens, through LDS
@@ -1980,22 +2022,24 @@ xdec_kernel(const StreamArgs a) {
   // ---- the owned tokens' words from every slice, in one round trip
   const int nown = slice < nval ? (nval - 1 - slice) / S + 1 : 0;   // owned tokens slice, slice + S, ...
   const int npairs = nown * kOW;
-  const int G = npairs ? min(kXDGroups, kThreads / npairs) : 1;
+  // slices summed in slice order when a thread can load them all (as the
+  // two-launch finish does), else in G interleaved groups
+  const int G = npairs && S > kXFOLoads ? min(kXFGroups, kThreads / npairs) : 1;
   const bool has_o = (int)threadIdx.x < npairs * G;
   const int opr = has_o ? threadIdx.x / G : 0, og = has_o ? threadIdx.x % G : 0;
   const int ok = opr / kOW, oq = opr % kOW;
   const int otm = slice + S * ok;
   auto wptr = [&](int i) { return tilew + ((size_t)(og + G * i) * kTT + otm) * kXW + oq; };
   auto wuse = [&](int i) { return has_o && og + G * i < S; };
-  u64 wv[kXDOLoads];
+  u64 wv[kXFOLoads];
 #pragma unroll
-  for (int i = 0; i < kXDOLoads; ++i) wv[i] = wuse(i) ? get_word(wptr(i)) : 0ull;
+  for (int i = 0; i < kXFOLoads; ++i) wv[i] = wuse(i) ? get_word(wptr(i)) : 0ull;
   bool dead = false;
   settle_all(wv, wptr, wuse, tag, a.err, dead);
   if (has_o) {
     float po = 0.f;
 #pragma unroll
-    for (int i = 0; i < kXDOLoads; ++i)
+    for (int i = 0; i < kXFOLoads; ++i)
       if (og + G * i < S) {
         const float v = __uint_as_float((u32)wv[i]);
         po = i == 0 ? v : po + v;
@@ -2010,15 +2054,13 @@ xdec_kernel(const StreamArgs a) {
     tot[k][q] = v;
   }
   __syncthreads();
-  // every word of this call read but the factors: count this workgroup done
-  // (a thread of the last wave, awaited at its end; the factor words are
-  // read before the count can complete, see below)
   constexpr int kDoneThread = kThreads - 1;
-  u64* rword = a.ctl + kCtlXdR + t0;
+  // the factor of token tm: its owner's sum y^2 slot, tagged ~tag
+  auto rword = [&](int tm) { return tilew + ((size_t)(tm % S) * kTT + tm) * kXW + kMix + 1; };
   if constexpr (NORM) {   // the owned tokens' factors, for every slice of the tile
     if ((int)threadIdx.x < nown) {
       const int tm = slice + S * threadIdx.x;
-      put_word(rword + tm, tag_word(1.0f / sqrtf(tot[threadIdx.x][kXW - 1] / (float)d + a.rms_eps), tag));
+      put_word(rword(tm), tag_word(1.0f / sqrtf(tot[threadIdx.x][kXW - 1] / (float)d + a.rms_eps), ~tag));
     }
   }
   // ---- the owned tokens' mixes, pre/post and comb: 16 lanes per token
@@ -2030,21 +2072,28 @@ xdec_kernel(const StreamArgs a) {
     derive_16(r, rx, q >> 2, q & 3, true, t0 + tm, s_cf + kMix, s_cf, a.iters, a.hc_eps,
               a.mixes_out, a.pre_out, a.post_out, a.comb_out);
   }
-  // ---- z = gamma * (y * r) for the chunk, r from the token's owner
+  // ---- z = gamma * (y * r) for the slice, r from the token's owner
   if constexpr (NORM) {
-    u64 rv[1] = {tv ? get_word(rword + m) : 0ull};
-    settle_all(rv, [&](int) { return rword + m; }, [&](int) { return tv; }, tag, a.err, dead);
+    u64 rv[1] = {tv ? get_word(rword(m)) : 0ull};
+    settle_all(rv, [&](int) { return rword(m); }, [&](int) { return tv; }, ~tag, a.err, dead);
     if (tv) {
       const float ry = __uint_as_float((u32)rv[0]);
-      u32 zp[4];
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2)
-        zp[e2] = pack_bf16(gm[2 * e2] * (bf_lo(yp[e2]) * ry), gm[2 * e2 + 1] * (bf_hi(yp[e2]) * ry));
-      st_stream(reinterpret_cast<u32x4*>(a.y_out + (t0 + lt) * d + fs + fl), u32x4{zp[0], zp[1], zp[2], zp[3]});
+      for (int c = 0; c < YK; ++c) {
+        const f32x4 g0 = g_slice[(c * kCF + fl) / 4];
+        const f32x4 g1 = g_slice[(c * kCF + fl) / 4 + 1];
+        const float gm[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+        u32 zp[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2)
+          zp[e2] = pack_bf16(gm[2 * e2] * (bf_lo(ykeep[c][e2]) * ry), gm[2 * e2 + 1] * (bf_hi(ykeep[c][e2]) * ry));
+        st_stream(reinterpret_cast<u32x4*>(a.y_out + (t0 + lt) * d + fs + c * kCF + fl), u32x4{zp[0], zp[1], zp[2], zp[3]});
+      }
     }
     __syncthreads();   // every factor word of this workgroup read before it counts itself done
   }
-  // the last workgroup to count itself done advances the call epoch
+  // every word of this call read: count this workgroup done; the last one
+  // advances the call epoch
   if (threadIdx.x == kDoneThread) {
     const u64 before = __hip_atomic_fetch_add(a.ctl + kCtlXDone, (u64)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (before % (u64)gridDim.x == (u64)(gridDim.x - 1)) {
@@ -2824,23 +2873,46 @@ hipError_t launch_exchange_t(const StreamArgs& a, unsigned grid, hipStream_t st)
   }
   return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, st);
 }
-// the given-pre boundary with the RMSNorm for few tokens: one chunk per workgroup
-template <bool POST, bool READ, bool NORM>
-hipError_t launch_xdec_t(const StreamArgs& a, unsigned grid, hipStream_t st) {
+// the few-tile exchange (decode, short prefill): YK chunks per workgroup
+template <bool POST, bool READ, bool NORM, int YK>
+hipError_t launch_xfew_yk(const StreamArgs& a, unsigned grid, hipStream_t st) {
   StreamArgs copy = a;
   void* args[] = {&copy};
-  const void* fn = a.x_mean ? reinterpret_cast<const void*>(&xdec_kernel<POST, true, READ, NORM>)
-                            : reinterpret_cast<const void*>(&xdec_kernel<POST, false, READ, NORM>);
+  const void* fn = a.x_mean ? reinterpret_cast<const void*>(&xfew_kernel<POST, true, READ, NORM, YK>)
+                            : reinterpret_cast<const void*>(&xfew_kernel<POST, false, READ, NORM, YK>);
   return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, st);
 }
-bool xdec_shape(int64_t n, int d) { return n <= kXDMaxN && d % kCF == 0 && d >= kXDMinD && d <= kXDMaxD; }
+template <bool POST, bool READ, bool NORM>
+hipError_t launch_xfew_t(const StreamArgs& a, int yk, unsigned grid, hipStream_t st) {
+  switch (yk) {
+    case 1: return launch_xfew_yk<POST, READ, NORM, 1>(a, grid, st);
+    case 2: return launch_xfew_yk<POST, READ, NORM, 2>(a, grid, st);
+    case 4: return launch_xfew_yk<POST, READ, NORM, 4>(a, grid, st);
+    case 5: return launch_xfew_yk<POST, READ, NORM, 5>(a, grid, st);
+    case 8: return launch_xfew_yk<POST, READ, NORM, 8>(a, grid, st);
+    default: return launch_xfew_yk<POST, READ, NORM, 10>(a, grid, st);
+  }
+}
+// Chunks per workgroup of the few-tile exchange for (n, d): the fewest of 1,
+// 2, 4, 5, 8, 10 that divide d / 64 and leave at most 256 workgroups (one per
+// compute unit, all resident) with at least 8 slices per tile; 0 if none does.
+int xfew_chunks(int64_t n, int d) {
+  if (d % kCF || d < kXFMinD || d > kXFMaxD) return 0;
+  const int64_t tiles = (n + kTT - 1) / kTT;
+  const int nch = d / kCF;
+  for (int yk : {1, 2, 4, 5, 8, 10})
+    if (nch % yk == 0 && nch / yk >= kXFMinS && tiles * (nch / yk) <= kXMaxGroups) return yk;
+  return 0;
+}
 // The read-row exchange: slices of 10 or 20 chunks (640 or 1280 features), 4
 // to kXS slices per tile (the owned (token, word) pairs of a workgroup fit its
 // threads), and every workgroup resident at once (at most 256, one per
 // compute unit).  The slices are the two-launch schedule's where those fit;
-// else, from 20 tiles up (fewer leave too many compute units idle; measured
-// at n = 1024 and 1536), slices of 10 chunks.  Returns the slice count, 0 if
-// the shape has no such split.
+// else, from 20 tiles up (fewer leave too many compute units idle), slices of
+// 10 chunks, else of 20.  Returns the slice count, 0 if the shape has no such
+// split.  (Shapes the few-tile exchange takes, up to 2048 tokens at d = 5120,
+// run that instead: measured at n = 1280 and 1536, 38.2 and 40.2 us against
+// 40.4 and 41.7 us; equal at 2048.)
 int exchange_slices(int64_t n, int d) {
   const int64_t tiles = (n + kTT - 1) / kTT;
   auto fits = [&](int S) {
@@ -2850,6 +2922,7 @@ int exchange_slices(int64_t n, int d) {
   const int S = stream_slices(n, d);
   if (fits(S)) return S;
   if (d / kCF % 10 == 0 && fits(d / kCF / 10) && tiles >= 20) return d / kCF / 10;
+  if (d / kCF % 20 == 0 && fits(d / kCF / 20)) return d / kCF / 20;   // more tiles than 10-chunk slices allow
   return 0;
 }
 template <int RM, bool NORM>
@@ -2876,25 +2949,26 @@ int launch_boundary(bool post, int rm, bool norm, StreamArgs s, FinishArgs f, vo
   s.rec = reinterpret_cast<float*>(static_cast<char*>(ws) + kRecOffset);
   const unsigned grid1 = (unsigned)(tiles * s.S);
   hipError_t e = hipSuccess;
-  if (exchange && phases == 3 && rm != kFreshPre && xdec_shape(s.n, s.d)) {
-    // few tokens: one 64-feature chunk per workgroup, the tile's slices exchanging their words
-    s.S = s.d / kCF;
-    s.F = kCF;
+  const int xyk = exchange && phases == 3 && rm != kFreshPre ? xfew_chunks(s.n, s.d) : 0;
+  const int xs = exchange && phases == 3 && rm == kGivenPre && norm && !xyk ? exchange_slices(s.n, s.d) : 0;
+  if (xyk) {
+    // few token tiles: slices of xyk chunks, the tile's slices exchanging their words
+    s.S = s.d / kCF / xyk;
+    s.F = s.d / s.S;
     s.ctl = static_cast<u64*>(ws);
     s.xw = reinterpret_cast<u64*>(static_cast<char*>(ws) + kXOffset);
     s.err = static_cast<u32*>(ws) + kErrWord;
     s.gamma = f.gamma; s.hc_base = f.hc_base; s.hc_scale = f.hc_scale; s.mixes_out = f.mixes_out;
     s.pre_out = f.pre_out; s.post_out = f.post_out; s.comb_out = f.comb_out; s.iters = f.iters;
     s.hc_eps = f.hc_eps; s.norm_eps = f.norm_eps; s.rms_eps = f.rms_eps;
-    static_assert((size_t)(kXDMaxN / kTT) * (kXDMaxD / kCF) * kTT * kXW * sizeof(u64) <= kXRegionBytes,
-                  "the few-token exchange's words fit the exchange region");
+    if ((size_t)tiles * s.S * kTT * kXW * sizeof(u64) > kXRegionBytes)
+      return fail(HC_ENOTSUP, "%s: %lld exchange groups exceed the region", what, (long long)(tiles * s.S));
     const unsigned grid = (unsigned)(tiles * s.S);
-    if (rm == kNoRead) e = launch_xdec_t<false, false, false>(s, grid, st);
-    else if (post) e = norm ? launch_xdec_t<true, true, true>(s, grid, st) : launch_xdec_t<true, true, false>(s, grid, st);
-    else e = norm ? launch_xdec_t<false, true, true>(s, grid, st) : launch_xdec_t<false, true, false>(s, grid, st);
+    if (rm == kNoRead) e = launch_xfew_t<false, false, false>(s, xyk, grid, st);
+    else if (post) e = norm ? launch_xfew_t<true, true, true>(s, xyk, grid, st) : launch_xfew_t<true, true, false>(s, xyk, grid, st);
+    else e = norm ? launch_xfew_t<false, true, true>(s, xyk, grid, st) : launch_xfew_t<false, true, false>(s, xyk, grid, st);
     return launched(e, what);
   }
-  const int xs = exchange && phases == 3 && rm == kGivenPre && norm ? exchange_slices(s.n, s.d) : 0;
   if (xs) {
     const int yk = s.d / kCF / xs;
     s.S = xs;
@@ -3201,7 +3275,7 @@ int hc_mixes(const hc_bf16* x, const void* fn_packed, int64_t n, int hc, int d, 
     if (split) { f.pre_out = pre; f.post_out = post; f.comb_out = comb; }
     return launch_mixes_generic(hc, x, hc * d, d, fn_packed, n, d, workspace, f, st, "hc_mixes");
   }
-  if (decode_shape(n, d) && !xdec_shape(n, d)) {
+  if (decode_shape(n, d) && !xfew_chunks(n, d)) {
     DecArgs a{};
     a.n = n; a.d = d; a.x = x; a.fn = reinterpret_cast<const u32x4*>(fn_packed); a.mixes_out = mixes;
     a.xtok = kHC * d; a.xstr = d;
@@ -3217,7 +3291,7 @@ int hc_mixes(const hc_bf16* x, const void* fn_packed, int64_t n, int hc, int d, 
   f.hc_eps = hc_eps;
   if (split) { f.pre_out = pre; f.post_out = post; f.comb_out = comb; }
   return launch_boundary(false, kNoRead, false, s, f, workspace, workspace_bytes, (hipStream_t)stream, "hc_mixes", 3,
-                         xdec_shape(n, d));
+                         n <= kXFMixesMaxN);
 }
 
 int hc_pre(const hc_bf16* x, const float* pre_mix, int64_t n, int hc, int d, hc_bf16* y, void* stream) {
@@ -3412,7 +3486,7 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
     }
     return HC_OK;
   }
-  if (phases == 3 && !two && !fresh && decode_shape(p->n, p->d) && !xdec_shape(p->n, p->d)) {
+  if (phases == 3 && !two && !fresh && decode_shape(p->n, p->d) && !xfew_chunks(p->n, p->d)) {
     DecArgs a{};
     a.n = p->n; a.d = p->d; a.x = p->x; a.delta = p->delta; a.post_in = p->post_in; a.comb_in = p->comb_in;
     a.pre_in = p->pre_in; a.fn = reinterpret_cast<const u32x4*>(p->fn_packed); a.hc_base = p->hc_base;
