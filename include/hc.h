@@ -105,33 +105,32 @@ int hc_fn_pack(const float* hc_fn, int hc, int d, void* fn_packed, void* stream)
  * the regions an hc = 4 call of the same d keeps, so one workspace may serve
  * calls of every hc.
  *
- * Decode schedule (hc = 4).  For n <= 128 with d a multiple of 256, hc_mixes, and
- * hc_boundary with a given pre_in (the pages' data flow at decode; with or
- * without gamma), run as one launch: 16-token tiles by 256-feature slices,
- * each slice adding its per-token partial sums to the workspace as tagged
- * words and counting itself in on the tile's arrival word; the last slice of a
- * tile to arrive sums them in slice order (the same bits whichever slice it
- * is) and derives mixes, pre/post and the comb ("Reading weights").  Without
- * gamma no workgroup waits for another to start; with gamma every slice sums
- * the slices' sum y^2 of its tokens and writes its part of z, so all of the
- * launch's workgroups (at most 256) must be resident at once.  A word a slice
- * waits for that never becomes visible sets bit 0 of the workspace's error mask (see
- * hc_workspace_status); the call then finishes with wrong results instead of
- * hanging.  The workspace holds a control block (the error mask and the
- * schedules' call counters), the decode schedule's words and the read-row
- * exchange's words at the same place whatever (n, hc, d), then the per-slice
- * sums of the two-launch schedule (or of hc = 2, 8).
+ * Few token tiles (hc = 4: decode, short prefill).  hc_mixes for n <= 128,
+ * and hc_boundary with a given pre_in (the pages' data flow; with or without
+ * gamma) for up to 32 tiles of 64 tokens (2048 tokens at d = 5120), with d a
+ * multiple of 64 from 256 to 8192, run as one launch: each workgroup streams a
+ * (64-token tile, slice of 1 to 10 chunks of 64 features) item and adds its
+ * per-token partial sums to the workspace as tagged words; the owner slice of
+ * each token sums the token's words over the slices, derives its mixes,
+ * pre/post and comb ("Reading weights") and, with gamma, publishes the
+ * token's RMS factor for the other slices, which then write their part of z.
+ * All of the launch's workgroups (at most 256) must be resident at once.  A
+ * word a workgroup waits for that never becomes visible sets bit 0 of the
+ * workspace's error mask (see hc_workspace_status); the call then finishes
+ * with wrong results instead of hanging.  The workspace holds a control block
+ * (the error mask and the exchanges' call counters) and the exchanges' words
+ * at the same place whatever (n, hc, d), then the per-slice sums of the
+ * two-launch schedule (or of hc = 2, 8).
  * ------------------------------------------------------------------------- */
 size_t hc_workspace_bytes(int64_t n, int hc, int d);
 
 /* The workspace's regions for a call of shape (n, hc, d), as byte offsets and
- * sizes in regions[0..7]: the control block, the decode schedule's tagged
- * words, the read-row exchange's tagged words (these three at the same place
- * and size for every shape, so that no call writes another schedule's
- * persistent words), then the per-slice sums of this shape.  Their end is
- * hc_workspace_bytes (for n > 0).  HC_EINVAL / HC_ENOTSUP as hc_workspace_bytes
- * would return 0. */
-int hc_workspace_layout(int64_t n, int hc, int d, size_t regions[8]);
+ * sizes in regions[0..5]: the control block, the exchanges' tagged words
+ * (these two at the same place and size for every shape, so that no call
+ * writes another call's persistent words), then the per-slice sums of this
+ * shape.  Their end is hc_workspace_bytes (for n > 0).  HC_EINVAL /
+ * HC_ENOTSUP as hc_workspace_bytes would return 0. */
+int hc_workspace_layout(int64_t n, int hc, int d, size_t regions[6]);
 
 /* Reads a workspace's sticky error mask into *mask (host memory), after the
  * work already enqueued on stream has finished (the call synchronises the
@@ -226,18 +225,18 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
  * flags: 0, or HC_BOUNDARY_* bits (below); a caller built against a header
  * without this field passes the shorter struct_size and gets 0.
  *
- * Schedules (hc = 4).  With a given pre_in and gamma, when the feature slices
- * of a token tile are 640 or 1280 features wide and a tile has 4 to 8 of them
- * (d = 5120 with n from about 1300 to 4096, or in general d / S for the slice
- * count S the call picks), the call is one launch: each slice keeps its read
- * row on chip, the slices of a tile exchange their per-token sums through the
- * workspace as tagged words, and the RMSNorm is applied without writing y
- * first; beyond 4096 tokens (when 4096 tokens take that form) the call runs
- * as consecutive such calls of 4096 tokens and a last one for the rest (so
- * does a call with a fresh pre from 16384 tokens on).
- * Otherwise, with a given pre_in and n <= 128, the decode schedule of
- * hc_workspace_bytes runs;
- * and in every other case two launches: a streaming pass (X', the read row of
+ * Schedules (hc = 4).  With a given pre_in (or at a block entry without a
+ * read) and few token tiles (see hc_workspace_bytes: up to 2048 tokens at d =
+ * 5120), the call is one launch, the few-tile exchange.  With a given pre_in
+ * and gamma beyond that, when the feature slices of a token tile are 640 or
+ * 1280 features wide and a tile has 4 to 8 of them (d = 5120 up to 4096
+ * tokens, or in general d / S for the slice count S the call picks), the call
+ * is one launch as well: each slice keeps its read row on chip, the slices of
+ * a tile exchange their per-token sums through the workspace as tagged words,
+ * and the RMSNorm is applied without writing y first; beyond 4096 tokens
+ * (when 4096 tokens take that form) the call runs as consecutive such calls
+ * of 4096 tokens and a last one for the rest (so does a call with a fresh pre
+ * from 16384 tokens on).  In every other case two launches: a streaming pass (X', the read row of
  * a given pre, per-slice sums) and a finish (mixes, pre/post/comb, and the read
  * row where it depends on them or on its RMSNorm).  A wait for another
  * workgroup's words that times out sets bit 0 of the workspace's error mask
@@ -251,7 +250,7 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
  * them. */
 #define HC_BOUNDARY_X_EXPANDED 4u
 /* Always the two-launch schedule (the one hc_boundary_begin / _end run):
- * never the decode schedule nor the one-launch read-row exchange. */
+ * never one of the one-launch exchanges. */
 #define HC_BOUNDARY_TWO_LAUNCH 16u
 
 typedef struct hc_boundary_args {

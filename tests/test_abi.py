@@ -80,11 +80,11 @@ def test_packed_and_workspace_bytes(L):
     assert L.hc_workspace_bytes(0, 4, 5120) == 0
     assert L.hc_workspace_bytes(4096, 3, 5120) == 0
     w = L.hc_workspace_bytes(4096, 4, 5120)
-    # 8 KB control block; decode words: 8 tiles x (8192/256) slices x 16 tokens x 26 tagged 8-byte words;
-    # read-row exchange words: 256 groups x 64 tokens x 26 tagged words; then the per-slice records:
-    # 64 tiles of 64 tokens x 36 floats x the larger slice count of the two first kernels (the stream
-    # kernel's 64 tiles take 4 slices, the projection kernel's 32 workgroups of 128 tokens 8)
-    fixed = 8192 + 8 * 32 * 16 * 26 * 8 + 256 * 64 * 26 * 8
+    # 8 KB control block; exchange words: 256 groups x 64 tokens x 26 tagged 8-byte words; then the
+    # per-slice records: 64 tiles of 64 tokens x 36 floats x the larger slice count of the two first
+    # kernels (the stream kernel's 64 tiles take 4 slices, the projection kernel's 32 workgroups of
+    # 128 tokens 8)
+    fixed = 8192 + 256 * 64 * 26 * 8
     assert w == fixed + 64 * 8 * 64 * 36 * 4
     # n = 128: 2 tiles x 40 slices
     assert L.hc_workspace_bytes(128, 4, 5120) == fixed + 2 * 40 * 64 * 36 * 4
@@ -94,33 +94,31 @@ def test_packed_and_workspace_bytes(L):
 
 
 def _layout(L, n, hc, d):
-    r = (ctypes.c_size_t * 8)()
+    r = (ctypes.c_size_t * 6)()
     assert L.hc_workspace_layout(n, hc, d, r) == H.HC_OK
     return list(r)
 
 
 def test_workspace_layout_regions_never_overlap(L):
-    """Every shape's workspace: the control block, the decode words and the
-    exchange words sit at one place and size whatever (n, hc, d), so no call's
-    per-slice sums (or any other region) can lie on another schedule's
-    persistent words; the regions are disjoint and end at hc_workspace_bytes."""
-    base = _layout(L, 1, 4, 64)[:6]
+    """Every shape's workspace: the control block and the exchange words sit
+    at one place and size whatever (n, hc, d), so no call's per-slice sums (or
+    any other region) can lie on another call's persistent words; the regions
+    are disjoint and end at hc_workspace_bytes."""
+    base = _layout(L, 1, 4, 64)[:4]
     assert base[0] == 0 and base[1] == 8192
-    # the decode words hold 8 tiles x (8192/256) slices x 16 tokens x 26 words; the
-    # exchange words 256 groups x 64 tokens x 26 words
-    assert base[3] >= 8 * (8192 // 256) * 16 * 26 * 8
-    assert base[5] >= 256 * 64 * 26 * 8
+    # the exchange words: 256 groups x 64 tokens x 26 words
+    assert base[3] >= 256 * 64 * 26 * 8
     ns = (1, 17, 128, 129, 2048, 3000, 4096, 4097, 32768)
     for hc in (2, 4, 8):
         for d in range(64, 32768 + 1, 64):
             for n in ns if d % 1024 == 0 else (1, 4096):
                 r = _layout(L, n, hc, d)
-                assert r[:6] == base, (n, hc, d)
-                spans = sorted((r[i], r[i] + r[i + 1]) for i in range(0, 8, 2))
+                assert r[:4] == base, (n, hc, d)
+                spans = sorted((r[i], r[i] + r[i + 1]) for i in range(0, 6, 2))
                 for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
                     assert a1 <= b0, (n, hc, d, spans)
-                assert r[6] + r[7] == L.hc_workspace_bytes(n, hc, d), (n, hc, d)
-    bad = (ctypes.c_size_t * 8)()
+                assert r[4] + r[5] == L.hc_workspace_bytes(n, hc, d), (n, hc, d)
+    bad = (ctypes.c_size_t * 6)()
     assert L.hc_workspace_layout(16, 3, 5120, bad) == H.HC_ENOTSUP
     assert L.hc_workspace_layout(-1, 4, 5120, bad) == H.HC_EINVAL
     assert L.hc_workspace_layout(16, 4, 5120, None) == H.HC_EINVAL
@@ -143,7 +141,7 @@ def test_packed_and_workspace_bytes_other_hc(L):
     # records [S][n][recw] after the fixed regions; S is the largest divisor of hc*d/64 with at most
     # ~512 workgroups of 128 tokens, 64 at most; recw = mix + 1 rounded up to 4 floats (12 at hc = 2,
     # 84 at hc = 8)
-    fixed = 8192 + 8 * 32 * 16 * 26 * 8 + 256 * 64 * 26 * 8
+    fixed = 8192 + 256 * 64 * 26 * 8
     assert L.hc_workspace_bytes(4096, 8, 5120) == fixed + 16 * 4096 * 84 * 4
 
 def test_null_misaligned_negative(L):

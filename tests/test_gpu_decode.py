@@ -1,15 +1,12 @@
-"""GPU parity of the decode schedules: hc_boundary with a given pre (with and
-without the RMSNorm of the read row), and hc_mixes, for n <= 128 run as one
-launch ("Source layer, pairs pooled": Block.forward at decode; "Reading
-weights"; "Final RMSNorm").  From d = 1024 to 8192 that is the few-token
-exchange (64-token tiles, one 64-feature chunk per workgroup; the owner slice
-of a token sums its words over the slices, derives its coefficients and, with
-the RMSNorm, publishes the token's factor r for the other slices); at other
-widths (multiples of 256) the decode kernel, whose last-arriving feature slice
-of each 16-token tile sums the slices' partial sums and derives the
-coefficients.  Checked against the oracle on ragged token counts and
-widths whose slice count spans one and two gather batches; on one workspace
-reused across calls of changing n and inputs (the tile epochs carried in the
+"""GPU parity of the few-tile exchange at decode sizes: hc_boundary with a
+given pre (with and without the RMSNorm of the read row), and hc_mixes, for
+n <= 128 run as one launch ("Source layer, pairs pooled": Block.forward at
+decode; "Reading weights"; "Final RMSNorm"): 64-token tiles, one 64-feature
+chunk per workgroup; the owner slice of a token sums its words over the
+slices, derives its coefficients and, with the RMSNorm, publishes the token's
+factor r for the other slices.  Checked against the oracle on ragged token
+counts and on widths that give a slice 1 to 16 owned tokens; on one workspace
+reused across calls of changing n and inputs (the call epoch carried in the
 workspace); and captured in a graph with the decode block's other calls and
 replayed on new inputs."""
 import numpy as np
@@ -26,11 +23,11 @@ from transformer_hyper_connection_amd import synth
 pytestmark = pytest.mark.gpu
 
 
-# widths from 1024 to 8192 run the few-token schedule (one 64-feature chunk
-# per workgroup: S = d / 64 slices, an owner slice per token); 1088 and 1344
-# (17 and 21 slices) give a slice up to four owned tokens, 2112 (33) two; n =
-# 65 leaves one valid token in the second tile; 512 and 768 run the decode
-# kernel
+# widths from 256 to 8192 run the few-tile exchange (one 64-feature chunk per
+# workgroup: S = d / 64 slices, an owner slice per token); 1088 and 1344 (17
+# and 21 slices) give a slice up to four owned tokens, 2112 (33) two, 512 (8
+# slices) eight and 768 (12) six; n = 65 leaves one valid token in the second
+# tile; d = 10240 runs the two launches
 @pytest.mark.parametrize("n,d", [(1, 5120), (16, 5120), (17, 5120), (100, 5120), (128, 5120), (129, 5120),
                                  (45, 7168), (70, 10240), (65, 1088), (128, 1344), (100, 2112), (3, 1024),
                                  (20, 512), (128, 768)])
@@ -55,7 +52,7 @@ def test_decode_boundary_norm(n, d, entry):
 
 
 def test_decode_norm_repeated_and_against_two_launches():
-    """The decode schedule with the RMSNorm on one workspace, called again on
+    """The few-tile exchange with the RMSNorm on one workspace, called again on
     new inputs (the call epoch advances) and beside the two launches of the
     same call (bit-equal streams); every call against the oracle."""
     ws = torch.zeros(H.lib().hc_workspace_bytes(128, 4, 5120), dtype=torch.uint8, device="cuda:0")
@@ -83,9 +80,9 @@ def _inputs(t0, t1, d=5120):
 
 
 def test_decode_workspace_reused_across_n():
-    """One zeroed workspace for calls of n = 128, 64, 128, 256 (two launches),
-    17 and d = 7168 on changing inputs: every call matches the oracle and no
-    wait times out."""
+    """One zeroed workspace for calls of n = 128, 64, 128, 256 (slices of two
+    chunks), 17 and d = 7168 on changing inputs: every call matches the
+    oracle and no wait times out."""
     ws = torch.zeros(max(H.lib().hc_workspace_bytes(256, 4, 5120), H.lib().hc_workspace_bytes(256, 4, 7168)),
                      dtype=torch.uint8, device="cuda:0")
     fns = {}

@@ -16,8 +16,8 @@ from transformer_hyper_connection_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-# (hc, n, d): hc = 4 at n = 40 runs the decode schedule with a given pre and the
-# two launches otherwise; n = 300 the two launches
+# (hc, n, d): hc = 4 at n = 40 and 300 runs the few-tile exchange with a given
+# pre and the two launches otherwise
 SHAPES = [(4, 40, 1024), (4, 300, 1024), (2, 40, 1024), (8, 40, 1024)]
 
 

@@ -35,11 +35,12 @@ def _epoch(ws):
     return int(ws[8 * CTL_X_EPOCH:8 * CTL_X_EPOCH + 8].cpu().numpy().view(np.uint64)[0])
 
 
-# n = 1300 (21 tiles, the last ragged), 1536 and 2048: slices of 640 features
-# (8 per tile); 4096: slices of 1280 (4 per tile); 3000 (47 tiles x 8 slices):
-# more groups than the exchange holds, so the two launches run instead; 4097,
-# 8192 and 9000: consecutive one-launch calls of 4096 tokens, the rest (1
-# token: the decode schedule; 808 tokens: two launches) as its own call
+# n = 1300 (21 tiles, the last ragged), 1536 and 2048: the few-tile exchange
+# (slices of 512 or 640 features, 10 or 8 per tile); 3000 (47 tiles) and
+# 4096: the read-row exchange with slices of 1280 (4 per tile); 4097, 8192
+# and 9000: consecutive one-launch calls of 4096 tokens, the rest (1 token:
+# the few-tile exchange; 808 tokens: the few-tile exchange too) as its own
+# call
 @pytest.mark.parametrize("n", [1300, 1536, 2048, 3000, 4096, 4097, 8192, 9000])
 def test_exchange_every_token(n):
     say(f"[exchange] n={n}: every token")

@@ -187,8 +187,8 @@ def test_stack_exit(hc):
 
 
 def test_hc4_workspace_survives_other_hc_calls():
-    """A workspace shared with hc = 8 calls (their per-slice records) keeps the hc = 4 decode schedule's words intact: the hc = 4 decode
-    boundary before and after gives the same bits."""
+    """A workspace shared with hc = 8 calls (their per-slice records) keeps the hc = 4 exchange words
+    intact: the hc = 4 few-tile boundary before and after gives the same bits."""
     say("[hc=4/8] shared workspace")
     s4 = synth.boundary_inputs("decode", 0, 64, 1024)
     s8 = _inputs(8, 64, 1024)

@@ -26,9 +26,9 @@ def test_streams_widest_rows(n):
     assert_bits_equal(host_bits(y), O.hc_pre(s["x"], s["pre_in"]), "hc_pre")
 
 
-# (n, d, fresh, norm): d = 32768 on the two launches (fresh) and the decode
-# schedule (given pre, no RMSNorm, n <= 128: the decode words of d > 8192 fall
-# back to the two launches); d = 10240 with the RMSNorm on the two launches
+# (n, d, fresh, norm): d = 32768 on the two launches (the few-tile exchange
+# takes d up to 8192, so a given pre falls back to them too); d = 10240 with the
+# RMSNorm on the two launches; d = 8192 on the few-tile exchange
 CASES = [(20, 32768, True, False), (20, 32768, False, False), (130, 32768, False, False),
          (70, 10240, True, True), (9, 10240, False, True), (20, 8192, False, False)]
 

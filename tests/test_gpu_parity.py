@@ -122,7 +122,7 @@ def test_identities_on_gpu():
 
 
 # ------------------------------------------------------------------ hc_mixes
-# n <= 128 (d a multiple of 256) runs the decode schedule; above, the stream
+# n <= 128 (d a multiple of 64 from 256 to 8192) runs the few-tile exchange; otherwise the stream
 # kernel (two chunks in flight, loop unrolled by two) with 64-feature chunks
 # per workgroup slice: 1 at d = 64, 2 at (300, 5120), 5 at (1000, 5120), 10 at
 # (2048, 5120), 20 at 4096 and 4097 (a ragged last tile), 4 at (5000, 1024):

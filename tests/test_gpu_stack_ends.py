@@ -39,7 +39,7 @@ def _case(n, fresh, norm, with_delta, want_mean, d=5120):
     return ref, got, dict(s, x=O.expand_streams(h))
 
 
-@pytest.mark.parametrize("n", [40, 300])                # decode schedule (given pre, no norm) / two launches
+@pytest.mark.parametrize("n", [40, 300])                # few-tile exchange (given pre) / two launches (fresh)
 @pytest.mark.parametrize("fresh,norm", [(False, False), (False, True), (True, True)])
 @pytest.mark.parametrize("with_delta", [False, True])
 def test_expanded_streams(n, fresh, norm, with_delta):

@@ -4,7 +4,7 @@ the C ABI: the same kernels in the same order, so every output must match to
 the bit.  Three calls in a row on the shared static workspace, each smaller
 than the one before and on another schedule: the one-launch given-pre
 boundary with the RMSNorm (n = 4096), the two launches with a fresh read
-(n = 300), the decode schedule (n = 64); then the first call again."""
+(n = 300), the few-tile exchange (n = 64); then the first call again."""
 import ctypes
 
 import numpy as np

@@ -23,8 +23,10 @@
 //   exchange_kernel<POST, MEAN, YK>  a given pre with the RMSNorm in one launch
 //       (tiles of 4 to 8 slices of YK chunks): the slices of a tile exchange
 //       their per-token sums as tagged words; the read row stays in registers.
-//   decode_kernel<POST, READ, NORM>  the same for n <= 128 in one launch: the last
-//       slice of a token tile to arrive sums the tile's records.
+//   xfew_kernel<POST, MEAN, READ, NORM, YK>  the same for few token tiles
+//       (decode, short prefill: up to 2048 tokens at d = 5120), a given pre
+//       or no read, with or without the RMSNorm: slices of 1 to 10 chunks, an
+//       owner slice per token derives it and publishes its RMS factor.
 //   row_kernel<POST, PRE, NORM, TPW, HC>  streams only (hc_post, hc_pre, the
 //       stack exit): whole token rows per wave, 1 KB per load or store.
 //   split_kernel<HC>  hc_split_sinkhorn, one token per lane.
@@ -718,35 +720,21 @@ __global__ void __launch_bounds__(kThreads) row_kernel(const RowArgs a) {
 typedef unsigned long long u64;
 constexpr int kCtrlBytes = 8192;             // control block at the head of the workspace
 constexpr int kErrWord = 1040;               // u32 index: sticky error mask (byte 4160)
-constexpr int kCtlDecArrive = 0;             // u64 index: decode arrival words [kDTiles]
-constexpr int kCtlDecEpoch = 8;              // u64 index: decode call epoch
-constexpr int kCtlDecDone = 9;               // u64 index: decode tiles-done count
-constexpr int kCtlXEpoch = 16;               // u64 index: read-row exchange call epoch
-constexpr int kCtlXDone = 17;                // u64 index: read-row exchange workgroups-done count
+constexpr int kCtlXEpoch = 16;               // u64 index: read-row exchanges' call epoch
+constexpr int kCtlXDone = 17;                // u64 index: read-row exchanges' workgroups-done count
 constexpr unsigned kPollLimit = 1u << 14;    // polls of one word (about 1 us each) before a wait gives up
 enum : unsigned { kErrPollTimeout = 1u };
 
 __device__ __forceinline__ u64 tag_word(float v, u32 tag) { return ((u64)tag << 32) | __float_as_uint(v); }
 __device__ __forceinline__ void put_word(u64* p, u64 w) { __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ __forceinline__ u64 get_word(const u64* p) { return __hip_atomic_load(const_cast<u64*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-// The word's value once its tag is this call's, polled again as needed.  After
-// a wait of this lane has timed out (dead), no further waiting: the call then
-// finishes quickly with the error flag set rather than polling on.
-__device__ __forceinline__ float settle(const u64* p, u64 w, u32 tag, u32* err, bool& dead) {
-  unsigned polls = 0;
-  while ((u32)(w >> 32) != tag && !dead) {
-    if (++polls > kPollLimit) { atomicOr(err, kErrPollTimeout); dead = true; break; }
-    __builtin_amdgcn_s_sleep(8);
-    w = get_word(p);
-  }
-  return __uint_as_float((u32)w);
-}
-
-// Batched form of settle for the words w[i] at ptr(i) with use(i): every
-// round checks all of them and reloads all the stale ones at once, so the wait
-// ends one round trip after the last of them became visible (polling them one
-// after another costs a round trip per stale word).  Gives up after
-// kPollLimit rounds like settle (dead, error mask).
+// Waits until each of the words w[i] (at ptr(i), those with use(i)) holds the
+// call's tag: every round checks all of them and reloads all the stale ones
+// at once, so the wait ends one round trip after the last of them became
+// visible (polling them one after another costs a round trip per stale word).
+// After kPollLimit rounds it gives up: it sets the error mask and dead, and a
+// later wait of this lane gives up at once, so the call finishes quickly with
+// wrong values rather than polling on.
 template <int N, typename P, typename U>
 __device__ __forceinline__ void settle_all(u64 (&w)[N], P ptr, U use, u32 tag, u32* err, bool& dead) {
   for (unsigned polls = 0; !dead; ++polls) {
@@ -764,62 +752,6 @@ __device__ __forceinline__ void settle_all(u64 (&w)[N], P ptr, U use, u32 tag, u
     for (int i = 0; i < N; ++i)
       if (use(i) && (u32)(w[i] >> 32) != tag) w[i] = get_word(ptr(i));
   }
-}
-
-// The split and Sinkhorn of one token, 4 lanes (a quad) per token, lane j
-// holding pre_j, post_j and comb row j (column sums by DPP quad sums), from the
-// token's dots (summed in a fixed order) and its RMS factor rx ("Reading
-// weights" kernel panel and reading-weight equation).  Every lane of the quad
-// calls it; the outputs are written if valid (pre/post/comb only if pre_out).
-__device__ __forceinline__ void derive_quad(float dpre, float dpost, const float (&dcomb)[4], float rx, int j,
-                                            bool valid, int64_t t, const float* hc_scale, const float* hc_base,
-                                            int iters, float eps, float* mixes_out, float* pre_out,
-                                            float* post_out, float* comb_out) {
-  constexpr int HC = 4, MIX = 24;
-  const float mp = dpre * rx, mq = dpost * rx;
-  float mc[HC];
-#pragma unroll
-  for (int k = 0; k < HC; ++k) mc[k] = dcomb[k] * rx;
-  if (valid && mixes_out) {
-    mixes_out[t * MIX + j] = mp;
-    mixes_out[t * MIX + HC + j] = mq;
-    *reinterpret_cast<f32x4*>(mixes_out + t * MIX + 2 * HC + j * HC) = f32x4{mc[0], mc[1], mc[2], mc[3]};
-  }
-  if (!pre_out) return;
-  const float pre = sigmoidf_(mp * hc_scale[0] + hc_base[j]) + eps;
-  const float post = 2.0f * sigmoidf_(mq * hc_scale[1] + hc_base[HC + j]);
-  const float s2 = hc_scale[2];
-  float A[HC];
-  float mxr = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < HC; ++k) {
-    A[k] = mc[k] * s2 + hc_base[2 * HC + j * HC + k];
-    mxr = fmaxf(mxr, A[k]);
-  }
-  float rsum = 0.f;
-#pragma unroll
-  for (int k = 0; k < HC; ++k) {
-    A[k] = expf(A[k] - mxr);
-    rsum = rsum + A[k];
-  }
-  const float rinv = __builtin_amdgcn_rcpf(rsum);
-#pragma unroll
-  for (int k = 0; k < HC; ++k) A[k] = A[k] * rinv + eps;
-  auto col_norm = [&]() {
-#pragma unroll
-    for (int k = 0; k < HC; ++k) A[k] = A[k] * __builtin_amdgcn_rcpf(quad_sum(A[k]) + eps);
-  };
-  col_norm();
-  for (int it = 1; it < iters; ++it) {
-    const float inv = __builtin_amdgcn_rcpf(((A[0] + A[1]) + A[2]) + A[3] + eps);
-#pragma unroll
-    for (int k = 0; k < HC; ++k) A[k] = A[k] * inv;
-    col_norm();
-  }
-  if (!valid) return;
-  pre_out[t * HC + j] = pre;
-  post_out[t * HC + j] = post;
-  *reinterpret_cast<f32x4*>(comb_out + t * HC * HC + j * HC) = f32x4{A[0], A[1], A[2], A[3]};
 }
 
 // Lane exchanges inside a 16-lane row for the 16-lanes-per-token derive: lane
@@ -1821,9 +1753,9 @@ exchange_kernel(const StreamArgs a) {
 // take no part in the exchange.  Every workgroup of a call must be resident
 // at once (at most 256, one per compute unit); a wait that times out sets the
 // error mask instead of hanging.
-constexpr int kXFMinD = 1024, kXFMaxD = 8192;   // widths of the schedule
-constexpr int kXFMinS = 8;                   // slices per tile at least
-constexpr int kXFMaxOwn = kTT / kXFMinS;     // owned tokens per slice at most (8)
+constexpr int kXFMinD = 256, kXFMaxD = 8192;    // widths of the schedule
+constexpr int kXFMinS = 4;                   // slices per tile at least
+constexpr int kXFMaxOwn = kTT / kXFMinS;     // owned tokens per slice at most (16)
 constexpr int kXFGroups = 20;                // partial sums per owned word at most
 constexpr int kXFOLoads = 8;                 // owned words per thread at most (S <= 8 G for every S)
 constexpr int kXFMixesMaxN = 128;            // hc_mixes takes the schedule up to this many tokens
@@ -1837,7 +1769,7 @@ xfew_kernel(const StreamArgs a) {
   __shared__ u32x4 a_lds[4][2][kHC][64];               // X' in A layout per row block (32 KB)
   __shared__ float red[4][2][16][32];                  // projection sums per (row block, step) (16 KB)
   __shared__ float ssum[2][kTT];                       // sum x'^2, sum y^2 per token
-  __shared__ float part[kXFMaxOwn][kXW][kXFGroups];    // owned words: group sums (16.6 KB)
+  __shared__ float part[kThreads];                     // owned words: group sums, [pair][group]
   __shared__ float tot[kXFMaxOwn][kXW];                // owned words summed over the slices
   __shared__ f32x4 g_slice[NORM ? YK * kCF / 4 : 1];   // gamma of the slice
   __shared__ float s_cf[kMix + 3];                     // hc_base, hc_scale (read by the derive)
@@ -2044,13 +1976,13 @@ xfew_kernel(const StreamArgs a) {
         const float v = __uint_as_float((u32)wv[i]);
         po = i == 0 ? v : po + v;
       }
-    part[ok][oq][og] = po;
+    part[opr * G + og] = po;
   }
   __syncthreads();
   if ((int)threadIdx.x < npairs) {
     const int k = threadIdx.x / kOW, q = threadIdx.x % kOW;
-    float v = part[k][q][0];
-    for (int g = 1; g < G; ++g) v += part[k][q][g];
+    float v = part[threadIdx.x * G];
+    for (int g = 1; g < G; ++g) v += part[threadIdx.x * G + g];
     tot[k][q] = v;
   }
   __syncthreads();
@@ -2314,377 +2246,6 @@ __global__ void __launch_bounds__(kFinThreads) finish_kernel(const FinishArgs a)
   }
 }
 
-// ======================================================= decode boundary
-// decode_kernel<POST, READ, NORM>: the boundary for few tokens in one launch,
-// the finalize (split + Sinkhorn) done by the last feature slice of each token
-// tile to finish ("Source layer, pairs pooled": Block.forward at decode, the
-// read taking the given pre; "Reading weights" for the split).  Without the
-// RMSNorm no workgroup waits for another, so the launch needs no co-residency;
-// with it ("Final RMSNorm") each slice keeps its part of the read row in
-// registers, adds sum y^2 to its record, and scales the row once the S
-// slices' sums of its tokens are visible (the last slice takes them from its
-// gather), so every workgroup of the launch must be resident.
-//
-// Work items are (tile of kDT = 16 tokens, slice of kDF = 256 features of each
-// stream), one workgroup each.  A workgroup streams its item (hc_post, X'
-// stored, the read row y = sum_j pre_j X'_j stored), projects X' on the
-// matrix cores with all of its weight tiles loaded into registers at the start,
-// and writes the item's per-token record (24 dots, sum x'^2) to the workspace
-// as tagged words (value, tile epoch).  It then counts itself in on the tile's
-// arrival word; the slice that arrives last sums the S records of each token in
-// slice order (the same bits whichever slice it is), waiting for any word not
-// yet visible, and derives mixes, pre/post and the Sinkhorn comb.
-//
-// Words carry the workspace's call epoch (+1): every workgroup reads it at the
-// start, and it advances only once every tile's last slice is known, so the
-// tags grow from call to call whatever n and d are (a captured graph stays
-// valid across replays).  A tile's arrival word and the tiles-done word are
-// reset by their last arriver, found as the arrival whose count before it is
-// S-1 (tiles-1) modulo S (tiles): exactly one in any run of S (tiles).  The
-// record words must not hold the current tag before the first call: a zeroed
-// workspace never does.
-constexpr int kDT = 16;                      // tokens per tile
-constexpr int kDF = 256;                     // features per slice and stream
-constexpr int kDSteps = kDF / kStepF;        // 32-feature steps per slice (8)
-constexpr int kDThreads = 256;               // 4 waves: 2 steps each in the projection
-constexpr int kDRec = 25;                    // record words per token the last slice sums: 24 dots, sum x'^2
-constexpr int kDRecW = kDRec + 1;            // words per token in the layout: + sum y^2 (with the RMSNorm)
-constexpr int kDMaxN = 128;                  // decode schedule up to this many tokens (measured crossover)
-constexpr int kDTiles = kDMaxN / kDT;        // tiles at most (the region is sized for them)
-constexpr int kDMaxD = 8192;                 // widest row of the decode schedule (the region is sized for it)
-static_assert(kCtlDecArrive + kDTiles <= kCtlDecEpoch, "decode arrival words fit before the epoch word");
-
-struct DecArgs {
-  const hc_bf16* x;
-  const hc_bf16* delta;
-  const float* post_in;
-  const float* comb_in;
-  const float* pre_in;
-  const u32x4* fn;
-  const float* hc_base;
-  const float* hc_scale;
-  hc_bf16* x_out;
-  hc_bf16* y_out;
-  hc_bf16* x_mean;    // mean over the streams of X' (MTP tap), or NULL
-  float* mixes_out;
-  float* pre_out;
-  float* post_out;
-  float* comb_out;
-  int xtok, xstr;     // elements per token / per stream of x (hc*d, d; or d, 0 when expanded)
-  u64* rec;           // [tiles][S][kDT][kDRecW] tagged words
-  const float* gamma; // RMSNorm gain of the read row (NORM)
-  float rms_eps;
-  u64* ctl;           // the workspace's control block (arrival, epoch and tiles-done words)
-  u32* err;           // sticky error mask (a wait timed out)
-  int tiles;
-  int64_t n;
-  int d, S, iters;
-  float hc_eps, norm_eps;
-};
-
-template <bool POST, bool READ, bool NORM>
-__global__ void __launch_bounds__(kDThreads) decode_kernel(const DecArgs a) {
-  static_assert(!NORM || READ, "the RMSNorm is of the read row");
-  __shared__ u32x4 a_lds[kDSteps][kHC][64];            // X' in A layout (32 KB)
-  __shared__ float red[kDThreads / 64][kDT][32];       // per-wave dots
-  __shared__ float ssq[4][kDT];                        // sum x'^2 per chunk
-  __shared__ float ssy[NORM ? 4 : 1][kDT];             // sum y^2 per chunk (NORM)
-  __shared__ float tot[kDT][kDRecW];                   // the tile's summed records (last slice)
-  __shared__ float s_cf[kMix + 3];                     // hc_base, hc_scale (read by the last slice)
-  __shared__ u32 s_tag, s_last;
-
-  const int S = a.S, d = a.d;
-  // the split's parameters, requested now so that the last slice's derive does
-  // not wait for them
-  if (a.pre_out && threadIdx.x < kMix + 3)
-    s_cf[threadIdx.x] = threadIdx.x < kMix ? a.hc_base[threadIdx.x] : a.hc_scale[threadIdx.x - kMix];
-  // XCD-aware numbering: consecutive workgroups land on different XCDs, so
-  // they are renumbered XCD by XCD and taken slice-major, the workgroups of an
-  // XCD sharing few slices (their weight tiles stay in that XCD's L2)
-  const int G = gridDim.x;
-  const int lin = (G & 7) ? blockIdx.x : (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  const int slice = lin / a.tiles, tile = lin % a.tiles;
-  const int64_t t0 = (int64_t)tile * kDT;
-  const int fs = slice * kDF;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int m = (threadIdx.x >> 3) & (kDT - 1);        // token of the tile
-  const int fl = (threadIdx.x & 7) * 8;                // first feature within the chunk
-  const int half = threadIdx.x >> 7;                   // chunk 2p + half in pass p
-  const bool tv = t0 + m < a.n;
-  const unsigned lt = tv ? (unsigned)m : 0u;
-
-  // ---- the call's epoch
-  u64* arw = a.ctl + kCtlDecArrive + tile;
-  u64* epw = a.ctl + kCtlDecEpoch;
-  u64* donew = a.ctl + kCtlDecDone;
-  if (threadIdx.x == 0) s_tag = (u32)get_word(epw) + 1u;   // words carry epoch + 1
-
-  // ---- all loads up front: the weight tiles of this wave's two steps, the
-  // streams of both passes and the token's coefficients
-  bf16x8 B[2][kHC][kNT];
-  {
-    const int gstep = fs / kStepF + 2 * wave;
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int k = 0; k < kHC; ++k)
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt)
-          B[st][k][nt] = __builtin_bit_cast(bf16x8, a.fn[((size_t)((gstep + st) * kHC + k) * kNT + nt) * 64 + lane]);
-  }
-  u32x4 r[2][kHC + 1];
-  const hc_bf16* xrow = a.x + (t0 + lt) * a.xtok;
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int f = fs + (2 * p + half) * kCF + fl;
-#pragma unroll
-    for (int j = 0; j < kHC; ++j) r[p][j] = ld_stream(reinterpret_cast<const u32x4*>(xrow + (j * a.xstr + f)));
-    r[p][kHC] = POST ? ld_stream(reinterpret_cast<const u32x4*>(a.delta + (t0 + lt) * d + f)) : u32x4{0u, 0u, 0u, 0u};
-  }
-  float cpost[kHC], ccomb[kHC * kHC], cpre[kHC];
-#pragma unroll
-  for (int j = 0; j < kHC; ++j) {
-    cpost[j] = POST ? a.post_in[(t0 + lt) * kHC + j] : 0.f;
-    cpre[j] = READ ? a.pre_in[(t0 + lt) * kHC + j] : 0.f;
-  }
-#pragma unroll
-  for (int j = 0; j < kHC * kHC; ++j) ccomb[j] = POST ? a.comb_in[(t0 + lt) * kHC * kHC + j] : 0.f;
-
-  // the RMSNorm gain of this lane's features (NORM)
-  float gm[NORM ? 2 : 1][8];
-  if constexpr (NORM) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const f32x4* g = reinterpret_cast<const f32x4*>(a.gamma + fs + (2 * p + half) * kCF + fl);
-      const f32x4 g0 = g[0], g1 = g[1];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        gm[p][e] = g0[e];
-        gm[p][4 + e] = g1[e];
-      }
-    }
-  }
-  u32 ykeep[NORM ? 2 : 1][4];                          // the read row (NORM: kept until its factor is known)
-
-  // ---- streams: X', the read row, sum x'^2, the A tile
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int c = 2 * p + half;
-    const int f = fs + c * kCF + fl;
-    u32 xp[kHC][4];
-    if constexpr (POST) {
-      post_8(r[p], cpost, ccomb, xp);
-      if (tv) {
-#pragma unroll
-        for (int k = 0; k < kHC; ++k)
-          st_stream(reinterpret_cast<u32x4*>(a.x_out + (t0 + lt) * kHC * d + k * d + f),
-                    u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]});
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < kHC; ++k)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) xp[k][e] = r[p][k][e];
-    }
-    if (a.x_mean && tv) st_stream(reinterpret_cast<u32x4*>(a.x_mean + (t0 + lt) * d + f), mean_8(xp));
-    if constexpr (READ) {
-      u32 yp[4];
-      pre_8(xp, cpre, yp);
-      if constexpr (NORM) {
-        float sy = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sy = dot2_bf16(yp[e], yp[e], sy);
-          ykeep[p][e] = yp[e];
-        }
-        sy = oct_sum(sy);
-        if ((threadIdx.x & 7) == 0) ssy[c][m] = sy;
-      } else if (tv) {
-        st_stream(reinterpret_cast<u32x4*>(a.y_out + (t0 + lt) * d + f), u32x4{yp[0], yp[1], yp[2], yp[3]});
-      }
-    }
-    float sx = 0.f;
-#pragma unroll
-    for (int k = 0; k < kHC; ++k) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sx = dot2_bf16(xp[k][e], xp[k][e], sx);
-      // step 2c + fl/32 of the slice; matrix-core lane (fl/8 % 4) * 16 + token
-      a_lds[2 * c + (fl >> 5)][k][((fl >> 3) & 3) * 16 + m] = u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]};
-    }
-    sx = oct_sum(sx);
-    if ((threadIdx.x & 7) == 0) ssq[c][m] = sx;
-  }
-  __syncthreads();
-
-  // ---- projection: wave w takes steps 2w, 2w+1 of the slice
-  f32x4 acc[kAcc];
-#pragma unroll
-  for (int t = 0; t < kAcc; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int st = 0; st < 2; ++st)
-#pragma unroll
-    for (int k = 0; k < kHC; ++k)
-      mfma_step(__builtin_bit_cast(bf16x8, a_lds[2 * wave + st][k][lane]), B[st][k], acc);
-#pragma unroll
-  for (int t = 0; t < kAcc; ++t)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) red[wave][4 * (lane >> 4) + rr][t * 16 + (lane & 15)] = acc[t][rr];
-  __syncthreads();
-
-  // ---- this slice's record of the tile, then count in
-  const u32 tag = s_tag;
-  u64* rt = a.rec + (size_t)tile * S * kDT * kDRecW;
-  constexpr int kPut = NORM ? kDRecW : kDRec;         // + sum y^2 with the RMSNorm
-  for (int idx = threadIdx.x; idx < kDT * kPut; idx += kDThreads) {
-    const int tm = idx / kPut, q = idx % kPut;
-    float v;
-    if (q < kMix) {
-      auto col = [&](int w, int cq) { return cq < 16 ? red[w][tm][cq] : red[w][tm][cq] + red[w][tm][cq + 8]; };
-      v = ((col(0, q) + col(1, q)) + col(2, q)) + col(3, q);
-    } else if (q == kMix) {
-      v = ((ssq[0][tm] + ssq[1][tm]) + ssq[2][tm]) + ssq[3][tm];
-    } else {
-      v = ((ssy[0][tm] + ssy[1][tm]) + ssy[2][tm]) + ssy[NORM ? 3 : 0][tm];
-    }
-    put_word(rt + ((size_t)slice * kDT + tm) * kDRecW + q, tag_word(v, tag));
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const u64 before = __hip_atomic_fetch_add(arw, (u64)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = before % (u64)S == (u64)(S - 1);
-    if (s_last) {
-      put_word(arw, 0ull);                       // every slice of the tile has counted in
-      // every workgroup of the call has read the epoch once every tile's last
-      // slice is known: the last of those advances it for the next call
-      const u64 b2 = __hip_atomic_fetch_add(donew, (u64)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (b2 % (u64)a.tiles == (u64)(a.tiles - 1)) {
-        put_word(donew, 0ull);
-        put_word(epw, (u64)s_tag);               // epoch + 1
-      }
-    }
-  }
-  __syncthreads();
-  bool dead = false;
-  // z = gamma * (y * r) of this lane's features from the kept read row
-  auto store_z = [&](float ry) __attribute__((always_inline)) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int f = fs + (2 * p + half) * kCF + fl;
-      u32 zp[4];
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2)
-        zp[e2] = pack_bf16(gm[p][2 * e2] * (bf_lo(ykeep[p][e2]) * ry), gm[p][2 * e2 + 1] * (bf_hi(ykeep[p][e2]) * ry));
-      if (tv) st_stream(reinterpret_cast<u32x4*>(a.y_out + (t0 + lt) * d + f), u32x4{zp[0], zp[1], zp[2], zp[3]});
-    }
-  };
-  if (NORM && !s_last) {
-    // the other slices: the S slices' sum y^2 of this lane's token, summed in
-    // slice order (the same factor in every slice; the last slice sums them in
-    // its gather), then this slice's z.  They wait for the others' words here,
-    // so the launch needs all of its workgroups resident (at most
-    // kDTiles * kDMaxD / kDF = 256).
-    u64 w[kDMaxD / kDF];
-    const u64* p0 = rt + (size_t)m * kDRecW + kDRec;   // slice b at + b * kDT * kDRecW
-#pragma unroll
-    for (int b = 0; b < kDMaxD / kDF; ++b) w[b] = b < S ? get_word(p0 + (size_t)b * kDT * kDRecW) : 0ull;
-    float ty = 0.f;
-#pragma unroll
-    for (int b = 0; b < kDMaxD / kDF; ++b)
-      if (b < S) {
-        const float v = settle(p0 + (size_t)b * kDT * kDRecW, w[b], tag, a.err, dead);
-        ty = b == 0 ? v : ty + v;
-      }
-    store_z(1.0f / sqrtf(ty / (float)d + a.rms_eps));
-  }
-  if (!s_last) return;
-
-  // ---- the last slice: sum the S records of each token in slice order; a
-  // thread's words of all slices are requested together (one round trip)
-  constexpr int kGath = NORM ? kDRecW : kDRec;                        // words summed per token (+ sum y^2)
-  constexpr int kPairs = (kDT * kGath + kDThreads - 1) / kDThreads;   // (token, word) pairs per thread
-  constexpr int kBatch = 32;                                          // slices in flight per pair
-  for (int b0 = 0; b0 < S; b0 += kBatch) {
-    u64 w[kPairs][kBatch];
-#pragma unroll
-    for (int i = 0; i < kPairs; ++i) {
-      const int idx = threadIdx.x + i * kDThreads;
-      const u64* p0 = rt + (size_t)(idx / kGath) * kDRecW + idx % kGath;   // slice b at + b * kDT * kDRecW
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b)
-        w[i][b] = (idx < kDT * kGath && b0 + b < S) ? get_word(p0 + (size_t)(b0 + b) * kDT * kDRecW) : 0ull;
-    }
-#pragma unroll
-    for (int i = 0; i < kPairs; ++i) {
-      const int idx = threadIdx.x + i * kDThreads;
-      if (idx >= kDT * kGath) continue;
-      const int tm = idx / kGath, q = idx % kGath;
-      const u64* p0 = rt + (size_t)tm * kDRecW + q;
-      float s = b0 == 0 ? 0.f : tot[tm][q];
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b)
-        if (b0 + b < S) {
-          const float v = settle(p0 + (size_t)(b0 + b) * kDT * kDRecW, w[i][b], tag, a.err, dead);
-          s = b0 + b == 0 ? v : s + v;
-        }
-      tot[tm][q] = s;
-    }
-  }
-  __syncthreads();
-  // the last slice's own z first (its stores drain while wave 0 derives)
-  if constexpr (NORM) store_z(1.0f / sqrtf(tot[m][kDRec] / (float)d + a.rms_eps));
-  // ---- derive: 4 lanes (a quad) per token, lane j holding comb row j
-  if (threadIdx.x < kDT * kHC) {
-    const int tm = threadIdx.x >> 2, j = threadIdx.x & 3;
-    const int64_t t = t0 + tm;
-    const bool valid = t < a.n;
-    const float* rec = tot[tm];
-    const float rx = 1.0f / sqrtf(rec[kMix] / (float)(kHC * d) + a.norm_eps);
-    if (valid && a.mixes_out) {
-#pragma unroll
-      for (int i = 0; i < kMix / kHC; ++i) a.mixes_out[t * kMix + i * kHC + j] = rec[i * kHC + j] * rx;
-    }
-    if (a.pre_out) {
-      const float s0 = s_cf[kMix], s1 = s_cf[kMix + 1], s2 = s_cf[kMix + 2];
-      const float pre = sigmoidf_((rec[j] * rx) * s0 + s_cf[j]) + a.hc_eps;
-      const float post = 2.0f * sigmoidf_((rec[kHC + j] * rx) * s1 + s_cf[kHC + j]);
-      float A[kHC];
-      float mxr = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < kHC; ++k) {
-        const int q = 2 * kHC + j * kHC + k;
-        A[k] = (rec[q] * rx) * s2 + s_cf[q];
-        mxr = fmaxf(mxr, A[k]);
-      }
-      float rsum = 0.f;
-#pragma unroll
-      for (int k = 0; k < kHC; ++k) {
-        A[k] = expf(A[k] - mxr);
-        rsum = rsum + A[k];
-      }
-      const float rinv = __builtin_amdgcn_rcpf(rsum);
-#pragma unroll
-      for (int k = 0; k < kHC; ++k) A[k] = A[k] * rinv + a.hc_eps;
-      auto col_norm = [&]() {
-#pragma unroll
-        for (int k = 0; k < kHC; ++k) A[k] = A[k] * __builtin_amdgcn_rcpf(quad_sum(A[k]) + a.hc_eps);
-      };
-      col_norm();
-      for (int it = 1; it < a.iters; ++it) {
-        const float inv = __builtin_amdgcn_rcpf(((A[0] + A[1]) + A[2]) + A[3] + a.hc_eps);
-#pragma unroll
-        for (int k = 0; k < kHC; ++k) A[k] = A[k] * inv;
-        col_norm();
-      }
-      if (valid) {
-        a.pre_out[t * kHC + j] = pre;
-        a.post_out[t * kHC + j] = post;
-        *reinterpret_cast<f32x4*>(a.comb_out + t * kHC * kHC + j * kHC) = f32x4{A[0], A[1], A[2], A[3]};
-      }
-    }
-  }
-}
-
 // The library's own workspace for hc_boundary_static, one copy per GPU the
 // library runs on (held until the process ends).  Zero when the code object
 // is loaded, as a fresh caller workspace must be; every call leaves it valid
@@ -2812,21 +2373,18 @@ size_t split_records_bytes(int64_t n, int d) {
 // Workspace layout, the same for every (n, hc, d), so that one workspace
 // serves calls of any shape and no region of one call lies on the persistent
 // words of another:
-//   [control block, kCtrlBytes]  error mask, the decode schedule's arrival /
-//                                epoch / tiles-done words, the read-row
-//                                exchange's epoch and done words
-//   [decode records]             [kDTiles][kDMaxD/kDF][kDT][kDRecW] tagged words
-//   [read-row exchange words]    [kXMaxGroups][kTT][kXW] tagged words
+//   [control block, kCtrlBytes]  error mask, the read-row exchanges' epoch and
+//                                done words
+//   [read-row exchange words]    [kXMaxGroups][kTT][kXW] tagged words (both
+//                                exchange kernels)
 //   [per-slice records]          two-launch schedule (hc = 4) or hc = 2, 8;
 //                                plain floats, rewritten by every call
-// Tagged words carry their schedule's call epoch + 1; the epochs only grow, so
-// a word left by an earlier call (of any shape) never holds a current tag.
-bool decode_shape(int64_t n, int d) { return n <= kDMaxN && d % kDF == 0 && d <= kDMaxD; }
-constexpr size_t kDecRegionBytes = (size_t)kDTiles * (kDMaxD / kDF) * kDT * kDRecW * sizeof(u64);
+// Tagged words carry the exchanges' call epoch + 1 (the few-tile exchange's
+// RMS factor words its complement); the epoch only grows, so a word left by an
+// earlier call (of any shape) never holds a current tag.
 constexpr int kXMaxGroups = 256;             // (tile, slice) groups (= workgroups) of one read-row exchange at most
 constexpr size_t kXRegionBytes = (size_t)kXMaxGroups * kTT * kXW * sizeof(u64);
-constexpr size_t kDecOffset = kCtrlBytes;
-constexpr size_t kXOffset = kDecOffset + kDecRegionBytes;
+constexpr size_t kXOffset = kCtrlBytes;
 constexpr size_t kRecOffset = kXOffset + kXRegionBytes;
 constexpr int64_t kXPart = (int64_t)kXMaxGroups / 4 * kTT;   // tokens of the largest exchange (4 slices a tile)
 // The per-slice records a call of n tokens can need: its own, and, since a
@@ -3019,42 +2577,6 @@ int launch_boundary(bool post, int rm, bool norm, StreamArgs s, FinishArgs f, vo
   if (rm == kFreshPre) e = norm ? launch_finish_t<kFreshPre, true>(f, grid2, st) : launch_finish_t<kFreshPre, false>(f, grid2, st);
   else if (rm == kGivenPre && norm) e = launch_finish_t<kGivenPre, true>(f, grid2, st);
   else e = launch_finish_t<kNoRead, false>(f, grid2, st);
-  return launched(e, what);
-}
-
-// ---- decode boundary
-template <bool POST, bool READ, bool NORM = false>
-hipError_t launch_decode_t(const DecArgs& a, unsigned grid, hipStream_t st) {
-  DecArgs copy = a;
-  void* args[] = {&copy};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<POST, READ, NORM>), dim3(grid), dim3(kDThreads),
-                         args, 0, st);
-}
-// a.gamma set: the read row's RMSNorm (read must be set)
-int launch_decode(bool post, bool read, DecArgs a, void* ws, size_t ws_bytes, hipStream_t st, const char* what) {
-  const size_t need = workspace_bytes(a.n, a.d);
-  if (!ws) return fail(HC_EINVAL, "%s: workspace must not be NULL (need %zu bytes)", what, need);
-  if (!aligned16(ws)) return fail(HC_EINVAL, "%s: workspace is not 16-byte aligned", what);
-  if (ws_bytes < need) return fail(HC_EINVAL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, need);
-  a.S = a.d / kDF;
-  const int64_t tiles = (a.n + kDT - 1) / kDT;
-  a.ctl = static_cast<u64*>(ws);
-  a.rec = reinterpret_cast<u64*>(static_cast<char*>(ws) + kDecOffset);
-  if ((size_t)((a.n + kDT - 1) / kDT) * (a.d / kDF) * kDT * kDRecW * sizeof(u64) > kDecRegionBytes)
-    return fail(HC_ENOTSUP, "%s: the decode records exceed their region", what);
-  a.err = static_cast<u32*>(ws) + kErrWord;
-  a.tiles = (int)tiles;
-  const unsigned grid = (unsigned)(tiles * a.S);
-  hipError_t e;
-  const bool norm = read && a.gamma != nullptr;
-  switch ((norm ? 4 : 0) | (post ? 2 : 0) | (read ? 1 : 0)) {
-    case 0: e = launch_decode_t<false, false>(a, grid, st); break;
-    case 1: e = launch_decode_t<false, true>(a, grid, st); break;
-    case 2: e = launch_decode_t<true, false>(a, grid, st); break;
-    case 3: e = launch_decode_t<true, true>(a, grid, st); break;
-    case 5: e = launch_decode_t<false, true, true>(a, grid, st); break;
-    default: e = launch_decode_t<true, true, true>(a, grid, st); break;
-  }
   return launched(e, what);
 }
 
@@ -3275,14 +2797,6 @@ int hc_mixes(const hc_bf16* x, const void* fn_packed, int64_t n, int hc, int d, 
     if (split) { f.pre_out = pre; f.post_out = post; f.comb_out = comb; }
     return launch_mixes_generic(hc, x, hc * d, d, fn_packed, n, d, workspace, f, st, "hc_mixes");
   }
-  if (decode_shape(n, d) && !xfew_chunks(n, d)) {
-    DecArgs a{};
-    a.n = n; a.d = d; a.x = x; a.fn = reinterpret_cast<const u32x4*>(fn_packed); a.mixes_out = mixes;
-    a.xtok = kHC * d; a.xstr = d;
-    a.hc_scale = hc_scale; a.hc_base = hc_base; a.iters = iters; a.hc_eps = hc_eps; a.norm_eps = norm_eps;
-    if (split) { a.pre_out = pre; a.post_out = post; a.comb_out = comb; }
-    return launch_decode(false, false, a, workspace, workspace_bytes, (hipStream_t)stream, "hc_mixes");
-  }
   StreamArgs s{};
   s.n = n; s.d = d; s.x = x; s.fn = reinterpret_cast<const u32x4*>(fn_packed);
   s.xtok = kHC * d; s.xstr = d;
@@ -3330,17 +2844,16 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
 
 size_t hc_boundary_workspace_bytes(int64_t n, int hc, int d) { return hc_workspace_bytes(n, hc, d); }
 
-int hc_workspace_layout(int64_t n, int hc, int d, size_t regions[8]) {
+int hc_workspace_layout(int64_t n, int hc, int d, size_t regions[6]) {
   g_err[0] = 0;
   if (!regions) return fail(HC_EINVAL, "regions must not be NULL");
   int rc = check_hd(hc, d);
   if (rc) return rc;
   if ((rc = check_n(n))) return rc;
   regions[0] = 0;            regions[1] = kCtrlBytes;
-  regions[2] = kDecOffset;   regions[3] = kDecRegionBytes;
-  regions[4] = kXOffset;     regions[5] = kXRegionBytes;
-  regions[6] = kRecOffset;
-  regions[7] = n == 0 ? 0 : (hc == kHC ? records_bytes(n, d) : generic_ws_bytes(n, hc, d) - kRecOffset);
+  regions[2] = kXOffset;     regions[3] = kXRegionBytes;
+  regions[4] = kRecOffset;
+  regions[5] = n == 0 ? 0 : (hc == kHC ? records_bytes(n, d) : generic_ws_bytes(n, hc, d) - kRecOffset);
   return HC_OK;
 }
 
@@ -3485,16 +2998,6 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
       if ((rc = boundary_phases(&q, stream, 3))) return rc;
     }
     return HC_OK;
-  }
-  if (phases == 3 && !two && !fresh && decode_shape(p->n, p->d) && !xfew_chunks(p->n, p->d)) {
-    DecArgs a{};
-    a.n = p->n; a.d = p->d; a.x = p->x; a.delta = p->delta; a.post_in = p->post_in; a.comb_in = p->comb_in;
-    a.pre_in = p->pre_in; a.fn = reinterpret_cast<const u32x4*>(p->fn_packed); a.hc_base = p->hc_base;
-    a.hc_scale = p->hc_scale; a.x_out = p->x_out; a.y_out = p->y_out; a.mixes_out = p->mixes_out;
-    a.pre_out = p->pre_out; a.post_out = p->post_out; a.comb_out = p->comb_out; a.iters = p->iters;
-    a.hc_eps = p->hc_eps; a.norm_eps = p->norm_eps; a.xtok = xtok; a.xstr = xstr; a.x_mean = x_mean;
-    a.gamma = p->gamma; a.rms_eps = p->rms_eps;
-    return launch_decode(post, true, a, p->workspace, p->workspace_bytes, st, "hc_boundary");
   }
   StreamArgs s{};
   s.n = p->n; s.d = p->d; s.x = p->x; s.delta = p->delta; s.post_in = p->post_in; s.comb_in = p->comb_in;
