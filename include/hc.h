@@ -295,7 +295,7 @@ int hc_boundary(const hc_boundary_args* args, void* stream);
  * (16 MiB on each GPU the library runs on, held until the process ends; zero
  * when the library is loaded).  It allocates nothing.  Shapes whose workspace
  * (hc_workspace_bytes) exceeds 16 MiB return HC_ENOTSUP -- hc = 4 fits up to
- * about 87 000 tokens at d = 5120.  Every call on one GPU shares that GPU's
+ * 92 736 tokens at d = 5120.  Every call on one GPU shares that GPU's
  * static workspace, which keeps the last call's contents: calls that may
  * overlap on one GPU (different streams, different threads) race and must be
  * serialised by the caller.  Same status codes as hc_boundary.
