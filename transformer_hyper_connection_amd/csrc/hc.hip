@@ -711,6 +711,170 @@ __global__ void __launch_bounds__(kThreads) row_kernel(const RowArgs a) {
   }
 }
 
+// hc = 2 with a write and a fresh pre: the write and the projection in one
+// pass ("Write the streams"; "Source layer, pairs pooled", Block.hc_mixes on
+// X'), so X' is not read back for the projection (only for the read, which
+// needs the pre the projection gives).  Slices of the feature range of d (all
+// hc streams of a feature together), 128 tokens per workgroup; per 64-feature
+// chunk each lane loads, for each of its two row tiles and two 32-feature
+// steps, its 8 features of the hc stream rows and of Delta in the matrix-core
+// A layout, forms X' (the fp32 sequence of Block.hc_post), stores it, and uses
+// it as the A operand against the weight tiles of its stream (staged through a
+// double-buffered LDS area, one chunk ahead).  The records are gmix_kernel's.
+// (hc = 8 would need 240 KB of weight tiles per chunk, more than LDS holds.)
+struct GStreamArgs {
+  const hc_bf16* x;
+  const hc_bf16* delta;
+  const float* post_in;
+  const float* comb_in;
+  const u32x4* fn;     // packed as for gmix_kernel
+  hc_bf16* x_out;
+  hc_bf16* x_mean;     // mean over the streams of X' (MTP tap), or NULL
+  float* rec;          // [S][n][RECW]
+  int64_t n;
+  int xtok, xstr;      // elements per token / per stream of x
+  int d, S, Fs;        // slices of the feature range of d, Fs features each
+};
+
+template <int HC, bool MEAN>
+__global__ void __launch_bounds__(kGThreads, 2) gstream_kernel(const GStreamArgs a) {
+  using G = GShape<HC>;
+  constexpr int NCT = G::NCT, RT = G::RT;
+  constexpr int BREC = HC * 2 * NCT * 64;       // 16-byte weight records per chunk: [stream][step][tile][lane]
+  constexpr int BPT = (BREC + kGThreads - 1) / kGThreads;
+  __shared__ u32x4 w_lds[2][BREC];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slice = blockIdx.x % a.S, group = blockIdx.x / a.S;
+  const int64_t tw = (int64_t)group * kGTok + wave * 32;
+  const int d = a.d;
+  int64_t tr[2];
+  bool tv[2];
+  float cpost[2][HC], ccomb[2][HC * HC];
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti) {
+    const int64_t t = tw + 16 * ti + (lane & 15);
+    tv[ti] = t < a.n;
+    tr[ti] = tv[ti] ? t : 0;                       // rows past n read token 0 and are never stored
+#pragma unroll
+    for (int j = 0; j < HC; ++j) cpost[ti][j] = a.post_in[tr[ti] * HC + j];
+#pragma unroll
+    for (int j = 0; j < HC * HC; ++j) ccomb[ti][j] = a.comb_in[tr[ti] * HC * HC + j];
+  }
+  const int kg = 8 * (lane >> 4);
+  const int c0 = slice * a.Fs;
+  const int nch = a.Fs / kGChunk;
+
+  auto load_src = [&](int ch, u32x4 (&R)[2][2][HC + 1]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int f = c0 + ch * kGChunk + 32 * st + kg;
+        const hc_bf16* xr = a.x + tr[ti] * a.xtok + f;
+        // plain (cached) loads: the two steps' 64-byte halves of a line meet in L2 as one fill
+#pragma unroll
+        for (int k = 0; k < HC; ++k) R[ti][st][k] = *reinterpret_cast<const u32x4*>(xr + k * a.xstr);
+        R[ti][st][HC] = *reinterpret_cast<const u32x4*>(a.delta + tr[ti] * d + f);
+      }
+  };
+  auto load_b = [&](int ch, u32x4 (&Bs)[BPT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < BPT; ++r) {
+      const int idx = threadIdx.x + kGThreads * r;
+      if (idx < BREC) {
+        const int k = idx / (2 * NCT * 64), rem = idx % (2 * NCT * 64);   // rem = (step, tile, lane)
+        const int step = (k * d + c0 + ch * kGChunk) / 32 + rem / (NCT * 64);
+        Bs[r] = a.fn[(size_t)step * NCT * 64 + rem % (NCT * 64)];
+      }
+    }
+  };
+  auto store_b = [&](int buf, const u32x4 (&Bs)[BPT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < BPT; ++r) {
+      const int idx = threadIdx.x + kGThreads * r;
+      if (idx < BREC) w_lds[buf][idx] = Bs[r];
+    }
+  };
+
+  f32x4 acc[2][NCT];
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[ti][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ss[2] = {0.f, 0.f};
+  u32x4 cur[2][2][HC + 1], nxt[2][2][HC + 1], Bs[BPT];
+  load_b(0, Bs);
+  load_src(0, cur);
+  store_b(0, Bs);
+  __syncthreads();
+  for (int ch = 0; ch < nch; ++ch) {
+    const bool more = ch + 1 < nch;
+    if (more) {
+      load_b(ch + 1, Bs);
+      load_src(ch + 1, nxt);
+    }
+    const u32x4* wb = w_lds[ch & 1];
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        u32 xp[HC][4];
+        post_8<HC>(cur[ti][st], cpost[ti], ccomb[ti], xp);
+        const int f = c0 + ch * kGChunk + 32 * st + kg;
+        if (tv[ti]) {
+#pragma unroll
+          for (int k = 0; k < HC; ++k)
+            *reinterpret_cast<u32x4*>(a.x_out + (tr[ti] * HC + k) * d + f) = u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]};
+          if constexpr (MEAN) st_stream(reinterpret_cast<u32x4*>(a.x_mean + tr[ti] * d + f), mean_8<HC>(xp));
+        }
+#pragma unroll
+        for (int k = 0; k < HC; ++k) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ss[ti] = dot2_bf16(xp[k][e], xp[k][e], ss[ti]);
+          const bf16x8 A = __builtin_bit_cast(bf16x8, u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]});
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+            acc[ti][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                A, __builtin_bit_cast(bf16x8, wb[((k * 2 + st) * NCT + ct) * 64 + lane]), acc[ti][ct], 0, 0, 0);
+        }
+      }
+    if (more) store_b((ch + 1) & 1, Bs);
+    __syncthreads();                              // next weights in place; this chunk's reads done
+    if (more) {
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int k = 0; k <= HC; ++k) cur[ti][st][k] = nxt[ti][st][k];
+    }
+  }
+
+  // the records, as gmix_kernel writes them
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti) {
+    ss[ti] += __shfl_xor(ss[ti], 16);
+    ss[ti] += __shfl_xor(ss[ti], 32);
+  }
+  float* rs = a.rec + (size_t)slice * a.n * G::RECW;
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = 16 * rt + (lane & 15);
+      if (row < G::MIX) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t t = tw + 16 * ti + 4 * (lane >> 4) + r;   // accumulator row = token
+          if (t < a.n) rs[t * G::RECW + row] = (acc[ti][rt][r] + acc[ti][rt + RT][r]) + acc[ti][rt + 2 * RT][r];
+        }
+      }
+    }
+    const int64_t t = tw + 16 * ti + lane;
+    if (lane < 16 && t < a.n) rs[t * G::RECW + G::MIX] = ss[ti];
+  }
+}
+
 // ======================================================= workgroup exchange
 // Words that one workgroup leaves for another travel through the workspace as
 // 64-bit (tag, value) pairs written and read with device scope: a word is valid
@@ -2646,12 +2810,25 @@ int gen_slices(int64_t n, int hc, int d) {
   return best;
 }
 
-// workspace of the hc != 4 path: the per-slice records, placed after the
-// control block and the decode region of the same d so that a workspace
-// shared with hc = 4 calls keeps their words intact
+// slices of the fused hc = 2 write and projection: of the feature range of d
+int fused_slices(int64_t n, int d) {
+  const int64_t groups = (n + kGTok - 1) / kGTok;
+  const int chunks = d / kGChunk;
+  const int64_t want = std::max<int64_t>(1, std::min<int64_t>(64, (512 + groups - 1) / groups));
+  int best = 1;
+  for (int s = 1; s <= want; ++s)
+    if (chunks % s == 0) best = s;
+  return best;
+}
+
+// workspace of the hc != 4 path: the per-slice records (of the projection
+// kernel or, at hc = 2, of the fused write and projection), placed after the
+// control block and the exchange words so that a workspace shared with
+// hc = 4 calls keeps their words intact
 size_t gen_rec_offset(int) { return kRecOffset; }
 size_t generic_ws_bytes(int64_t n, int hc, int d) {
-  return gen_rec_offset(d) + (size_t)gen_slices(n, hc, d) * n * gen_recw(hc) * 4;
+  const int S = hc == 2 ? std::max(gen_slices(n, hc, d), fused_slices(n, d)) : gen_slices(n, hc, d);
+  return gen_rec_offset(d) + (size_t)S * n * gen_recw(hc) * 4;
 }
 
 int check_generic_ws(int64_t n, int hc, int d, const void* ws, size_t ws_bytes, const char* what) {
@@ -2666,6 +2843,16 @@ int check_generic_ws(int64_t n, int hc, int d, const void* ws, size_t ws_bytes, 
 
 // projection + split for hc 2 or 8: records into the workspace, then one
 // token per lane sums them and derives mixes / pre, post, comb
+// the finish of the hc != 4 projection: f.rec, f.n, f.S and f.K set
+int launch_gfinish(int hc, GFinArgs f, hipStream_t st, const char* what) {
+  void* fargs[] = {&f};
+  const int64_t tpb = 256 / hc;                   // tokens per workgroup: hc lanes each
+  const hipError_t e = hipLaunchKernel(hc == 2 ? reinterpret_cast<const void*>(&gfinish_kernel<2>)
+                                               : reinterpret_cast<const void*>(&gfinish_kernel<8>),
+                                       dim3((unsigned)((f.n + tpb - 1) / tpb)), dim3(256), fargs, 0, st);
+  return launched(e, what);
+}
+
 int launch_mixes_generic(int hc, const hc_bf16* x, int xtok, int xstr, const void* fn, int64_t n, int d,
                          void* ws, GFinArgs f, hipStream_t st, const char* what) {
   GMixArgs m{};
@@ -2681,12 +2868,30 @@ int launch_mixes_generic(int hc, const hc_bf16* x, int xtok, int xstr, const voi
   int rc = launched(e, what);
   if (rc) return rc;
   f.rec = m.rec; f.n = n; f.S = m.S; f.K = hc * d;
-  void* fargs[] = {&f};
-  const int64_t tpb = 256 / hc;                   // tokens per workgroup: hc lanes each
-  e = hipLaunchKernel(hc == 2 ? reinterpret_cast<const void*>(&gfinish_kernel<2>)
-                              : reinterpret_cast<const void*>(&gfinish_kernel<8>),
-                      dim3((unsigned)((n + tpb - 1) / tpb)), dim3(256), fargs, 0, st);
-  return launched(e, what);
+  return launch_gfinish(hc, f, st, what);
+}
+
+// hc = 2, a write with a fresh pre: the fused write and projection (phase 1), the finish (phase 2)
+int launch_stream_generic(const hc_boundary_args* p, int xtok, int xstr, hc_bf16* x_mean, GFinArgs f,
+                          hipStream_t st, const char* what, int phases) {
+  GStreamArgs g{};
+  g.x = p->x; g.delta = p->delta; g.post_in = p->post_in; g.comb_in = p->comb_in;
+  g.fn = static_cast<const u32x4*>(p->fn_packed); g.x_out = p->x_out; g.x_mean = x_mean;
+  g.n = p->n; g.xtok = xtok; g.xstr = xstr; g.d = p->d;
+  g.S = fused_slices(p->n, p->d);
+  g.Fs = p->d / g.S;
+  g.rec = reinterpret_cast<float*>(static_cast<char*>(p->workspace) + gen_rec_offset(p->d));
+  if (phases & 1) {
+    void* args[] = {&g};
+    const dim3 grid((unsigned)((p->n + kGTok - 1) / kGTok * g.S));
+    const hipError_t e = hipLaunchKernel(x_mean ? reinterpret_cast<const void*>(&gstream_kernel<2, true>)
+                                                : reinterpret_cast<const void*>(&gstream_kernel<2, false>),
+                                         grid, dim3(kGThreads), args, 0, st);
+    const int rc = launched(e, what);
+    if (rc || !(phases & 2)) return rc;
+  }
+  f.rec = g.rec; f.n = p->n; f.S = g.S; f.K = 2 * p->d;
+  return launch_gfinish(2, f, st, what);
 }
 
 int launch_split(int hc, const float* mixes, const float* scale, const float* base, int64_t n, int iters,
@@ -2941,6 +3146,19 @@ static int boundary_phases(const hc_boundary_args* p, void* stream, int phases) 
     r.n = p->n; r.d = d; r.x = p->x; r.delta = p->delta; r.post_in = p->post_in; r.comb_in = p->comb_in;
     r.gamma = p->gamma; r.x_out = p->x_out; r.y_out = p->y_out; r.rms_eps = p->rms_eps;
     r.xtok = xtok; r.xstr = xstr;
+    if (hc == 2 && post && fresh) {
+      // the write and the projection in one pass (begin); the finish and the read (end)
+      GFinArgs f{};
+      f.hc_scale = p->hc_scale; f.hc_base = p->hc_base; f.mixes_out = p->mixes_out; f.pre_out = p->pre_out;
+      f.post_out = p->post_out; f.comb_out = p->comb_out; f.iters = p->iters; f.norm_eps = p->norm_eps;
+      f.hc_eps = p->hc_eps;
+      if ((rc = launch_stream_generic(p, xtok, xstr, x_mean, f, st, "hc_boundary", phases))) return rc;
+      if (!(phases & 2)) return HC_OK;
+      RowArgs rd = r;
+      rd.x = p->x_out; rd.xtok = hc * d; rd.xstr = d; rd.delta = nullptr; rd.post_in = nullptr;
+      rd.comb_in = nullptr; rd.x_out = nullptr; rd.pre_in = p->pre_out; rd.x_mean = nullptr;
+      return launch_row(false, true, norm, rd, st, "hc_boundary (read)", hc);
+    }
     if ((phases & 1) && (post || !fresh)) {
       RowArgs w = r;
       w.pre_in = fresh ? nullptr : p->pre_in;
