@@ -24,7 +24,8 @@
  *   - n = number of tokens (batch x positions, flattened).  hc is 2, 4 or 8;
  *     hc = 4 (the pages' setting) runs the fused kernels, hc = 2 and 8 a
  *     plainer schedule of separate launches (the write, the projection, the
- *     split, the read), with the same arithmetic.  d must be a positive
+ *     split, the read; at hc = 2 a boundary with a write and a fresh pre does
+ *     the write and the projection in one pass), with the same arithmetic.  d must be a positive
  *     multiple of 64 and at most 32768 (at most 10240 where the read row is
  *     RMS-normalised).
  *   - stream is a hipStream_t (NULL = the null stream).  Calls enqueue work on
@@ -214,7 +215,9 @@ int hc_post(const hc_bf16* delta, const hc_bf16* x, const float* post, const flo
  * most (from the rounding of y), which moves z by at most half a bf16 ulp.
  * (hc = 2 and 8 take the mean square of the bf16 y in every case, running the
  * write, the projection, the split and the read as separate launches: begin
- * enqueues the write, and the read when pre_in is given; end the rest.)
+ * enqueues the write, and the read when pre_in is given; end the rest.  At
+ * hc = 2 with delta and a fresh pre, begin enqueues the write and the
+ * projection as one pass, end the split and the read.)
  * With pre_in given the call follows the pages' data flow: the streams are
  * read with the reading mix of the previous boundary and the call returns the
  * (pre, post, comb) of this boundary for the next one.  Use delta == NULL at a
