@@ -2003,16 +2003,27 @@ xfew_kernel(const StreamArgs a) {
 #pragma unroll
   for (int t = 0; t < kAcc; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   u32 ykeep[NORM ? YK : 1][4];                         // the read row, chunk by chunk (RMSNorm)
+  u32 xlast[kHC][4];                                   // X' of the last chunk, stored after the words
+  auto store_x = [&](int c, const u32 (&xp)[kHC][4]) __attribute__((always_inline)) {
+    if (tv) {
+      hc_bf16* xob = a.x_out + (t0 + lt) * kHC * d + fs + c * kCF + fl;
+#pragma unroll
+      for (int j = 0; j < kHC; ++j)
+        st_stream(reinterpret_cast<u32x4*>(xob + j * d), u32x4{xp[j][0], xp[j][1], xp[j][2], xp[j][3]});
+    }
+  };
   auto stream_phase = [&](int c, const u32x4 (&src)[kHC + 1]) __attribute__((always_inline)) {
     const unsigned f = fs + c * kCF + fl;
     u32 xp[kHC][4];
     if constexpr (POST) {
       post_8(src, cpost, ccomb, xp);
-      if (tv) {
-        hc_bf16* xob = a.x_out + (t0 + lt) * kHC * d;
+      if (c + 1 < YK) {
+        store_x(c, xp);
+      } else {
 #pragma unroll
         for (int j = 0; j < kHC; ++j)
-          st_stream(reinterpret_cast<u32x4*>(xob + (j * d + f)), u32x4{xp[j][0], xp[j][1], xp[j][2], xp[j][3]});
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xlast[j][e] = xp[j][e];
       }
     } else {
 #pragma unroll
@@ -2114,6 +2125,7 @@ xfew_kernel(const StreamArgs a) {
     }
     put_word(mine + tm * kXW + q, tag_word(v, tag));
   }
+  if constexpr (POST) store_x(YK - 1, xlast);   // so that the words do not queue behind these stores
 
   // ---- the owned tokens' words from every slice, in one round trip
   const int nown = slice < nval ? (nval - 1 - slice) / S + 1 : 0;   // owned tokens slice, slice + S, ...
