@@ -892,6 +892,12 @@ enum : unsigned { kErrPollTimeout = 1u };
 __device__ __forceinline__ u64 tag_word(float v, u32 tag) { return ((u64)tag << 32) | __float_as_uint(v); }
 __device__ __forceinline__ void put_word(u64* p, u64 w) { __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ __forceinline__ u64 get_word(const u64* p) { return __hip_atomic_load(const_cast<u64*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+// The low half of the call epoch word (a 32-bit load: no dead half register
+// for the allocator to reuse while the load is in flight).
+__device__ __forceinline__ u32 epoch_low(const u64* ctl) {
+  return __hip_atomic_load(reinterpret_cast<u32*>(const_cast<u64*>(ctl + kCtlXEpoch)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
 // Waits until each of the words w[i] (at ptr(i), those with use(i)) holds the
 // call's tag: every round checks all of them and reloads all the stale ones
 // at once, so the wait ends one round trip after the last of them became
@@ -1608,7 +1614,9 @@ exchange_kernel(const StreamArgs a) {
   const bool has_pair = pr < nown * kXW;
   const int ptm = has_pair ? slice + S * (pr / kXW) : 0, pq = has_pair ? pr % kXW : 0;
 
-  if (threadIdx.x == 0) s_tag = (u32)get_word(a.ctl + kCtlXEpoch) + 1u;   // words carry epoch + 1
+  // (Issuing these after the first chunk's loads, as xfew_kernel does,
+  // measured no faster here, where the first loads of every workgroup queue.)
+  if (threadIdx.x == 0) s_tag = epoch_low(a.ctl) + 1u;   // words carry epoch + 1
   if (threadIdx.x < YK * kCF / 4) g_slice[threadIdx.x] = reinterpret_cast<const f32x4*>(a.gamma + fs)[threadIdx.x];
   // the split's parameters, requested now so that the derive does not wait for them
   if (a.pre_out && threadIdx.x >= kThreads - (kMix + 3)) {
@@ -1937,7 +1945,6 @@ xfew_kernel(const StreamArgs a) {
   __shared__ float tot[kXFMaxOwn][kXW];                // owned words summed over the slices
   __shared__ f32x4 g_slice[NORM ? YK * kCF / 4 : 1];   // gamma of the slice
   __shared__ float s_cf[kMix + 3];                     // hc_base, hc_scale (read by the derive)
-  __shared__ u32 s_tag;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1953,13 +1960,20 @@ xfew_kernel(const StreamArgs a) {
   const int a_st = fl >> 5, a_g = (fl >> 3) & 3;
   const int a_lane = a_g * 16 + hw * 8 + hl;
 
-  if (threadIdx.x == 0) s_tag = (u32)get_word(a.ctl + kCtlXEpoch) + 1u;   // words carry epoch + 1
-  if (NORM && threadIdx.x < YK * kCF / 4) g_slice[threadIdx.x] = reinterpret_cast<const f32x4*>(a.gamma + fs)[threadIdx.x];
-  // the split's parameters, requested now so that the derive does not wait for them
-  if (a.pre_out && threadIdx.x >= kThreads - (kMix + 3)) {
-    const int i = threadIdx.x - (kThreads - (kMix + 3));
-    s_cf[i] = i < kMix ? a.hc_base[i] : a.hc_scale[i - kMix];
-  }
+  // The call's tag, the slice's gamma and the split's parameters are
+  // requested by every lane without a branch, and written to LDS only once
+  // the first chunk's loads are in flight (a load inside a branch, with its
+  // wait, holds every later load of the wave behind it: a round trip at the
+  // start of a call that is all latency).
+  const u32 tag = epoch_low(a.ctl) + 1u;   // words carry epoch + 1 (one value for every lane)
+  f32x4 gv = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (NORM) gv = reinterpret_cast<const f32x4*>(a.gamma + fs)[min((int)threadIdx.x, YK * kCF / 4 - 1)];
+  const int cfi = max((int)threadIdx.x - (kThreads - (kMix + 3)), 0);
+  const float cfv = *(!a.pre_out ? reinterpret_cast<const float*>(a.ctl) : cfi < kMix ? a.hc_base + cfi : a.hc_scale + (cfi - kMix));
+  auto stage_params = [&]() __attribute__((always_inline)) {
+    if (NORM && threadIdx.x < YK * kCF / 4) g_slice[threadIdx.x] = gv;
+    if (threadIdx.x >= kThreads - (kMix + 3)) s_cf[cfi] = cfv;   // read by the derive only with pre_out
+  };
   const int64_t t0 = (int64_t)tile * kTT;
   const int nval = (int)min<int64_t>(kTT, a.n - t0);  // valid tokens of the tile
   const bool tv = m < nval;
@@ -2071,6 +2085,7 @@ xfew_kernel(const StreamArgs a) {
     u32x4 cur[kHC + 1], wst[kNT];
     load_wst(0, wst);
     load_stream(0, cur);
+    stage_params();
     store_wst(0, wst);
     lds_barrier();
     auto chunk = [&]<int C>(IC<C>) __attribute__((always_inline)) {
@@ -2096,7 +2111,6 @@ xfew_kernel(const StreamArgs a) {
   }
 
   // ---- the words of the valid tokens, through LDS
-  const u32 tag = s_tag;
   u64* tilew = a.xw + (size_t)tile * S * kTT * kXW;
   u64* mine = tilew + (size_t)slice * kTT * kXW;
 #pragma unroll
