@@ -711,6 +711,60 @@ __global__ void __launch_bounds__(kThreads) row_kernel(const RowArgs a) {
   }
 }
 
+// The stream-only calls without the RMSNorm (hc_post, hc_pre, the write of
+// a boundary at hc other than 4 or the read after it): one unit of work per
+// wave, a (token, 512-feature chunk) pair, four waves per workgroup, units
+// and workgroups in address order (token-major), so that the chip sweeps the
+// streams front to back (a sweep in address order streams faster than the
+// same bytes walked as many concurrent rows).  Each unit is row_kernel's
+// chunk: the same loads, arithmetic and stores.
+constexpr int kSweepWaves = 4;
+template <bool POST, bool PRE, int HC = kHC>
+__global__ void __launch_bounds__(kSweepWaves * 64) sweep_row_kernel(const RowArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int d = a.d;
+  const int nch = (d + kRowChunk - 1) / kRowChunk;
+  const int64_t u = (int64_t)blockIdx.x * kSweepWaves + wave;
+  const int64_t t = u / nch;
+  if (t >= a.n) return;                          // a whole wave: no barrier in this kernel
+  const int c = (int)(u - t * nch);
+  const int f0 = c * kRowChunk + lane * 8;
+  const bool act = f0 < d;
+  const int f = act ? f0 : 0;                    // idle lanes of a partial chunk read feature 0 and never store
+  float cpost[HC], ccomb[HC * HC], cpre[HC];
+#pragma unroll
+  for (int j = 0; j < HC; ++j) {
+    cpost[j] = POST ? a.post_in[t * HC + j] : 0.f;
+    cpre[j] = PRE ? a.pre_in[t * HC + j] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < HC * HC; ++j) ccomb[j] = POST ? a.comb_in[t * HC * HC + j] : 0.f;
+  u32x4 r[HC + 1];
+  row_load<POST, HC>(r, reinterpret_cast<const u32x4*>(a.x + t * a.xtok),
+                     reinterpret_cast<const u32x4*>(POST ? a.delta + t * d : a.x), a.xstr, f);
+  u32 xp[HC][4];
+  if constexpr (POST) {
+    post_8<HC>(r, cpost, ccomb, xp);
+    if (act) {
+      u32x4* xo = reinterpret_cast<u32x4*>(a.x_out + t * HC * d);
+#pragma unroll
+      for (int k = 0; k < HC; ++k) st_stream(xo + (k * d + f) / 8, u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]});
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < HC; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xp[k][e] = r[k][e];
+  }
+  if (a.x_mean && act) st_stream(reinterpret_cast<u32x4*>(a.x_mean + t * d) + f / 8, mean_8<HC>(xp));
+  if constexpr (PRE) {
+    u32 yp[4];
+    pre_8<HC>(xp, cpre, yp);
+    if (act) st_stream(reinterpret_cast<u32x4*>(a.y_out + t * d) + f / 8, u32x4{yp[0], yp[1], yp[2], yp[3]});
+  }
+}
+
 // hc = 2 with a write and a fresh pre: the write and the projection in one
 // pass ("Write the streams"; "Source layer, pairs pooled", Block.hc_mixes on
 // X'), so X' is not read back for the projection (only for the read, which
@@ -2783,6 +2837,29 @@ hipError_t launch_row_t(const RowArgs& a, hipStream_t st) {
                          dim3(kThreads), args, 0, st);
 }
 
+// the stream-only calls without the RMSNorm as an address-order sweep; false
+// if the grid would not fit (then the row kernel runs)
+template <bool POST, bool PRE, int HC = kHC>
+bool launch_sweep_t(const RowArgs& a, hipStream_t st, hipError_t& e) {
+  const int64_t units = a.n * (int64_t)((a.d + kRowChunk - 1) / kRowChunk);
+  const int64_t grid = (units + kSweepWaves - 1) / kSweepWaves;
+  if (grid > INT32_MAX) return false;
+  RowArgs copy = a;
+  void* args[] = {&copy};
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&sweep_row_kernel<POST, PRE, HC>), dim3((unsigned)grid),
+                      dim3(kSweepWaves * 64), args, 0, st);
+  return true;
+}
+template <int HC>
+bool launch_sweep_hc(int key, const RowArgs& a, hipStream_t st, hipError_t& e) {
+  switch (key) {
+    case 0b100: return launch_sweep_t<true, false, HC>(a, st, e);
+    case 0b010: return launch_sweep_t<false, true, HC>(a, st, e);
+    case 0b110: return launch_sweep_t<true, true, HC>(a, st, e);
+    default: return false;
+  }
+}
+
 // hc other than 4: one token per wave, every stage combination
 template <int HC>
 hipError_t launch_row_hc(int key, const RowArgs& a, hipStream_t st) {
@@ -2803,6 +2880,11 @@ int launch_row(bool post, bool pre, bool norm, const RowArgs& a, hipStream_t st,
   if (key != 0b100 && key != 0b010 && key != 0b110 && key != 0b011 && key != 0b111)
     return fail(HC_EINVAL, "%s: unsupported stage combination", what);
   hipError_t e;
+  if (!norm) {   // no row-wide statistic: the address-order sweep
+    const bool ok = hc == 2 ? launch_sweep_hc<2>(key, a, st, e)
+                  : hc == 8 ? launch_sweep_hc<8>(key, a, st, e) : launch_sweep_hc<kHC>(key, a, st, e);
+    if (ok) return launched(e, what);
+  }
   if (hc != kHC) {
     e = hc == 2 ? launch_row_hc<2>(key, a, st) : launch_row_hc<8>(key, a, st);
     return launched(e, what);
