@@ -765,6 +765,91 @@ __global__ void __launch_bounds__(kSweepWaves * 64) sweep_row_kernel(const RowAr
   }
 }
 
+// The same sweep for the calls with the RMSNorm of the read row ("Final
+// RMSNorm"; the stack exit, the read of a boundary at hc other than 4): a
+// workgroup per token, W = blockDim / 64 waves, wave w taking the chunks w,
+// w + W, ... (at most CPW), the read row kept in registers until the token's
+// sum y^2 is summed over the waves (in wave order) through LDS.
+constexpr int kSweepNormMaxW = 10;
+template <bool POST, int CPW, int HC = kHC>
+__global__ void __launch_bounds__(kSweepNormMaxW * 64) sweep_norm_kernel(const RowArgs a) {
+  __shared__ float red[kSweepNormMaxW];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = blockDim.x >> 6;
+  const int d = a.d;
+  const int nch = (d + kRowChunk - 1) / kRowChunk;
+  const int64_t t = blockIdx.x;
+  float cpost[HC], ccomb[HC * HC], cpre[HC];
+#pragma unroll
+  for (int j = 0; j < HC; ++j) {
+    cpost[j] = POST ? a.post_in[t * HC + j] : 0.f;
+    cpre[j] = a.pre_in[t * HC + j];
+  }
+#pragma unroll
+  for (int j = 0; j < HC * HC; ++j) ccomb[j] = POST ? a.comb_in[t * HC * HC + j] : 0.f;
+  u32x4 r[CPW][HC + 1];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int c = wave + W * i;
+    const int f0 = c * kRowChunk + lane * 8;
+    const int f = c < nch && f0 < d ? f0 : 0;
+    row_load<POST, HC>(r[i], reinterpret_cast<const u32x4*>(a.x + t * a.xtok),
+                       reinterpret_cast<const u32x4*>(POST ? a.delta + t * d : a.x), a.xstr, f);
+  }
+  u32 ykeep[CPW][4];
+  float ssy = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int c = wave + W * i;
+    const int f0 = c * kRowChunk + lane * 8;
+    const bool act = c < nch && f0 < d;
+    u32 xp[HC][4];
+    if constexpr (POST) {
+      post_8<HC>(r[i], cpost, ccomb, xp);
+      if (act) {
+        u32x4* xo = reinterpret_cast<u32x4*>(a.x_out + t * HC * d);
+#pragma unroll
+        for (int k = 0; k < HC; ++k) st_stream(xo + (k * d + f0) / 8, u32x4{xp[k][0], xp[k][1], xp[k][2], xp[k][3]});
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < HC; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xp[k][e] = r[i][k][e];
+    }
+    if (a.x_mean && act) st_stream(reinterpret_cast<u32x4*>(a.x_mean + t * d) + f0 / 8, mean_8<HC>(xp));
+    pre_8<HC>(xp, cpre, ykeep[i]);
+    if (act) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ssy = dot2_bf16(ykeep[i][e], ykeep[i][e], ssy);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ssy += __shfl_xor(ssy, o);
+  if (lane == 0) red[wave] = ssy;
+  __syncthreads();
+  float sy = red[0];
+  for (int w = 1; w < W; ++w) sy += red[w];
+  const float ry = 1.0f / sqrtf(sy / (float)d + a.rms_eps);
+  u32x4* yo = reinterpret_cast<u32x4*>(a.y_out + t * d);
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int c = wave + W * i;
+    const int f0 = c * kRowChunk + lane * 8;
+    if (c < nch && f0 < d) {
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(a.gamma + f0);
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(a.gamma + f0 + 4);
+      const float gm[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+      u32 zp[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2)
+        zp[e2] = pack_bf16(gm[2 * e2] * (bf_lo(ykeep[i][e2]) * ry), gm[2 * e2 + 1] * (bf_hi(ykeep[i][e2]) * ry));
+      st_stream(yo + f0 / 8, u32x4{zp[0], zp[1], zp[2], zp[3]});
+    }
+  }
+}
+
 // hc = 2 with a write and a fresh pre: the write and the projection in one
 // pass ("Write the streams"; "Source layer, pairs pooled", Block.hc_mixes on
 // X'), so X' is not read back for the projection (only for the read, which
@@ -2850,12 +2935,36 @@ bool launch_sweep_t(const RowArgs& a, hipStream_t st, hipError_t& e) {
                       dim3(kSweepWaves * 64), args, 0, st);
   return true;
 }
+// with the RMSNorm: a workgroup per token, up to kSweepNormMaxW waves, at most
+// two chunks per wave (d <= 10240); false if the shape does not fit
+template <bool POST, int HC>
+bool launch_sweep_norm_t(const RowArgs& a, hipStream_t st, hipError_t& e) {
+  const int nch = (a.d + kRowChunk - 1) / kRowChunk;
+  const int W = std::min(nch, kSweepNormMaxW);
+  const int cpw = (nch + W - 1) / W;
+  if (cpw > 2 || a.n > INT32_MAX) return false;
+  RowArgs copy = a;
+  void* args[] = {&copy};
+  const void* fn = cpw == 1 ? reinterpret_cast<const void*>(&sweep_norm_kernel<POST, 1, HC>)
+                            : reinterpret_cast<const void*>(&sweep_norm_kernel<POST, 2, HC>);
+  e = hipLaunchKernel(fn, dim3((unsigned)a.n), dim3(W * 64), args, 0, st);
+  return true;
+}
 template <int HC>
 bool launch_sweep_hc(int key, const RowArgs& a, hipStream_t st, hipError_t& e) {
   switch (key) {
     case 0b100: return launch_sweep_t<true, false, HC>(a, st, e);
     case 0b010: return launch_sweep_t<false, true, HC>(a, st, e);
     case 0b110: return launch_sweep_t<true, true, HC>(a, st, e);
+    // with the RMSNorm only at hc = 4 (at hc = 2 and 8 the read after the
+    // projection measured slower as a sweep: 65.3 against 63.6 and 303.7
+    // against 289.8 us per boundary at n = 4096)
+    case 0b011:
+      if constexpr (HC == kHC) return launch_sweep_norm_t<false, HC>(a, st, e);
+      return false;
+    case 0b111:
+      if constexpr (HC == kHC) return launch_sweep_norm_t<true, HC>(a, st, e);
+      return false;
     default: return false;
   }
 }
@@ -2880,7 +2989,7 @@ int launch_row(bool post, bool pre, bool norm, const RowArgs& a, hipStream_t st,
   if (key != 0b100 && key != 0b010 && key != 0b110 && key != 0b011 && key != 0b111)
     return fail(HC_EINVAL, "%s: unsupported stage combination", what);
   hipError_t e;
-  if (!norm) {   // no row-wide statistic: the address-order sweep
+  {   // the address-order sweep where the shape fits it
     const bool ok = hc == 2 ? launch_sweep_hc<2>(key, a, st, e)
                   : hc == 8 ? launch_sweep_hc<8>(key, a, st, e) : launch_sweep_hc<kHC>(key, a, st, e);
     if (ok) return launched(e, what);
