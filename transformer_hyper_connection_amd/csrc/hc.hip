@@ -27,13 +27,18 @@
 //       (decode, short prefill: up to 2048 tokens at d = 5120), a given pre
 //       or no read, with or without the RMSNorm: slices of 1 to 10 chunks, an
 //       owner slice per token derives it and publishes its RMS factor.
-//   row_kernel<POST, PRE, NORM, TPW, HC>  streams only (hc_post, hc_pre, the
-//       stack exit): whole token rows per wave, 1 KB per load or store.
+//   sweep_row_kernel<POST, PRE, HC>, sweep_norm_kernel<POST, CPW, HC>  streams
+//       only (hc_post, hc_pre, the stack exit) as a sweep through memory in
+//       address order: a (token, 512-feature chunk) per wave, or a token per
+//       workgroup with the RMSNorm.
+//   row_kernel<POST, PRE, NORM, TPW, HC>  streams only where the sweeps do
+//       not apply: whole token rows per wave, 1 KB per load or store.
 //   split_kernel<HC>  hc_split_sinkhorn, one token per lane.
 //   pack_kernel     fp32 projection weight -> bf16 hi/mid/lo terms in tile order.
-// hc = 2 and 8: row_kernel and split_kernel instantiated for that hc, and
-//   gpack_kernel / gmix_kernel / gfinish_kernel<HC>, the projection on the
-//   matrix cores with per-slice records and their finish.
+// hc = 2 and 8: the sweeps, row_kernel and split_kernel instantiated for that
+//   hc, and gpack_kernel / gmix_kernel / gfinish_kernel<HC>, the projection on
+//   the matrix cores with per-slice records and their finish (gstream_kernel<2>
+//   fuses the write into the projection at hc = 2).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
