@@ -89,6 +89,19 @@ def test_split_sinkhorn_stage(iters):
     assert_coef_close(host_f32(comb), rc, "comb")
 
 
+@pytest.mark.parametrize("n", [1, 17, 8192, 8193])
+def test_split_sinkhorn_both_layouts(n):
+    """16 lanes per token up to 8192 tokens, a comb row per lane beyond."""
+    say(f"[split] n={n}")
+    mixes = (np.random.default_rng(n).standard_normal((n, 24)) * 2.86).astype(np.float32)
+    _, base, scale = params(64, 11)
+    pre, post, comb = H.hc_split_sinkhorn(f32_dev(mixes), f32_dev(scale), f32_dev(base), 4, 20, 1e-6)
+    rp, rq, rc = O.hc_split_sinkhorn(mixes, scale, base, 4, 20, 1e-6)
+    assert_coef_close(host_f32(pre), rp, "pre")
+    assert_coef_close(host_f32(post), rq, "post")
+    assert_coef_close(host_f32(comb), rc, "comb")
+
+
 # ------------------------------------------------------------------ hc_post / hc_pre
 @pytest.mark.parametrize("n,d", [(37, 5120), (16, 64), (1, 128), (300, 320), (17, 7168)])
 def test_hc_post_bit_exact(n, d):

@@ -33,7 +33,8 @@
 //       workgroup with the RMSNorm.
 //   row_kernel<POST, PRE, NORM, TPW, HC>  streams only where the sweeps do
 //       not apply: whole token rows per wave, 1 KB per load or store.
-//   split_kernel<HC>  hc_split_sinkhorn, one token per lane.
+//   split16_kernel, split_kernel<HC>  hc_split_sinkhorn: 16 lanes per token at
+//       hc = 4 up to 8192 tokens (derive_16), else hc lanes per token.
 //   pack_kernel     fp32 projection weight -> bf16 hi/mid/lo terms in tile order.
 // hc = 2 and 8: the sweeps, row_kernel and split_kernel instantiated for that
 //   hc, and gpack_kernel / gmix_kernel / gfinish_kernel<HC>, the projection on
@@ -1118,6 +1119,20 @@ __device__ __forceinline__ void derive_16(const float* r, float rx, int j, int k
   if (k == 0) pre_out[t * HC + j] = g;
   if (k == 1) post_out[t * HC + j] = g;
   comb_out[t * HC * HC + 4 * j + k] = a;
+}
+
+// hc_split_sinkhorn at hc = 4 ("Reading weights" kernel panel): 16 lanes per
+// token (derive_16, one comb element per lane), 16 tokens per workgroup; the
+// shorter dependency chain per Sinkhorn round than hc lanes per token.
+__global__ void __launch_bounds__(256) split16_kernel(const float* __restrict__ mixes, const float* __restrict__ scale,
+                                                      const float* __restrict__ base, int64_t n, int iters, float eps,
+                                                      float* __restrict__ pre, float* __restrict__ post,
+                                                      float* __restrict__ comb) {
+  const int q = threadIdx.x & 15;
+  const int64_t tq = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool valid = tq < n;
+  const int64_t t = valid ? tq : 0;   // lanes past n compute on token 0 and store nothing
+  derive_16(mixes + t * kMix, 1.0f, q >> 2, q & 3, valid, t, scale, base, iters, eps, nullptr, pre, post, comb);
 }
 
 // ====================================================== boundary: two kernels
@@ -3116,6 +3131,7 @@ int launch_stream_generic(const hc_boundary_args* p, int xtok, int xstr, hc_bf16
   return launch_gfinish(2, f, st, what);
 }
 
+constexpr int64_t kSplit16MaxN = 8192;   // hc_split_sinkhorn at hc = 4 takes 16 lanes per token up to here
 int launch_split(int hc, const float* mixes, const float* scale, const float* base, int64_t n, int iters,
                  float eps, float* pre, float* post, float* comb, hipStream_t st) {
   const int64_t tpb = 256 / hc;                   // tokens per workgroup: hc lanes each
@@ -3124,7 +3140,10 @@ int launch_split(int hc, const float* mixes, const float* scale, const float* ba
     hipLaunchKernelGGL(split_kernel<2>, grid, block, 0, st, mixes, scale, base, n, iters, eps, pre, post, comb);
   else if (hc == 8)
     hipLaunchKernelGGL(split_kernel<8>, grid, block, 0, st, mixes, scale, base, n, iters, eps, pre, post, comb);
-  else
+  else if (n <= kSplit16MaxN)   // latency-bound: the shorter chain wins (n = 4096: 3.1 against 3.5 us)
+    hipLaunchKernelGGL(split16_kernel, dim3((unsigned)((n + 15) / 16)), block, 0, st, mixes, scale, base, n, iters, eps,
+                       pre, post, comb);
+  else                          // throughput-bound: 4x fewer lanes (n = 32768: 5.0 against 6.4 us)
     hipLaunchKernelGGL(split_kernel<kHC>, grid, block, 0, st, mixes, scale, base, n, iters, eps, pre, post, comb);
   return launched(hipGetLastError(), "split_kernel");
 }
