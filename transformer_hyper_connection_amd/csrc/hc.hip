@@ -717,13 +717,14 @@ __global__ void __launch_bounds__(kThreads) row_kernel(const RowArgs a) {
   }
 }
 
-// The stream-only calls without the RMSNorm (hc_post, hc_pre, the write of
-// a boundary at hc other than 4 or the read after it): one unit of work per
-// wave, a (token, 512-feature chunk) pair, four waves per workgroup, units
-// and workgroups in address order (token-major), so that the chip sweeps the
-// streams front to back (a sweep in address order streams faster than the
-// same bytes walked as many concurrent rows).  Each unit is row_kernel's
-// chunk: the same loads, arithmetic and stores.
+// The stream-only calls without the RMSNorm ("Write the streams"; "Source
+// layer, pairs pooled": Block.hc_post, Block.hc_pre; also the write of a
+// boundary at hc other than 4, and a read after it without the RMSNorm): one
+// unit of work per wave, a (token, 512-feature chunk) pair, four waves per
+// workgroup, units and workgroups in address order (token-major), so that the
+// chip sweeps the streams front to back (a sweep in address order streams
+// faster than the same bytes walked as many concurrent rows).  Each unit is
+// row_kernel's chunk: the same loads, arithmetic and stores.
 constexpr int kSweepWaves = 4;
 template <bool POST, bool PRE, int HC = kHC>
 __global__ void __launch_bounds__(kSweepWaves * 64) sweep_row_kernel(const RowArgs a) {
@@ -771,11 +772,11 @@ __global__ void __launch_bounds__(kSweepWaves * 64) sweep_row_kernel(const RowAr
   }
 }
 
-// The same sweep for the calls with the RMSNorm of the read row ("Final
-// RMSNorm"; the stack exit, the read of a boundary at hc other than 4): a
-// workgroup per token, W = blockDim / 64 waves, wave w taking the chunks w,
-// w + W, ... (at most CPW), the read row kept in registers until the token's
-// sum y^2 is summed over the waves (in wave order) through LDS.
+// The same sweep for the calls with the RMSNorm of the read row at hc = 4
+// ("Final RMSNorm"; the stack exit, a read of given streams): a workgroup per
+// token, W = blockDim / 64 waves, wave w taking the chunks w, w + W, ... (at
+// most CPW), the read row kept in registers until the token's sum y^2 is
+// summed over the waves (in wave order) through LDS.
 constexpr int kSweepNormMaxW = 10;
 template <bool POST, int CPW, int HC = kHC>
 __global__ void __launch_bounds__(kSweepNormMaxW * 64) sweep_norm_kernel(const RowArgs a) {
