@@ -137,11 +137,14 @@ def test_identities_on_gpu():
 # ------------------------------------------------------------------ hc_mixes
 # n <= 128 (d a multiple of 64 from 256 to 8192) runs the few-tile exchange; otherwise the stream
 # kernel (two chunks in flight, loop unrolled by two) with 64-feature chunks
-# per workgroup slice: 1 at d = 64, 2 at (300, 5120), 5 at (1000, 5120), 10 at
-# (2048, 5120), 20 at 4096 and 4097 (a ragged last tile), 4 at (5000, 1024):
-# every tail of the unrolled loop
+# up to 2048 tokens and from d = 256 the few-tile exchange (one launch; 1 chunk
+# per slice at n <= 192 and d = 5120, 2 at (300, 5120), 5 at (1000, 5120), 10
+# at (2048, 5120), 2 at (700, 2048), 8 at (1500, 4096)); else the projection
+# kernel and the finish (d = 64; 20 chunks per slice at 4096 and 4097, a
+# ragged last tile; 4 at (5000, 1024)): every tail of the unrolled loops
 @pytest.mark.parametrize("n,d", [(32, 5120), (45, 5120), (16, 64), (3, 1024), (19, 7168), (1000, 5120),
-                                 (2048, 5120), (300, 5120), (4096, 5120), (4097, 5120), (5000, 1024)])
+                                 (2048, 5120), (300, 5120), (4096, 5120), (4097, 5120), (5000, 1024),
+                                 (129, 1024), (700, 2048), (1500, 4096)])
 def test_hc_mixes_end_to_end(n, d):
     say(f"[hc_mixes] n={n} d={d}")
     x = rand_bits((n, 4, d))

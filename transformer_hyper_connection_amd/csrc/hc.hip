@@ -2090,7 +2090,7 @@ constexpr int kXFMinS = 4;                   // slices per tile at least
 constexpr int kXFMaxOwn = kTT / kXFMinS;     // owned tokens per slice at most (16)
 constexpr int kXFGroups = 20;                // partial sums per owned word at most
 constexpr int kXFOLoads = 8;                 // owned words per thread at most (S <= 8 G for every S)
-constexpr int kXFMixesMaxN = 128;            // hc_mixes takes the schedule up to this many tokens
+constexpr int kXFMixesMaxN = 2048;           // hc_mixes takes the schedule up to this many tokens
 
 template <bool POST, bool MEAN, bool READ, bool NORM, int YK>
 __global__ void __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 2)))
