@@ -106,9 +106,9 @@ int hc_fn_pack(const float* hc_fn, int hc, int d, void* fn_packed, void* stream)
  * the regions an hc = 4 call of the same d keeps, so one workspace may serve
  * calls of every hc.
  *
- * Few token tiles (hc = 4: decode, short prefill).  hc_mixes for n <= 128,
+ * Few token tiles (hc = 4: decode, short prefill).  hc_mixes for n <= 2048,
  * and hc_boundary with a given pre_in (the pages' data flow; with or without
- * gamma) for up to 32 tiles of 64 tokens (2048 tokens at d = 5120), with d a
+ * gamma), for up to 32 tiles of 64 tokens (2048 tokens at d = 5120), with d a
  * multiple of 64 from 256 to 8192, run as one launch: each workgroup streams a
  * (64-token tile, slice of 1 to 10 chunks of 64 features) item and adds its
  * per-token partial sums to the workspace as tagged words; the owner slice of

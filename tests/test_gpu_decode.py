@@ -1,6 +1,6 @@
 """GPU parity of the few-tile exchange at decode sizes: hc_boundary with a
-given pre (with and without the RMSNorm of the read row), and hc_mixes, for
-n <= 128 run as one launch ("Source layer, pairs pooled": Block.forward at
+given pre (with and without the RMSNorm of the read row), for n <= 128 run
+as one launch ("Source layer, pairs pooled": Block.forward at
 decode; "Reading weights"; "Final RMSNorm"): 64-token tiles, one 64-feature
 chunk per workgroup; the owner slice of a token sums its words over the
 slices, derives its coefficients and, with the RMSNorm, publishes the token's
